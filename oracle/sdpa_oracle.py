@@ -1,0 +1,233 @@
+"""Plain, slow, fp64 CPU oracle for exact scaled dot-product attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the package smoke check and the
+bench's CPU-baseline leg use it.  It shares no code, constant or helper with
+the HIP library; the only thing both sides see is the seeded input tensors.
+
+What it computes is the plain definition, written out with one library
+primitive (a dense matmul) per contraction and nothing fused, blocked or
+reordered:
+
+* scores     s_ij = scale * sum_d q[i,d] * k[j,d]
+  (tensai autograd guide, section "Attention の組み立て": q.MatMul(k.T()) then
+  Scale(1/sqrt(headDim)); HOF Flash Attention essay, section 4 "カーネル":
+  q.dot(k.t()) divided by a square root).  The scale is an argument; the
+  essay's width-based scale and the guide's headDim-based scale are both
+  particular values of it.
+* mask       z_ij = s_ij + mask_ij, mask 0 where key j is visible to query i
+  and -inf elsewhere, added after scaling (tensai guide, same section: the
+  constant (1,1,seq,seq) mask is 0 on and below the diagonal, -inf above, and
+  broadcasts over batch and head; "ブロードキャスト" section).  Key padding
+  hides keys j >= key_lens[b] for every query of batch b.
+* softmax    a_ij = exp(z_ij - m_i) / sum_j exp(z_ij - m_i), m_i = max_j z_ij,
+  over the last (key) axis (tensai guide, section "演算": Softmax acts on the
+  final axis; HOF essay section 4: exp of the scores divided by the row sums
+  gives a row-stochastic A).  Subtracting the row max is the one departure
+  from the essay's printed kernel, which exponentiates raw scores; the two
+  agree exactly in real arithmetic because softmax is shift invariant.
+* output     o_i = sum_j a_ij v_j   (HOF essay section 4: weights.dot(v)).
+* lse        lse_i = m_i + ln(sum_j exp(z_ij - m_i))  (the log of the softmax
+  denominator, used by the split-KV partials).
+* head map   query head h reads K/V head floor(h / (Hq / Hkv)) (grouped K/V,
+  ruDNN user guide section 9 "ページ化アテンションと MLA": Hq must be divisible
+  by Hkv; contiguous groups is the reading taken).
+* split-KV   partial attention over disjoint key ranges, each with its own lse,
+  and the log-sum-exp merge of those partials (ruDNN user guide section 9:
+  history split into 2..=32 pieces, partial statistics and merge in FP32).
+
+A row with no visible key has 0/0 weights and yields NaN, the literal result
+of the essay's normalisation (ruDNN user guide section 4 likewise keeps NaN
+for rows with no finite logit).
+
+Every function here is pinned by tests/test_oracle.py against closed forms,
+invariants, special cases and brute force; none is "parity unpinned".
+"""
+
+import numpy as np
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KEY_PADDING = 2
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D (batch, head, seq, headDim)")
+    B, Hq, _, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape:
+        raise ValueError("inconsistent q/k/v shapes %s %s %s" % (q.shape, k.shape, v.shape))
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, Sk, D
+
+
+def visible_rows(mask_kind, rows, Sk, key_len):
+    """Boolean [len(rows), Sk]: True where key j is visible to query row i.
+
+    rows are query positions.  Causal: j <= i (tensai guide, "Attention の組み立て":
+    0 on and below the diagonal).  Key padding: j < key_len.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    vis = np.ones((rows.shape[0], Sk), dtype=bool)
+    if mask_kind & MASK_CAUSAL:
+        vis &= j <= rows[:, None]
+    if mask_kind & MASK_KEY_PADDING:
+        vis &= j < int(key_len)
+    return vis
+
+
+def attend(qrows, kh, vh, scale, vis):
+    """Attention of query rows over one K/V head, by the definition.
+
+    qrows [n, D], kh and vh [Sk, D], vis [n, Sk] bool.  Returns
+    (o [n, D], lse [n], a [n, Sk]) in fp64.
+    """
+    qrows = np.asarray(qrows, dtype=np.float64)
+    kh = np.asarray(kh, dtype=np.float64)
+    vh = np.asarray(vh, dtype=np.float64)
+    s = float(scale) * (qrows @ kh.T)          # scale first ...
+    z = np.where(vis, s, -np.inf)              # ... then the additive 0 / -inf mask
+    with np.errstate(invalid="ignore", divide="ignore"):
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)                      # exp(-inf) = 0 on hidden keys
+        l = e.sum(axis=1, keepdims=True)
+        a = e / l                              # row-stochastic weights
+        o = a @ vh
+        lse = (m + np.log(l))[:, 0]
+    return o, lse, a
+
+
+def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
+                 return_lse=False, return_probs=False):
+    """Full forward O = softmax(Q K^T * scale + mask) V for every (b, h, i).
+
+    q [B,Hq,Sq,D], k and v [B,Hkv,Sk,D]; key_lens [B] when mask_kind has the
+    key-padding bit.  The causal mask is defined for square attention only
+    (the tensai guide's (seq, seq) mask), so causal with Sq != Sk is an error.
+    Returns o (fp64), plus lse [B,Hq,Sq] and/or probs [B,Hq,Sq,Sk] on request.
+    """
+    q = np.asarray(q)
+    B, Hq, Hkv, Sk, D = _check_shapes(q, np.asarray(k), np.asarray(v))
+    Sq = q.shape[2]
+    if mask_kind & MASK_CAUSAL and Sq != Sk:
+        raise ValueError("causal mask needs Sq == Sk")
+    if bool(mask_kind & MASK_KEY_PADDING) != (key_lens is not None):
+        raise ValueError("key_lens is given exactly when the key-padding bit is set")
+    G = Hq // Hkv
+    o = np.empty((B, Hq, Sq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64)
+    probs = np.empty((B, Hq, Sq, Sk), dtype=np.float64) if return_probs else None
+    rows = np.arange(Sq)
+    for b in range(B):
+        vis = visible_rows(mask_kind, rows, Sk, key_lens[b] if key_lens is not None else 0)
+        for h in range(Hq):
+            g = h // G
+            o[b, h], lse[b, h], a = attend(q[b, h], k[b, g], v[b, g], scale, vis)
+            if return_probs:
+                probs[b, h] = a
+    out = [o]
+    if return_lse:
+        out.append(lse)
+    if return_probs:
+        out.append(probs)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def sdpa_forward_rows(q, k, v, scale, mask_kind, key_lens, index):
+    """Selected output rows only: index is an int array [n, 3] of (b, h, i).
+
+    Same definition as sdpa_forward, evaluated only for the listed query rows
+    (grouped by head) so that it scales to full-size workloads.  q, k, v may be
+    any array-likes indexable as [b, h] (only the needed heads are read).
+    Returns (o [n, D], lse [n]) in the order of index.
+    """
+    B, Hq, _ = q.shape[0], q.shape[1], q.shape[2]
+    Hkv, Sk, D = k.shape[1], k.shape[2], k.shape[3]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if mask_kind & MASK_CAUSAL and q.shape[2] != Sk:
+        raise ValueError("causal mask needs Sq == Sk")
+    G = Hq // Hkv
+    index = np.asarray(index, dtype=np.int64).reshape(-1, 3)
+    o = np.empty((index.shape[0], D), dtype=np.float64)
+    lse = np.empty(index.shape[0], dtype=np.float64)
+    heads = {}
+    for n, (b, h, i) in enumerate(index):
+        heads.setdefault((int(b), int(h)), []).append((n, int(i)))
+    for (b, h), items in heads.items():
+        pos = np.array([n for n, _ in items])
+        rows = np.array([i for _, i in items])
+        klen = key_lens[b] if key_lens is not None else 0
+        vis = visible_rows(mask_kind, rows, Sk, klen)
+        g = h // G
+        qh = np.asarray(q[b, h])
+        o[pos], lse[pos], _ = attend(qh[rows], k[b, g], v[b, g], scale, vis)
+    return o, lse
+
+
+def sdpa_decode(q, k, v, scale, key_lens=None):
+    """Single-query decode: the forward with Sq = 1 and no causal mask.
+
+    Every cached key is visible except those past key_lens[b] when given.
+    """
+    kind = MASK_KEY_PADDING if key_lens is not None else MASK_NONE
+    return sdpa_forward(q, k, v, scale, kind, key_lens)
+
+
+def split_ranges(Sk, num_splits):
+    """Key range [lo, hi) of each split: chunks of ceil(Sk / num_splits) keys."""
+    chunk = -(-Sk // num_splits)
+    return [(min(s * chunk, Sk), min((s + 1) * chunk, Sk)) for s in range(num_splits)]
+
+
+def decode_split_partials(q, k, v, scale, key_lens, num_splits):
+    """Per-split partial attention for decode (q [B,Hq,1,D]).
+
+    Split s attends only to its key range (intersected with the visible keys)
+    and yields a normalised partial output and its log-sum-exp.  A split with
+    no visible key contributes o = 0 and lse = -inf (an empty softmax
+    denominator).  Returns (o_part [B,Hq,n,D], lse_part [B,Hq,n]).
+    """
+    B, Hq, Hkv, Sk, D = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    o_part = np.zeros((B, Hq, num_splits, D), dtype=np.float64)
+    lse_part = np.full((B, Hq, num_splits), -np.inf, dtype=np.float64)
+    for b in range(B):
+        vis_all = visible_rows(MASK_KEY_PADDING if key_lens is not None else MASK_NONE,
+                               [0], Sk, key_lens[b] if key_lens is not None else 0)
+        for s, (lo, hi) in enumerate(split_ranges(Sk, num_splits)):
+            vis = vis_all[:, lo:hi]
+            if not vis.any():
+                continue
+            for h in range(Hq):
+                g = h // G
+                on, ln, _ = attend(q[b, h, 0:1], k[b, g, lo:hi], v[b, g, lo:hi], scale, vis)
+                o_part[b, h, s], lse_part[b, h, s] = on[0], ln[0]
+    return o_part, lse_part
+
+
+def merge_partials(o_part, lse_part):
+    """Log-sum-exp merge of split partials over the split axis.
+
+    o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M), M = max_s lse_s.
+    o_part [..., n, D], lse_part [..., n]; returns (o [..., D], lse [...]).
+    """
+    o_part = np.asarray(o_part, dtype=np.float64)
+    lse_part = np.asarray(lse_part, dtype=np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        M = lse_part.max(axis=-1, keepdims=True)
+        w = np.exp(lse_part - M)
+        den = w.sum(axis=-1, keepdims=True)
+        o = (w[..., None] * o_part).sum(axis=-2) / den
+        lse = (M + np.log(den))[..., 0]
+    return o, lse
+
+
+__all__ = [
+    "MASK_NONE", "MASK_CAUSAL", "MASK_KEY_PADDING", "visible_rows", "attend",
+    "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
+    "decode_split_partials", "merge_partials",
+]

@@ -1,0 +1,365 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+Each pin is a closed form, an invariant the mathematics fixes, a special case
+that reduces to something elementary, or brute force on tiny inputs, chosen so
+that a plausible slip in the oracle (a dropped scale, a wrong sign, a transposed
+operand, the wrong softmax axis, an off-by-one mask, a wrong head map, a
+missing merge weight) fails at least one of them.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+RNG = np.random.default_rng(12345)
+
+
+def rand(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_hand_example_square():
+    # D = 1, scale = 1, q = k = [[1],[0]], v = [[1],[0]]:
+    # S = [[1, 0], [0, 0]] so row 0 weights (e, 1)/(1+e), row 1 weights (1/2, 1/2).
+    q = np.array([[[[1.0], [0.0]]]])
+    k = q.copy()
+    v = np.array([[[[1.0], [0.0]]]])
+    o, lse = O.sdpa_forward(q, k, v, 1.0, return_lse=True)
+    assert o[0, 0, 0, 0] == pytest.approx(math.e / (1 + math.e), abs=1e-15)
+    assert o[0, 0, 1, 0] == pytest.approx(0.5, abs=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(math.log(math.e + 1), abs=1e-15)
+    assert lse[0, 0, 1] == pytest.approx(math.log(2.0), abs=1e-15)
+
+
+def test_hand_example_rectangular_asymmetric():
+    # Sq = 2, Sk = 3, D = 2, scale = 1/2.  Non-square and asymmetric, so a
+    # transposed product, a dropped scale or a wrong exponent sign all change it.
+    q = np.array([[1.0, 0.0], [0.0, 2.0]])
+    k = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 3.0]])
+    # row 0 scores (0.5, 0, 0.5); row 1 scores (0, 1, 1)
+    e0 = [math.exp(0.5), 1.0, math.exp(0.5)]
+    e1 = [1.0, math.e, math.e]
+    want0 = [sum(e * v[j, d] for j, e in enumerate(e0)) / sum(e0) for d in range(2)]
+    want1 = [sum(e * v[j, d] for j, e in enumerate(e1)) / sum(e1) for d in range(2)]
+    o, lse = O.sdpa_forward(q[None, None], k[None, None], v[None, None], 0.5, return_lse=True)
+    np.testing.assert_allclose(o[0, 0, 0], want0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 1], want1, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], [math.log(sum(e0)), math.log(sum(e1))], atol=1e-15)
+
+
+def test_hand_example_causal_and_padding():
+    # Same rectangular data made square (Sq = Sk = 3) with a causal mask:
+    # row 0 sees key 0 only; row 1 sees keys 0,1; row 2 sees all three.
+    q = np.array([[1.0, 0.0], [0.0, 2.0], [1.0, 1.0]])
+    k = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 3.0]])
+    o = O.sdpa_forward(q[None, None], k[None, None], v[None, None], 0.5, O.MASK_CAUSAL)
+    w1 = [1.0, math.e]                                  # row 1 scores (0, 1)
+    w2 = [math.exp(0.5), math.exp(0.5), math.e]         # row 2 scores (.5, .5, 1)
+    np.testing.assert_allclose(o[0, 0, 0], v[0], atol=0)
+    np.testing.assert_allclose(o[0, 0, 1], (w1[0] * v[0] + w1[1] * v[1]) / sum(w1), atol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 2], (w2[0] * v[0] + w2[1] * v[1] + w2[2] * v[2]) / sum(w2),
+                               atol=1e-15)
+    # key padding with length 2 on the non-causal problem: row 2 sees keys 0,1
+    o = O.sdpa_forward(q[None, None], k[None, None], v[None, None], 0.5, O.MASK_KEY_PADDING,
+                       key_lens=np.array([2]))
+    w2p = [math.exp(0.5), math.exp(0.5)]
+    np.testing.assert_allclose(o[0, 0, 2], (w2p[0] * v[0] + w2p[1] * v[1]) / sum(w2p), atol=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("mask", [O.MASK_NONE, O.MASK_CAUSAL, O.MASK_KEY_PADDING,
+                                  O.MASK_CAUSAL | O.MASK_KEY_PADDING])
+def test_rows_stochastic_and_masked_zero(mask):
+    B, H, S, D = 2, 3, 9, 5
+    q, k, v = rand(B, H, S, D), rand(B, H, S, D), rand(B, H, S, D)
+    lens = np.array([4, 9]) if mask & O.MASK_KEY_PADDING else None
+    o, probs = O.sdpa_forward(q, k, v, 0.7, mask, lens, return_probs=True)
+    np.testing.assert_allclose(probs.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert (probs >= 0).all()
+    for b in range(B):
+        i = np.arange(S)[:, None]
+        j = np.arange(S)[None, :]
+        hidden = np.zeros((S, S), bool)
+        if mask & O.MASK_CAUSAL:
+            hidden |= j > i
+        if mask & O.MASK_KEY_PADDING:
+            hidden |= j >= lens[b]
+        assert (probs[b][:, hidden] == 0.0).all()
+        assert (probs[b][:, ~hidden] > 0.0).all()
+    # o is the weight matrix applied to V
+    np.testing.assert_allclose(o, probs @ v, atol=1e-13)
+
+
+def test_single_key_gives_v():
+    q, k, v = rand(2, 4, 7, 8), rand(2, 2, 1, 8), rand(2, 2, 1, 8)
+    o = O.sdpa_forward(q, k, v, 0.3)
+    for h in range(4):
+        np.testing.assert_array_equal(o[:, h], np.broadcast_to(v[:, h // 2], o[:, h].shape))
+
+
+def test_identical_v_rows():
+    q, k = rand(1, 2, 6, 4), rand(1, 2, 10, 4, scale=3.0)
+    r = rand(4)
+    v = np.broadcast_to(r, (1, 2, 10, 4)).copy()
+    for mask, lens in [(O.MASK_NONE, None), (O.MASK_CAUSAL | O.MASK_KEY_PADDING, np.array([3]))]:
+        if mask & O.MASK_CAUSAL:
+            qq, kk, vv = q, k[:, :, :6], v[:, :, :6]
+        else:
+            qq, kk, vv = q, k, v
+        o = O.sdpa_forward(qq, kk, vv, 1.0, mask, lens)
+        np.testing.assert_allclose(o, np.broadcast_to(r, o.shape), rtol=1e-14, atol=1e-15)
+
+
+def test_zero_query_gives_visible_means():
+    # Q = 0 makes every visible score 0, so the weights are uniform over the
+    # visible keys: plain mean, causal prefix means, or mean of the first len keys.
+    B, H, S, D = 2, 2, 11, 3
+    q = np.zeros((B, H, S, D))
+    k, v = rand(B, H, S, D), rand(B, H, S, D)
+    o, lse = O.sdpa_forward(q, k, v, 0.9, return_lse=True)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(2, keepdims=True), o.shape), atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(S), atol=1e-14)
+    o, lse = O.sdpa_forward(q, k, v, 0.9, O.MASK_CAUSAL, return_lse=True)
+    prefix = np.cumsum(v, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, prefix, atol=1e-14)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(np.arange(1, S + 1)), lse.shape),
+                               atol=1e-14)
+    lens = np.array([5, 1])
+    o = O.sdpa_forward(q, k, v, 0.9, O.MASK_KEY_PADDING, lens)
+    for b in range(B):
+        np.testing.assert_allclose(o[b], np.broadcast_to(v[b, :, :lens[b]].mean(1, keepdims=True),
+                                                         o[b].shape), atol=1e-14)
+    o = O.sdpa_forward(q, k, v, 0.9, O.MASK_CAUSAL | O.MASK_KEY_PADDING, lens)
+    for b in range(B):
+        for i in range(S):
+            n = min(i + 1, lens[b])
+            np.testing.assert_allclose(o[b, :, i], v[b, :, :n].mean(1), atol=1e-14)
+
+
+def test_causal_first_row_is_v0():
+    q, k, v = rand(3, 2, 8, 6), rand(3, 2, 8, 6), rand(3, 2, 8, 6)
+    o = O.sdpa_forward(q, k, v, 0.4, O.MASK_CAUSAL)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_shift_invariance_of_keys():
+    # Adding the same vector u to every key adds scale*q_i.u to all of row i.
+    q, k, v = rand(1, 2, 7, 5), rand(1, 2, 9, 5), rand(1, 2, 9, 5)
+    u = rand(5) * 2
+    for mask, lens in [(O.MASK_NONE, None), (O.MASK_KEY_PADDING, np.array([6]))]:
+        o1 = O.sdpa_forward(q, k, v, 0.6, mask, lens)
+        o2 = O.sdpa_forward(q, k + u, v, 0.6, mask, lens)
+        np.testing.assert_allclose(o1, o2, atol=1e-12)
+
+
+def test_permutation_equivariance():
+    q, k, v = rand(1, 1, 6, 4), rand(1, 1, 8, 4), rand(1, 1, 8, 4)
+    o = O.sdpa_forward(q, k, v, 0.8)
+    pk = RNG.permutation(8)
+    np.testing.assert_allclose(O.sdpa_forward(q, k[:, :, pk], v[:, :, pk], 0.8), o, atol=1e-13)
+    pq = RNG.permutation(6)
+    np.testing.assert_allclose(O.sdpa_forward(q[:, :, pq], k, v, 0.8), o[:, :, pq], atol=1e-13)
+
+
+def test_scale_acts_on_scores_only():
+    # softmax((2q) k^T * s/2) == softmax(q k^T * s): the scale multiplies scores.
+    q, k, v = rand(1, 2, 5, 3), rand(1, 2, 5, 3), rand(1, 2, 5, 3)
+    o1 = O.sdpa_forward(q, k, v, 0.5, O.MASK_CAUSAL)
+    o2 = O.sdpa_forward(2 * q, k, v, 0.25, O.MASK_CAUSAL)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    # scale -> 0 gives uniform weights over visible keys
+    o3 = O.sdpa_forward(q, k, v, 1e-300, O.MASK_CAUSAL)
+    np.testing.assert_allclose(o3[0, :, 4], v[0].mean(1), atol=1e-13)
+
+
+# ---------------------------------------------------------------- reductions
+
+def test_gqa_equals_repeated_mha():
+    q, k, v = rand(2, 8, 5, 4), rand(2, 2, 7, 4), rand(2, 2, 7, 4)
+    o = O.sdpa_forward(q, k, v, 0.5)
+    o_mha = O.sdpa_forward(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), 0.5)
+    np.testing.assert_array_equal(o, o_mha)
+
+
+def test_gqa_contiguous_head_groups():
+    # Each K/V head's V is a distinct constant, so the output names the head read:
+    # query head h must read K/V head h // (Hq / Hkv).
+    Hq, Hkv = 12, 3
+    q, k = rand(1, Hq, 4, 2), rand(1, Hkv, 6, 2)
+    v = np.ones((1, Hkv, 6, 2)) * (np.arange(Hkv) + 1.0)[None, :, None, None]
+    o = O.sdpa_forward(q, k, v, 1.0)
+    for h in range(Hq):
+        np.testing.assert_allclose(o[0, h], h // (Hq // Hkv) + 1.0, rtol=1e-14)
+
+
+def test_causal_row_equals_prefix_problem():
+    q, k, v = rand(1, 2, 10, 4), rand(1, 2, 10, 4), rand(1, 2, 10, 4)
+    o = O.sdpa_forward(q, k, v, 0.7, O.MASK_CAUSAL)
+    for i in range(10):
+        oi = O.sdpa_forward(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], 0.7)
+        np.testing.assert_allclose(o[:, :, i], oi[:, :, 0], atol=1e-14)
+
+
+def test_padding_equals_truncation():
+    q, k, v = rand(3, 2, 5, 4), rand(3, 2, 12, 4), rand(3, 2, 12, 4)
+    lens = np.array([1, 7, 12])
+    o = O.sdpa_forward(q, k, v, 0.7, O.MASK_KEY_PADDING, lens)
+    for b in range(3):
+        ob = O.sdpa_forward(q[b:b + 1], k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], 0.7)
+        np.testing.assert_allclose(o[b], ob[0], atol=1e-14)
+
+
+def test_rows_match_full():
+    q, k, v = rand(2, 4, 16, 8), rand(2, 2, 16, 8), rand(2, 2, 16, 8)
+    lens = np.array([9, 16])
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL, O.MASK_CAUSAL | O.MASK_KEY_PADDING):
+        kl = lens if mask & O.MASK_KEY_PADDING else None
+        o, lse = O.sdpa_forward(q, k, v, 0.3, mask, kl, return_lse=True)
+        idx = np.array([[0, 0, 0], [1, 3, 15], [0, 2, 7], [1, 1, 8], [0, 0, 5]])
+        orow, lrow = O.sdpa_forward_rows(q, k, v, 0.3, mask, kl, idx)
+        for n, (b, h, i) in enumerate(idx):
+            np.testing.assert_allclose(orow[n], o[b, h, i], atol=1e-14)
+            assert lrow[n] == pytest.approx(lse[b, h, i], abs=1e-14)
+
+
+def test_decode_is_single_query_forward():
+    q, k, v = rand(3, 4, 1, 8), rand(3, 2, 20, 8), rand(3, 2, 20, 8)
+    lens = np.array([20, 1, 13])
+    o = O.sdpa_decode(q, k, v, 0.35, lens)
+    for b in range(3):
+        for h in range(4):
+            ob = O.sdpa_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h // 2:h // 2 + 1, :lens[b]],
+                                v[b:b + 1, h // 2:h // 2 + 1, :lens[b]], 0.35)
+            np.testing.assert_allclose(o[b, h, 0], ob[0, 0, 0], atol=1e-14)
+
+
+# ---------------------------------------------------------------- split / merge
+
+def test_split_ranges_partition_keys():
+    for Sk, n in [(1, 1), (7, 2), (32768, 32), (5, 8), (100, 7), (1024, 32)]:
+        r = O.split_ranges(Sk, n)
+        assert len(r) == n and r[0][0] == 0 and r[-1][1] == Sk
+        for (a, b), (c, d) in zip(r, r[1:]):
+            assert b == c and a <= b
+        assert all(hi - lo <= -(-Sk // n) for lo, hi in r)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 32])
+def test_split_merge_identity(n):
+    # Merging the partials of any partition of the keys reproduces the unsplit result.
+    q, k, v = rand(2, 4, 1, 8), rand(2, 2, 19, 8, scale=2.0), rand(2, 2, 19, 8)
+    for lens in (None, np.array([19, 3])):
+        o_full, lse_full = O.sdpa_forward(q, k, v, 0.5,
+                                          O.MASK_KEY_PADDING if lens is not None else O.MASK_NONE,
+                                          lens, return_lse=True)
+        op, lp = O.decode_split_partials(q, k, v, 0.5, lens, n)
+        o, lse = O.merge_partials(op, lp)
+        np.testing.assert_allclose(o, o_full[:, :, 0], atol=1e-14)
+        np.testing.assert_allclose(lse, lse_full[:, :, 0], atol=1e-13)
+        # each partial is itself the attention over its own key range
+        for s, (lo, hi) in enumerate(O.split_ranges(19, n)):
+            top = hi if lens is None else None
+            for b in range(2):
+                hib = min(hi, lens[b]) if lens is not None else top
+                if hib <= lo:
+                    assert lp[b, :, s].tolist() == [-np.inf] * 4
+                    assert (op[b, :, s] == 0).all()
+                    continue
+                ob, lb = O.sdpa_forward(q[b:b + 1], k[b:b + 1, :, lo:hib], v[b:b + 1, :, lo:hib],
+                                        0.5, return_lse=True)
+                np.testing.assert_allclose(op[b, :, s], ob[0, :, 0], atol=1e-14)
+                np.testing.assert_allclose(lp[b, :, s], lb[0, :, 0], atol=1e-14)
+
+
+def test_merge_closed_form():
+    # Two partials with lse (0, ln 3): weights 1/4 and 3/4.
+    op = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    lp = np.array([[0.0, math.log(3.0)]])
+    o, lse = O.merge_partials(op, lp)
+    np.testing.assert_allclose(o, [[0.25, 0.75]], atol=1e-15)
+    assert lse[0] == pytest.approx(math.log(4.0), abs=1e-15)
+    # an empty partial (lse = -inf) carries zero weight
+    o, _ = O.merge_partials(np.array([[[5.0], [7.0]]]), np.array([[-np.inf, 2.0]]))
+    assert o[0, 0] == 7.0
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_force(q, k, v, scale, mask, lens):
+    """Scalar loops with exactly rounded sums (math.fsum), tiny shapes only."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    out = np.zeros(q.shape)
+    for b, h, i in itertools.product(range(B), range(Hq), range(Sq)):
+        g = h * Hkv // Hq
+        keys = [j for j in range(Sk)
+                if (not mask & O.MASK_CAUSAL or j <= i)
+                and (not mask & O.MASK_KEY_PADDING or j < lens[b])]
+        s = {j: scale * math.fsum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)) for j in keys}
+        mx = max(s.values())
+        e = {j: math.exp(s[j] - mx) for j in keys}
+        den = math.fsum(e.values())
+        for d in range(D):
+            out[b, h, i, d] = math.fsum(e[j] * v[b, g, j, d] for j in keys) / den
+    return out
+
+
+@pytest.mark.parametrize("mask", [O.MASK_NONE, O.MASK_CAUSAL, O.MASK_KEY_PADDING,
+                                  O.MASK_CAUSAL | O.MASK_KEY_PADDING])
+def test_brute_force_tiny(mask):
+    for S, D, Hq, Hkv in [(1, 1, 1, 1), (3, 2, 2, 1), (5, 4, 4, 2), (8, 3, 3, 3)]:
+        q, k, v = rand(2, Hq, S, D, scale=2), rand(2, Hkv, S, D, scale=2), rand(2, Hkv, S, D)
+        lens = np.array([max(1, S // 2), S]) if mask & O.MASK_KEY_PADDING else None
+        o = O.sdpa_forward(q, k, v, 0.75, mask, lens)
+        np.testing.assert_allclose(o, brute_force(q, k, v, 0.75, mask, lens), rtol=0, atol=1e-13)
+
+
+def test_printed_kernel_without_max_subtraction():
+    # The essay's printed kernel exponentiates raw scores and divides by the row
+    # sums; on small scores (no overflow) it must agree with the max-shifted form.
+    x = rand(6, 4, scale=0.5)
+    wq, wk, wv = rand(4, 4), rand(4, 4), rand(4, 4)
+    q, k, v = x @ wq, x @ wk, x @ wv
+    scale = 1.0 / math.sqrt(x.shape[1])
+    ex = [[math.exp(scale * sum(q[i, d] * k[j, d] for d in range(4))) for j in range(6)]
+          for i in range(6)]
+    want = np.array([[sum(ex[i][j] / sum(ex[i]) * v[j, d] for j in range(6)) for d in range(4)]
+                     for i in range(6)])
+    o = O.sdpa_forward(q[None, None], k[None, None], v[None, None], scale)
+    np.testing.assert_allclose(o[0, 0], want, atol=1e-13)
+
+
+def test_large_scores_do_not_overflow():
+    # Scores far beyond exp's range: the max-shifted definition stays finite and
+    # puts all weight on the largest score.
+    q = np.array([[[[1000.0], [-1000.0]]]])
+    k = np.array([[[[1.0], [2.0]]]])
+    v = np.array([[[[3.0], [5.0]]]])
+    o = O.sdpa_forward(q, k, v, 1.0)
+    assert o[0, 0, 0, 0] == 5.0 and o[0, 0, 1, 0] == 3.0
+
+
+def test_fully_masked_row_is_nan():
+    q, k, v = rand(1, 1, 3, 2), rand(1, 1, 3, 2), rand(1, 1, 3, 2)
+    o = O.sdpa_forward(q, k, v, 1.0, O.MASK_KEY_PADDING, np.array([0]))
+    assert np.isnan(o).all()
+
+
+def test_argument_checks():
+    q, k, v = rand(1, 3, 2, 2), rand(1, 2, 2, 2), rand(1, 2, 2, 2)
+    with pytest.raises(ValueError):
+        O.sdpa_forward(q, k, v, 1.0)
+    with pytest.raises(ValueError):
+        O.sdpa_forward(rand(1, 1, 2, 2), rand(1, 1, 3, 2), rand(1, 1, 3, 2), 1.0, O.MASK_CAUSAL)
+    with pytest.raises(ValueError):
+        O.sdpa_forward(rand(1, 1, 2, 2), rand(1, 1, 3, 2), rand(1, 1, 3, 2), 1.0,
+                       O.MASK_KEY_PADDING)
