@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of libsdpa on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over synthetic inputs already
+resident in HBM:
+  * prefill, causal, bf16, B=4 Hq=Hkv=16 Sq=Sk=4096 D=128   (the headline)
+  * prefill, grouped K/V 32/8 with key padding, bf16, B=2 S=8192 D=128
+  * split-KV decode, bf16, B=64 Hq=32 Hkv=8 Sk=32768 D=128, 32 splits + merge
+Each call is bracketed by HIP events on the stream it is launched on (torch's
+current stream, which is the stream the binding hands to the library).
+
+`value` is the causal prefill's TFLOP/s by the headline formula
+4*B*Hq*Sq*Sk*D, halved when causal; `roofline` is that kernel's fraction of
+the bf16 dense MFMA peak.  The decode result (HBM GB/s over the K+V+Q+O bytes
+of one call, fraction of the 8 TB/s HBM peak) and the padded prefill are
+reported in their own objects on the same line.  `cpu_baseline` times the fp64
+oracle on a bounded sample of the causal prefill workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (+% bf16 MFMA peak); decode HBM GB/s (+% peak)"
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+PREFILL = "bf16_causal_b4_h16_s4096_d128"
+PADDED = "bf16_gqa32x8_padded_b2_s8192_d128"
+DECODE = "bf16_gqa32x8_decode_b64_sk32768_d128"
+
+
+def kernel_source_hash(name):
+    path = os.path.join(ROOT, "exact_scaled_dot_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload, source):
+    """HBM bytes per launch from the committed counter summary, if still valid."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(source):
+        return None  # the kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def formula_flops(B, Hq, Sq, Sk, D, causal):
+    f = 4.0 * B * Hq * Sq * Sk * D
+    return f / 2 if causal else f
+
+
+def padded_algorithmic_flops(w, key_lens):
+    # 4 * Hq * Sq * D per visible key, summed over the batch (no causal mask here)
+    return 4.0 * w.Hq * w.Sq * w.D * float(sum(int(x) for x in key_lens))
+
+
+def cpu_baseline(budget_s):
+    """fp64 oracle on the first (batch, head) pairs of the causal prefill workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from exact_scaled_dot_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[PREFILL]
+    inp = make_inputs(w, "cpu")
+    q, k, v = (inp[x].to(torch.float64).numpy() for x in ("q", "k", "v"))
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.B * w.Hq:
+        b, h = divmod(heads, w.Hq)
+        oracle.sdpa_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.scale,
+                            oracle.MASK_CAUSAL)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    flops = heads * formula_flops(1, 1, w.Sq, w.Sk, w.D, True)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) pairs of %s, %.1f s, fp64 NumPy/BLAS; affinity %d cores"
+                      % (heads, w.B * w.Hq, w.name, dt, len(os.sched_getaffinity(0)))}
+
+
+def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
+    """Turn two rocprofv3 --pmc runs of a full-step bench (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into HBM bytes per launch for each workload,
+    calibrated on the plain 1 GiB device copy that --copy-calibration adds, and
+    tagged with the hash of the kernel source they were measured on."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Dispatch_Id"]), float(r["Counter_Value"]) * 1024.0))
+        return {k: [x for _, x in sorted(v)] for k, v in rows.items()}
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy = "__amd_rocclr_copyBuffer"
+    f_scale = copy_bytes / max(fetch[copy])   # true bytes / counted bytes
+    w_scale = copy_bytes / max(write[copy])
+    out = {"_calibration": {"copy_bytes": copy_bytes, "fetch_scale": round(f_scale, 4),
+                            "write_scale": round(w_scale, 4),
+                            "note": "FETCH_SIZE/WRITE_SIZE KiB per dispatch x scale"}}
+
+    def entry(kernel, src, reads, writes):
+        r = statistics.median(reads) * f_scale
+        w = statistics.median(writes) * w_scale
+        return {"kernel": kernel, "source_sha256_16": kernel_source_hash(src),
+                "read_bytes": round(r), "write_bytes": round(w),
+                "hbm_bytes_per_launch": round(r + w)}
+
+    fwd = "forward_bf16_kernel"
+    if fwd in fetch:  # a full step launches the causal prefill, then the padded one
+        out["prefill"] = entry(fwd, "forward.hip", fetch[fwd][0::2], write[fwd][0::2])
+        out["padded"] = entry(fwd, "forward.hip", fetch[fwd][1::2], write[fwd][1::2])
+    for key, name in (("decode_split", "decode_split_bf16_kernel"),
+                      ("decode_merge", "decode_merge_bf16_kernel")):
+        if name in fetch:
+            out[key] = entry(name, "decode.hip", fetch[name], write[name])
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--only", choices=["prefill", "padded", "decode"], default=None,
+                    help="run one call per step (for per-kernel profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
+    args = ap.parse_args()
+
+    if args.ingest_counters:
+        rec = ingest_counters(*args.ingest_counters)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec, indent=1))
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_scaled_dot_amd as sd
+    from exact_scaled_dot_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sd.load_library()
+
+    wp, wg, wd = WORKLOADS[PREFILL], WORKLOADS[PADDED], WORKLOADS[DECODE]
+    ip = make_inputs(wp, dev)
+    ig = make_inputs(wg, dev)
+    idd = make_inputs(wd, dev)
+    out_p = torch.empty_like(ip["q"])
+    out_g = torch.empty_like(ig["q"])
+    out_d = torch.empty_like(idd["q"])
+    ws = torch.empty(sd.sdpa_decode_workspace_size(wd.B, wd.Hq, wd.D, wd.num_splits),
+                     dtype=torch.uint8, device=dev)
+    lens_g = ig["key_lens"].cpu().tolist()
+    torch.cuda.synchronize()
+
+    calls = {
+        "prefill": lambda: sd.sdpa_forward(ip["q"], ip["k"], ip["v"], wp.scale, sd.MASK_CAUSAL,
+                                           None, out_p),
+        "padded": lambda: sd.sdpa_forward(ig["q"], ig["k"], ig["v"], wg.scale,
+                                          sd.MASK_KEY_PADDING, ig["key_lens"], out_g),
+        "decode": lambda: sd.sdpa_decode(idd["q"], idd["k"], idd["v"], wd.scale, None,
+                                         wd.num_splits, ws, out_d),
+    }
+    order = [args.only] if args.only else ["prefill", "padded", "decode"]
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        for name in order:
+            calls[name]()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = {name: [] for name in order}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name in order:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            calls[name]()
+            b.record(stream)
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name in order}
+
+    rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+
+    if "prefill" in ms:
+        fl = formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
+        tf = fl / (ms["prefill"] * 1e-3) / 1e12
+        traffic = stored_traffic("prefill", "forward.hip")
+        rec.update({"value": round(tf, 3), "unit": "TFLOP/s"})
+        rec["config"] = {"workload": wp.name, "B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq,
+                         "Sk": wp.Sk, "D": wp.D, "mask": "causal", "scale": wp.scale,
+                         "step_calls": order}
+        rec["prefill_ms"] = round(ms["prefill"], 4)
+        rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 3),
+                           "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                           "kernel": "forward_bf16_kernel<128>",
+                           "flops_per_launch": fl}
+    if "padded" in ms:
+        fl = formula_flops(wg.B, wg.Hq, wg.Sq, wg.Sk, wg.D, False)
+        fa = padded_algorithmic_flops(wg, lens_g)
+        rec["padded"] = {"workload": wg.name, "ms": round(ms["padded"], 4),
+                         "tflops_formula": round(fl / (ms["padded"] * 1e-3) / 1e12, 3),
+                         "tflops_algorithmic": round(fa / (ms["padded"] * 1e-3) / 1e12, 3),
+                         "frac_algorithmic": round(fa / (ms["padded"] * 1e-3) / 1e12
+                                                   / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "key_lens": lens_g}
+    if "decode" in ms:
+        kv_bytes = 2 * wd.B * wd.Hkv * wd.Sk * wd.D * 2
+        qo_bytes = 2 * wd.B * wd.Hq * wd.D * 2
+        by = kv_bytes + qo_bytes
+        gbs = by / (ms["decode"] * 1e-3) / 1e9
+        rec["decode"] = {"workload": wd.name, "ms": round(ms["decode"], 4), "value": round(gbs, 1),
+                         "unit": "GB/s",
+                         "tflops_formula": round(formula_flops(wd.B, wd.Hq, 1, wd.Sk, wd.D, False)
+                                                 / (ms["decode"] * 1e-3) / 1e12, 3),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                      "traffic": stored_traffic("decode_split", "decode.hip"),
+                                      "kernel": "decode_split_bf16_kernel<128> + merge",
+                                      "bytes_per_launch": by}}
+    if "value" not in rec:
+        rec.update({"value": rec["decode"]["value"], "unit": "GB/s"})
+        rec["config"] = {"workload": wd.name}
+
+    del ip, ig, idd
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and args.only in (None, "prefill"):
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

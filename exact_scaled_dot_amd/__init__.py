@@ -1,0 +1,12 @@
+"""libsdpa: exact scaled dot-product attention forward on MI355X (gfx950).
+
+The computation lives in the HIP library libsdpa.so (include/sdpa.h); this
+package is its thin ctypes binding plus the seeded workload generator.
+"""
+
+from .sdpa import (  # noqa: F401
+    MASK_CAUSAL, MASK_KEY_PADDING, MASK_NONE, MAX_SPLITS, SDPA_BF16, SDPA_ERR_HIP,
+    SDPA_ERR_INVALID_ARGUMENT, SDPA_ERR_UNSUPPORTED, SDPA_ERR_WORKSPACE, SDPA_F32, SDPA_OK,
+    SdpaError, decode_workspace_views, last_error, load_library, sdpa_decode,
+    sdpa_decode_workspace_size, sdpa_forward, status_string,
+)

@@ -1,0 +1,39 @@
+// Internal interface between the C-ABI front end (sdpa_api.cpp) and the
+// kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+struct ForwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const int32_t* key_lens;  // nullptr unless key padding is on
+    int B, Hq, Hkv, Sq, Sk, D;
+    float scale;
+    bool causal;
+    bool padded;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const int32_t* key_lens;  // nullptr = every key valid
+    float* o_part;            // [B, Hq, splits, D]
+    float* lse_part;          // [B, Hq, splits]
+    int B, Hq, Hkv, Sk, D;
+    int splits;
+    float scale;
+};
+
+hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace sdpa

@@ -1,0 +1,209 @@
+// C-ABI front end of libsdpa: argument validation (on the host, before any
+// HIP call), kernel choice and launch on the caller's stream.  The contract
+// is documented in include/sdpa.h.
+#include "sdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sdpa_status_t fail(sdpa_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+sdpa_status_t ok() {
+    g_last_error[0] = '\0';
+    return SDPA_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+// Element count of a 4-D tensor, or -1 on int64 overflow.
+int64_t numel4(int64_t a, int64_t b, int64_t c, int64_t d) {
+    int64_t r;
+    if (!mul_ok(a, b, &r) || !mul_ok(r, c, &r) || !mul_ok(r, d, &r)) return -1;
+    return r;
+}
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int64_t elem_size(int dtype) { return dtype == SDPA_BF16 ? 2 : 4; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shared checks of both entry points.  On success fills the tensor byte sizes.
+sdpa_status_t check_common(const void* q, const void* k, const void* v, void* out, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                           float scale, int dtype, int64_t* qbytes, int64_t* kbytes) {
+    if (!q || !k || !v || !out) return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "every size must be >= 1 (B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld)",
+                    (long long)B, (long long)Hq, (long long)Hkv, (long long)Sq, (long long)Sk,
+                    (long long)D);
+    if (Hq % Hkv != 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                    (long long)Hq, (long long)Hkv);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if (dtype != SDPA_F32 && dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    const int64_t es = elem_size(dtype);
+    const int64_t nq = numel4(B, Hq, Sq, D), nk = numel4(B, Hkv, Sk, D);
+    if (nq < 0 || nk < 0 || !mul_ok(nq, es, qbytes) || !mul_ok(nk, es, kbytes))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
+    if (overlap(out, *qbytes, q, *qbytes) || overlap(out, *qbytes, k, *kbytes) ||
+        overlap(out, *qbytes, v, *kbytes))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
+    if (B > INT_MAX || Hq > INT_MAX || Sq > INT_MAX || Sk > INT_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
+    if (D != 64 && D != 128)
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
+    return SDPA_OK;
+}
+
+sdpa_status_t hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdpa_status_string(int status) {
+    switch (status) {
+        case SDPA_OK: return "ok";
+        case SDPA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case SDPA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SDPA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SDPA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* sdpa_last_error(void) { return g_last_error; }
+
+sdpa_status_t sdpa_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                           int mask_kind, const int32_t* key_lens, void* out, int dtype,
+                           void* stream) {
+    int64_t qbytes = 0, kbytes = 0;
+    sdpa_status_t st = check_common(q, k, v, out, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
+                                    &kbytes);
+    if (st != SDPA_OK) return st;
+    if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
+    const bool causal = mask_kind & SDPA_MASK_CAUSAL;
+    const bool padded = mask_kind & SDPA_MASK_KEY_PADDING;
+    if (causal && Sq != Sk)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "causal mask needs Sq == Sk (got %lld, %lld)",
+                    (long long)Sq, (long long)Sk);
+    if (padded != (key_lens != nullptr))
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "key_lens must be given exactly when SDPA_MASK_KEY_PADDING is set");
+    if (padded && overlap(out, qbytes, key_lens, B * (int64_t)sizeof(int32_t)))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps key_lens");
+    const int64_t blocks = ((Sq + 127) / 128) * B * Hq;
+    if (blocks > INT_MAX / 256)
+        return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
+
+    sdpa::ForwardArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.key_lens = key_lens;
+    a.B = (int)B;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.Sq = (int)Sq;
+    a.Sk = (int)Sk;
+    a.D = (int)D;
+    a.scale = scale;
+    a.causal = causal;
+    a.padded = padded;
+    (void)hipGetLastError();  // clear an unrelated pending error
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_forward_bf16(a, s)
+                                            : sdpa::launch_forward_f32(a, s);
+    return hip_status(e, "sdpa_forward launch");
+}
+
+size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_splits) {
+    if (B < 1 || Hq < 1 || D < 1 || num_splits < 1 || num_splits > SDPA_MAX_SPLITS) return 0;
+    const int64_t rows = numel4(B, Hq, num_splits, 1);
+    const int64_t no = numel4(B, Hq, num_splits, D);
+    if (rows < 0 || no < 0 || no > INT64_MAX / 8) return 0;
+    return round_up((size_t)no * sizeof(float)) + round_up((size_t)rows * sizeof(float));
+}
+
+sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t Sk, int64_t D, float scale,
+                          const int32_t* key_lens, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* out, int dtype, void* stream) {
+    int64_t qbytes = 0, kbytes = 0;
+    sdpa_status_t st =
+        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes);
+    if (st != SDPA_OK) return st;
+    if (num_splits < 1 || num_splits > SDPA_MAX_SPLITS)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..%d", num_splits,
+                    SDPA_MAX_SPLITS);
+    if (key_lens && overlap(out, qbytes, key_lens, B * (int64_t)sizeof(int32_t)))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps key_lens");
+    const size_t need = sdpa_decode_workspace_size(B, Hq, D, num_splits);
+    if (need == 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    if (!workspace || workspace_bytes < need)
+        return fail(SDPA_ERR_WORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (overlap(out, qbytes, workspace, (int64_t)need))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps the workspace");
+    if (dtype != SDPA_BF16)
+        return fail(SDPA_ERR_UNSUPPORTED, "decode supports bf16 only");
+    const int64_t G = Hq / Hkv;
+    const int64_t blocks = B * Hkv * ((G + 3) / 4) * num_splits;
+    if (blocks > INT_MAX / 256)
+        return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
+
+    sdpa::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.key_lens = key_lens;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          round_up((size_t)numel4(B, Hq, num_splits, D) * 4));
+    a.B = (int)B;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.Sk = (int)Sk;
+    a.D = (int)D;
+    a.splits = num_splits;
+    a.scale = scale;
+    (void)hipGetLastError();
+    const hipError_t e = sdpa::launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sdpa_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+"""ctypes binding of libsdpa (include/sdpa.h).
+
+Argument marshalling only: tensor shapes become the C sizes, data pointers and
+torch's current HIP stream are passed through, and every step of the
+computation runs in the library's HIP kernels.  If libsdpa.so is not built the
+first call raises; there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+# Mirrors of the C enums in include/sdpa.h.
+SDPA_OK = 0
+SDPA_ERR_INVALID_ARGUMENT = 1
+SDPA_ERR_UNSUPPORTED = 2
+SDPA_ERR_WORKSPACE = 3
+SDPA_ERR_HIP = 4
+SDPA_F32 = 0
+SDPA_BF16 = 1
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KEY_PADDING = 2
+MAX_SPLITS = 32
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+EXPORTED = ("sdpa_forward", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_status_string",
+            "sdpa_last_error")
+
+_lib = None
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("libsdpa: %s (%d): %s" % (status_string(status), status, detail))
+
+
+def load_library():
+    """Load libsdpa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsdpa.so is not built (%s); run `python -m exact_scaled_dot_amd.build`"
+                           % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.sdpa_forward.restype = i32
+    lib.sdpa_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, i32, vp,
+                                 vp, i32, vp]
+    lib.sdpa_decode.restype = i32
+    lib.sdpa_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, i32, vp,
+                                ctypes.c_size_t, vp, i32, vp]
+    lib.sdpa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_decode_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.sdpa_status_string.restype = ctypes.c_char_p
+    lib.sdpa_status_string.argtypes = [i32]
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().sdpa_status_string(status).decode()
+
+
+def last_error():
+    return load_library().sdpa_last_error().decode()
+
+
+def _check(status):
+    if status != SDPA_OK:
+        raise SdpaError(status, last_error())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SDPA_BF16
+    if t.dtype == torch.float32:
+        return SDPA_F32
+    raise TypeError("libsdpa supports bfloat16 and float32 tensors, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(name, t, ndim):
+    if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+        raise ValueError("%s must be a %d-D torch tensor" % (name, ndim))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=None, stream=None):
+    """O = softmax(Q K^T * scale + mask) V.  q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D]."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, 4)
+    if key_lens is not None:
+        _check_tensor("key_lens", key_lens, 1)
+        if key_lens.dtype != torch.int32:
+            raise TypeError("key_lens must be int32")
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Sk, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    lib = load_library()
+    _check(lib.sdpa_forward(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                            int(mask_kind), _ptr(key_lens), _ptr(out), _dtype_code(q),
+                            _stream(stream)))
+    return out
+
+
+def sdpa_decode_workspace_size(B, Hq, D, num_splits):
+    return int(load_library().sdpa_decode_workspace_size(B, Hq, D, num_splits))
+
+
+def sdpa_decode(q, k, v, scale, key_lens=None, num_splits=MAX_SPLITS, workspace=None, out=None,
+                stream=None):
+    """Single-query decode: q [B,Hq,1,D], k/v [B,Hkv,Sk,D], split-KV + merge."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, 4)
+    B, Hq, Sq, D = q.shape
+    if Sq != 1:
+        raise ValueError("decode takes one query per (batch, head): q must be [B, Hq, 1, D]")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Sk, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if key_lens is not None:
+        _check_tensor("key_lens", key_lens, 1)
+        if key_lens.dtype != torch.int32:
+            raise TypeError("key_lens must be int32")
+    lib = load_library()
+    need = int(lib.sdpa_decode_workspace_size(B, Hq, D, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.sdpa_decode(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sk, D, float(scale),
+                           _ptr(key_lens), int(num_splits), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _ptr(out),
+                           _dtype_code(q), _stream(stream)))
+    return out
+
+
+def decode_workspace_views(workspace, B, Hq, D, num_splits):
+    """(o_part [B,Hq,n,D], lse [B,Hq,n]) fp32 views of a decode workspace."""
+    n_o = B * Hq * num_splits * D
+    off = (n_o * 4 + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    o_part = f[: n_o * 4].view(torch.float32).view(B, Hq, num_splits, D)
+    lse = f[off: off + B * Hq * num_splits * 4].view(torch.float32).view(B, Hq, num_splits)
+    return o_part, lse

@@ -1,0 +1,140 @@
+/*
+ * libsdpa — exact scaled dot-product attention forward on MI355X (gfx950).
+ *
+ * Computes O = softmax(Q K^T * scale + mask) V over the last (key) axis, with
+ * the score matrix never written to memory.  The operation is the one built
+ * from reshape, two batched products, a scale, an additive 0/-inf causal mask
+ * and a last-axis softmax in the tensai autograd guide (section
+ * "Attention の組み立て"), the exact dense kernel of the HOF Flash Attention
+ * essay (distillative.ai, section 4 "カーネル"), and the dense / paged
+ * attention entry points of the ruDNN user guide (sections 2 and 9).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layout: q is [B, Hq, Sq, D], k and v are [B, Hkv, Sk, D], out is
+ *    [B, Hq, Sq, D]; all contiguous, row-major, innermost dimension D
+ *    (the (batch, head, seq, headDim) layout of the tensai guide).
+ *  - Grouped K/V: Hq must be a multiple of Hkv; query head h reads K/V head
+ *    h / (Hq / Hkv) (contiguous groups; ruDNN guide section 9 requires only
+ *    divisibility).
+ *  - dtype: q, k, v and out share one element type, SDPA_BF16 or SDPA_F32.
+ *    Products accumulate in fp32; softmax statistics (running max, sum,
+ *    log-sum-exp) are fp32; the output is rounded to the input type (round to
+ *    nearest even), as the ruDNN guide's normalisation ops do (section 7).
+ *    On the bf16 path the softmax weights are rounded to bf16 before the
+ *    product with V; scores, statistics and Q are never rounded.
+ *  - Pointers: every tensor pointer (q, k, v, out, key_lens, workspace) is a
+ *    DEVICE pointer on the current HIP device, owned by the caller.  The
+ *    library allocates nothing and keeps no per-call state.
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *    enqueued and the call returns; out is valid once the stream has reached
+ *    that point.  The library never synchronises.
+ *  - Errors: arguments are validated on the host before any HIP call; on
+ *    error nothing is launched and out is left untouched.  A launch failure
+ *    returns SDPA_ERR_HIP.  There is no fallback kernel: a valid call that no
+ *    kernel covers returns SDPA_ERR_UNSUPPORTED (the ruDNN guide's rule that
+ *    an automatic choice falls back only for unsupported configurations and
+ *    never hides an execution failure, section 10).
+ *  - Not checked (device data): finiteness of q, k, v, and key_lens values.
+ *    Contract: 1 <= key_lens[b] <= Sk.  A value above Sk acts as Sk; a value
+ *    <= 0 leaves every key of that batch hidden and its output rows NaN
+ *    (0/0, the literal result of normalising an empty softmax).
+ *  - Aliasing: out must not overlap q, k, v, key_lens or the workspace
+ *    (ruDNN guide section 11: outputs may not overlap inputs).
+ *  - Concurrency: calls are reentrant; calls on different streams do not
+ *    interact.  Calls that share a decode workspace must be ordered on one
+ *    stream (ruDNN guide section 9: a split workspace is reused only with the
+ *    same shapes and one ordered queue).
+ */
+#ifndef LIBSDPA_SDPA_H
+#define LIBSDPA_SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDPA_OK = 0,
+    SDPA_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, flag or aliasing       */
+    SDPA_ERR_UNSUPPORTED = 2,      /* valid, but no kernel covers it (e.g. D)    */
+    SDPA_ERR_WORKSPACE = 3,        /* decode workspace missing or too small      */
+    SDPA_ERR_HIP = 4               /* a HIP runtime call or launch failed        */
+} sdpa_status_t;
+
+typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1 } sdpa_dtype_t;
+
+/* Mask flags, combinable with |. */
+enum {
+    SDPA_MASK_NONE = 0,
+    SDPA_MASK_CAUSAL = 1,      /* key j visible to query i iff j <= i (needs Sq == Sk);
+                                  tensai guide: 0 on and below the diagonal, -inf above */
+    SDPA_MASK_KEY_PADDING = 2  /* key j of batch b visible iff j < key_lens[b]          */
+};
+
+/* Largest split count of the decode path (ruDNN guide section 9: 2..=32 splits,
+ * plus the unsplit case 1). */
+#define SDPA_MAX_SPLITS 32
+
+/*
+ * Prefill / full forward.
+ *   q        device [B, Hq, Sq, D], dtype
+ *   k, v     device [B, Hkv, Sk, D], dtype
+ *   B, Hq, Hkv, Sq, Sk, D   sizes, all >= 1, Hq % Hkv == 0
+ *   scale    finite, > 0; multiplies the scores before the mask is added
+ *   mask_kind  SDPA_MASK_* flags; SDPA_MASK_CAUSAL requires Sq == Sk
+ *   key_lens device int32 [B] when mask_kind has SDPA_MASK_KEY_PADDING, else NULL
+ *   out      device [B, Hq, Sq, D], dtype; written completely
+ *   dtype    SDPA_BF16 or SDPA_F32
+ *   stream   hipStream_t as void*
+ * Supported head dims: D in {64, 128} (SDPA_ERR_UNSUPPORTED otherwise).
+ */
+sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                           float scale, int mask_kind, const int32_t *key_lens,
+                           void *out, int dtype, void *stream);
+
+/*
+ * Bytes of device workspace sdpa_decode needs for these sizes (0 if the sizes
+ * are invalid).  Layout, fp32, 256-byte aligned sections:
+ *   o_part [B, Hq, num_splits, D]  normalised partial outputs
+ *   lse    [B, Hq, num_splits]     natural-log log-sum-exp of each partial
+ * Split s covers keys [s*C, min((s+1)*C, len_b)) with C = ceil(Sk / num_splits)
+ * and len_b = key_lens[b] (or Sk); an empty split holds o_part = 0, lse = -inf.
+ * (ruDNN guide section 9: split partial statistics and the merge are FP32.)
+ */
+size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_splits);
+
+/*
+ * Single-query decode with split-KV and a log-sum-exp merge (ruDNN guide
+ * section 9, split history).  Equivalent to sdpa_forward with Sq = 1 and no
+ * causal mask: every cached key below key_lens[b] (or Sk) is visible.
+ *   q          device [B, Hq, 1, D]
+ *   k, v       device [B, Hkv, Sk, D]
+ *   key_lens   device int32 [B] or NULL (all Sk keys valid)
+ *   num_splits 1..SDPA_MAX_SPLITS
+ *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
+ *   out        device [B, Hq, 1, D]
+ * Two kernels are enqueued on stream: the split pass, then the merge.
+ * Supported: dtype SDPA_BF16, D in {64, 128}.
+ */
+sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D,
+                          float scale, const int32_t *key_lens, int num_splits,
+                          void *workspace, size_t workspace_bytes,
+                          void *out, int dtype, void *stream);
+
+/* Static English name of a status code; never NULL. */
+const char *sdpa_status_string(int status);
+
+/* Detail of the last failed call on this host thread ("" if none); valid
+ * until the next call on the same thread. */
+const char *sdpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSDPA_SDPA_H */

@@ -1,0 +1,53 @@
+"""Tolerance checks shared by the GPU parity tests.
+
+Bars: fp32 inputs, max |O_gpu - O_ref| <= 1e-4; bf16 inputs, max-abs <= 2e-2
+and ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 5e-3 over the compared elements; no
+NaN or Inf anywhere (unless the reference row itself is NaN: a row with no
+visible key).  O_ref is the fp64 oracle output, never rounded first.
+"""
+
+import numpy as np
+import torch
+
+F32_MAX_ABS = 1e-4
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 5e-3
+
+
+def to64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def compare(got, ref, dtype, what=""):
+    """Assert the bars; returns (max_abs, rel_l2) for reporting."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), "%s: NaN pattern differs" % what
+    g, r = got[~nan_ref], ref[~nan_ref]
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    if g.size == 0:
+        return 0.0, 0.0
+    max_abs = float(np.abs(g - r).max())
+    den = float(np.linalg.norm(r))
+    rel = float(np.linalg.norm(g - r) / den) if den > 0 else float(np.linalg.norm(g - r))
+    if dtype == torch.float32:
+        assert max_abs <= F32_MAX_ABS, "%s: max-abs %.3e > %.0e" % (what, max_abs, F32_MAX_ABS)
+    else:
+        assert max_abs <= BF16_MAX_ABS, "%s: max-abs %.3e > %.0e" % (what, max_abs, BF16_MAX_ABS)
+        assert rel <= BF16_REL_L2, "%s: rel-L2 %.3e > %.0e" % (what, rel, BF16_REL_L2)
+    return max_abs, rel
+
+
+def sample_rows(B, Hq, Sq, n, seed, must=()):
+    """n distinct (b, h, i) rows: the listed ones, tile edges, and random ones."""
+    rng = np.random.default_rng(seed)
+    rows = set(tuple(int(x) for x in m) for m in must)
+    edges = [0, 1, 31, 32, 63, 64, 65, 127, 128, 129, Sq // 2, Sq - 2, Sq - 1]
+    for i in edges:
+        if 0 <= i < Sq:
+            rows.add((int(rng.integers(B)), int(rng.integers(Hq)), i))
+    while len(rows) < n:
+        rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq))))
+    return np.array(sorted(rows), dtype=np.int64)

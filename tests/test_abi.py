@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports what include/sdpa.h declares, and rejects
+bad arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_scaled_dot_amd as sd
+from exact_scaled_dot_amd import sdpa as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libsdpa.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE_K = ctypes.c_void_p(0x20000000)
+FAKE_V = ctypes.c_void_p(0x40000000)
+FAKE_O = ctypes.c_void_p(0x60000000)
+FAKE_W = ctypes.c_void_p(0x70000000)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sd.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert sd.status_string(sd.SDPA_OK) == "ok"
+    assert "invalid" in sd.status_string(sd.SDPA_ERR_INVALID_ARGUMENT)
+    assert sd.status_string(99) == "unknown status"
+
+
+def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, scale=0.125,
+        mask=0, key_lens=None, out=FAKE_O, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    return lib.sdpa_forward(q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, mask, key_lens, out, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(out=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(B=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Sk=-5), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(scale=0.0), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(scale=float("nan")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(scale=float("inf")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(dtype=7), sd.SDPA_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(mask=4), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),
+    (dict(mask=1, Sq=64), sd.SDPA_ERR_INVALID_ARGUMENT, "Sq == Sk"),
+    (dict(mask=2), sd.SDPA_ERR_INVALID_ARGUMENT, "key_lens"),
+    (dict(mask=0, key_lens=ctypes.c_void_p(0x50000000)), sd.SDPA_ERR_INVALID_ARGUMENT, "key_lens"),
+    (dict(out=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(out=ctypes.c_void_p(0x40000000 - 2)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(B=1 << 40, Hq=1 << 20), sd.SDPA_ERR_INVALID_ARGUMENT, "overflow"),
+    (dict(D=96), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(Sq=1 << 33, Sk=1 << 33, B=1, Hq=1, Hkv=1, D=64, out=ctypes.c_void_p(1 << 46)),
+     sd.SDPA_ERR_UNSUPPORTED, "32-bit"),
+])
+def test_forward_rejects(kw, status, needle):
+    assert fwd(**kw) == status
+    assert needle in sd.last_error()
+
+
+def test_key_lens_must_not_alias_out():
+    st = fwd(mask=2, key_lens=ctypes.c_void_p(0x60000000 + 8))
+    assert st == sd.SDPA_ERR_INVALID_ARGUMENT and "key_lens" in sd.last_error()
+
+
+def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1, key_lens=None,
+        splits=8, ws=FAKE_W, ws_bytes=None, out=FAKE_O, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.sdpa_decode_workspace_size(B, Hq, D, splits)
+    return lib.sdpa_decode(q, k, v, B, Hq, Hkv, Sk, D, scale, key_lens, splits, ws, ws_bytes, out,
+                           dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(v=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(splits=0), sd.SDPA_ERR_INVALID_ARGUMENT, "num_splits"),
+    (dict(splits=33, ws_bytes=1 << 30), sd.SDPA_ERR_INVALID_ARGUMENT, "num_splits"),
+    (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(scale=-1.0), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(D=80), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+])
+def test_decode_rejects(kw, status, needle):
+    assert dec(**kw) == status
+    assert needle in sd.last_error()
+
+
+def test_decode_workspace_size():
+    lib = sd.load_library()
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    for B, Hq, D, n in [(64, 32, 128, 32), (1, 1, 64, 1), (3, 5, 64, 7)]:
+        assert lib.sdpa_decode_workspace_size(B, Hq, D, n) == up(B * Hq * n * D * 4) + up(B * Hq * n * 4)
+    # 64 x 32 heads x 32 splits x 128 dims stays inside the 64 MiB split-workspace budget
+    assert lib.sdpa_decode_workspace_size(64, 32, 128, 32) <= 64 << 20
+    for bad in [(0, 1, 64, 1), (1, 1, 64, 0), (1, 1, 64, 33), (1, 0, 64, 2)]:
+        assert lib.sdpa_decode_workspace_size(*bad) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sd.sdpa_forward(q, q, q, 0.125)
