@@ -41,24 +41,31 @@ struct TileInfo {
     int b, h, gk, q0;
 };
 
-// Workgroup -> (batch, head, query block).  Consecutive workgroups take
-// consecutive (batch, head) pairs of one query block: workgroups are dealt to
-// the 8 XCDs round-robin, so as long as B*Hq is a multiple of 8 every
-// workgroup of a given head lands on the same XCD and its K/V stays in that
-// XCD's L2.  With a causal mask the longest query blocks come first so the
-// short ones fill the tail.
+// Workgroup -> (batch, head, query block).  Workgroups are dealt to the 8
+// XCDs round-robin (id % 8), and each XCD has its own L2, so the id is first
+// turned into a position in a logical order in which every XCD owns one
+// contiguous run.  The logical order walks K/V heads outermost, then query
+// blocks (longest first under a causal mask, so short blocks fill the tail),
+// then the Hq/Hkv query heads that share the K/V head: the workgroups an XCD
+// runs at the same time read the same K/V rows, and every K/V head is
+// fetched into one L2 only.
 __device__ __forceinline__ TileInfo decode_tile(const ForwardArgs& a) {
     const int nqb = (a.Sq + kBr - 1) / kBr;
-    const int BH = a.B * a.Hq;
-    const int bh = blockIdx.x % BH;
-    int qb = blockIdx.x / BH;
-    if (a.causal) qb = nqb - 1 - qb;
-    TileInfo t;
-    t.b = bh / a.Hq;
-    t.h = bh % a.Hq;
-    t.gk = t.h / (a.Hq / a.Hkv);
-    t.q0 = qb * kBr;
-    return t;
+    const int G = a.Hq / a.Hkv;
+    const int T = a.B * a.Hq * nqb;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int nx = T >> 3, rem = T & 7;
+    int t = xcd * nx + min(xcd, rem) + local;
+    const int hsub = t % G;
+    t /= G;
+    const int qord = t % nqb;
+    const int unit = t / nqb;
+    TileInfo ti;
+    ti.b = unit / a.Hkv;
+    ti.gk = unit % a.Hkv;
+    ti.h = ti.gk * G + hsub;
+    ti.q0 = (a.causal ? nqb - 1 - qord : qord) * kBr;
+    return ti;
 }
 
 // Number of keys this workgroup must visit and the per-batch key limit.
@@ -72,23 +79,72 @@ __device__ __forceinline__ void key_extent(const ForwardArgs& a, int b, int q0, 
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
+//
+// Tiles reach LDS by buffer-load DMA (buffer_load_dwordx4 ... lds): each
+// instruction writes 64 lanes x 16 B = 1 KB contiguously, loads past the
+// buffer's num_records return zeros (keys >= Sk need no branch), and no VGPR
+// holds the in-flight tile.  The loads of tile j+1 are issued before tile j is
+// computed, into the other of two LDS stages; one barrier per tile.
+//
+// LDS rows are unpadded, so 16-byte chunks are XOR-swizzled instead:
+//   K: chunk c of LDS row r sits at c ^ fk(r), fk(r) = (r / RPW) % (16 / RPW);
+//      the 16 rows one MFMA operand read touches land in 16 distinct 16-byte
+//      bank groups.
+//   V: chunk c of row r sits at c ^ fv(r), fv(r) = 4 * ((r / RPW) % (4 / RPW));
+//      the 4 rows x 64 B of one 32-lane transposed read are conflict free.
+// (RPW = rows per 256-byte bank window: 1 for D = 128, 2 for D = 64.)
+//
+// The V^T operand of the second product is read with ds_read_b64_tr_b16:
+// inside each 16-lane group, lane t receives element t%4 of the 8-byte chunks
+// addressed by lanes t/4, 4+t/4, 8+t/4 and 12+t/4, so pointing lane j at
+// V[k0 + j/4][d0 + 4*(j%4)] hands lane t the four keys V[k0..k0+3][d0 + t].
 // ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x2 lds_read_tr16x4(const uint16_t* p) {
+    lds_i16x4* lp = (lds_i16x4*)((__attribute__((address_space(3))) char*)p);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16*l (the destination is wave-uniform; M0 carries it).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes); loads beyond it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int D>
+struct Bf16Geo {
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int RPW = 256 / (2 * D);        // rows per 256-byte bank window
+    static constexpr int TILE = kBc * D;             // bf16 elements per K or V tile
+    static constexpr int STAGE = 2 * TILE;           // K tile then V tile
+    static constexpr int DMA = TILE * 2 / 1024 / 4;  // 1-KB DMA loads per wave per tensor
+    __device__ static int fk(int r) { return (r / RPW) % (16 / RPW); }
+    __device__ static int fv(int r) { return 4 * ((r / RPW) % (4 / RPW)); }
+};
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a) {
-    constexpr int KS = D + 8;    // K row stride in LDS (bf16), 16 B of padding
-    constexpr int VS = kBc + 8;  // V^T row stride in LDS (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kBc * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+    using L = Bf16Geo<D>;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * L::STAGE];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hg = lane >> 5;  // which half of the wave
 
     const TileInfo ti = decode_tile(a);
     const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + bh * a.Sq * D;
     const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * D;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kvh;
     const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kvh;
@@ -100,122 +156,176 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
     const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
 
-    // Q fragment for the B operand of S^T = K Q^T: lane holds Q[qi][16t + 8hg .. +7].
+    // Q fragment for the B operand of S^T = K Q^T: lane holds Q[qi][16t + 8hg .. +7]
+    // (rows >= Sq read as zeros).
     bf16x8 qr[D / 16];
+    {
+        const __amdgpu_buffer_rsrc_t qrs =
+            make_rsrc(static_cast<const uint16_t*>(a.q) + bh * a.Sq * D, (uint32_t)a.Sq * D * 2);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (qi < a.Sq) w = ldg128(qp + (int64_t)qi * D + 16 * t + 8 * hg);
-        qr[t] = as_bf16x8(w);
+        for (int t = 0; t < D / 16; ++t)
+            qr[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+                qrs, (qi * D + 16 * t + 8 * hg) * 2, 0, 0));
+    }
+
+    // DMA source offsets (bytes, relative to the tile's first key).  DMA load i
+    // of this wave fills LDS bytes [1024*(DMA*wave + i), +1024); lane l's 16 B
+    // land at 16-byte slot p = 64*(DMA*wave + i) + l = (row, physical chunk).
+    uint32_t koff[L::DMA], voff[L::DMA];
+#pragma unroll
+    for (int i = 0; i < L::DMA; ++i) {
+        const int p = 64 * (L::DMA * wave + i) + lane;
+        const int row = p / L::CPR, pc = p % L::CPR;
+        koff[i] = k_lds_row(row) * D * 2 + ((pc ^ L::fk(row)) * 16);
+        voff[i] = row * D * 2 + ((pc ^ L::fv(row)) * 16);
+    }
+    auto issue_tile = [&](int j0, int stage) {
+        // Resources start at the tile's first key; num_records ends at key Sk.
+        const uint32_t left = (uint32_t)(a.Sk - j0) * D * 2;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp + (int64_t)j0 * D, left);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp + (int64_t)j0 * D, left);
+        uint16_t* ks = smem + stage * L::STAGE;
+        uint16_t* vs = ks + L::TILE;
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) {
+            dma16(krs, ks + 512 * (L::DMA * wave + i), koff[i]);
+            dma16(vrs, vs + 512 * (L::DMA * wave + i), voff[i]);
+        }
+    };
+
+    // Lane-constant LDS read offsets (bf16 elements).
+    // K operand: LDS row 32*kb2 + l32, logical chunk 2t + hg.
+    int krd[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) krd[t] = l32 * D + (((2 * t + hg) ^ L::fk(l32)) * 8);
+    // V^T operand: row 16*kk + tr_row (+4), element column 32*db + tr_col.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int tr_row = 8 * hg + (j16 >> 2);
+    const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
+    int vrd[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int col = 32 * db + tr_col;
+        vrd[db] = tr_row * D + (((col >> 3) ^ L::fv(tr_row)) * 8) + (col & 7);
     }
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;  // running max of the raw scores of row qi
+    float m_run = -INFINITY;  // reference max of row qi (raw score units)
     float l_run = 0.f;        // this lane's share of the running denominator
     const float c = a.scale * kLog2e;
+    // The reference max moves only when a row's tile max exceeds it by more
+    // than 8 in log2 units; weights then stay <= 2^8 and O / l is unchanged.
+    const float tau = 8.0f / c;
+    const uint32_t ones_bf16x2 = 0x3f803f80u;
 
-    for (int jt = 0; jt < ntiles; ++jt) {
+    if (ntiles > 0) issue_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // One tile: issue the DMA of the next tile into the other stage, compute
+    // this one.  Both calls below pass a literal stage, so after inlining
+    // every LDS read of the tile carries its stage base as an instruction
+    // offset.
+    auto step = [&](int jt, const int cur) __attribute__((always_inline)) {
         const int j0 = jt * kBc;
-        __syncthreads();  // previous tile fully consumed
-        // K tile, row-major, rows permuted by k_lds_row; keys >= Sk read as 0.
-#pragma unroll
-        for (int cidx = tid; cidx < kBc * (D / 8); cidx += kThreads) {
-            const int row = cidx / (D / 8), cc = cidx % (D / 8);
-            const int key = j0 + row;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (key < a.Sk) w = ldg128(kp + (int64_t)key * D + cc * 8);
-            *reinterpret_cast<u32x4*>(ks + k_lds_row(row) * KS + cc * 8) = w;
-        }
-        // V tile, stored transposed (V^T[d][key]): each item moves 4 keys x 8 dims.
-#pragma unroll
-        for (int it = tid; it < (kBc / 4) * (D / 8); it += kThreads) {
-            const int dg = it % (D / 8), kg = it / (D / 8);
-            u32x4 r[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = j0 + 4 * kg + rr;
-                r[rr] = u32x4{0u, 0u, 0u, 0u};
-                if (key < a.Sk) r[rr] = ldg128(vp + (int64_t)key * D + dg * 8);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {  // dword e holds dims 2e (low half) and 2e+1
-                const u32x2 lo = {pack_lo16(r[0][e], r[1][e]), pack_lo16(r[2][e], r[3][e])};
-                const u32x2 hi = {pack_hi16(r[0][e], r[1][e]), pack_hi16(r[2][e], r[3][e])};
-                *reinterpret_cast<u32x2*>(vt + (dg * 8 + 2 * e) * VS + 4 * kg) = lo;
-                *reinterpret_cast<u32x2*>(vt + (dg * 8 + 2 * e + 1) * VS + 4 * kg) = hi;
-            }
-        }
-        __syncthreads();
-        if (a.causal && j0 > qw + 31) continue;  // every key here is after every row of this wave
+        const bool more = jt + 1 < ntiles;
+        if (more) issue_tile(j0 + kBc, cur ^ 1);
 
-        // S^T tile: sacc[kb2] covers keys j0 + 32*kb2 .. +31 for query qi.
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            sacc[kb2] = f32x16{};
-            const uint16_t* krow = ks + (32 * kb2 + l32) * KS + 8 * hg;
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * t);
-                sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[t], sacc[kb2], 0, 0, 0);
-            }
-        }
+        if (!(a.causal && j0 > qw + 31)) {  // else every key here is after every row of this wave
+            const uint16_t* ks = smem + cur * L::STAGE;
+            const uint16_t* vs = ks + L::TILE;
 
-        const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
-        if (need_mask) {
+            // S^T tile: register r of sacc[kb2] holds key j0 + 32*kb2 + 16*(r/8) + 8*hg + r%8.
+            // (two independent accumulator chains, interleaved)
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
+                    const bf16x8 kf =
+                        *reinterpret_cast<const bf16x8*>(ks + 32 * kb2 * D + krd[t]);
+                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[t], sacc[kb2], 0, 0, 0);
+                }
+
+            const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
+            if (need_mask) {
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
+                        const bool hide = key >= kv_lim || (a.causal && key > qi);
+                        if (hide) sacc[kb2][r] = -INFINITY;
+                    }
+            }
+
+            // Row max: a tree of 3-input maxima, then the partner half-wave.
+            float m8[8];
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const int kb2 = g >> 2, r = 4 * (g & 3);
+                m8[g] = fmaxf(fmaxf(sacc[kb2][r], sacc[kb2][r + 1]),
+                              fmaxf(sacc[kb2][r + 2], sacc[kb2][r + 3]));
+            }
+            float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                             fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+            mx = fmaxf(mx, swap_half_wave(mx));
+            if (__any(mx > m_run + tau)) {  // wave-uniform: move the reference max
+                const float m_new = fmaxf(m_run, mx);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2((m_run - m_use) * c);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            }
+            const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+
+            // Weights, rounded to bf16; the denominator sums the rounded weights
+            // (v_dot2 with (1, 1)), i.e. exactly the weights multiplied into V.
+            uint32_t pk[2][8];
+            float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
-                    const bool hide = key >= kv_lim || (a.causal && key > qi);
-                    if (hide) sacc[kb2][r] = -INFINITY;
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(fmaf(sacc[kb2][r], c, neg));
+                    const float p1 = fast_exp2(fmaf(sacc[kb2][r + 1], c, neg));
+                    pk[kb2][r >> 1] = pack_bf16x2(p0, p1);
+                    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                    const bf16x2_t pv = __builtin_bit_cast(bf16x2_t, pk[kb2][r >> 1]);
+                    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, ones_bf16x2);
+                    if (r & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps1, false);
+                    else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps0, false);
                 }
-        }
+            l_run += ps0 + ps1;
 
-        float mx = sacc[0][0];
+            // O^T += V^T P^T over four 16-key slices.
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+            for (int kk = 0; kk < 4; ++kk) {
+                const int kb2 = kk >> 1, half = kk & 1;
+                const u32x4 pw = {pk[kb2][4 * half], pk[kb2][4 * half + 1], pk[kb2][4 * half + 2],
+                                  pk[kb2][4 * half + 3]};
+                const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-        mx = fmaxf(mx, swap_half_wave(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2((m_run - m_use) * c);
-        const float neg = -m_use * c;
-        m_run = m_new;
-
-        float psum = 0.f;
-        uint32_t pk[2][8];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(fmaf(sacc[kb2][r], c, neg));
-                const float p1 = fast_exp2(fmaf(sacc[kb2][r + 1], c, neg));
-                psum += p0 + p1;
-                pk[kb2][r >> 1] = pack_bf16x2(p0, p1);
-            }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-
-        // O^T += V^T P^T over four 16-key slices.
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int kb2 = kk >> 1, half = kk & 1;
-            const u32x4 pw = {pk[kb2][4 * half], pk[kb2][4 * half + 1], pk[kb2][4 * half + 2],
-                              pk[kb2][4 * half + 3]};
-            const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                    vt + (32 * db + l32) * VS + 32 * kb2 + 16 * half + 8 * hg);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[db], 0, 0, 0);
+                for (int db = 0; db < D / 32; ++db) {
+                    const uint16_t* vb = vs + 16 * kk * D + vrd[db];
+                    const u32x2 lo = lds_read_tr16x4(vb);
+                    const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
+                    const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[db], 0, 0, 0);
+                }
             }
         }
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile j+1 landed
+        __syncthreads();
+    };
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        step(jt, 0);
+        if (jt + 1 < ntiles) step(jt + 1, 1);
     }
 
     // Epilogue: O = O_acc / l, rounded to bf16.  Register r of d-block db holds
@@ -325,12 +435,16 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
                 }
         }
         // Work in log2-scaled units t = s * scale * log2(e): the row maximum
-        // then gets weight exp2(t - m) = exp2(0) = 1 exactly.  __fmul_rn keeps
-        // the product rounded on its own (no fusion into the later subtraction).
+        // then gets weight exp2(t - m) = exp2(0) = 1 exactly.  Contraction is
+        // off so the product is rounded on its own and never fused into the
+        // later subtraction of m.
+        {
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb2][r] = __fmul_rn(sacc[kb2][r], c);
+                for (int r = 0; r < 16; ++r) sacc[kb2][r] = sacc[kb2][r] * c;
+        }
 
         float mx = sacc[0][0];
 #pragma unroll
@@ -348,6 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+#pragma clang fp contract(off)
                 const float p = fast_exp2(sacc[kb2][r] - m_use);
                 sacc[kb2][r] = p;
                 psum += p;
