@@ -4,19 +4,8 @@
 // K and V of a (batch, K/V head) is read once for all the query heads that
 // share it.
 //
-// Split pass: one workgroup per (batch, K/V head, block of up to 4 query
-// heads of that group, split).  Each wave walks 16-key steps of the split.
-// Scores come from one v_mfma_f32_16x16x32_bf16 per 32 dims: A = the (up to 4)
-// query rows, each repeated 4 times to fill the 16 rows, B = K^T of 16 keys,
-// so every lane receives the scores of all 4 queries for ONE key (lane % 16).
-// Lane quarter l/16 owns a quarter of the head dimension and accumulates
-// p * V for its key over those dims in fp32 on the vector ALU.  Each lane
-// keeps its own running max / sum / output over the keys it saw; the max is
-// moved only when a score exceeds it by more than 2^8 (the ratio O / l is
-// unchanged by a stale max, so this is exact), which removes almost every
-// rescale.  At the end the lane states are merged inside the wave (DPP row
-// reductions) and across the 4 waves (LDS), and the normalised partial output
-// and its natural-log log-sum-exp are written to the workspace.
+// Split pass: see decode_split_bf16_kernel.  Every byte of K and V of a
+// (batch, K/V head) is read once for up to 16 query heads that share it.
 //
 // Merge pass: one thread per (batch, query head, dim) combines the splits:
 // O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M), M = max_s lse_s.
@@ -28,31 +17,53 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = 4;
-constexpr int kQ = 4;          // query heads per workgroup
+constexpr int kQ = 16;         // query heads per workgroup (the 16 MFMA columns)
+constexpr int kStep = 32;      // keys per wave step
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
 
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 1));
-    x = fmaxf(x, __shfl_xor(x, 2));
-    x = fmaxf(x, __shfl_xor(x, 4));
-    x = fmaxf(x, __shfl_xor(x, 8));
-    return x;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x2 lds_read_tr16x4(const uint16_t* p) {
+    lds_i16x4* lp = (lds_i16x4*)((__attribute__((address_space(3))) char*)p);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
-    return x;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, 0);
 }
 
 template <int D>
-__global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(DecodeArgs a) {
-    constexpr int DQ = D / 4;       // dims owned by one lane quarter
-    constexpr int KSTEPS = D / 32;  // MFMA steps per 16-key score tile
-    __shared__ float red_m[kDecWaves][kQ];
-    __shared__ float red_l[kDecWaves][kQ];
-    __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][kQ][D];
+struct DecGeo {
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int RPW = 256 / (2 * D);         // rows per 256-byte bank window
+    static constexpr int STAGE = kStep * D;           // bf16 elements of one V step
+    static constexpr int DMA = STAGE * 2 / 1024;      // 1-KB DMA loads per step
+    static constexpr int KSTEPS = D / 32;             // MFMA contraction steps
+    // V chunk swizzle: the 8 rows x 32 B one 32-lane transposed read touches
+    // fall on 16 distinct 16-byte bank groups.
+    __device__ static int fv(int r) { return 2 * ((r / RPW) % (8 / RPW)); }
+};
+
+// Split pass.  Workgroup = (batch, K/V head, block of <= 16 query heads, split);
+// each wave walks 32-key steps (wave w takes steps w, w+4, ...) with no
+// workgroup barrier until the final merge:
+//   S^T[32 keys x 16 queries] = K Q^T      two v_mfma_f32_16x16x32_bf16 chains
+//   O^T[D x 16 queries]      += V^T P^T    D/16 v_mfma_f32_16x16x32_bf16
+// K goes straight from HBM into the A-operand registers (one step ahead);
+// V goes HBM -> LDS by buffer-load DMA into a per-wave 2-stage ring and comes
+// back transposed with ds_read_b64_tr_b16.  Lane l owns query column l % 16;
+// its 8 scores per step are keys 4*(l/16) + i and 16 + 4*(l/16) + i, which are
+// exactly the 8 contraction slots it feeds to the P.V product.
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_bf16_kernel(DecodeArgs a) {
+    using L = DecGeo<D>;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * 2 * L::STAGE];
 
     const int G = a.Hq / a.Hkv;
     const int nqc = (G + kQ - 1) / kQ;
@@ -71,136 +82,187 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(Decod
     const int chunk = (a.Sk + a.splits - 1) / a.splits;
     const int lo = split * chunk;
     const int hi = min(lo + chunk, len);
-    const int nsteps = hi > lo ? (hi - lo + 15) / 16 : 0;
+    const int nsteps = hi > lo ? (hi - lo + kStep - 1) / kStep : 0;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int kslot = lane & 15;
-    const int quarter = lane >> 4;
+    const int col = lane & 15;   // query column (and key row within a 16-key tile)
+    const int grp = lane >> 4;   // lane group: contraction slots 8*grp .. 8*grp+7
 
-    const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h0) * D;
     const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kvh + DQ * quarter;
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kvh + DQ * quarter;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const uint16_t*>(a.k) + kvh,
+                                                 (uint32_t)a.Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kvh,
+                                                 (uint32_t)a.Sk * D * 2);
 
-    // A operand: row kslot is query head h0 + kslot % 4 (rows repeat every 4);
-    // contraction slot (step t, quarter, element e) <-> dim DQ*quarter + 8t + e.
-    bf16x8 qa[KSTEPS];
+    // Contraction slot (kstep t, group g, element e) <-> dim (D/4)*g + 8t + e, so a
+    // lane's K operand over all ksteps is (D/4) contiguous dims of one key row.
+    bf16x8 qb[L::KSTEPS];
     {
-        const int qh = kslot & 3;
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+            static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h0) * D, (uint32_t)nh * D * 2);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (qh < nh) w = ldg128(qbase + (int64_t)qh * D + DQ * quarter + 8 * t);
-            qa[t] = as_bf16x8(w);
-        }
+        for (int t = 0; t < L::KSTEPS; ++t)
+            qb[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+                qrs, (col * D + (D / 4) * grp + 8 * t) * 2, 0, 0));  // columns >= nh read 0
     }
     const float c = a.scale * kLog2e;
+    const float tau = kTau / c;
 
-    float m_run[kQ], l_run[kQ], o[kQ][DQ];
+    // Per-lane byte offsets (relative to the step's first key).
+    uint32_t koff[2][L::KSTEPS];
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-        m_run[i] = -INFINITY;
-        l_run[i] = 0.f;
+    for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-        for (int d = 0; d < DQ; ++d) o[i][d] = 0.f;
+        for (int t = 0; t < L::KSTEPS; ++t)
+            koff[tile][t] = ((16 * tile + col) * D + (D / 4) * grp + 8 * t) * 2;
+    uint32_t voff[L::DMA];
+#pragma unroll
+    for (int i = 0; i < L::DMA; ++i) {
+        const int p = 64 * i + lane, row = p / L::CPR, pc = p % L::CPR;
+        voff[i] = row * D * 2 + (pc ^ L::fv(row)) * 16;
+    }
+    // Transposed V read: lane j of group grp points at row k0 + j/4, dims d0 + 4*(j%4),
+    // k0 = 4*grp (+16), d0 = 16*dt; it receives V[k0..k0+3][d0 + col].
+    const int tr_row = 4 * grp + (col >> 2);
+    int vrd[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int e = 16 * dt + 4 * (col & 3);
+        vrd[dt] = tr_row * D + (((e >> 3) ^ L::fv(tr_row)) * 8) + (e & 7);
     }
 
-    for (int st = wave; st < nsteps; st += kDecWaves) {
-        const int key = lo + 16 * st + kslot;
-        const bool valid = key < hi;
-        u32x4 kw[KSTEPS], vw[DQ / 8];
+    uint16_t* ring = smem + wave * 2 * L::STAGE;
+    auto issue = [&](int st, int stage, u32x4 (&kr)[2][L::KSTEPS]) {
+        const uint32_t base = (uint32_t)(lo + kStep * st) * D * 2;
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            kw[t] = u32x4{0u, 0u, 0u, 0u};
-            if (valid) kw[t] = ldg128(kp + (int64_t)key * D + 8 * t);
-        }
+        for (int i = 0; i < L::DMA; ++i) dma16(vrs, ring + stage * L::STAGE + 512 * i, base + voff[i]);
 #pragma unroll
-        for (int e = 0; e < DQ / 8; ++e) {
-            vw[e] = u32x4{0u, 0u, 0u, 0u};
-            if (valid) vw[e] = ldg128(vp + (int64_t)key * D + 8 * e);
-        }
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], as_bf16x8(kw[t]), sacc, 0, 0, 0);
+            for (int t = 0; t < L::KSTEPS; ++t)
+                kr[tile][t] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + koff[tile][t], 0, 0);
+    };
 
-        float p[kQ];
+    f32x4 oacc[D / 16];
 #pragma unroll
-        for (int i = 0; i < kQ; ++i) {
-            const float s = sacc[i] * c;  // log2-scaled score of query i for this key
-            if (valid && s > m_run[i] + kTau) {
-                const float alpha = fast_exp2(m_run[i] - s);
-                m_run[i] = s;
-                l_run[i] *= alpha;
+    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    u32x4 kcur[2][L::KSTEPS], knext[2][L::KSTEPS];
+    if (wave < nsteps) issue(wave, 0, kcur);
+    int n = 0;
+    for (int st = wave; st < nsteps; st += kDecWaves, ++n) {
+        const int stage = n & 1;
+        const bool more = st + kDecWaves < nsteps;
+        if (more) issue(st + kDecWaves, stage ^ 1, knext);
+        // Everything but the loads just issued for the next step has landed.
+        if (more)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::DMA + 2 * L::KSTEPS) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+        const int k0 = lo + kStep * st;
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int d = 0; d < DQ; ++d) o[i][d] *= alpha;
-            }
-            p[i] = valid ? fast_exp2(s - m_run[i]) : 0.f;
-            l_run[i] += p[i];
+        for (int t = 0; t < L::KSTEPS; ++t)
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile)
+                sacc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[tile][t]), qb[t],
+                                                                     sacc[tile], 0, 0, 0);
+        if (k0 + kStep > hi) {
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + 16 * tile + 4 * grp + i >= hi) sacc[tile][i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // all four lanes of a column agree
+        if (__any(mx > m_run + tau)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2((m_run - m_use) * c);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+        }
+        const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+        uint32_t pk[4];
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2)
+                pk[2 * tile + (i >> 1)] = pack_bf16x2(fast_exp2(fmaf(sacc[tile][i], c, neg)),
+                                                      fast_exp2(fmaf(sacc[tile][i + 1], c, neg)));
+        {
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+            float ps = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[w]), one, ps, false);
+            l_run += ps;
+        }
+        const bf16x8 pb = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const uint16_t* vs = ring + stage * L::STAGE;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const u32x2 lo4 = lds_read_tr16x4(vs + vrd[dt]);
+            const u32x2 hi4 = lds_read_tr16x4(vs + vrd[dt] + 16 * D);
+            const bf16x8 vf = as_bf16x8(u32x4{lo4[0], lo4[1], hi4[0], hi4[1]});
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[dt], 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < DQ / 8; ++e)
+        for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float v0 = bf16_lo_to_f32(vw[e][w]);
-                const float v1 = bf16_hi_to_f32(vw[e][w]);
-#pragma unroll
-                for (int i = 0; i < kQ; ++i) {
-                    o[i][8 * e + 2 * w] = fmaf(p[i], v0, o[i][8 * e + 2 * w]);
-                    o[i][8 * e + 2 * w + 1] = fmaf(p[i], v1, o[i][8 * e + 2 * w + 1]);
-                }
-            }
+            for (int t = 0; t < L::KSTEPS; ++t) kcur[tile][t] = knext[tile][t];
     }
 
-    // Merge the 16 key slots of this wave (lanes of one 16-lane row).
+    // Column totals: the denominator is spread over the 4 lane groups.
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    // Merge the 4 waves through LDS (the ring is free now).
+    __syncthreads();
+    float* red_o = reinterpret_cast<float*>(smem);              // [wave][q][D]
+    float* red_m = red_o + kDecWaves * kQ * D;                  // [wave][q]
+    float* red_l = red_m + kDecWaves * kQ;                      // [wave][q]
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-        const float M = row16_max(m_run[i]);
-        const float w = (m_run[i] == -INFINITY) ? 0.f : fast_exp2(m_run[i] - M);
-        l_run[i] = row16_sum(l_run[i] * w);
+    for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-        for (int d = 0; d < DQ; ++d) o[i][d] = row16_sum(o[i][d] * w);
-        m_run[i] = M;
-    }
-    if (kslot == 0) {
-#pragma unroll
-        for (int i = 0; i < kQ; ++i) {
-#pragma unroll
-            for (int d = 0; d < DQ; d += 4)
-                *reinterpret_cast<f32x4*>(&red_o[wave][i][DQ * quarter + d]) =
-                    f32x4{o[i][d], o[i][d + 1], o[i][d + 2], o[i][d + 3]};
-            if (quarter == 0) {
-                red_m[wave][i] = m_run[i];
-                red_l[wave][i] = l_run[i];
-            }
-        }
+        for (int i = 0; i < 4; ++i)  // O^T register i of tile dt: dim 16*dt + 4*grp + i, column col
+            red_o[(wave * kQ + col) * D + 16 * dt + 4 * grp + i] = oacc[dt][i];
+    if (grp == 0) {
+        red_m[wave * kQ + col] = m_run;
+        red_l[wave * kQ + col] = l_run;
     }
     __syncthreads();
-
-    // Merge the 4 waves and write the normalised partial and its lse.
-    for (int e = tid; e < kQ * D; e += kDecThreads) {
-        const int i = e / D, d = e % D;
-        if (i >= nh) continue;
+    for (int e = tid; e < nh * D; e += kDecThreads) {
+        const int q = e / D, d = e % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int wv = 0; wv < kDecWaves; ++wv) M = fmaxf(M, red_m[wv][i]);
-        const int64_t prow = ((int64_t)b * a.Hq + h0 + i) * a.splits + split;
+        for (int wv = 0; wv < kDecWaves; ++wv) M = fmaxf(M, red_m[wv * kQ + q]);
+        const int64_t prow = ((int64_t)b * a.Hq + h0 + q) * a.splits + split;
         if (M == -INFINITY) {  // no visible key in this split
             a.o_part[prow * D + d] = 0.f;
             if (d == 0) a.lse_part[prow] = -INFINITY;
             continue;
         }
-        float L = 0.f, acc = 0.f;
+        float Ls = 0.f, acc = 0.f;
 #pragma unroll
         for (int wv = 0; wv < kDecWaves; ++wv) {
-            const float w = (red_m[wv][i] == -INFINITY) ? 0.f : fast_exp2(red_m[wv][i] - M);
-            L = fmaf(w, red_l[wv][i], L);
-            acc = fmaf(w, red_o[wv][i][d], acc);
+            const float mw = red_m[wv * kQ + q];
+            const float w = (mw == -INFINITY) ? 0.f : fast_exp2((mw - M) * c);
+            Ls = fmaf(w, red_l[wv * kQ + q], Ls);
+            acc = fmaf(w, red_o[(wv * kQ + q) * D + d], acc);
         }
-        a.o_part[prow * D + d] = acc / L;
-        if (d == 0) a.lse_part[prow] = (M + __log2f(L)) * kLn2;
+        a.o_part[prow * D + d] = acc / Ls;
+        if (d == 0) a.lse_part[prow] = M * a.scale + __logf(Ls);
     }
 }
 

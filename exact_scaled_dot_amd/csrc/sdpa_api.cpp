@@ -76,6 +76,9 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
     if (B > INT_MAX || Hq > INT_MAX || Sq > INT_MAX || Sk > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
+    // Per-head rows are addressed through buffer resources with 32-bit extents.
+    if (Sq * D * es > INT_MAX || Sk * D * es > INT_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "one head of q, k or v exceeds 2 GiB");
     if (D != 64 && D != 128)
         return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
     return SDPA_OK;

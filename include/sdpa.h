@@ -22,7 +22,8 @@
  *    log-sum-exp) are fp32; the output is rounded to the input type (round to
  *    nearest even), as the ruDNN guide's normalisation ops do (section 7).
  *    On the bf16 path the softmax weights are rounded to bf16 before the
- *    product with V; scores, statistics and Q are never rounded.
+ *    product with V, and the running denominator is the fp32 sum of those
+ *    same rounded weights; scores, the running max and Q are never rounded.
  *  - Pointers: every tensor pointer (q, k, v, out, key_lens, workspace) is a
  *    DEVICE pointer on the current HIP device, owned by the caller.  The
  *    library allocates nothing and keeps no per-call state.
@@ -89,7 +90,8 @@ enum {
  *   out      device [B, Hq, Sq, D], dtype; written completely
  *   dtype    SDPA_BF16 or SDPA_F32
  *   stream   hipStream_t as void*
- * Supported head dims: D in {64, 128} (SDPA_ERR_UNSUPPORTED otherwise).
+ * Supported head dims: D in {64, 128}; one head (Sq*D or Sk*D elements) must
+ * be under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
  */
 sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,

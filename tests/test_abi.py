@@ -72,6 +72,8 @@ def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, sca
     (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(Sq=1 << 33, Sk=1 << 33, B=1, Hq=1, Hkv=1, D=64, out=ctypes.c_void_p(1 << 46)),
      sd.SDPA_ERR_UNSUPPORTED, "32-bit"),
+    (dict(Sq=1, Sk=1 << 24, B=1, Hq=1, Hkv=1, D=64, out=ctypes.c_void_p(1 << 46)),
+     sd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
 ])
 def test_forward_rejects(kw, status, needle):
     assert fwd(**kw) == status

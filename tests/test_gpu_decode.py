@@ -37,7 +37,10 @@ def run_decode(B, Hq, Hkv, Sk, D, splits, lens=None, seed=0, check_partials=True
         empty = np.isneginf(rlp)
         assert np.array_equal(np.isneginf(lp), empty), what + ": empty-split pattern differs"
         assert (op[empty] == 0).all()
-        assert np.abs(lp[~empty] - rlp[~empty]).max() <= 1e-3, what + ": lse"
+        # l is the fp32 sum of the bf16-rounded weights (the weights multiplied
+        # into V); rounding each weight to nearest bf16 moves it by at most
+        # 2^-9 of itself, so |ln l - ln l_exact| <= 2^-9 ~ 1.95e-3 (+ fp32 noise).
+        assert np.abs(lp[~empty] - rlp[~empty]).max() <= 2.5e-3, what + ": lse"
         # P is rounded to bf16 before P.V, so partial outputs meet the bf16 bars.
         compare(op[~empty], rop[~empty], torch.bfloat16, what + ": partial outputs")
     return res
