@@ -267,9 +267,13 @@ def main():
                                       "traffic": stored_traffic("decode_split", "decode.hip"),
                                       "kernel": "decode_split_bf16_kernel<128> + merge",
                                       "bytes_per_launch": by}}
-    if "value" not in rec:
-        rec.update({"value": rec["decode"]["value"], "unit": "GB/s"})
-        rec["config"] = {"workload": wd.name}
+    if "value" not in rec:  # --only padded / --only decode: report that call
+        if "decode" in rec:
+            rec.update({"value": rec["decode"]["value"], "unit": "GB/s"})
+            rec["config"] = {"workload": wd.name}
+        else:
+            rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": wg.name}
 
     del ip, ig, idd
     torch.cuda.empty_cache()

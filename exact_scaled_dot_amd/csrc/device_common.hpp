@@ -57,4 +57,20 @@ __device__ __forceinline__ float swap_half_wave(float x) {
     return __shfl_xor(x, 32);
 }
 
+// max(x[l], x[l^32]) in every lane, without the LDS: v_permlane32_swap on two
+// copies of x yields (x_lo, x_lo) and (x_hi, x_hi).
+__device__ __forceinline__ float max_half_waves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                   __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// Three-input maximum as one v_max3_f32 (the inputs are MFMA results or -inf,
+// so the NaN canonicalisation the compiler adds around fmaxf is not needed).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 }  // namespace sdpa

@@ -238,16 +238,19 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
             const uint16_t* vs = ks + L::TILE;
 
             // S^T tile: register r of sacc[kb2] holds key j0 + 32*kb2 + 16*(r/8) + 8*hg + r%8.
-            // (two independent accumulator chains, interleaved)
+            // (all K fragments read first; two independent accumulator chains)
+            bf16x8 kf[2][D / 16];
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+                    kf[kb2][t] = *reinterpret_cast<const bf16x8*>(ks + 32 * kb2 * D + krd[t]);
             f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2) {
-                    const bf16x8 kf =
-                        *reinterpret_cast<const bf16x8*>(ks + 32 * kb2 * D + krd[t]);
-                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[t], sacc[kb2], 0, 0, 0);
-                }
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb2][t], qr[t], sacc[kb2], 0, 0, 0);
 
             const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
             if (need_mask) {
@@ -261,17 +264,17 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
                     }
             }
 
-            // Row max: a tree of 3-input maxima, then the partner half-wave.
-            float m8[8];
+            // Row max: a tree of 3-input maxima (32 -> 11 -> 4 -> 1), then the
+            // partner half-wave.
+            const float* sv = reinterpret_cast<const float*>(sacc);
+            float m11[11];
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                const int kb2 = g >> 2, r = 4 * (g & 3);
-                m8[g] = fmaxf(fmaxf(sacc[kb2][r], sacc[kb2][r + 1]),
-                              fmaxf(sacc[kb2][r + 2], sacc[kb2][r + 3]));
-            }
-            float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                             fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-            mx = fmaxf(mx, swap_half_wave(mx));
+            for (int g = 0; g < 10; ++g) m11[g] = max3f(sv[3 * g], sv[3 * g + 1], sv[3 * g + 2]);
+            m11[10] = fmaxf(sv[30], sv[31]);
+            const float m4a = max3f(m11[0], m11[1], m11[2]), m4b = max3f(m11[3], m11[4], m11[5]);
+            const float m4c = max3f(m11[6], m11[7], m11[8]), m4d = fmaxf(m11[9], m11[10]);
+            float mx = max3f(m4a, m4b, fmaxf(m4c, m4d));
+            mx = max_half_waves(mx);
             if (__any(mx > m_run + tau)) {  // wave-uniform: move the reference max
                 const float m_new = fmaxf(m_run, mx);
                 const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
