@@ -44,22 +44,33 @@ struct TileInfo {
 // Workgroup -> (batch, head, query block).  Workgroups are dealt to the 8
 // XCDs round-robin (id % 8), and each XCD has its own L2, so the id is first
 // turned into a position in a logical order in which every XCD owns one
-// contiguous run.  The logical order walks K/V heads outermost, then query
-// blocks (longest first under a causal mask, so short blocks fill the tail),
-// then the Hq/Hkv query heads that share the K/V head: the workgroups an XCD
-// runs at the same time read the same K/V rows, and every K/V head is
-// fetched into one L2 only.
+// contiguous run.  The logical order walks K/V heads ("units") outermost and
+// the Hq/Hkv query heads that share a K/V head innermost, so the workgroups
+// an XCD runs together read the same K/V rows and every K/V head is fetched
+// into one L2.  Under a causal mask the work of a query block grows with its
+// index; there the units go in pairs and, inside a pair, query blocks run
+// longest first across both units (a longest-first list schedule, which
+// keeps the XCD's last workgroups short).
 __device__ __forceinline__ TileInfo decode_tile(const ForwardArgs& a) {
     const int nqb = (a.Sq + kBr - 1) / kBr;
     const int G = a.Hq / a.Hkv;
-    const int T = a.B * a.Hq * nqb;
+    const int units = a.B * a.Hkv;
+    const int T = units * G * nqb;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     const int nx = T >> 3, rem = T & 7;
     int t = xcd * nx + min(xcd, rem) + local;
     const int hsub = t % G;
     t /= G;
-    const int qord = t % nqb;
-    const int unit = t / nqb;
+    int unit, qord;
+    if (a.causal && (units & 1) == 0) {
+        const int pair_member = t & 1;
+        t >>= 1;
+        qord = t % nqb;
+        unit = 2 * (t / nqb) + pair_member;
+    } else {
+        qord = t % nqb;
+        unit = t / nqb;
+    }
     TileInfo ti;
     ti.b = unit / a.Hkv;
     ti.gk = unit % a.Hkv;
@@ -83,8 +94,9 @@ __device__ __forceinline__ void key_extent(const ForwardArgs& a, int b, int q0, 
 // Tiles reach LDS by buffer-load DMA (buffer_load_dwordx4 ... lds): each
 // instruction writes 64 lanes x 16 B = 1 KB contiguously, loads past the
 // buffer's num_records return zeros (keys >= Sk need no branch), and no VGPR
-// holds the in-flight tile.  The loads of tile j+1 are issued before tile j is
-// computed, into the other of two LDS stages; one barrier per tile.
+// holds the in-flight tile.  K and V have two LDS stages each and K runs one
+// tile ahead: while tile j's weights are formed on the VALU, tile j+1's
+// scores run on the MFMA unit; one barrier per tile.
 //
 // LDS rows are unpadded, so 16-byte chunks are XOR-swizzled instead:
 //   K: chunk c of LDS row r sits at c ^ fk(r), fk(r) = (r / RPW) % (16 / RPW);
@@ -135,7 +147,9 @@ struct Bf16Geo {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a) {
     using L = Bf16Geo<D>;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * L::STAGE];
+    // Two K stages then two V stages.  K runs one tile ahead of V: while the
+    // weights of tile j are formed, the scores of tile j+1 are computed.
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -155,6 +169,9 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     int kv_lim, kv_end;
     key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
     const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
+    // Under a causal mask a wave stops taking part once a tile starts past
+    // its last row (and never resumes: tiles only move forward).
+    const int wave_tiles = a.causal ? min(ntiles, (qw + 31) / kBc + 1) : ntiles;
 
     // Q fragment for the B operand of S^T = K Q^T: lane holds Q[qi][16t + 8hg .. +7]
     // (rows >= Sq read as zeros).
@@ -169,8 +186,8 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     }
 
     // DMA source offsets (bytes, relative to the tile's first key).  DMA load i
-    // of this wave fills LDS bytes [1024*(DMA*wave + i), +1024); lane l's 16 B
-    // land at 16-byte slot p = 64*(DMA*wave + i) + l = (row, physical chunk).
+    // of this wave fills LDS bytes [1024*(DMA*wave + i), +1024) of a tile;
+    // lane l's 16 B land at 16-byte slot p = 64*(DMA*wave + i) + l.
     uint32_t koff[L::DMA], voff[L::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
@@ -179,18 +196,18 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
         koff[i] = k_lds_row(row) * D * 2 + ((pc ^ L::fk(row)) * 16);
         voff[i] = row * D * 2 + ((pc ^ L::fv(row)) * 16);
     }
-    auto issue_tile = [&](int j0, int stage) {
-        // Resources start at the tile's first key; num_records ends at key Sk.
-        const uint32_t left = (uint32_t)(a.Sk - j0) * D * 2;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp + (int64_t)j0 * D, left);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp + (int64_t)j0 * D, left);
-        uint16_t* ks = smem + stage * L::STAGE;
-        uint16_t* vs = ks + L::TILE;
+    // Resources start at the tile's first key; num_records ends at key Sk.
+    auto issue_k = [&](int j0, int stage) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(kp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
+        uint16_t* dst = smem + stage * L::TILE + 512 * L::DMA * wave;
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) {
-            dma16(krs, ks + 512 * (L::DMA * wave + i), koff[i]);
-            dma16(vrs, vs + 512 * (L::DMA * wave + i), voff[i]);
-        }
+        for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, koff[i]);
+    };
+    auto issue_v = [&](int j0, int stage) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(vp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
+        uint16_t* dst = smem + (2 + stage) * L::TILE + 512 * L::DMA * wave;
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
     };
 
     // Lane-constant LDS read offsets (bf16 elements).
@@ -218,117 +235,152 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     // The reference max moves only when a row's tile max exceeds it by more
     // than 8 in log2 units; weights then stay <= 2^8 and O / l is unchanged.
     const float tau = 8.0f / c;
-    const uint32_t ones_bf16x2 = 0x3f803f80u;
 
-    if (ntiles > 0) issue_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // S^T tile of the K stage at ks: register r of s[kb2] holds key
+    // 32*kb2 + 16*(r/8) + 8*hg + r%8 of the tile.
+    auto scores = [&](const uint16_t* ks, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+        // K fragments are read two k-steps ahead of the MFMAs that use them.
+        constexpr int T = D / 16;
+        bf16x8 kf[3][2];
+        auto rd = [&](int t, int slot) __attribute__((always_inline)) {
+            kf[slot][0] = *reinterpret_cast<const bf16x8*>(ks + krd[t]);
+            kf[slot][1] = *reinterpret_cast<const bf16x8*>(ks + 32 * D + krd[t]);
+        };
+        rd(0, 0);
+        rd(1, 1);
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (t + 2 < T) rd(t + 2, (t + 2) % 3);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3][kb2], qr[t], sacc[kb2], 0, 0, 0);
+        }
+        // Keep the read-ahead: 4 reads, then (2 MFMAs, 2 reads) per k-step.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+            if (t + 2 < T) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+    };
 
-    // One tile: issue the DMA of the next tile into the other stage, compute
-    // this one.  Both calls below pass a literal stage, so after inlining
-    // every LDS read of the tile carries its stage base as an instruction
-    // offset.
-    auto step = [&](int jt, const int cur) __attribute__((always_inline)) {
-        const int j0 = jt * kBc;
-        const bool more = jt + 1 < ntiles;
-        if (more) issue_tile(j0 + kBc, cur ^ 1);
-
-        if (!(a.causal && j0 > qw + 31)) {  // else every key here is after every row of this wave
-            const uint16_t* ks = smem + cur * L::STAGE;
-            const uint16_t* vs = ks + L::TILE;
-
-            // S^T tile: register r of sacc[kb2] holds key j0 + 32*kb2 + 16*(r/8) + 8*hg + r%8.
-            // (all K fragments read first; two independent accumulator chains)
-            bf16x8 kf[2][D / 16];
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-                    kf[kb2][t] = *reinterpret_cast<const bf16x8*>(ks + 32 * kb2 * D + krd[t]);
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb2][t], qr[t], sacc[kb2], 0, 0, 0);
-
-            const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
-            if (need_mask) {
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
-                        const bool hide = key >= kv_lim || (a.causal && key > qi);
-                        if (hide) sacc[kb2][r] = -INFINITY;
-                    }
-            }
-
-            // Row max: a tree of 3-input maxima (32 -> 11 -> 4 -> 1), then the
-            // partner half-wave.
-            const float* sv = reinterpret_cast<const float*>(sacc);
-            float m11[11];
-#pragma unroll
-            for (int g = 0; g < 10; ++g) m11[g] = max3f(sv[3 * g], sv[3 * g + 1], sv[3 * g + 2]);
-            m11[10] = fmaxf(sv[30], sv[31]);
-            const float m4a = max3f(m11[0], m11[1], m11[2]), m4b = max3f(m11[3], m11[4], m11[5]);
-            const float m4c = max3f(m11[6], m11[7], m11[8]), m4d = fmaxf(m11[9], m11[10]);
-            float mx = max3f(m4a, m4b, fmaxf(m4c, m4d));
-            mx = max_half_waves(mx);
-            if (__any(mx > m_run + tau)) {  // wave-uniform: move the reference max
-                const float m_new = fmaxf(m_run, mx);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = fast_exp2((m_run - m_use) * c);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-            }
-            const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-
-            // Weights, rounded to bf16; the denominator sums the rounded weights
-            // (v_dot2 with (1, 1)), i.e. exactly the weights multiplied into V.
-            uint32_t pk[2][8];
-            float ps0 = 0.f, ps1 = 0.f;
+    // Hide keys of tile j0 that a row may not see (causal / key limit).
+    auto mask_tile = [&](int j0, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+        const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
+        if (need_mask) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(fmaf(sacc[kb2][r], c, neg));
-                    const float p1 = fast_exp2(fmaf(sacc[kb2][r + 1], c, neg));
-                    pk[kb2][r >> 1] = pack_bf16x2(p0, p1);
-                    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-                    const bf16x2_t pv = __builtin_bit_cast(bf16x2_t, pk[kb2][r >> 1]);
-                    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, ones_bf16x2);
-                    if (r & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps1, false);
-                    else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps0, false);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
+                    const bool hide = key >= kv_lim || (a.causal && key > qi);
+                    if (hide) sacc[kb2][r] = -INFINITY;
                 }
-            l_run += ps0 + ps1;
+        }
+    };
+    // Row max of a (masked) score tile; moves the reference max when needed.
+    auto update_max = [&](const f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+        // A tree of 3-input maxima (32 -> 11 -> 4 -> 1), then the partner half-wave.
+        const float* sv = reinterpret_cast<const float*>(sacc);
+        float m11[11];
+#pragma unroll
+        for (int g = 0; g < 10; ++g) m11[g] = max3f(sv[3 * g], sv[3 * g + 1], sv[3 * g + 2]);
+        m11[10] = fmaxf(sv[30], sv[31]);
+        const float m4a = max3f(m11[0], m11[1], m11[2]), m4b = max3f(m11[3], m11[4], m11[5]);
+        const float m4c = max3f(m11[6], m11[7], m11[8]), m4d = fmaxf(m11[9], m11[10]);
+        float mx = max3f(m4a, m4b, fmaxf(m4c, m4d));
+        mx = max_half_waves(mx);
+        if (__any(mx > m_run + tau)) {  // wave-uniform: move the reference max
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2((m_run - m_use) * c);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        }
+    };
+    // bf16 weights of a score tile against the reference max; the denominator
+    // sums the rounded weights (v_dot2 with (1, 1)), i.e. exactly the weights
+    // multiplied into V.  Straight-line code.
+    auto weights = [&](const f32x16 (&sacc)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+        const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(sacc[kb2][r], c, neg));
+                const float p1 = fast_exp2(fmaf(sacc[kb2][r + 1], c, neg));
+                pk[kb2][r >> 1] = pack_bf16x2(p0, p1);
+                const bf16x2_t pv = __builtin_bit_cast(bf16x2_t, pk[kb2][r >> 1]);
+                if (r & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps1, false);
+                else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps0, false);
+            }
+        l_run += ps0 + ps1;
+    };
 
-            // O^T += V^T P^T over four 16-key slices.
+    // O^T += V^T P^T over the four 16-key slices of the V stage at vs.
+    auto accumulate = [&](const uint16_t* vs, const uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int kb2 = kk >> 1, half = kk & 1;
-                const u32x4 pw = {pk[kb2][4 * half], pk[kb2][4 * half + 1], pk[kb2][4 * half + 2],
-                                  pk[kb2][4 * half + 3]};
-                const bf16x8 pb = as_bf16x8(pw);
+        for (int kk = 0; kk < 4; ++kk) {
+            const int kb2 = kk >> 1, half = kk & 1;
+            const u32x4 pw = {pk[kb2][4 * half], pk[kb2][4 * half + 1], pk[kb2][4 * half + 2],
+                              pk[kb2][4 * half + 3]};
+            const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const uint16_t* vb = vs + 16 * kk * D + vrd[db];
-                    const u32x2 lo = lds_read_tr16x4(vb);
-                    const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
-                    const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[db], 0, 0, 0);
-                }
+            for (int db = 0; db < D / 32; ++db) {
+                const uint16_t* vb = vs + 16 * kk * D + vrd[db];
+                const u32x2 lo = lds_read_tr16x4(vb);
+                const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
+                const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[db], 0, 0, 0);
             }
         }
+    };
 
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile j+1 landed
+    // Prologue: K(0), V(0), K(1) resident; scores of tile 0.
+    if (ntiles > 0) {
+        issue_k(0, 0);
+        issue_v(0, 0);
+    }
+    if (ntiles > 1) issue_k(kBc, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 sA[2], sB[2];
+    if (wave_tiles > 0) {
+        scores(smem, sA);
+        mask_tile(0, sA);
+    }
+    __syncthreads();  // K stage 0 is refilled with K(2) by the first step
+
+    // Tile jt: K(jt+1) sits in K stage cur^1, V(jt) in V stage cur.  Issue
+    // K(jt+2) into K stage cur and V(jt+1) into V stage cur^1, compute the
+    // scores of tile jt+1 next to the weights of tile jt, then P V.  Both
+    // calls below pass literal stages, so after inlining every LDS read
+    // carries its stage base as an instruction offset and the two score
+    // tiles swap roles without copies.
+    auto step = [&](int jt, const int cur, f32x16 (&scur)[2], f32x16 (&snext)[2]) __attribute__((always_inline)) {
+        if (jt + 2 < ntiles) issue_k((jt + 2) * kBc, cur);
+        if (jt + 1 < ntiles) issue_v((jt + 1) * kBc, cur ^ 1);
+        if (jt < wave_tiles) {
+            uint32_t pk[2][8];
+            if (jt + 1 < wave_tiles) scores(smem + (cur ^ 1) * L::TILE, snext);
+            update_max(scur);
+            weights(scur, pk);
+            accumulate(smem + (2 + cur) * L::TILE, pk);
+            if (jt + 1 < wave_tiles) mask_tile((jt + 1) * kBc, snext);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA landed
         __syncthreads();
     };
     for (int jt = 0; jt < ntiles; jt += 2) {
-        step(jt, 0);
-        if (jt + 1 < ntiles) step(jt + 1, 1);
+        step(jt, 0, sA, sB);
+        if (jt + 1 < ntiles) step(jt + 1, 1, sB, sA);
     }
 
     // Epilogue: O = O_acc / l, rounded to bf16.  Register r of d-block db holds
