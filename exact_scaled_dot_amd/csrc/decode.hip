@@ -1,14 +1,22 @@
 // Single-query decode with split-KV and a log-sum-exp merge (ruDNN user guide,
 // section 9: the history is split into 2..=32 pieces whose partial statistics
 // and merge are kept in FP32).  The split pass is memory bound: every byte of
-// K and V of a (batch, K/V head) is read once for all the query heads that
+// K and V of a (batch, K/V head) is read once for up to 16 query heads that
 // share it.
 //
-// Split pass: see decode_split_bf16_kernel.  Every byte of K and V of a
-// (batch, K/V head) is read once for up to 16 query heads that share it.
+// Split pass: a persistent grid, one workgroup of 4 independent waves per
+// compute unit.  A work item is (batch, K/V head, block of <= 16 query heads,
+// split).  A workgroup owns a contiguous run of items and its waves take them
+// in turn (wave w: items w, w+4, ...), so at any time the 4 waves stream 4
+// neighbouring splits of one head.  A wave computes each of its items whole
+// and writes its normalised partial output and log-sum-exp; its K/V loads
+// form one stream across items, so the prefetch never drains at a split
+// boundary.  K and V are loaded non-temporally: each byte is read once.
 //
-// Merge pass: one thread per (batch, query head, dim) combines the splits:
-// O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M), M = max_s lse_s.
+// Merge pass: O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M), with
+// M = max_s lse_s, one thread per (batch, query head, 4 dims).
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -17,17 +25,54 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = 4;
-constexpr int kQ = 16;         // query heads per workgroup (the 16 MFMA columns)
-constexpr int kStep = 32;      // keys per wave step
-constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
+constexpr int kQ = 16;              // query heads per item (the 16 MFMA columns)
+constexpr int kStep = 16;           // keys per step
+constexpr float kTau = 8.0f;        // lazy-rescale threshold, log2 units
+constexpr int kRingBytes = 32768;   // LDS ring per wave
+constexpr int kNonTemporal = 2;     // buffer-load cache policy: nt (streamed once)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-__device__ __forceinline__ u32x2 lds_read_tr16x4(const uint16_t* p) {
+// Transposed read of 4 bf16.  The __restrict__ parameter gives the inlined load
+// its own alias scope, which keeps the compiler from putting a vmcnt(0) drain
+// of the in-flight LDS-DMA writes in front of it (those are ordered by the
+// explicit waits instead).
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     lds_i16x4* lp = (lds_i16x4*)((__attribute__((address_space(3))) char*)p);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+__device__ __forceinline__ u32x4 lds_read128(const uint16_t* __restrict__ p) {
+    return *(lds_u32x4*)((__attribute__((address_space(3))) char*)p);
+}
+// fp32x4 LDS store / load of the cross-wave merge (same alias-scope reason).
+__device__ __forceinline__ void lds_store_f32x4(float* __restrict__ p, f32x4 v) {
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    *(lds_f32x4*)((__attribute__((address_space(3))) char*)p) = v;
+}
+__device__ __forceinline__ f32x4 lds_load_f32x4(const float* __restrict__ p) {
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    return *(lds_f32x4*)((__attribute__((address_space(3))) char*)p);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(T* __restrict__ p, T v) {
+    *(__attribute__((address_space(3))) T*)((__attribute__((address_space(3))) char*)p) = v;
+}
+template <typename T>
+__device__ __forceinline__ T lds_load(const T* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) T*)((const __attribute__((address_space(3))) char*)p);
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then s_barrier.  (__syncthreads() also waits for every outstanding global
+// access, which would drain the K/V loads in flight.)  The memory clobbers keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -35,269 +80,346 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, 0);
+        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, kNonTemporal);
 }
 
 template <int D>
 struct DecGeo {
-    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    static constexpr int RPW = 256 / (2 * D);         // rows per 256-byte bank window
-    static constexpr int STAGE = kStep * D;           // bf16 elements of one V step
-    static constexpr int DMA = STAGE * 2 / 1024;      // 1-KB DMA loads per step
-    static constexpr int KSTEPS = D / 32;             // MFMA contraction steps
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int RPW = 256 / (2 * D);          // rows per 256-byte bank window
+    static constexpr int TILE = kStep * D;             // bf16 elements of one K or V step
+    static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
+    static constexpr int NS = kRingBytes / (2 * STAGE);  // ring stages per wave
+    static constexpr int DMA = TILE * 2 / 1024;        // 1-KB DMA loads per tile
+    static constexpr int OPS = 2 * DMA;                // vector memory ops per step
+    static constexpr int KSTEPS = D / 32;              // MFMA contraction steps of S
+    // K chunk swizzle: the 16 rows one 16-lane ds_read_b128 touches (same
+    // logical chunk) land on 16 distinct 16-byte bank groups.
+    __device__ static int fk(int r) { return (r / RPW) % CPR; }
     // V chunk swizzle: the 8 rows x 32 B one 32-lane transposed read touches
     // fall on 16 distinct 16-byte bank groups.
     __device__ static int fv(int r) { return 2 * ((r / RPW) % (8 / RPW)); }
 };
+static_assert(DecGeo<128>::NS == 4 && DecGeo<64>::NS == 8, "ring depth");
 
-// Split pass.  Workgroup = (batch, K/V head, block of <= 16 query heads, split);
-// each wave walks 32-key steps (wave w takes steps w, w+4, ...) with no
-// workgroup barrier until the final merge:
-//   S^T[32 keys x 16 queries] = K Q^T      two v_mfma_f32_16x16x32_bf16 chains
-//   O^T[D x 16 queries]      += V^T P^T    D/16 v_mfma_f32_16x16x32_bf16
-// K goes straight from HBM into the A-operand registers (one step ahead);
-// V goes HBM -> LDS by buffer-load DMA into a per-wave 2-stage ring and comes
-// back transposed with ds_read_b64_tr_b16.  Lane l owns query column l % 16;
-// its 8 scores per step are keys 4*(l/16) + i and 16 + 4*(l/16) + i, which are
-// exactly the 8 contraction slots it feeds to the P.V product.
-template <int D>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_split_bf16_kernel(DecodeArgs a) {
-    using L = DecGeo<D>;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * 2 * L::STAGE];
+// Geometry of one work item.
+struct Item {
+    int b, h0, nh, split, lo, hi, nst;
+    int64_t kvh;  // element offset of the item's K/V head
+};
 
-    const int G = a.Hq / a.Hkv;
-    const int nqc = (G + kQ - 1) / kQ;
-    int idx = blockIdx.x;
-    const int split = idx % a.splits;
-    idx /= a.splits;
-    const int qc = idx % nqc;
-    idx /= nqc;
-    const int gk = idx % a.Hkv;
-    const int b = idx / a.Hkv;
-    const int h0 = gk * G + qc * kQ;
-    const int nh = min(kQ, G - qc * kQ);
-
+__device__ __forceinline__ Item item_geo(const DecodeArgs& a, const int32_t* __restrict__ key_lens,
+                                         int it, int G, int nqc, int chunk, int D) {
+    Item g;
+    g.split = it % a.splits;
+    int r = it / a.splits;
+    const int qc = r % nqc;
+    r /= nqc;
+    const int gk = r % a.Hkv;
+    g.b = r / a.Hkv;
+    g.h0 = gk * G + qc * kQ;
+    g.nh = min(kQ, G - qc * kQ);
     int len = a.Sk;
-    if (a.key_lens) len = min(len, a.key_lens[b]);
-    const int chunk = (a.Sk + a.splits - 1) / a.splits;
-    const int lo = split * chunk;
-    const int hi = min(lo + chunk, len);
-    const int nsteps = hi > lo ? (hi - lo + kStep - 1) / kStep : 0;
+    if (key_lens) len = min(len, key_lens[g.b]);
+    g.lo = g.split * chunk;
+    g.hi = min(g.lo + chunk, len);
+    g.nst = g.hi > g.lo ? (g.hi - g.lo + kStep - 1) / kStep : 0;
+    g.kvh = ((int64_t)g.b * a.Hkv + gk) * a.Sk * D;
+    return g;
+}
+
+// Split pass.  Per 16-key step of an item, in one wave:
+//   S^T[16 keys x 16 queries] = K Q^T   D/32 v_mfma_f32_16x16x32_bf16
+//   O^T[D x 16 queries]      += V^T P^T  D/16 v_mfma_f32_16x16x16_bf16
+// K and V of a step go HBM -> LDS by buffer-load DMA into the wave's private
+// ring of NS stages, NS-1 steps ahead; K comes back with ds_read_b128 (the A
+// operand), V transposed with ds_read_b64_tr_b16.  Lane l owns query column
+// l % 16; its 4 scores per step are keys 4*(l/16) + i, exactly the 4
+// contraction slots it feeds to the P.V product.  The kernel has no
+// workgroup barrier: every wave runs its own items start to end.
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
+    DecodeArgs a, const int32_t* __restrict__ key_lens, int items) {
+    using L = DecGeo<D>;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * L::NS * L::STAGE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int col = lane & 15;   // query column (and key row within a 16-key tile)
-    const int grp = lane >> 4;   // lane group: contraction slots 8*grp .. 8*grp+7
+    const int col = lane & 15;  // query column (and key row of the S^T tile)
+    const int grp = lane >> 4;  // lane group
 
-    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const uint16_t*>(a.k) + kvh,
-                                                 (uint32_t)a.Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kvh,
-                                                 (uint32_t)a.Sk * D * 2);
+    // The workgroup owns items [wg0, it1); wave w takes wg0 + w, wg0 + w + 4, ...
+    // so the 4 waves stream 4 neighbouring splits at a time.
+    const int wg0 = (int)((int64_t)blockIdx.x * items / gridDim.x);
+    const int it1 = (int)((int64_t)(blockIdx.x + 1) * items / gridDim.x);
+    const int it0 = wg0 + wave;
+    if (it0 >= it1) return;
 
-    // Contraction slot (kstep t, group g, element e) <-> dim (D/4)*g + 8t + e, so a
-    // lane's K operand over all ksteps is (D/4) contiguous dims of one key row.
-    bf16x8 qb[L::KSTEPS];
-    {
-        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
-            static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h0) * D, (uint32_t)nh * D * 2);
-#pragma unroll
-        for (int t = 0; t < L::KSTEPS; ++t)
-            qb[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
-                qrs, (col * D + (D / 4) * grp + 8 * t) * 2, 0, 0));  // columns >= nh read 0
-    }
+    const int G = a.Hq / a.Hkv;
+    const int nqc = (G + kQ - 1) / kQ;
+    const int chunk = (a.Sk + a.splits - 1) / a.splits;
     const float c = a.scale * kLog2e;
     const float tau = kTau / c;
+    const uint32_t head_bytes = (uint32_t)a.Sk * D * 2;
 
-    // Per-lane byte offsets (relative to the step's first key).
-    uint32_t koff[2][L::KSTEPS];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-        for (int t = 0; t < L::KSTEPS; ++t)
-            koff[tile][t] = ((16 * tile + col) * D + (D / 4) * grp + 8 * t) * 2;
-    uint32_t voff[L::DMA];
+    // Lane-constant DMA offsets (bytes from the step's first key) and LDS read
+    // offsets (elements from the stage start).
+    uint32_t koff[L::DMA], voff[L::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int p = 64 * i + lane, row = p / L::CPR, pc = p % L::CPR;
+        koff[i] = row * D * 2 + (pc ^ L::fk(row)) * 16;
         voff[i] = row * D * 2 + (pc ^ L::fv(row)) * 16;
     }
-    // Transposed V read: lane j of group grp points at row k0 + j/4, dims d0 + 4*(j%4),
-    // k0 = 4*grp (+16), d0 = 16*dt; it receives V[k0..k0+3][d0 + col].
+    // K fragment of kstep t: key row col, dims (D/4)*grp + 8t .. +7 (contraction
+    // slot (t, grp, e) <-> dim (D/4)*grp + 8t + e, matching qb below).
+    int krd[L::KSTEPS];
+#pragma unroll
+    for (int t = 0; t < L::KSTEPS; ++t)
+        krd[t] = col * D + ((((D / 32) * grp + t) ^ L::fk(col)) * 8);
+    // Transposed V read: lane j of group grp points at row 4*grp + j/4, dims
+    // 16*dt + 4*(j%4); it receives V[4*grp .. 4*grp+3][16*dt + col].
     const int tr_row = 4 * grp + (col >> 2);
     int vrd[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
         const int e = 16 * dt + 4 * (col & 3);
-        vrd[dt] = tr_row * D + (((e >> 3) ^ L::fv(tr_row)) * 8) + (e & 7);
+        vrd[dt] = L::TILE + tr_row * D + (((e >> 3) ^ L::fv(tr_row)) * 8) + (e & 7);
     }
 
-    uint16_t* ring = smem + wave * 2 * L::STAGE;
-    auto issue = [&](int st, int stage, u32x4 (&kr)[2][L::KSTEPS]) {
-        const uint32_t base = (uint32_t)(lo + kStep * st) * D * 2;
-#pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(vrs, ring + stage * L::STAGE + 512 * i, base + voff[i]);
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-            for (int t = 0; t < L::KSTEPS; ++t)
-                kr[tile][t] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + koff[tile][t], 0, 0);
+    uint16_t* ring = smem + wave * L::NS * L::STAGE;
+
+    // Issue cursor: the next step to load, running NS-1 steps ahead of compute
+    // across item boundaries.  Empty items (no visible key) are skipped.
+    int i_it = it0, i_st = 0, i_nst = 0, i_k0 = 0;
+    __amdgpu_buffer_rsrc_t ikrs = make_rsrc(a.k, 0), ivrs = make_rsrc(a.v, 0);
+    auto seek = [&](int from) {
+        for (i_it = from; i_it < it1; i_it += kDecWaves) {
+            const Item g = item_geo(a, key_lens, i_it, G, nqc, chunk, D);
+            if (g.nst > 0) {
+                i_st = 0;
+                i_nst = g.nst;
+                i_k0 = g.lo;
+                ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + g.kvh, head_bytes);
+                ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + g.kvh, head_bytes);
+                return;
+            }
+        }
     };
-
-    f32x4 oacc[D / 16];
+    int issued = 0;
+    auto issue_next = [&]() {
+        uint16_t* st = ring + (issued % L::NS) * L::STAGE;
+        const uint32_t base = (uint32_t)i_k0 * D * 2;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    u32x4 kcur[2][L::KSTEPS], knext[2][L::KSTEPS];
-    if (wave < nsteps) issue(wave, 0, kcur);
-    int n = 0;
-    for (int st = wave; st < nsteps; st += kDecWaves, ++n) {
-        const int stage = n & 1;
-        const bool more = st + kDecWaves < nsteps;
-        if (more) issue(st + kDecWaves, stage ^ 1, knext);
-        // Everything but the loads just issued for the next step has landed.
-        if (more)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::DMA + 2 * L::KSTEPS) : "memory");
+        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, base + koff[i]);
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, base + voff[i]);
+        ++issued;
+        if (++i_st < i_nst)
+            i_k0 += kStep;
         else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            seek(i_it + kDecWaves);
+    };
+    seek(it0);
+    for (int j = 0; j < L::NS - 1 && i_it < it1; ++j) issue_next();
 
-        const int k0 = lo + kStep * st;
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    bf16x8 qb[L::KSTEPS];
+    int q_head = -1;
+    int done = 0;  // steps computed
+    for (int it = it0; it < it1; it += kDecWaves) {
+        const Item g = item_geo(a, key_lens, it, G, nqc, chunk, D);
+        const int64_t prow0 = ((int64_t)g.b * a.Hq + g.h0) * a.splits + g.split;
+        if (g.nst == 0) {  // no visible key in this split
+            if (col < g.nh) {
+                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * D + 4 * grp;
 #pragma unroll
-        for (int t = 0; t < L::KSTEPS; ++t)
-#pragma unroll
-            for (int tile = 0; tile < 2; ++tile)
-                sacc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[tile][t]), qb[t],
-                                                                     sacc[tile], 0, 0, 0);
-        if (k0 + kStep > hi) {
-#pragma unroll
-            for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (k0 + 16 * tile + 4 * grp + i >= hi) sacc[tile][i] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));  // all four lanes of a column agree
-        if (__any(mx > m_run + tau)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2((m_run - m_use) * c);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
-        }
-        const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-        uint32_t pk[4];
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-            for (int i = 0; i < 4; i += 2)
-                pk[2 * tile + (i >> 1)] = pack_bf16x2(fast_exp2(fmaf(sacc[tile][i], c, neg)),
-                                                      fast_exp2(fmaf(sacc[tile][i + 1], c, neg)));
-        {
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-            float ps = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[w]), one, ps, false);
-            l_run += ps;
-        }
-        const bf16x8 pb = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-        const uint16_t* vs = ring + stage * L::STAGE;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            const u32x2 lo4 = lds_read_tr16x4(vs + vrd[dt]);
-            const u32x2 hi4 = lds_read_tr16x4(vs + vrd[dt] + 16 * D);
-            const bf16x8 vf = as_bf16x8(u32x4{lo4[0], lo4[1], hi4[0], hi4[1]});
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[dt], 0, 0, 0);
-        }
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-            for (int t = 0; t < L::KSTEPS; ++t) kcur[tile][t] = knext[tile][t];
-    }
-
-    // Column totals: the denominator is spread over the 4 lane groups.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-
-    // Merge the 4 waves through LDS (the ring is free now).
-    __syncthreads();
-    float* red_o = reinterpret_cast<float*>(smem);              // [wave][q][D]
-    float* red_m = red_o + kDecWaves * kQ * D;                  // [wave][q]
-    float* red_l = red_m + kDecWaves * kQ;                      // [wave][q]
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)  // O^T register i of tile dt: dim 16*dt + 4*grp + i, column col
-            red_o[(wave * kQ + col) * D + 16 * dt + 4 * grp + i] = oacc[dt][i];
-    if (grp == 0) {
-        red_m[wave * kQ + col] = m_run;
-        red_l[wave * kQ + col] = l_run;
-    }
-    __syncthreads();
-    for (int e = tid; e < nh * D; e += kDecThreads) {
-        const int q = e / D, d = e % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int wv = 0; wv < kDecWaves; ++wv) M = fmaxf(M, red_m[wv * kQ + q]);
-        const int64_t prow = ((int64_t)b * a.Hq + h0 + q) * a.splits + split;
-        if (M == -INFINITY) {  // no visible key in this split
-            a.o_part[prow * D + d] = 0.f;
-            if (d == 0) a.lse_part[prow] = -INFINITY;
+                for (int dt = 0; dt < D / 16; ++dt)
+                    *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (grp == 0) a.lse_part[prow0 + (int64_t)col * a.splits] = -INFINITY;
+            }
             continue;
         }
-        float Ls = 0.f, acc = 0.f;
+        const int head = g.b * a.Hq + g.h0;
+        if (head != q_head) {
+            // Q^T B operand: column col = query head h0 + col (reads beyond the
+            // block's nh heads return 0), slots as in krd.
+            const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+                static_cast<const uint16_t*>(a.q) + (int64_t)head * D, (uint32_t)g.nh * D * 2);
 #pragma unroll
-        for (int wv = 0; wv < kDecWaves; ++wv) {
-            const float mw = red_m[wv * kQ + q];
-            const float w = (mw == -INFINITY) ? 0.f : fast_exp2((mw - M) * c);
-            Ls = fmaf(w, red_l[wv * kQ + q], Ls);
-            acc = fmaf(w, red_o[(wv * kQ + q) * D + d], acc);
+            for (int t = 0; t < L::KSTEPS; ++t)
+                qb[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+                    qrs, (col * D + (D / 4) * grp + 8 * t) * 2, 0, 0));
+            // Take the wait for the Q loads here, once per head, not inside the
+            // step loop.
+#pragma unroll
+            for (int t = 0; t < L::KSTEPS; ++t) asm volatile("" ::"v"(qb[t]));
+            q_head = head;
         }
-        a.o_part[prow * D + d] = acc / Ls;
-        if (d == 0) a.lse_part[prow] = M * a.scale + __logf(Ls);
+
+        f32x4 oacc[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.f;
+
+        for (int st = 0; st < g.nst; ++st, ++done) {
+            if (i_it < it1) issue_next();
+            // Every load but those of the steps issued after this one has landed.
+            const int ahead = issued - done - 1;
+            if (L::NS == 8 && ahead >= 7)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(7 * L::OPS) : "memory");
+            else if (L::NS == 8 && ahead == 6)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * L::OPS) : "memory");
+            else if (L::NS == 8 && ahead == 5)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * L::OPS) : "memory");
+            else if (L::NS == 8 && ahead == 4)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * L::OPS) : "memory");
+            else if (ahead >= 3)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L::OPS) : "memory");
+            else if (ahead == 2)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L::OPS) : "memory");
+            else if (ahead == 1)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::OPS) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+            const uint16_t* stg = ring + (done % L::NS) * L::STAGE;
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < L::KSTEPS; ++t)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_read128(stg + krd[t])),
+                                                            qb[t], s, 0, 0, 0);
+            const int k0 = g.lo + kStep * st;
+            if (k0 + kStep > g.hi) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + 4 * grp + i >= g.hi) s[i] = -INFINITY;
+            }
+            // Weights against the current reference max.  They are >= 0, so a
+            // lane sum <= 2^8 bounds each by 2^8, the lazy-rescale bound; only
+            // otherwise (or before the first max) take the tile max and maybe
+            // move the reference.
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+            uint32_t p01, p23;
+            auto weights = [&]() -> float {
+                const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+                p01 = pack_bf16x2(fast_exp2(fmaf(s[0], c, neg)), fast_exp2(fmaf(s[1], c, neg)));
+                p23 = pack_bf16x2(fast_exp2(fmaf(s[2], c, neg)), fast_exp2(fmaf(s[3], c, neg)));
+                const float ps =
+                    __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), one, 0.f, false);
+                return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), one, ps, false);
+            };
+            float ps = weights();
+            if (__any(ps > 256.f || m_run == -INFINITY)) {
+                float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = max_half_waves(mx);  // all four lanes of a column agree
+                if (__any(mx > m_run + tau)) {
+                    const float m_new = fmaxf(m_run, mx);
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    const float alpha = fast_exp2((m_run - m_use) * c);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+                }
+                ps = weights();
+            }
+            l_run += ps;
+            const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
+            u32x2 vf[D / 16];
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) vf[dt] = lds_read_tr(stg + vrd[dt]);
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vf[dt]), pb,
+                                                                     oacc[dt], 0, 0, 0);
+        }
+
+        // Column totals: the denominator is spread over the 4 lane groups.
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        if (col < g.nh) {
+            const int64_t prow = prow0 + (int64_t)col * a.splits;
+            float* op = a.o_part + prow * D + 4 * grp;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
+                *reinterpret_cast<f32x4*>(op + 16 * dt) =
+                    f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
+                          oacc[dt][3] / l_run};
+            if (grp == 0) a.lse_part[prow] = m_run * a.scale + __logf(l_run);
+        }
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
-    constexpr int RPB = 256 / D;  // rows (batch, query head) per block
-    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / D;
-    const int d = threadIdx.x % D;
+    constexpr int TPR = D / 4;       // threads per row, 4 dims each
+    constexpr int RPB = 256 / TPR;   // rows (batch, query head) per block
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int d4 = threadIdx.x % TPR;
     if (row >= (int64_t)a.B * a.Hq) return;
     const float* lse = a.lse_part + row * a.splits;
-    const float* op = a.o_part + row * a.splits * D + d;
+    const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * D) + d4;
     float M = -INFINITY;
     for (int s = 0; s < a.splits; ++s) M = fmaxf(M, lse[s]);
-    float den = 0.f, acc = 0.f;
+    float den = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int s = 0; s < a.splits; ++s) {
         const float w = fast_exp2((lse[s] - M) * kLog2e);  // empty split: exp(-inf) = 0
         den += w;
-        acc = fmaf(w, op[(int64_t)s * D], acc);
+        const f32x4 o = op[(int64_t)s * (D / 4)];
+        acc[0] = fmaf(w, o[0], acc[0]);
+        acc[1] = fmaf(w, o[1], acc[1]);
+        acc[2] = fmaf(w, o[2], acc[2]);
+        acc[3] = fmaf(w, o[3], acc[3]);
     }
     // Every split empty (no visible key): M = -inf, w = NaN, and the row is NaN.
-    static_cast<uint16_t*>(a.out)[row * D + d] = (uint16_t)f32_to_bf16_bits(acc / den);
+    const uint32_t lo = pack_lo16(f32_to_bf16_bits(acc[0] / den), f32_to_bf16_bits(acc[1] / den));
+    const uint32_t hi = pack_lo16(f32_to_bf16_bits(acc[2] / den), f32_to_bf16_bits(acc[3] / den));
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + 4 * d4) = u32x2{lo, hi};
+}
+
+// Compute units of the current device (cached per device).
+hipError_t compute_units(int* n) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && (*n = cache[dev].load(std::memory_order_relaxed)) > 0)
+        return hipSuccess;
+    e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (*n < 1) *n = 1;
+    if (dev >= 0 && dev < 64) cache[dev].store(*n, std::memory_order_relaxed);
+    return hipSuccess;
 }
 
 }  // namespace
 
+int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits) {
+    const int64_t G = Hq / Hkv;
+    return B * Hkv * ((G + kQ - 1) / kQ) * splits;
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
-    const int G = a.Hq / a.Hkv;
-    const int nqc = (G + kQ - 1) / kQ;
-    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * nqc * a.splits));
-    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * a.D + 255) / 256));
+    const int items = (int)decode_work_items(a.B, a.Hq, a.Hkv, a.splits);
+    int cus = 0;
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+    // One workgroup per compute unit (the LDS ring admits no second one), or
+    // fewer when there are fewer items than waves.
+    const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * a.D / 4 + 255) / 256));
     if (a.D == 64) {
-        hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, dim3(kDecThreads), 0, s, a);
+        hipLaunchKernelGGL(decode_split_bf16_kernel<64>, dim3(wgs), dim3(kDecThreads), 0, s, a,
+                           a.key_lens, items);
         hipLaunchKernelGGL(decode_merge_bf16_kernel<64>, mgrid, dim3(256), 0, s, a);
     } else if (a.D == 128) {
-        hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, dim3(kDecThreads), 0, s, a);
+        hipLaunchKernelGGL(decode_split_bf16_kernel<128>, dim3(wgs), dim3(kDecThreads), 0, s, a,
+                           a.key_lens, items);
         hipLaunchKernelGGL(decode_merge_bf16_kernel<128>, mgrid, dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;

@@ -115,7 +115,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ u32x2 lds_read_tr16x4(const uint16_t* p) {
+// The __restrict__ parameter gives the inlined read its own alias scope, which
+// keeps the compiler from putting a vmcnt(0) drain of the in-flight LDS-DMA
+// writes in front of it (the explicit waits and barriers order those).
+__device__ __forceinline__ u32x2 lds_read_tr16x4(const uint16_t* __restrict__ p) {
     lds_i16x4* lp = (lds_i16x4*)((__attribute__((address_space(3))) char*)p);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     // bf16 weights of a score tile against the reference max; the denominator
     // sums the rounded weights (v_dot2 with (1, 1)), i.e. exactly the weights
     // multiplied into V.  Straight-line code.
-    auto weights = [&](const f32x16 (&sacc)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+    auto weights = [&](const f32x16 (&sacc)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) -> float {
         const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
         typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
         const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
                 if (r & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps1, false);
                 else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps0, false);
             }
-        l_run += ps0 + ps1;
+        return ps0 + ps1;
     };
 
     // O^T += V^T P^T over the four 16-key slices of the V stage at vs.
@@ -370,8 +373,16 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
         if (jt < wave_tiles) {
             uint32_t pk[2][8];
             if (jt + 1 < wave_tiles) scores(smem + (cur ^ 1) * L::TILE, snext);
-            update_max(scur);
-            weights(scur, pk);
+            // Weights against the current reference max.  They are >= 0, so a
+            // lane sum <= 2^8 bounds every weight by 2^8, the lazy-rescale
+            // bound; only otherwise (or before the first max) look at the
+            // tile max and maybe move the reference.
+            float ps = weights(scur, pk);
+            if (__any(ps > 256.f || m_run == -INFINITY)) {
+                update_max(scur);
+                ps = weights(scur, pk);
+            }
+            l_run += ps;
             accumulate(smem + (2 + cur) * L::TILE, pk);
             if (jt + 1 < wave_tiles) mask_tile((jt + 1) * kBc, snext);
         }

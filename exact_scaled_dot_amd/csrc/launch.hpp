@@ -36,4 +36,8 @@ hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
+// Work items of the decode split pass: (batch, K/V head, block of <= 16 query
+// heads, split).
+int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits);
+
 }  // namespace sdpa

@@ -183,10 +183,9 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps the workspace");
     if (dtype != SDPA_BF16)
         return fail(SDPA_ERR_UNSUPPORTED, "decode supports bf16 only");
-    const int64_t G = Hq / Hkv;
-    const int64_t blocks = B * Hkv * ((G + 3) / 4) * num_splits;
-    if (blocks > INT_MAX / 256)
-        return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
+    const int64_t items = sdpa::decode_work_items(B, Hq, Hkv, num_splits);
+    if (items > INT_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "too many decode work items (%lld)", (long long)items);
 
     sdpa::DecodeArgs a;
     a.q = q;
