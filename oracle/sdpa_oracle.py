@@ -35,6 +35,13 @@ reordered:
 * split-KV   partial attention over disjoint key ranges, each with its own lse,
   and the log-sum-exp merge of those partials (ruDNN user guide section 9:
   history split into 2..=32 pieces, partial statistics and merge in FP32).
+* paged      packed queries [queries, Hq, D] over a physical K/V page cache
+  [pages, page_size, Hkv, D] (ruDNN user guide section 9): query t belongs to
+  sequence query_seq[t] at zero-based absolute position query_pos[t]; the
+  sequence's logical key j (j < seq_lens[s]) sits in physical page
+  block_tables[s][j // page_size], slot j % page_size; with the causal flag
+  key j is visible only when j <= query_pos[t] (absolute positions, so a
+  chunk of new queries at the end of a sequence is aligned bottom-right).
 
 A row with no visible key has 0/0 weights and yields NaN, the literal result
 of the essay's normalisation (ruDNN user guide section 4 likewise keeps NaN
@@ -226,8 +233,57 @@ def merge_partials(o_part, lse_part):
     return o, lse
 
 
+def paged_gather(cache, table_row, length, page_size):
+    """Logical rows 0..length-1 of one sequence read through its page table.
+
+    cache [pages, page_size, Hkv, D]; logical row j is physical page
+    table_row[j // page_size], slot j % page_size (ruDNN user guide section 9:
+    the kernels read the physical cache pages directly).  Returns
+    [length, Hkv, D].
+    """
+    j = np.arange(int(length), dtype=np.int64)
+    table_row = np.asarray(table_row, dtype=np.int64)
+    return np.asarray(cache)[table_row[j // page_size], j % page_size]
+
+
+def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq, query_pos,
+                    scale, causal):
+    """Packed paged attention (ruDNN user guide section 9).
+
+    q [queries, Hq, D]; k_cache, v_cache [pages, page_size, Hkv, D];
+    block_tables [num_seqs, max_pages_per_seq]; seq_lens [num_seqs];
+    query_seq, query_pos [queries].  Query t (sequence s = query_seq[t],
+    position p = query_pos[t]) attends to keys j < seq_lens[s] of its own
+    sequence, and with causal only to j <= p.  Query head h reads K/V head
+    h // (Hq / Hkv).  Returns o [queries, Hq, D] in fp64 (NaN rows where no key
+    is visible).
+    """
+    q = np.asarray(q)
+    nq, Hq, D = q.shape
+    pages, page_size, Hkv, Dk = np.asarray(k_cache).shape
+    if Dk != D or np.asarray(v_cache).shape != np.asarray(k_cache).shape:
+        raise ValueError("inconsistent q / cache shapes")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    o = np.empty((nq, Hq, D), dtype=np.float64)
+    for t in range(nq):
+        s_id, pos = int(query_seq[t]), int(query_pos[t])
+        length = int(seq_lens[s_id])
+        ks = paged_gather(k_cache, block_tables[s_id], length, page_size)
+        vs = paged_gather(v_cache, block_tables[s_id], length, page_size)
+        j = np.arange(length, dtype=np.int64)
+        vis = np.ones((1, length), dtype=bool)
+        if causal:
+            vis &= (j <= pos)[None, :]
+        for h in range(Hq):
+            g = h // G
+            o[t, h] = attend(q[t, h:h + 1], ks[:, g], vs[:, g], scale, vis)[0][0]
+    return o
+
+
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KEY_PADDING", "visible_rows", "attend",
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
-    "decode_split_partials", "merge_partials",
+    "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
 ]

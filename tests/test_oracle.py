@@ -363,3 +363,161 @@ def test_argument_checks():
     with pytest.raises(ValueError):
         O.sdpa_forward(rand(1, 1, 2, 2), rand(1, 1, 3, 2), rand(1, 1, 3, 2), 1.0,
                        O.MASK_KEY_PADDING)
+
+
+# ------------------------------------------------------------------ paged cache
+
+def make_paged(k, v, lens, page_size, extra_pages, rng):
+    """Scatter dense K/V [nseq, Hkv, S, D] into a shuffled page pool.
+
+    Returns (k_cache, v_cache, block_tables); every unused slot and page is
+    filled with large garbage so that reading one by mistake shows.
+    """
+    nseq, Hkv, S, D = k.shape
+    need = [-(-int(n) // page_size) for n in lens]
+    max_pages = max(need)
+    pages = sum(need) + extra_pages
+    perm = rng.permutation(pages)
+    k_cache = rng.standard_normal((pages, page_size, Hkv, D)) * 50.0
+    v_cache = rng.standard_normal((pages, page_size, Hkv, D)) * 50.0
+    tables = np.full((nseq, max_pages), -1, dtype=np.int64)
+    nxt = 0
+    for s in range(nseq):
+        for lp in range(need[s]):
+            tables[s, lp] = perm[nxt]
+            nxt += 1
+        for j in range(int(lens[s])):
+            pg, sl = tables[s, j // page_size], j % page_size
+            k_cache[pg, sl] = k[s, :, j]
+            v_cache[pg, sl] = v[s, :, j]
+    return k_cache, v_cache, tables
+
+
+@pytest.mark.parametrize("page_size", [1, 4, 16])
+def test_paged_prefill_equals_dense_causal(page_size):
+    # Every position of every sequence as a packed query, causal by absolute
+    # position: the rows of the dense causal forward of each sequence.
+    rng = np.random.default_rng(7 + page_size)
+    lens = [37, 5, 20]
+    nseq, Hq, Hkv, D, S = len(lens), 4, 2, 8, max(lens)
+    q = rng.standard_normal((nseq, Hq, S, D))
+    k = rng.standard_normal((nseq, Hkv, S, D))
+    v = rng.standard_normal((nseq, Hkv, S, D))
+    kc, vc, tables = make_paged(k, v, lens, page_size, 3, rng)
+    qs = np.array([s for s in range(nseq) for _ in range(lens[s])])
+    qp = np.array([i for s in range(nseq) for i in range(lens[s])])
+    qq = np.stack([q[s, :, i] for s, i in zip(qs, qp)])
+    got = O.paged_attention(qq, kc, vc, tables, lens, qs, qp, 0.3, True)
+    for s in range(nseq):
+        n = lens[s]
+        ref = O.sdpa_forward(q[s:s + 1, :, :n], k[s:s + 1, :, :n], v[s:s + 1, :, :n], 0.3,
+                             O.MASK_CAUSAL)[0]
+        rows = got[qs == s]
+        np.testing.assert_allclose(rows, ref.transpose(1, 0, 2), rtol=0, atol=1e-13)
+
+
+def test_paged_decode_equals_padded_decode():
+    # One query per sequence: non-causal, or causal at the last position, is
+    # the padded dense decode with key_lens = seq_lens.
+    rng = np.random.default_rng(11)
+    lens = np.array([1, 17, 64, 33])
+    nseq, Hq, Hkv, D, S = len(lens), 8, 2, 16, 64
+    q = rng.standard_normal((nseq, Hq, 1, D))
+    k = rng.standard_normal((nseq, Hkv, S, D))
+    v = rng.standard_normal((nseq, Hkv, S, D))
+    kc, vc, tables = make_paged(k, v, lens, 16, 2, rng)
+    ref = O.sdpa_decode(q, k, v, 0.25, lens)[:, :, 0]
+    seqs = np.arange(nseq)
+    for causal, pos in ((False, np.zeros(nseq, dtype=np.int64)), (True, lens - 1)):
+        got = O.paged_attention(q[:, :, 0], kc, vc, tables, lens, seqs, pos, 0.25, causal)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
+
+
+def test_paged_bottom_right_chunk():
+    # A chunk of 5 new queries at the end of a 29-key sequence sees exactly
+    # keys 0..pos: the last 5 rows of the dense causal forward.
+    rng = np.random.default_rng(3)
+    L, n, Hq, Hkv, D = 29, 5, 2, 1, 8
+    q = rng.standard_normal((1, Hq, L, D))
+    k = rng.standard_normal((1, Hkv, L, D))
+    v = rng.standard_normal((1, Hkv, L, D))
+    kc, vc, tables = make_paged(k, v, [L], 8, 1, rng)
+    pos = np.arange(L - n, L)
+    got = O.paged_attention(q[0, :, L - n:].transpose(1, 0, 2), kc, vc, tables, [L],
+                            np.zeros(n, dtype=np.int64), pos, 0.5, True)
+    ref = O.sdpa_forward(q, k, v, 0.5, O.MASK_CAUSAL)[0][:, L - n:]
+    np.testing.assert_allclose(got, ref.transpose(1, 0, 2), rtol=0, atol=1e-13)
+    # without the causal flag every cached key is visible to every query
+    got_nc = O.paged_attention(q[0, :, L - n:].transpose(1, 0, 2), kc, vc, tables, [L],
+                               np.zeros(n, dtype=np.int64), pos, 0.5, False)
+    ref_nc = O.sdpa_forward(q[:, :, L - n:], k, v, 0.5)[0]
+    np.testing.assert_allclose(got_nc, ref_nc.transpose(1, 0, 2), rtol=0, atol=1e-13)
+
+
+def test_paged_invariances():
+    rng = np.random.default_rng(5)
+    lens = [13, 30]
+    nseq, Hq, Hkv, D, S = 2, 4, 4, 8, 30
+    q = rng.standard_normal((nseq, Hq, S, D))
+    k = rng.standard_normal((nseq, Hkv, S, D))
+    v = rng.standard_normal((nseq, Hkv, S, D))
+    kc, vc, tables = make_paged(k, v, lens, 4, 4, rng)
+    qs = np.array([0] * 13 + [1] * 30)
+    qp = np.array(list(range(13)) + list(range(30)))
+    qq = np.stack([q[s, :, i] for s, i in zip(qs, qp)])
+    base = O.paged_attention(qq, kc, vc, tables, lens, qs, qp, 0.4, True)
+    # relabelling the physical pages changes nothing
+    perm = rng.permutation(kc.shape[0])
+    inv = np.argsort(perm)
+    t2 = np.where(tables >= 0, inv[np.maximum(tables, 0)], -1)
+    got = O.paged_attention(qq, kc[perm], vc[perm], t2, lens, qs, qp, 0.4, True)
+    assert np.array_equal(got, base)
+    # rewriting slots past a sequence's length and unreferenced pages changes nothing
+    kc2, vc2 = kc.copy(), vc.copy()
+    used = set()
+    for s in range(nseq):
+        for j in range(lens[s]):
+            used.add((int(tables[s, j // 4]), j % 4))
+    for pg in range(kc.shape[0]):
+        for sl in range(4):
+            if (pg, sl) not in used:
+                kc2[pg, sl] = 1e6
+                vc2[pg, sl] = -1e6
+    got = O.paged_attention(qq, kc2, vc2, tables, lens, qs, qp, 0.4, True)
+    assert np.array_equal(got, base)
+    # query order is irrelevant: each query is answered on its own
+    order = rng.permutation(len(qs))
+    got = O.paged_attention(qq[order], kc, vc, tables, lens, qs[order], qp[order], 0.4, True)
+    assert np.array_equal(got, base[order])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_paged_brute_force_tiny(causal):
+    # Scalar loops with math.exp straight from the definition; page size 2,
+    # two sequences sharing one pool, pages out of order.
+    rng = np.random.default_rng(21 + causal)
+    ps, Hq, Hkv, D = 2, 2, 1, 3
+    kc = rng.standard_normal((5, ps, Hkv, D))
+    vc = rng.standard_normal((5, ps, Hkv, D))
+    tables = np.array([[3, 0, 4], [1, 2, -1]])
+    lens = [5, 3]
+    qs = np.array([0, 0, 1, 1])
+    qp = np.array([4, 1, 2, 0])
+    qq = rng.standard_normal((4, Hq, D))
+    scale = 0.7
+    got = O.paged_attention(qq, kc, vc, tables, lens, qs, qp, scale, causal)
+    for t in range(4):
+        s, p = qs[t], qp[t]
+        keys = [j for j in range(lens[s]) if not causal or j <= p]
+        for h in range(Hq):
+            sc = []
+            for j in keys:
+                row = kc[tables[s][j // ps], j % ps, 0]
+                sc.append(scale * sum(qq[t, h, d] * row[d] for d in range(D)))
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = math.fsum(w)
+            for d in range(D):
+                ref = math.fsum(w[i] * vc[tables[s][j // ps], j % ps, 0, d]
+                                for i, j in enumerate(keys)) / tot
+                assert got[t, h, d] == pytest.approx(ref, abs=1e-13)
