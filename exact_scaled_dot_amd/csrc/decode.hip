@@ -78,9 +78,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
+// 16 bytes per lane from a buffer straight into LDS (lane l's bytes land at
+// lds + 16*l); voff is per lane, soff wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff,
+                                      uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, kNonTemporal);
+        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, soff, 0, kNonTemporal);
 }
 
 template <int D>
@@ -102,29 +105,54 @@ struct DecGeo {
 };
 static_assert(DecGeo<128>::NS == 4 && DecGeo<64>::NS == 8, "ring depth");
 
-// Geometry of one work item.
-struct Item {
-    int b, h0, nh, split, lo, hi, nst;
-    int64_t kvh;  // element offset of the item's K/V head
+// Per-launch metadata pointers, each read with scalar loads (hence separate
+// __restrict__ kernel arguments rather than struct members).
+struct Meta {
+    const int32_t* __restrict__ key_lens;   // dense: [B] or null
+    const int32_t* __restrict__ tables;     // paged: [num_seqs, max_pages]
+    const int32_t* __restrict__ seq_lens;   // paged: [num_seqs]
+    const int32_t* __restrict__ query_seq;  // paged: [queries]
+    const int32_t* __restrict__ query_pos;  // paged: [queries]
 };
 
-__device__ __forceinline__ Item item_geo(const DecodeArgs& a, const int32_t* __restrict__ key_lens,
-                                         int it, int G, int nqc, int chunk, int D) {
+// Geometry of one work item.  b is the batch (dense) or the query (paged); seq
+// the query's sequence (paged, -1 if out of range).
+struct Item {
+    int b, gk, h0, nh, split, lo, hi, nst, seq;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ Item item_geo(const DecodeArgs& a, const PagedArgs& p, const Meta& m,
+                                         int it, int G, int nqc, int chunk) {
     Item g;
     g.split = it % a.splits;
     int r = it / a.splits;
     const int qc = r % nqc;
     r /= nqc;
-    const int gk = r % a.Hkv;
+    g.gk = r % a.Hkv;
     g.b = r / a.Hkv;
-    g.h0 = gk * G + qc * kQ;
+    g.h0 = g.gk * G + qc * kQ;
     g.nh = min(kQ, G - qc * kQ);
     int len = a.Sk;
-    if (key_lens) len = min(len, key_lens[g.b]);
+    g.seq = -1;
+    if (PAGED) {
+        // Visible keys of query b: j < seq_lens[seq] (capped at max_seq_len)
+        // and, under the causal flag, j <= its absolute position.  A sequence
+        // id outside [0, num_seqs) leaves nothing visible.
+        const int s = m.query_seq[g.b];
+        if (s >= 0 && s < p.num_seqs) {
+            g.seq = s;
+            len = min(len, m.seq_lens[s]);
+            if (p.causal) len = min(len, m.query_pos[g.b] + 1);
+        } else {
+            len = 0;
+        }
+    } else if (m.key_lens) {
+        len = min(len, m.key_lens[g.b]);
+    }
     g.lo = g.split * chunk;
     g.hi = min(g.lo + chunk, len);
     g.nst = g.hi > g.lo ? (g.hi - g.lo + kStep - 1) / kStep : 0;
-    g.kvh = ((int64_t)g.b * a.Hkv + gk) * a.Sk * D;
     return g;
 }
 
@@ -137,10 +165,19 @@ __device__ __forceinline__ Item item_geo(const DecodeArgs& a, const int32_t* __r
 // l % 16; its 4 scores per step are keys 4*(l/16) + i, exactly the 4
 // contraction slots it feeds to the P.V product.  The kernel has no
 // workgroup barrier: every wave runs its own items start to end.
-template <int D>
+//
+// PAGED: K and V come from a page cache [pages, page_size, Hkv, D]; a step's
+// 16 keys lie in one page (page_size and the split length are multiples of
+// 16), found through the sequence's page table when the step enters a new
+// page.  A table entry outside [0, pages) is never dereferenced: its keys
+// load as zeros and are masked out.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
-    DecodeArgs a, const int32_t* __restrict__ key_lens, int items) {
+    DecodeArgs a, PagedArgs p, const int32_t* __restrict__ key_lens,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ query_seq, const int32_t* __restrict__ query_pos, int items) {
     using L = DecGeo<D>;
+    const Meta meta{key_lens, tables, seq_lens, query_seq, query_pos};
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * L::NS * L::STAGE];
 
     const int tid = threadIdx.x;
@@ -158,19 +195,26 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
 
     const int G = a.Hq / a.Hkv;
     const int nqc = (G + kQ - 1) / kQ;
-    const int chunk = (a.Sk + a.splits - 1) / a.splits;
+    // Split length: ceil(Sk / splits) keys (paged: rounded up to a multiple of
+    // the 16-key step, so no step crosses a page).
+    int chunk = (a.Sk + a.splits - 1) / a.splits;
+    if (PAGED) chunk = (chunk + kStep - 1) / kStep * kStep;
     const float c = a.scale * kLog2e;
     const float tau = kTau / c;
     const uint32_t head_bytes = (uint32_t)a.Sk * D * 2;
+    // Bytes between consecutive keys of one K/V head: D*2 in a dense head,
+    // Hkv*D*2 inside a page.
+    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * D * 2 : (uint32_t)D * 2;
+    const uint32_t page_bytes = PAGED ? (uint32_t)p.page_size * row_bytes : 0u;
 
     // Lane-constant DMA offsets (bytes from the step's first key) and LDS read
     // offsets (elements from the stage start).
     uint32_t koff[L::DMA], voff[L::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
-        const int p = 64 * i + lane, row = p / L::CPR, pc = p % L::CPR;
-        koff[i] = row * D * 2 + (pc ^ L::fk(row)) * 16;
-        voff[i] = row * D * 2 + (pc ^ L::fv(row)) * 16;
+        const int q = 64 * i + lane, row = q / L::CPR, pc = q % L::CPR;
+        koff[i] = row * row_bytes + (pc ^ L::fk(row)) * 16;
+        voff[i] = row * row_bytes + (pc ^ L::fv(row)) * 16;
     }
     // K fragment of kstep t: key row col, dims (D/4)*grp + 8t .. +7 (contraction
     // slot (t, grp, e) <-> dim (D/4)*grp + 8t + e, matching qb below).
@@ -192,17 +236,26 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
 
     // Issue cursor: the next step to load, running NS-1 steps ahead of compute
     // across item boundaries.  Empty items (no visible key) are skipped.
-    int i_it = it0, i_st = 0, i_nst = 0, i_k0 = 0;
+    int i_it = it0, i_st = 0, i_nst = 0, i_k0 = 0, i_seq = 0, i_gk = 0, i_page = -1;
     __amdgpu_buffer_rsrc_t ikrs = make_rsrc(a.k, 0), ivrs = make_rsrc(a.v, 0);
+    // Bit (n % 32): step n's keys come from a valid page (paged; at most NS-1
+    // steps are ahead of compute, so 32 bits never wrap onto a live step).
+    uint32_t valid_bits = 0xffffffffu;
     auto seek = [&](int from) {
         for (i_it = from; i_it < it1; i_it += kDecWaves) {
-            const Item g = item_geo(a, key_lens, i_it, G, nqc, chunk, D);
+            const Item g = item_geo<PAGED>(a, p, meta, i_it, G, nqc, chunk);
             if (g.nst > 0) {
                 i_st = 0;
                 i_nst = g.nst;
                 i_k0 = g.lo;
-                ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + g.kvh, head_bytes);
-                ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + g.kvh, head_bytes);
+                i_seq = g.seq;
+                i_gk = g.gk;
+                i_page = -1;
+                if (!PAGED) {
+                    const int64_t kvh = ((int64_t)g.b * a.Hkv + g.gk) * a.Sk * D;
+                    ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + kvh, head_bytes);
+                    ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kvh, head_bytes);
+                }
                 return;
             }
         }
@@ -210,11 +263,36 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     int issued = 0;
     auto issue_next = [&]() {
         uint16_t* st = ring + (issued % L::NS) * L::STAGE;
-        const uint32_t base = (uint32_t)i_k0 * D * 2;
+        uint32_t base;
+        if (PAGED) {
+            const int lp = i_k0 / p.page_size;
+            if (lp != i_page) {  // entering a new page: look it up
+                i_page = lp;
+                const int pg = lp < p.max_pages ? meta.tables[(int64_t)i_seq * p.max_pages + lp] : -1;
+                const bool ok = pg >= 0 && pg < p.pages;
+                const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * D : 0;
+                ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + off, ok ? page_bytes : 0u);
+                ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + off, ok ? page_bytes : 0u);
+                valid_bits = ok ? (valid_bits | (1u << (issued & 31))) : (valid_bits & ~(1u << (issued & 31)));
+            } else {
+                // same page as the previous step: same validity
+                const uint32_t prev = (valid_bits >> ((issued - 1) & 31)) & 1u;
+                valid_bits = (valid_bits & ~(1u << (issued & 31))) | (prev << (issued & 31));
+            }
+            base = ((uint32_t)(i_k0 % p.page_size) * a.Hkv + i_gk) * D * 2;
+        } else {
+            base = (uint32_t)i_k0 * D * 2;
+        }
+        // The buffer range check covers the per-lane offset but not the scalar
+        // one.  Dense: the step offset goes into the per-lane offset, so rows
+        // past Sk read zeros.  Paged: a step never leaves its page (and an
+        // invalid page has no records at all), so it can ride in the scalar
+        // offset.
+        const uint32_t vb = PAGED ? 0u : base, sb = PAGED ? base : 0u;
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, base + koff[i]);
+        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, koff[i] + vb, sb);
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, base + voff[i]);
+        for (int i = 0; i < L::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, voff[i] + vb, sb);
         ++issued;
         if (++i_st < i_nst)
             i_k0 += kStep;
@@ -228,7 +306,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     int q_head = -1;
     int done = 0;  // steps computed
     for (int it = it0; it < it1; it += kDecWaves) {
-        const Item g = item_geo(a, key_lens, it, G, nqc, chunk, D);
+        const Item g = item_geo<PAGED>(a, p, meta, it, G, nqc, chunk);
         const int64_t prow0 = ((int64_t)g.b * a.Hq + g.h0) * a.splits + g.split;
         if (g.nst == 0) {  // no visible key in this split
             if (col < g.nh) {
@@ -295,6 +373,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 for (int i = 0; i < 4; ++i)
                     if (k0 + 4 * grp + i >= g.hi) s[i] = -INFINITY;
             }
+            if (PAGED && !((valid_bits >> (done & 31)) & 1u)) s = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             // Weights against the current reference max.  They are >= 0, so a
             // lane sum <= 2^8 bounds each by 2^8, the lazy-rescale bound; only
             // otherwise (or before the first max) take the tile max and maybe
@@ -343,12 +422,19 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
             float* op = a.o_part + prow * D + 4 * grp;
+            if (m_run == -INFINITY) {  // every key masked (paged: invalid pages only)
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
-                *reinterpret_cast<f32x4*>(op + 16 * dt) =
-                    f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
-                          oacc[dt][3] / l_run};
-            if (grp == 0) a.lse_part[prow] = m_run * a.scale + __logf(l_run);
+                for (int dt = 0; dt < D / 16; ++dt)
+                    *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (grp == 0) a.lse_part[prow] = -INFINITY;
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
+                    *reinterpret_cast<f32x4*>(op + 16 * dt) =
+                        f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
+                              oacc[dt][3] / l_run};
+                if (grp == 0) a.lse_part[prow] = m_run * a.scale + __logf(l_run);
+            }
         }
     }
 }
@@ -397,6 +483,32 @@ hipError_t compute_units(int* n) {
     return hipSuccess;
 }
 
+template <bool PAGED>
+hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
+    const int items = (int)decode_work_items(a.B, a.Hq, a.Hkv, a.splits);
+    int cus = 0;
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+    // One workgroup per compute unit (the LDS rings admit no second one), or
+    // fewer when there are fewer items.
+    const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * a.D / 4 + 255) / 256));
+    if (a.D == 64) {
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED>), dim3(wgs), dim3(kDecThreads), 0, s,
+                           a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
+                           items);
+        hipLaunchKernelGGL(decode_merge_bf16_kernel<64>, mgrid, dim3(256), 0, s, a);
+    } else if (a.D == 128) {
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED>), dim3(wgs), dim3(kDecThreads), 0, s,
+                           a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
+                           items);
+        hipLaunchKernelGGL(decode_merge_bf16_kernel<128>, mgrid, dim3(256), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits) {
@@ -405,26 +517,11 @@ int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
-    const int items = (int)decode_work_items(a.B, a.Hq, a.Hkv, a.splits);
-    int cus = 0;
-    const hipError_t e = compute_units(&cus);
-    if (e != hipSuccess) return e;
-    // One workgroup per compute unit (the LDS ring admits no second one), or
-    // fewer when there are fewer items than waves.
-    const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
-    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * a.D / 4 + 255) / 256));
-    if (a.D == 64) {
-        hipLaunchKernelGGL(decode_split_bf16_kernel<64>, dim3(wgs), dim3(kDecThreads), 0, s, a,
-                           a.key_lens, items);
-        hipLaunchKernelGGL(decode_merge_bf16_kernel<64>, mgrid, dim3(256), 0, s, a);
-    } else if (a.D == 128) {
-        hipLaunchKernelGGL(decode_split_bf16_kernel<128>, dim3(wgs), dim3(kDecThreads), 0, s, a,
-                           a.key_lens, items);
-        hipLaunchKernelGGL(decode_merge_bf16_kernel<128>, mgrid, dim3(256), 0, s, a);
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return launch_split_and_merge<false>(a, PagedArgs{}, s);
+}
+
+hipError_t launch_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
+    return launch_split_and_merge<true>(a, p, s);
 }
 
 }  // namespace sdpa

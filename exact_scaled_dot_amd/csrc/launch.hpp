@@ -32,9 +32,22 @@ struct DecodeArgs {
     float scale;
 };
 
+// Paged K/V cache (packed queries).  With these, DecodeArgs holds B = queries,
+// Sk = max_seq_len, k / v = the page caches [pages, page_size, Hkv, D] and no
+// key_lens.
+struct PagedArgs {
+    const int32_t* block_tables;  // [num_seqs, max_pages]
+    const int32_t* seq_lens;      // [num_seqs]
+    const int32_t* query_seq;     // [queries]
+    const int32_t* query_pos;     // [queries]
+    int num_seqs, max_pages, pages, page_size;
+    bool causal;
+};
+
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
 
 // Work items of the decode split pass: (batch, K/V head, block of <= 16 query
 // heads, split).

@@ -26,8 +26,8 @@ MAX_SPLITS = 32
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
-EXPORTED = ("sdpa_forward", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_status_string",
-            "sdpa_last_error")
+EXPORTED = ("sdpa_forward", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
+            "sdpa_status_string", "sdpa_last_error")
 
 _lib = None
 
@@ -56,6 +56,10 @@ def load_library():
                                 ctypes.c_size_t, vp, i32, vp]
     lib.sdpa_decode_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_decode_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.sdpa_paged_attention.restype = i32
+    lib.sdpa_paged_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
+                                         vp, vp, i64, ctypes.c_float, i32, i32, vp, ctypes.c_size_t,
+                                         vp, i32, vp]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_status_string.argtypes = [i32]
     lib.sdpa_last_error.restype = ctypes.c_char_p
@@ -173,3 +177,46 @@ def decode_workspace_views(workspace, B, Hq, D, num_splits):
     o_part = f[: n_o * 4].view(torch.float32).view(B, Hq, num_splits, D)
     lse = f[off: off + B * Hq * num_splits * 4].view(torch.float32).view(B, Hq, num_splits)
     return o_part, lse
+
+
+def sdpa_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq, query_pos, scale,
+                         causal, max_seq_len, num_splits=MAX_SPLITS, workspace=None, out=None,
+                         stream=None):
+    """Packed queries over a K/V page cache.
+
+    q [queries, Hq, D]; k_cache, v_cache [pages, page_size, Hkv, D];
+    block_tables int32 [num_seqs, max_pages_per_seq]; seq_lens int32
+    [num_seqs]; query_seq, query_pos int32 [queries]; max_seq_len (host int)
+    bounds seq_lens.  Returns out [queries, Hq, D].
+    """
+    _check_tensor("q", q, 3)
+    _check_tensor("k_cache", k_cache, 4)
+    _check_tensor("v_cache", v_cache, 4)
+    _check_tensor("block_tables", block_tables, 2)
+    for name, t in (("seq_lens", seq_lens), ("query_seq", query_seq), ("query_pos", query_pos)):
+        _check_tensor(name, t, 1)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_seq", query_seq), ("query_pos", query_pos)):
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % name)
+    nq, Hq, D = q.shape
+    pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [pages, page_size, Hkv, D] matching q")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    num_seqs, max_pages = block_tables.shape
+    if seq_lens.shape[0] != num_seqs or query_seq.shape[0] != nq or query_pos.shape[0] != nq:
+        raise ValueError("seq_lens must have num_seqs entries, query_seq and query_pos one per query")
+    lib = load_library()
+    need = int(lib.sdpa_decode_workspace_size(nq, Hq, D, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.sdpa_paged_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, pages, page_size, _ptr(block_tables),
+        num_seqs, max_pages, _ptr(seq_lens), _ptr(query_seq), _ptr(query_pos), int(max_seq_len),
+        float(scale), int(bool(causal)), int(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _dtype_code(q), _stream(stream)))
+    return out

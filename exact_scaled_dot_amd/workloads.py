@@ -95,3 +95,41 @@ def make_inputs(w, device="cpu", seed=None):
 def to_f64_numpy(t):
     """Exact float64 copy of a float32 / bfloat16 tensor (for the CPU side)."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def draw_paged(seq_lens, query_seq, query_pos, Hq, Hkv, D, page_size, dtype, seed, device="cpu",
+               extra_pages=3):
+    """Packed queries over a shuffled K/V page cache.
+
+    seq_lens, query_seq, query_pos: host integer lists.  Sequence s owns
+    ceil(seq_lens[s] / page_size) physical pages, dealt from a random
+    permutation of all pages (CPU generator seeded with seed + 104729), and
+    extra_pages pages belong to nobody; unused table entries are -1.  Q and
+    the whole cache (unused slots included) are i.i.d. N(0, 1) float32 drawn in
+    the order Q, K cache, V cache on a device generator seeded with seed, then
+    rounded to dtype.  Returns a dict of device tensors plus the sizes.
+    """
+    seq_lens = [int(x) for x in seq_lens]
+    need = [-(-n // page_size) for n in seq_lens]
+    max_pages = max(1, max(need))
+    pages = sum(need) + int(extra_pages)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    nq = len(query_seq)
+    q = torch.randn(nq, Hq, D, generator=g, device=device, dtype=torch.float32).to(dtype)
+    kc = torch.randn(pages, page_size, Hkv, D, generator=g, device=device, dtype=torch.float32).to(dtype)
+    vc = torch.randn(pages, page_size, Hkv, D, generator=g, device=device, dtype=torch.float32).to(dtype)
+    gc = torch.Generator(device="cpu")
+    gc.manual_seed(seed + 104729)
+    perm = torch.randperm(pages, generator=gc).tolist()
+    tables = torch.full((len(seq_lens), max_pages), -1, dtype=torch.int32)
+    nxt = 0
+    for s, n in enumerate(need):
+        for lp in range(n):
+            tables[s, lp] = perm[nxt]
+            nxt += 1
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(q=q, k_cache=kc, v_cache=vc, block_tables=tables.to(device),
+                seq_lens=torch.tensor(seq_lens, **i32), query_seq=torch.tensor(list(query_seq), **i32),
+                query_pos=torch.tensor(list(query_pos), **i32), pages=pages, max_pages=max_pages,
+                page_size=page_size)

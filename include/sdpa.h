@@ -128,6 +128,50 @@ sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
                           void *workspace, size_t workspace_bytes,
                           void *out, int dtype, void *stream);
 
+/*
+ * Paged attention over a shared K/V page cache (ruDNN guide section 9): packed
+ * queries of several sequences, prefill chunks and decode alike, each query
+ * attending to the cached keys of its own sequence through that sequence's
+ * page table.  Split-KV with the same log-sum-exp merge as sdpa_decode.
+ *   q            device [queries, Hq, D]
+ *   k_cache      device [pages, page_size, Hkv, D]
+ *   v_cache      device [pages, page_size, Hkv, D]
+ *   block_tables device int32 [num_seqs, max_pages_per_seq]: logical key j of
+ *                sequence s is slot j % page_size of physical page
+ *                block_tables[s][j / page_size]
+ *   seq_lens     device int32 [num_seqs]: cached keys of each sequence
+ *   query_seq    device int32 [queries]: the sequence of each query
+ *   query_pos    device int32 [queries]: zero-based absolute position of each
+ *                query within its sequence (used by the causal flag)
+ *   max_seq_len  host: bound on seq_lens; splits cover [0, max_seq_len) in
+ *                chunks of ceil(max_seq_len / num_splits) keys rounded up to a
+ *                multiple of 16.  Must be <= max_pages_per_seq * page_size.
+ *   causal       0: query t sees keys j < seq_lens[s]; 1: additionally only
+ *                j <= query_pos[t] (absolute positions: a chunk of new queries
+ *                at the end of a sequence is aligned bottom-right)
+ *   num_splits   1..SDPA_MAX_SPLITS
+ *   workspace    device buffer of at least
+ *                sdpa_decode_workspace_size(queries, Hq, D, num_splits) bytes
+ *                (same layout as sdpa_decode's with B = queries)
+ *   out          device [queries, Hq, D]
+ * Two kernels are enqueued on stream: the split pass, then the merge.
+ * Supported: dtype SDPA_BF16, D in {64, 128}, page_size a multiple of 16
+ * (SDPA_ERR_UNSUPPORTED otherwise).
+ * Not checked (device data), with the kernels' behaviour outside the
+ * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
+ * [0, num_seqs), a negative query_pos under the causal flag, or a sequence
+ * with no cached key leave the query with no visible key (NaN output row); a
+ * block_tables entry outside [0, pages) is never read: its keys are hidden.
+ */
+sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const void *v_cache,
+                                   int64_t queries, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int64_t pages, int64_t page_size, const int32_t *block_tables,
+                                   int64_t num_seqs, int64_t max_pages_per_seq,
+                                   const int32_t *seq_lens, const int32_t *query_seq,
+                                   const int32_t *query_pos, int64_t max_seq_len, float scale,
+                                   int causal, int num_splits, void *workspace,
+                                   size_t workspace_bytes, void *out, int dtype, void *stream);
+
 /* Static English name of a status code; never NULL. */
 const char *sdpa_status_string(int status);
 

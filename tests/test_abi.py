@@ -130,3 +130,43 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sd.sdpa_forward(q, q, q, 0.125)
+
+
+FAKE_T = ctypes.c_void_p(0x7a000000)
+FAKE_L = ctypes.c_void_p(0x7b000000)
+FAKE_S = ctypes.c_void_p(0x7c000000)
+FAKE_P = ctypes.c_void_p(0x7d000000)
+
+
+def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_size=16,
+          tables=FAKE_T, num_seqs=2, max_pages=50, seq_lens=FAKE_L, qseq=FAKE_S, qpos=FAKE_P,
+          max_seq_len=800, scale=0.1, causal=0, splits=4, ws=FAKE_W, ws_bytes=None, out=FAKE_O,
+          dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.sdpa_decode_workspace_size(nq, Hq, D, splits)
+    return lib.sdpa_paged_attention(q, k, v, nq, Hq, Hkv, D, pages, page_size, tables, num_seqs,
+                                    max_pages, seq_lens, qseq, qpos, max_seq_len, scale, causal,
+                                    splits, ws, ws_bytes, out, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(tables=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(qpos=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(pages=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(max_seq_len=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(scale=float("nan")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(causal=2), sd.SDPA_ERR_INVALID_ARGUMENT, "causal"),
+    (dict(splits=33, ws_bytes=1 << 30), sd.SDPA_ERR_INVALID_ARGUMENT, "num_splits"),
+    (dict(max_seq_len=801), sd.SDPA_ERR_INVALID_ARGUMENT, "capacity"),
+    (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=64), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(out=ctypes.c_void_p(0x7a000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(D=96), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
+])
+def test_paged_rejects(kw, status, needle):
+    assert paged(**kw) == status
+    assert needle in sd.last_error()

@@ -1,0 +1,176 @@
+"""GPU parity of sdpa_paged_attention (paged K/V cache, packed queries) against
+the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_scaled_dot_amd as sd
+import oracle as O
+from exact_scaled_dot_amd.workloads import draw_paged, draw_qkv
+from parity import compare, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run_paged(seq_lens, query_seq, query_pos, Hq, Hkv, D, page_size, causal, splits, seed,
+              max_seq_len=None, scale=None, tables=None):
+    inp = draw_paged(seq_lens, query_seq, query_pos, Hq, Hkv, D, page_size, torch.bfloat16, seed, DEV)
+    if tables is not None:
+        inp["block_tables"] = torch.tensor(tables, dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if max_seq_len is None:
+        max_seq_len = inp["block_tables"].shape[1] * page_size
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale,
+                                  causal, max_seq_len, splits)
+    torch.cuda.synchronize()
+    return inp, out, scale
+
+
+def oracle_of(inp, scale, causal):
+    return O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                             inp["block_tables"].cpu().numpy(), inp["seq_lens"].cpu().numpy(),
+                             inp["query_seq"].cpu().numpy(), inp["query_pos"].cpu().numpy(),
+                             scale, causal)
+
+
+def check(seq_lens, query_seq, query_pos, Hq, Hkv, D, page_size, causal, splits, seed, **kw):
+    inp, out, scale = run_paged(seq_lens, query_seq, query_pos, Hq, Hkv, D, page_size, causal,
+                                splits, seed, **kw)
+    ref = oracle_of(inp, scale, causal)
+    what = "lens=%s ps=%d Hq=%d Hkv=%d D=%d causal=%d splits=%d" % (
+        seq_lens, page_size, Hq, Hkv, D, causal, splits)
+    return compare(to64(out), ref, torch.bfloat16, what)
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 64])
+@pytest.mark.parametrize("splits", [1, 4, 32])
+def test_paged_decode(page_size, splits):
+    # one query per sequence at its last position; ragged lengths around the
+    # 16-key step and page boundaries
+    lens = [1, 15, 16, 17, 100, 1000]
+    n = len(lens)
+    for causal in (False, True):
+        check(lens, range(n), [x - 1 for x in lens], 8, 2, 128, page_size, causal, splits,
+              seed=page_size + splits + causal)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_paged_decode_group_sizes(D, G):
+    lens = [300, 77]
+    check(lens, [0, 1], [299, 76], 2 * G, 2, D, 16, True, 5, seed=G + D)
+
+
+def test_paged_packed_prefill():
+    # every position of three sequences as packed queries, causal by position
+    lens = [37, 5, 100]
+    qs = [s for s, n in enumerate(lens) for _ in range(n)]
+    qp = [i for n in lens for i in range(n)]
+    check(lens, qs, qp, 4, 2, 128, 16, True, 3, seed=11)
+    check(lens, qs, qp, 4, 4, 64, 32, False, 1, seed=12)
+
+
+def test_paged_chunked_prefill_bottom_right():
+    # 20 new queries at the end of a 300-key sequence and 7 at the end of a
+    # 1000-key one, interleaved in the packed order
+    qs = [0, 1] * 7 + [0] * 13
+    qp = [280 + i // 2 if i % 2 == 0 else 993 + i // 2 for i in range(14)] + list(range(287, 300))
+    check([300, 1000], qs, qp, 8, 2, 128, 16, True, 8, seed=13)
+
+
+def test_paged_random_positions_and_order():
+    rng = np.random.default_rng(14)
+    lens = [64, 513, 2000, 16]
+    qs = rng.integers(0, 4, size=40)
+    qp = [int(rng.integers(0, lens[s])) for s in qs]
+    for causal in (False, True):
+        check(lens, qs.tolist(), qp, 8, 1, 128, 16, causal, 7, seed=15 + causal)
+
+
+def test_paged_empty_and_out_of_range():
+    # seq_len 0, a query of an unknown sequence, and a causal query at a
+    # negative position see no key: NaN rows, the rest unaffected
+    inp, out, scale = run_paged([0, 50, 30], [0, 1, 2, 1, 1], [0, 49, 29, 10, 20], 4, 2, 128, 16,
+                                True, 4, seed=16)
+    inp["query_seq"][3] = 7
+    inp["query_pos"][4] = -1
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, True,
+                                  64, 4)
+    torch.cuda.synchronize()
+    got = to64(out)
+    assert np.isnan(got[[0, 3, 4]]).all()
+    keep = [1, 2]
+    ref = O.paged_attention(to64(inp["q"])[keep], to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            inp["block_tables"].cpu().numpy(), inp["seq_lens"].cpu().numpy(),
+                            inp["query_seq"].cpu().numpy()[keep], inp["query_pos"].cpu().numpy()[keep],
+                            scale, True)
+    compare(got[keep], ref, torch.bfloat16, "valid rows next to empty ones")
+
+
+def test_paged_invalid_table_entries_hide_their_keys():
+    # logical pages 1 and 3 of a 64-key sequence point outside the cache: the
+    # kernel must not read them and must hide their keys (non-causal, so the
+    # result is the attention over logical pages 0 and 2 alone)
+    inp, out, scale = run_paged([64], [0, 0], [63, 63], 4, 2, 128, 16, False, 2, seed=17,
+                                tables=[[0, -1, 2, 99999]])
+    valid = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                              np.array([[0, 2]]), np.array([32]), np.array([0, 0]),
+                              np.array([31, 31]), scale, False)
+    compare(to64(out), valid, torch.bfloat16, "invalid pages hidden")
+
+
+def test_paged_decode_matches_dense_decode_bitwise():
+    # Same keys, contiguous pages in order, splits of a multiple of 16 keys:
+    # the paged and the dense decode run the same arithmetic.
+    B, Hq, Hkv, Sk, D, ps = 3, 16, 4, 1024, 128, 64
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, torch.bfloat16, 18, DEV)
+    kc = torch.cat([k[b].permute(1, 0, 2).reshape(Sk // ps, ps, Hkv, D) for b in range(B)]).contiguous()
+    vc = torch.cat([v[b].permute(1, 0, 2).reshape(Sk // ps, ps, Hkv, D) for b in range(B)]).contiguous()
+    tables = torch.arange(B * Sk // ps, dtype=torch.int32, device=DEV).view(B, Sk // ps)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    lens = torch.full((B,), Sk, **i32)
+    got = sd.sdpa_paged_attention(q[:, :, 0].contiguous(), kc, vc, tables, lens,
+                                  torch.arange(B, **i32), torch.full((B,), Sk - 1, **i32), 0.09,
+                                  True, Sk, 8)
+    ref = sd.sdpa_decode(q, k, v, 0.09, None, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref[:, :, 0])
+
+
+def test_paged_deterministic():
+    inp, a, scale = run_paged([5000, 3000], [0, 1], [4999, 2999], 32, 8, 128, 16, True, 32, seed=19)
+    b = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, True,
+                                inp["block_tables"].shape[1] * 16, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_full_size_paged_decode_sampled():
+    # the serving shape next to the dense decode workload: 64 sequences of
+    # 32768 cached keys in 16-key pages, shuffled; check 4 whole queries
+    n, L = 64, 32768
+    inp = draw_paged([L] * n, range(n), [L - 1] * n, 32, 8, 128, 16, torch.bfloat16, 20, DEV,
+                     extra_pages=0)
+    scale = 1.0 / math.sqrt(128)
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, True,
+                                  L, 32)
+    torch.cuda.synchronize()
+    got = to64(out)
+    tables = inp["block_tables"].cpu().numpy()
+    for t in (0, 1, 31, 63):
+        pg = tables[t]
+        kq = to64(inp["k_cache"][torch.as_tensor(pg, device=DEV).long()])  # this query's pages only
+        vq = to64(inp["v_cache"][torch.as_tensor(pg, device=DEV).long()])
+        ref = O.paged_attention(to64(inp["q"][t:t + 1]), kq, vq, np.arange(len(pg))[None, :],
+                                np.array([L]), np.array([0]), np.array([L - 1]), scale, True)
+        compare(got[t:t + 1], ref, torch.bfloat16, "paged decode query %d" % t)
