@@ -38,6 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 PREFILL = "bf16_causal_b4_h16_s4096_d128"
 PADDED = "bf16_gqa32x8_padded_b2_s8192_d128"
 DECODE = "bf16_gqa32x8_decode_b64_sk32768_d128"
+PAGE_SIZE = 16                      # paged decode: keys per cache page
 
 
 def kernel_source_hash(name):
@@ -132,10 +133,14 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     if fwd in fetch:  # a full step launches the causal prefill, then the padded one
         out["prefill"] = entry(fwd, "forward.hip", fetch[fwd][0::2], write[fwd][0::2])
         out["padded"] = entry(fwd, "forward.hip", fetch[fwd][1::2], write[fwd][1::2])
+    # A full step runs the dense decode, then the paged one: their split and
+    # merge dispatches alternate.
     for key, name in (("decode_split", "decode_split_bf16_kernel"),
                       ("decode_merge", "decode_merge_bf16_kernel")):
         if name in fetch:
-            out[key] = entry(name, "decode.hip", fetch[name], write[name])
+            out[key] = entry(name, "decode.hip", fetch[name][0::2], write[name][0::2])
+            out["paged_" + key.split("_")[1]] = entry(name, "decode.hip", fetch[name][1::2],
+                                                      write[name][1::2])
     return out
 
 
@@ -146,7 +151,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["prefill", "padded", "decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged"], default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -170,7 +175,7 @@ def main():
     import torch
 
     import exact_scaled_dot_amd as sd
-    from exact_scaled_dot_amd.workloads import WORKLOADS, make_inputs
+    from exact_scaled_dot_amd.workloads import WORKLOADS, draw_paged, make_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -186,6 +191,14 @@ def main():
     ws = torch.empty(sd.sdpa_decode_workspace_size(wd.B, wd.Hq, wd.D, wd.num_splits),
                      dtype=torch.uint8, device=dev)
     lens_g = ig["key_lens"].cpu().tolist()
+    # Paged decode: the decode workload's shape (B sequences of Sk cached keys,
+    # Hq/Hkv heads, D) in shuffled 16-key pages, one query per sequence at its
+    # last position, causal, same split count.
+    ipg = None
+    if args.only in (None, "paged"):
+        ipg = draw_paged([wd.Sk] * wd.B, range(wd.B), [wd.Sk - 1] * wd.B, wd.Hq, wd.Hkv, wd.D,
+                         PAGE_SIZE, wd.dtype, wd.seed, dev, extra_pages=0)
+        out_pg = torch.empty_like(ipg["q"])
     torch.cuda.synchronize()
 
     calls = {
@@ -195,8 +208,12 @@ def main():
                                           sd.MASK_KEY_PADDING, ig["key_lens"], out_g),
         "decode": lambda: sd.sdpa_decode(idd["q"], idd["k"], idd["v"], wd.scale, None,
                                          wd.num_splits, ws, out_d),
+        "paged": lambda: sd.sdpa_paged_attention(ipg["q"], ipg["k_cache"], ipg["v_cache"],
+                                                 ipg["block_tables"], ipg["seq_lens"],
+                                                 ipg["query_seq"], ipg["query_pos"], wd.scale,
+                                                 True, wd.Sk, wd.num_splits, ws, out_pg),
     }
-    order = [args.only] if args.only else ["prefill", "padded", "decode"]
+    order = [args.only] if args.only else ["prefill", "padded", "decode", "paged"]
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -267,15 +284,31 @@ def main():
                                       "traffic": stored_traffic("decode_split", "decode.hip"),
                                       "kernel": "decode_split_bf16_kernel<128> + merge",
                                       "bytes_per_launch": by}}
-    if "value" not in rec:  # --only padded / --only decode: report that call
-        if "decode" in rec:
+    if "paged" in ms:
+        kv_bytes = 2 * wd.B * wd.Hkv * wd.Sk * wd.D * 2
+        by = kv_bytes + 2 * wd.B * wd.Hq * wd.D * 2 + ipg["block_tables"].numel() * 4
+        gbs = by / (ms["paged"] * 1e-3) / 1e9
+        rec["paged"] = {"workload": "bf16_gqa32x8_paged_decode_b64_sk32768_d128_page16",
+                        "ms": round(ms["paged"], 4), "value": round(gbs, 1), "unit": "GB/s",
+                        "page_size": PAGE_SIZE, "pages": ipg["pages"],
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                     "traffic": stored_traffic("paged_split", "decode.hip"),
+                                     "kernel": "decode_split_bf16_kernel<128, paged> + merge",
+                                     "bytes_per_launch": by}}
+    if "value" not in rec:  # --only padded / decode / paged: report that call
+        if "paged" in rec:
+            rec.update({"value": rec["paged"]["value"], "unit": "GB/s"})
+            rec["config"] = {"workload": rec["paged"]["workload"]}
+        elif "decode" in rec:
             rec.update({"value": rec["decode"]["value"], "unit": "GB/s"})
             rec["config"] = {"workload": wd.name}
         else:
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd
+    del ip, ig, idd, ipg
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

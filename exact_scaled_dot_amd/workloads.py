@@ -121,13 +121,12 @@ def draw_paged(seq_lens, query_seq, query_pos, Hq, Hkv, D, page_size, dtype, see
     vc = torch.randn(pages, page_size, Hkv, D, generator=g, device=device, dtype=torch.float32).to(dtype)
     gc = torch.Generator(device="cpu")
     gc.manual_seed(seed + 104729)
-    perm = torch.randperm(pages, generator=gc).tolist()
+    perm = torch.randperm(pages, generator=gc).to(torch.int32)
     tables = torch.full((len(seq_lens), max_pages), -1, dtype=torch.int32)
     nxt = 0
     for s, n in enumerate(need):
-        for lp in range(n):
-            tables[s, lp] = perm[nxt]
-            nxt += 1
+        tables[s, :n] = perm[nxt:nxt + n]
+        nxt += n
     i32 = dict(dtype=torch.int32, device=device)
     return dict(q=q, k_cache=kc, v_cache=vc, block_tables=tables.to(device),
                 seq_lens=torch.tensor(seq_lens, **i32), query_seq=torch.tensor(list(query_seq), **i32),
