@@ -282,8 +282,28 @@ def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq, quer
     return o
 
 
+def chunk_positions(cu_seqlens_q, seq_lens):
+    """Sequence and absolute position of every packed query of a prefill chunk.
+
+    Queries cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 belong to sequence s and are
+    its last n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s] tokens: query i of the
+    sequence sits at position seq_lens[s] - n_s + i (the new tokens are
+    appended after the cached ones, ruDNN user guide section 9: positions are
+    zero-based absolute positions within each sequence).  Returns
+    (query_seq, query_pos) for paged_attention.
+    """
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    qs, qp = [], []
+    for s in range(len(cu) - 1):
+        n = int(cu[s + 1] - cu[s])
+        qs.extend([s] * n)
+        qp.extend(int(seq_lens[s]) - n + i for i in range(n))
+    return np.array(qs, dtype=np.int64), np.array(qp, dtype=np.int64)
+
+
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KEY_PADDING", "visible_rows", "attend",
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
     "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
+    "chunk_positions",
 ]

@@ -521,3 +521,14 @@ def test_paged_brute_force_tiny(causal):
                 ref = math.fsum(w[i] * vc[tables[s][j // ps], j % ps, 0, d]
                                 for i, j in enumerate(keys)) / tot
                 assert got[t, h, d] == pytest.approx(ref, abs=1e-13)
+
+
+def test_chunk_positions_closed_form():
+    # full prefills (chunk = whole sequence) are positions 0..n-1; a chunk of n
+    # new tokens after c cached ones is c..c+n-1; an empty chunk contributes
+    # nothing
+    qs, qp = O.chunk_positions([0, 3, 3, 8, 9], [3, 10, 5, 40])
+    assert qs.tolist() == [0, 0, 0, 2, 2, 2, 2, 2, 3]
+    assert qp.tolist() == [0, 1, 2, 0, 1, 2, 3, 4, 39]
+    qs, qp = O.chunk_positions([0, 4], [100])
+    assert qp.tolist() == [96, 97, 98, 99]
