@@ -130,6 +130,25 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, u
         r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, 0);
 }
 
+// Same with a wave-uniform scalar offset added to the address.  The buffer
+// range check covers voff but not soff.
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff,
+                                       uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, soff, 0, 0);
+}
+
+// 32-bit LDS store / 4 x 32-bit load with an alias scope of their own (see
+// lds_read_tr16x4).
+__device__ __forceinline__ void lds_store_i32(int* __restrict__ p, int v) {
+    *(__attribute__((address_space(3))) int*)((__attribute__((address_space(3))) char*)p) = v;
+}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 lds_load_i32x4(const int* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) i32x4*)(
+        (const __attribute__((address_space(3))) char*)p);
+}
+
 // Raw buffer resource over [base, base + bytes); loads beyond it return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -147,12 +166,24 @@ struct Bf16Geo {
     __device__ static int fv(int r) { return 4 * ((r / RPW) % (4 / RPW)); }
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a) {
+// PAGED: prefill chunks over a page cache.  Workgroup = (sequence, head,
+// 128-row block of the sequence's chunk); the chunk's rows are packed rows
+// cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q / out ([rows, Hq, D]) and row i
+// sits at absolute position seq_lens[s] - n_s + i (n_s = chunk length).  In a
+// 64-key tile wave w loads keys 16w .. 16w+15, which lie in one page (page
+// size a multiple of 16): one table lookup per wave and tile, a buffer
+// resource over that page, the wave-uniform row offset in the scalar offset.
+// A table entry outside the cache is never read; its 16 keys are hidden
+// (validity shared through LDS).
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
+    ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
     using L = Bf16Geo<D>;
     // Two K stages then two V stages.  K runs one tile ahead of V: while the
     // weights of tile j are formed, the scores of tile j+1 are computed.
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE];
+    // (Paged: then the validity of each K stage's four 16-key groups.)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE + (PAGED ? 16 : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -161,56 +192,123 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     const int hg = lane >> 5;  // which half of the wave
 
     const TileInfo ti = decode_tile(a);
-    const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
-    const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * D;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kvh;
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kvh;
-    uint16_t* op = static_cast<uint16_t*>(a.out) + bh * a.Sq * D;
+    const uint16_t* kp;
+    const uint16_t* vp;
+    const uint16_t* qbase;
+    uint16_t* op;
+    int nrows, qoff, kv_lim, kv_end;
+    uint32_t qstride;  // bytes between consecutive query rows
+    if (PAGED) {
+        // This workgroup's rows of sequence b's chunk (bounds clamped to the
+        // packed rows so no store can leave out).
+        const int r0 = min(max(cu_q[ti.b], 0), p.total_q);
+        const int r1 = min(max(cu_q[ti.b + 1], r0), p.total_q);
+        nrows = r1 - r0;
+        if (ti.q0 >= nrows) return;  // the whole workgroup: no barrier reached yet
+        kv_lim = min(seq_lens[ti.b], a.Sk);
+        qoff = kv_lim - nrows;  // absolute position of the chunk's first row
+        kv_end = kv_lim;
+        if (a.causal) kv_end = min(kv_end, qoff + ti.q0 + kBr);
+        const int64_t rb = ((int64_t)r0 * a.Hq + ti.h) * D;
+        qbase = static_cast<const uint16_t*>(a.q) + rb;
+        op = static_cast<uint16_t*>(a.out) + rb;
+        qstride = (uint32_t)a.Hq * D * 2;
+        kp = static_cast<const uint16_t*>(a.k);
+        vp = static_cast<const uint16_t*>(a.v);
+    } else {
+        const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
+        const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * D;
+        kp = static_cast<const uint16_t*>(a.k) + kvh;
+        vp = static_cast<const uint16_t*>(a.v) + kvh;
+        qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * D;
+        op = static_cast<uint16_t*>(a.out) + bh * a.Sq * D;
+        qstride = (uint32_t)D * 2;
+        nrows = a.Sq;
+        qoff = 0;
+        key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
+    }
 
     const int qw = ti.q0 + wave * 32;  // first query row of this wave
     const int qi = qw + l32;           // this lane's query row
-    int kv_lim, kv_end;
-    key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
     const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
     // Under a causal mask a wave stops taking part once a tile starts past
     // its last row (and never resumes: tiles only move forward).
-    const int wave_tiles = a.causal ? min(ntiles, (qw + 31) / kBc + 1) : ntiles;
+    const int wave_tiles = a.causal ? max(0, min(ntiles, (qoff + qw + 31) / kBc + 1)) : ntiles;
 
     // Q fragment for the B operand of S^T = K Q^T: lane holds Q[qi][16t + 8hg .. +7]
-    // (rows >= Sq read as zeros).
+    // (rows >= nrows read as zeros).
     bf16x8 qr[D / 16];
     {
-        const __amdgpu_buffer_rsrc_t qrs =
-            make_rsrc(static_cast<const uint16_t*>(a.q) + bh * a.Sq * D, (uint32_t)a.Sq * D * 2);
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, (uint32_t)nrows * qstride);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
             qr[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
-                qrs, (qi * D + 16 * t + 8 * hg) * 2, 0, 0));
+                qrs, qi * qstride + (16 * t + 8 * hg) * 2, 0, 0));
     }
 
     // DMA source offsets (bytes, relative to the tile's first key).  DMA load i
     // of this wave fills LDS bytes [1024*(DMA*wave + i), +1024) of a tile;
     // lane l's 16 B land at 16-byte slot p = 64*(DMA*wave + i) + l.
+    // (Paged: relative to the wave's 16-key group, rows Hkv*D*2 bytes apart.)
+    // The wave's LDS rows are 16*wave .. 16*wave+15, i.e. keys of the same group.
+    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * D * 2 : (uint32_t)D * 2;
+    const int row_base = PAGED ? 16 * wave : 0;
     uint32_t koff[L::DMA], voff[L::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
-        const int p = 64 * (L::DMA * wave + i) + lane;
-        const int row = p / L::CPR, pc = p % L::CPR;
-        koff[i] = k_lds_row(row) * D * 2 + ((pc ^ L::fk(row)) * 16);
-        voff[i] = row * D * 2 + ((pc ^ L::fv(row)) * 16);
+        const int q = 64 * (L::DMA * wave + i) + lane;
+        const int row = q / L::CPR, pc = q % L::CPR;
+        koff[i] = (k_lds_row(row) - row_base) * row_bytes + ((pc ^ L::fk(row)) * 16);
+        voff[i] = (row - row_base) * row_bytes + ((pc ^ L::fv(row)) * 16);
     }
-    // Resources start at the tile's first key; num_records ends at key Sk.
+    // Paged: resource over the page of keys j0 + 16*wave .. +15 (zero records
+    // when the table entry is outside the cache) and the group's scalar
+    // offset inside it; the validity goes to LDS for the mask.
+    int* const kvalid = reinterpret_cast<int*>(smem + 4 * L::TILE);  // [K stage][group]
+    auto page_of = [&](int j0, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv,
+                       uint32_t& soff) -> bool {
+        const int key = j0 + 16 * wave;
+        const int lp = key / p.page_size;
+        const int pg = lp < p.max_pages ? tables[(int64_t)ti.b * p.max_pages + lp] : -1;
+        const bool ok = pg >= 0 && pg < p.pages;
+        const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * D : 0;
+        const uint32_t bytes = ok ? (uint32_t)p.page_size * row_bytes : 0u;
+        rk = make_rsrc(kp + off, bytes);
+        rv = make_rsrc(vp + off, bytes);
+        soff = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * D * 2;
+        return ok;
+    };
+    // Dense: resources start at the tile's first key; num_records ends at key Sk.
     auto issue_k = [&](int j0, int stage) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(kp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
         uint16_t* dst = smem + stage * L::TILE + 512 * L::DMA * wave;
+        if (PAGED) {
+            __amdgpu_buffer_rsrc_t rk, rv;
+            uint32_t soff;
+            const bool ok = page_of(j0, rk, rv, soff);
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, koff[i]);
+            for (int i = 0; i < L::DMA; ++i) dma16s(rk, dst + 512 * i, koff[i], soff);
+            if (lane == 0) lds_store_i32(kvalid + 4 * stage + wave, ok ? 1 : 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(kp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
+#pragma unroll
+            for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, koff[i]);
+        }
     };
     auto issue_v = [&](int j0, int stage) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(vp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
         uint16_t* dst = smem + (2 + stage) * L::TILE + 512 * L::DMA * wave;
+        if (PAGED) {
+            __amdgpu_buffer_rsrc_t rk, rv;
+            uint32_t soff;
+            page_of(j0, rk, rv, soff);
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
+            for (int i = 0; i < L::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], soff);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(vp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
+#pragma unroll
+            for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
+        }
     };
 
     // Lane-constant LDS read offsets (bf16 elements).
@@ -270,17 +368,43 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     };
 
     // Hide keys of tile j0 that a row may not see (causal / key limit).
+    // Row qi sits at absolute position qoff + qi (dense: qoff = 0).  Paged:
+    // keys of a 16-key group whose table entry is invalid are hidden too.
     auto mask_tile = [&](int j0, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
-        const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
+        bool need_mask = (a.causal && j0 + kBc - 1 > qoff + qw) || (j0 + kBc > kv_lim);
+        int vmask = 15;  // bit g: keys 16g .. 16g+15 of the tile come from a valid page
+        if (PAGED) {
+            const i32x4 vg = lds_load_i32x4(kvalid + 4 * ((j0 / kBc) & 1));
+            vmask = __builtin_amdgcn_readfirstlane((vg[0] ? 1 : 0) | (vg[1] ? 2 : 0) |
+                                                   (vg[2] ? 4 : 0) | (vg[3] ? 8 : 0));
+            need_mask = need_mask || vmask != 15;
+        }
         if (need_mask) {
+            if constexpr (PAGED) {
+                // A group on an invalid page gets a -inf bias (wave-uniform, so
+                // this stays straight-line code: an add and a select per score).
+                float gbias[4];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+                for (int g = 0; g < 4; ++g) gbias[g] = ((vmask >> g) & 1) ? 0.f : -INFINITY;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
-                    const bool hide = key >= kv_lim || (a.causal && key > qi);
-                    if (hide) sacc[kb2][r] = -INFINITY;
-                }
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
+                        const bool hide = key >= kv_lim || (a.causal && key > qoff + qi);
+                        const float v = sacc[kb2][r] + gbias[2 * kb2 + (r >> 3)];
+                        sacc[kb2][r] = hide ? -INFINITY : v;
+                    }
+            } else {
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = j0 + 32 * kb2 + 16 * (r >> 3) + 8 * hg + (r & 7);
+                        const bool hide = key >= kv_lim || (a.causal && key > qi);
+                        if (hide) sacc[kb2][r] = -INFINITY;
+                    }
+            }
         }
     };
     // Row max of a (masked) score tile; moves the reference max when needed.
@@ -398,8 +522,8 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(ForwardArgs a
     // dim 32*db + 8*(r/4) + 4*hg + r%4 of row qi.
     const float lt = l_run + swap_half_wave(l_run);
     const float inv = 1.f / lt;
-    if (qi < a.Sq) {
-        uint16_t* orow = op + (int64_t)qi * D;
+    if (qi < nrows) {
+        uint16_t* orow = op + (int64_t)qi * (qstride / 2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -571,16 +695,27 @@ inline dim3 forward_grid(const ForwardArgs& a) {
     return dim3((unsigned)(nqb * a.B * a.Hq));
 }
 
-}  // namespace
-
-hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s) {
+template <bool PAGED>
+hipError_t launch_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
     if (a.D == 64)
-        hipLaunchKernelGGL(forward_bf16_kernel<64>, forward_grid(a), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED>), forward_grid(a), dim3(kThreads), 0, s, a,
+                           p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else if (a.D == 128)
-        hipLaunchKernelGGL(forward_bf16_kernel<128>, forward_grid(a), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED>), forward_grid(a), dim3(kThreads), 0, s,
+                           a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s) {
+    return launch_bf16<false>(a, PagedArgs{}, s);
+}
+
+hipError_t launch_paged_prefill_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
+    return launch_bf16<true>(a, p, s);
 }
 
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s) {

@@ -38,14 +38,18 @@ struct DecodeArgs {
 struct PagedArgs {
     const int32_t* block_tables;  // [num_seqs, max_pages]
     const int32_t* seq_lens;      // [num_seqs]
-    const int32_t* query_seq;     // [queries]
-    const int32_t* query_pos;     // [queries]
+    const int32_t* query_seq;     // [queries]      (per-query attention)
+    const int32_t* query_pos;     // [queries]      (per-query attention)
+    const int32_t* cu_seqlens_q;  // [num_seqs + 1] (prefill chunks)
     int num_seqs, max_pages, pages, page_size;
+    int total_q;                  // packed query rows (prefill chunks)
     bool causal;
 };
 
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
+// Paged prefill chunks: a.B = num_seqs, a.Sq = longest chunk, a.Sk = max_seq_len.
+hipError_t launch_paged_prefill_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
 

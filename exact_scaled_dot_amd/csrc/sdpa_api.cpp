@@ -309,4 +309,94 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     return hip_status(e, "sdpa_paged_attention launch");
 }
 
+sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                 int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t pages,
+                                 int64_t page_size, const int32_t* block_tables, int64_t num_seqs,
+                                 int64_t max_pages_per_seq, const int32_t* seq_lens,
+                                 const int32_t* cu_seqlens_q, int64_t max_q, int64_t max_seq_len,
+                                 float scale, int causal, void* out, int dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !cu_seqlens_q)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || pages < 1 || page_size < 1 || num_seqs < 1 ||
+        max_pages_per_seq < 1 || max_q < 1 || max_seq_len < 1)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "every size must be >= 1 (total_q=%lld Hq=%lld Hkv=%lld D=%lld pages=%lld "
+                    "page_size=%lld num_seqs=%lld max_pages_per_seq=%lld max_q=%lld "
+                    "max_seq_len=%lld)",
+                    (long long)total_q, (long long)Hq, (long long)Hkv, (long long)D, (long long)pages,
+                    (long long)page_size, (long long)num_seqs, (long long)max_pages_per_seq,
+                    (long long)max_q, (long long)max_seq_len);
+    if (Hq % Hkv != 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                    (long long)Hq, (long long)Hkv);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if (dtype != SDPA_F32 && dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (causal != 0 && causal != 1)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+    int64_t cap = 0;
+    if (!mul_ok(max_pages_per_seq, page_size, &cap) || max_seq_len > cap)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "max_seq_len (%lld) exceeds the page table capacity max_pages_per_seq * "
+                    "page_size",
+                    (long long)max_seq_len);
+    const int64_t es = elem_size(dtype);
+    const int64_t nq = numel4(total_q, Hq, D, 1), nc = numel4(pages, page_size, Hkv, D);
+    const int64_t nt = numel4(num_seqs, max_pages_per_seq, 1, 1);
+    int64_t qbytes = 0, cbytes = 0;
+    if (nq < 0 || nc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) || !mul_ok(nc, es, &cbytes))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
+    if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_cache, cbytes) ||
+        overlap(out, qbytes, v_cache, cbytes) || overlap(out, qbytes, block_tables, nt * 4) ||
+        overlap(out, qbytes, seq_lens, num_seqs * 4) ||
+        overlap(out, qbytes, cu_seqlens_q, (num_seqs + 1) * 4))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
+        max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
+    if (D != 64 && D != 128)
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
+    if (dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 only");
+    if (page_size % 16 != 0)
+        return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
+                    (long long)page_size);
+    const int64_t page_elems = numel4(page_size, Hkv, D, es);
+    const int64_t chunk_bytes = numel4(max_q + 127, Hq, D, es);  // one workgroup's Q rows
+    if (page_elems < 0 || page_elems > INT_MAX || chunk_bytes < 0 || chunk_bytes > INT_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "one page or one chunk of q exceeds 2 GiB");
+    const int64_t blocks = ((max_q + 127) / 128) * num_seqs * Hq;
+    if (blocks > INT_MAX / 256)
+        return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
+
+    sdpa::ForwardArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.key_lens = nullptr;
+    a.B = (int)num_seqs;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.Sq = (int)max_q;
+    a.Sk = (int)max_seq_len;
+    a.D = (int)D;
+    a.scale = scale;
+    a.causal = causal != 0;
+    a.padded = false;
+    sdpa::PagedArgs p{};
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.num_seqs = (int)num_seqs;
+    p.max_pages = (int)max_pages_per_seq;
+    p.pages = (int)pages;
+    p.page_size = (int)page_size;
+    p.total_q = (int)total_q;
+    p.causal = causal != 0;
+    (void)hipGetLastError();
+    const hipError_t e = sdpa::launch_paged_prefill_bf16(a, p, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sdpa_paged_prefill launch");
+}
+
 }  // extern "C"

@@ -27,7 +27,7 @@ MAX_SPLITS = 32
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
 EXPORTED = ("sdpa_forward", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
-            "sdpa_status_string", "sdpa_last_error")
+            "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
 
 _lib = None
 
@@ -60,6 +60,9 @@ def load_library():
     lib.sdpa_paged_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
                                          vp, vp, i64, ctypes.c_float, i32, i32, vp, ctypes.c_size_t,
                                          vp, i32, vp]
+    lib.sdpa_paged_prefill.restype = i32
+    lib.sdpa_paged_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp, vp,
+                                       i64, i64, ctypes.c_float, i32, vp, i32, vp]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_status_string.argtypes = [i32]
     lib.sdpa_last_error.restype = ctypes.c_char_p
@@ -219,4 +222,43 @@ def sdpa_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq,
         num_seqs, max_pages, _ptr(seq_lens), _ptr(query_seq), _ptr(query_pos), int(max_seq_len),
         float(scale), int(bool(causal)), int(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _dtype_code(q), _stream(stream)))
+    return out
+
+
+def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, scale, causal,
+                       max_q, max_seq_len, out=None, stream=None):
+    """Packed prefill chunks over a K/V page cache.
+
+    q [total_q, Hq, D]; k_cache, v_cache [pages, page_size, Hkv, D];
+    block_tables int32 [num_seqs, max_pages_per_seq]; seq_lens int32
+    [num_seqs] (the chunk included); cu_seqlens_q int32 [num_seqs + 1];
+    max_q, max_seq_len host bounds.  Row i of sequence s's chunk sits at
+    position seq_lens[s] - n_s + i.  Returns out [total_q, Hq, D].
+    """
+    _check_tensor("q", q, 3)
+    _check_tensor("k_cache", k_cache, 4)
+    _check_tensor("v_cache", v_cache, 4)
+    _check_tensor("block_tables", block_tables, 2)
+    _check_tensor("seq_lens", seq_lens, 1)
+    _check_tensor("cu_seqlens_q", cu_seqlens_q, 1)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("cu_seqlens_q", cu_seqlens_q)):
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % name)
+    nq, Hq, D = q.shape
+    pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [pages, page_size, Hkv, D] matching q")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    num_seqs, max_pages = block_tables.shape
+    if seq_lens.shape[0] != num_seqs or cu_seqlens_q.shape[0] != num_seqs + 1:
+        raise ValueError("seq_lens needs num_seqs entries and cu_seqlens_q num_seqs + 1")
+    if out is None:
+        out = torch.empty_like(q)
+    lib = load_library()
+    _check(lib.sdpa_paged_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, pages, page_size, _ptr(block_tables),
+        num_seqs, max_pages, _ptr(seq_lens), _ptr(cu_seqlens_q), int(max_q), int(max_seq_len),
+        float(scale), int(bool(causal)), _ptr(out), _dtype_code(q), _stream(stream)))
     return out

@@ -172,6 +172,44 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
                                    int causal, int num_splits, void *workspace,
                                    size_t workspace_bytes, void *out, int dtype, void *stream);
 
+/*
+ * Packed prefill chunks over the same page cache (ruDNN guide section 9:
+ * packed variable-length prefill): query-tiled, each K/V page of a sequence
+ * read once per 128 query rows of its chunk.  The queries of sequence s are
+ * the packed rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q and are the
+ * last n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s] tokens of the sequence (they
+ * are already in the cache): row i of the chunk sits at absolute position
+ * seq_lens[s] - n_s + i.  Equivalent to sdpa_paged_attention with those
+ * query_seq / query_pos.
+ *   q             device [total_q, Hq, D]
+ *   k_cache,
+ *   v_cache       device [pages, page_size, Hkv, D]
+ *   block_tables  device int32 [num_seqs, max_pages_per_seq] (as above)
+ *   seq_lens      device int32 [num_seqs]: cached keys, the chunk included
+ *   cu_seqlens_q  device int32 [num_seqs + 1]: 0 = cu[0] <= cu[1] <= ... <=
+ *                 cu[num_seqs] = total_q
+ *   max_q         host: bound on the chunk lengths (sizes the grid)
+ *   max_seq_len   host: bound on seq_lens, <= max_pages_per_seq * page_size
+ *   causal        0: every cached key of the sequence is visible; 1: only
+ *                 keys j <= the row's absolute position
+ *   out           device [total_q, Hq, D]
+ * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16, D in
+ * {64, 128}, page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
+ * Not checked (device data), with the kernel's behaviour outside the
+ * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside
+ * out is ever written); a chunk longer than max_q is only computed for its
+ * first ceil(max_q / 128) * 128 rows (the rest are not written);
+ * seq_lens above max_seq_len act as max_seq_len; rows left with no visible
+ * key are NaN; a block_tables entry outside [0, pages) is never read and its
+ * keys are hidden.
+ */
+sdpa_status_t sdpa_paged_prefill(const void *q, const void *k_cache, const void *v_cache,
+                                 int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t pages,
+                                 int64_t page_size, const int32_t *block_tables, int64_t num_seqs,
+                                 int64_t max_pages_per_seq, const int32_t *seq_lens,
+                                 const int32_t *cu_seqlens_q, int64_t max_q, int64_t max_seq_len,
+                                 float scale, int causal, void *out, int dtype, void *stream);
+
 /* Static English name of a status code; never NULL. */
 const char *sdpa_status_string(int status);
 

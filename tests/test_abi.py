@@ -170,3 +170,34 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_
 def test_paged_rejects(kw, status, needle):
     assert paged(**kw) == status
     assert needle in sd.last_error()
+
+
+FAKE_C = ctypes.c_void_p(0x7e000000)
+
+
+def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, pages=100, page_size=16,
+            tables=FAKE_T, num_seqs=3, max_pages=50, seq_lens=FAKE_L, cu=FAKE_C, max_q=200,
+            max_seq_len=800, scale=0.1, causal=1, out=FAKE_O, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    return lib.sdpa_paged_prefill(q, k, v, nq, Hq, Hkv, D, pages, page_size, tables, num_seqs,
+                                  max_pages, seq_lens, cu, max_q, max_seq_len, scale, causal, out,
+                                  dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cu=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(seq_lens=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(max_q=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(nq=-1), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(scale=float("inf")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(causal=-1), sd.SDPA_ERR_INVALID_ARGUMENT, "causal"),
+    (dict(max_seq_len=801), sd.SDPA_ERR_INVALID_ARGUMENT, "capacity"),
+    (dict(out=ctypes.c_void_p(0x7e000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(D=256), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
+])
+def test_paged_prefill_rejects(kw, status, needle):
+    assert prefill(**kw) == status
+    assert needle in sd.last_error()

@@ -174,3 +174,120 @@ def test_full_size_paged_decode_sampled():
         ref = O.paged_attention(to64(inp["q"][t:t + 1]), kq, vq, np.arange(len(pg))[None, :],
                                 np.array([L]), np.array([0]), np.array([L - 1]), scale, True)
         compare(got[t:t + 1], ref, torch.bfloat16, "paged decode query %d" % t)
+
+
+# ------------------------------------------------------------ prefill chunks
+
+def run_prefill(seq_lens, chunks, Hq, Hkv, D, page_size, causal, seed, tables=None, max_q=None,
+                scale=None):
+    nq = int(sum(chunks))
+    inp = draw_paged(seq_lens, [0] * nq, [0] * nq, Hq, Hkv, D, page_size, torch.bfloat16, seed, DEV)
+    if tables is not None:
+        inp["block_tables"] = torch.tensor(tables, dtype=torch.int32, device=DEV)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    max_q = max(chunks) if max_q is None else max_q
+    out = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                inp["seq_lens"], torch.tensor(cu, device=DEV), scale, causal,
+                                max_q, inp["block_tables"].shape[1] * page_size)
+    torch.cuda.synchronize()
+    qs, qp = O.chunk_positions(cu, seq_lens)
+    return inp, out, scale, cu, qs, qp
+
+
+def check_prefill(seq_lens, chunks, Hq, Hkv, D, page_size, causal, seed, **kw):
+    inp, out, scale, cu, qs, qp = run_prefill(seq_lens, chunks, Hq, Hkv, D, page_size, causal, seed,
+                                              **kw)
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            inp["block_tables"].cpu().numpy(), np.asarray(seq_lens), qs, qp, scale,
+                            causal)
+    what = "prefill lens=%s chunks=%s ps=%d Hq=%d Hkv=%d D=%d causal=%d" % (
+        seq_lens, chunks, page_size, Hq, Hkv, D, causal)
+    return compare(to64(out), ref, torch.bfloat16, what)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_paged_prefill_full_sequences(D, page_size):
+    lens = [300, 129, 1000]
+    check_prefill(lens, lens, 8, 2, D, page_size, True, seed=D + page_size)
+
+
+def test_paged_prefill_chunks_after_cache():
+    # chunks appended after cached history, bottom-right aligned; one sequence
+    # is a whole prefill, one a single decode-like token
+    check_prefill([500, 2000, 64, 777], [37, 256, 64, 1], 4, 4, 128, 16, True, seed=31)
+    check_prefill([500, 2000, 64, 777], [37, 256, 64, 1], 4, 4, 128, 32, False, seed=32)
+
+
+def test_paged_prefill_ragged_chunk_sizes():
+    chunks = [1, 127, 128, 129, 255, 257]
+    lens = [c + 40 * i for i, c in enumerate(chunks)]
+    check_prefill(lens, chunks, 16, 2, 128, 16, True, seed=33)
+
+
+def test_paged_prefill_grid_larger_than_chunks():
+    # max_q well above every chunk: the extra workgroups find no rows
+    check_prefill([90, 300], [90, 20], 8, 8, 64, 16, True, seed=34, max_q=700)
+
+
+def test_paged_prefill_invalid_table_entries_hide_their_keys():
+    # non-causal chunk of 10 over a 64-key sequence whose logical pages 1 and
+    # 3 point outside the cache: attention over pages 0 and 2 only
+    inp, out, scale, cu, qs, qp = run_prefill([64], [10], 4, 2, 128, 16, False, seed=35,
+                                              tables=[[0, -1, 2, 99999]])
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            np.array([[0, 2]]), np.array([32]), np.zeros(10, dtype=np.int64),
+                            np.full(10, 31), scale, False)
+    compare(to64(out), ref, torch.bfloat16, "prefill: invalid pages hidden")
+
+
+def test_paged_prefill_matches_per_query_entry_point():
+    lens, chunks = [700, 333], [200, 333]
+    inp, out, scale, cu, qs, qp = run_prefill(lens, chunks, 8, 2, 128, 16, True, seed=36)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    per_query = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                        inp["seq_lens"], torch.tensor(qs, **i32),
+                                        torch.tensor(qp, **i32), scale, True,
+                                        inp["block_tables"].shape[1] * 16, 8)
+    torch.cuda.synchronize()
+    compare(to64(out), to64(per_query), torch.bfloat16, "prefill vs per-query paged")
+
+
+def test_paged_prefill_matches_dense_prefill_bitwise():
+    # whole-sequence causal prefill on contiguous in-order pages runs the same
+    # tiles, masks and arithmetic as the dense causal forward
+    B, H, S, D, ps = 2, 4, 300, 128, 16
+    q, k, v = draw_qkv(B, H, H, S, S, D, torch.bfloat16, 37, DEV)
+    npg = -(-S // ps)
+    pad = npg * ps - S
+
+    def pages_of(t):
+        t = torch.nn.functional.pad(t.permute(0, 2, 1, 3), (0, 0, 0, 0, 0, pad))  # [B, S+pad, H, D]
+        return t.reshape(B * npg, ps, H, D).contiguous()
+
+    kc, vc = pages_of(k), pages_of(v)
+    tables = torch.arange(B * npg, dtype=torch.int32, device=DEV).view(B, npg)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    qp = q.permute(0, 2, 1, 3).reshape(B * S, H, D).contiguous()
+    got = sd.sdpa_paged_prefill(qp, kc, vc, tables, torch.full((B,), S, **i32),
+                                torch.tensor([0, S, 2 * S], **i32), 0.07, True, S, npg * ps)
+    ref = sd.sdpa_forward(q, k, v, 0.07, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(B, S, H, D).permute(0, 2, 1, 3), ref)
+
+
+@pytest.mark.slow
+def test_full_size_paged_prefill_sampled():
+    # the long causal prefill workload's shape (4 sequences x 4096, 16 heads,
+    # D 128) as whole-sequence chunks over shuffled 16-key pages; 24 rows
+    n, L, H = 4, 4096, 16
+    inp, out, scale, cu, qs, qp = run_prefill([L] * n, [L] * n, H, H, 128, 16, True, seed=38)
+    got = to64(out)
+    rng = np.random.default_rng(38)
+    rows = sorted(set([0, 1, 127, 128, L - 1, L, 2 * L + 4000, 4 * L - 1]
+                      + rng.integers(0, 4 * L, size=16).tolist()))
+    kc, vc = to64(inp["k_cache"]), to64(inp["v_cache"])
+    ref = O.paged_attention(to64(inp["q"])[rows], kc, vc, inp["block_tables"].cpu().numpy(),
+                            np.array([L] * n), qs[rows], qp[rows], scale, True)
+    compare(got[rows], ref, torch.bfloat16, "full-size paged prefill rows")
