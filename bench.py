@@ -130,9 +130,10 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
                 "hbm_bytes_per_launch": round(r + w)}
 
     fwd = "forward_bf16_kernel"
-    if fwd in fetch:  # a full step launches the causal prefill, then the padded one
-        out["prefill"] = entry(fwd, "forward.hip", fetch[fwd][0::2], write[fwd][0::2])
-        out["padded"] = entry(fwd, "forward.hip", fetch[fwd][1::2], write[fwd][1::2])
+    if fwd in fetch:  # a full step launches the causal prefill, the padded one, the paged one
+        out["prefill"] = entry(fwd, "forward.hip", fetch[fwd][0::3], write[fwd][0::3])
+        out["padded"] = entry(fwd, "forward.hip", fetch[fwd][1::3], write[fwd][1::3])
+        out["paged_prefill"] = entry(fwd, "forward.hip", fetch[fwd][2::3], write[fwd][2::3])
     # A full step runs the dense decode, then the paged one: their split and
     # merge dispatches alternate.
     for key, name in (("decode_split", "decode_split_bf16_kernel"),
@@ -151,7 +152,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged"], default=None,
+    ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill"],
+                    default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -199,6 +201,15 @@ def main():
         ipg = draw_paged([wd.Sk] * wd.B, range(wd.B), [wd.Sk - 1] * wd.B, wd.Hq, wd.Hkv, wd.D,
                          PAGE_SIZE, wd.dtype, wd.seed, dev, extra_pages=0)
         out_pg = torch.empty_like(ipg["q"])
+    # Paged prefill: the causal prefill workload's shape (B sequences of S
+    # tokens, H heads, D) as whole-sequence chunks in shuffled 16-key pages.
+    ipp = None
+    if args.only in (None, "paged_prefill"):
+        nq = wp.B * wp.Sq
+        ipp = draw_paged([wp.Sk] * wp.B, [0] * nq, [0] * nq, wp.Hq, wp.Hkv, wp.D, PAGE_SIZE,
+                         wp.dtype, wp.seed, dev, extra_pages=0)
+        ipp["cu"] = torch.arange(0, nq + 1, wp.Sq, dtype=torch.int32, device=dev)
+        out_pp = torch.empty_like(ipp["q"])
     torch.cuda.synchronize()
 
     calls = {
@@ -212,8 +223,13 @@ def main():
                                                  ipg["block_tables"], ipg["seq_lens"],
                                                  ipg["query_seq"], ipg["query_pos"], wd.scale,
                                                  True, wd.Sk, wd.num_splits, ws, out_pg),
+        "paged_prefill": lambda: sd.sdpa_paged_prefill(ipp["q"], ipp["k_cache"], ipp["v_cache"],
+                                                       ipp["block_tables"], ipp["seq_lens"],
+                                                       ipp["cu"], wp.scale, True, wp.Sq, wp.Sk,
+                                                       out_pp),
     }
-    order = [args.only] if args.only else ["prefill", "padded", "decode", "paged"]
+    order = ([args.only] if args.only else
+             ["prefill", "padded", "decode", "paged", "paged_prefill"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -297,8 +313,24 @@ def main():
                                      "traffic": stored_traffic("paged_split", "decode.hip"),
                                      "kernel": "decode_split_bf16_kernel<128, paged> + merge",
                                      "bytes_per_launch": by}}
-    if "value" not in rec:  # --only padded / decode / paged: report that call
-        if "paged" in rec:
+    if "paged_prefill" in ms:
+        fl = formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
+        tf = fl / (ms["paged_prefill"] * 1e-3) / 1e12
+        rec["paged_prefill"] = {"workload": "bf16_causal_paged_prefill_b4_h16_s4096_d128_page16",
+                                "ms": round(ms["paged_prefill"], 4), "value": round(tf, 3),
+                                "unit": "TFLOP/s", "page_size": PAGE_SIZE,
+                                "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                             "traffic": stored_traffic("paged_prefill",
+                                                                       "forward.hip"),
+                                             "kernel": "forward_bf16_kernel<128, paged>",
+                                             "flops_per_launch": fl}}
+    if "value" not in rec:  # --only padded / decode / paged / paged_prefill: report that call
+        if "paged_prefill" in rec:
+            rec.update({"value": rec["paged_prefill"]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec["paged_prefill"]["workload"]}
+        elif "paged" in rec:
             rec.update({"value": rec["paged"]["value"], "unit": "GB/s"})
             rec["config"] = {"workload": rec["paged"]["workload"]}
         elif "decode" in rec:
@@ -308,7 +340,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg
+    del ip, ig, idd, ipg, ipp
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -265,28 +265,28 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // when the table entry is outside the cache) and the group's scalar
     // offset inside it; the validity goes to LDS for the mask.
     int* const kvalid = reinterpret_cast<int*>(smem + 4 * L::TILE);  // [K stage][group]
-    auto page_of = [&](int j0, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv,
-                       uint32_t& soff) -> bool {
+    // The lookup for a tile is made when its K is issued and kept (per K
+    // stage) for its V, issued one step later.
+    int64_t pg_off[2] = {0, 0};
+    uint32_t pg_bytes[2] = {0u, 0u}, pg_soff[2] = {0u, 0u};
+    auto page_of = [&](int j0, int stage) -> bool {
         const int key = j0 + 16 * wave;
         const int lp = key / p.page_size;
         const int pg = lp < p.max_pages ? tables[(int64_t)ti.b * p.max_pages + lp] : -1;
         const bool ok = pg >= 0 && pg < p.pages;
-        const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * D : 0;
-        const uint32_t bytes = ok ? (uint32_t)p.page_size * row_bytes : 0u;
-        rk = make_rsrc(kp + off, bytes);
-        rv = make_rsrc(vp + off, bytes);
-        soff = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * D * 2;
+        pg_off[stage] = ok ? (int64_t)pg * p.page_size * a.Hkv * D : 0;
+        pg_bytes[stage] = ok ? (uint32_t)p.page_size * row_bytes : 0u;
+        pg_soff[stage] = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * D * 2;
         return ok;
     };
     // Dense: resources start at the tile's first key; num_records ends at key Sk.
     auto issue_k = [&](int j0, int stage) {
         uint16_t* dst = smem + stage * L::TILE + 512 * L::DMA * wave;
         if (PAGED) {
-            __amdgpu_buffer_rsrc_t rk, rv;
-            uint32_t soff;
-            const bool ok = page_of(j0, rk, rv, soff);
+            const bool ok = page_of(j0, stage);
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + pg_off[stage], pg_bytes[stage]);
 #pragma unroll
-            for (int i = 0; i < L::DMA; ++i) dma16s(rk, dst + 512 * i, koff[i], soff);
+            for (int i = 0; i < L::DMA; ++i) dma16s(rk, dst + 512 * i, koff[i], pg_soff[stage]);
             if (lane == 0) lds_store_i32(kvalid + 4 * stage + wave, ok ? 1 : 0);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
@@ -298,11 +298,11 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     auto issue_v = [&](int j0, int stage) {
         uint16_t* dst = smem + (2 + stage) * L::TILE + 512 * L::DMA * wave;
         if (PAGED) {
-            __amdgpu_buffer_rsrc_t rk, rv;
-            uint32_t soff;
-            page_of(j0, rk, rv, soff);
+            // K of this tile went to K stage (j0 / kBc) % 2 with the lookup.
+            const int ks = (j0 / kBc) & 1;
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + pg_off[ks], pg_bytes[ks]);
 #pragma unroll
-            for (int i = 0; i < L::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], soff);
+            for (int i = 0; i < L::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], pg_soff[ks]);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(vp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
@@ -370,15 +370,17 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // Hide keys of tile j0 that a row may not see (causal / key limit).
     // Row qi sits at absolute position qoff + qi (dense: qoff = 0).  Paged:
     // keys of a 16-key group whose table entry is invalid are hidden too.
-    auto mask_tile = [&](int j0, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+    // Paged: bit g of a tile's validity word says keys 16g .. 16g+15 come from
+    // a valid page; read once the tile's K issue is behind a barrier.
+    auto tile_validity = [&](int j0) -> int {
+        if (!PAGED) return 15;
+        const i32x4 vg = lds_load_i32x4(kvalid + 4 * ((j0 / kBc) & 1));
+        return __builtin_amdgcn_readfirstlane((vg[0] ? 1 : 0) | (vg[1] ? 2 : 0) | (vg[2] ? 4 : 0) |
+                                              (vg[3] ? 8 : 0));
+    };
+    auto mask_tile = [&](int j0, f32x16 (&sacc)[2], int vmask) __attribute__((always_inline)) {
         bool need_mask = (a.causal && j0 + kBc - 1 > qoff + qw) || (j0 + kBc > kv_lim);
-        int vmask = 15;  // bit g: keys 16g .. 16g+15 of the tile come from a valid page
-        if (PAGED) {
-            const i32x4 vg = lds_load_i32x4(kvalid + 4 * ((j0 / kBc) & 1));
-            vmask = __builtin_amdgcn_readfirstlane((vg[0] ? 1 : 0) | (vg[1] ? 2 : 0) |
-                                                   (vg[2] ? 4 : 0) | (vg[3] ? 8 : 0));
-            need_mask = need_mask || vmask != 15;
-        }
+        if (PAGED) need_mask = need_mask || vmask != 15;
         if (need_mask) {
             if constexpr (PAGED) {
                 // A group on an invalid page gets a -inf bias (wave-uniform, so
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     f32x16 sA[2], sB[2];
     if (wave_tiles > 0) {
         scores(smem, sA);
-        mask_tile(0, sA);
+        mask_tile(0, sA, tile_validity(0));
     }
     __syncthreads();  // K stage 0 is refilled with K(2) by the first step
 
@@ -492,6 +494,9 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // carries its stage base as an instruction offset and the two score
     // tiles swap roles without copies.
     auto step = [&](int jt, const int cur, f32x16 (&scur)[2], f32x16 (&snext)[2]) __attribute__((always_inline)) {
+        // Tile jt+1's validity (written when its K was issued, a barrier ago);
+        // K(jt+2)'s goes to the other slot.
+        const int vnext = tile_validity((jt + 1) * kBc);
         if (jt + 2 < ntiles) issue_k((jt + 2) * kBc, cur);
         if (jt + 1 < ntiles) issue_v((jt + 1) * kBc, cur ^ 1);
         if (jt < wave_tiles) {
@@ -508,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             }
             l_run += ps;
             accumulate(smem + (2 + cur) * L::TILE, pk);
-            if (jt + 1 < wave_tiles) mask_tile((jt + 1) * kBc, snext);
+            if (jt + 1 < wave_tiles) mask_tile((jt + 1) * kBc, snext, vnext);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA landed
         __syncthreads();
