@@ -171,7 +171,7 @@ __device__ __forceinline__ Item item_geo(const DecodeArgs& a, const PagedArgs& p
 // 16), found through the sequence's page table when the step enters a new
 // page.  A table entry outside [0, pages) is never dereferenced: its keys
 // load as zeros and are masked out.
-template <int D, bool PAGED>
+template <int D, bool PAGED, class T>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     DecodeArgs a, PagedArgs p, const int32_t* __restrict__ key_lens,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     seek(it0);
     for (int j = 0; j < L::NS - 1 && i_it < it1; ++j) issue_next();
 
-    bf16x8 qb[L::KSTEPS];
+    u32x4 qb[L::KSTEPS];
     int q_head = -1;
     int done = 0;  // steps computed
     for (int it = it0; it < it1; it += kDecWaves) {
@@ -326,8 +326,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 static_cast<const uint16_t*>(a.q) + (int64_t)head * D, (uint32_t)g.nh * D * 2);
 #pragma unroll
             for (int t = 0; t < L::KSTEPS; ++t)
-                qb[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
-                    qrs, (col * D + (D / 4) * grp + 8 * t) * 2, 0, 0));
+                qb[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (col * D + (D / 4) * grp + 8 * t) * 2,
+                                                              0, 0);
             // Take the wait for the Q loads here, once per head, not inside the
             // step loop.
 #pragma unroll
@@ -365,8 +365,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < L::KSTEPS; ++t)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_read128(stg + krd[t])),
-                                                            qb[t], s, 0, 0, 0);
+                s = mfma_16x16x32<T>(lds_read128(stg + krd[t]), qb[t], s);
             const int k0 = g.lo + kStep * st;
             if (k0 + kStep > g.hi) {
 #pragma unroll
@@ -378,16 +377,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
             // lane sum <= 2^8 bounds each by 2^8, the lazy-rescale bound; only
             // otherwise (or before the first max) take the tile max and maybe
             // move the reference.
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
             uint32_t p01, p23;
             auto weights = [&]() -> float {
                 const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-                p01 = pack_bf16x2(fast_exp2(fmaf(s[0], c, neg)), fast_exp2(fmaf(s[1], c, neg)));
-                p23 = pack_bf16x2(fast_exp2(fmaf(s[2], c, neg)), fast_exp2(fmaf(s[3], c, neg)));
-                const float ps =
-                    __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), one, 0.f, false);
-                return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), one, ps, false);
+                p01 = pack2<T>(fast_exp2(fmaf(s[0], c, neg)), fast_exp2(fmaf(s[1], c, neg)));
+                p23 = pack2<T>(fast_exp2(fmaf(s[2], c, neg)), fast_exp2(fmaf(s[3], c, neg)));
+                return sum2<T>(p23, sum2<T>(p01, 0.f));
             };
             float ps = weights();
             if (__any(ps > 256.f || m_run == -INFINITY)) {
@@ -406,14 +401,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 ps = weights();
             }
             l_run += ps;
-            const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
+            const u32x2 pb = u32x2{p01, p23};
             u32x2 vf[D / 16];
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) vf[dt] = lds_read_tr(stg + vrd[dt]);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vf[dt]), pb,
-                                                                     oacc[dt], 0, 0, 0);
+                oacc[dt] = mfma_16x16x16<T>(vf[dt], pb, oacc[dt]);
         }
 
         // Column totals: the denominator is spread over the 4 lane groups.
@@ -439,7 +433,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     }
 }
 
-template <int D>
+template <int D, class T>
 __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     constexpr int TPR = D / 4;       // threads per row, 4 dims each
     constexpr int RPB = 256 / TPR;   // rows (batch, query head) per block
@@ -463,8 +457,8 @@ __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
         acc[3] = fmaf(w, o[3], acc[3]);
     }
     // Every split empty (no visible key): M = -inf, w = NaN, and the row is NaN.
-    const uint32_t lo = pack_lo16(f32_to_bf16_bits(acc[0] / den), f32_to_bf16_bits(acc[1] / den));
-    const uint32_t hi = pack_lo16(f32_to_bf16_bits(acc[2] / den), f32_to_bf16_bits(acc[3] / den));
+    const uint32_t lo = pack_lo16(to16<T>(acc[0] / den), to16<T>(acc[1] / den));
+    const uint32_t hi = pack_lo16(to16<T>(acc[2] / den), to16<T>(acc[3] / den));
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + 4 * d4) = u32x2{lo, hi};
 }
 
@@ -483,7 +477,7 @@ hipError_t compute_units(int* n) {
     return hipSuccess;
 }
 
-template <bool PAGED>
+template <bool PAGED, class T>
 hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
     const int items = (int)decode_work_items(a.B, a.Hq, a.Hkv, a.splits);
     int cus = 0;
@@ -494,15 +488,15 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
     const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * a.D / 4 + 255) / 256));
     if (a.D == 64) {
-        hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED>), dim3(wgs), dim3(kDecThreads), 0, s,
-                           a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED, T>), dim3(wgs), dim3(kDecThreads), 0,
+                           s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
                            items);
-        hipLaunchKernelGGL(decode_merge_bf16_kernel<64>, mgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<64, T>), mgrid, dim3(256), 0, s, a);
     } else if (a.D == 128) {
-        hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED>), dim3(wgs), dim3(kDecThreads), 0, s,
-                           a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED, T>), dim3(wgs), dim3(kDecThreads), 0,
+                           s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
                            items);
-        hipLaunchKernelGGL(decode_merge_bf16_kernel<128>, mgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<128, T>), mgrid, dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }
@@ -516,12 +510,13 @@ int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits) {
     return B * Hkv * ((G + kQ - 1) / kQ) * splits;
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
-    return launch_split_and_merge<false>(a, PagedArgs{}, s);
+hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s) {
+    return f16 ? launch_split_and_merge<false, F16T>(a, PagedArgs{}, s)
+               : launch_split_and_merge<false, Bf16T>(a, PagedArgs{}, s);
 }
 
-hipError_t launch_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
-    return launch_split_and_merge<true>(a, p, s);
+hipError_t launch_paged_16bit(const DecodeArgs& a, const PagedArgs& p, bool f16, hipStream_t s) {
+    return f16 ? launch_split_and_merge<true, F16T>(a, p, s) : launch_split_and_merge<true, Bf16T>(a, p, s);
 }
 
 }  // namespace sdpa

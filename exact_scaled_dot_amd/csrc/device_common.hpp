@@ -73,4 +73,79 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return d;
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit element types of the MFMA paths (bf16 and fp16 inputs).  Operands
+// travel as raw 32-bit words; these wrappers pick the instruction.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+struct Bf16T {
+    static constexpr bool kF16 = false;
+};
+struct F16T {
+    static constexpr bool kF16 = true;
+};
+
+template <class T>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (T::kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <class T>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (T::kF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <class T>
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+    if constexpr (T::kF16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                         __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+// Two fp32 values -> packed 16-bit pair (lo = a, hi = b), round to nearest even.
+template <class T>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (T::kF16) {
+        const f16x2 r = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, r);
+    } else {
+        return pack_bf16x2(a, b);
+    }
+}
+// acc + lo + hi of a packed pair, in fp32 (v_dot2 with (1, 1)).
+template <class T>
+__device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    if constexpr (T::kF16) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+    } else {
+        const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+    }
+}
+// fp32 -> 16-bit bits in the low half, round to nearest even.
+template <class T>
+__device__ __forceinline__ uint32_t to16(float f) {
+    if constexpr (T::kF16)
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+    else
+        return f32_to_bf16_bits(f);
+}
+
 }  // namespace sdpa

@@ -175,7 +175,7 @@ struct Bf16Geo {
 // resource over that page, the wave-uniform row offset in the scalar offset.
 // A table entry outside the cache is never read; its 16 keys are hidden
 // (validity shared through LDS).
-template <int D, bool PAGED>
+template <int D, bool PAGED, class T>
 __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
@@ -237,13 +237,12 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
 
     // Q fragment for the B operand of S^T = K Q^T: lane holds Q[qi][16t + 8hg .. +7]
     // (rows >= nrows read as zeros).
-    bf16x8 qr[D / 16];
+    u32x4 qr[D / 16];
     {
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, (uint32_t)nrows * qstride);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-            qr[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
-                qrs, qi * qstride + (16 * t + 8 * hg) * 2, 0, 0));
+            qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qi * qstride + (16 * t + 8 * hg) * 2, 0, 0);
     }
 
     // DMA source offsets (bytes, relative to the tile's first key).  DMA load i
@@ -341,29 +340,29 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // 32*kb2 + 16*(r/8) + 8*hg + r%8 of the tile.
     auto scores = [&](const uint16_t* ks, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
         // K fragments are read two k-steps ahead of the MFMAs that use them.
-        constexpr int T = D / 16;
-        bf16x8 kf[3][2];
+        constexpr int NK = D / 16;  // contraction steps
+        u32x4 kf[3][2];
         auto rd = [&](int t, int slot) __attribute__((always_inline)) {
-            kf[slot][0] = *reinterpret_cast<const bf16x8*>(ks + krd[t]);
-            kf[slot][1] = *reinterpret_cast<const bf16x8*>(ks + 32 * D + krd[t]);
+            kf[slot][0] = *reinterpret_cast<const u32x4*>(ks + krd[t]);
+            kf[slot][1] = *reinterpret_cast<const u32x4*>(ks + 32 * D + krd[t]);
         };
         rd(0, 0);
         rd(1, 1);
         sacc[0] = f32x16{};
         sacc[1] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t + 2 < T) rd(t + 2, (t + 2) % 3);
+        for (int t = 0; t < NK; ++t) {
+            if (t + 2 < NK) rd(t + 2, (t + 2) % 3);
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
-                sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3][kb2], qr[t], sacc[kb2], 0, 0, 0);
+                sacc[kb2] = mfma_32x32x16<T>(kf[t % 3][kb2], qr[t], sacc[kb2]);
         }
         // Keep the read-ahead: 4 reads, then (2 MFMAs, 2 reads) per k-step.
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
+        for (int t = 0; t < NK; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-            if (t + 2 < T) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            if (t + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
     };
 
@@ -436,8 +435,6 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // multiplied into V.  Straight-line code.
     auto weights = [&](const f32x16 (&sacc)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) -> float {
         const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -445,10 +442,9 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = fast_exp2(fmaf(sacc[kb2][r], c, neg));
                 const float p1 = fast_exp2(fmaf(sacc[kb2][r + 1], c, neg));
-                pk[kb2][r >> 1] = pack_bf16x2(p0, p1);
-                const bf16x2_t pv = __builtin_bit_cast(bf16x2_t, pk[kb2][r >> 1]);
-                if (r & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps1, false);
-                else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pv, one, ps0, false);
+                pk[kb2][r >> 1] = pack2<T>(p0, p1);
+                if (r & 2) ps1 = sum2<T>(pk[kb2][r >> 1], ps1);
+                else ps0 = sum2<T>(pk[kb2][r >> 1], ps0);
             }
         return ps0 + ps1;
     };
@@ -460,14 +456,13 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             const int kb2 = kk >> 1, half = kk & 1;
             const u32x4 pw = {pk[kb2][4 * half], pk[kb2][4 * half + 1], pk[kb2][4 * half + 2],
                               pk[kb2][4 * half + 3]};
-            const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 const uint16_t* vb = vs + 16 * kk * D + vrd[db];
                 const u32x2 lo = lds_read_tr16x4(vb);
                 const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
-                const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[db], 0, 0, 0);
+                const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                oacc[db] = mfma_32x32x16<T>(vf, pw, oacc[db]);
             }
         }
     };
@@ -533,8 +528,8 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const u32x2 w = {pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
-                                 pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
+                const u32x2 w = {pack2<T>(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
+                                 pack2<T>(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
                 *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * hg) = w;
             }
     }
@@ -700,13 +695,13 @@ inline dim3 forward_grid(const ForwardArgs& a) {
     return dim3((unsigned)(nqb * a.B * a.Hq));
 }
 
-template <bool PAGED>
-hipError_t launch_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
+template <bool PAGED, class T>
+hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
     if (a.D == 64)
-        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED>), forward_grid(a), dim3(kThreads), 0, s, a,
-                           p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T>), forward_grid(a), dim3(kThreads), 0, s,
+                           a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else if (a.D == 128)
-        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED>), forward_grid(a), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T>), forward_grid(a), dim3(kThreads), 0, s,
                            a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else
         return hipErrorInvalidValue;
@@ -716,11 +711,16 @@ hipError_t launch_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) 
 }  // namespace
 
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s) {
-    return launch_bf16<false>(a, PagedArgs{}, s);
+    return launch_16bit<false, Bf16T>(a, PagedArgs{}, s);
 }
 
-hipError_t launch_paged_prefill_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
-    return launch_bf16<true>(a, p, s);
+hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s) {
+    return launch_16bit<false, F16T>(a, PagedArgs{}, s);
+}
+
+hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
+                                      hipStream_t s) {
+    return f16 ? launch_16bit<true, F16T>(a, p, s) : launch_16bit<true, Bf16T>(a, p, s);
 }
 
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s) {

@@ -47,11 +47,15 @@ struct PagedArgs {
 };
 
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
-// Paged prefill chunks: a.B = num_seqs, a.Sq = longest chunk, a.Sk = max_seq_len.
-hipError_t launch_paged_prefill_bf16(const ForwardArgs& a, const PagedArgs& p, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
+// Paged prefill chunks: a.B = num_seqs, a.Sq = longest chunk, a.Sk = max_seq_len;
+// bf16 or (f16) fp16.
+hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
+                                      hipStream_t s);
+// Split-KV decode and paged attention, bf16 or (f16) fp16.
+hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s);
+hipError_t launch_paged_16bit(const DecodeArgs& a, const PagedArgs& p, bool f16, hipStream_t s);
 
 // Work items of the decode split pass: (batch, K/V head, block of <= 16 query
 // heads, split).

@@ -45,7 +45,8 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-int64_t elem_size(int dtype) { return dtype == SDPA_BF16 ? 2 : 4; }
+int64_t elem_size(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
+bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || dtype == SDPA_F16; }
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -65,8 +66,7 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
                     (long long)Hq, (long long)Hkv);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
-    if (dtype != SDPA_F32 && dtype != SDPA_BF16)
-        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (!known_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
     const int64_t es = elem_size(dtype);
     const int64_t nq = numel4(B, Hq, Sq, D), nk = numel4(B, Hkv, Sk, D);
     if (nq < 0 || nk < 0 || !mul_ok(nq, es, qbytes) || !mul_ok(nk, es, kbytes))
@@ -148,8 +148,9 @@ sdpa_status_t sdpa_forward(const void* q, const void* k, const void* v, int64_t 
     a.padded = padded;
     (void)hipGetLastError();  // clear an unrelated pending error
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_forward_bf16(a, s)
-                                            : sdpa::launch_forward_f32(a, s);
+    const hipError_t e = dtype == SDPA_BF16  ? sdpa::launch_forward_bf16(a, s)
+                         : dtype == SDPA_F16 ? sdpa::launch_forward_f16(a, s)
+                                             : sdpa::launch_forward_f32(a, s);
     return hip_status(e, "sdpa_forward launch");
 }
 
@@ -181,8 +182,8 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
                     workspace ? workspace_bytes : (size_t)0);
     if (overlap(out, qbytes, workspace, (int64_t)need))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps the workspace");
-    if (dtype != SDPA_BF16)
-        return fail(SDPA_ERR_UNSUPPORTED, "decode supports bf16 only");
+    if (dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "decode supports bf16 and fp16 only");
     const int64_t items = sdpa::decode_work_items(B, Hq, Hkv, num_splits);
     if (items > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "too many decode work items (%lld)", (long long)items);
@@ -204,7 +205,8 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
     a.splits = num_splits;
     a.scale = scale;
     (void)hipGetLastError();
-    const hipError_t e = sdpa::launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        sdpa::launch_decode_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
     return hip_status(e, "sdpa_decode launch");
 }
 
@@ -231,8 +233,7 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
                     (long long)Hq, (long long)Hkv);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
-    if (dtype != SDPA_F32 && dtype != SDPA_BF16)
-        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (!known_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
     if (causal != 0 && causal != 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
     if (num_splits < 1 || num_splits > SDPA_MAX_SPLITS)
@@ -267,7 +268,8 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
     if (D != 64 && D != 128)
         return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
-    if (dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 only");
+    if (dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 and fp16 only");
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
@@ -305,7 +307,8 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     p.page_size = (int)page_size;
     p.causal = causal != 0;
     (void)hipGetLastError();
-    const hipError_t e = sdpa::launch_paged_bf16(a, p, static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        sdpa::launch_paged_16bit(a, p, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
     return hip_status(e, "sdpa_paged_attention launch");
 }
 
@@ -331,8 +334,7 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                     (long long)Hq, (long long)Hkv);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
-    if (dtype != SDPA_F32 && dtype != SDPA_BF16)
-        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (!known_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
     if (causal != 0 && causal != 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
     int64_t cap = 0;
@@ -357,7 +359,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
     if (D != 64 && D != 128)
         return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
-    if (dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 only");
+    if (dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 and fp16 only");
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
@@ -395,7 +398,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     p.total_q = (int)total_q;
     p.causal = causal != 0;
     (void)hipGetLastError();
-    const hipError_t e = sdpa::launch_paged_prefill_bf16(a, p, static_cast<hipStream_t>(stream));
+    const hipError_t e = sdpa::launch_paged_prefill_16bit(a, p, dtype == SDPA_F16,
+                                                          static_cast<hipStream_t>(stream));
     return hip_status(e, "sdpa_paged_prefill launch");
 }
 

@@ -19,6 +19,7 @@ SDPA_ERR_WORKSPACE = 3
 SDPA_ERR_HIP = 4
 SDPA_F32 = 0
 SDPA_BF16 = 1
+SDPA_F16 = 2
 MASK_NONE = 0
 MASK_CAUSAL = 1
 MASK_KEY_PADDING = 2
@@ -87,9 +88,11 @@ def _check(status):
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return SDPA_BF16
+    if t.dtype == torch.float16:
+        return SDPA_F16
     if t.dtype == torch.float32:
         return SDPA_F32
-    raise TypeError("libsdpa supports bfloat16 and float32 tensors, got %s" % t.dtype)
+    raise TypeError("libsdpa supports bfloat16, float16 and float32 tensors, got %s" % t.dtype)
 
 
 def _ptr(t):

@@ -17,13 +17,15 @@
  *  - Grouped K/V: Hq must be a multiple of Hkv; query head h reads K/V head
  *    h / (Hq / Hkv) (contiguous groups; ruDNN guide section 9 requires only
  *    divisibility).
- *  - dtype: q, k, v and out share one element type, SDPA_BF16 or SDPA_F32.
+ *  - dtype: q, k, v and out share one element type, SDPA_BF16, SDPA_F16 or
+ *    SDPA_F32 (the ruDNN guide's F32/F16/BF16 inputs, sections 9 and 10).
  *    Products accumulate in fp32; softmax statistics (running max, sum,
  *    log-sum-exp) are fp32; the output is rounded to the input type (round to
  *    nearest even), as the ruDNN guide's normalisation ops do (section 7).
- *    On the bf16 path the softmax weights are rounded to bf16 before the
- *    product with V, and the running denominator is the fp32 sum of those
- *    same rounded weights; scores, the running max and Q are never rounded.
+ *    On the 16-bit paths the softmax weights are rounded to the input type
+ *    before the product with V, and the running denominator is the fp32 sum
+ *    of those same rounded weights; scores, the running max and Q are never
+ *    rounded.
  *  - Pointers: every tensor pointer (q, k, v, out, key_lens, workspace) is a
  *    DEVICE pointer on the current HIP device, owned by the caller.  The
  *    library allocates nothing and keeps no per-call state.
@@ -65,7 +67,7 @@ typedef enum {
     SDPA_ERR_HIP = 4               /* a HIP runtime call or launch failed        */
 } sdpa_status_t;
 
-typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1 } sdpa_dtype_t;
+typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_F16 = 2 } sdpa_dtype_t;
 
 /* Mask flags, combinable with |. */
 enum {
@@ -88,7 +90,7 @@ enum {
  *   mask_kind  SDPA_MASK_* flags; SDPA_MASK_CAUSAL requires Sq == Sk
  *   key_lens device int32 [B] when mask_kind has SDPA_MASK_KEY_PADDING, else NULL
  *   out      device [B, Hq, Sq, D], dtype; written completely
- *   dtype    SDPA_BF16 or SDPA_F32
+ *   dtype    SDPA_BF16, SDPA_F16 or SDPA_F32
  *   stream   hipStream_t as void*
  * Supported head dims: D in {64, 128}; one head (Sq*D or Sk*D elements) must
  * be under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
@@ -120,7 +122,7 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
  *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
  *   out        device [B, Hq, 1, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16, D in {64, 128}.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}.
  */
 sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D,
@@ -155,8 +157,8 @@ sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
  *                (same layout as sdpa_decode's with B = queries)
  *   out          device [queries, Hq, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16, D in {64, 128}, page_size a multiple of 16
- * (SDPA_ERR_UNSUPPORTED otherwise).
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}, page_size a
+ * multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
  * [0, num_seqs), a negative query_pos under the causal flag, or a sequence
@@ -193,8 +195,9 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *   causal        0: every cached key of the sequence is visible; 1: only
  *                 keys j <= the row's absolute position
  *   out           device [total_q, Hq, D]
- * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16, D in
- * {64, 128}, page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
+ * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
+ * SDPA_F16, D in {64, 128}, page_size a multiple of 16
+ * (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside
  * out is ever written); a chunk longer than max_q is only computed for its

@@ -201,3 +201,13 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, pages=100, p
 def test_paged_prefill_rejects(kw, status, needle):
     assert prefill(**kw) == status
     assert needle in sd.last_error()
+
+
+def test_dtype_codes():
+    # F16 is accepted everywhere (no rejection on dtype); an unknown code is invalid
+    assert fwd(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
+    assert dec(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
+    assert paged(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
+    assert prefill(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
+    assert fwd(dtype=sd.SDPA_F16, D=96) == sd.SDPA_ERR_UNSUPPORTED  # reaches the head-dim check
+    assert dec(dtype=sd.SDPA_F16, D=96) == sd.SDPA_ERR_UNSUPPORTED
