@@ -35,6 +35,15 @@ reordered:
 * split-KV   partial attention over disjoint key ranges, each with its own lse,
   and the log-sum-exp merge of those partials (ruDNN user guide section 9:
   history split into 2..=32 pieces, partial statistics and merge in FP32).
+* backward   gradients of a loss L through O = softmax(S) V, S = scale Q K^T +
+  mask, given dO = dL/dO (ruDNN user guide section 11: the attention backward
+  returns dq, dk, dv and recomputes the probabilities instead of storing the
+  score matrix; tensai guide, the block step's backward).  With P the row
+  softmax: dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(dO * O)) (the
+  softmax Jacobian applied row by row); dQ = scale dS K; dK = scale dS^T Q.
+  Grouped K/V: a K/V head's dK, dV sum the contributions of its query heads.
+  A row with no visible key has no defined output and contributes nothing
+  (its dQ row is 0).
 * paged      packed queries [queries, Hq, D] over a physical K/V page cache
   [pages, page_size, Hkv, D] (ruDNN user guide section 9): query t belongs to
   sequence query_seq[t] at zero-based absolute position query_pos[t]; the
@@ -233,6 +242,45 @@ def merge_partials(o_part, lse_part):
     return o, lse
 
 
+def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None):
+    """dQ, dK, dV of L with dL/dO = dout, by the definition (fp64).
+
+    q, dout [B,Hq,Sq,D]; k, v [B,Hkv,Sk,D].  Per (b, h): P is the row softmax
+    of the masked scaled scores (hidden keys get exactly 0), O = P V, then
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)), dQ = scale dS K,
+    dK = scale dS^T Q; dK and dV of a K/V head sum over its Hq/Hkv query heads.
+    Rows with no visible key contribute nothing.  Returns (dq, dk, dv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Hq, Hkv, Sk, D = _check_shapes(q, k, v)
+    Sq = q.shape[2]
+    if mask_kind & MASK_CAUSAL and Sq != Sk:
+        raise ValueError("causal mask needs Sq == Sk")
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(Sq)
+    for b in range(B):
+        vis = visible_rows(mask_kind, rows, Sk, key_lens[b] if key_lens is not None else 0)
+        live = vis.any(axis=1)                 # rows with at least one visible key
+        for h in range(Hq):
+            g = h // G
+            _, _, p = attend(q[b, h], k[b, g], v[b, g], scale, vis)
+            p = np.where(live[:, None], p, 0.0)
+            do = np.where(live[:, None], dout[b, h], 0.0)
+            o = p @ v[b, g]
+            dv[b, g] += p.T @ do
+            dp = do @ v[b, g].T
+            ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
+            dq[b, h] = float(scale) * (ds @ k[b, g])
+            dk[b, g] += float(scale) * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
 def paged_gather(cache, table_row, length, page_size):
     """Logical rows 0..length-1 of one sequence read through its page table.
 
@@ -305,5 +353,5 @@ __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KEY_PADDING", "visible_rows", "attend",
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
     "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
-    "chunk_positions",
+    "chunk_positions", "sdpa_backward",
 ]

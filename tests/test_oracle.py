@@ -532,3 +532,86 @@ def test_chunk_positions_closed_form():
     assert qp.tolist() == [0, 1, 2, 0, 1, 2, 3, 4, 39]
     qs, qp = O.chunk_positions([0, 4], [100])
     assert qp.tolist() == [96, 97, 98, 99]
+
+
+# ------------------------------------------------------------------ backward
+
+def _loss(q, k, v, g, scale, mask, lens):
+    return float((O.sdpa_forward(q, k, v, scale, mask, lens) * g).sum())
+
+
+@pytest.mark.parametrize("mask,lens", [(O.MASK_NONE, None), (O.MASK_CAUSAL, None),
+                                       (O.MASK_KEY_PADDING, [3, 5])])
+def test_backward_matches_finite_differences(mask, lens):
+    # central differences of L = sum(O * G) through the (pinned) forward
+    rng = np.random.default_rng(61 + mask)
+    B, Hq, Hkv, S, D = 2, 4, 2, 5, 3
+    q, k, v = (rng.standard_normal((B, Hq, S, D)), rng.standard_normal((B, Hkv, S, D)),
+               rng.standard_normal((B, Hkv, S, D)))
+    g = rng.standard_normal((B, Hq, S, D))
+    lens = None if lens is None else np.array(lens)
+    dq, dk, dv = O.sdpa_backward(q, k, v, g, 0.7, mask, lens)
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_loss(args_p["q"], args_p["k"], args_p["v"], g, 0.7, mask, lens)
+                        - _loss(args_m["q"], args_m["k"], args_m["v"], g, 0.7, mask, lens)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_backward_key_gradients_sum_to_zero():
+    # each row of dS sums to 0 (softmax is shift invariant), so the dK rows of
+    # a K/V head sum to the zero vector
+    rng = np.random.default_rng(62)
+    q, k, v = rng.standard_normal((2, 6, 40, 8)), rng.standard_normal((2, 3, 40, 8)), \
+        rng.standard_normal((2, 3, 40, 8))
+    g = rng.standard_normal((2, 6, 40, 8))
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL):
+        _, dk, _ = O.sdpa_backward(q, k, v, g, 0.3, mask)
+        assert np.abs(dk.sum(axis=2)).max() < 1e-12
+
+
+def test_backward_zero_query_closed_form():
+    # Q = 0: every visible key gets weight 1/n_i, so dV_j = sum over the rows
+    # that see key j of dO_i / n_i (causal: n_i = i + 1), and dK = 0
+    rng = np.random.default_rng(63)
+    S, D = 7, 4
+    q = np.zeros((1, 1, S, D))
+    k, v = rng.standard_normal((1, 1, S, D)), rng.standard_normal((1, 1, S, D))
+    g = rng.standard_normal((1, 1, S, D))
+    _, dk, dv = O.sdpa_backward(q, k, v, g, 1.0, O.MASK_CAUSAL)
+    for j in range(S):
+        ref = sum(g[0, 0, i] / (i + 1) for i in range(j, S))
+        np.testing.assert_allclose(dv[0, 0, j], ref, rtol=0, atol=1e-14)
+    assert np.abs(dk).max() < 1e-14
+
+
+def test_backward_gqa_equals_summed_mha():
+    rng = np.random.default_rng(64)
+    B, Hq, Hkv, S, D = 1, 6, 2, 9, 5
+    q, k, v = rng.standard_normal((B, Hq, S, D)), rng.standard_normal((B, Hkv, S, D)), \
+        rng.standard_normal((B, Hkv, S, D))
+    g = rng.standard_normal((B, Hq, S, D))
+    dq, dk, dv = O.sdpa_backward(q, k, v, g, 0.4, O.MASK_CAUSAL)
+    kr, vr = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    dq2, dk2, dv2 = O.sdpa_backward(q, kr, vr, g, 0.4, O.MASK_CAUSAL)
+    np.testing.assert_allclose(dq, dq2, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=2), atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=2), atol=1e-13)
+
+
+def test_backward_hidden_keys_and_dead_rows():
+    rng = np.random.default_rng(65)
+    q, k, v = rng.standard_normal((2, 2, 6, 4)), rng.standard_normal((2, 2, 6, 4)), \
+        rng.standard_normal((2, 2, 6, 4))
+    g = rng.standard_normal((2, 2, 6, 4))
+    dq, dk, dv = O.sdpa_backward(q, k, v, g, 0.5, O.MASK_KEY_PADDING, np.array([4, 0]))
+    assert (dk[0, :, 4:] == 0).all() and (dv[0, :, 4:] == 0).all()     # padded keys
+    assert (dq[1] == 0).all() and (dk[1] == 0).all() and (dv[1] == 0).all()  # no visible key
