@@ -62,7 +62,10 @@ __device__ __forceinline__ float swap_half_wave(float x) {
 __device__ __forceinline__ float max_half_waves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                                    __builtin_bit_cast(unsigned, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    // The two results are copied to scalars before the bit casts: this hipcc
+    // folds __builtin_bit_cast of a vector element to element 0.
+    const unsigned r0 = r[0], r1 = r[1];
+    return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // Three-input maximum as one v_max3_f32 (the inputs are MFMA results or -inf,

@@ -176,3 +176,38 @@ def test_full_size_workload_sampled(name):
                                  lens, idx)
     max_abs, rel = compare(got, ref, w.dtype, name)
     print("%s sampled %d rows: max-abs %.3e rel-L2 %.3e" % (name, len(idx), max_abs, rel))
+
+
+def _hot_key_inputs(B, Hq, Sq, Sk, D, dtype, seed):
+    # batch b: one key (position 3*b) scores 100 above every other key of
+    # every query; without the hot key's score in the row max the weights
+    # would overflow exp2, so every tile position of the hot key is tried
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    q = torch.zeros(B, Hq, Sq, D)
+    q[..., 0] = 10.0
+    k = torch.zeros(B, 1, Sk, D)
+    for b in range(B):
+        k[b, 0, 3 * b, 0] = 10.0
+    v = torch.randn(B, 1, Sk, D, generator=gen)
+    return [t.to(dtype).to(DEV) for t in (q, k, v)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_row_max_covers_every_key(D):
+    B, Hq, Sq, Sk = 64, 2, 40, 192
+    q, k, v = _hot_key_inputs(B, Hq, Sq, Sk, D, torch.bfloat16, 77)
+    out = sd.sdpa_forward(q, k, v, 1.0)
+    torch.cuda.synchronize()
+    ref = O.sdpa_forward(to64(q), to64(k), to64(v), 1.0)
+    compare(to64(out), ref, torch.bfloat16, "hot key forward D=%d" % D)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_row_max_covers_every_key(splits):
+    B, Hq, Sk, D = 64, 16, 192, 128
+    q, k, v = _hot_key_inputs(B, Hq, 1, Sk, D, torch.bfloat16, 78)
+    out = sd.sdpa_decode(q, k, v, 1.0, None, splits)
+    torch.cuda.synchronize()
+    ref = O.sdpa_decode(to64(q), to64(k), to64(v), 1.0)
+    compare(to64(out), ref, torch.bfloat16, "hot key decode splits=%d" % splits)
