@@ -1,0 +1,546 @@
+// Attention backward: dQ, dK and dV of O = softmax(Q K^T * scale + mask) V
+// for a loss whose gradient with respect to O is dO.  The probabilities are
+// recomputed from the forward's per-row log-sum-exp instead of being stored
+// (ruDNN user guide, section 11: the attention backward returns dq, dk, dv and
+// never keeps the full score matrix).  The derivatives are those of the
+// tensai autograd guide's attention block (reshape, two batched products, a
+// scale, the mask and a last-axis softmax):
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_i = sum_d dO_id O_id,
+//   dQ = scale dS K,  dK = scale dS^T Q,
+// with P_ij = exp(scale * s_ij - lse_i) and hidden keys at P = 0.  Grouped K/V
+// heads sum the contributions of their Hq / Hkv query heads.
+//
+// Two passes, both deterministic (every sum has a fixed order; the ruDNN
+// guide's ordered history reduction, section 11):
+//   1. dQ pass, query-parallel: a workgroup owns 128 rows of one (batch, query
+//      head) and walks its visible keys in tiles of 64.  It also forms delta
+//      from the rows of O and dO it holds and writes (lse * log2 e, delta) per
+//      row to the workspace for pass 2.
+//   2. dK / dV pass, key-parallel: a workgroup owns 128 keys of one (batch,
+//      K/V head) and walks the query tiles of every query head of the group.
+// Neither pass needs an atomic: each output element is owned by one lane.
+//
+// MFMA layouts (v_mfma_f32_32x32x16, fp32 accumulation).  Lane l, half
+// hg = l / 32: the A operand holds row l%32 with contraction slots
+// k = 8*hg + e (e = 0..7), the B operand column l%32 with the same slots, and
+// the accumulator column l%32 with row 8*(r/4) + 4*hg + r%4 in register r.  So
+// an accumulator tile X [M x N] is, after rounding to 16 bits, already the B
+// operand of a product that contracts over M, provided the A operand maps
+// slot (hg, e) of 16-row step kk to row 16*kk + 8*(e/4) + 4*hg + e%4.  A
+// transposed LDS read (ds_read_b64_tr_b16) of four consecutive rows gives
+// exactly that: the rows 4*hg..4*hg+3 (e < 4) and 8+4*hg.. (e >= 4).
+//
+//   dQ pass (per wave: 32 queries, Q and dO in registers as B operands):
+//     S^T = K Q^T, dP^T = V dO^T         (K, V: row reads of the LDS tile)
+//     dQ^T += K^T dS^T                    (K^T: transposed reads)
+//   dK / dV pass (per wave: 32 keys, K and V in registers as B operands):
+//     S = Q K^T, dP = dO V^T              (Q, dO: row reads)
+//     dV^T += dO^T P,  dK^T += Q^T dS     (dO^T, Q^T: transposed reads)
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int kBwThreads = 256;  // 4 waves of 64
+constexpr int kBwRows = 128;     // rows a workgroup owns (queries in pass 1, keys in pass 2)
+constexpr int kBwTile = 64;      // rows of the streamed operand per step
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS helpers.  The __restrict__ parameters give each inlined access an alias
+// scope of its own, which keeps the compiler from putting a vmcnt(0) drain of
+// the in-flight LDS-DMA writes in front of it (explicit waits order those).
+__device__ __forceinline__ u32x2 lds_tr(const uint16_t* __restrict__ p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    lds_i16x4* lp = (lds_i16x4*)((__attribute__((address_space(3))) char*)p);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+__device__ __forceinline__ u32x4 lds_row(const uint16_t* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) u32x4*)(
+        (const __attribute__((address_space(3))) char*)p);
+}
+__device__ __forceinline__ f32x4 lds_f4(const float* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) f32x4*)(
+        (const __attribute__((address_space(3))) char*)p);
+}
+
+// Raw buffer resource over [base, base + bytes); loads beyond it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16*l (the destination is wave-uniform).
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, 0);
+}
+
+// sum of the eight products of two packed 16-bit vectors, added to acc (fp32).
+// The words are copied to scalars before the bit casts: this hipcc folds
+// __builtin_bit_cast of a vector element to element 0.
+template <class T>
+__device__ __forceinline__ float dot8(u32x4 x, u32x4 y, float acc) {
+    const uint32_t xs[4] = {x[0], x[1], x[2], x[3]}, ys[4] = {y[0], y[1], y[2], y[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (T::kF16)
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xs[i]),
+                                         __builtin_bit_cast(f16x2, ys[i]), acc, false);
+        else
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xs[i]),
+                                                  __builtin_bit_cast(bf16x2, ys[i]), acc, false);
+    }
+    return acc;
+}
+
+// LDS tile of kBwTile rows x D 16-bit elements, rows unpadded, 16-byte chunk c
+// of row r stored at chunk c ^ f(r).  With u = r / RPW (RPW = rows per
+// 256-byte bank window) and NB = D / 32 blocks of four chunks per row,
+// f(r) = 4 * (u % NB) + (u / NB) % 4:
+//   - a row read (one chunk of 16 consecutive rows, one lane each) hits 16
+//     distinct 16-byte bank groups, since f is one-to-one over 16 rows;
+//   - a transposed read (4 consecutive rows x 4 consecutive chunks per 32
+//     lanes) does too, since the four rows differ in f's block bits.
+// f repeats every 16 rows, so offsets computed for rows 0..31 serve every
+// 16-aligned row block.
+template <int D>
+struct BwGeo {
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int RPW = 256 / (2 * D);        // rows per bank window
+    static constexpr int NB = CPR / 4;               // 4-chunk blocks per row
+    static constexpr int TILE = kBwTile * D;         // elements per tile
+    static constexpr int DMA = TILE * 2 / 1024 / 4;  // 1-KB DMA loads per wave per tile
+    __device__ static int f(int r) {
+        const int u = r / RPW;
+        return 4 * (u % NB) + (u / NB) % 4;
+    }
+};
+
+// Lane-constant LDS offsets (elements) shared by both passes.
+template <int D>
+struct BwOffsets {
+    using L = BwGeo<D>;
+    int row[D / 16];  // row read: row l32, logical chunk 2t + hg
+    int trl[D / 32];  // transposed read, rows 4hg + j/4 of a 16-row step, dims 32db + ...
+    int trh[D / 32];  // the same 8 rows further on
+    uint32_t dma[L::DMA];  // DMA source offsets (bytes) of this wave's tile slots
+    __device__ BwOffsets(int wave, int lane) {
+        const int l32 = lane & 31, hg = lane >> 5;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) row[t] = l32 * D + (((2 * t + hg) ^ L::f(l32)) * 8);
+        // Inside each 16-lane group, lane j points at row k0 + j/4, dims
+        // d0 + 4*(j%4) .. +3; lane j then receives rows k0..k0+3 of dim d0 + j.
+        const int g16 = lane >> 4, j16 = lane & 15;
+        const int rl = 4 * hg + (j16 >> 2), rh = rl + 8;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+            trl[db] = rl * D + (((col >> 3) ^ L::f(rl)) * 8) + (col & 7);
+            trh[db] = rh * D + (((col >> 3) ^ L::f(rh)) * 8) + (col & 7);
+        }
+        // DMA load i of this wave fills 16-byte slot s = 64*(DMA*wave + i) + lane
+        // of the tile: row s / CPR, stored chunk s % CPR.
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) {
+            const int s = 64 * (L::DMA * wave + i) + lane;
+            const int r = s / L::CPR, pc = s % L::CPR;
+            dma[i] = (uint32_t)r * D * 2 + (uint32_t)((pc ^ L::f(r)) * 16);
+        }
+    }
+};
+
+// Rows of one head in the (lse2, delta) workspace: Sq rounded up to even, so
+// every head's slice starts 16-byte aligned.
+__host__ __device__ __forceinline__ int64_t stats_stride(int Sq) { return (Sq + 1) & ~1; }
+
+// Workgroup id -> position in a logical order in which each of the 8 XCDs
+// (workgroups are dealt to them round-robin, id % 8) owns one contiguous run,
+// so workgroups sharing K/V (pass 1) or Q/dO (pass 2) share one L2.
+__device__ __forceinline__ int xcd_order(int total) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int nx = total >> 3, rem = total & 7;
+    return xcd * nx + min(xcd, rem) + local;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: dQ (and the per-row statistics for pass 2).
+// Logical order: (batch, K/V head) outermost, query block, then the query
+// heads of the group innermost; under a causal mask the longest blocks (the
+// last rows) first.
+// ---------------------------------------------------------------------------
+template <int D, class T>
+__global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
+                                                               const int32_t* __restrict__ key_lens) {
+    using L = BwGeo<D>;
+    // Stage s: K tile at 2*s*TILE, V tile at (2*s+1)*TILE.
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hg = lane >> 5;
+
+    const int G = a.Hq / a.Hkv;
+    const int nqb = (a.Sq + kBwRows - 1) / kBwRows;
+    int t = xcd_order(a.B * a.Hkv * nqb * G);
+    const int hsub = t % G;
+    t /= G;
+    const int qord = t % nqb;
+    const int unit = t / nqb;
+    const int b = unit / a.Hkv, gk = unit % a.Hkv, h = gk * G + hsub;
+    const int q0 = (a.causal ? nqb - 1 - qord : qord) * kBwRows;
+
+    const int64_t bh = (int64_t)b * a.Hq + h;
+    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kvh;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kvh;
+    const int64_t qoff = bh * a.Sq * D;
+
+    int kv_lim = a.Sk;
+    if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
+    int kv_end = kv_lim;
+    if (a.causal) kv_end = min(kv_end, q0 + kBwRows);
+    const int qw = q0 + 32 * wave;  // first query row of this wave
+    const int qi = qw + l32;        // this lane's query row
+    const int ntiles = kv_end > 0 ? (kv_end + kBwTile - 1) / kBwTile : 0;
+    // Tiles this wave computes on (it still takes part in every load and barrier).
+    int wave_tiles = a.causal ? max(0, min(ntiles, (qw + 31) / kBwTile + 1)) : ntiles;
+    if (qw >= a.Sq) wave_tiles = 0;
+
+    // Q and dO rows as B operands: lane holds row qi, dims 16t + 8hg .. +7
+    // (rows >= Sq read as zeros).  delta_i = sum_d dO_id O_id in fp32.
+    u32x4 qr[D / 16], dr[D / 16];
+    float delta;
+    {
+        const uint32_t bytes = (uint32_t)a.Sq * D * 2;
+        const __amdgpu_buffer_rsrc_t rq = rsrc(static_cast<const uint16_t*>(a.q) + qoff, bytes);
+        const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const uint16_t*>(a.dout) + qoff, bytes);
+        const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const uint16_t*>(a.out) + qoff, bytes);
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            const uint32_t off = (uint32_t)qi * D * 2 + (16 * k + 8 * hg) * 2;
+            qr[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+            dr[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
+            part = dot8<T>(dr[k], __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0), part);
+        }
+        delta = part + swap_half_wave(part);
+    }
+    // lse in log2 units; a row with no visible key (lse = -inf) gets +inf so
+    // that every recomputed probability of it is exactly 0, and delta 0 (its
+    // forward output row is 0/0, so O o dO would be NaN).
+    float lse2 = INFINITY;
+    if (qi < a.Sq) {
+        const float l = a.lse[bh * a.Sq + qi];
+        lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        if (l == -INFINITY) delta = 0.f;
+        if (hg == 0) {
+            float2* st = reinterpret_cast<float2*>(a.delta) + bh * stats_stride(a.Sq) + qi;
+            *st = make_float2(lse2, delta);
+        }
+    }
+
+    const BwOffsets<D> off(wave, lane);
+    auto issue = [&](int j0, int stage) {
+        const uint32_t bytes = (uint32_t)(a.Sk - j0) * D * 2;
+        const __amdgpu_buffer_rsrc_t rk = rsrc(kp + (int64_t)j0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vp + (int64_t)j0 * D, bytes);
+        uint16_t* dk = smem + 2 * stage * L::TILE + 512 * L::DMA * wave;
+        uint16_t* dv = dk + L::TILE;
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) {
+            dma(rk, dk + 512 * i, off.dma[i]);
+            dma(rv, dv + 512 * i, off.dma[i]);
+        }
+    };
+
+    const float c = a.scale * kLog2e;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+    // One 64-key tile: per 32-key block, S^T and dP^T, then dS^T, then
+    // dQ^T += K^T dS^T.  Register r of a score block holds key
+    // j0 + 32*kb2 + 8*(r/4) + 4*hg + r%4 of query qi.
+    auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int kb0 = j0 + 32 * kb2;
+            if (kb0 >= kv_lim || (a.causal && kb0 > qw + 31)) continue;  // wave-uniform
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                s = mfma_32x32x16<T>(lds_row(ks + 32 * kb2 * D + off.row[k]), qr[k], s);
+                dp = mfma_32x32x16<T>(lds_row(vs + 32 * kb2 * D + off.row[k]), dr[k], dp);
+            }
+            const bool need_mask = kb0 + 32 > kv_lim || (a.causal && kb0 + 31 > qw);
+            uint32_t w[8];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float p0 = fast_exp2(fmaf(s[r], c, -lse2));
+                float p1 = fast_exp2(fmaf(s[r + 1], c, -lse2));
+                if (need_mask) {
+                    const int key = kb0 + 8 * (r >> 2) + 4 * hg + (r & 3);
+                    if (key >= kv_lim || (a.causal && key > qi)) p0 = 0.f;
+                    if (key + 1 >= kv_lim || (a.causal && key + 1 > qi)) p1 = 0.f;
+                }
+                w[r >> 1] = pack2<T>(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 bw = {w[4 * kk], w[4 * kk + 1], w[4 * kk + 2], w[4 * kk + 3]};
+                const uint16_t* kt = ks + (32 * kb2 + 16 * kk) * D;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const u32x2 lo = lds_tr(kt + off.trl[db]);
+                    const u32x2 hi = lds_tr(kt + off.trh[db]);
+                    acc[db] = mfma_32x32x16<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, bw, acc[db]);
+                }
+            }
+        }
+    };
+
+    if (ntiles > 0) issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // Tile jt sits in stage jt % 2; the next one is loaded into the other
+    // stage meanwhile (it was last read before the previous barrier).
+    auto step = [&](int jt, const int cur) __attribute__((always_inline)) {
+        if (jt + 1 < ntiles) issue((jt + 1) * kBwTile, cur ^ 1);
+        if (jt < wave_tiles)
+            compute(smem + 2 * cur * L::TILE, smem + (2 * cur + 1) * L::TILE, jt * kBwTile);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        step(jt, 0);
+        if (jt + 1 < ntiles) step(jt + 1, 1);
+    }
+
+    // dQ = scale * (dS K): register r of d-block db holds dim
+    // 32*db + 8*(r/4) + 4*hg + r%4 of row qi.
+    if (qi < a.Sq) {
+        uint16_t* row = static_cast<uint16_t*>(a.dq) + qoff + (int64_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x16& x = acc[db];
+                const u32x2 w = {pack2<T>(x[4 * r4] * a.scale, x[4 * r4 + 1] * a.scale),
+                                 pack2<T>(x[4 * r4 + 2] * a.scale, x[4 * r4 + 3] * a.scale)};
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * r4 + 4 * hg) = w;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: dK and dV.
+// Logical order: (batch, K/V head) outermost, then key blocks; under a causal
+// mask the first key blocks (which see the most queries) first.
+// ---------------------------------------------------------------------------
+template <int D, class T>
+__global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
+                                                                 const int32_t* __restrict__ key_lens) {
+    using L = BwGeo<D>;
+    // Stage s: Q tile, dO tile, then the tile rows' (lse2, delta) pairs
+    // (512 B used of a 1-KB slot).
+    constexpr int STAGE = 2 * L::TILE + 512;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hg = lane >> 5;
+
+    const int G = a.Hq / a.Hkv;
+    const int nkb = (a.Sk + kBwRows - 1) / kBwRows;
+    const int t = xcd_order(a.B * a.Hkv * nkb);
+    const int unit = t / nkb;
+    const int k0 = (t % nkb) * kBwRows;
+    const int b = unit / a.Hkv, gk = unit % a.Hkv;
+
+    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
+    int kv_lim = a.Sk;
+    if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
+    const int kw = k0 + 32 * wave;  // first key of this wave
+    const int kj = kw + l32;        // this lane's key
+
+    // K and V rows as B operands: lane holds key kj, dims 16t + 8hg .. +7.
+    u32x4 kr[D / 16], vr[D / 16];
+    {
+        const uint32_t bytes = (uint32_t)a.Sk * D * 2;
+        const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const uint16_t*>(a.k) + kvh, bytes);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const uint16_t*>(a.v) + kvh, bytes);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            const uint32_t off = (uint32_t)kj * D * 2 + (16 * k + 8 * hg) * 2;
+            kr[k] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+            vr[k] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        }
+    }
+
+    // Query tiles: all of them, or (causal) those holding a row >= k0; a block
+    // whose keys are all hidden does no work at all.
+    const int qt0 = a.causal ? k0 / kBwTile : 0;
+    const int nqt = (k0 < kv_lim) ? max(0, (a.Sq + kBwTile - 1) / kBwTile - qt0) : 0;
+    const int steps = G * nqt;
+
+    const BwOffsets<D> off(wave, lane);
+    auto issue = [&](int st, int stage) {
+        const int h = gk * G + st / nqt;
+        const int q0 = (qt0 + st % nqt) * kBwTile;
+        const int64_t bh = (int64_t)b * a.Hq + h;
+        const int64_t qoff = (bh * a.Sq + q0) * D;
+        const uint32_t bytes = (uint32_t)(a.Sq - q0) * D * 2;
+        const __amdgpu_buffer_rsrc_t rq = rsrc(static_cast<const uint16_t*>(a.q) + qoff, bytes);
+        const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const uint16_t*>(a.dout) + qoff, bytes);
+        uint16_t* dq = smem + stage * STAGE + 512 * L::DMA * wave;
+        uint16_t* dd = dq + L::TILE;
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) {
+            dma(rq, dq + 512 * i, off.dma[i]);
+            dma(rd, dd + 512 * i, off.dma[i]);
+        }
+        if (wave == 0) {
+            // 8 bytes per row; rows >= Sq read as zeros (and meet zero Q and
+            // dO rows, which contribute nothing).
+            const __amdgpu_buffer_rsrc_t rs =
+                rsrc(reinterpret_cast<const float2*>(a.delta) + bh * stats_stride(a.Sq) + q0,
+                     (uint32_t)(a.Sq - q0) * 8);
+            dma(rs, smem + stage * STAGE + 2 * L::TILE, 16 * lane);
+        }
+    };
+
+    const float c = a.scale * kLog2e;
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    // One 64-query tile of one query head: per 32-query block, S and dP, then
+    // P and dS, then dV^T += dO^T P and dK^T += Q^T dS.  Register r of a score
+    // block holds query q0 + 32*qb2 + 8*(r/4) + 4*hg + r%4 of key kj.
+    auto compute = [&](const uint16_t* qs, const uint16_t* ds, const float* st, int q0)
+                       __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb2 = 0; qb2 < 2; ++qb2) {
+            const int qb0 = q0 + 32 * qb2;
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                s = mfma_32x32x16<T>(lds_row(qs + 32 * qb2 * D + off.row[k]), kr[k], s);
+                dp = mfma_32x32x16<T>(lds_row(ds + 32 * qb2 * D + off.row[k]), vr[k], dp);
+            }
+            const bool need_mask = a.causal && qb0 < kw + 31;
+            uint32_t pw[8], dw[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // (lse2, delta) of rows 32*qb2 + 8*i + 4*hg + 0..3.
+                const float* sp = st + 2 * (32 * qb2 + 8 * i + 4 * hg);
+                const f32x4 s01 = lds_f4(sp), s23 = lds_f4(sp + 4);
+                const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+                const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+#pragma unroll
+                for (int j = 0; j < 4; j += 2) {
+                    const int r = 4 * i + j;
+                    float p0 = fast_exp2(fmaf(s[r], c, -l2[j]));
+                    float p1 = fast_exp2(fmaf(s[r + 1], c, -l2[j + 1]));
+                    if (need_mask) {
+                        const int q = qb0 + 8 * i + 4 * hg + j;
+                        if (kj > q) p0 = 0.f;
+                        if (kj > q + 1) p1 = 0.f;
+                    }
+                    pw[r >> 1] = pack2<T>(p0, p1);
+                    dw[r >> 1] = pack2<T>(p0 * (dp[r] - dl[j]), p1 * (dp[r + 1] - dl[j + 1]));
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 bp = {pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
+                const u32x4 bd = {dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]};
+                const uint16_t* qt = qs + (32 * qb2 + 16 * kk) * D;
+                const uint16_t* dt = ds + (32 * qb2 + 16 * kk) * D;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const u32x2 dlo = lds_tr(dt + off.trl[db]), dhi = lds_tr(dt + off.trh[db]);
+                    dv[db] = mfma_32x32x16<T>(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, dv[db]);
+                    const u32x2 qlo = lds_tr(qt + off.trl[db]), qhi = lds_tr(qt + off.trh[db]);
+                    dk[db] = mfma_32x32x16<T>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, dk[db]);
+                }
+            }
+        }
+    };
+
+    if (steps > 0) issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    auto step = [&](int st, const int cur) __attribute__((always_inline)) {
+        if (st + 1 < steps) issue(st + 1, cur ^ 1);
+        const int q0 = (qt0 + st % nqt) * kBwTile;
+        if (kw < kv_lim && (!a.causal || q0 + kBwTile - 1 >= kw)) {
+            const uint16_t* base = smem + cur * STAGE;
+            compute(base, base + L::TILE, reinterpret_cast<const float*>(base + 2 * L::TILE), q0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    for (int st = 0; st < steps; st += 2) {
+        step(st, 0);
+        if (st + 1 < steps) step(st + 1, 1);
+    }
+
+    // dK = scale * (dS^T Q), dV = P^T dO: register r of d-block db holds dim
+    // 32*db + 8*(r/4) + 4*hg + r%4 of key kj.  Keys at or past the batch's
+    // key limit were never visible: their gradients are 0.
+    if (kj < a.Sk) {
+        const bool live = kj < kv_lim;
+        const float ks = live ? a.scale : 0.f, vs = live ? 1.f : 0.f;
+        uint16_t* krow = static_cast<uint16_t*>(a.dk) + kvh + (int64_t)kj * D;
+        uint16_t* vrow = static_cast<uint16_t*>(a.dv) + kvh + (int64_t)kj * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x16& x = dk[db];
+                const f32x16& y = dv[db];
+                const u32x2 wk = {pack2<T>(x[4 * r4] * ks, x[4 * r4 + 1] * ks),
+                                  pack2<T>(x[4 * r4 + 2] * ks, x[4 * r4 + 3] * ks)};
+                const u32x2 wv = {pack2<T>(y[4 * r4] * vs, y[4 * r4 + 1] * vs),
+                                  pack2<T>(y[4 * r4 + 2] * vs, y[4 * r4 + 3] * vs)};
+                *reinterpret_cast<u32x2*>(krow + 32 * db + 8 * r4 + 4 * hg) = wk;
+                *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * r4 + 4 * hg) = wv;
+            }
+    }
+}
+
+template <int D, class T>
+hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
+    const int nqb = (a.Sq + kBwRows - 1) / kBwRows;
+    const int nkb = (a.Sk + kBwRows - 1) / kBwRows;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T>), dim3(a.B * a.Hq * nqb), dim3(kBwThreads), 0, s, a,
+                       a.key_lens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.B * a.Hkv * nkb), dim3(kBwThreads), 0, s,
+                       a, a.key_lens);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s) {
+    if (a.D == 128)
+        return f16 ? launch_backward_d<128, F16T>(a, s) : launch_backward_d<128, Bf16T>(a, s);
+    if (a.D == 64)
+        return f16 ? launch_backward_d<64, F16T>(a, s) : launch_backward_d<64, Bf16T>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -522,6 +522,12 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // dim 32*db + 8*(r/4) + 4*hg + r%4 of row qi.
     const float lt = l_run + swap_half_wave(l_run);
     const float inv = 1.f / lt;
+    // Optional log-sum-exp of the row (natural log, scaled-score units) for
+    // the backward: the reference max plus ln of the denominator; -inf for a
+    // row with no visible key.
+    if (!PAGED && a.lse && hg == 0 && qi < nrows)
+        a.lse[((int64_t)ti.b * a.Hq + ti.h) * a.Sq + qi] =
+            m_run == -INFINITY ? -INFINITY : m_run * a.scale + __logf(lt);
     if (qi < nrows) {
         uint16_t* orow = op + (int64_t)qi * (qstride / 2);
 #pragma unroll

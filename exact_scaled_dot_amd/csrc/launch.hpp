@@ -17,6 +17,26 @@ struct ForwardArgs {
     float scale;
     bool causal;
     bool padded;
+    float* lse = nullptr;     // optional [B, Hq, Sq] natural-log log-sum-exp (16-bit dense path)
+};
+
+// Attention backward (16-bit inputs): dq [B,Hq,Sq,D], dk / dv [B,Hkv,Sk,D].
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;         // [B, Hq, Sq] from the forward
+    const int32_t* key_lens;  // nullptr unless key padding is on
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;             // workspace [B, Hq, Sq]: rowsum(dO * O)
+    int B, Hq, Hkv, Sq, Sk, D;
+    float scale;
+    bool causal;
+    bool padded;
 };
 
 struct DecodeArgs {
@@ -53,6 +73,9 @@ hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
 // bf16 or (f16) fp16.
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
                                       hipStream_t s);
+// Backward: the dQ pass (also writes delta), then the dK / dV pass.
+hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s);
+
 // Split-KV decode and paged attention, bf16 or (f16) fp16.
 hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s);
 hipError_t launch_paged_16bit(const DecodeArgs& a, const PagedArgs& p, bool f16, hipStream_t s);

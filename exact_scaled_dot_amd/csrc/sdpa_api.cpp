@@ -107,10 +107,14 @@ const char* sdpa_status_string(int status) {
 
 const char* sdpa_last_error(void) { return g_last_error; }
 
-sdpa_status_t sdpa_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
+}  // extern "C"
+
+namespace {
+
+sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
                            int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
-                           int mask_kind, const int32_t* key_lens, void* out, int dtype,
-                           void* stream) {
+                           int mask_kind, const int32_t* key_lens, void* out, float* lse,
+                           int dtype, void* stream) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st = check_common(q, k, v, out, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
                                     &kbytes);
@@ -127,6 +131,15 @@ sdpa_status_t sdpa_forward(const void* q, const void* k, const void* v, int64_t 
                     "key_lens must be given exactly when SDPA_MASK_KEY_PADDING is set");
     if (padded && overlap(out, qbytes, key_lens, B * (int64_t)sizeof(int32_t)))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps key_lens");
+    if (lse) {
+        if (dtype == SDPA_F32)
+            return fail(SDPA_ERR_UNSUPPORTED, "the log-sum-exp output needs 16-bit inputs");
+        const int64_t lbytes = B * Hq * Sq * (int64_t)sizeof(float);
+        if (overlap(lse, lbytes, out, qbytes) || overlap(lse, lbytes, q, qbytes) ||
+            overlap(lse, lbytes, k, kbytes) || overlap(lse, lbytes, v, kbytes) ||
+            (padded && overlap(lse, lbytes, key_lens, B * (int64_t)sizeof(int32_t))))
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "lse overlaps another tensor");
+    }
     const int64_t blocks = ((Sq + 127) / 128) * B * Hq;
     if (blocks > INT_MAX / 256)
         return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
@@ -146,12 +159,120 @@ sdpa_status_t sdpa_forward(const void* q, const void* k, const void* v, int64_t 
     a.scale = scale;
     a.causal = causal;
     a.padded = padded;
+    a.lse = lse;
     (void)hipGetLastError();  // clear an unrelated pending error
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == SDPA_BF16  ? sdpa::launch_forward_bf16(a, s)
                          : dtype == SDPA_F16 ? sdpa::launch_forward_f16(a, s)
                                              : sdpa::launch_forward_f32(a, s);
     return hip_status(e, "sdpa_forward launch");
+}
+
+// Rows per head in the backward's statistics workspace (8 bytes per row):
+// Sq rounded up to even, as the kernels index it.
+int64_t stats_rows(int64_t Sq) { return (Sq + 1) & ~int64_t(1); }
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                           int mask_kind, const int32_t* key_lens, void* out, int dtype,
+                           void* stream) {
+    return forward_impl(q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens, out, nullptr,
+                        dtype, stream);
+}
+
+sdpa_status_t sdpa_forward_lse(const void* q, const void* k, const void* v, int64_t B,
+                               int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                               float scale, int mask_kind, const int32_t* key_lens, void* out,
+                               float* lse, int dtype, void* stream) {
+    if (!lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "null lse pointer");
+    return forward_impl(q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens, out, lse,
+                        dtype, stream);
+}
+
+size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq) {
+    if (B < 1 || Hq < 1 || Sq < 1) return 0;
+    const int64_t rows = numel4(B, Hq, stats_rows(Sq), 1);
+    if (rows < 0 || rows > INT64_MAX / 16) return 0;
+    return round_up((size_t)rows * 2 * sizeof(float));
+}
+
+sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                            int mask_kind, const int32_t* key_lens, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    if (!out || !dout || !lse || !dk || !dv)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    int64_t qbytes = 0, kbytes = 0;
+    sdpa_status_t st = check_common(q, k, v, dq, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
+                                    &kbytes);
+    if (st != SDPA_OK) return st;
+    if (dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "the backward needs 16-bit inputs (bf16 or fp16)");
+    if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
+    const bool causal = mask_kind & SDPA_MASK_CAUSAL;
+    const bool padded = mask_kind & SDPA_MASK_KEY_PADDING;
+    if (causal && Sq != Sk)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "causal mask needs Sq == Sk (got %lld, %lld)",
+                    (long long)Sq, (long long)Sk);
+    if (padded != (key_lens != nullptr))
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "key_lens must be given exactly when SDPA_MASK_KEY_PADDING is set");
+    const size_t need = sdpa_backward_workspace_size(B, Hq, Sq);
+    if (!workspace || workspace_bytes < need)
+        return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace_bytes);
+    // Outputs and workspace overlap nothing else.
+    const int64_t lbytes = B * Hq * Sq * (int64_t)sizeof(float);
+    const int64_t kl = padded ? B * (int64_t)sizeof(int32_t) : 0;
+    struct Span {
+        const void* p;
+        int64_t n;
+    };
+    const Span ins[] = {{q, qbytes}, {k, kbytes}, {v, kbytes}, {out, qbytes},
+                        {dout, qbytes}, {lse, lbytes}, {key_lens, kl}};
+    const Span outs[] = {{dq, qbytes}, {dk, kbytes}, {dv, kbytes}, {workspace, (int64_t)need}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span& x : ins)
+            if (overlap(outs[i].p, outs[i].n, x.p, x.n))
+                return fail(SDPA_ERR_INVALID_ARGUMENT, "an output or the workspace overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(SDPA_ERR_INVALID_ARGUMENT, "outputs overlap each other or the workspace");
+    }
+    const int64_t qblocks = ((Sq + 127) / 128) * B * Hq, kblocks = ((Sk + 127) / 128) * B * Hkv;
+    if (qblocks > INT_MAX / 256 || kblocks > INT_MAX / 256)
+        return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large");
+
+    sdpa::BackwardArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.key_lens = key_lens;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = static_cast<float*>(workspace);
+    a.B = (int)B;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.Sq = (int)Sq;
+    a.Sk = (int)Sk;
+    a.D = (int)D;
+    a.scale = scale;
+    a.causal = causal;
+    a.padded = padded;
+    (void)hipGetLastError();
+    return hip_status(sdpa::launch_backward_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream)),
+                      "sdpa_backward launch");
 }
 
 size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_splits) {

@@ -27,7 +27,8 @@ MAX_SPLITS = 32
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
-EXPORTED = ("sdpa_forward", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_backward", "sdpa_backward_workspace_size",
+            "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
             "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
 
 _lib = None
@@ -52,6 +53,14 @@ def load_library():
     lib.sdpa_forward.restype = i32
     lib.sdpa_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, i32, vp,
                                  vp, i32, vp]
+    lib.sdpa_forward_lse.restype = i32
+    lib.sdpa_forward_lse.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, i32,
+                                     vp, vp, vp, i32, vp]
+    lib.sdpa_backward_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_backward_workspace_size.argtypes = [i64, i64, i64]
+    lib.sdpa_backward.restype = i32
+    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  ctypes.c_float, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, i32, vp]
     lib.sdpa_decode.restype = i32
     lib.sdpa_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, i32, vp,
                                 ctypes.c_size_t, vp, i32, vp]
@@ -114,8 +123,8 @@ def _check_tensor(name, t, ndim):
         raise ValueError("%s must be contiguous" % name)
 
 
-def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=None, stream=None):
-    """O = softmax(Q K^T * scale + mask) V.  q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D]."""
+def _check_qkv(q, k, v, key_lens):
+    """Shape / dtype checks shared by the dense entry points; returns the sizes."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, 4)
     if key_lens is not None:
@@ -128,6 +137,12 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=None, s
         raise ValueError("k and v must be [B, Hkv, Sk, D] matching q")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
+    return B, Hq, Hkv, Sq, Sk, D
+
+
+def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=None, stream=None):
+    """O = softmax(Q K^T * scale + mask) V.  q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D]."""
+    B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -139,6 +154,70 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=None, s
                             int(mask_kind), _ptr(key_lens), _ptr(out), _dtype_code(q),
                             _stream(stream)))
     return out
+
+
+def sdpa_forward_lse(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=None, lse=None,
+                     stream=None):
+    """sdpa_forward that also returns each row's log-sum-exp: (out, lse [B,Hq,Sq] fp32)."""
+    B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("lse", lse, 3)
+        if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, Hq, Sq]")
+    lib = load_library()
+    _check(lib.sdpa_forward_lse(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                int(mask_kind), _ptr(key_lens), _ptr(out), _ptr(lse),
+                                _dtype_code(q), _stream(stream)))
+    return out, lse
+
+
+def sdpa_backward_workspace_size(B, Hq, Sq):
+    return int(load_library().sdpa_backward_workspace_size(B, Hq, Sq))
+
+
+def sdpa_backward(q, k, v, out, dout, lse, scale, mask_kind=MASK_NONE, key_lens=None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of O = softmax(Q K^T * scale + mask) V given dout = dL/dO.
+
+    out and lse are the forward's (sdpa_forward_lse); dq is [B,Hq,Sq,D], dk and
+    dv [B,Hkv,Sk,D], all in the input dtype.
+    """
+    B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
+    for name, t in (("out", out), ("dout", dout)):
+        _check_tensor(name, t, 4)
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("%s must match q in shape and dtype" % name)
+    _check_tensor("lse", lse, 3)
+    if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Sq]")
+    outs = []
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _check_tensor(name, t, 4)
+            if t.shape != like.shape or t.dtype != like.dtype:
+                raise ValueError("%s must match its input in shape and dtype" % name)
+        outs.append(t)
+    dq, dk, dv = outs
+    need = sdpa_backward_workspace_size(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check(lib.sdpa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                             B, Hq, Hkv, Sq, Sk, D, float(scale), int(mask_kind), _ptr(key_lens),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _dtype_code(q),
+                             _stream(stream)))
+    return dq, dk, dv
 
 
 def sdpa_decode_workspace_size(B, Hq, D, num_splits):

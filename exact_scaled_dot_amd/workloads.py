@@ -74,6 +74,14 @@ def draw_qkv(B, Hq, Hkv, Sq, Sk, D, dtype, seed, device="cpu"):
     return tuple(out)
 
 
+def draw_grad(shape, dtype, seed, device="cpu"):
+    """Upstream gradient dO of the given shape: i.i.d. N(0,1) rounded to dtype."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 15485863)
+    t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
 def draw_key_lens(B, lo, hi, seed, device="cpu"):
     """Per-batch valid key lengths, uniform integers in [lo, hi] (int32)."""
     gen = torch.Generator(device="cpu")

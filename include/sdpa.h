@@ -101,6 +101,58 @@ sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
                            void *out, int dtype, void *stream);
 
 /*
+ * sdpa_forward that also writes each row's log-sum-exp, the statistic the
+ * backward recomputes the probabilities from (ruDNN guide section 11: the
+ * backward keeps no score matrix).
+ *   lse      device float [B, Hq, Sq]: lse_i = ln(sum_j exp(scale * s_ij))
+ *            over the visible keys j of row i (natural log, scaled-score
+ *            units), -inf for a row with no visible key
+ * Every other argument as sdpa_forward; lse must not overlap any tensor.
+ * Supported: dtype SDPA_BF16 or SDPA_F16 (SDPA_ERR_UNSUPPORTED for SDPA_F32).
+ */
+sdpa_status_t sdpa_forward_lse(const void *q, const void *k, const void *v,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                               int64_t D, float scale, int mask_kind, const int32_t *key_lens,
+                               void *out, float *lse, int dtype, void *stream);
+
+/*
+ * Bytes of device workspace sdpa_backward needs (0 if the sizes are invalid):
+ * 8 bytes per query row, rows of a head padded to an even count.
+ */
+size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq);
+
+/*
+ * Attention backward (ruDNN guide section 11; the derivative of the tensai
+ * guide's attention block): the gradients of a loss L through
+ * O = softmax(Q K^T * scale + mask) V, given dout = dL/dO,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - rowsum(dO o O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * with P recomputed as exp(scale * s_ij - lse_i) (hidden keys 0).  A K/V head's
+ * dK and dV sum over its Hq / Hkv query heads; rows with no visible key
+ * contribute nothing and get dQ = 0; keys at or past key_lens[b] get dK = dV = 0.
+ *   q, out, dout   device [B, Hq, Sq, D], dtype (out: the forward's output)
+ *   k, v           device [B, Hkv, Sk, D], dtype
+ *   lse            device float [B, Hq, Sq] from sdpa_forward_lse
+ *   scale, mask_kind, key_lens   as in the forward call
+ *   dq             device [B, Hq, Sq, D], dtype; written completely
+ *   dk, dv         device [B, Hkv, Sk, D], dtype; written completely
+ *   workspace      device buffer of at least sdpa_backward_workspace_size bytes
+ * Two kernels are enqueued on stream: a query-parallel pass (dQ, and each
+ * row's rowsum(dO o O) into the workspace) then a key-parallel pass (dK, dV).
+ * Every sum runs in a fixed order: the result is bitwise reproducible (the
+ * guide's ordered, atomic-free reduction).  Accumulation is fp32; P and dS are
+ * rounded to dtype before their products, and the gradients to dtype at the end.
+ * Outputs and workspace must not overlap each other or any input.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}.
+ */
+sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const void *out,
+                            const void *dout, const float *lse,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                            float scale, int mask_kind, const int32_t *key_lens,
+                            void *dq, void *dk, void *dv,
+                            void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/*
  * Bytes of device workspace sdpa_decode needs for these sizes (0 if the sizes
  * are invalid).  Layout, fp32, 256-byte aligned sections:
  *   o_part [B, Hq, num_splits, D]  normalised partial outputs

@@ -13,6 +13,13 @@ F32_MAX_ABS = 1e-4
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
 
+# Backward (dQ, dK, dV): P and dS are rounded to the input type before their
+# products, and each gradient to the input type at the end.  Bars per gradient
+# tensor, relative to its own scale: ||g - r||_2 / ||r||_2 and
+# max|g - r| / max|r|.
+GRAD_REL_L2 = {torch.bfloat16: 1e-2, torch.float16: 2e-3}
+GRAD_MAX_REL = {torch.bfloat16: 4e-2, torch.float16: 8e-3}
+
 
 def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
@@ -51,3 +58,22 @@ def sample_rows(B, Hq, Sq, n, seed, must=()):
     while len(rows) < n:
         rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq))))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def compare_grad(got, ref, dtype, what=""):
+    """Assert the backward bars on one gradient tensor; returns (max_rel, rel_l2)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), "%s: non-finite gradient" % what
+    scale = float(np.abs(ref).max())
+    if scale == 0.0:
+        assert not got.any(), "%s: reference is 0, got nonzero" % what
+        return 0.0, 0.0
+    max_rel = float(np.abs(got - ref).max()) / scale
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print("%s: max-rel %.3e rel-L2 %.3e" % (what, max_rel, rel))
+    assert rel <= GRAD_REL_L2[dtype], "%s: rel-L2 %.3e > %.0e" % (what, rel, GRAD_REL_L2[dtype])
+    assert max_rel <= GRAD_MAX_REL[dtype], "%s: max-rel %.3e > %.0e" % (
+        what, max_rel, GRAD_MAX_REL[dtype])
+    return max_rel, rel

@@ -211,3 +211,69 @@ def test_dtype_codes():
     assert prefill(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
     assert fwd(dtype=sd.SDPA_F16, D=96) == sd.SDPA_ERR_UNSUPPORTED  # reaches the head-dim check
     assert dec(dtype=sd.SDPA_F16, D=96) == sd.SDPA_ERR_UNSUPPORTED
+
+
+def fwd_lse(lse=ctypes.c_void_p(0x78000000), dtype=sd.SDPA_BF16, q=FAKE, out=FAKE_O, Sq=128):
+    lib = sd.load_library()
+    return lib.sdpa_forward_lse(q, FAKE_K, FAKE_V, 2, 4, 2, Sq, 128, 128, 0.125, 0, None, out, lse,
+                                dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), sd.SDPA_ERR_INVALID_ARGUMENT, "lse"),
+    (dict(q=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(lse=ctypes.c_void_p(0x60000000 + 4096)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
+    (dict(lse=ctypes.c_void_p(0x20000000 + 16)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
+])
+def test_forward_lse_rejects(kw, status, needle):
+    assert fwd_lse(**kw) == status
+    assert needle in sd.last_error()
+
+
+FAKE_DO = ctypes.c_void_p(0x68000000)
+FAKE_L = ctypes.c_void_p(0x6c000000)
+FAKE_DQ = ctypes.c_void_p(0x80000000)
+FAKE_DK = ctypes.c_void_p(0x90000000)
+FAKE_DV = ctypes.c_void_p(0xa0000000)
+FAKE_BW = ctypes.c_void_p(0xb0000000)
+
+
+def bwd(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128,
+        scale=0.125, mask=0, key_lens=None, dq=FAKE_DQ, dk=FAKE_DK, dv=FAKE_DV, ws=FAKE_BW,
+        ws_bytes=None, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.sdpa_backward_workspace_size(B, Hq, Sq)
+    return lib.sdpa_backward(q, FAKE_K, FAKE_V, out, dout, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask,
+                             key_lens, dq, dk, dv, ws, ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dout=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(lse=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(dq=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(D=256), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(mask=1, Sq=64), sd.SDPA_ERR_INVALID_ARGUMENT, "Sq == Sk"),
+    (dict(mask=2), sd.SDPA_ERR_INVALID_ARGUMENT, "key_lens"),
+    (dict(mask=8), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),
+    (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(dk=ctypes.c_void_p(0x68000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(dv=ctypes.c_void_p(0x90000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(ws=ctypes.c_void_p(0x6c000000)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(dq=ctypes.c_void_p(0x10000 + 2)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+])
+def test_backward_rejects(kw, status, needle):
+    assert bwd(**kw) == status
+    assert needle in sd.last_error()
+
+
+def test_backward_workspace_size():
+    lib = sd.load_library()
+    for B, Hq, Sq in [(4, 16, 4096), (1, 1, 1), (3, 5, 333)]:
+        rows = B * Hq * (Sq + (Sq & 1))
+        assert lib.sdpa_backward_workspace_size(B, Hq, Sq) == (rows * 8 + 255) // 256 * 256
+    for bad in [(0, 1, 1), (1, 0, 1), (1, 1, 0)]:
+        assert lib.sdpa_backward_workspace_size(*bad) == 0
