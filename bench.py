@@ -8,6 +8,10 @@ resident in HBM:
   * prefill, causal, bf16, B=4 Hq=Hkv=16 Sq=Sk=4096 D=128   (the headline)
   * prefill, grouped K/V 32/8 with key padding, bf16, B=2 S=8192 D=128
   * split-KV decode, bf16, B=64 Hq=32 Hkv=8 Sk=32768 D=128, 32 splits + merge
+  * the same decode over a shuffled 16-key page cache, and the causal prefill
+    as whole-sequence chunks over such a cache
+  * the attention backward (dQ, dK, dV) of the causal prefill workload, from
+    its forward output and log-sum-exp (computed once, before the timing)
 Each call is bracketed by HIP events on the stream it is launched on (torch's
 current stream, which is the stream the binding hands to the library).
 
@@ -15,7 +19,9 @@ current stream, which is the stream the binding hands to the library).
 4*B*Hq*Sq*Sk*D, halved when causal; `roofline` is that kernel's fraction of
 the bf16 dense MFMA peak.  The decode result (HBM GB/s over the K+V+Q+O bytes
 of one call, fraction of the 8 TB/s HBM peak) and the padded prefill are
-reported in their own objects on the same line.  `cpu_baseline` times the fp64
+reported in their own objects on the same line; the backward's TFLOP/s counts
+2.5 times the forward formula (five products of the same shape against two).
+`cpu_baseline` times the fp64
 oracle on a bounded sample of the causal prefill workload on the host cores.
 """
 
@@ -131,9 +137,16 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
 
     fwd = "forward_bf16_kernel"
     if fwd in fetch:  # a full step launches the causal prefill, the padded one, the paged one
-        out["prefill"] = entry(fwd, "forward.hip", fetch[fwd][0::3], write[fwd][0::3])
-        out["padded"] = entry(fwd, "forward.hip", fetch[fwd][1::3], write[fwd][1::3])
-        out["paged_prefill"] = entry(fwd, "forward.hip", fetch[fwd][2::3], write[fwd][2::3])
+        # (after one setup forward that gives the backward its output and lse)
+        fr, wr = fetch[fwd], write[fwd]
+        if len(fr) % 3 == 1:
+            fr, wr = fr[1:], wr[1:]
+        out["prefill"] = entry(fwd, "forward.hip", fr[0::3], wr[0::3])
+        out["padded"] = entry(fwd, "forward.hip", fr[1::3], wr[1::3])
+        out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::3], wr[2::3])
+    for key, name in (("backward_dq", "bwd_dq_kernel"), ("backward_dkdv", "bwd_dkdv_kernel")):
+        if name in fetch:
+            out[key] = entry(name, "backward.hip", fetch[name], write[name])
     # A full step runs the dense decode, then the paged one: their split and
     # merge dispatches alternate.
     for key, name in (("decode_split", "decode_split_bf16_kernel"),
@@ -152,7 +165,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill"],
+    ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
+                                       "backward"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -177,7 +191,7 @@ def main():
     import torch
 
     import exact_scaled_dot_amd as sd
-    from exact_scaled_dot_amd.workloads import WORKLOADS, draw_paged, make_inputs
+    from exact_scaled_dot_amd.workloads import WORKLOADS, draw_grad, draw_paged, make_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -210,6 +224,17 @@ def main():
                          wp.dtype, wp.seed, dev, extra_pages=0)
         ipp["cu"] = torch.arange(0, nq + 1, wp.Sq, dtype=torch.int32, device=dev)
         out_pp = torch.empty_like(ipp["q"])
+    # Backward: the causal prefill workload; its forward output and lse come
+    # from one forward call here, outside the timed region.
+    ibw = None
+    if args.only in (None, "backward"):
+        out_b, lse_b = sd.sdpa_forward_lse(ip["q"], ip["k"], ip["v"], wp.scale, sd.MASK_CAUSAL)
+        ibw = {"out": out_b, "lse": lse_b,
+               "dout": draw_grad(tuple(ip["q"].shape), wp.dtype, wp.seed, dev),
+               "dq": torch.empty_like(ip["q"]), "dk": torch.empty_like(ip["k"]),
+               "dv": torch.empty_like(ip["v"]),
+               "ws": torch.empty(sd.sdpa_backward_workspace_size(wp.B, wp.Hq, wp.Sq),
+                                 dtype=torch.uint8, device=dev)}
     torch.cuda.synchronize()
 
     calls = {
@@ -227,9 +252,12 @@ def main():
                                                        ipp["block_tables"], ipp["seq_lens"],
                                                        ipp["cu"], wp.scale, True, wp.Sq, wp.Sk,
                                                        out_pp),
+        "backward": lambda: sd.sdpa_backward(ip["q"], ip["k"], ip["v"], ibw["out"], ibw["dout"],
+                                             ibw["lse"], wp.scale, sd.MASK_CAUSAL, None,
+                                             ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"]),
     }
     order = ([args.only] if args.only else
-             ["prefill", "padded", "decode", "paged", "paged_prefill"])
+             ["prefill", "padded", "decode", "paged", "paged_prefill", "backward"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -326,8 +354,23 @@ def main():
                                                                        "forward.hip"),
                                              "kernel": "forward_bf16_kernel<128, paged>",
                                              "flops_per_launch": fl}}
-    if "value" not in rec:  # --only padded / decode / paged / paged_prefill: report that call
-        if "paged_prefill" in rec:
+    if "backward" in ms:
+        fl = 2.5 * formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
+        tf = fl / (ms["backward"] * 1e-3) / 1e12
+        rec["backward"] = {"workload": "bf16_causal_backward_b4_h16_s4096_d128",
+                           "ms": round(ms["backward"], 4), "value": round(tf, 3),
+                           "unit": "TFLOP/s",
+                           "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                        "traffic": None,
+                                        "kernel": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>",
+                                        "flops_per_launch": fl}}
+    if "value" not in rec:  # --only another call: report that call
+        if "backward" in rec:
+            rec.update({"value": rec["backward"]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec["backward"]["workload"]}
+        elif "paged_prefill" in rec:
             rec.update({"value": rec["paged_prefill"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["paged_prefill"]["workload"]}
         elif "paged" in rec:
@@ -340,7 +383,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp
+    del ip, ig, idd, ipg, ipp, ibw
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

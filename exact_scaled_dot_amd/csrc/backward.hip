@@ -66,6 +66,32 @@ __device__ __forceinline__ f32x4 lds_f4(const float* __restrict__ p) {
         (const __attribute__((address_space(3))) char*)p);
 }
 
+__device__ __forceinline__ void lds_st4(uint32_t* __restrict__ p, u32x4 v) {
+    *(__attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) char*)p) = v;
+}
+__device__ __forceinline__ u32x4 lds_ld4(const uint32_t* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) u32x4*)(
+        (const __attribute__((address_space(3))) char*)p);
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then s_barrier (__syncthreads() would also drain the DMA loads in flight).
+// The memory clobbers keep the compiler from moving accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// A packed 16-bit pair back to two floats (exact).
+template <class T>
+__device__ __forceinline__ float2 unpack2(uint32_t w) {
+    if constexpr (T::kF16) {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        return make_float2((float)h[0], (float)h[1]);
+    } else {
+        return make_float2(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u));
+    }
+}
+
 // Raw buffer resource over [base, base + bytes); loads beyond it return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -339,20 +365,43 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
 
 // ---------------------------------------------------------------------------
 // Pass 2: dK and dV.
+// A workgroup of 8 waves owns 128 keys of one (batch, K/V head).  Waves w and
+// w + 4 (one pair per SIMD) share keys 32w .. 32w+31 and split the work:
+//   wave w     (role P):  S = Q K^T, P = exp(scale S - lse) (masked), P to LDS,
+//                         dV^T += dO^T P
+//   wave w + 4 (role dS): dP = dO V^T, then (P from LDS) dS = P o (dP - delta),
+//                         dK^T += Q^T dS
+// so each wave holds one K/V operand and one accumulator (two waves fit per
+// SIMD) while the LDS reads per product stay those of 32-key blocks.  One LDS
+// barrier inside each step hands P over.  Products are v_mfma_f32_32x32x16:
+// S and dP are [query x key] with Q / dO as row-read A operands and K / V in
+// registers, so their accumulators hold key l%32 in each lane and are already
+// the B operands of the gradient products, whose A operands are transposed
+// reads of dO and Q.  P is exchanged rounded to the input type (the values
+// multiplied into dV).
 // Logical order: (batch, K/V head) outermost, then key blocks; under a causal
 // mask the first key blocks (which see the most queries) first.
 // ---------------------------------------------------------------------------
+constexpr int kKvThreads = 512;  // 8 waves
+
 template <int D, class T>
-__global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                                                                  const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
-    // Stage s: Q tile, dO tile, then the tile rows' (lse2, delta) pairs
-    // (512 B used of a 1-KB slot).
+    constexpr int NK = D / 16;              // contraction steps of S and dP
+    constexpr int ND = D / 32;              // 32-dim blocks of dK and dV
+    constexpr int DMA = L::TILE * 2 / 1024 / 8;  // 1-KB DMA loads per wave per tile
+    // Three stages of: Q tile, dO tile, the tile rows' (lse2, delta) pairs
+    // (512 B used of a 1-KB slot); then the P hand-over, 64 B per lane of
+    // each role-P wave.
     constexpr int STAGE = 2 * L::TILE + 512;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    constexpr int EX = 3 * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[3 * STAGE + 4 * 64 * 32];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int role = wave >> 2;  // 0: P and dV; 1: dS and dK
+    const int pair = wave & 3;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hg = lane >> 5;
@@ -367,21 +416,19 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
     int kv_lim = a.Sk;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
-    const int kw = k0 + 32 * wave;  // first key of this wave
+    const int kw = k0 + 32 * pair;  // first key of this pair
     const int kj = kw + l32;        // this lane's key
 
-    // K and V rows as B operands: lane holds key kj, dims 16t + 8hg .. +7.
-    u32x4 kr[D / 16], vr[D / 16];
+    // Role P holds K, role dS holds V, as B operands: key kj, dims 16t + 8hg .. +7.
+    u32x4 xr[NK];
     {
-        const uint32_t bytes = (uint32_t)a.Sk * D * 2;
-        const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const uint16_t*>(a.k) + kvh, bytes);
-        const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const uint16_t*>(a.v) + kvh, bytes);
+        const void* src = role ? a.v : a.k;
+        const __amdgpu_buffer_rsrc_t rx =
+            rsrc(static_cast<const uint16_t*>(src) + kvh, (uint32_t)a.Sk * D * 2);
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-            const uint32_t off = (uint32_t)kj * D * 2 + (16 * k + 8 * hg) * 2;
-            kr[k] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-            vr[k] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-        }
+        for (int k = 0; k < NK; ++k)
+            xr[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)kj * D * 2 + (16 * k + 8 * hg) * 2,
+                                                          0, 0);
     }
 
     // Query tiles: all of them, or (causal) those holding a row >= k0; a block
@@ -390,7 +437,15 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     const int nqt = (k0 < kv_lim) ? max(0, (a.Sq + kBwTile - 1) / kBwTile - qt0) : 0;
     const int steps = G * nqt;
 
-    const BwOffsets<D> off(wave, lane);
+    const BwOffsets<D> off(0, lane);  // row and transposed read offsets
+    uint32_t dmo[DMA];
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+        const int s = 64 * (DMA * wave + i) + lane;
+        const int r = s / L::CPR, pc = s % L::CPR;
+        dmo[i] = (uint32_t)r * D * 2 + (uint32_t)((pc ^ L::f(r)) * 16);
+    }
+
     auto issue = [&](int st, int stage) {
         const int h = gk * G + st / nqt;
         const int q0 = (qt0 + st % nqt) * kBwTile;
@@ -399,12 +454,12 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         const uint32_t bytes = (uint32_t)(a.Sq - q0) * D * 2;
         const __amdgpu_buffer_rsrc_t rq = rsrc(static_cast<const uint16_t*>(a.q) + qoff, bytes);
         const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const uint16_t*>(a.dout) + qoff, bytes);
-        uint16_t* dq = smem + stage * STAGE + 512 * L::DMA * wave;
+        uint16_t* dq = smem + stage * STAGE + 512 * DMA * wave;
         uint16_t* dd = dq + L::TILE;
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) {
-            dma(rq, dq + 512 * i, off.dma[i]);
-            dma(rd, dd + 512 * i, off.dma[i]);
+        for (int i = 0; i < DMA; ++i) {
+            dma(rq, dq + 512 * i, dmo[i]);
+            dma(rd, dd + 512 * i, dmo[i]);
         }
         if (wave == 0) {
             // 8 bytes per row; rows >= Sq read as zeros (and meet zero Q and
@@ -417,105 +472,153 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     };
 
     const float c = a.scale * kLog2e;
-    f32x16 dk[D / 32], dv[D / 32];
+    f32x16 acc[ND];  // role P: dV^T; role dS: dK^T
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
+    for (int db = 0; db < ND; ++db) acc[db] = f32x16{};
+    // The hand-over keeps 4 chunks of 16 B per lane; chunk i of lane l sits in
+    // slot (i + l/4) % 4, so 16 lanes storing one chunk hit 16 bank groups.
+    uint32_t* const ex = reinterpret_cast<uint32_t*>(smem + EX) + (pair * 64 + lane) * 16;
+    auto exslot = [&](int i) { return 4 * ((i + (lane >> 2)) & 3); };
 
-    // One 64-query tile of one query head: per 32-query block, S and dP, then
-    // P and dS, then dV^T += dO^T P and dK^T += Q^T dS.  Register r of a score
-    // block holds query q0 + 32*qb2 + 8*(r/4) + 4*hg + r%4 of key kj.
-    auto compute = [&](const uint16_t* qs, const uint16_t* ds, const float* st, int q0)
-                       __attribute__((always_inline)) {
+    // S (role P) or dP (role dS) of 32-query block qb: A = Q or dO rows.
+    // Register r holds query 32*qb + 8*(r/4) + 4*hg + r%4 of the tile, key kj.
+    auto scores = [&](const uint16_t* xs, int qb) __attribute__((always_inline)) -> f32x16 {
+        f32x16 sacc = {};
+        u32x4 fr[3];
+        fr[0] = lds_row(xs + 32 * qb * D + off.row[0]);
+        fr[1] = lds_row(xs + 32 * qb * D + off.row[1]);
 #pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-            const int qb0 = q0 + 32 * qb2;
-            f32x16 s = {}, dp = {};
+        for (int k = 0; k < NK; ++k) {
+            if (k + 2 < NK) fr[(k + 2) % 3] = lds_row(xs + 32 * qb * D + off.row[k + 2]);
+            sacc = mfma_32x32x16<T>(fr[k % 3], xr[k], sacc);
+        }
+        return sacc;
+    };
+    // acc^T += X^T W over 32-query block qb: A = transposed reads of X (dO for
+    // role P, Q for role dS), B = the block's 16-bit weights w (word 4*kk + i
+    // holds registers 8*kk + 2*i, +1).
+    auto grads = [&](const uint16_t* xs, int qb, const uint32_t* w) __attribute__((always_inline)) {
 #pragma unroll
-            for (int k = 0; k < D / 16; ++k) {
-                s = mfma_32x32x16<T>(lds_row(qs + 32 * qb2 * D + off.row[k]), kr[k], s);
-                dp = mfma_32x32x16<T>(lds_row(ds + 32 * qb2 * D + off.row[k]), vr[k], dp);
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4 bw = {w[4 * kk], w[4 * kk + 1], w[4 * kk + 2], w[4 * kk + 3]};
+            const uint16_t* xt = xs + (32 * qb + 16 * kk) * D;
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                const u32x2 lo = lds_tr(xt + off.trl[db]), hi = lds_tr(xt + off.trh[db]);
+                acc[db] = mfma_32x32x16<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, bw, acc[db]);
             }
-            const bool need_mask = a.causal && qb0 < kw + 31;
-            uint32_t pw[8], dw[8];
+        }
+    };
+
+    // One 64-query tile.  live: this pair has work here; mask: hide queries
+    // before key kj (causal diagonal).
+    auto compute = [&](const uint16_t* qs, const uint16_t* ds, const float* st, int q0, bool live,
+                       bool mask) __attribute__((always_inline)) {
+        if (role == 0) {
+            uint32_t pw[16];
+            if (live) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // (lse2, delta) of rows 32*qb2 + 8*i + 4*hg + 0..3.
-                const float* sp = st + 2 * (32 * qb2 + 8 * i + 4 * hg);
-                const f32x4 s01 = lds_f4(sp), s23 = lds_f4(sp + 4);
-                const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-                const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+                for (int qb = 0; qb < 2; ++qb) {
+                    const f32x16 s = scores(qs, qb);
 #pragma unroll
-                for (int j = 0; j < 4; j += 2) {
-                    const int r = 4 * i + j;
-                    float p0 = fast_exp2(fmaf(s[r], c, -l2[j]));
-                    float p1 = fast_exp2(fmaf(s[r + 1], c, -l2[j + 1]));
-                    if (need_mask) {
-                        const int q = qb0 + 8 * i + 4 * hg + j;
-                        if (kj > q) p0 = 0.f;
-                        if (kj > q + 1) p1 = 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        // lse2 of tile rows 32*qb + 8*i + 4*hg + 0..3
+                        const float* sp = st + 2 * (32 * qb + 8 * i + 4 * hg);
+                        const f32x4 s01 = lds_f4(sp), s23 = lds_f4(sp + 4);
+                        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+                        float p[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            p[j] = fast_exp2(fmaf(s[4 * i + j], c, -l2[j]));
+                            if (mask) p[j] = kj > q0 + 32 * qb + 8 * i + 4 * hg + j ? 0.f : p[j];
+                        }
+                        pw[8 * qb + 2 * i] = pack2<T>(p[0], p[1]);
+                        pw[8 * qb + 2 * i + 1] = pack2<T>(p[2], p[3]);
                     }
-                    pw[r >> 1] = pack2<T>(p0, p1);
-                    dw[r >> 1] = pack2<T>(p0 * (dp[r] - dl[j]), p1 * (dp[r + 1] - dl[j + 1]));
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_st4(ex + exslot(i), u32x4{pw[4 * i], pw[4 * i + 1], pw[4 * i + 2], pw[4 * i + 3]});
             }
+            lds_barrier();  // P handed over
+            if (live) {
+                grads(ds, 0, pw);
+                grads(ds, 1, pw + 8);
+            }
+        } else {
+            f32x16 dp[2];
+            if (live) {
+                dp[0] = scores(ds, 0);
+                dp[1] = scores(ds, 1);
+            }
+            lds_barrier();  // P handed over
+            if (live) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const u32x4 bp = {pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
-                const u32x4 bd = {dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]};
-                const uint16_t* qt = qs + (32 * qb2 + 16 * kk) * D;
-                const uint16_t* dt = ds + (32 * qb2 + 16 * kk) * D;
+                for (int qb = 0; qb < 2; ++qb) {
+                    uint32_t dw[8];
+                    const u32x4 p0 = lds_ld4(ex + exslot(2 * qb)), p1 = lds_ld4(ex + exslot(2 * qb + 1));
+                    const uint32_t pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const u32x2 dlo = lds_tr(dt + off.trl[db]), dhi = lds_tr(dt + off.trh[db]);
-                    dv[db] = mfma_32x32x16<T>(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, dv[db]);
-                    const u32x2 qlo = lds_tr(qt + off.trl[db]), qhi = lds_tr(qt + off.trh[db]);
-                    dk[db] = mfma_32x32x16<T>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, dk[db]);
+                    for (int i = 0; i < 4; ++i) {
+                        // delta of tile rows 32*qb + 8*i + 4*hg + 0..3
+                        const float* sp = st + 2 * (32 * qb + 8 * i + 4 * hg);
+                        const f32x4 s01 = lds_f4(sp), s23 = lds_f4(sp + 4);
+                        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+                        const float2 pa = unpack2<T>(pv[2 * i]), pb = unpack2<T>(pv[2 * i + 1]);
+                        const f32x16& x = dp[qb];
+                        dw[2 * i] = pack2<T>(pa.x * (x[4 * i] - dl[0]), pa.y * (x[4 * i + 1] - dl[1]));
+                        dw[2 * i + 1] = pack2<T>(pb.x * (x[4 * i + 2] - dl[2]), pb.y * (x[4 * i + 3] - dl[3]));
+                    }
+                    grads(qs, qb, dw);
                 }
             }
         }
     };
 
+    // Three LDS stages: the loads of step st+2 are issued at the start of step
+    // st, so each tile has two steps to arrive.
+    auto wait_older = [&](bool last) __attribute__((always_inline)) {
+        // Everything but this step's own loads has landed (vmcnt counts loads
+        // in issue order; wave 0 also issued the statistics load).
+        if (last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA) : "memory");
+    };
     if (steps > 0) issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (steps > 1) issue(1, 1);
+    wait_older(steps <= 1);
     __syncthreads();
     auto step = [&](int st, const int cur) __attribute__((always_inline)) {
-        if (st + 1 < steps) issue(st + 1, cur ^ 1);
+        if (st + 2 < steps) issue(st + 2, (cur + 2) % 3);
         const int q0 = (qt0 + st % nqt) * kBwTile;
-        if (kw < kv_lim && (!a.causal || q0 + kBwTile - 1 >= kw)) {
-            const uint16_t* base = smem + cur * STAGE;
-            compute(base, base + L::TILE, reinterpret_cast<const float*>(base + 2 * L::TILE), q0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const bool live = kw < kv_lim && (!a.causal || q0 + kBwTile - 1 >= kw);
+        const uint16_t* base = smem + cur * STAGE;
+        compute(base, base + L::TILE, reinterpret_cast<const float*>(base + 2 * L::TILE), q0, live,
+                a.causal && q0 < kw + 31);
+        wait_older(st + 2 >= steps);
         __syncthreads();
     };
-    for (int st = 0; st < steps; st += 2) {
+    for (int st = 0; st < steps; st += 3) {
         step(st, 0);
         if (st + 1 < steps) step(st + 1, 1);
+        if (st + 2 < steps) step(st + 2, 2);
     }
 
-    // dK = scale * (dS^T Q), dV = P^T dO: register r of d-block db holds dim
-    // 32*db + 8*(r/4) + 4*hg + r%4 of key kj.  Keys at or past the batch's
-    // key limit were never visible: their gradients are 0.
+    // Role P: dV = P^T dO; role dS: dK = scale * (dS^T Q).  Register r of
+    // d-block db holds dim 32*db + 8*(r/4) + 4*hg + r%4 of key kj.  Keys at or
+    // past the batch's key limit were never visible: their gradients are 0.
     if (kj < a.Sk) {
-        const bool live = kj < kv_lim;
-        const float ks = live ? a.scale : 0.f, vs = live ? 1.f : 0.f;
-        uint16_t* krow = static_cast<uint16_t*>(a.dk) + kvh + (int64_t)kj * D;
-        uint16_t* vrow = static_cast<uint16_t*>(a.dv) + kvh + (int64_t)kj * D;
+        const bool keep = kj < kv_lim;
+        const float sc = keep ? (role ? a.scale : 1.f) : 0.f;
+        uint16_t* row = static_cast<uint16_t*>(role ? a.dk : a.dv) + kvh + (int64_t)kj * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x16& x = dk[db];
-                const f32x16& y = dv[db];
-                const u32x2 wk = {pack2<T>(x[4 * r4] * ks, x[4 * r4 + 1] * ks),
-                                  pack2<T>(x[4 * r4 + 2] * ks, x[4 * r4 + 3] * ks)};
-                const u32x2 wv = {pack2<T>(y[4 * r4] * vs, y[4 * r4 + 1] * vs),
-                                  pack2<T>(y[4 * r4 + 2] * vs, y[4 * r4 + 3] * vs)};
-                *reinterpret_cast<u32x2*>(krow + 32 * db + 8 * r4 + 4 * hg) = wk;
-                *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * r4 + 4 * hg) = wv;
+                const f32x16& x = acc[db];
+                const u32x2 w = {pack2<T>(x[4 * r4] * sc, x[4 * r4 + 1] * sc),
+                                 pack2<T>(x[4 * r4 + 2] * sc, x[4 * r4 + 3] * sc)};
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * r4 + 4 * hg) = w;
             }
     }
 }
@@ -528,7 +631,7 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
                        a.key_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.B * a.Hkv * nkb), dim3(kBwThreads), 0, s,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.B * a.Hkv * nkb), dim3(kKvThreads), 0, s,
                        a, a.key_lens);
     return hipGetLastError();
 }
