@@ -65,6 +65,12 @@ def stored_traffic(workload, source):
     return rec.get("hbm_bytes_per_launch")
 
 
+def backward_traffic():
+    """HBM bytes of one backward call (both passes), if both records are valid."""
+    parts = [stored_traffic(k, "backward.hip") for k in ("backward_dq", "backward_dkdv")]
+    return None if None in parts else sum(parts)
+
+
 def formula_flops(B, Hq, Sq, Sk, D, causal):
     f = 4.0 * B * Hq * Sq * Sk * D
     return f / 2 if causal else f
@@ -363,7 +369,7 @@ def main():
                            "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                        "traffic": None,
+                                        "traffic": backward_traffic(),
                                         "kernel": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>",
                                         "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
