@@ -28,10 +28,15 @@ reordered:
   agree exactly in real arithmetic because softmax is shift invariant.
 * output     o_i = sum_j a_ij v_j   (HOF essay section 4: weights.dot(v)).
 * lse        lse_i = m_i + ln(sum_j exp(z_ij - m_i))  (the log of the softmax
-  denominator, used by the split-KV partials).
+  denominator, used by the split-KV partials); -inf for a row with no
+  visible key (the log of an empty sum).
 * head map   query head h reads K/V head floor(h / (Hq / Hkv)) (grouped K/V,
   ruDNN user guide section 9 "ページ化アテンションと MLA": Hq must be divisible
   by Hkv; contiguous groups is the reading taken).
+* bias       a general additive mask [B or 1, Hq or 1, Sq, Sk] added to the
+  scaled scores next to the 0 / -inf masks (tensai guide, "Attention の
+  組み立て": the scores are scaled and then Add(mask) with a mask tensor that
+  broadcasts over its size-1 batch and head axes); -inf entries hide keys.
 * split-KV   partial attention over disjoint key ranges, each with its own lse,
   and the log-sum-exp merge of those partials (ruDNN user guide section 9:
   history split into 2..=32 pieces, partial statistics and merge in FP32).
@@ -95,34 +100,61 @@ def visible_rows(mask_kind, rows, Sk, key_len):
     return vis
 
 
-def attend(qrows, kh, vh, scale, vis):
+def attend(qrows, kh, vh, scale, vis, bias=None):
     """Attention of query rows over one K/V head, by the definition.
 
-    qrows [n, D], kh and vh [Sk, D], vis [n, Sk] bool.  Returns
-    (o [n, D], lse [n], a [n, Sk]) in fp64.
+    qrows [n, D], kh and vh [Sk, D], vis [n, Sk] bool, bias None or [n, Sk]
+    (an additive mask, added to the scaled scores like the 0 / -inf one).
+    Returns (o [n, D], lse [n], a [n, Sk]) in fp64.
     """
     qrows = np.asarray(qrows, dtype=np.float64)
     kh = np.asarray(kh, dtype=np.float64)
     vh = np.asarray(vh, dtype=np.float64)
     s = float(scale) * (qrows @ kh.T)          # scale first ...
-    z = np.where(vis, s, -np.inf)              # ... then the additive 0 / -inf mask
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)   # ... then the additive masks:
+    z = np.where(vis, s, -np.inf)              # the bias, and the 0 / -inf mask
     with np.errstate(invalid="ignore", divide="ignore"):
         m = z.max(axis=1, keepdims=True)
         e = np.exp(z - m)                      # exp(-inf) = 0 on hidden keys
         l = e.sum(axis=1, keepdims=True)
         a = e / l                              # row-stochastic weights
         o = a @ vh
-        lse = (m + np.log(l))[:, 0]
+        # ln of the denominator; a row with no visible key has the empty sum,
+        # ln 0 = -inf (the max-shifted form would give NaN there)
+        lse = np.where(np.isneginf(m[:, 0]), -np.inf, (m + np.log(l))[:, 0])
     return o, lse, a
 
 
+def bias_slice(bias, b, h):
+    """The [Sq, Sk] additive mask of (batch b, query head h) from a bias of
+    shape [B or 1, Hq or 1, Sq, Sk] (a size-1 axis broadcasts, as the tensai
+    guide's (1, 1, seq, seq) mask does over batch and heads)."""
+    if bias is None:
+        return None
+    return bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
+
+
+def _check_bias(bias, B, Hq, Sq, Sk):
+    if bias is None:
+        return None
+    bias = np.asarray(bias)
+    if (bias.ndim != 4 or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq)
+            or bias.shape[2:] != (Sq, Sk)):
+        raise ValueError("bias must be [B or 1, Hq or 1, Sq, Sk], got %s" % (bias.shape,))
+    return bias
+
+
 def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
-                 return_lse=False, return_probs=False):
+                 return_lse=False, return_probs=False, bias=None):
     """Full forward O = softmax(Q K^T * scale + mask) V for every (b, h, i).
 
     q [B,Hq,Sq,D], k and v [B,Hkv,Sk,D]; key_lens [B] when mask_kind has the
     key-padding bit.  The causal mask is defined for square attention only
     (the tensai guide's (seq, seq) mask), so causal with Sq != Sk is an error.
+    bias: optional general additive mask [B or 1, Hq or 1, Sq, Sk] added to
+    the scaled scores (the tensai guide's Add(mask) with any mask tensor),
+    together with the causal / padding masks.
     Returns o (fp64), plus lse [B,Hq,Sq] and/or probs [B,Hq,Sq,Sk] on request.
     """
     q = np.asarray(q)
@@ -132,6 +164,7 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
         raise ValueError("causal mask needs Sq == Sk")
     if bool(mask_kind & MASK_KEY_PADDING) != (key_lens is not None):
         raise ValueError("key_lens is given exactly when the key-padding bit is set")
+    bias = _check_bias(bias, B, Hq, Sq, Sk)
     G = Hq // Hkv
     o = np.empty((B, Hq, Sq, D), dtype=np.float64)
     lse = np.empty((B, Hq, Sq), dtype=np.float64)
@@ -141,7 +174,8 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
         vis = visible_rows(mask_kind, rows, Sk, key_lens[b] if key_lens is not None else 0)
         for h in range(Hq):
             g = h // G
-            o[b, h], lse[b, h], a = attend(q[b, h], k[b, g], v[b, g], scale, vis)
+            o[b, h], lse[b, h], a = attend(q[b, h], k[b, g], v[b, g], scale, vis,
+                                           bias_slice(bias, b, h))
             if return_probs:
                 probs[b, h] = a
     out = [o]
@@ -152,12 +186,13 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def sdpa_forward_rows(q, k, v, scale, mask_kind, key_lens, index):
+def sdpa_forward_rows(q, k, v, scale, mask_kind, key_lens, index, bias=None):
     """Selected output rows only: index is an int array [n, 3] of (b, h, i).
 
     Same definition as sdpa_forward, evaluated only for the listed query rows
-    (grouped by head) so that it scales to full-size workloads.  q, k, v may be
-    any array-likes indexable as [b, h] (only the needed heads are read).
+    (grouped by head) so that it scales to full-size workloads.  q, k, v (and
+    bias, [B or 1, Hq or 1, Sq, Sk]) may be any array-likes indexable as
+    [b, h] (only the needed heads are read).
     Returns (o [n, D], lse [n]) in the order of index.
     """
     B, Hq, _ = q.shape[0], q.shape[1], q.shape[2]
@@ -180,7 +215,10 @@ def sdpa_forward_rows(q, k, v, scale, mask_kind, key_lens, index):
         vis = visible_rows(mask_kind, rows, Sk, klen)
         g = h // G
         qh = np.asarray(q[b, h])
-        o[pos], lse[pos], _ = attend(qh[rows], k[b, g], v[b, g], scale, vis)
+        bh = None
+        if bias is not None:
+            bh = np.asarray(bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0])[rows]
+        o[pos], lse[pos], _ = attend(qh[rows], k[b, g], v[b, g], scale, vis, bh)
     return o, lse
 
 
@@ -353,5 +391,5 @@ __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KEY_PADDING", "visible_rows", "attend",
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
     "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
-    "chunk_positions", "sdpa_backward",
+    "chunk_positions", "sdpa_backward", "bias_slice",
 ]

@@ -615,3 +615,99 @@ def test_backward_hidden_keys_and_dead_rows():
     dq, dk, dv = O.sdpa_backward(q, k, v, g, 0.5, O.MASK_KEY_PADDING, np.array([4, 0]))
     assert (dk[0, :, 4:] == 0).all() and (dv[0, :, 4:] == 0).all()     # padded keys
     assert (dq[1] == 0).all() and (dk[1] == 0).all() and (dv[1] == 0).all()  # no visible key
+
+
+# ------------------------------------------------------------------ additive bias
+
+def _bias_inputs(seed, B=2, Hq=4, Hkv=2, Sq=6, Sk=6, D=5):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Hq, Sq, D)), rng.standard_normal((B, Hkv, Sk, D)),
+            rng.standard_normal((B, Hkv, Sk, D)), rng)
+
+
+def test_bias_zero_is_no_bias():
+    q, k, v, _ = _bias_inputs(70)
+    ref = O.sdpa_forward(q, k, v, 0.6, O.MASK_CAUSAL)
+    got = O.sdpa_forward(q, k, v, 0.6, O.MASK_CAUSAL, bias=np.zeros((1, 1, 6, 6)))
+    assert np.array_equal(ref, got)
+
+
+def test_bias_of_zeros_and_minus_inf_is_the_causal_and_padding_masks():
+    q, k, v, _ = _bias_inputs(71)
+    tri = np.where(np.arange(6)[None, :] <= np.arange(6)[:, None], 0.0, -np.inf)
+    assert np.array_equal(O.sdpa_forward(q, k, v, 0.6, O.MASK_CAUSAL),
+                          O.sdpa_forward(q, k, v, 0.6, bias=tri[None, None]))
+    lens = np.array([4, 2])
+    pad = np.zeros((2, 1, 6, 6))
+    pad[0, :, :, 4:] = -np.inf
+    pad[1, :, :, 2:] = -np.inf
+    assert np.array_equal(O.sdpa_forward(q, k, v, 0.6, O.MASK_KEY_PADDING, lens),
+                          O.sdpa_forward(q, k, v, 0.6, bias=pad))
+
+
+def test_row_constant_bias_changes_nothing():
+    # softmax is shift invariant along a row
+    q, k, v, rng = _bias_inputs(72)
+    c = rng.standard_normal((2, 4, 6, 1)) * 5
+    np.testing.assert_allclose(O.sdpa_forward(q, k, v, 0.6, bias=np.broadcast_to(c, (2, 4, 6, 6))),
+                               O.sdpa_forward(q, k, v, 0.6), rtol=0, atol=1e-12)
+
+
+def test_bias_zero_query_closed_form():
+    # Q = 0: the weights of row i are softmax(bias[i]) exactly, independent of scale
+    _, k, v, rng = _bias_inputs(73)
+    q = np.zeros((2, 4, 6, 5))
+    bias = rng.standard_normal((2, 4, 6, 6)) * 2
+    got = O.sdpa_forward(q, k, v, 3.0, bias=bias)
+    for b in range(2):
+        for h in range(4):
+            for i in range(6):
+                w = [math.exp(x) for x in bias[b, h, i]]
+                tot = math.fsum(w)
+                ref = [math.fsum(w[j] / tot * v[b, h // 2, j, d] for j in range(6)) for d in range(5)]
+                np.testing.assert_allclose(got[b, h, i], ref, rtol=0, atol=1e-13)
+
+
+def test_bias_brute_force_is_added_after_the_scale():
+    # exp(scale * q.k + bias) by scalar loops; scale != 1 separates the
+    # bias from the scaled scores
+    q, k, v, rng = _bias_inputs(74, B=1, Hq=2, Hkv=1, Sq=3, Sk=4, D=2)
+    bias = rng.standard_normal((1, 2, 3, 4))
+    got = O.sdpa_forward(q, k, v, 0.35, O.MASK_NONE, bias=bias)
+    for h in range(2):
+        for i in range(3):
+            z = [0.35 * math.fsum(q[0, h, i, d] * k[0, 0, j, d] for d in range(2)) + bias[0, h, i, j]
+                 for j in range(4)]
+            w = [math.exp(x) for x in z]
+            tot = math.fsum(w)
+            ref = [math.fsum(w[j] / tot * v[0, 0, j, d] for j in range(4)) for d in range(2)]
+            np.testing.assert_allclose(got[0, h, i], ref, rtol=0, atol=1e-13)
+
+
+def test_bias_broadcasts_over_size_one_axes():
+    q, k, v, rng = _bias_inputs(75)
+    per_head = rng.standard_normal((1, 4, 6, 6))
+    per_batch = rng.standard_normal((2, 1, 6, 6))
+    np.testing.assert_array_equal(O.sdpa_forward(q, k, v, 0.6, bias=per_head),
+                                  O.sdpa_forward(q, k, v, 0.6, bias=np.repeat(per_head, 2, axis=0)))
+    np.testing.assert_array_equal(O.sdpa_forward(q, k, v, 0.6, bias=per_batch),
+                                  O.sdpa_forward(q, k, v, 0.6, bias=np.repeat(per_batch, 4, axis=1)))
+    # a query head's bias is its own, not its K/V head's
+    h_only = np.zeros((1, 4, 6, 6))
+    h_only[0, 1] = rng.standard_normal((6, 6)) * 3
+    got = O.sdpa_forward(q, k, v, 0.6, bias=h_only)
+    base = O.sdpa_forward(q, k, v, 0.6)
+    assert np.array_equal(got[:, [0, 2, 3]], base[:, [0, 2, 3]])
+    assert not np.allclose(got[:, 1], base[:, 1])
+
+
+def test_bias_rows_equal_full_and_minus_inf_row_is_nan():
+    q, k, v, rng = _bias_inputs(76)
+    bias = rng.standard_normal((1, 4, 6, 6))
+    bias[0, 2, 3, :] = -np.inf
+    full, lse = O.sdpa_forward(q, k, v, 0.6, O.MASK_CAUSAL, bias=bias, return_lse=True)
+    idx = np.array([[0, 0, 0], [1, 3, 5], [0, 2, 3], [1, 1, 2]])
+    o, l = O.sdpa_forward_rows(q, k, v, 0.6, O.MASK_CAUSAL, None, idx, bias=bias)
+    for n, (b, h, i) in enumerate(idx):
+        np.testing.assert_allclose(o[n], full[b, h, i], rtol=0, atol=1e-14)
+    assert np.isnan(full[:, 2, 3]).all() and np.isneginf(lse[:, 2, 3]).all()
