@@ -12,6 +12,8 @@ resident in HBM:
     as whole-sequence chunks over such a cache
   * the attention backward (dQ, dK, dV) of the causal prefill workload, from
     its forward output and log-sum-exp (computed once, before the timing)
+  * the causal prefill with a general additive mask: a per-head bias tensor
+    [1, 16, 4096, 4096] bf16 added to the scaled scores
 Each call is bracketed by HIP events on the stream it is launched on (torch's
 current stream, which is the stream the binding hands to the library).
 
@@ -144,12 +146,14 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     fwd = "forward_bf16_kernel"
     if fwd in fetch:  # a full step launches the causal prefill, the padded one, the paged one
         # (after one setup forward that gives the backward its output and lse)
+        # (a step: causal prefill, padded prefill, paged prefill, bias prefill)
         fr, wr = fetch[fwd], write[fwd]
-        if len(fr) % 3 == 1:
+        if len(fr) % 4 == 1:
             fr, wr = fr[1:], wr[1:]
-        out["prefill"] = entry(fwd, "forward.hip", fr[0::3], wr[0::3])
-        out["padded"] = entry(fwd, "forward.hip", fr[1::3], wr[1::3])
-        out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::3], wr[2::3])
+        out["prefill"] = entry(fwd, "forward.hip", fr[0::4], wr[0::4])
+        out["padded"] = entry(fwd, "forward.hip", fr[1::4], wr[1::4])
+        out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::4], wr[2::4])
+        out["bias"] = entry(fwd, "forward.hip", fr[3::4], wr[3::4])
     for key, name in (("backward_dq", "bwd_dq_kernel"), ("backward_dkdv", "bwd_dkdv_kernel")):
         if name in fetch:
             out[key] = entry(name, "backward.hip", fetch[name], write[name])
@@ -172,7 +176,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward"],
+                                       "backward", "bias"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -197,7 +201,8 @@ def main():
     import torch
 
     import exact_scaled_dot_amd as sd
-    from exact_scaled_dot_amd.workloads import WORKLOADS, draw_grad, draw_paged, make_inputs
+    from exact_scaled_dot_amd.workloads import (WORKLOADS, draw_bias, draw_grad, draw_paged,
+                                                 make_inputs)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -241,6 +246,11 @@ def main():
                "dv": torch.empty_like(ip["v"]),
                "ws": torch.empty(sd.sdpa_backward_workspace_size(wp.B, wp.Hq, wp.Sq),
                                  dtype=torch.uint8, device=dev)}
+    # Bias: the causal prefill workload with a per-head [1, Hq, Sq, Sk] bias.
+    ibias = None
+    if args.only in (None, "bias"):
+        ibias = {"bias": draw_bias((1, wp.Hq, wp.Sq, wp.Sk), wp.dtype, wp.seed, dev),
+                 "out": torch.empty_like(ip["q"])}
     torch.cuda.synchronize()
 
     calls = {
@@ -262,8 +272,10 @@ def main():
                                              ibw["lse"], wp.scale, sd.MASK_CAUSAL, None,
                                              ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"]),
     }
+    calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
+                                                 sd.MASK_CAUSAL, None, ibias["out"])
     order = ([args.only] if args.only else
-             ["prefill", "padded", "decode", "paged", "paged_prefill", "backward"])
+             ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "bias"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -372,8 +384,30 @@ def main():
                                         "traffic": backward_traffic(),
                                         "kernel": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>",
                                         "flops_per_launch": fl}}
+    if "bias" in ms:
+        fl = formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
+        tf = fl / (ms["bias"] * 1e-3) / 1e12
+        # bias bytes the kernel must read: the visible (causal) part of each
+        # (batch, head)'s [Sq, Sk] slice, at 2 bytes, whole 64-key tiles
+        nqb = wp.Sq // 128
+        tiles = sum(2 * (qb + 1) for qb in range(nqb))          # 64-key tiles per (b, h)
+        bias_bytes = wp.B * wp.Hq * 128 * 64 * 2 * tiles
+        rec["bias"] = {"workload": "bf16_causal_bias_b4_h16_s4096_d128",
+                       "ms": round(ms["bias"], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                       "bias_shape": [1, wp.Hq, wp.Sq, wp.Sk],
+                       "bias_bytes_read": bias_bytes,
+                       "bias_gbs": round(bias_bytes / (ms["bias"] * 1e-3) / 1e9, 1),
+                       "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                    "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                    "traffic": stored_traffic("bias", "forward.hip"),
+                                    "kernel": "forward_bf16_kernel<128, bias>",
+                                    "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
-        if "backward" in rec:
+        if "bias" in rec:
+            rec.update({"value": rec["bias"]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec["bias"]["workload"]}
+        elif "backward" in rec:
             rec.update({"value": rec["backward"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["backward"]["workload"]}
         elif "paged_prefill" in rec:
@@ -389,7 +423,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw
+    del ip, ig, idd, ipg, ipp, ibw, ibias
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -131,6 +131,16 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
         return pack_bf16x2(a, b);
     }
 }
+// Element `hi` (0: low half, 1: high half) of a packed 16-bit pair as fp32 (exact).
+template <class T>
+__device__ __forceinline__ float bias_elem(uint32_t w, int hi) {
+    if constexpr (T::kF16) {
+        const uint16_t h = (uint16_t)(hi ? (w >> 16) : (w & 0xffffu));
+        return (float)__builtin_bit_cast(_Float16, h);
+    } else {
+        return __builtin_bit_cast(float, hi ? (w & 0xffff0000u) : (w << 16));
+    }
+}
 // acc + lo + hi of a packed pair, in fp32 (v_dot2 with (1, 1)).
 template <class T>
 __device__ __forceinline__ float sum2(uint32_t w, float acc) {

@@ -175,7 +175,13 @@ struct Bf16Geo {
 // resource over that page, the wave-uniform row offset in the scalar offset.
 // A table entry outside the cache is never read; its 16 keys are hidden
 // (validity shared through LDS).
-template <int D, bool PAGED, class T>
+//
+// BIAS (dense only): an additive mask tile is added to the scaled scores.
+// Lane (row qi, half hg) holds keys 16g + 8hg .. +7 (g = 0..3) of a tile, so
+// it loads those four 16-byte runs of its bias row (one tile ahead, next to
+// the DMA issue) and adds bias / scale in raw-score units during the mask
+// step; every visited tile takes the mask step.
+template <int D, bool PAGED, class T, bool BIAS = false>
 __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
@@ -244,6 +250,22 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         for (int t = 0; t < D / 16; ++t)
             qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qi * qstride + (16 * t + 8 * hg) * 2, 0, 0);
     }
+
+    // Bias: a resource over this (batch, head)'s [Sq, Sk] slice (rows >= Sq
+    // and keys >= Sk read as 0); bq holds the four 16-byte runs of the next
+    // tile to be masked.
+    u32x4 bq[4];
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(
+        BIAS ? static_cast<const uint16_t*>(a.bias) + ti.b * a.bias_sb + ti.h * a.bias_sh : qbase,
+        BIAS ? (uint32_t)a.Sq * a.Sk * 2 : 0u);
+    const uint32_t brow = BIAS ? (uint32_t)qi * a.Sk * 2 + 16 * hg : 0u;
+    auto load_bias = [&](int j0) __attribute__((always_inline)) {
+        if constexpr (BIAS) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bq[g] = __builtin_amdgcn_raw_buffer_load_b128(brs, brow + (uint32_t)(j0 + 16 * g) * 2, 0, 0);
+        }
+    };
 
     // DMA source offsets (bytes, relative to the tile's first key).  DMA load i
     // of this wave fills LDS bytes [1024*(DMA*wave + i), +1024) of a tile;
@@ -380,7 +402,21 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     auto mask_tile = [&](int j0, f32x16 (&sacc)[2], int vmask) __attribute__((always_inline)) {
         bool need_mask = (a.causal && j0 + kBc - 1 > qoff + qw) || (j0 + kBc > kv_lim);
         if (PAGED) need_mask = need_mask || vmask != 15;
-        if (need_mask) {
+        if constexpr (BIAS) {
+            // score + bias / scale, then the causal / key-limit hiding on
+            // every element: one per-lane limit per tile (first hidden key
+            // offset) against the element's constant key offset.
+            const float inv_scale = 1.f / a.scale;
+            const int lim = (a.causal ? min(kv_lim, qi + 1) : kv_lim) - j0 - 8 * hg;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int g = 2 * kb2 + (r >> 3), e = r & 7;
+                    const float bv = fmaf(bias_elem<T>(bq[g][e >> 1], e & 1), inv_scale, sacc[kb2][r]);
+                    sacc[kb2][r] = (32 * kb2 + 16 * (r >> 3) + (r & 7) >= lim) ? -INFINITY : bv;
+                }
+        } else if (need_mask) {
             if constexpr (PAGED) {
                 // A group on an invalid page gets a -inf bias (wave-uniform, so
                 // this stays straight-line code: an add and a select per score).
@@ -473,6 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         issue_v(0, 0);
     }
     if (ntiles > 1) issue_k(kBc, 1);
+    if (ntiles > 0) load_bias(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 sA[2], sB[2];
@@ -494,6 +531,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         const int vnext = tile_validity((jt + 1) * kBc);
         if (jt + 2 < ntiles) issue_k((jt + 2) * kBc, cur);
         if (jt + 1 < ntiles) issue_v((jt + 1) * kBc, cur ^ 1);
+        if (BIAS && jt + 1 < wave_tiles) load_bias((jt + 1) * kBc);
         if (jt < wave_tiles) {
             uint32_t pk[2][8];
             if (jt + 1 < wave_tiles) scores(smem + (cur ^ 1) * L::TILE, snext);
@@ -701,14 +739,14 @@ inline dim3 forward_grid(const ForwardArgs& a) {
     return dim3((unsigned)(nqb * a.B * a.Hq));
 }
 
-template <bool PAGED, class T>
+template <bool PAGED, class T, bool BIAS = false>
 hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
     if (a.D == 64)
-        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T>), forward_grid(a), dim3(kThreads), 0, s,
-                           a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS>), forward_grid(a), dim3(kThreads), 0,
+                           s, a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else if (a.D == 128)
-        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T>), forward_grid(a), dim3(kThreads), 0, s,
-                           a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS>), forward_grid(a), dim3(kThreads), 0,
+                           s, a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -717,11 +755,13 @@ hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s)
 }  // namespace
 
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s) {
-    return launch_16bit<false, Bf16T>(a, PagedArgs{}, s);
+    return a.bias ? launch_16bit<false, Bf16T, true>(a, PagedArgs{}, s)
+                  : launch_16bit<false, Bf16T>(a, PagedArgs{}, s);
 }
 
 hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s) {
-    return launch_16bit<false, F16T>(a, PagedArgs{}, s);
+    return a.bias ? launch_16bit<false, F16T, true>(a, PagedArgs{}, s)
+                  : launch_16bit<false, F16T>(a, PagedArgs{}, s);
 }
 
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,

@@ -18,6 +18,10 @@ struct ForwardArgs {
     bool causal;
     bool padded;
     float* lse = nullptr;     // optional [B, Hq, Sq] natural-log log-sum-exp (16-bit dense path)
+    // Optional additive mask (16-bit dense path): element (b, h, i, j) at
+    // bias[b * bias_sb + h * bias_sh + i * Sk + j], input dtype.
+    const void* bias = nullptr;
+    int64_t bias_sb = 0, bias_sh = 0;
 };
 
 // Attention backward (16-bit inputs): dq [B,Hq,Sq,D], dk / dv [B,Hkv,Sk,D].

@@ -114,7 +114,8 @@ namespace {
 sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
                            int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
                            int mask_kind, const int32_t* key_lens, void* out, float* lse,
-                           int dtype, void* stream) {
+                           int dtype, void* stream, const void* bias = nullptr,
+                           int64_t bias_sb = 0, int64_t bias_sh = 0) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st = check_common(q, k, v, out, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
                                     &kbytes);
@@ -140,6 +141,29 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
             (padded && overlap(lse, lbytes, key_lens, B * (int64_t)sizeof(int32_t))))
             return fail(SDPA_ERR_INVALID_ARGUMENT, "lse overlaps another tensor");
     }
+    if (bias) {
+        if (dtype == SDPA_F32)
+            return fail(SDPA_ERR_UNSUPPORTED, "an additive bias needs 16-bit inputs");
+        if (bias_sb < 0 || bias_sh < 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "bias strides must be >= 0");
+        if (Sk % 8 != 0 || bias_sb % 8 != 0 || bias_sh % 8 != 0 ||
+            reinterpret_cast<uintptr_t>(bias) % 16 != 0)
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "bias rows must be 16-byte aligned (Sk and the strides multiples of 8, "
+                        "pointer 16-byte aligned)");
+        if (Sq * Sk * 2 > INT_MAX)
+            return fail(SDPA_ERR_UNSUPPORTED, "one head's bias exceeds 2 GiB");
+        int64_t last = 0;
+        if (!mul_ok(B - 1, bias_sb, &last)) return fail(SDPA_ERR_INVALID_ARGUMENT, "bias extent overflows");
+        int64_t hext = 0;
+        if (!mul_ok(Hq - 1, bias_sh, &hext) || __builtin_add_overflow(last, hext, &last) ||
+            __builtin_add_overflow(last, Sq * Sk, &last) || last > INT64_MAX / 2)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "bias extent overflows");
+        const int64_t bbytes = last * 2;
+        if (overlap(out, qbytes, bias, bbytes) ||
+            (lse && overlap(lse, B * Hq * Sq * (int64_t)sizeof(float), bias, bbytes)))
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "out or lse overlaps the bias");
+    }
     const int64_t blocks = ((Sq + 127) / 128) * B * Hq;
     if (blocks > INT_MAX / 256)
         return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
@@ -160,6 +184,9 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
     a.causal = causal;
     a.padded = padded;
     a.lse = lse;
+    a.bias = bias;
+    a.bias_sb = bias_sb;
+    a.bias_sh = bias_sh;
     (void)hipGetLastError();  // clear an unrelated pending error
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == SDPA_BF16  ? sdpa::launch_forward_bf16(a, s)
@@ -191,6 +218,16 @@ sdpa_status_t sdpa_forward_lse(const void* q, const void* k, const void* v, int6
     if (!lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "null lse pointer");
     return forward_impl(q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens, out, lse,
                         dtype, stream);
+}
+
+sdpa_status_t sdpa_forward_bias(const void* q, const void* k, const void* v, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                                float scale, int mask_kind, const int32_t* key_lens,
+                                const void* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                                void* out, float* lse, int dtype, void* stream) {
+    if (!bias) return fail(SDPA_ERR_INVALID_ARGUMENT, "null bias pointer");
+    return forward_impl(q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens, out, lse,
+                        dtype, stream, bias, bias_stride_b, bias_stride_h);
 }
 
 size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq) {

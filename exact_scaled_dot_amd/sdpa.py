@@ -27,7 +27,8 @@ MAX_SPLITS = 32
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
-EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_backward", "sdpa_backward_workspace_size",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_bias", "sdpa_backward",
+            "sdpa_backward_workspace_size",
             "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
             "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
 
@@ -56,6 +57,9 @@ def load_library():
     lib.sdpa_forward_lse.restype = i32
     lib.sdpa_forward_lse.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, i32,
                                      vp, vp, vp, i32, vp]
+    lib.sdpa_forward_bias.restype = i32
+    lib.sdpa_forward_bias.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, i32,
+                                      vp, vp, i64, i64, vp, vp, i32, vp]
     lib.sdpa_backward_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_backward_workspace_size.argtypes = [i64, i64, i64]
     lib.sdpa_backward.restype = i32
@@ -177,6 +181,47 @@ def sdpa_forward_lse(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=Non
                                 int(mask_kind), _ptr(key_lens), _ptr(out), _ptr(lse),
                                 _dtype_code(q), _stream(stream)))
     return out, lse
+
+
+def sdpa_forward_bias(q, k, v, bias, scale, mask_kind=MASK_NONE, key_lens=None, out=None,
+                      lse=None, stream=None):
+    """O = softmax(Q K^T * scale + bias + mask) V.
+
+    bias is [B or 1, Hq or 1, Sq, Sk] in q's dtype, contiguous in its last two
+    axes (a size-1 leading axis broadcasts).  lse: None, or True to allocate
+    and return it, or a float32 [B, Hq, Sq] tensor.  Returns out, or
+    (out, lse) when lse is requested.
+    """
+    B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
+    if not isinstance(bias, torch.Tensor) or bias.dim() != 4 or not bias.is_cuda:
+        raise ValueError("bias must be a 4-D device tensor")
+    if bias.dtype != q.dtype:
+        raise TypeError("bias must have q's dtype")
+    if (bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq)
+            or tuple(bias.shape[2:]) != (Sq, Sk)):
+        raise ValueError("bias must be [B or 1, Hq or 1, Sq, Sk]")
+    if bias.stride(3) != 1 or bias.stride(2) != Sk:
+        raise ValueError("bias rows must be contiguous (stride Sk between rows)")
+    sb = bias.stride(0) if bias.shape[0] > 1 else 0
+    sh = bias.stride(1) if bias.shape[1] > 1 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    want_lse = lse is not None
+    if lse is True:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_tensor("lse", lse, 3)
+        if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, Hq, Sq]")
+    lib = load_library()
+    _check(lib.sdpa_forward_bias(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                 int(mask_kind), _ptr(key_lens), _ptr(bias), sb, sh, _ptr(out),
+                                 _ptr(lse), _dtype_code(q), _stream(stream)))
+    return (out, lse) if want_lse else out
 
 
 def sdpa_backward_workspace_size(B, Hq, Sq):

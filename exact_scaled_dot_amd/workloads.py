@@ -82,6 +82,14 @@ def draw_grad(shape, dtype, seed, device="cpu"):
     return t.to(dtype) if dtype != torch.float32 else t
 
 
+def draw_bias(shape, dtype, seed, device="cpu"):
+    """Additive mask tensor of the given shape: i.i.d. N(0, 4) rounded to dtype."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 32452843)
+    t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * 2.0
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
 def draw_key_lens(B, lo, hi, seed, device="cpu"):
     """Per-batch valid key lengths, uniform integers in [lo, hi] (int32)."""
     gen = torch.Generator(device="cpu")

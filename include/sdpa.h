@@ -116,6 +116,28 @@ sdpa_status_t sdpa_forward_lse(const void *q, const void *k, const void *v,
                                void *out, float *lse, int dtype, void *stream);
 
 /*
+ * Forward with a general additive mask: O = softmax(Q K^T * scale + bias +
+ * mask) V, the tensai guide's Add(mask) with an arbitrary mask tensor
+ * ("Attention の組み立て"), combinable with the causal / key-padding flags.
+ *   bias       device [B or 1, Hq or 1, Sq, Sk], dtype; element (b, h, i, j)
+ *              at bias[b * bias_stride_b + h * bias_stride_h + i * Sk + j]
+ *              (a stride of 0 broadcasts over that axis).  Finite values or
+ *              -inf (hides the key); a row left with no visible key is NaN
+ *              (lse -inf).
+ *   lse        NULL, or device float [B, Hq, Sq] as in sdpa_forward_lse
+ * Every other argument as sdpa_forward.  The bias is read once per 128-row
+ * query block.  Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}, bias
+ * rows 16-byte aligned (Sk, bias_stride_b and bias_stride_h multiples of 8,
+ * pointer 16-byte aligned), one head's bias (Sq * Sk elements) under 2 GiB
+ * (SDPA_ERR_UNSUPPORTED otherwise).  out and lse must not overlap the bias.
+ */
+sdpa_status_t sdpa_forward_bias(const void *q, const void *k, const void *v,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                                int64_t D, float scale, int mask_kind, const int32_t *key_lens,
+                                const void *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                                void *out, float *lse, int dtype, void *stream);
+
+/*
  * Bytes of device workspace sdpa_backward needs (0 if the sizes are invalid):
  * 8 bytes per query row, rows of a head padded to an even count.
  */

@@ -277,3 +277,30 @@ def test_backward_workspace_size():
         assert lib.sdpa_backward_workspace_size(B, Hq, Sq) == (rows * 8 + 255) // 256 * 256
     for bad in [(0, 1, 1), (1, 0, 1), (1, 1, 0)]:
         assert lib.sdpa_backward_workspace_size(*bad) == 0
+
+
+FAKE_B = ctypes.c_void_p(0x30000000)
+
+
+def fwd_bias(bias=FAKE_B, sb=0, sh=128 * 128, Sq=128, Sk=128, dtype=sd.SDPA_BF16, out=FAKE_O,
+             lse=None, mask=0):
+    lib = sd.load_library()
+    return lib.sdpa_forward_bias(FAKE, FAKE_K, FAKE_V, 2, 4, 2, Sq, Sk, 128, 0.125, mask, None, bias,
+                                 sb, sh, out, lse, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(bias=None), sd.SDPA_ERR_INVALID_ARGUMENT, "bias"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(sb=-8), sd.SDPA_ERR_INVALID_ARGUMENT, "stride"),
+    (dict(Sk=100, Sq=100, sh=100 * 100), sd.SDPA_ERR_UNSUPPORTED, "aligned"),
+    (dict(sh=12), sd.SDPA_ERR_UNSUPPORTED, "aligned"),
+    (dict(bias=ctypes.c_void_p(0x30000000 + 8)), sd.SDPA_ERR_UNSUPPORTED, "aligned"),
+    (dict(Sq=1 << 15, Sk=1 << 15, sh=0), sd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(out=ctypes.c_void_p(0x30000000 + 4096)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(lse=ctypes.c_void_p(0x30000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(mask=1, Sq=64, sh=64 * 128), sd.SDPA_ERR_INVALID_ARGUMENT, "Sq == Sk"),
+])
+def test_forward_bias_rejects(kw, status, needle):
+    assert fwd_bias(**kw) == status
+    assert needle in sd.last_error()
