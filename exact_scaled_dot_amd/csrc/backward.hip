@@ -45,6 +45,7 @@ namespace {
 constexpr int kBwThreads = 256;  // 4 waves of 64
 constexpr int kBwRows = 128;     // rows a workgroup owns (queries in pass 1, keys in pass 2)
 constexpr int kBwTile = 64;      // rows of the streamed operand per step
+constexpr uint32_t kOutside = 0x80000000u;  // a buffer offset past any num_records (<= INT_MAX)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -153,7 +154,9 @@ struct BwOffsets {
     int trl[D / 32];  // transposed read, rows 4hg + j/4 of a 16-row step, dims 32db + ...
     int trh[D / 32];  // the same 8 rows further on
     uint32_t dma[L::DMA];  // DMA source offsets (bytes) of this wave's tile slots
-    __device__ BwOffsets(int wave, int lane) {
+    // DR: head dim in memory (rows DR wide in HBM; chunks at or past DR are
+    // pointed outside the buffer and read as zeros).
+    __device__ BwOffsets(int wave, int lane, int DR) {
         const int l32 = lane & 31, hg = lane >> 5;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) row[t] = l32 * D + (((2 * t + hg) ^ L::f(l32)) * 8);
@@ -172,8 +175,8 @@ struct BwOffsets {
 #pragma unroll
         for (int i = 0; i < L::DMA; ++i) {
             const int s = 64 * (L::DMA * wave + i) + lane;
-            const int r = s / L::CPR, pc = s % L::CPR;
-            dma[i] = (uint32_t)r * D * 2 + (uint32_t)((pc ^ L::f(r)) * 16);
+            const int r = s / L::CPR, c = (s % L::CPR) ^ L::f(r);  // logical chunk
+            dma[i] = 8 * c < DR ? (uint32_t)r * DR * 2 + (uint32_t)(c * 16) : kOutside;
         }
     }
 };
@@ -197,7 +200,7 @@ __device__ __forceinline__ int xcd_order(int total) {
 // heads of the group innermost; under a causal mask the longest blocks (the
 // last rows) first.
 // ---------------------------------------------------------------------------
-template <int D, class T>
+template <int D, class T, bool GEN = false>
 __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                                                                const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
@@ -220,11 +223,13 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
     const int b = unit / a.Hkv, gk = unit % a.Hkv, h = gk * G + hsub;
     const int q0 = (a.causal ? nqb - 1 - qord : qord) * kBwRows;
 
+    // Head dim in memory: DR (GEN: a multiple of 8 below D; else D).
+    const int DR = GEN ? a.D : D;
     const int64_t bh = (int64_t)b * a.Hq + h;
-    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
+    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * DR;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kvh;
     const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kvh;
-    const int64_t qoff = bh * a.Sq * D;
+    const int64_t qoff = bh * a.Sq * DR;
 
     int kv_lim = a.Sk;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
@@ -242,14 +247,15 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
     u32x4 qr[D / 16], dr[D / 16];
     float delta;
     {
-        const uint32_t bytes = (uint32_t)a.Sq * D * 2;
+        const uint32_t bytes = (uint32_t)a.Sq * DR * 2;
         const __amdgpu_buffer_rsrc_t rq = rsrc(static_cast<const uint16_t*>(a.q) + qoff, bytes);
         const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const uint16_t*>(a.dout) + qoff, bytes);
         const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const uint16_t*>(a.out) + qoff, bytes);
         float part = 0.f;
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) {
-            const uint32_t off = (uint32_t)qi * D * 2 + (16 * k + 8 * hg) * 2;
+            const int d0 = 16 * k + 8 * hg;
+            const uint32_t off = d0 < DR ? (uint32_t)qi * DR * 2 + d0 * 2 : kOutside;
             qr[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
             dr[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
             part = dot8<T>(dr[k], __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0), part);
@@ -270,11 +276,11 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
         }
     }
 
-    const BwOffsets<D> off(wave, lane);
+    const BwOffsets<D> off(wave, lane, DR);
     auto issue = [&](int j0, int stage) {
-        const uint32_t bytes = (uint32_t)(a.Sk - j0) * D * 2;
-        const __amdgpu_buffer_rsrc_t rk = rsrc(kp + (int64_t)j0 * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = rsrc(vp + (int64_t)j0 * D, bytes);
+        const uint32_t bytes = (uint32_t)(a.Sk - j0) * DR * 2;
+        const __amdgpu_buffer_rsrc_t rk = rsrc(kp + (int64_t)j0 * DR, bytes);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vp + (int64_t)j0 * DR, bytes);
         uint16_t* dk = smem + 2 * stage * L::TILE + 512 * L::DMA * wave;
         uint16_t* dv = dk + L::TILE;
 #pragma unroll
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
     // dQ = scale * (dS K): register r of d-block db holds dim
     // 32*db + 8*(r/4) + 4*hg + r%4 of row qi.
     if (qi < a.Sq) {
-        uint16_t* row = static_cast<uint16_t*>(a.dq) + qoff + (int64_t)qi * D;
+        uint16_t* row = static_cast<uint16_t*>(a.dq) + qoff + (int64_t)qi * DR;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -358,7 +364,8 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                 const f32x16& x = acc[db];
                 const u32x2 w = {pack2<T>(x[4 * r4] * a.scale, x[4 * r4 + 1] * a.scale),
                                  pack2<T>(x[4 * r4 + 2] * a.scale, x[4 * r4 + 3] * a.scale)};
-                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * r4 + 4 * hg) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
+                if (d0 < DR) *reinterpret_cast<u32x2*>(row + d0) = w;
             }
     }
 }
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
 // ---------------------------------------------------------------------------
 constexpr int kKvThreads = 512;  // 8 waves
 
-template <int D, class T>
+template <int D, class T, bool GEN = false>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                                                                  const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
@@ -413,7 +420,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     const int k0 = (t % nkb) * kBwRows;
     const int b = unit / a.Hkv, gk = unit % a.Hkv;
 
-    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
+    const int DR = GEN ? a.D : D;  // head dim in memory (a multiple of 8, <= D)
+    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * DR;
     int kv_lim = a.Sk;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
     const int kw = k0 + 32 * pair;  // first key of this pair
@@ -424,11 +432,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     {
         const void* src = role ? a.v : a.k;
         const __amdgpu_buffer_rsrc_t rx =
-            rsrc(static_cast<const uint16_t*>(src) + kvh, (uint32_t)a.Sk * D * 2);
+            rsrc(static_cast<const uint16_t*>(src) + kvh, (uint32_t)a.Sk * DR * 2);
 #pragma unroll
-        for (int k = 0; k < NK; ++k)
-            xr[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)kj * D * 2 + (16 * k + 8 * hg) * 2,
-                                                          0, 0);
+        for (int k = 0; k < NK; ++k) {
+            const int d0 = 16 * k + 8 * hg;
+            xr[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                rx, d0 < DR ? (uint32_t)kj * DR * 2 + d0 * 2 : kOutside, 0, 0);
+        }
     }
 
     // Query tiles: all of them, or (causal) those holding a row >= k0; a block
@@ -437,21 +447,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     const int nqt = (k0 < kv_lim) ? max(0, (a.Sq + kBwTile - 1) / kBwTile - qt0) : 0;
     const int steps = G * nqt;
 
-    const BwOffsets<D> off(0, lane);  // row and transposed read offsets
+    const BwOffsets<D> off(0, lane, DR);  // row and transposed read offsets
     uint32_t dmo[DMA];
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
         const int s = 64 * (DMA * wave + i) + lane;
-        const int r = s / L::CPR, pc = s % L::CPR;
-        dmo[i] = (uint32_t)r * D * 2 + (uint32_t)((pc ^ L::f(r)) * 16);
+        const int r = s / L::CPR, c = (s % L::CPR) ^ L::f(r);  // logical chunk
+        dmo[i] = 8 * c < DR ? (uint32_t)r * DR * 2 + (uint32_t)(c * 16) : kOutside;
     }
 
     auto issue = [&](int st, int stage) {
         const int h = gk * G + st / nqt;
         const int q0 = (qt0 + st % nqt) * kBwTile;
         const int64_t bh = (int64_t)b * a.Hq + h;
-        const int64_t qoff = (bh * a.Sq + q0) * D;
-        const uint32_t bytes = (uint32_t)(a.Sq - q0) * D * 2;
+        const int64_t qoff = (bh * a.Sq + q0) * DR;
+        const uint32_t bytes = (uint32_t)(a.Sq - q0) * DR * 2;
         const __amdgpu_buffer_rsrc_t rq = rsrc(static_cast<const uint16_t*>(a.q) + qoff, bytes);
         const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const uint16_t*>(a.dout) + qoff, bytes);
         uint16_t* dq = smem + stage * STAGE + 512 * DMA * wave;
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     if (kj < a.Sk) {
         const bool keep = kj < kv_lim;
         const float sc = keep ? (role ? a.scale : 1.f) : 0.f;
-        uint16_t* row = static_cast<uint16_t*>(role ? a.dk : a.dv) + kvh + (int64_t)kj * D;
+        uint16_t* row = static_cast<uint16_t*>(role ? a.dk : a.dv) + kvh + (int64_t)kj * DR;
 #pragma unroll
         for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -618,32 +628,39 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                 const f32x16& x = acc[db];
                 const u32x2 w = {pack2<T>(x[4 * r4] * sc, x[4 * r4 + 1] * sc),
                                  pack2<T>(x[4 * r4 + 2] * sc, x[4 * r4 + 3] * sc)};
-                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * r4 + 4 * hg) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
+                if (d0 < DR) *reinterpret_cast<u32x2*>(row + d0) = w;
             }
     }
 }
 
-template <int D, class T>
+template <int D, class T, bool GEN>
 hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int nqb = (a.Sq + kBwRows - 1) / kBwRows;
     const int nkb = (a.Sk + kBwRows - 1) / kBwRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, T>), dim3(a.B * a.Hq * nqb), dim3(kBwThreads), 0, s, a,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, GEN>), dim3(a.B * a.Hq * nqb), dim3(kBwThreads), 0, s, a,
                        a.key_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.B * a.Hkv * nkb), dim3(kKvThreads), 0, s,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, GEN>), dim3(a.B * a.Hkv * nkb), dim3(kKvThreads), 0, s,
                        a, a.key_lens);
     return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
+    if (a.D == 128) return launch_backward_d<128, T, false>(a, s);
+    if (a.D == 64) return launch_backward_d<64, T, false>(a, s);
+    // other multiples of 8: the 64- or 128-wide kernels with zero-filled chunks
+    if (a.D < 64) return launch_backward_d<64, T, true>(a, s);
+    return launch_backward_d<128, T, true>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s) {
-    if (a.D == 128)
-        return f16 ? launch_backward_d<128, F16T>(a, s) : launch_backward_d<128, Bf16T>(a, s);
-    if (a.D == 64)
-        return f16 ? launch_backward_d<64, F16T>(a, s) : launch_backward_d<64, Bf16T>(a, s);
-    return hipErrorInvalidValue;
+    if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
+    return f16 ? launch_backward_t<F16T>(a, s) : launch_backward_t<Bf16T>(a, s);
 }
 
 }  // namespace sdpa

@@ -171,7 +171,7 @@ __device__ __forceinline__ Item item_geo(const DecodeArgs& a, const PagedArgs& p
 // 16), found through the sequence's page table when the step enters a new
 // page.  A table entry outside [0, pages) is never dereferenced: its keys
 // load as zeros and are masked out.
-template <int D, bool PAGED, class T>
+template <int D, bool PAGED, class T, bool GEN = false>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     DecodeArgs a, PagedArgs p, const int32_t* __restrict__ key_lens,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -201,10 +201,15 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     if (PAGED) chunk = (chunk + kStep - 1) / kStep * kStep;
     const float c = a.scale * kLog2e;
     const float tau = kTau / c;
-    const uint32_t head_bytes = (uint32_t)a.Sk * D * 2;
-    // Bytes between consecutive keys of one K/V head: D*2 in a dense head,
-    // Hkv*D*2 inside a page.
-    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * D * 2 : (uint32_t)D * 2;
+    // Head dim in memory: DR (GEN: a multiple of 8 below D; else D).  Rows
+    // are DR wide in HBM and D wide on chip; chunks at or past DR read as
+    // zeros (offsets outside the buffer) and are never stored.
+    const int DR = GEN ? a.D : D;
+    constexpr uint32_t kOut = 0x80000000u;  // past any num_records (<= INT_MAX)
+    const uint32_t head_bytes = (uint32_t)a.Sk * DR * 2;
+    // Bytes between consecutive keys of one K/V head: DR*2 in a dense head,
+    // Hkv*DR*2 inside a page.
+    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * DR * 2 : (uint32_t)DR * 2;
     const uint32_t page_bytes = PAGED ? (uint32_t)p.page_size * row_bytes : 0u;
 
     // Lane-constant DMA offsets (bytes from the step's first key) and LDS read
@@ -213,8 +218,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int q = 64 * i + lane, row = q / L::CPR, pc = q % L::CPR;
-        koff[i] = row * row_bytes + (pc ^ L::fk(row)) * 16;
-        voff[i] = row * row_bytes + (pc ^ L::fv(row)) * 16;
+        const int ck = pc ^ L::fk(row), cv = pc ^ L::fv(row);  // logical chunks
+        koff[i] = 8 * ck < DR ? row * row_bytes + ck * 16 : kOut;
+        voff[i] = 8 * cv < DR ? row * row_bytes + cv * 16 : kOut;
     }
     // K fragment of kstep t: key row col, dims (D/4)*grp + 8t .. +7 (contraction
     // slot (t, grp, e) <-> dim (D/4)*grp + 8t + e, matching qb below).
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 i_gk = g.gk;
                 i_page = -1;
                 if (!PAGED) {
-                    const int64_t kvh = ((int64_t)g.b * a.Hkv + g.gk) * a.Sk * D;
+                    const int64_t kvh = ((int64_t)g.b * a.Hkv + g.gk) * a.Sk * DR;
                     ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + kvh, head_bytes);
                     ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kvh, head_bytes);
                 }
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 i_page = lp;
                 const int pg = lp < p.max_pages ? meta.tables[(int64_t)i_seq * p.max_pages + lp] : -1;
                 const bool ok = pg >= 0 && pg < p.pages;
-                const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * D : 0;
+                const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * DR : 0;
                 ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + off, ok ? page_bytes : 0u);
                 ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + off, ok ? page_bytes : 0u);
                 valid_bits = ok ? (valid_bits | (1u << (issued & 31))) : (valid_bits & ~(1u << (issued & 31)));
@@ -279,9 +285,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 const uint32_t prev = (valid_bits >> ((issued - 1) & 31)) & 1u;
                 valid_bits = (valid_bits & ~(1u << (issued & 31))) | (prev << (issued & 31));
             }
-            base = ((uint32_t)(i_k0 % p.page_size) * a.Hkv + i_gk) * D * 2;
+            base = ((uint32_t)(i_k0 % p.page_size) * a.Hkv + i_gk) * DR * 2;
         } else {
-            base = (uint32_t)i_k0 * D * 2;
+            base = (uint32_t)i_k0 * DR * 2;
         }
         // The buffer range check covers the per-lane offset but not the scalar
         // one.  Dense: the step offset goes into the per-lane offset, so rows
@@ -310,10 +316,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         const int64_t prow0 = ((int64_t)g.b * a.Hq + g.h0) * a.splits + g.split;
         if (g.nst == 0) {  // no visible key in this split
             if (col < g.nh) {
-                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * D + 4 * grp;
+                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * DR + 4 * grp;
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt)
-                    *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (16 * dt + 4 * grp < DR)
+                        *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (grp == 0) a.lse_part[prow0 + (int64_t)col * a.splits] = -INFINITY;
             }
             continue;
@@ -323,11 +330,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
             // Q^T B operand: column col = query head h0 + col (reads beyond the
             // block's nh heads return 0), slots as in krd.
             const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
-                static_cast<const uint16_t*>(a.q) + (int64_t)head * D, (uint32_t)g.nh * D * 2);
+                static_cast<const uint16_t*>(a.q) + (int64_t)head * DR, (uint32_t)g.nh * DR * 2);
 #pragma unroll
-            for (int t = 0; t < L::KSTEPS; ++t)
-                qb[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (col * D + (D / 4) * grp + 8 * t) * 2,
-                                                              0, 0);
+            for (int t = 0; t < L::KSTEPS; ++t) {
+                const int d0 = (D / 4) * grp + 8 * t;
+                qb[t] = __builtin_amdgcn_raw_buffer_load_b128(
+                    qrs, d0 < DR ? (col * DR + d0) * 2 : kOut, 0, 0);
+            }
             // Take the wait for the Q loads here, once per head, not inside the
             // step loop.
 #pragma unroll
@@ -415,33 +424,36 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         l_run += __shfl_xor(l_run, 32);
         if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
-            float* op = a.o_part + prow * D + 4 * grp;
+            float* op = a.o_part + prow * DR + 4 * grp;
             if (m_run == -INFINITY) {  // every key masked (paged: invalid pages only)
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt)
-                    *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (16 * dt + 4 * grp < DR)
+                        *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (grp == 0) a.lse_part[prow] = -INFINITY;
             } else {
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
-                    *reinterpret_cast<f32x4*>(op + 16 * dt) =
-                        f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
-                              oacc[dt][3] / l_run};
+                    if (16 * dt + 4 * grp < DR)
+                        *reinterpret_cast<f32x4*>(op + 16 * dt) =
+                            f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
+                                  oacc[dt][3] / l_run};
                 if (grp == 0) a.lse_part[prow] = m_run * a.scale + __logf(l_run);
             }
         }
     }
 }
 
-template <int D, class T>
+template <int D, class T, bool GEN = false>
 __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     constexpr int TPR = D / 4;       // threads per row, 4 dims each
     constexpr int RPB = 256 / TPR;   // rows (batch, query head) per block
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int d4 = threadIdx.x % TPR;
-    if (row >= (int64_t)a.B * a.Hq) return;
+    const int DR = GEN ? a.D : D;  // head dim in memory (a multiple of 8, <= D)
+    if (row >= (int64_t)a.B * a.Hq || 4 * d4 >= DR) return;
     const float* lse = a.lse_part + row * a.splits;
-    const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * D) + d4;
+    const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * DR) + d4;
     float M = -INFINITY;
     for (int s = 0; s < a.splits; ++s) M = fmaxf(M, lse[s]);
     float den = 0.f;
@@ -450,7 +462,7 @@ __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     for (int s = 0; s < a.splits; ++s) {
         const float w = fast_exp2((lse[s] - M) * kLog2e);  // empty split: exp(-inf) = 0
         den += w;
-        const f32x4 o = op[(int64_t)s * (D / 4)];
+        const f32x4 o = op[(int64_t)s * (DR / 4)];
         acc[0] = fmaf(w, o[0], acc[0]);
         acc[1] = fmaf(w, o[1], acc[1]);
         acc[2] = fmaf(w, o[2], acc[2]);
@@ -459,7 +471,7 @@ __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     // Every split empty (no visible key): M = -inf, w = NaN, and the row is NaN.
     const uint32_t lo = pack_lo16(to16<T>(acc[0] / den), to16<T>(acc[1] / den));
     const uint32_t hi = pack_lo16(to16<T>(acc[2] / den), to16<T>(acc[3] / den));
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + 4 * d4) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * DR + 4 * d4) = u32x2{lo, hi};
 }
 
 // Compute units of the current device (cached per device).
@@ -486,19 +498,29 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
-    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * a.D / 4 + 255) / 256));
+    if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
+    // Head dims that are multiples of 8 run on the 64- or 128-wide kernels.
+    const int dpad = a.D <= 64 ? 64 : 128;
+    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * dpad / 4 + 255) / 256));
+    const dim3 sg(wgs), st(kDecThreads), mt(256);
+    const int32_t *kl = a.key_lens, *bt = p.block_tables, *sl = p.seq_lens, *qs = p.query_seq,
+                  *qp = p.query_pos;
     if (a.D == 64) {
-        hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED, T>), dim3(wgs), dim3(kDecThreads), 0,
-                           s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
-                           items);
-        hipLaunchKernelGGL((decode_merge_bf16_kernel<64, T>), mgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED, T>), sg, st, 0, s, a, p, kl, bt, sl, qs,
+                           qp, items);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<64, T>), mgrid, mt, 0, s, a);
     } else if (a.D == 128) {
-        hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED, T>), dim3(wgs), dim3(kDecThreads), 0,
-                           s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos,
-                           items);
-        hipLaunchKernelGGL((decode_merge_bf16_kernel<128, T>), mgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED, T>), sg, st, 0, s, a, p, kl, bt, sl, qs,
+                           qp, items);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<128, T>), mgrid, mt, 0, s, a);
+    } else if (dpad == 64) {
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED, T, true>), sg, st, 0, s, a, p, kl, bt, sl,
+                           qs, qp, items);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<64, T, true>), mgrid, mt, 0, s, a);
     } else {
-        return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED, T, true>), sg, st, 0, s, a, p, kl, bt,
+                           sl, qs, qp, items);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<128, T, true>), mgrid, mt, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -181,7 +181,7 @@ struct Bf16Geo {
 // it loads those four 16-byte runs of its bias row (one tile ahead, next to
 // the DMA issue) and adds bias / scale in raw-score units during the mask
 // step; every visited tile takes the mask step.
-template <int D, bool PAGED, class T, bool BIAS = false>
+template <int D, bool PAGED, class T, bool BIAS = false, bool GEN = false>
 __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
@@ -198,6 +198,11 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     const int hg = lane >> 5;  // which half of the wave
 
     const TileInfo ti = decode_tile(a);
+    // Head dim in memory: DR (GEN: a multiple of 8 below D; else D).  Rows are
+    // DR wide in HBM and D wide on chip; the 16-byte chunks at or past DR are
+    // read as zeros (their offsets lie outside the buffer) and never stored.
+    const int DR = GEN ? a.D : D;
+    constexpr uint32_t kOut = 0x80000000u;  // past any num_records (<= INT_MAX)
     const uint16_t* kp;
     const uint16_t* vp;
     const uint16_t* qbase;
@@ -215,20 +220,20 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         qoff = kv_lim - nrows;  // absolute position of the chunk's first row
         kv_end = kv_lim;
         if (a.causal) kv_end = min(kv_end, qoff + ti.q0 + kBr);
-        const int64_t rb = ((int64_t)r0 * a.Hq + ti.h) * D;
+        const int64_t rb = ((int64_t)r0 * a.Hq + ti.h) * DR;
         qbase = static_cast<const uint16_t*>(a.q) + rb;
         op = static_cast<uint16_t*>(a.out) + rb;
-        qstride = (uint32_t)a.Hq * D * 2;
+        qstride = (uint32_t)a.Hq * DR * 2;
         kp = static_cast<const uint16_t*>(a.k);
         vp = static_cast<const uint16_t*>(a.v);
     } else {
         const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
-        const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * D;
+        const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * DR;
         kp = static_cast<const uint16_t*>(a.k) + kvh;
         vp = static_cast<const uint16_t*>(a.v) + kvh;
-        qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * D;
-        op = static_cast<uint16_t*>(a.out) + bh * a.Sq * D;
-        qstride = (uint32_t)D * 2;
+        qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * DR;
+        op = static_cast<uint16_t*>(a.out) + bh * a.Sq * DR;
+        qstride = (uint32_t)DR * 2;
         nrows = a.Sq;
         qoff = 0;
         key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
@@ -247,8 +252,10 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     {
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, (uint32_t)nrows * qstride);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-            qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qi * qstride + (16 * t + 8 * hg) * 2, 0, 0);
+        for (int t = 0; t < D / 16; ++t) {
+            const int d0 = 16 * t + 8 * hg;
+            qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, d0 < DR ? qi * qstride + d0 * 2 : kOut, 0, 0);
+        }
     }
 
     // Bias: a resource over this (batch, head)'s [Sq, Sk] slice (rows >= Sq
@@ -272,15 +279,16 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // lane l's 16 B land at 16-byte slot p = 64*(DMA*wave + i) + l.
     // (Paged: relative to the wave's 16-key group, rows Hkv*D*2 bytes apart.)
     // The wave's LDS rows are 16*wave .. 16*wave+15, i.e. keys of the same group.
-    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * D * 2 : (uint32_t)D * 2;
+    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * DR * 2 : (uint32_t)DR * 2;
     const int row_base = PAGED ? 16 * wave : 0;
     uint32_t koff[L::DMA], voff[L::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int q = 64 * (L::DMA * wave + i) + lane;
         const int row = q / L::CPR, pc = q % L::CPR;
-        koff[i] = (k_lds_row(row) - row_base) * row_bytes + ((pc ^ L::fk(row)) * 16);
-        voff[i] = (row - row_base) * row_bytes + ((pc ^ L::fv(row)) * 16);
+        const int ck = pc ^ L::fk(row), cv = pc ^ L::fv(row);  // logical chunks
+        koff[i] = 8 * ck < DR ? (k_lds_row(row) - row_base) * row_bytes + ck * 16 : kOut;
+        voff[i] = 8 * cv < DR ? (row - row_base) * row_bytes + cv * 16 : kOut;
     }
     // Paged: resource over the page of keys j0 + 16*wave .. +15 (zero records
     // when the table entry is outside the cache) and the group's scalar
@@ -295,9 +303,9 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         const int lp = key / p.page_size;
         const int pg = lp < p.max_pages ? tables[(int64_t)ti.b * p.max_pages + lp] : -1;
         const bool ok = pg >= 0 && pg < p.pages;
-        pg_off[stage] = ok ? (int64_t)pg * p.page_size * a.Hkv * D : 0;
+        pg_off[stage] = ok ? (int64_t)pg * p.page_size * a.Hkv * DR : 0;
         pg_bytes[stage] = ok ? (uint32_t)p.page_size * row_bytes : 0u;
-        pg_soff[stage] = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * D * 2;
+        pg_soff[stage] = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * DR * 2;
         return ok;
     };
     // Dense: resources start at the tile's first key; num_records ends at key Sk.
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             if (lane == 0) lds_store_i32(kvalid + 4 * stage + wave, ok ? 1 : 0);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(kp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
+                make_rsrc(kp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
 #pragma unroll
             for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, koff[i]);
         }
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             for (int i = 0; i < L::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], pg_soff[ks]);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(vp + (int64_t)j0 * D, (uint32_t)(a.Sk - j0) * D * 2);
+                make_rsrc(vp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
 #pragma unroll
             for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
         }
@@ -574,7 +582,8 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             for (int r4 = 0; r4 < 4; ++r4) {
                 const u32x2 w = {pack2<T>(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
                                  pack2<T>(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * hg) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
+                if (d0 < DR) *reinterpret_cast<u32x2*>(orow + d0) = w;
             }
     }
 }
@@ -739,16 +748,24 @@ inline dim3 forward_grid(const ForwardArgs& a) {
     return dim3((unsigned)(nqb * a.B * a.Hq));
 }
 
+// Head dims that are multiples of 8 run on the 64- or 128-wide kernel (the
+// general-width instantiation unless D is exactly 64 or 128).
 template <bool PAGED, class T, bool BIAS = false>
 hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
+    if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
+    const dim3 g = forward_grid(a), t(kThreads);
     if (a.D == 64)
-        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS>), forward_grid(a), dim3(kThreads), 0,
-                           s, a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS>), g, t, 0, s, a, p, p.block_tables,
+                           p.seq_lens, p.cu_seqlens_q);
     else if (a.D == 128)
-        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS>), forward_grid(a), dim3(kThreads), 0,
-                           s, a, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS>), g, t, 0, s, a, p, p.block_tables,
+                           p.seq_lens, p.cu_seqlens_q);
+    else if (a.D < 64)
+        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS, true>), g, t, 0, s, a, p,
+                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else
-        return hipErrorInvalidValue;
+        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS, true>), g, t, 0, s, a, p,
+                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
     return hipGetLastError();
 }
 

@@ -48,6 +48,14 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 int64_t elem_size(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
 bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || dtype == SDPA_F16; }
 
+// Head dims the kernels cover: 16-bit inputs any multiple of 8 up to 128
+// (the 64- and 128-wide kernels read the missing chunks as zeros), fp32
+// exactly 64 or 128.
+bool head_dim_ok(int64_t D, int dtype) {
+    if (dtype == SDPA_F32) return D == 64 || D == 128;
+    return D >= 8 && D <= 128 && D % 8 == 0;
+}
+
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -79,8 +87,9 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
     // Per-head rows are addressed through buffer resources with 32-bit extents.
     if (Sq * D * es > INT_MAX || Sk * D * es > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "one head of q, k or v exceeds 2 GiB");
-    if (D != 64 && D != 128)
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
+    if (!head_dim_ok(D, dtype))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (%s)", (long long)D,
+                    dtype == SDPA_F32 ? "64 or 128 for fp32" : "a multiple of 8 up to 128");
     return SDPA_OK;
 }
 
@@ -424,8 +433,9 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     if (queries > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (D != 64 && D != 128)
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
+    if (!head_dim_ok(D, dtype))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 128)",
+                    (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 and fp16 only");
     if (page_size % 16 != 0)
@@ -515,8 +525,9 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (D != 64 && D != 128)
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64 or 128)", (long long)D);
+    if (!head_dim_ok(D, dtype))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 128)",
+                    (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 and fp16 only");
     if (page_size % 16 != 0)

@@ -68,7 +68,9 @@ def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, sca
     (dict(out=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(out=ctypes.c_void_p(0x40000000 - 2)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(B=1 << 40, Hq=1 << 20), sd.SDPA_ERR_INVALID_ARGUMENT, "overflow"),
-    (dict(D=96), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=96, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(Sq=1 << 33, Sk=1 << 33, B=1, Hq=1, Hkv=1, D=64, out=ctypes.c_void_p(1 << 46)),
      sd.SDPA_ERR_UNSUPPORTED, "32-bit"),
@@ -103,7 +105,7 @@ def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1,
     (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=80), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
 ])
 def test_decode_rejects(kw, status, needle):
@@ -163,7 +165,9 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_
     (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws_bytes=64), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(out=ctypes.c_void_p(0x7a000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=96), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=96, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
 ])
@@ -209,8 +213,8 @@ def test_dtype_codes():
     assert dec(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
     assert paged(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
     assert prefill(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
-    assert fwd(dtype=sd.SDPA_F16, D=96) == sd.SDPA_ERR_UNSUPPORTED  # reaches the head-dim check
-    assert dec(dtype=sd.SDPA_F16, D=96) == sd.SDPA_ERR_UNSUPPORTED
+    assert fwd(dtype=sd.SDPA_F16, D=100) == sd.SDPA_ERR_UNSUPPORTED  # reaches the head-dim check
+    assert dec(dtype=sd.SDPA_F16, D=100) == sd.SDPA_ERR_UNSUPPORTED
 
 
 def fwd_lse(lse=ctypes.c_void_p(0x78000000), dtype=sd.SDPA_BF16, q=FAKE, out=FAKE_O, Sq=128):

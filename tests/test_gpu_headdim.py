@@ -1,0 +1,117 @@
+"""GPU parity at head dims other than 64 and 128 (any multiple of 8 up to 128,
+16-bit inputs) on every entry point, against the fp64 oracle.
+
+The 64- and 128-wide kernels serve these widths: rows are D wide in memory,
+the chunks past D are read as zeros on chip and never stored.  Bars:
+tests/parity.py."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_scaled_dot_amd as sd
+import oracle as O
+from exact_scaled_dot_amd.workloads import draw_bias, draw_grad, draw_paged, draw_qkv
+from parity import compare, compare_grad, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF16, F16 = torch.bfloat16, torch.float16
+
+
+@pytest.mark.parametrize("D", [8, 16, 24, 40, 56, 72, 80, 96, 104, 120])
+@pytest.mark.parametrize("mask", [0, 1, 2], ids=["none", "causal", "padding"])
+def test_forward_head_dims(D, mask):
+    B, Hq, Hkv, S = 2, 4, 2, 200
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 700 + D + mask, DEV)
+    lens = torch.tensor([200, 77], dtype=torch.int32, device=DEV) if mask == 2 else None
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask, ln, return_lse=True)
+    compare(to64(out), ref, BF16, "forward D=%d mask=%d" % (D, mask))
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
+
+
+def test_forward_head_dim_fp16_and_bias():
+    B, Hq, Hkv, S, D = 2, 4, 4, 136, 96
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, F16, 720, DEV)
+    out = sd.sdpa_forward(q, k, v, 0.1, sd.MASK_CAUSAL)
+    bias = draw_bias((1, Hq, S, S), F16, 721, DEV)
+    outb = sd.sdpa_forward_bias(q, k, v, bias, 0.1, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL), F16,
+            "fp16 D=96")
+    compare(to64(outb), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL,
+                                       bias=to64(bias)), F16, "fp16 D=96 bias")
+
+
+@pytest.mark.parametrize("D", [40, 80, 112])
+@pytest.mark.parametrize("splits", [1, 5])
+def test_decode_head_dims(D, splits):
+    B, Hq, Hkv, Sk = 3, 16, 4, 1000
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 730 + D, DEV)
+    lens = torch.tensor([1000, 333, 17], dtype=torch.int32, device=DEV)
+    out = sd.sdpa_decode(q, k, v, 0.1, lens, splits)
+    torch.cuda.synchronize()
+    ref = O.sdpa_decode(to64(q), to64(k), to64(v), 0.1, lens.cpu().numpy())
+    compare(to64(out), ref, BF16, "decode D=%d splits=%d" % (D, splits))
+
+
+@pytest.mark.parametrize("D", [48, 96])
+def test_paged_head_dims(D):
+    lens = [300, 129]
+    inp = draw_paged(lens, [0, 1, 1], [299, 128, 64], 8, 2, D, 16, BF16, 740 + D, DEV)
+    scale = 1 / math.sqrt(D)
+    msl = inp["block_tables"].shape[1] * 16
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, True,
+                                  msl, 4)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            inp["block_tables"].cpu().numpy(), np.array(lens),
+                            inp["query_seq"].cpu().numpy(), inp["query_pos"].cpu().numpy(), scale, True)
+    compare(to64(out), ref, BF16, "paged decode D=%d" % D)
+    # prefill chunks: the last 150 and 129 tokens
+    chunks = [150, 129]
+    cu = torch.tensor([0, 150, 279], dtype=torch.int32, device=DEV)
+    qc = draw_qkv(1, 1, 1, sum(chunks), 1, 8 * D, BF16, 742 + D, DEV)[0].reshape(sum(chunks), 8, D)
+    outp = sd.sdpa_paged_prefill(qc.contiguous(), inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                 inp["seq_lens"], cu, scale, True, max(chunks), msl)
+    torch.cuda.synchronize()
+    qs, qp = O.chunk_positions(cu.cpu().numpy(), np.array(lens))
+    refp = O.paged_attention(to64(qc), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                             inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, scale, True)
+    compare(to64(outp), refp, BF16, "paged prefill D=%d" % D)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("D", [40, 96])
+def test_backward_head_dims(dtype, D):
+    B, Hq, Hkv, S = 2, 4, 2, 200
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, dtype, 750 + D, DEV)
+    dout = draw_grad((B, Hq, S, D), dtype, 751 + D, DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, sd.MASK_CAUSAL)
+    dq, dk, dv = sd.sdpa_backward(q, k, v, out, dout, lse, scale, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.sdpa_backward(to64(q), to64(k), to64(v), to64(dout), scale, O.MASK_CAUSAL)
+    compare_grad(to64(dq), rq, dtype, "D=%d dq" % D)
+    compare_grad(to64(dk), rk, dtype, "D=%d dk" % D)
+    compare_grad(to64(dv), rv, dtype, "D=%d dv" % D)
+
+
+def test_outputs_past_head_dim_untouched():
+    # a D=72 output lives in a larger buffer: the elements after it keep their values
+    B, Hq, S, D = 1, 2, 70, 72
+    q, k, v = draw_qkv(B, Hq, Hq, S, S, D, BF16, 760, DEV)
+    big = torch.full((B * Hq * S * D + 64,), 7.0, dtype=BF16, device=DEV)
+    out = big[: B * Hq * S * D].view(B, Hq, S, D)
+    sd.sdpa_forward(q, k, v, 0.12, sd.MASK_CAUSAL, out=out)
+    torch.cuda.synchronize()
+    assert (big[B * Hq * S * D:] == 7.0).all()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.12, O.MASK_CAUSAL), BF16, "D=72")
