@@ -92,7 +92,9 @@ enum {
  *   out      device [B, Hq, Sq, D], dtype; written completely
  *   dtype    SDPA_BF16, SDPA_F16 or SDPA_F32
  *   stream   hipStream_t as void*
- * Supported head dims: D in {64, 128}; one head (Sq*D or Sk*D elements) must
+ * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 128
+ * (the 64- and 128-wide kernels, with the dims past D read as zeros on chip),
+ * SDPA_F32 D in {64, 128}; one head (Sq*D or Sk*D elements) must
  * be under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
  */
 sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
@@ -126,7 +128,8 @@ sdpa_status_t sdpa_forward_lse(const void *q, const void *k, const void *v,
  *              (lse -inf).
  *   lse        NULL, or device float [B, Hq, Sq] as in sdpa_forward_lse
  * Every other argument as sdpa_forward.  The bias is read once per 128-row
- * query block.  Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}, bias
+ * query block.  Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up
+ * to 128, bias
  * rows 16-byte aligned (Sk, bias_stride_b and bias_stride_h multiples of 8,
  * pointer 16-byte aligned), one head's bias (Sq * Sk elements) under 2 GiB
  * (SDPA_ERR_UNSUPPORTED otherwise).  out and lse must not overlap the bias.
@@ -165,7 +168,7 @@ size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq);
  * guide's ordered, atomic-free reduction).  Accumulation is fp32; P and dS are
  * rounded to dtype before their products, and the gradients to dtype at the end.
  * Outputs and workspace must not overlap each other or any input.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128.
  */
 sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const void *out,
                             const void *dout, const float *lse,
@@ -196,7 +199,7 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
  *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
  *   out        device [B, Hq, 1, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128.
  */
 sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D,
@@ -231,7 +234,8 @@ sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
  *                (same layout as sdpa_decode's with B = queries)
  *   out          device [queries, Hq, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D in {64, 128}, page_size a
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128,
+ * page_size a
  * multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
@@ -270,7 +274,7 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *                 keys j <= the row's absolute position
  *   out           device [total_q, Hq, D]
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
- * SDPA_F16, D in {64, 128}, page_size a multiple of 16
+ * SDPA_F16, D a multiple of 8 up to 128, page_size a multiple of 16
  * (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside
