@@ -11,7 +11,8 @@ resident in HBM:
   * the same decode over a shuffled 16-key page cache, and the causal prefill
     as whole-sequence chunks over such a cache
   * the attention backward (dQ, dK, dV) of the causal prefill workload, from
-    its forward output and log-sum-exp (computed once, before the timing)
+    its forward output and log-sum-exp (computed once, before the timing),
+    with the ordered reduction and with the atomic-dQ one
   * the causal prefill with a general additive mask: a per-head bias tensor
     [1, 16, 4096, 4096] bf16 added to the scaled scores
 Each call is bracketed by HIP events on the stream it is launched on (torch's
@@ -176,7 +177,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward", "bias"],
+                                       "backward", "backward_atomic", "bias"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,13 +239,13 @@ def main():
     # Backward: the causal prefill workload; its forward output and lse come
     # from one forward call here, outside the timed region.
     ibw = None
-    if args.only in (None, "backward"):
+    if args.only in (None, "backward", "backward_atomic"):
         out_b, lse_b = sd.sdpa_forward_lse(ip["q"], ip["k"], ip["v"], wp.scale, sd.MASK_CAUSAL)
         ibw = {"out": out_b, "lse": lse_b,
                "dout": draw_grad(tuple(ip["q"].shape), wp.dtype, wp.seed, dev),
                "dq": torch.empty_like(ip["q"]), "dk": torch.empty_like(ip["k"]),
                "dv": torch.empty_like(ip["v"]),
-               "ws": torch.empty(sd.sdpa_backward_workspace_size(wp.B, wp.Hq, wp.Sq),
+               "ws": torch.empty(sd.sdpa_backward_atomic_workspace_size(wp.B, wp.Hq, wp.Sq, wp.D),
                                  dtype=torch.uint8, device=dev)}
     # Bias: the causal prefill workload with a per-head [1, Hq, Sq, Sk] bias.
     ibias = None
@@ -272,10 +273,14 @@ def main():
                                              ibw["lse"], wp.scale, sd.MASK_CAUSAL, None,
                                              ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"]),
     }
+    calls["backward_atomic"] = lambda: sd.sdpa_backward(
+        ip["q"], ip["k"], ip["v"], ibw["out"], ibw["dout"], ibw["lse"], wp.scale, sd.MASK_CAUSAL,
+        None, ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"], atomic=True)
     calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
                                                  sd.MASK_CAUSAL, None, ibias["out"])
     order = ([args.only] if args.only else
-             ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "bias"])
+             ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
+              "bias"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -384,6 +389,19 @@ def main():
                                         "traffic": backward_traffic(),
                                         "kernel": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>",
                                         "flops_per_launch": fl}}
+    if "backward_atomic" in ms:
+        fl = 2.5 * formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
+        tf = fl / (ms["backward_atomic"] * 1e-3) / 1e12
+        rec["backward_atomic"] = {"workload": "bf16_causal_backward_atomic_b4_h16_s4096_d128",
+                                  "ms": round(ms["backward_atomic"], 4), "value": round(tf, 3),
+                                  "unit": "TFLOP/s",
+                                  "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                               "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                               "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                               "traffic": None,
+                                               "kernel": "bwd_prep + bwd_dkdv<128, atomic dQ> + "
+                                                         "bwd_dq_convert",
+                                               "flops_per_launch": fl}}
     if "bias" in ms:
         fl = formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
         tf = fl / (ms["bias"] * 1e-3) / 1e12
@@ -407,6 +425,9 @@ def main():
         if "bias" in rec:
             rec.update({"value": rec["bias"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["bias"]["workload"]}
+        elif "backward_atomic" in rec:
+            rec.update({"value": rec["backward_atomic"]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec["backward_atomic"]["workload"]}
         elif "backward" in rec:
             rec.update({"value": rec["backward"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["backward"]["workload"]}

@@ -70,6 +70,9 @@ __device__ __forceinline__ f32x4 lds_f4(const float* __restrict__ p) {
 __device__ __forceinline__ void lds_st4(uint32_t* __restrict__ p, u32x4 v) {
     *(__attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) char*)p) = v;
 }
+__device__ __forceinline__ void lds_st2(uint16_t* __restrict__ p, u32x2 v) {
+    *(__attribute__((address_space(3))) u32x2*)((__attribute__((address_space(3))) char*)p) = v;
+}
 __device__ __forceinline__ u32x4 lds_ld4(const uint32_t* __restrict__ p) {
     return *(const __attribute__((address_space(3))) u32x4*)(
         (const __attribute__((address_space(3))) char*)p);
@@ -391,19 +394,34 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
 // ---------------------------------------------------------------------------
 constexpr int kKvThreads = 512;  // 8 waves
 
-template <int D, class T, bool GEN = false>
+//
+// DQ (the atomic variant): the same pass also forms dQ.  After P is handed
+// over, each role-dS wave writes its dS block ([key][query], 16-bit) into its
+// pair's dS slot; after a second barrier every wave takes one 32x32
+// tile of dQ = dS K over the block's 128 keys (both operands by transposed
+// reads: dS from the slots, K from a copy of the key block kept in LDS) and
+// adds it into the fp32 accumulator dq_acc with buffer atomics.  Keys past
+// the batch's limit get P = 0 here, so they add nothing.  Atomics count in
+// vmcnt on this GPU, so each step ends with vmcnt(0) and the tiles use two
+// LDS stages (loaded one step ahead) instead of three.
+template <int D, class T, bool GEN = false, bool DQ = false>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                                                                  const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
+    using L64 = BwGeo<64>;                  // the [32 key x 64 query] dS slots
     constexpr int NK = D / 16;              // contraction steps of S and dP
     constexpr int ND = D / 32;              // 32-dim blocks of dK and dV
     constexpr int DMA = L::TILE * 2 / 1024 / 8;  // 1-KB DMA loads per wave per tile
-    // Three stages of: Q tile, dO tile, the tile rows' (lse2, delta) pairs
+    // NSTG stages of: Q tile, dO tile, the tile rows' (lse2, delta) pairs
     // (512 B used of a 1-KB slot); then the P hand-over, 64 B per lane of
-    // each role-P wave.
+    // each role-P wave; (DQ) then the dS slots [pair][32 keys][64 queries]
+    // and the workgroup's 128 K rows.
+    constexpr int NSTG = DQ ? 2 : 3;
     constexpr int STAGE = 2 * L::TILE + 512;
-    constexpr int EX = 3 * STAGE;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[3 * STAGE + 4 * 64 * 32];
+    constexpr int EX = NSTG * STAGE;
+    constexpr int DSX = EX + 4 * 64 * 32;
+    constexpr int KB = DSX + 4 * 32 * 64;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[DQ ? KB + kBwRows * D : DSX];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -446,6 +464,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     const int qt0 = a.causal ? k0 / kBwTile : 0;
     const int nqt = (k0 < kv_lim) ? max(0, (a.Sq + kBwTile - 1) / kBwTile - qt0) : 0;
     const int steps = G * nqt;
+
+    if constexpr (DQ) {
+        // The block's 128 K rows into LDS (same swizzle as the tiles; rows
+        // past Sk and chunks past DR read as zeros).
+        constexpr int KD = kBwRows * D * 2 / 1024 / 8;  // 1-KB loads per wave
+        const __amdgpu_buffer_rsrc_t rk =
+            rsrc(static_cast<const uint16_t*>(a.k) + kvh + (int64_t)k0 * DR, (uint32_t)(a.Sk - k0) * DR * 2);
+#pragma unroll
+        for (int i = 0; i < KD; ++i) {
+            const int s = 64 * (KD * wave + i) + lane;
+            const int r = s / L::CPR, c = (s % L::CPR) ^ L::f(r);
+            dma(rk, smem + KB + 512 * (KD * wave + i),
+                8 * c < DR ? (uint32_t)r * DR * 2 + (uint32_t)(c * 16) : kOutside);
+        }
+    }
 
     const BwOffsets<D> off(0, lane, DR);  // row and transposed read offsets
     uint32_t dmo[DMA];
@@ -523,7 +556,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     // One 64-query tile.  live: this pair has work here; mask: hide queries
     // before key kj (causal diagonal).
     auto compute = [&](const uint16_t* qs, const uint16_t* ds, const float* st, int q0, bool live,
-                       bool mask) __attribute__((always_inline)) {
+                       bool mask, int hstep) __attribute__((always_inline)) {
         if (role == 0) {
             uint32_t pw[16];
             if (live) {
@@ -541,6 +574,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                         for (int j = 0; j < 4; ++j) {
                             p[j] = fast_exp2(fmaf(s[4 * i + j], c, -l2[j]));
                             if (mask) p[j] = kj > q0 + 32 * qb + 8 * i + 4 * hg + j ? 0.f : p[j];
+                            if (DQ) p[j] = kj >= kv_lim ? 0.f : p[j];  // dQ must not see them
                         }
                         pw[8 * qb + 2 * i] = pack2<T>(p[0], p[1]);
                         pw[8 * qb + 2 * i + 1] = pack2<T>(p[2], p[3]);
@@ -579,7 +613,61 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                         dw[2 * i] = pack2<T>(pa.x * (x[4 * i] - dl[0]), pa.y * (x[4 * i + 1] - dl[1]));
                         dw[2 * i + 1] = pack2<T>(pb.x * (x[4 * i + 2] - dl[2]), pb.y * (x[4 * i + 3] - dl[3]));
                     }
+                    if constexpr (DQ) {
+                        // dS of queries 32*qb + 8*i + 4*hg .. +3, key l32: one 8-byte
+                        // run of slot row l32 (64 queries wide, swizzled).
+                        uint16_t* slot = smem + DSX + pair * 2048;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            lds_st2(slot + l32 * 64 + (((4 * qb + i) ^ L64::f(l32)) * 8) + 4 * hg,
+                                    u32x2{dw[2 * i], dw[2 * i + 1]});
+                    }
                     grads(qs, qb, dw);
+                }
+            }
+        }
+        if constexpr (DQ) {
+            lds_barrier();  // every live pair's dS is in its slot
+            // Wave w: queries 32*(w%2) .. +31 of the tile, dims 32*(w/2) .. +31.
+            const int qb3 = wave & 1, db3 = wave >> 1;
+            if (db3 < ND) {
+                // transposed-read offsets into a dS slot (64 queries wide)
+                int slot_lo, slot_hi;
+                {
+                    const int g16 = lane >> 4, j16 = lane & 15;
+                    const int rl = 4 * hg + (j16 >> 2), rh = rl + 8;
+                    const int col = 32 * qb3 + 16 * (g16 & 1) + 4 * (j16 & 3);
+                    slot_lo = rl * 64 + (((col >> 3) ^ L64::f(rl)) * 8) + (col & 7);
+                    slot_hi = rh * 64 + (((col >> 3) ^ L64::f(rh)) * 8) + (col & 7);
+                }
+                f32x16 acc3 = {};
+                bool any = false;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {  // 16 keys per step, 32 per pair slot
+                    const int pr = kk >> 1, kp0 = k0 + 32 * pr;
+                    const bool plive = kp0 < kv_lim && (!a.causal || q0 + kBwTile - 1 >= kp0);
+                    if (!plive) continue;  // workgroup-uniform
+                    any = true;
+                    const uint16_t* sl = smem + DSX + pr * 2048 + 16 * (kk & 1) * 64;
+                    const uint16_t* kb = smem + KB + 16 * kk * D;
+                    const u32x2 alo = lds_tr(sl + slot_lo), ahi = lds_tr(sl + slot_hi);
+                    const u32x2 blo = lds_tr(kb + off.trl[db3]), bhi = lds_tr(kb + off.trh[db3]);
+                    acc3 = mfma_32x32x16<T>(u32x4{alo[0], alo[1], ahi[0], ahi[1]},
+                                            u32x4{blo[0], blo[1], bhi[0], bhi[1]}, acc3);
+                }
+                // register r: query q0 + 32*qb3 + 8*(r/4) + 4*hg + r%4, dim 32*db3 + l32.
+                // Buffer atomics over this head's [Sq, DR] accumulator: rows past
+                // Sq fall outside it and are dropped; dims past DR go nowhere.
+                const int dim = 32 * db3 + l32;
+                if (any) {
+                    const __amdgpu_buffer_rsrc_t ra = rsrc(a.dq_acc + ((int64_t)b * a.Hq + hstep) * a.Sq * DR,
+                                                           (uint32_t)a.Sq * DR * 4);
+                    const uint32_t base = dim < DR ? (uint32_t)((q0 + 32 * qb3 + 4 * hg) * DR + dim) * 4
+                                                   : kOutside;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                            acc3[r], ra, base + (uint32_t)((8 * (r >> 2) + (r & 3)) * DR * 4), 0, 0);
                 }
             }
         }
@@ -591,27 +679,28 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         // Everything but this step's own loads has landed (vmcnt counts loads
         // in issue order; wave 0 also issued the statistics load).
         if (last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (DQ) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // atomics count too
         else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA + 1) : "memory");
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA) : "memory");
     };
     if (steps > 0) issue(0, 0);
-    if (steps > 1) issue(1, 1);
-    wait_older(steps <= 1);
+    if (NSTG == 3 && steps > 1) issue(1, 1);
+    wait_older(steps <= NSTG - 2);
     __syncthreads();
     auto step = [&](int st, const int cur) __attribute__((always_inline)) {
-        if (st + 2 < steps) issue(st + 2, (cur + 2) % 3);
+        if (st + NSTG - 1 < steps) issue(st + NSTG - 1, (cur + NSTG - 1) % NSTG);
         const int q0 = (qt0 + st % nqt) * kBwTile;
         const bool live = kw < kv_lim && (!a.causal || q0 + kBwTile - 1 >= kw);
         const uint16_t* base = smem + cur * STAGE;
         compute(base, base + L::TILE, reinterpret_cast<const float*>(base + 2 * L::TILE), q0, live,
-                a.causal && q0 < kw + 31);
-        wait_older(st + 2 >= steps);
+                a.causal && q0 < kw + 31, gk * G + st / nqt);
+        wait_older(st + NSTG - 1 >= steps);
         __syncthreads();
     };
-    for (int st = 0; st < steps; st += 3) {
+    for (int st = 0; st < steps; st += NSTG) {
         step(st, 0);
         if (st + 1 < steps) step(st + 1, 1);
-        if (st + 2 < steps) step(st + 2, 2);
+        if (NSTG == 3 && st + 2 < steps) step(st + 2, 2);
     }
 
     // Role P: dV = P^T dO; role dS: dK = scale * (dS^T Q).  Register r of
@@ -634,6 +723,67 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Atomic variant, around the fused pass: the row statistics (what the dQ
+// pass writes in the ordered variant) plus a zeroed fp32 dQ accumulator, and
+// the final conversion dQ = scale * dq_acc rounded to the input type.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardArgs a) {
+    // 16 lanes per row, 8 dims each; a 16-lane group leaves together.
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int j = threadIdx.x & 15;
+    if (row >= (int64_t)a.B * a.Hq * a.Sq) return;
+    const int DR = a.D;
+    float part = 0.f;
+    if (8 * j < DR) {
+        const uint32_t* o = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.out) + row * DR + 8 * j);
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.dout) + row * DR + 8 * j);
+        part = dot8<T>(u32x4{d[0], d[1], d[2], d[3]}, u32x4{o[0], o[1], o[2], o[3]}, 0.f);
+        float* z = a.dq_acc + row * DR + 8 * j;
+        *reinterpret_cast<f32x4*>(z) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(z + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (j == 0) {
+        const int64_t bh = row / a.Sq, i = row % a.Sq;
+        const float l = a.lse[row];
+        float2* st = reinterpret_cast<float2*>(a.delta) + bh * stats_stride(a.Sq) + i;
+        *st = l == -INFINITY ? make_float2(INFINITY, 0.f) : make_float2(l * kLog2e, part);
+    }
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BackwardArgs a) {
+    const int64_t n = (int64_t)a.B * a.Hq * a.Sq * a.D;  // a multiple of 8
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(a.dq_acc + i);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(a.dq_acc + i + 4);
+    uint16_t* dq = static_cast<uint16_t*>(a.dq) + i;
+    *reinterpret_cast<u32x2*>(dq) = u32x2{pack2<T>(x0[0] * a.scale, x0[1] * a.scale),
+                                          pack2<T>(x0[2] * a.scale, x0[3] * a.scale)};
+    *reinterpret_cast<u32x2*>(dq + 4) = u32x2{pack2<T>(x1[0] * a.scale, x1[1] * a.scale),
+                                              pack2<T>(x1[2] * a.scale, x1[3] * a.scale)};
+}
+
+template <int D, class T, bool GEN>
+hipError_t launch_backward_atomic_d(const BackwardArgs& a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkb = (a.Sk + kBwRows - 1) / kBwRows;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, GEN, true>), dim3(a.B * a.Hkv * nkb), dim3(kKvThreads), 0,
+                       s, a, a.key_lens);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n8 = rows * a.D / 8;
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<T>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D, class T, bool GEN>
 hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int nqb = (a.Sq + kBwRows - 1) / kBwRows;
@@ -649,6 +799,12 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
 
 template <class T>
 hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
+    if (a.dq_acc) {  // atomic dQ
+        if (a.D == 128) return launch_backward_atomic_d<128, T, false>(a, s);
+        if (a.D == 64) return launch_backward_atomic_d<64, T, false>(a, s);
+        if (a.D < 64) return launch_backward_atomic_d<64, T, true>(a, s);
+        return launch_backward_atomic_d<128, T, true>(a, s);
+    }
     if (a.D == 128) return launch_backward_d<128, T, false>(a, s);
     if (a.D == 64) return launch_backward_d<64, T, false>(a, s);
     // other multiples of 8: the 64- or 128-wide kernels with zero-filled chunks

@@ -37,6 +37,7 @@ struct BackwardArgs {
     void* dk;
     void* dv;
     float* delta;             // workspace [B, Hq, Sq]: rowsum(dO * O)
+    float* dq_acc = nullptr;  // atomic variant: fp32 [B, Hq, Sq, D] dQ accumulator (workspace)
     int B, Hq, Hkv, Sq, Sk, D;
     float scale;
     bool causal;

@@ -246,11 +246,16 @@ size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq) {
     return round_up((size_t)rows * 2 * sizeof(float));
 }
 
-sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const void* out,
+}  // extern "C"
+
+namespace {
+
+sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const void* out,
                             const void* dout, const float* lse, int64_t B, int64_t Hq,
                             int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
                             int mask_kind, const int32_t* key_lens, void* dq, void* dk, void* dv,
-                            void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+                            void* workspace, size_t workspace_bytes, int dtype, void* stream,
+                            bool atomic) {
     if (!out || !dout || !lse || !dk || !dv)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     int64_t qbytes = 0, kbytes = 0;
@@ -269,7 +274,10 @@ sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const v
     if (padded != (key_lens != nullptr))
         return fail(SDPA_ERR_INVALID_ARGUMENT,
                     "key_lens must be given exactly when SDPA_MASK_KEY_PADDING is set");
-    const size_t need = sdpa_backward_workspace_size(B, Hq, Sq);
+    const size_t need = atomic ? sdpa_backward_atomic_workspace_size(B, Hq, Sq, D)
+                               : sdpa_backward_workspace_size(B, Hq, Sq);
+    if (atomic && Sq * D * 4 > INT_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "one head's fp32 dQ accumulator exceeds 2 GiB");
     if (!workspace || workspace_bytes < need)
         return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace_bytes);
@@ -307,6 +315,9 @@ sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const v
     a.dk = dk;
     a.dv = dv;
     a.delta = static_cast<float*>(workspace);
+    if (atomic)
+        a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            sdpa_backward_workspace_size(B, Hq, Sq));
     a.B = (int)B;
     a.Hq = (int)Hq;
     a.Hkv = (int)Hkv;
@@ -319,6 +330,37 @@ sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const v
     (void)hipGetLastError();
     return hip_status(sdpa::launch_backward_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream)),
                       "sdpa_backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                            int mask_kind, const int32_t* key_lens, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    return backward_impl(q, k, v, out, dout, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens,
+                         dq, dk, dv, workspace, workspace_bytes, dtype, stream, false);
+}
+
+size_t sdpa_backward_atomic_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t D) {
+    const size_t st = sdpa_backward_workspace_size(B, Hq, Sq);
+    if (st == 0 || D < 1) return 0;
+    const int64_t n = numel4(B, Hq, Sq, D);
+    if (n < 0 || n > INT64_MAX / 8) return 0;
+    return st + round_up((size_t)n * sizeof(float));
+}
+
+sdpa_status_t sdpa_backward_atomic(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, int64_t B, int64_t Hq,
+                                   int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                                   int mask_kind, const int32_t* key_lens, void* dq, void* dk,
+                                   void* dv, void* workspace, size_t workspace_bytes, int dtype,
+                                   void* stream) {
+    return backward_impl(q, k, v, out, dout, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens,
+                         dq, dk, dv, workspace, workspace_bytes, dtype, stream, true);
 }
 
 size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_splits) {

@@ -28,7 +28,8 @@ MAX_SPLITS = 32
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
 EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_bias", "sdpa_backward",
-            "sdpa_backward_workspace_size",
+            "sdpa_backward_workspace_size", "sdpa_backward_atomic",
+            "sdpa_backward_atomic_workspace_size",
             "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
             "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
 
@@ -65,6 +66,10 @@ def load_library():
     lib.sdpa_backward.restype = i32
     lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, i32, vp]
+    lib.sdpa_backward_atomic.restype = i32
+    lib.sdpa_backward_atomic.argtypes = lib.sdpa_backward.argtypes
+    lib.sdpa_backward_atomic_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_backward_atomic_workspace_size.argtypes = [i64, i64, i64, i64]
     lib.sdpa_decode.restype = i32
     lib.sdpa_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, i32, vp,
                                 ctypes.c_size_t, vp, i32, vp]
@@ -228,12 +233,18 @@ def sdpa_backward_workspace_size(B, Hq, Sq):
     return int(load_library().sdpa_backward_workspace_size(B, Hq, Sq))
 
 
+def sdpa_backward_atomic_workspace_size(B, Hq, Sq, D):
+    return int(load_library().sdpa_backward_atomic_workspace_size(B, Hq, Sq, D))
+
+
 def sdpa_backward(q, k, v, out, dout, lse, scale, mask_kind=MASK_NONE, key_lens=None,
-                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+                  dq=None, dk=None, dv=None, workspace=None, stream=None, atomic=False):
     """(dq, dk, dv) of O = softmax(Q K^T * scale + mask) V given dout = dL/dO.
 
     out and lse are the forward's (sdpa_forward_lse); dq is [B,Hq,Sq,D], dk and
-    dv [B,Hkv,Sk,D], all in the input dtype.
+    dv [B,Hkv,Sk,D], all in the input dtype.  atomic=True calls
+    sdpa_backward_atomic (dQ summed with fp32 atomics) instead of the ordered
+    sdpa_backward.
     """
     B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
     for name, t in (("out", out), ("dout", dout)):
@@ -253,11 +264,13 @@ def sdpa_backward(q, k, v, out, dout, lse, scale, mask_kind=MASK_NONE, key_lens=
                 raise ValueError("%s must match its input in shape and dtype" % name)
         outs.append(t)
     dq, dk, dv = outs
-    need = sdpa_backward_workspace_size(B, Hq, Sq)
+    need = (sdpa_backward_atomic_workspace_size(B, Hq, Sq, D) if atomic
+            else sdpa_backward_workspace_size(B, Hq, Sq))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     lib = load_library()
-    _check(lib.sdpa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+    fn = lib.sdpa_backward_atomic if atomic else lib.sdpa_backward
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                              B, Hq, Hkv, Sq, Sk, D, float(scale), int(mask_kind), _ptr(key_lens),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _dtype_code(q),

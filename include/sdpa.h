@@ -178,6 +178,32 @@ sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const v
                             void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
 /*
+ * Bytes of device workspace sdpa_backward_atomic needs (0 if the sizes are
+ * invalid): the row statistics of sdpa_backward_workspace_size, then an fp32
+ * dQ accumulator [B, Hq, Sq, D], each section 256-byte aligned.
+ */
+size_t sdpa_backward_atomic_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t D);
+
+/*
+ * The attention backward with an atomic dQ reduction (ruDNN guide section 11:
+ * the history gradients by fp32 atomic addition, next to the ordered
+ * reduction of sdpa_backward).  Same arguments, results and contract as
+ * sdpa_backward except the workspace (sdpa_backward_atomic_workspace_size)
+ * and the order of dQ's sums: three kernels are enqueued — row statistics
+ * and a zeroed accumulator; one key-parallel pass that forms dK, dV and adds
+ * every key block's share of dQ into the accumulator with fp32 atomics; and
+ * the conversion dQ = scale * accumulator rounded to dtype.  dK and dV are
+ * bitwise reproducible; dQ's summation order varies from call to call, so
+ * dQ is not.  One head's accumulator (Sq * D floats) must be under 2 GiB.
+ */
+sdpa_status_t sdpa_backward_atomic(const void *q, const void *k, const void *v, const void *out,
+                                   const void *dout, const float *lse,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                                   int64_t D, float scale, int mask_kind, const int32_t *key_lens,
+                                   void *dq, void *dk, void *dv,
+                                   void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/*
  * Bytes of device workspace sdpa_decode needs for these sizes (0 if the sizes
  * are invalid).  Layout, fp32, 256-byte aligned sections:
  *   o_part [B, Hq, num_splits, D]  normalised partial outputs

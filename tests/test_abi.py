@@ -308,3 +308,22 @@ def fwd_bias(bias=FAKE_B, sb=0, sh=128 * 128, Sq=128, Sk=128, dtype=sd.SDPA_BF16
 def test_forward_bias_rejects(kw, status, needle):
     assert fwd_bias(**kw) == status
     assert needle in sd.last_error()
+
+
+def test_backward_atomic_workspace_and_rejects():
+    lib = sd.load_library()
+    for B, Hq, Sq, D in [(4, 16, 4096, 128), (1, 1, 1, 8), (3, 5, 333, 96)]:
+        st = lib.sdpa_backward_workspace_size(B, Hq, Sq)
+        assert lib.sdpa_backward_atomic_workspace_size(B, Hq, Sq, D) == \
+            st + (B * Hq * Sq * D * 4 + 255) // 256 * 256
+    assert lib.sdpa_backward_atomic_workspace_size(1, 1, 1, 0) == 0
+    ws_small = lib.sdpa_backward_workspace_size(2, 4, 128)  # enough for the ordered one only
+    st = lib.sdpa_backward_atomic(FAKE, FAKE_K, FAKE_V, FAKE_O, FAKE_DO, FAKE_L, 2, 4, 2, 128, 128,
+                                  128, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, ws_small,
+                                  sd.SDPA_BF16, None)
+    assert st == sd.SDPA_ERR_WORKSPACE and "workspace" in sd.last_error()
+    st = lib.sdpa_backward_atomic(FAKE, FAKE_K, FAKE_V, FAKE_O, FAKE_DO, FAKE_L, 1, 1, 1, 1 << 23,
+                                  128, 128, 0.125, 0, None, ctypes.c_void_p(1 << 44),
+                                  ctypes.c_void_p(1 << 45), ctypes.c_void_p(1 << 46),
+                                  ctypes.c_void_p(1 << 47), 1 << 40, sd.SDPA_BF16, None)
+    assert st == sd.SDPA_ERR_UNSUPPORTED

@@ -127,3 +127,68 @@ def test_backward_full_size_sampled_heads():
         compare_grad(to64(dq[sl]), rq, BF16, "full b=%d h=%d dq" % (b, h))
         compare_grad(to64(dk[sl]), rk, BF16, "full b=%d h=%d dk" % (b, h))
         compare_grad(to64(dv[sl]), rv, BF16, "full b=%d h=%d dv" % (b, h))
+
+
+# ------------------------------------------------------------------ atomic dQ
+
+def run_backward_atomic(q, k, v, dout, scale, mask, lens):
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    dq, dk, dv = sd.sdpa_backward(q, k, v, out, dout, lse, scale, mask, lens, atomic=True)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128, 96])
+@pytest.mark.parametrize("mask", [0, 1, 2, 3], ids=["none", "causal", "padding", "causal+padding"])
+def test_backward_atomic_parity(dtype, D, mask):
+    B, Hq, Hkv, S = 2, 4, 2, 300
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, dtype, 800 + D + mask, DEV)
+    dout = draw_grad((B, Hq, S, D), dtype, 801 + D + mask, DEV)
+    lens = torch.tensor([300, 97], dtype=torch.int32, device=DEV) if mask & 2 else None
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv = run_backward_atomic(q, k, v, dout, scale, mask, lens)
+    ln = None if lens is None else lens.cpu().numpy()
+    rq, rk, rv = O.sdpa_backward(to64(q), to64(k), to64(v), to64(dout), scale, mask, ln)
+    what = "atomic %s D=%d mask=%d" % (dtype, D, mask)
+    compare_grad(to64(dq), rq, dtype, what + " dq")
+    compare_grad(to64(dk), rk, dtype, what + " dk")
+    compare_grad(to64(dv), rv, dtype, what + " dv")
+
+
+def test_backward_atomic_dead_rows_and_rectangular():
+    B, Hq, Hkv, Sq, Sk, D = 3, 6, 2, 200, 333, 128
+    q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, BF16, 810, DEV)
+    dout = draw_grad((B, Hq, Sq, D), BF16, 811, DEV)
+    lens = torch.tensor([333, 0, 45], dtype=torch.int32, device=DEV)
+    dq, dk, dv = run_backward_atomic(q, k, v, dout, 0.1, sd.MASK_KEY_PADDING, lens)
+    rq, rk, rv = O.sdpa_backward(to64(q), to64(k), to64(v), to64(dout), 0.1, O.MASK_KEY_PADDING,
+                                 lens.cpu().numpy())
+    compare_grad(to64(dq), rq, BF16, "atomic rect dq")
+    compare_grad(to64(dk), rk, BF16, "atomic rect dk")
+    compare_grad(to64(dv), rv, BF16, "atomic rect dv")
+    assert not dq[1].any() and not dk[1].any() and not dv[1].any()
+
+
+def test_backward_atomic_agrees_with_ordered_full_size():
+    # the causal prefill workload: the two reductions agree to the bars, and
+    # dK, dV of the atomic variant are reproducible call to call
+    B, H, S, D = 4, 16, 4096, 128
+    q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 820, DEV)
+    dout = draw_grad((B, H, S, D), BF16, 821, DEV)
+    scale = 1 / math.sqrt(D)
+    o_dq, o_dk, o_dv = run_backward(q, k, v, dout, scale, sd.MASK_CAUSAL, None)[2:]
+    a_dq, a_dk, a_dv = run_backward_atomic(q, k, v, dout, scale, sd.MASK_CAUSAL, None)
+    _, a_dk2, a_dv2 = run_backward_atomic(q, k, v, dout, scale, sd.MASK_CAUSAL, None)
+    assert torch.equal(a_dk, a_dk2) and torch.equal(a_dv, a_dv2)
+    for x, y, name in ((a_dq, o_dq, "dq"), (a_dk, o_dk, "dk"), (a_dv, o_dv, "dv")):
+        d = (x.float() - y.float())
+        rel = (d.norm() / y.float().norm()).item()
+        print("atomic vs ordered %s: rel-L2 %.3e" % (name, rel))
+        assert rel < 5e-3
+    sl = (slice(1, 2), slice(7, 8))
+    rq, rk, rv = O.sdpa_backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(dout[sl]), scale,
+                                 O.MASK_CAUSAL)
+    compare_grad(to64(a_dq[sl]), rq, BF16, "atomic full dq")
+    compare_grad(to64(a_dk[sl]), rk, BF16, "atomic full dk")
+    compare_grad(to64(a_dv[sl]), rv, BF16, "atomic full dv")
