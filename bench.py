@@ -74,6 +74,13 @@ def backward_traffic():
     return None if None in parts else sum(parts)
 
 
+def atomic_traffic():
+    """HBM bytes of one atomic-dQ backward call (its three kernels), if valid."""
+    parts = [stored_traffic(k, "backward.hip")
+             for k in ("backward_atomic_prep", "backward_atomic_dkdv", "backward_atomic_convert")]
+    return None if None in parts else sum(parts)
+
+
 def formula_flops(B, Hq, Sq, Sk, D, causal):
     f = 4.0 * B * Hq * Sq * Sk * D
     return f / 2 if causal else f
@@ -155,7 +162,18 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
         out["padded"] = entry(fwd, "forward.hip", fr[1::4], wr[1::4])
         out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::4], wr[2::4])
         out["bias"] = entry(fwd, "forward.hip", fr[3::4], wr[3::4])
-    for key, name in (("backward_dq", "bwd_dq_kernel"), ("backward_dkdv", "bwd_dkdv_kernel")):
+    if "bwd_dq_kernel" in fetch:
+        out["backward_dq"] = entry("bwd_dq_kernel", "backward.hip", fetch["bwd_dq_kernel"],
+                                   write["bwd_dq_kernel"])
+    dk = "bwd_dkdv_kernel"
+    if dk in fetch:
+        if "bwd_prep_kernel" in fetch:  # ordered and atomic passes alternate
+            out["backward_dkdv"] = entry(dk, "backward.hip", fetch[dk][0::2], write[dk][0::2])
+            out["backward_atomic_dkdv"] = entry(dk, "backward.hip", fetch[dk][1::2], write[dk][1::2])
+        else:
+            out["backward_dkdv"] = entry(dk, "backward.hip", fetch[dk], write[dk])
+    for key, name in (("backward_atomic_prep", "bwd_prep_kernel"),
+                      ("backward_atomic_convert", "bwd_dq_convert_kernel")):
         if name in fetch:
             out[key] = entry(name, "backward.hip", fetch[name], write[name])
     # A full step runs the dense decode, then the paged one: their split and
@@ -398,7 +416,7 @@ def main():
                                   "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                                "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                               "traffic": None,
+                                               "traffic": atomic_traffic(),
                                                "kernel": "bwd_prep + bwd_dkdv<128, atomic dQ> + "
                                                          "bwd_dq_convert",
                                                "flops_per_launch": fl}}
