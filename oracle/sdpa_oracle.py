@@ -37,6 +37,10 @@ reordered:
   scaled scores next to the 0 / -inf masks (tensai guide, "Attention の
   組み立て": the scores are scaled and then Add(mask) with a mask tensor that
   broadcasts over its size-1 batch and head axes); -inf entries hide keys.
+* block      the multi-head attention block around it (tensai guide,
+  "Attention の組み立て"): q, k, v = heads(x . w) for w in wq, wk, wv, where
+  heads reshapes (batch, seq, model) to (batch, seq, head, headDim) and swaps
+  seq and head; the attention above; y = heads^-1(o) . wo.
 * split-KV   partial attention over disjoint key ranges, each with its own lse,
   and the log-sum-exp merge of those partials (ruDNN user guide section 9:
   history split into 2..=32 pieces, partial statistics and merge in FP32).
@@ -319,6 +323,45 @@ def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None):
     return dq, dk, dv
 
 
+def split_heads(t, n_heads):
+    """(batch, seq, model) -> (batch, head, seq, headDim): reshape to
+    (batch, seq, head, headDim), then swap the seq and head axes (tensai guide,
+    "Attention の組み立て", the heads helper)."""
+    B, S, M = t.shape
+    return t.reshape(B, S, n_heads, M // n_heads).transpose(0, 2, 1, 3)
+
+
+def merge_heads(t):
+    """(batch, head, seq, headDim) -> (batch, seq, model): the inverse of split_heads."""
+    B, H, S, hd = t.shape
+    return t.transpose(0, 2, 1, 3).reshape(B, S, H * hd)
+
+
+def block_forward(x, wq, wk, wv, wo, n_heads, scale=None, mask_kind=MASK_NONE, key_lens=None):
+    """Multi-head attention block of the tensai guide ("Attention の組み立て").
+
+    x [B, S, model]; wq, wk, wv, wo [model, model] (x is multiplied on the
+    left: x . w).  q, k, v = split_heads(x . w{q,k,v}); the attention of
+    sdpa_forward (scale defaults to 1 / sqrt(headDim)); y = merge_heads(o) . wo.
+    Returns y [B, S, model] in fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    wq, wk, wv, wo = (np.asarray(w, dtype=np.float64) for w in (wq, wk, wv, wo))
+    B, S, M = x.shape
+    if M % n_heads != 0:
+        raise ValueError("model width must be a multiple of the head count")
+    for w in (wq, wk, wv, wo):
+        if w.shape != (M, M):
+            raise ValueError("weights must be [model, model]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(M // n_heads)
+    q = split_heads(x @ wq, n_heads)
+    k = split_heads(x @ wk, n_heads)
+    v = split_heads(x @ wv, n_heads)
+    o = sdpa_forward(q, k, v, scale, mask_kind, key_lens)
+    return merge_heads(o) @ wo
+
+
 def paged_gather(cache, table_row, length, page_size):
     """Logical rows 0..length-1 of one sequence read through its page table.
 
@@ -391,5 +434,6 @@ __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KEY_PADDING", "visible_rows", "attend",
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
     "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
-    "chunk_positions", "sdpa_backward", "bias_slice",
+    "chunk_positions", "sdpa_backward", "bias_slice", "split_heads", "merge_heads",
+    "block_forward",
 ]

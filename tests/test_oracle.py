@@ -711,3 +711,70 @@ def test_bias_rows_equal_full_and_minus_inf_row_is_nan():
     for n, (b, h, i) in enumerate(idx):
         np.testing.assert_allclose(o[n], full[b, h, i], rtol=0, atol=1e-14)
     assert np.isnan(full[:, 2, 3]).all() and np.isneginf(lse[:, 2, 3]).all()
+
+
+# ------------------------------------------------------------------ attention block
+
+def _block_inputs(seed, B=2, S=5, M=8):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, S, M))
+    ws = [rng.standard_normal((M, M)) / np.sqrt(M) for _ in range(4)]
+    return x, ws, rng
+
+
+def test_block_single_head_is_the_essays_kernel():
+    # one head, no mask, wo = I, scale 1/sqrt(model): the HOF essay's
+    # compute_attention (section 4): q, k, v = x.w, exp(q k^T / sqrt(d)),
+    # row sums, row-stochastic weights, weights . v -- by scalar loops
+    x, (wq, wk, wv, _), _ = _block_inputs(90, B=1, S=4, M=3)
+    y = O.block_forward(x, wq, wk, wv, np.eye(3), 1)
+    xs = x[0]
+    q = [[math.fsum(xs[i, a] * wq[a, j] for a in range(3)) for j in range(3)] for i in range(4)]
+    k = [[math.fsum(xs[i, a] * wk[a, j] for a in range(3)) for j in range(3)] for i in range(4)]
+    v = [[math.fsum(xs[i, a] * wv[a, j] for a in range(3)) for j in range(3)] for i in range(4)]
+    for i in range(4):
+        e = [math.exp(math.fsum(q[i][d] * k[j][d] for d in range(3)) / math.sqrt(3)) for j in range(4)]
+        tot = math.fsum(e)
+        ref = [math.fsum(e[j] / tot * v[j][d] for j in range(4)) for d in range(3)]
+        np.testing.assert_allclose(y[0, i], ref, rtol=0, atol=1e-13)
+
+
+def test_block_single_token_closed_form():
+    # one token sees only itself: y = x . wv . wo, whatever wq, wk, the scale
+    x, (wq, wk, wv, wo), _ = _block_inputs(91, S=1)
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL):
+        y = O.block_forward(x, wq, wk, wv, wo, 2, scale=0.37, mask_kind=mask)
+        np.testing.assert_allclose(y, x @ wv @ wo, rtol=0, atol=1e-13)
+
+
+def test_block_causal_first_token_and_identity_projections():
+    x, (wq, wk, wv, wo), _ = _block_inputs(92)
+    y = O.block_forward(x, wq, wk, wv, wo, 2, mask_kind=O.MASK_CAUSAL)
+    np.testing.assert_allclose(y[:, 0], x[:, 0] @ wv @ wo, rtol=0, atol=1e-13)
+    # identity projections: head h attends with columns 4h..4h+3 of x
+    I = np.eye(8)
+    yi = O.block_forward(x, I, I, I, I, 2, mask_kind=O.MASK_CAUSAL)
+    for h in range(2):
+        xh = x[:, :, 4 * h:4 * h + 4]
+        ref = O.sdpa_forward(xh[:, None], xh[:, None], xh[:, None], 0.5, O.MASK_CAUSAL)[:, 0]
+        np.testing.assert_allclose(yi[:, :, 4 * h:4 * h + 4], ref, rtol=0, atol=1e-13)
+
+
+def test_block_head_permutation_invariance():
+    # permuting the heads (column blocks of wq, wk, wv and the matching row
+    # blocks of wo) leaves y unchanged
+    x, (wq, wk, wv, wo), _ = _block_inputs(93, M=12)
+    perm = [2, 0, 1]
+    cols = np.concatenate([np.arange(4 * p, 4 * p + 4) for p in perm])
+    y = O.block_forward(x, wq, wk, wv, wo, 3, mask_kind=O.MASK_CAUSAL)
+    yp = O.block_forward(x, wq[:, cols], wk[:, cols], wv[:, cols], wo[cols], 3,
+                         mask_kind=O.MASK_CAUSAL)
+    np.testing.assert_allclose(y, yp, rtol=0, atol=1e-12)
+
+
+def test_block_split_merge_heads_roundtrip():
+    t = np.arange(2 * 3 * 12, dtype=np.float64).reshape(2, 3, 12)
+    h = O.split_heads(t, 4)
+    assert h.shape == (2, 4, 3, 3)
+    assert h[1, 2, 0, 1] == t[1, 0, 2 * 3 + 1]      # (b, head, seq, d) <- (b, seq, head*hd + d)
+    np.testing.assert_array_equal(O.merge_heads(h), t)
