@@ -78,6 +78,26 @@ hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
 // bf16 or (f16) fp16.
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
                                       hipStream_t s);
+// C = A . B (16-bit, fp32 accumulation) for the attention block's
+// projections.  a_heads: A [M = B*S, K = model] is read from (batch, head,
+// seq, headDim) layout; c_heads: C [M, N = model] is written to it (headDim
+// hd, sequence length S).  blockIdx.y < nz selects (b_z, c_z).
+struct GemmArgs {
+    const void* a;
+    const void* b0;
+    const void* b1;
+    const void* b2;
+    void* c0;
+    void* c1;
+    void* c2;
+    int M, N, K;
+    int S, hd;
+    int nz;
+    bool a_heads, c_heads;
+    uint32_t a_bytes;  // extent of A in bytes (< 2 GiB)
+};
+hipError_t launch_gemm_16bit(const GemmArgs& g, bool f16, hipStream_t s);
+
 // Backward: the dQ pass (also writes delta), then the dK / dV pass.
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s);
 

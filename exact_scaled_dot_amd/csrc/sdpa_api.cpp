@@ -363,6 +363,112 @@ sdpa_status_t sdpa_backward_atomic(const void* q, const void* k, const void* v, 
                          dq, dk, dv, workspace, workspace_bytes, dtype, stream, true);
 }
 
+size_t sdpa_block_workspace_size(int64_t B, int64_t S, int64_t model) {
+    if (B < 1 || S < 1 || model < 1) return 0;
+    const int64_t n = numel4(B, S, model, 1);
+    if (n < 0 || n > INT64_MAX / 16) return 0;
+    return 4 * round_up((size_t)n * 2);
+}
+
+sdpa_status_t sdpa_block_forward(const void* x, const void* wq, const void* wk, const void* wv,
+                                 const void* wo, int64_t B, int64_t S, int64_t model,
+                                 int64_t heads, float scale, int mask_kind,
+                                 const int32_t* key_lens, void* y, void* workspace,
+                                 size_t workspace_bytes, int dtype, void* stream) {
+    if (!x || !wq || !wk || !wv || !wo || !y)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (B < 1 || S < 1 || model < 1 || heads < 1)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "every size must be >= 1");
+    if (!known_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "the attention block needs 16-bit inputs (bf16 or fp16)");
+    if (model % heads != 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "model width %lld is not a multiple of heads %lld",
+                    (long long)model, (long long)heads);
+    const int64_t hd = model / heads;
+    if (!head_dim_ok(hd, dtype))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld not supported (a multiple of 8 up to 128)",
+                    (long long)hd);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
+    const bool padded = mask_kind & SDPA_MASK_KEY_PADDING;
+    if (padded != (key_lens != nullptr))
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "key_lens must be given exactly when SDPA_MASK_KEY_PADDING is set");
+    const int64_t n = numel4(B, S, model, 1);
+    if (n < 0 || n > INT_MAX / 2 || model * model > INT_MAX / 2)
+        return fail(SDPA_ERR_UNSUPPORTED, "an activation or weight exceeds 2 GiB");
+    const size_t need = sdpa_block_workspace_size(B, S, model);
+    if (!workspace || workspace_bytes < need)
+        return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace_bytes);
+    const int64_t xb = n * 2, wb = model * model * 2;
+    const void* ins[] = {x, wq, wk, wv, wo};
+    const int64_t insz[] = {xb, wb, wb, wb, wb};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(y, xb, ins[i], insz[i]) || overlap(workspace, (int64_t)need, ins[i], insz[i]))
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "y or the workspace overlaps an input");
+    if (overlap(y, xb, workspace, (int64_t)need) ||
+        (padded && (overlap(y, xb, key_lens, B * 4) || overlap(workspace, (int64_t)need, key_lens, B * 4))))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "y, the workspace and key_lens overlap");
+
+    char* ws = static_cast<char*>(workspace);
+    const size_t part = round_up((size_t)n * 2);
+    void *qb = ws, *kb = ws + part, *vb = ws + 2 * part, *ob = ws + 3 * part;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool f16 = dtype == SDPA_F16;
+    (void)hipGetLastError();
+    // q, k, v = heads(x . w): one launch, written straight into head layout.
+    sdpa::GemmArgs g{};
+    g.a = x;
+    g.b0 = wq;
+    g.b1 = wk;
+    g.b2 = wv;
+    g.c0 = qb;
+    g.c1 = kb;
+    g.c2 = vb;
+    g.M = (int)(B * S);
+    g.N = (int)model;
+    g.K = (int)model;
+    g.S = (int)S;
+    g.hd = (int)hd;
+    g.nz = 3;
+    g.a_heads = false;
+    g.c_heads = true;
+    g.a_bytes = (uint32_t)xb;
+    hipError_t e = sdpa::launch_gemm_16bit(g, f16, s);
+    if (e != hipSuccess) return hip_status(e, "sdpa_block_forward projection launch");
+    sdpa::ForwardArgs a;
+    a.q = qb;
+    a.k = kb;
+    a.v = vb;
+    a.out = ob;
+    a.key_lens = key_lens;
+    a.B = (int)B;
+    a.Hq = (int)heads;
+    a.Hkv = (int)heads;
+    a.Sq = (int)S;
+    a.Sk = (int)S;
+    a.D = (int)hd;
+    a.scale = scale;
+    a.causal = mask_kind & SDPA_MASK_CAUSAL;
+    a.padded = padded;
+    e = f16 ? sdpa::launch_forward_f16(a, s) : sdpa::launch_forward_bf16(a, s);
+    if (e != hipSuccess) return hip_status(e, "sdpa_block_forward attention launch");
+    // y = heads^-1(o) . wo: A read from head layout.
+    sdpa::GemmArgs go = g;
+    go.a = ob;
+    go.b0 = wo;
+    go.c0 = y;
+    go.nz = 1;
+    go.a_heads = true;
+    go.c_heads = false;
+    e = sdpa::launch_gemm_16bit(go, f16, s);
+    return hip_status(e, "sdpa_block_forward output projection launch");
+}
+
 size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_splits) {
     if (B < 1 || Hq < 1 || D < 1 || num_splits < 1 || num_splits > SDPA_MAX_SPLITS) return 0;
     const int64_t rows = numel4(B, Hq, num_splits, 1);

@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so"
 
 EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_bias", "sdpa_backward",
             "sdpa_backward_workspace_size", "sdpa_backward_atomic",
-            "sdpa_backward_atomic_workspace_size",
+            "sdpa_backward_atomic_workspace_size", "sdpa_block_forward",
+            "sdpa_block_workspace_size",
             "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
             "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
 
@@ -70,6 +71,11 @@ def load_library():
     lib.sdpa_backward_atomic.argtypes = lib.sdpa_backward.argtypes
     lib.sdpa_backward_atomic_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_backward_atomic_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.sdpa_block_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_block_workspace_size.argtypes = [i64, i64, i64]
+    lib.sdpa_block_forward.restype = i32
+    lib.sdpa_block_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32,
+                                       vp, vp, vp, ctypes.c_size_t, i32, vp]
     lib.sdpa_decode.restype = i32
     lib.sdpa_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, i32, vp,
                                 ctypes.c_size_t, vp, i32, vp]
@@ -276,6 +282,45 @@ def sdpa_backward(q, k, v, out, dout, lse, scale, mask_kind=MASK_NONE, key_lens=
                              workspace.numel() * workspace.element_size(), _dtype_code(q),
                              _stream(stream)))
     return dq, dk, dv
+
+
+def sdpa_block_workspace_size(B, S, model):
+    return int(load_library().sdpa_block_workspace_size(B, S, model))
+
+
+def sdpa_block_forward(x, wq, wk, wv, wo, heads, scale=None, mask_kind=MASK_NONE, key_lens=None,
+                       y=None, workspace=None, stream=None):
+    """The multi-head attention block: heads^-1(sdpa(heads(x.wq), heads(x.wk), heads(x.wv))).wo.
+
+    x [B, S, model]; weights [model, model]; scale defaults to 1/sqrt(model/heads).
+    """
+    _check_tensor("x", x, 3)
+    for name, w in (("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo)):
+        _check_tensor(name, w, 2)
+        if tuple(w.shape) != (x.shape[2], x.shape[2]) or w.dtype != x.dtype:
+            raise ValueError("%s must be [model, model] in x's dtype" % name)
+    if key_lens is not None:
+        _check_tensor("key_lens", key_lens, 1)
+        if key_lens.dtype != torch.int32:
+            raise TypeError("key_lens must be int32")
+    B, S, M = x.shape
+    if scale is None:
+        scale = 1.0 / (M // heads) ** 0.5
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _check_tensor("y", y, 3)
+        if y.shape != x.shape or y.dtype != x.dtype:
+            raise ValueError("y must match x in shape and dtype")
+    need = sdpa_block_workspace_size(B, S, M)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    lib = load_library()
+    _check(lib.sdpa_block_forward(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), B, S, M, heads,
+                                  float(scale), int(mask_kind), _ptr(key_lens), _ptr(y),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _dtype_code(x), _stream(stream)))
+    return y
 
 
 def sdpa_decode_workspace_size(B, Hq, D, num_splits):

@@ -90,6 +90,19 @@ def draw_bias(shape, dtype, seed, device="cpu"):
     return t.to(dtype) if dtype != torch.float32 else t
 
 
+def draw_block(B, S, model, dtype, seed, device="cpu"):
+    """Attention block inputs: x [B, S, model] i.i.d. N(0, 1) and four weights
+    wq, wk, wv, wo [model, model] i.i.d. N(0, 1 / model) (so the projections
+    keep unit variance), drawn in that order and rounded to dtype."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 49979687)
+    out = [torch.randn((B, S, model), generator=gen, device=device, dtype=torch.float32)]
+    for _ in range(4):
+        out.append(torch.randn((model, model), generator=gen, device=device, dtype=torch.float32)
+                   / math.sqrt(model))
+    return tuple(t.to(dtype) if dtype != torch.float32 else t for t in out)
+
+
 def draw_key_lens(B, lo, hi, seed, device="cpu"):
     """Per-batch valid key lengths, uniform integers in [lo, hi] (int32)."""
     gen = torch.Generator(device="cpu")

@@ -204,6 +204,39 @@ sdpa_status_t sdpa_backward_atomic(const void *q, const void *k, const void *v, 
                                    void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
 /*
+ * Bytes of device workspace sdpa_block_forward needs (0 if the sizes are
+ * invalid): q, k, v and the attention output, each [B, heads, S, model/heads]
+ * in the input dtype, 256-byte aligned.
+ */
+size_t sdpa_block_workspace_size(int64_t B, int64_t S, int64_t model);
+
+/*
+ * The multi-head attention block of the tensai guide ("Attention の組み立て"):
+ *   q, k, v = heads(x . wq), heads(x . wk), heads(x . wv)
+ *   y       = heads^-1(softmax(q k^T * scale + mask) v) . wo
+ * where heads reshapes (batch, seq, model) to (batch, seq, head, headDim)
+ * and swaps seq and head, and heads^-1 undoes it.
+ *   x              device [B, S, model], dtype
+ *   wq, wk, wv, wo device [model, model], dtype (x is multiplied on the left)
+ *   heads          model % heads == 0; headDim = model / heads
+ *   scale, mask_kind, key_lens   as in sdpa_forward (with Sq = Sk = S)
+ *   y              device [B, S, model], dtype; written completely
+ *   workspace      device buffer of at least sdpa_block_workspace_size bytes
+ * Three kernels are enqueued: the q, k, v projections in one launch (written
+ * straight into head layout), the attention, and the output projection
+ * (reading the attention output from head layout).  Products accumulate in
+ * fp32; q, k, v, the attention output and y are rounded to dtype.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, headDim a multiple of 8 up to 128,
+ * x and each weight under 2 GiB.  y and the workspace must not overlap each
+ * other or any input.
+ */
+sdpa_status_t sdpa_block_forward(const void *x, const void *wq, const void *wk, const void *wv,
+                                 const void *wo, int64_t B, int64_t S, int64_t model,
+                                 int64_t heads, float scale, int mask_kind,
+                                 const int32_t *key_lens, void *y, void *workspace,
+                                 size_t workspace_bytes, int dtype, void *stream);
+
+/*
  * Bytes of device workspace sdpa_decode needs for these sizes (0 if the sizes
  * are invalid).  Layout, fp32, 256-byte aligned sections:
  *   o_part [B, Hq, num_splits, D]  normalised partial outputs

@@ -362,6 +362,38 @@ def block_forward(x, wq, wk, wv, wo, n_heads, scale=None, mask_kind=MASK_NONE, k
     return merge_heads(o) @ wo
 
 
+def block_forward_rows(x, wq, wk, wv, wo, n_heads, rows, scale=None, mask_kind=MASK_NONE,
+                       key_lens=None):
+    """Selected rows of block_forward: rows is an int array [n, 2] of (b, s).
+
+    Same definition as block_forward, with the projections computed only for
+    the batches that hold a listed row and the attention only for the listed
+    query positions (sdpa_forward_rows), so that it scales to full-size
+    workloads.  Returns y [n, model] in fp64, in the order of rows.
+    """
+    B, S, M = x.shape
+    if M % n_heads != 0:
+        raise ValueError("model width must be a multiple of the head count")
+    if scale is None:
+        scale = 1.0 / np.sqrt(M // n_heads)
+    wq, wk, wv, wo = (np.asarray(w, dtype=np.float64) for w in (wq, wk, wv, wo))
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    y = np.empty((rows.shape[0], M), dtype=np.float64)
+    for b in np.unique(rows[:, 0]):
+        sel = np.nonzero(rows[:, 0] == b)[0]
+        xb = np.asarray(x[b:b + 1], dtype=np.float64)
+        q = split_heads(xb @ wq, n_heads)
+        k = split_heads(xb @ wk, n_heads)
+        v = split_heads(xb @ wv, n_heads)
+        index = np.array([(0, h, rows[n, 1]) for n in sel for h in range(n_heads)])
+        lens = None if key_lens is None else np.asarray(key_lens)[b:b + 1]
+        o, _ = sdpa_forward_rows(q, k, v, scale, mask_kind, lens, index)
+        # o holds, per listed row, its heads in order: concatenated they are
+        # the merged (seq, model) row
+        y[sel] = o.reshape(sel.size, M) @ wo
+    return y
+
+
 def paged_gather(cache, table_row, length, page_size):
     """Logical rows 0..length-1 of one sequence read through its page table.
 
@@ -435,5 +467,5 @@ __all__ = [
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
     "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
     "chunk_positions", "sdpa_backward", "bias_slice", "split_heads", "merge_heads",
-    "block_forward",
+    "block_forward", "block_forward_rows",
 ]

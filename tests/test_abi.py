@@ -327,3 +327,45 @@ def test_backward_atomic_workspace_and_rejects():
                                   ctypes.c_void_p(1 << 45), ctypes.c_void_p(1 << 46),
                                   ctypes.c_void_p(1 << 47), 1 << 40, sd.SDPA_BF16, None)
     assert st == sd.SDPA_ERR_UNSUPPORTED
+
+
+def block(x=FAKE, wq=FAKE_K, wk=FAKE_V, wv=FAKE_O, wo=FAKE_W, B=2, S=128, model=512, heads=8,
+          scale=0.125, mask=0, key_lens=None, y=ctypes.c_void_p(0x78000000),
+          ws=ctypes.c_void_p(0x7c000000), ws_bytes=1 << 20, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    return lib.sdpa_block_forward(x, wq, wk, wv, wo, B, S, model, heads, scale, mask, key_lens, y,
+                                  ws, ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(wo=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(B=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(heads=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(dtype=9), sd.SDPA_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(model=500), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(model=1088), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 136 wide
+    (dict(model=168, heads=2), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 84 wide
+    (dict(scale=float("nan")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(mask=4), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),
+    (dict(mask=sd.MASK_KEY_PADDING), sd.SDPA_ERR_INVALID_ARGUMENT, "key_lens"),
+    (dict(S=1 << 20, model=2048, heads=16), sd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(ws_bytes=(1 << 20) - 1), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(y=ctypes.c_void_p(0x10000 + 4096)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(ws=ctypes.c_void_p(0x6ff80000)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap"),   # reaches wo
+    (dict(y=ctypes.c_void_p(0x7c000000 + 512)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap"),
+])
+def test_block_rejects(kw, status, needle):
+    assert block(**kw) == status
+    assert needle in sd.last_error()
+
+
+def test_block_workspace_size():
+    lib = sd.load_library()
+    # q, k, v and the attention output, each B*S*model 16-bit values
+    assert lib.sdpa_block_workspace_size(2, 128, 512) == 4 * 2 * 128 * 512 * 2 == 1 << 20
+    assert lib.sdpa_block_workspace_size(1, 3, 8) == 4 * 256
+    assert lib.sdpa_block_workspace_size(0, 3, 8) == 0
+    assert lib.sdpa_block_workspace_size(1, 3, -8) == 0

@@ -778,3 +778,18 @@ def test_block_split_merge_heads_roundtrip():
     assert h.shape == (2, 4, 3, 3)
     assert h[1, 2, 0, 1] == t[1, 0, 2 * 3 + 1]      # (b, head, seq, d) <- (b, seq, head*hd + d)
     np.testing.assert_array_equal(O.merge_heads(h), t)
+
+
+def test_block_rows_equal_full():
+    # the row-sampled block is the full block at the listed (b, s), under
+    # every mask, including a batch whose keys are all padded away (NaN rows)
+    x, (wq, wk, wv, wo), _ = _block_inputs(94, B=3, S=7, M=12)
+    lens = np.array([7, 3, 0])
+    rows = np.array([[0, 0], [2, 6], [1, 2], [1, 5], [0, 6], [2, 0]])
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL, O.MASK_KEY_PADDING, 3):
+        kl = lens if mask & O.MASK_KEY_PADDING else None
+        full = O.block_forward(x, wq, wk, wv, wo, 3, 0.4, mask, kl)
+        got = O.block_forward_rows(x, wq, wk, wv, wo, 3, rows, 0.4, mask, kl)
+        np.testing.assert_allclose(got, full[rows[:, 0], rows[:, 1]], rtol=0, atol=1e-13)
+        if kl is not None:
+            assert np.isnan(got[rows[:, 0] == 2]).all()
