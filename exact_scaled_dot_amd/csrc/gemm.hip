@@ -8,12 +8,18 @@
 // (the q, k and v projections in one launch).
 //
 // Tiles: a workgroup of 4 waves owns C rows m0 .. m0+255 and columns
-// n0 .. n0+127; wave w owns rows m0 + 64w .. +63.  The kernel computes the
-// transposed tile C^T = B^T A^T with v_mfma_f32_32x32x16 so that each lane's
-// accumulator holds 4 consecutive columns of one row (8-byte stores, and the
-// 4 columns stay inside one head).  A and B tiles of depth 32 reach LDS by
-// buffer-load DMA into two stages; MFMA A operands (B^T) are transposed LDS
-// reads of the B tile, B operands (A^T) are row reads of the A tile.
+// n0 .. n0+255; wave w owns the 128 x 128 quarter (rows + 128 (w % 2),
+// columns + 128 (w / 2)), 256 accumulator registers, one wave per SIMD.  The
+// kernel computes the transposed tile C^T = B^T A^T with v_mfma_f32_32x32x16
+// so that each lane's accumulator holds 4 consecutive columns of one row
+// (8-byte stores, and the 4 columns stay inside one head).  A and B tiles of
+// depth 32 reach LDS by buffer-load DMA into a ring of four stages (32 KB
+// each), each load issued between the MFMAs of the stage three before its
+// use, so it has over two stages of MFMA work to land; MFMA A operands (B^T)
+// are transposed LDS reads of the B tile,
+// B operands (A^T) are row reads of the A tile.  Per 16-deep step a wave
+// reads 8 KB of LDS for 16 MFMAs, so operand reads plus the DMA writes stay
+// under the LDS bandwidth while the matrix cores run.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -22,8 +28,9 @@ namespace {
 
 constexpr int kGThreads = 256;
 constexpr int kTM = 256;  // C rows per workgroup
-constexpr int kTN = 128;  // C columns per workgroup
+constexpr int kTN = 256;  // C columns per workgroup
 constexpr int kTK = 32;   // contraction per stage
+constexpr int kStages = 4;  // LDS ring depth
 constexpr uint32_t kFar = 0x80000000u;  // a buffer offset past any num_records (<= INT_MAX)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -47,35 +54,45 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void* lds, uint32_
         r, (lds_void*)((__attribute__((address_space(3))) char*)lds), 16, voff, 0, 0, 0);
 }
 
-// Element offset of (row m, column c) of a [M x width] matrix stored either
-// row-major (heads = false) or, for m = b*S + s and c = h*hd + d, in
-// (batch, head, seq, headDim) layout.
-__device__ __forceinline__ int64_t mat_off(int m, int c, int width, bool heads, int S, int hd) {
-    if (!heads) return (int64_t)m * width + c;
-    const int b = m / S, s = m - b * S, h = c / hd, d = c - h * hd;
-    const int H = width / hd;
-    return (((int64_t)b * H + h) * S + s) * hd + d;
-}
-
 // LDS swizzles (16-byte chunk c of tile row r stored at c ^ f(r)):
 //   A tile, rows of 32 elements (4 chunks, 4 rows per 256-byte bank window):
 //     fa(r) = (r / 4) % 4 — a row read (one chunk of 16 consecutive rows)
 //     hits 16 distinct bank groups.
-//   B tile, rows of 128 elements (16 chunks, one bank window):
-//     fb(r) = 4 * (r % 4) — a transposed read (4 consecutive rows x 4 chunks
-//     per 32 lanes) hits 16 distinct bank groups.
+//   B tile, rows of 256 elements (32 chunks, two bank windows):
+//     fb(r) = 4 * (r % 4) — a transposed read (4 consecutive rows x 4 aligned
+//     chunks per 16 lanes) hits 16 distinct bank groups.
+// Workgroup barrier for LDS hand-over only.  __syncthreads() would also
+// fence global memory, which waits for every buffer load in flight (the DMA
+// stages issued ahead included) and so undoes the prefetch; the waves' own
+// vmcnt waits before the barrier cover the DMA that the next stage reads.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ int fa(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int fb(int r) { return 4 * (r & 3); }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <class T, bool AH, bool CH>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
-    constexpr int A_EL = kTM * kTK;   // 8192 elements
-    constexpr int B_EL = kTK * kTN;   // 4096
+__global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
+    constexpr int NST = kStages;
+    constexpr int CPR = kTK / 8;       // 16-byte chunks per A tile row
+    constexpr int LPT = kTK / 8;       // DMA loads per wave per tile (A and B alike)
+    constexpr int A_EL = kTM * kTK;    // 8192 elements
+    constexpr int B_EL = kTK * kTN;    // 8192
     constexpr int STAGE = A_EL + B_EL;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    static_assert(NST * STAGE * 2 <= 160 * 1024, "LDS ring exceeds 160 KB");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NST * STAGE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hg = lane >> 5;
@@ -97,52 +114,65 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t ra = rsrc(g.a, g.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = rsrc(bsrc, (uint32_t)g.K * g.N * 2);
 
-    // DMA slots of this wave: A tile 1024 slots (4 loads), B tile 512 (2 loads).
-    // A slot s: tile row s/4, stored chunk s%4; B slot s: tile row s/16, stored chunk s%16.
-    int a_row[4], a_chk[4], b_row[2], b_chk[2];
+    // DMA slots of this wave: LPT loads per tile.
+    // A slot s: tile row s/CPR, stored chunk s%CPR; B slot s: tile row s/32, stored chunk s%32.
+    // Byte offsets are 32-bit (every operand is under 2 GiB): a per-slot base
+    // set once (kFar for a row or column past the matrix, which keeps any sum
+    // below 2^32 and past num_records, so the load returns zeros) plus the
+    // part that moves with k.
+    const float inv_hd = 1.0f / (float)g.hd;
+    uint32_t a_base[LPT], b_base[LPT];
+    int a_kx[LPT], b_row[LPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s = 64 * (4 * wave + i) + lane;
-        a_row[i] = s >> 2;
-        a_chk[i] = (s & 3) ^ fa(s >> 2);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int s = 64 * (2 * wave + i) + lane;
-        b_row[i] = s >> 4;
-        b_chk[i] = (s & 15) ^ fb(s >> 4);
+    for (int i = 0; i < LPT; ++i) {
+        const int s = 64 * (LPT * wave + i) + lane;
+        const int ar = s / CPR, m = m0 + ar;
+        a_kx[i] = 8 * ((s % CPR) ^ fa(ar));
+        if (AH) {
+            const int b = m / g.S, sq = m - b * g.S;
+            a_base[i] = m < g.M ? 2u * (uint32_t)(b * g.S * g.K + sq * g.hd) : kFar;
+        } else {
+            a_base[i] = m < g.M ? 2u * (uint32_t)m * (uint32_t)g.K : kFar;
+        }
+        const int br = s >> 5, n = n0 + 8 * ((s & 31) ^ fb(br));
+        b_row[i] = br;
+        b_base[i] = n < g.N ? 2u * (uint32_t)n : kFar;
     }
     auto issue = [&](int k0, int stage) {
-        uint16_t* sa = smem + stage * STAGE + 512 * 4 * wave;
-        uint16_t* sb = smem + stage * STAGE + A_EL + 512 * 2 * wave;
+        uint16_t* sa = smem + stage * STAGE + 512 * LPT * wave;
+        uint16_t* sb = smem + stage * STAGE + A_EL + 512 * LPT * wave;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + a_row[i], k = k0 + 8 * a_chk[i];
-            const uint32_t off = (m < g.M && k < g.K)
-                                     ? (uint32_t)(mat_off(m, k, g.K, AH, g.S, g.hd) * 2)
-                                     : kFar;
-            dma(ra, sa + 512 * i, off);
+        for (int i = 0; i < LPT; ++i) {
+            const int k = k0 + a_kx[i];
+            uint32_t part = 2u * (uint32_t)k;
+            if (AH) {
+                // head h = k / hd by a float reciprocal: k < 2^16 and hd <= 128
+                // keep (k + 1/2) / hd at least 2^-16 (relative) from an integer,
+                // far above the product's rounding error
+                const int h = (int)(((float)k + 0.5f) * inv_hd);
+                part = 2u * ((uint32_t)h * (uint32_t)(g.S * g.hd) + (uint32_t)(k - h * g.hd));
+            }
+            // k past K: bit 31 set (the sum stays below 2^32), so the load
+            // reads zeros; an OR rather than a select keeps the loop body one
+            // basic block for the schedule below
+            dma(ra, sa + 512 * i, (a_base[i] + part) | (k < g.K ? 0u : kFar));
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int k = k0 + b_row[i], n = n0 + 8 * b_chk[i];
-            const uint32_t off = (k < g.K && n < g.N) ? (uint32_t)(((int64_t)k * g.N + n) * 2) : kFar;
-            dma(rb, sb + 512 * i, off);
+        for (int i = 0; i < LPT; ++i) {
+            const int k = k0 + b_row[i];
+            dma(rb, sb + 512 * i, (b_base[i] + 2u * (uint32_t)k * (uint32_t)g.N) | (k < g.K ? 0u : kFar));
         }
     };
 
     // LDS read offsets (elements within a stage).
-    // A^T operand of block mb: tile row 64*wave + 32*mb + l32, logical chunk 2t + hg.
-    int ard[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int r = 64 * wave + 32 * mb + l32;
-            ard[mb][k] = r * kTK + (((2 * k + hg) ^ fa(r)) * 8);
-        }
+    // A^T operand of block mb, step kk: tile row 128wm + 32mb + l32, logical
+    // chunk 2kk + hg; fa of that row equals fa(l32) (128wm + 32mb is a
+    // multiple of 16), so one swizzle register serves every mb.
+    const int ard0 = (128 * wm + l32) * kTK;
+    const int afx0 = hg ^ fa(l32);
     // B^T operand of block nb: lane j of 16-lane group g16 points at tile row
-    // 16t + 8hg + j/4 (+4 for the second read), columns 32nb + 16(g16&1) + 4(j%4).
+    // 16kk + 8hg + j/4 (+4 for the second read), columns 128wn + 32nb +
+    // 16(g16&1) + 4(j%4); the swizzle depends on the row only through j/4.
     const int g16 = lane >> 4, j16 = lane & 15;
     int brd[4][2];
 #pragma unroll
@@ -150,66 +180,120 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = 8 * hg + (j16 >> 2) + 4 * h;
-            const int col = 32 * nb + 16 * (g16 & 1) + 4 * (j16 & 3);
+            const int col = 128 * wn + 32 * nb + 16 * (g16 & 1) + 4 * (j16 & 3);
             brd[nb][h] = A_EL + r * kTN + (((col >> 3) ^ fb(r)) * 8) + (col & 7);
         }
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
 
     auto compute = [&](const uint16_t* st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {  // 16-deep MFMA steps
-            u32x4 af[2], bf[4];
+        for (int kk = 0; kk < 2; ++kk) {  // 16-deep MFMA steps
+            u32x4 af[4], bf[4];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) af[mb] = lds_row(st + ard[mb][k]);
+            for (int mb = 0; mb < 4; ++mb) af[mb] = lds_row(st + ard0 + 32 * mb * kTK + ((2 * kk) ^ afx0) * 8);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const u32x2 lo = lds_tr(st + brd[nb][0] + 16 * k * kTN);
-                const u32x2 hi = lds_tr(st + brd[nb][1] + 16 * k * kTN);
+                const u32x2 lo = lds_tr(st + brd[nb][0] + 16 * kk * kTN);
+                const u32x2 hi = lds_tr(st + brd[nb][1] + 16 * kk * kTN);
                 bf[nb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < 4; ++mb)
                     acc[nb][mb] = mfma_32x32x16<T>(bf[nb], af[mb], acc[nb][mb]);
         }
     };
 
+    // Ring of four buffers: stage kt lives in buffer kt % 4.  Iteration kt
+    // waits for its own loads of stage kt (the loads of kt + 1 and kt + 2, 8
+    // per stage, may stay in flight), meets the other waves at the barrier
+    // (their loads have landed too, and every wave is done reading buffer
+    // (kt - 1) % 4), computes, and refills buffer (kt - 1) % 4 with stage
+    // kt + 3.  Every iteration refills (with zeros once past K), so the wait
+    // count is the same in each.  The refill comes after the LDS reads in
+    // program order: the compiler cannot tell the ring buffers apart, and
+    // this order lets the loads go between the MFMAs of the second 16-deep
+    // step instead of ahead of every read.  The schedule below asks for: the
+    // first step's 12 reads, its 16 MFMAs two at a time with the second
+    // step's 12 reads between them, then the second step's 16 MFMAs two at a
+    // time with one load after each pair (a burst of loads at the top of the
+    // stage stalls the wave's MFMA issue).
     const int nk = (g.K + kTK - 1) / kTK;
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    auto step = [&](int kt, const int cur) __attribute__((always_inline)) {
-        if (kt + 1 < nk) issue((kt + 1) * kTK, cur ^ 1);
-        compute(smem + cur * STAGE);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, 0);
-        if (kt + 1 < nk) step(kt + 1, 1);
-    }
-
-    // acc[nb][mb] register r: column n0 + 32nb + 8(r/4) + 4hg + r%4 of row
-    // m0 + 64w + 32mb + l32; four consecutive columns per 8-byte store.
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + 64 * wave + 32 * mb + l32;
+    for (int p = 0; p < NST - 1; ++p) issue(p * kTK, p);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<2 * LPT * (NST - 2)>();
+        lds_barrier();
+        compute(smem + (kt % NST) * STAGE);
+        issue((kt + NST - 1) * kTK, (kt + NST - 1) % NST);
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+    }
+    wait_vmcnt<0>();  // no LDS DMA may land after the workgroup ends
+
+    // acc[nb][mb] register r: column n0 + 128wn + 32nb + 8(r/4) + 4hg + r%4 of
+    // row m0 + 128wm + 32mb + l32; four consecutive columns per 8-byte store.
+    // Element offset = row part + column part (both int: C is under 2 GiB).
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int m = m0 + 128 * wm + 32 * mb + l32;
         if (m >= g.M) continue;
+        int rp = m * g.N;
+        if (CH) {
+            const int b = m / g.S, sq = m - b * g.S;
+            rp = b * g.S * g.N + sq * g.hd;
+        }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int n = n0 + 32 * nb + 8 * r4 + 4 * hg;
+                const int n = n0 + 128 * wn + 32 * nb + 8 * r4 + 4 * hg;
                 if (n >= g.N) continue;
+                int cp = n;
+                if (CH) {
+                    const int h = n / g.hd;
+                    cp = h * g.S * g.hd + (n - h * g.hd);
+                }
                 const f32x16& x = acc[nb][mb];
                 const u32x2 w = {pack2<T>(x[4 * r4], x[4 * r4 + 1]), pack2<T>(x[4 * r4 + 2], x[4 * r4 + 3])};
-                *reinterpret_cast<u32x2*>(cdst + mat_off(m, n, g.N, CH, g.S, g.hd)) = w;
+                *reinterpret_cast<u32x2*>(cdst + rp + cp) = w;
             }
     }
 }
