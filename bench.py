@@ -15,6 +15,10 @@ resident in HBM:
     with the ordered reduction and with the atomic-dQ one
   * the causal prefill with a general additive mask: a per-head bias tensor
     [1, 16, 4096, 4096] bf16 added to the scaled scores
+  * the multi-head attention block (q/k/v projections, causal attention,
+    output projection) at the tensai guide's shape (batch 8, 128 tokens,
+    model 256, 4 heads) and at the prefill's (batch 4, 4096 tokens, model
+    2048, 16 heads of 128)
 Each call is bracketed by HIP events on the stream it is launched on (torch's
 current stream, which is the stream the binding hands to the library).
 
@@ -48,6 +52,8 @@ PREFILL = "bf16_causal_b4_h16_s4096_d128"
 PADDED = "bf16_gqa32x8_padded_b2_s8192_d128"
 DECODE = "bf16_gqa32x8_decode_b64_sk32768_d128"
 PAGE_SIZE = 16                      # paged decode: keys per cache page
+# attention blocks: (batch, tokens, model width, heads)
+BLOCKS = {"block": (4, 4096, 2048, 16), "block_small": (8, 128, 256, 4)}
 
 
 def kernel_source_hash(name):
@@ -79,6 +85,18 @@ def atomic_traffic():
     parts = [stored_traffic(k, "backward.hip")
              for k in ("backward_atomic_prep", "backward_atomic_dkdv", "backward_atomic_convert")]
     return None if None in parts else sum(parts)
+
+
+def block_traffic(tag):
+    """HBM bytes of one attention-block call (its three kernels), if valid."""
+    parts = [stored_traffic(tag + "_qkv", "gemm.hip"), stored_traffic(tag + "_attn", "forward.hip"),
+             stored_traffic(tag + "_out", "gemm.hip")]
+    return None if None in parts else sum(parts)
+
+
+def block_flops(B, S, M, H, causal):
+    """Four [B*S, M] x [M, M] projections plus the attention formula."""
+    return 8.0 * B * S * M * M + formula_flops(B, H, S, S, M // H, causal)
 
 
 def formula_flops(B, Hq, Sq, Sk, D, causal):
@@ -152,16 +170,27 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
                 "hbm_bytes_per_launch": round(r + w)}
 
     fwd = "forward_bf16_kernel"
-    if fwd in fetch:  # a full step launches the causal prefill, the padded one, the paged one
-        # (after one setup forward that gives the backward its output and lse)
-        # (a step: causal prefill, padded prefill, paged prefill, bias prefill)
+    if fwd in fetch:
+        # a full step launches, in order: the causal prefill, the padded one,
+        # the paged one, the bias prefill, the large block's attention and the
+        # small block's (after one setup forward that gives the backward its
+        # output and lse)
         fr, wr = fetch[fwd], write[fwd]
-        if len(fr) % 4 == 1:
+        if len(fr) % 6 == 1:
             fr, wr = fr[1:], wr[1:]
-        out["prefill"] = entry(fwd, "forward.hip", fr[0::4], wr[0::4])
-        out["padded"] = entry(fwd, "forward.hip", fr[1::4], wr[1::4])
-        out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::4], wr[2::4])
-        out["bias"] = entry(fwd, "forward.hip", fr[3::4], wr[3::4])
+        out["prefill"] = entry(fwd, "forward.hip", fr[0::6], wr[0::6])
+        out["padded"] = entry(fwd, "forward.hip", fr[1::6], wr[1::6])
+        out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::6], wr[2::6])
+        out["bias"] = entry(fwd, "forward.hip", fr[3::6], wr[3::6])
+        out["block_attn"] = entry(fwd, "forward.hip", fr[4::6], wr[4::6])
+        out["block_small_attn"] = entry(fwd, "forward.hip", fr[5::6], wr[5::6])
+    # each block call: q/k/v projection GEMM, attention, output projection
+    # GEMM; a step runs the large block, then the small one (names are
+    # truncated, so the four GEMM dispatches of a step are told apart by order)
+    gm = "gemm_kernel"
+    if gm in fetch:
+        for i, key in enumerate(("block_qkv", "block_out", "block_small_qkv", "block_small_out")):
+            out[key] = entry(gm, "gemm.hip", fetch[gm][i::4], write[gm][i::4])
     if "bwd_dq_kernel" in fetch:
         out["backward_dq"] = entry("bwd_dq_kernel", "backward.hip", fetch["bwd_dq_kernel"],
                                    write["bwd_dq_kernel"])
@@ -195,7 +224,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward", "backward_atomic", "bias"],
+                                       "backward", "backward_atomic", "bias", "block",
+                                       "block_small"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,8 +250,8 @@ def main():
     import torch
 
     import exact_scaled_dot_amd as sd
-    from exact_scaled_dot_amd.workloads import (WORKLOADS, draw_bias, draw_grad, draw_paged,
-                                                 make_inputs)
+    from exact_scaled_dot_amd.workloads import (WORKLOADS, draw_bias, draw_block, draw_grad,
+                                                 draw_paged, make_inputs)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -270,6 +300,15 @@ def main():
     if args.only in (None, "bias"):
         ibias = {"bias": draw_bias((1, wp.Hq, wp.Sq, wp.Sk), wp.dtype, wp.seed, dev),
                  "out": torch.empty_like(ip["q"])}
+    # Attention blocks: x and four weights per shape (N(0,1) activations,
+    # N(0, 1/model) weights), the output and the workspace allocated here.
+    iblk = {}
+    for name, (B, S, M, H) in BLOCKS.items():
+        if args.only in (None, name):
+            ins = draw_block(B, S, M, wp.dtype, wp.seed + 17, dev)
+            iblk[name] = {"ins": ins, "y": torch.empty_like(ins[0]), "H": H,
+                          "ws": torch.empty(sd.sdpa_block_workspace_size(B, S, M),
+                                            dtype=torch.uint8, device=dev)}
     torch.cuda.synchronize()
 
     calls = {
@@ -296,9 +335,12 @@ def main():
         None, ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"], atomic=True)
     calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
                                                  sd.MASK_CAUSAL, None, ibias["out"])
+    for name in iblk:
+        calls[name] = (lambda blk: lambda: sd.sdpa_block_forward(
+            *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "bias"])
+              "bias", "block", "block_small"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -439,8 +481,27 @@ def main():
                                     "traffic": stored_traffic("bias", "forward.hip"),
                                     "kernel": "forward_bf16_kernel<128, bias>",
                                     "flops_per_launch": fl}}
+    for name, (B, S, M, H) in BLOCKS.items():
+        if name not in ms:
+            continue
+        fl = block_flops(B, S, M, H, True)
+        tf = fl / (ms[name] * 1e-3) / 1e12
+        rec[name] = {"workload": "bf16_causal_block_b%d_s%d_m%d_h%d" % (B, S, M, H),
+                     "ms": round(ms[name], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                     "flops": "8*B*S*model^2 (four projections) + the causal attention formula",
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                  "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "traffic": block_traffic(name),
+                                  "kernel": "gemm_kernel<q/k/v> + forward_bf16_kernel + "
+                                            "gemm_kernel<out>",
+                                  "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
-        if "bias" in rec:
+        blk = [n for n in BLOCKS if n in rec]
+        if blk:
+            rec.update({"value": rec[blk[0]]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec[blk[0]]["workload"]}
+        elif "bias" in rec:
             rec.update({"value": rec["bias"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["bias"]["workload"]}
         elif "backward_atomic" in rec:
@@ -462,7 +523,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw, ibias
+    del ip, ig, idd, ipg, ipp, ibw, ibias, iblk
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

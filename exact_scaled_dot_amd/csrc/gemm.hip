@@ -190,81 +190,86 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
 
-    auto compute = [&](const uint16_t* st) __attribute__((always_inline)) {
+    auto read_frags = [&](const uint16_t* st, int kk, u32x4 (&af)[4], u32x4 (&bf)[4])
+                          __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {  // 16-deep MFMA steps
-            u32x4 af[4], bf[4];
+        for (int mb = 0; mb < 4; ++mb) af[mb] = lds_row(st + ard0 + 32 * mb * kTK + ((2 * kk) ^ afx0) * 8);
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) af[mb] = lds_row(st + ard0 + 32 * mb * kTK + ((2 * kk) ^ afx0) * 8);
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const u32x2 lo = lds_tr(st + brd[nb][0] + 16 * kk * kTN);
-                const u32x2 hi = lds_tr(st + brd[nb][1] + 16 * kk * kTN);
-                bf[nb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc[nb][mb] = mfma_32x32x16<T>(bf[nb], af[mb], acc[nb][mb]);
+        for (int nb = 0; nb < 4; ++nb) {
+            const u32x2 lo = lds_tr(st + brd[nb][0] + 16 * kk * kTN);
+            const u32x2 hi = lds_tr(st + brd[nb][1] + 16 * kk * kTN);
+            bf[nb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
     };
+    auto mfmas = [&](const u32x4 (&af)[4], const u32x4 (&bf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_32x32x16<T>(bf[nb], af[mb], acc[nb][mb]);
+    };
 
-    // Ring of four buffers: stage kt lives in buffer kt % 4.  Iteration kt
-    // waits for its own loads of stage kt (the loads of kt + 1 and kt + 2, 8
-    // per stage, may stay in flight), meets the other waves at the barrier
-    // (their loads have landed too, and every wave is done reading buffer
-    // (kt - 1) % 4), computes, and refills buffer (kt - 1) % 4 with stage
-    // kt + 3.  Every iteration refills (with zeros once past K), so the wait
-    // count is the same in each.  The refill comes after the LDS reads in
-    // program order: the compiler cannot tell the ring buffers apart, and
-    // this order lets the loads go between the MFMAs of the second 16-deep
-    // step instead of ahead of every read.  The schedule below asks for: the
-    // first step's 12 reads, its 16 MFMAs two at a time with the second
-    // step's 12 reads between them, then the second step's 16 MFMAs two at a
-    // time with one load after each pair (a burst of loads at the top of the
-    // stage stalls the wave's MFMA issue).
+    // Ring of four buffers: stage kt lives in buffer kt % 4; the prologue
+    // fills all four.  Iteration kt runs stage kt's first 16-deep step (its
+    // fragments were read at the end of the previous iteration) while reading
+    // the second step's; then waits for its own loads of stage kt + 1 (those
+    // of kt + 2 and kt + 3, 8 per stage, may stay in flight) and meets the
+    // other waves at an LDS-only barrier: stage kt + 1 has landed for every
+    // wave, and every wave is done reading buffer kt % 4.  The second step's
+    // MFMAs then run next to the reads of stage kt + 1's first step and the
+    // refill of buffer kt % 4 with stage kt + 4.  Every iteration refills
+    // (with zeros once past K), so the wait counts never change.  The
+    // refill follows the reads in program order because the compiler cannot
+    // tell the ring buffers apart; the schedule puts two MFMAs between
+    // consecutive groups of reads or loads (a burst of loads stalls the
+    // wave's MFMA issue, a read right before its MFMA exposes its latency).
     const int nk = (g.K + kTK - 1) / kTK;
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p) issue(p * kTK, p);
+    for (int p = 0; p < NST; ++p) issue(p * kTK, p);
+    wait_vmcnt<2 * LPT * (NST - 1)>();
+    lds_barrier();
+    u32x4 a0[4], b0[4], a1[4], b1[4];
+    read_frags(smem, 0, a0, b0);
     for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t* st = smem + (kt % NST) * STAGE;
+        mfmas(a0, b0);
+        read_frags(st, 1, a1, b1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         wait_vmcnt<2 * LPT * (NST - 2)>();
         lds_barrier();
-        compute(smem + (kt % NST) * STAGE);
-        issue((kt + NST - 1) * kTK, (kt + NST - 1) % NST);
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        mfmas(a1, b1);
+        read_frags(smem + ((kt + 1) % NST) * STAGE, 0, a0, b0);
+        issue((kt + NST) * kTK, kt % NST);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
     }
     wait_vmcnt<0>();  // no LDS DMA may land after the workgroup ends
 
