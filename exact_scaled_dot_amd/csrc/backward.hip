@@ -541,15 +541,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     // role P, Q for role dS), B = the block's 16-bit weights w (word 4*kk + i
     // holds registers 8*kk + 2*i, +1).
     auto grads = [&](const uint16_t* xs, int qb, const uint32_t* w) __attribute__((always_inline)) {
+        // all of a 16-query step's fragments are read before its MFMAs
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const u32x4 bw = {w[4 * kk], w[4 * kk + 1], w[4 * kk + 2], w[4 * kk + 3]};
             const uint16_t* xt = xs + (32 * qb + 16 * kk) * D;
+            u32x4 fa[ND];
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
                 const u32x2 lo = lds_tr(xt + off.trl[db]), hi = lds_tr(xt + off.trh[db]);
-                acc[db] = mfma_32x32x16<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, bw, acc[db]);
+                fa[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
+#pragma unroll
+            for (int db = 0; db < ND; ++db) acc[db] = mfma_32x32x16<T>(fa[db], bw, acc[db]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * ND, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, ND, 2);
         }
     };
 
@@ -683,10 +689,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA + 1) : "memory");
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA) : "memory");
     };
+    // The barriers below are LDS-only: __syncthreads() would fence global
+    // memory, i.e. wait for every load in flight, the newest stage's included,
+    // and cut the prefetch to one step.  Each wave's own wait covers what the
+    // next step reads; the barrier then covers every wave's.
     if (steps > 0) issue(0, 0);
     if (NSTG == 3 && steps > 1) issue(1, 1);
     wait_older(steps <= NSTG - 2);
-    __syncthreads();
+    lds_barrier();
     auto step = [&](int st, const int cur) __attribute__((always_inline)) {
         if (st + NSTG - 1 < steps) issue(st + NSTG - 1, (cur + NSTG - 1) % NSTG);
         const int q0 = (qt0 + st % nqt) * kBwTile;
@@ -695,7 +705,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         compute(base, base + L::TILE, reinterpret_cast<const float*>(base + 2 * L::TILE), q0, live,
                 a.causal && q0 < kw + 31, gk * G + st / nqt);
         wait_older(st + NSTG - 1 >= steps);
-        __syncthreads();
+        lds_barrier();
     };
     for (int st = 0; st < steps; st += NSTG) {
         step(st, 0);
