@@ -500,14 +500,20 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             const int kb2 = kk >> 1, half = kk & 1;
             const u32x4 pw = {pk[kb2][4 * half], pk[kb2][4 * half + 1], pk[kb2][4 * half + 2],
                               pk[kb2][4 * half + 3]};
+            // all of a 16-key slice's V^T fragments are read before its MFMAs
+            // (each pair read right before its MFMA exposed the read latency)
+            u32x4 vf[D / 32];
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 const uint16_t* vb = vs + 16 * kk * D + vrd[db];
                 const u32x2 lo = lds_read_tr16x4(vb);
                 const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
-                const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = mfma_32x32x16<T>(vf, pw, oacc[db]);
+                vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] = mfma_32x32x16<T>(vf[db], pw, oacc[db]);
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 4);
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 4);
         }
     };
 
