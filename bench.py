@@ -15,6 +15,9 @@ resident in HBM:
     with the ordered reduction and with the atomic-dQ one
   * the causal prefill with a general additive mask: a per-head bias tensor
     [1, 16, 4096, 4096] bf16 added to the scaled scores
+  * the causal prefill with 256-wide heads, bf16, B=4 Hq=Hkv=8 S=4096 D=256
+    (the same formula FLOPs as the headline; the kernel computes the output
+    in two 128-dim slices that each recompute the scores)
   * the multi-head attention block (q/k/v projections, causal attention,
     output projection) at the tensai guide's shape (batch 8, 128 tokens,
     model 256, 4 heads) and at the prefill's (batch 4, 4096 tokens, model
@@ -54,6 +57,7 @@ DECODE = "bf16_gqa32x8_decode_b64_sk32768_d128"
 PAGE_SIZE = 16                      # paged decode: keys per cache page
 # attention blocks: (batch, tokens, model width, heads)
 BLOCKS = {"block": (4, 4096, 2048, 16), "block_small": (8, 128, 256, 4)}
+WIDE = (4, 8, 4096, 256)            # wide heads: (batch, heads, tokens, head dim)
 
 
 def kernel_source_hash(name):
@@ -172,18 +176,15 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     fwd = "forward_bf16_kernel"
     if fwd in fetch:
         # a full step launches, in order: the causal prefill, the padded one,
-        # the paged one, the bias prefill, the large block's attention and the
-        # small block's (after one setup forward that gives the backward its
-        # output and lse)
+        # the paged one, the bias prefill, the wide-head prefill, the large
+        # block's attention and the small block's (after one setup forward
+        # that gives the backward its output and lse)
         fr, wr = fetch[fwd], write[fwd]
-        if len(fr) % 6 == 1:
+        if len(fr) % 7 == 1:
             fr, wr = fr[1:], wr[1:]
-        out["prefill"] = entry(fwd, "forward.hip", fr[0::6], wr[0::6])
-        out["padded"] = entry(fwd, "forward.hip", fr[1::6], wr[1::6])
-        out["paged_prefill"] = entry(fwd, "forward.hip", fr[2::6], wr[2::6])
-        out["bias"] = entry(fwd, "forward.hip", fr[3::6], wr[3::6])
-        out["block_attn"] = entry(fwd, "forward.hip", fr[4::6], wr[4::6])
-        out["block_small_attn"] = entry(fwd, "forward.hip", fr[5::6], wr[5::6])
+        for i, key in enumerate(("prefill", "padded", "paged_prefill", "bias", "wide", "block_attn",
+                                 "block_small_attn")):
+            out[key] = entry(fwd, "forward.hip", fr[i::7], wr[i::7])
     # each block call: q/k/v projection GEMM, attention, output projection
     # GEMM; a step runs the large block, then the small one (names are
     # truncated, so the four GEMM dispatches of a step are told apart by order)
@@ -224,7 +225,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward", "backward_atomic", "bias", "block",
+                                       "backward", "backward_atomic", "bias", "wide", "block",
                                        "block_small"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
@@ -251,7 +252,7 @@ def main():
 
     import exact_scaled_dot_amd as sd
     from exact_scaled_dot_amd.workloads import (WORKLOADS, draw_bias, draw_block, draw_grad,
-                                                 draw_paged, make_inputs)
+                                                 draw_paged, draw_qkv, make_inputs)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -300,6 +301,13 @@ def main():
     if args.only in (None, "bias"):
         ibias = {"bias": draw_bias((1, wp.Hq, wp.Sq, wp.Sk), wp.dtype, wp.seed, dev),
                  "out": torch.empty_like(ip["q"])}
+    # Wide heads: the causal prefill's token count and model width in 8 heads
+    # of 256.
+    iwide = None
+    if args.only in (None, "wide"):
+        iwide = dict(zip(("q", "k", "v"), draw_qkv(WIDE[0], WIDE[1], WIDE[1], WIDE[2], WIDE[2],
+                                                   WIDE[3], wp.dtype, wp.seed + 31, dev)))
+        iwide["out"] = torch.empty_like(iwide["q"])
     # Attention blocks: x and four weights per shape (N(0,1) activations,
     # N(0, 1/model) weights), the output and the workspace allocated here.
     iblk = {}
@@ -335,12 +343,15 @@ def main():
         None, ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"], atomic=True)
     calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
                                                  sd.MASK_CAUSAL, None, ibias["out"])
+    calls["wide"] = lambda: sd.sdpa_forward(iwide["q"], iwide["k"], iwide["v"],
+                                            1.0 / math.sqrt(WIDE[3]), sd.MASK_CAUSAL, None,
+                                            iwide["out"])
     for name in iblk:
         calls[name] = (lambda blk: lambda: sd.sdpa_block_forward(
             *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "bias", "block", "block_small"])
+              "bias", "wide", "block", "block_small"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -481,6 +492,19 @@ def main():
                                     "traffic": stored_traffic("bias", "forward.hip"),
                                     "kernel": "forward_bf16_kernel<128, bias>",
                                     "flops_per_launch": fl}}
+    if "wide" in ms:
+        B, H, S, D = WIDE
+        fl = formula_flops(B, H, S, S, D, True)
+        tf = fl / (ms["wide"] * 1e-3) / 1e12
+        rec["wide"] = {"workload": "bf16_causal_b%d_h%d_s%d_d%d" % (B, H, S, D),
+                       "ms": round(ms["wide"], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                       "executed_mfma_flops": 1.5 * fl,
+                       "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                    "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                    "traffic": stored_traffic("wide", "forward.hip"),
+                                    "kernel": "forward_bf16_kernel<256, DV=128> x 2 slices",
+                                    "flops_per_launch": fl}}
     for name, (B, S, M, H) in BLOCKS.items():
         if name not in ms:
             continue
@@ -497,7 +521,7 @@ def main():
                                             "gemm_kernel<out>",
                                   "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
-        blk = [n for n in BLOCKS if n in rec]
+        blk = [n for n in list(BLOCKS) + ["wide"] if n in rec]
         if blk:
             rec.update({"value": rec[blk[0]]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec[blk[0]]["workload"]}
@@ -523,7 +547,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw, ibias, iblk
+    del ip, ig, idd, ipg, ipp, ibw, ibias, iblk, iwide
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -158,7 +158,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <int D>
 struct Bf16Geo {
     static constexpr int CPR = D / 8;                // 16-byte chunks per row
-    static constexpr int RPW = 256 / (2 * D);        // rows per 256-byte bank window
+    static constexpr int RPW = D > 128 ? 1 : 256 / (2 * D);  // rows per 256-byte bank window (1: a row spans two)
     static constexpr int TILE = kBc * D;             // bf16 elements per K or V tile
     static constexpr int STAGE = 2 * TILE;           // K tile then V tile
     static constexpr int DMA = TILE * 2 / 1024 / 4;  // 1-KB DMA loads per wave per tensor
@@ -181,15 +181,22 @@ struct Bf16Geo {
 // it loads those four 16-byte runs of its bias row (one tile ahead, next to
 // the DMA issue) and adds bias / scale in raw-score units during the mask
 // step; every visited tile takes the mask step.
-template <int D, bool PAGED, class T, bool BIAS = false, bool GEN = false>
-__global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
+//
+// DV < D (head dims above 128): the workgroup computes the scores over all D
+// dims but only the DV output dims of slice blockIdx.y (V columns
+// DV*y .. DV*y + DV - 1), so the registers hold D-wide Q fragments and a
+// DV-wide output; the slices of a query block recompute its scores.
+template <int D, bool PAGED, class T, bool BIAS = false, bool GEN = false, int DV = D>
+__global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel(
     ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
-    using L = Bf16Geo<D>;
+    using L = Bf16Geo<D>;    // K tiles
+    using LV = Bf16Geo<DV>;  // V tiles (the slice)
     // Two K stages then two V stages.  K runs one tile ahead of V: while the
     // weights of tile j are formed, the scores of tile j+1 are computed.
     // (Paged: then the validity of each K stage's four 16-key groups.)
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE + (PAGED ? 16 : 0)];
+    constexpr int VBASE = 2 * L::TILE;  // first V stage
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * L::TILE + 2 * LV::TILE + (PAGED ? 16 : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -202,6 +209,9 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // DR wide in HBM and D wide on chip; the 16-byte chunks at or past DR are
     // read as zeros (their offsets lie outside the buffer) and never stored.
     const int DR = GEN ? a.D : D;
+    // Output slice: dims dv0 .. dv0 + DRV - 1 of the DR in memory.
+    const int dv0 = DV < D ? DV * (int)blockIdx.y : 0;
+    const int DRV = DV < D ? min(DV, DR - dv0) : DR;
     constexpr uint32_t kOut = 0x80000000u;  // past any num_records (<= INT_MAX)
     const uint16_t* kp;
     const uint16_t* vp;
@@ -281,19 +291,25 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // The wave's LDS rows are 16*wave .. 16*wave+15, i.e. keys of the same group.
     const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * DR * 2 : (uint32_t)DR * 2;
     const int row_base = PAGED ? 16 * wave : 0;
-    uint32_t koff[L::DMA], voff[L::DMA];
+    uint32_t koff[L::DMA], voff[LV::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int q = 64 * (L::DMA * wave + i) + lane;
         const int row = q / L::CPR, pc = q % L::CPR;
-        const int ck = pc ^ L::fk(row), cv = pc ^ L::fv(row);  // logical chunks
+        const int ck = pc ^ L::fk(row);  // logical chunk
         koff[i] = 8 * ck < DR ? (k_lds_row(row) - row_base) * row_bytes + ck * 16 : kOut;
-        voff[i] = 8 * cv < DR ? (row - row_base) * row_bytes + cv * 16 : kOut;
+    }
+#pragma unroll
+    for (int i = 0; i < LV::DMA; ++i) {
+        const int q = 64 * (LV::DMA * wave + i) + lane;
+        const int row = q / LV::CPR, pc = q % LV::CPR;
+        const int cv = pc ^ LV::fv(row);  // logical chunk of the slice
+        voff[i] = 8 * cv < DRV ? (row - row_base) * row_bytes + (dv0 + 8 * cv) * 2 : kOut;
     }
     // Paged: resource over the page of keys j0 + 16*wave .. +15 (zero records
     // when the table entry is outside the cache) and the group's scalar
     // offset inside it; the validity goes to LDS for the mask.
-    int* const kvalid = reinterpret_cast<int*>(smem + 4 * L::TILE);  // [K stage][group]
+    int* const kvalid = reinterpret_cast<int*>(smem + VBASE + 2 * LV::TILE);  // [K stage][group]
     // The lookup for a tile is made when its K is issued and kept (per K
     // stage) for its V, issued one step later.
     int64_t pg_off[2] = {0, 0};
@@ -325,18 +341,18 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
         }
     };
     auto issue_v = [&](int j0, int stage) {
-        uint16_t* dst = smem + (2 + stage) * L::TILE + 512 * L::DMA * wave;
+        uint16_t* dst = smem + VBASE + stage * LV::TILE + 512 * LV::DMA * wave;
         if (PAGED) {
             // K of this tile went to K stage (j0 / kBc) % 2 with the lookup.
             const int ks = (j0 / kBc) & 1;
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + pg_off[ks], pg_bytes[ks]);
 #pragma unroll
-            for (int i = 0; i < L::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], pg_soff[ks]);
+            for (int i = 0; i < LV::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], pg_soff[ks]);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(vp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
 #pragma unroll
-            for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
+            for (int i = 0; i < LV::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
         }
     };
 
@@ -349,16 +365,16 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     const int g16 = lane >> 4, j16 = lane & 15;
     const int tr_row = 8 * hg + (j16 >> 2);
     const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
-    int vrd[D / 32];
+    int vrd[DV / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < DV / 32; ++db) {
         const int col = 32 * db + tr_col;
-        vrd[db] = tr_row * D + (((col >> 3) ^ L::fv(tr_row)) * 8) + (col & 7);
+        vrd[db] = tr_row * DV + (((col >> 3) ^ LV::fv(tr_row)) * 8) + (col & 7);
     }
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[DV / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < DV / 32; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY;  // reference max of row qi (raw score units)
     float l_run = 0.f;        // this lane's share of the running denominator
     const float c = a.scale * kLog2e;
@@ -471,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < DV / 32; ++db) oacc[db] *= alpha;
         }
     };
     // bf16 weights of a score tile against the reference max; the denominator
@@ -502,18 +518,18 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
                               pk[kb2][4 * half + 3]};
             // all of a 16-key slice's V^T fragments are read before its MFMAs
             // (each pair read right before its MFMA exposed the read latency)
-            u32x4 vf[D / 32];
+            u32x4 vf[DV / 32];
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint16_t* vb = vs + 16 * kk * D + vrd[db];
+            for (int db = 0; db < DV / 32; ++db) {
+                const uint16_t* vb = vs + 16 * kk * DV + vrd[db];
                 const u32x2 lo = lds_read_tr16x4(vb);
-                const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
+                const u32x2 hi = lds_read_tr16x4(vb + 4 * DV);
                 vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] = mfma_32x32x16<T>(vf[db], pw, oacc[db]);
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 4);
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 4);
+            for (int db = 0; db < DV / 32; ++db) oacc[db] = mfma_32x32x16<T>(vf[db], pw, oacc[db]);
+            __builtin_amdgcn_sched_group_barrier(0x100, DV / 16, 4);
+            __builtin_amdgcn_sched_group_barrier(0x008, DV / 32, 4);
         }
     };
 
@@ -559,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
                 ps = weights(scur, pk);
             }
             l_run += ps;
-            accumulate(smem + (2 + cur) * L::TILE, pk);
+            accumulate(smem + VBASE + cur * LV::TILE, pk);
             if (jt + 1 < wave_tiles) mask_tile((jt + 1) * kBc, snext, vnext);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA landed
@@ -577,19 +593,19 @@ __global__ __launch_bounds__(kThreads, 2) void forward_bf16_kernel(
     // Optional log-sum-exp of the row (natural log, scaled-score units) for
     // the backward: the reference max plus ln of the denominator; -inf for a
     // row with no visible key.
-    if (!PAGED && a.lse && hg == 0 && qi < nrows)
+    if (!PAGED && a.lse && hg == 0 && qi < nrows && dv0 == 0)
         a.lse[((int64_t)ti.b * a.Hq + ti.h) * a.Sq + qi] =
             m_run == -INFINITY ? -INFINITY : m_run * a.scale + __logf(lt);
     if (qi < nrows) {
-        uint16_t* orow = op + (int64_t)qi * (qstride / 2);
+        uint16_t* orow = op + (int64_t)qi * (qstride / 2) + dv0;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const u32x2 w = {pack2<T>(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
                                  pack2<T>(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
-                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
-                if (d0 < DR) *reinterpret_cast<u32x2*>(orow + d0) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims of the slice, all < DRV or none
+                if (d0 < DRV) *reinterpret_cast<u32x2*>(orow + d0) = w;
             }
     }
 }
@@ -751,14 +767,15 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
 
 inline dim3 forward_grid(const ForwardArgs& a) {
     const int nqb = (a.Sq + kBr - 1) / kBr;
-    return dim3((unsigned)(nqb * a.B * a.Hq));
+    return dim3((unsigned)(nqb * a.B * a.Hq), a.D > 128 ? 2u : 1u);  // y: output slice of 128 dims
 }
 
-// Head dims that are multiples of 8 run on the 64- or 128-wide kernel (the
-// general-width instantiation unless D is exactly 64 or 128).
+// Head dims that are multiples of 8 run on the 64-, 128- or 256-wide kernel
+// (the general-width instantiation unless D is exactly 64, 128 or 256); above
+// 128 the output is computed in two 128-dim slices.
 template <bool PAGED, class T, bool BIAS = false>
 hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
-    if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
+    if (a.D % 8 != 0 || a.D < 8 || a.D > 256) return hipErrorInvalidValue;
     const dim3 g = forward_grid(a), t(kThreads);
     if (a.D == 64)
         hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS>), g, t, 0, s, a, p, p.block_tables,
@@ -766,11 +783,17 @@ hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s)
     else if (a.D == 128)
         hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS>), g, t, 0, s, a, p, p.block_tables,
                            p.seq_lens, p.cu_seqlens_q);
+    else if (a.D == 256)
+        hipLaunchKernelGGL((forward_bf16_kernel<256, PAGED, T, BIAS, false, 128>), g, t, 0, s, a, p,
+                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
     else if (a.D < 64)
         hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS, true>), g, t, 0, s, a, p,
                            p.block_tables, p.seq_lens, p.cu_seqlens_q);
-    else
+    else if (a.D < 128)
         hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS, true>), g, t, 0, s, a, p,
+                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
+    else
+        hipLaunchKernelGGL((forward_bf16_kernel<256, PAGED, T, BIAS, true, 128>), g, t, 0, s, a, p,
                            p.block_tables, p.seq_lens, p.cu_seqlens_q);
     return hipGetLastError();
 }

@@ -51,9 +51,12 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // Head dims the kernels cover: 16-bit inputs any multiple of 8 up to 128
 // (the 64- and 128-wide kernels read the missing chunks as zeros), fp32
 // exactly 64 or 128.
-bool head_dim_ok(int64_t D, int dtype) {
+// max16: the widest 16-bit head dim of the entry point (256 where the
+// prefill kernel runs, whose output goes in two 128-dim slices above 128;
+// 128 for the decode and backward kernels).
+bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D == 64 || D == 128;
-    return D >= 8 && D <= 128 && D % 8 == 0;
+    return D >= 8 && D <= max16 && D % 8 == 0;
 }
 
 constexpr size_t kAlign = 256;
@@ -62,7 +65,8 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Shared checks of both entry points.  On success fills the tensor byte sizes.
 sdpa_status_t check_common(const void* q, const void* k, const void* v, void* out, int64_t B,
                            int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
-                           float scale, int dtype, int64_t* qbytes, int64_t* kbytes) {
+                           float scale, int dtype, int64_t* qbytes, int64_t* kbytes,
+                           int64_t max16 = 128) {
     if (!q || !k || !v || !out) return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT,
@@ -87,9 +91,10 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
     // Per-head rows are addressed through buffer resources with 32-bit extents.
     if (Sq * D * es > INT_MAX || Sk * D * es > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "one head of q, k or v exceeds 2 GiB");
-    if (!head_dim_ok(D, dtype))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (%s)", (long long)D,
-                    dtype == SDPA_F32 ? "64 or 128 for fp32" : "a multiple of 8 up to 128");
+    if (!head_dim_ok(D, dtype, max16))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (%s%lld)", (long long)D,
+                    dtype == SDPA_F32 ? "64 or 128 for fp32; " : "a multiple of 8 up to ",
+                    dtype == SDPA_F32 ? 0LL : (long long)max16);
     return SDPA_OK;
 }
 
@@ -127,7 +132,7 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
                            int64_t bias_sb = 0, int64_t bias_sh = 0) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st = check_common(q, k, v, out, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
-                                    &kbytes);
+                                    &kbytes, 256);
     if (st != SDPA_OK) return st;
     if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
@@ -386,8 +391,8 @@ sdpa_status_t sdpa_block_forward(const void* x, const void* wq, const void* wk, 
         return fail(SDPA_ERR_INVALID_ARGUMENT, "model width %lld is not a multiple of heads %lld",
                     (long long)model, (long long)heads);
     const int64_t hd = model / heads;
-    if (!head_dim_ok(hd, dtype))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld not supported (a multiple of 8 up to 128)",
+    if (!head_dim_ok(hd, dtype, 256))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld not supported (a multiple of 8 up to 256)",
                     (long long)hd);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
@@ -673,8 +678,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (!head_dim_ok(D, dtype))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 128)",
+    if (!head_dim_ok(D, dtype, 256))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 256)",
                     (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 and fp16 only");

@@ -92,10 +92,12 @@ enum {
  *   out      device [B, Hq, Sq, D], dtype; written completely
  *   dtype    SDPA_BF16, SDPA_F16 or SDPA_F32
  *   stream   hipStream_t as void*
- * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 128
- * (the 64- and 128-wide kernels, with the dims past D read as zeros on chip),
- * SDPA_F32 D in {64, 128}; one head (Sq*D or Sk*D elements) must
- * be under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
+ * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 256
+ * (the 64-, 128- and 256-wide kernels, with the dims past D read as zeros on
+ * chip; above 128 two workgroups per query block each produce 128 output
+ * dims and both compute the scores), SDPA_F32 D in {64, 128}; one head
+ * (Sq*D or Sk*D elements) must be under 2 GiB (SDPA_ERR_UNSUPPORTED
+ * otherwise).
  */
 sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
@@ -128,8 +130,8 @@ sdpa_status_t sdpa_forward_lse(const void *q, const void *k, const void *v,
  *              (lse -inf).
  *   lse        NULL, or device float [B, Hq, Sq] as in sdpa_forward_lse
  * Every other argument as sdpa_forward.  The bias is read once per 128-row
- * query block.  Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up
- * to 128, bias
+ * query block (and output slice, D > 128).  Supported: dtype SDPA_BF16 or
+ * SDPA_F16, D a multiple of 8 up to 256, bias
  * rows 16-byte aligned (Sk, bias_stride_b and bias_stride_h multiples of 8,
  * pointer 16-byte aligned), one head's bias (Sq * Sk elements) under 2 GiB
  * (SDPA_ERR_UNSUPPORTED otherwise).  out and lse must not overlap the bias.
@@ -226,7 +228,7 @@ size_t sdpa_block_workspace_size(int64_t B, int64_t S, int64_t model);
  * straight into head layout), the attention, and the output projection
  * (reading the attention output from head layout).  Products accumulate in
  * fp32; q, k, v, the attention output and y are rounded to dtype.
- * Supported: dtype SDPA_BF16 or SDPA_F16, headDim a multiple of 8 up to 128,
+ * Supported: dtype SDPA_BF16 or SDPA_F16, headDim a multiple of 8 up to 256,
  * x and each weight under 2 GiB.  y and the workspace must not overlap each
  * other or any input.
  */
@@ -333,7 +335,7 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *                 keys j <= the row's absolute position
  *   out           device [total_q, Hq, D]
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
- * SDPA_F16, D a multiple of 8 up to 128, page_size a multiple of 16
+ * SDPA_F16, D a multiple of 8 up to 256, page_size a multiple of 16
  * (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside

@@ -69,7 +69,8 @@ def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, sca
     (dict(out=ctypes.c_void_p(0x40000000 - 2)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(B=1 << 40, Hq=1 << 20), sd.SDPA_ERR_INVALID_ARGUMENT, "overflow"),
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),     # past the 256-wide kernel
+    (dict(D=252), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=96, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(Sq=1 << 33, Sk=1 << 33, B=1, Hq=1, Hkv=1, D=64, out=ctypes.c_void_p(1 << 46)),
@@ -106,6 +107,7 @@ def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1,
     (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),     # the decode kernel stops at 128
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
 ])
 def test_decode_rejects(kw, status, needle):
@@ -198,7 +200,7 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, pages=100, p
     (dict(causal=-1), sd.SDPA_ERR_INVALID_ARGUMENT, "causal"),
     (dict(max_seq_len=801), sd.SDPA_ERR_INVALID_ARGUMENT, "capacity"),
     (dict(out=ctypes.c_void_p(0x7e000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=256), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
 ])
@@ -259,6 +261,7 @@ def bwd(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128, 
     (dict(dq=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
     (dict(D=256), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),     # the backward kernels stop at 128
     (dict(mask=1, Sq=64), sd.SDPA_ERR_INVALID_ARGUMENT, "Sq == Sk"),
     (dict(mask=2), sd.SDPA_ERR_INVALID_ARGUMENT, "key_lens"),
     (dict(mask=8), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),
@@ -345,7 +348,7 @@ def block(x=FAKE, wq=FAKE_K, wk=FAKE_V, wv=FAKE_O, wo=FAKE_W, B=2, S=128, model=
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
     (dict(dtype=9), sd.SDPA_ERR_INVALID_ARGUMENT, "dtype"),
     (dict(model=500), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
-    (dict(model=1088), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 136 wide
+    (dict(model=2112), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 264 wide
     (dict(model=168, heads=2), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 84 wide
     (dict(scale=float("nan")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
     (dict(mask=4), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),

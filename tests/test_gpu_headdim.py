@@ -14,7 +14,7 @@ import torch
 import exact_scaled_dot_amd as sd
 import oracle as O
 from exact_scaled_dot_amd.workloads import draw_bias, draw_grad, draw_paged, draw_qkv
-from parity import compare, compare_grad, to64
+from parity import compare, compare_grad, sample_rows, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +115,104 @@ def test_outputs_past_head_dim_untouched():
     torch.cuda.synchronize()
     assert (big[B * Hq * S * D:] == 7.0).all()
     compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.12, O.MASK_CAUSAL), BF16, "D=72")
+
+
+# ------------------------------------------------------------- wide head dims
+# Above 128 the prefill kernel computes the output in two 128-dim slices (two
+# workgroups per query block, each with the full-width scores).
+
+@pytest.mark.parametrize("D", [136, 200, 256])
+@pytest.mark.parametrize("mask", [0, 1, 3], ids=["none", "causal", "causal+padding"])
+def test_forward_wide_head_dims(D, mask):
+    B, Hq, Hkv, S = 2, 4, 2, 200
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 780 + D + mask, DEV)
+    lens = torch.tensor([200, 77], dtype=torch.int32, device=DEV) if mask & 2 else None
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask, ln, return_lse=True)
+    compare(to64(out), ref, BF16, "wide forward D=%d mask=%d" % (D, mask))
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
+
+
+def test_forward_wide_fp16_bias_and_gqa():
+    B, Hq, Hkv, S, D = 2, 8, 2, 150, 256
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, F16, 790, DEV)
+    out = sd.sdpa_forward(q, k, v, 0.07, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.07, O.MASK_CAUSAL), F16,
+            "fp16 D=256")
+    # Sk = 150 is not a multiple of 8: the bias path needs 16-byte rows, so use 152 keys
+    S2 = 152
+    q2, k2, v2 = draw_qkv(B, Hq, Hkv, S2, S2, D, F16, 792, DEV)
+    bias = draw_bias((B, 1, S2, S2), F16, 793, DEV)
+    outb = sd.sdpa_forward_bias(q2, k2, v2, bias, 0.07, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    compare(to64(outb), O.sdpa_forward(to64(q2), to64(k2), to64(v2), 0.07, O.MASK_CAUSAL,
+                                       bias=to64(bias)), F16, "fp16 D=256 bias")
+
+
+def test_wide_outputs_past_head_dim_untouched():
+    # D=200: the second slice covers dims 128..199 only
+    B, Hq, S, D = 1, 2, 70, 200
+    q, k, v = draw_qkv(B, Hq, Hq, S, S, D, BF16, 794, DEV)
+    big = torch.full((B * Hq * S * D + 64,), 7.0, dtype=BF16, device=DEV)
+    out = big[: B * Hq * S * D].view(B, Hq, S, D)
+    sd.sdpa_forward(q, k, v, 0.1, sd.MASK_CAUSAL, out=out)
+    torch.cuda.synchronize()
+    assert (big[B * Hq * S * D:] == 7.0).all()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL), BF16, "D=200")
+
+
+def test_paged_prefill_wide_head_dim():
+    D = 256
+    lens = [300, 129]
+    inp = draw_paged(lens, [0, 1, 1], [299, 128, 64], 8, 2, D, 16, BF16, 795, DEV)
+    scale = 1 / math.sqrt(D)
+    msl = inp["block_tables"].shape[1] * 16
+    chunks = [150, 129]
+    cu = torch.tensor([0, 150, 279], dtype=torch.int32, device=DEV)
+    qc = draw_qkv(1, 1, 1, sum(chunks), 1, 8 * D, BF16, 796, DEV)[0].reshape(sum(chunks), 8, D)
+    outp = sd.sdpa_paged_prefill(qc.contiguous(), inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                 inp["seq_lens"], cu, scale, True, max(chunks), msl)
+    torch.cuda.synchronize()
+    qs, qp = O.chunk_positions(cu.cpu().numpy(), np.array(lens))
+    refp = O.paged_attention(to64(qc), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                             inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, scale, True)
+    compare(to64(outp), refp, BF16, "paged prefill D=256")
+
+
+def test_forward_wide_full_size_sampled_rows():
+    # a 4096-token causal prefill with 256-wide heads; the oracle checks
+    # sampled rows (tile edges included) of every head
+    B, H, S, D = 1, 8, 4096, 256
+    q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 797, DEV)
+    scale = 1 / math.sqrt(D)
+    out = sd.sdpa_forward(q, k, v, scale, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    rows = sample_rows(B, H, S, 64, 798)
+    ref, _ = O.sdpa_forward_rows(to64(q), to64(k), to64(v), scale, O.MASK_CAUSAL, None, rows)
+    got = to64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    compare(got, ref, BF16, "wide full size")
+
+
+def test_block_wide_heads():
+    # model 512 in 2 heads of 256
+    from exact_scaled_dot_amd.workloads import draw_block
+    from parity import compare_block
+    x, wq, wk, wv, wo = draw_block(2, 100, 512, BF16, 799, DEV)
+    y = sd.sdpa_block_forward(x, wq, wk, wv, wo, 2, None, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    ref = O.block_forward(to64(x), to64(wq), to64(wk), to64(wv), to64(wo), 2, None, O.MASK_CAUSAL)
+    compare_block(to64(y), ref, BF16, "block hd=256")
+
+
+def test_decode_and_backward_reject_wide_head_dims():
+    q, k, v = draw_qkv(1, 2, 1, 1, 64, 256, BF16, 800, DEV)
+    with pytest.raises(sd.SdpaError, match="up to 128"):
+        sd.sdpa_decode(q, k, v, 0.1, None, 1)
+    q, k, v = draw_qkv(1, 2, 1, 64, 64, 256, BF16, 801, DEV)
+    out, lse = sd.sdpa_forward_lse(q, k, v, 0.1, 0)
+    with pytest.raises(sd.SdpaError, match="up to 128"):
+        sd.sdpa_backward(q, k, v, out, out, lse, 0.1, 0)
