@@ -8,6 +8,7 @@ missing merge weight) fails at least one of them.
 """
 
 import itertools
+import os
 import math
 
 import numpy as np
@@ -793,3 +794,39 @@ def test_block_rows_equal_full():
         np.testing.assert_allclose(got, full[rows[:, 0], rows[:, 1]], rtol=0, atol=1e-13)
         if kl is not None:
             assert np.isnan(got[rows[:, 0] == 2]).all()
+
+
+# ------------------------------------------------------------------ page fixtures
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [l.split() for l in f if l.strip() and not l.startswith("#")]
+
+
+def test_golden_essay_single_row():
+    rows = dict((l[0], np.array([float(x) for x in l[1:]])) for l in _golden_lines("essay_single_row.txt"))
+    x = rows["input"].reshape(1, 1, 4)
+    rng = np.random.default_rng(95)
+    I = np.eye(4)
+    for wq, wk in ((I, I), (rng.standard_normal((4, 4)), rng.standard_normal((4, 4)))):
+        # the essay's scale 1 / sqrt(d) and another one: the single weight is 1 either way
+        for scale in (0.5, 3.0):
+            y = O.block_forward(x, wq, wk, I, I, 1, scale)
+            np.testing.assert_allclose(y.reshape(4), rows["output"], rtol=0, atol=1e-15)
+
+
+def test_golden_tensai_causal_mask():
+    m = np.array([[float(x) for x in l] for l in _golden_lines("tensai_causal_mask_seq4.txt")])
+    assert m.shape == (4, 4)
+    # the causal flag hides exactly the -inf entries ...
+    vis = O.visible_rows(O.MASK_CAUSAL, np.arange(4), 4, 0)
+    np.testing.assert_array_equal(vis, m == 0)
+    # ... and adding the page's mask as a bias gives the flag's result
+    rng = np.random.default_rng(96)
+    q, k, v = (rng.standard_normal((2, 3, 4, 8)) for _ in range(3))
+    via_flag = O.sdpa_forward(q, k, v, 0.3, O.MASK_CAUSAL)
+    via_bias = O.sdpa_forward(q, k, v, 0.3, O.MASK_NONE, bias=m[None, None])
+    np.testing.assert_array_equal(via_bias, via_flag)
