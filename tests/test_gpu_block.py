@@ -92,3 +92,12 @@ def test_block_full_size_sampled_rows():
     ref = O.block_forward_rows(x64, *(to64(t) for t in ins[1:]), H, rows, None, O.MASK_CAUSAL)
     got = to64(y)[rows[:, 0], rows[:, 1]]
     compare_block(got, ref, BF16, "full-size block rows")
+
+
+def test_block_tile_sizes():
+    # the projections pick 256-, 128- or 64-wide tiles by grid size: batch 4,
+    # 512 tokens, model 1024 runs the q/k/v projections on 128 x 128 tiles
+    # (384 workgroups) and the output projection on 64 x 64 ones; the small
+    # and full-size tests above cover 64 and 256
+    ins, y = run_block(4, 512, 1024, 8, BF16, 960, sd.MASK_CAUSAL)
+    compare_block(to64(y), oracle_block(ins, 8, O.MASK_CAUSAL), BF16, "block 128-wide tiles")
