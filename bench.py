@@ -17,7 +17,9 @@ resident in HBM:
     [1, 16, 4096, 4096] bf16 added to the scaled scores
   * the causal prefill with 256-wide heads, bf16, B=4 Hq=Hkv=8 S=4096 D=256
     (the same formula FLOPs as the headline; the kernel computes the output
-    in two 128-dim slices that each recompute the scores)
+    in two 128-dim slices that each recompute the scores), and the split-KV
+    decode with 256-wide heads, B=32 Hq=32 Hkv=8 Sk=32768 (the decode's K+V
+    bytes), 32 splits
   * the multi-head attention block (q/k/v projections, causal attention,
     output projection) at the tensai guide's shape (batch 8, 128 tokens,
     model 256, 4 heads) and at the prefill's (batch 4, 4096 tokens, model
@@ -58,6 +60,7 @@ PAGE_SIZE = 16                      # paged decode: keys per cache page
 # attention blocks: (batch, tokens, model width, heads)
 BLOCKS = {"block": (4, 4096, 2048, 16), "block_small": (8, 128, 256, 4)}
 WIDE = (4, 8, 4096, 256)            # wide heads: (batch, heads, tokens, head dim)
+DECODE_WIDE = (32, 32, 8, 32768, 256)  # wide decode: (batch, Hq, Hkv, Sk, head dim)
 
 
 def kernel_source_hash(name):
@@ -225,8 +228,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward", "backward_atomic", "bias", "wide", "block",
-                                       "block_small"],
+                                       "backward", "backward_atomic", "bias", "wide",
+                                       "decode_wide", "block", "block_small"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -308,6 +311,13 @@ def main():
         iwide = dict(zip(("q", "k", "v"), draw_qkv(WIDE[0], WIDE[1], WIDE[1], WIDE[2], WIDE[2],
                                                    WIDE[3], wp.dtype, wp.seed + 31, dev)))
         iwide["out"] = torch.empty_like(iwide["q"])
+    idw = None
+    if args.only in (None, "decode_wide"):
+        B, Hq, Hkv, Sk, D = DECODE_WIDE
+        idw = dict(zip(("q", "k", "v"), draw_qkv(B, Hq, Hkv, 1, Sk, D, wd.dtype, wd.seed + 31, dev)))
+        idw["out"] = torch.empty_like(idw["q"])
+        idw["ws"] = torch.empty(sd.sdpa_decode_workspace_size(B, Hq, D, wd.num_splits),
+                                dtype=torch.uint8, device=dev)
     # Attention blocks: x and four weights per shape (N(0,1) activations,
     # N(0, 1/model) weights), the output and the workspace allocated here.
     iblk = {}
@@ -343,6 +353,9 @@ def main():
         None, ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"], atomic=True)
     calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
                                                  sd.MASK_CAUSAL, None, ibias["out"])
+    calls["decode_wide"] = lambda: sd.sdpa_decode(idw["q"], idw["k"], idw["v"],
+                                                  1.0 / math.sqrt(DECODE_WIDE[4]), None,
+                                                  wd.num_splits, idw["ws"], idw["out"])
     calls["wide"] = lambda: sd.sdpa_forward(iwide["q"], iwide["k"], iwide["v"],
                                             1.0 / math.sqrt(WIDE[3]), sd.MASK_CAUSAL, None,
                                             iwide["out"])
@@ -351,7 +364,7 @@ def main():
             *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "bias", "wide", "block", "block_small"])
+              "bias", "wide", "decode_wide", "block", "block_small"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -505,6 +518,19 @@ def main():
                                     "traffic": stored_traffic("wide", "forward.hip"),
                                     "kernel": "forward_bf16_kernel<256, DV=128> x 2 slices",
                                     "flops_per_launch": fl}}
+    if "decode_wide" in ms:
+        B, Hq, Hkv, Sk, D = DECODE_WIDE
+        by = 2 * B * Hkv * Sk * D * 2 + 2 * B * Hq * D * 2
+        gbs = by / (ms["decode_wide"] * 1e-3) / 1e9
+        rec["decode_wide"] = {"workload": "bf16_gqa32x8_decode_b%d_sk%d_d%d" % (B, Sk, D),
+                              "ms": round(ms["decode_wide"], 4), "value": round(gbs, 1),
+                              "unit": "GB/s", "num_splits": wd.num_splits,
+                              "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                           "traffic": None,
+                                           "kernel": "decode_split_bf16_kernel<256> + merge",
+                                           "bytes_per_launch": by}}
     for name, (B, S, M, H) in BLOCKS.items():
         if name not in ms:
             continue
@@ -521,9 +547,9 @@ def main():
                                             "gemm_kernel<out>",
                                   "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
-        blk = [n for n in list(BLOCKS) + ["wide"] if n in rec]
+        blk = [n for n in list(BLOCKS) + ["wide", "decode_wide"] if n in rec]
         if blk:
-            rec.update({"value": rec[blk[0]]["value"], "unit": "TFLOP/s"})
+            rec.update({"value": rec[blk[0]]["value"], "unit": rec[blk[0]]["unit"]})
             rec["config"] = {"workload": rec[blk[0]]["workload"]}
         elif "bias" in rec:
             rec.update({"value": rec["bias"]["value"], "unit": "TFLOP/s"})
@@ -547,7 +573,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw, ibias, iblk, iwide
+    del ip, ig, idd, ipg, ipp, ibw, ibias, iblk, iwide, idw
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -89,7 +89,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, u
 template <int D>
 struct DecGeo {
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int RPW = 256 / (2 * D);          // rows per 256-byte bank window
+    static constexpr int RPW = D > 128 ? 1 : 256 / (2 * D);  // rows per 256-byte bank window (1: a row spans two)
     static constexpr int TILE = kStep * D;             // bf16 elements of one K or V step
     static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
     static constexpr int NS = kRingBytes / (2 * STAGE);  // ring stages per wave
@@ -103,7 +103,7 @@ struct DecGeo {
     // fall on 16 distinct 16-byte bank groups.
     __device__ static int fv(int r) { return 2 * ((r / RPW) % (8 / RPW)); }
 };
-static_assert(DecGeo<128>::NS == 4 && DecGeo<64>::NS == 8, "ring depth");
+static_assert(DecGeo<256>::NS == 2 && DecGeo<128>::NS == 4 && DecGeo<64>::NS == 8, "ring depth");
 
 // Per-launch metadata pointers, each read with scalar loads (hence separate
 // __restrict__ kernel arguments rather than struct members).
@@ -498,9 +498,10 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
-    if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
-    // Head dims that are multiples of 8 run on the 64- or 128-wide kernels.
-    const int dpad = a.D <= 64 ? 64 : 128;
+    if (a.D % 8 != 0 || a.D < 8 || a.D > 256) return hipErrorInvalidValue;
+    // Head dims that are multiples of 8 run on the 64-, 128- or 256-wide
+    // kernels (the 256-wide ring holds two steps per wave: one step ahead).
+    const int dpad = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
     const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * dpad / 4 + 255) / 256));
     const dim3 sg(wgs), st(kDecThreads), mt(256);
     const int32_t *kl = a.key_lens, *bt = p.block_tables, *sl = p.seq_lens, *qs = p.query_seq,
@@ -513,10 +514,18 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
         hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED, T>), sg, st, 0, s, a, p, kl, bt, sl, qs,
                            qp, items);
         hipLaunchKernelGGL((decode_merge_bf16_kernel<128, T>), mgrid, mt, 0, s, a);
+    } else if (a.D == 256) {
+        hipLaunchKernelGGL((decode_split_bf16_kernel<256, PAGED, T>), sg, st, 0, s, a, p, kl, bt, sl, qs,
+                           qp, items);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<256, T>), mgrid, mt, 0, s, a);
     } else if (dpad == 64) {
         hipLaunchKernelGGL((decode_split_bf16_kernel<64, PAGED, T, true>), sg, st, 0, s, a, p, kl, bt, sl,
                            qs, qp, items);
         hipLaunchKernelGGL((decode_merge_bf16_kernel<64, T, true>), mgrid, mt, 0, s, a);
+    } else if (dpad == 256) {
+        hipLaunchKernelGGL((decode_split_bf16_kernel<256, PAGED, T, true>), sg, st, 0, s, a, p, kl, bt,
+                           sl, qs, qp, items);
+        hipLaunchKernelGGL((decode_merge_bf16_kernel<256, T, true>), mgrid, mt, 0, s, a);
     } else {
         hipLaunchKernelGGL((decode_split_bf16_kernel<128, PAGED, T, true>), sg, st, 0, s, a, p, kl, bt,
                            sl, qs, qp, items);

@@ -51,9 +51,9 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // Head dims the kernels cover: 16-bit inputs any multiple of 8 up to 128
 // (the 64- and 128-wide kernels read the missing chunks as zeros), fp32
 // exactly 64 or 128.
-// max16: the widest 16-bit head dim of the entry point (256 where the
-// prefill kernel runs, whose output goes in two 128-dim slices above 128;
-// 128 for the decode and backward kernels).
+// max16: the widest 16-bit head dim of the entry point (256 for the prefill
+// and decode kernels; 128 for the backward, whose lanes hold a full-width
+// operand and gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D == 64 || D == 128;
     return D >= 8 && D <= max16 && D % 8 == 0;
@@ -488,7 +488,7 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
                           size_t workspace_bytes, void* out, int dtype, void* stream) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st =
-        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes);
+        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes, 256);
     if (st != SDPA_OK) return st;
     if (num_splits < 1 || num_splits > SDPA_MAX_SPLITS)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..%d", num_splits,
@@ -586,8 +586,8 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     if (queries > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (!head_dim_ok(D, dtype))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 128)",
+    if (!head_dim_ok(D, dtype, 256))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 256)",
                     (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 and fp16 only");

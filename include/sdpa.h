@@ -260,7 +260,8 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
  *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
  *   out        device [B, Hq, 1, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 256
+ * (above 128 each wave's LDS ring holds two 16-key steps instead of four).
  */
 sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D,
@@ -295,7 +296,7 @@ sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
  *                (same layout as sdpa_decode's with B = queries)
  *   out          device [queries, Hq, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128,
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 256,
  * page_size a
  * multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the

@@ -107,7 +107,7 @@ def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1,
     (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),     # the decode kernel stops at 128
+    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "up to 256"),     # the decode kernel stops at 256
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
 ])
 def test_decode_rejects(kw, status, needle):
@@ -168,7 +168,7 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_
     (dict(ws_bytes=64), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(out=ctypes.c_void_p(0x7a000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=96, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),

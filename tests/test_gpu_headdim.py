@@ -208,10 +208,34 @@ def test_block_wide_heads():
     compare_block(to64(y), ref, BF16, "block hd=256")
 
 
-def test_decode_and_backward_reject_wide_head_dims():
-    q, k, v = draw_qkv(1, 2, 1, 1, 64, 256, BF16, 800, DEV)
-    with pytest.raises(sd.SdpaError, match="up to 128"):
-        sd.sdpa_decode(q, k, v, 0.1, None, 1)
+@pytest.mark.parametrize("D", [200, 256])
+@pytest.mark.parametrize("splits", [1, 7])
+def test_decode_wide_head_dims(D, splits):
+    B, Hq, Hkv, Sk = 3, 16, 4, 1000
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 802 + D, DEV)
+    lens = torch.tensor([1000, 333, 17], dtype=torch.int32, device=DEV)
+    out = sd.sdpa_decode(q, k, v, 0.07, lens, splits)
+    torch.cuda.synchronize()
+    ref = O.sdpa_decode(to64(q), to64(k), to64(v), 0.07, lens.cpu().numpy())
+    compare(to64(out), ref, BF16, "decode D=%d splits=%d" % (D, splits))
+
+
+def test_paged_decode_wide_head_dim():
+    D = 256
+    lens = [300, 129]
+    inp = draw_paged(lens, [0, 1, 1], [299, 128, 64], 8, 2, D, 16, BF16, 804, DEV)
+    msl = inp["block_tables"].shape[1] * 16
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], 0.06, True,
+                                  msl, 3)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            inp["block_tables"].cpu().numpy(), np.array(lens),
+                            inp["query_seq"].cpu().numpy(), inp["query_pos"].cpu().numpy(), 0.06, True)
+    compare(to64(out), ref, BF16, "paged decode D=256")
+
+
+def test_backward_rejects_wide_head_dims():
     q, k, v = draw_qkv(1, 2, 1, 64, 64, 256, BF16, 801, DEV)
     out, lse = sd.sdpa_forward_lse(q, k, v, 0.1, 0)
     with pytest.raises(sd.SdpaError, match="up to 128"):
