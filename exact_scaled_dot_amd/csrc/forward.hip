@@ -613,7 +613,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
 // ---------------------------------------------------------------------------
 // fp32 inputs, fp32 MFMA (v_mfma_f32_32x32x2_f32): every product exact in fp32.
 // ---------------------------------------------------------------------------
-template <int D>
+// GEN: rows are DR = a.D floats in memory (a multiple of 4 below D); the
+// 16-byte chunks past DR load as zeros and are never stored.
+template <int D, bool GEN = false>
 __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a) {
     constexpr int RS = D + 4;  // row stride in LDS (floats), 16 B of padding
     __shared__ __attribute__((aligned(16))) float ks[kBc * RS];
@@ -626,12 +628,13 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
     const int hg = lane >> 5;
 
     const TileInfo ti = decode_tile(a);
+    const int DR = GEN ? a.D : D;
     const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
-    const float* qp = static_cast<const float*>(a.q) + bh * a.Sq * D;
-    const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * D;
+    const float* qp = static_cast<const float*>(a.q) + bh * a.Sq * DR;
+    const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * DR;
     const float* kp = static_cast<const float*>(a.k) + kvh;
     const float* vp = static_cast<const float*>(a.v) + kvh;
-    float* op = static_cast<float*>(a.out) + bh * a.Sq * D;
+    float* op = static_cast<float*>(a.out) + bh * a.Sq * DR;
 
     const int qw = ti.q0 + wave * 32;
     const int qi = qw + l32;
@@ -645,7 +648,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
 #pragma unroll
     for (int T = 0; T < D / 8; ++T) {
         qf[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (qi < a.Sq) qf[T] = *reinterpret_cast<const f32x4*>(qp + (int64_t)qi * D + 8 * T + 4 * hg);
+        if (qi < a.Sq && 8 * T + 4 * hg < DR)
+            qf[T] = *reinterpret_cast<const f32x4*>(qp + (int64_t)qi * DR + 8 * T + 4 * hg);
     }
 
     f32x16 oacc[D / 32];
@@ -663,9 +667,9 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
             const int row = cidx / (D / 4), cc = cidx % (D / 4);
             const int key = j0 + row;
             f32x4 wk = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
-            if (key < a.Sk) {
-                wk = *reinterpret_cast<const f32x4*>(kp + (int64_t)key * D + cc * 4);
-                wv = *reinterpret_cast<const f32x4*>(vp + (int64_t)key * D + cc * 4);
+            if (key < a.Sk && 4 * cc < DR) {
+                wk = *reinterpret_cast<const f32x4*>(kp + (int64_t)key * DR + cc * 4);
+                wv = *reinterpret_cast<const f32x4*>(vp + (int64_t)key * DR + cc * 4);
             }
             *reinterpret_cast<f32x4*>(ks + row * RS + cc * 4) = wk;
             *reinterpret_cast<f32x4*>(vs + row * RS + cc * 4) = wv;
@@ -753,14 +757,15 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
     const float lt = l_run + swap_half_wave(l_run);
     const float inv = 1.f / lt;
     if (qi < a.Sq) {
-        float* orow = op + (int64_t)qi * D;
+        float* orow = op + (int64_t)qi * DR;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 w = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv,
                                  oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv};
-                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * hg) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
+                if (d0 < DR) *reinterpret_cast<f32x4*>(orow + d0) = w;
             }
     }
 }
@@ -816,12 +821,15 @@ hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, 
 }
 
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s) {
+    if (a.D % 4 != 0 || a.D < 4 || a.D > 128) return hipErrorInvalidValue;
     if (a.D == 64)
         hipLaunchKernelGGL(forward_f32_kernel<64>, forward_grid(a), dim3(kThreads), 0, s, a);
     else if (a.D == 128)
         hipLaunchKernelGGL(forward_f32_kernel<128>, forward_grid(a), dim3(kThreads), 0, s, a);
+    else if (a.D < 64)
+        hipLaunchKernelGGL((forward_f32_kernel<64, true>), forward_grid(a), dim3(kThreads), 0, s, a);
     else
-        return hipErrorInvalidValue;
+        hipLaunchKernelGGL((forward_f32_kernel<128, true>), forward_grid(a), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

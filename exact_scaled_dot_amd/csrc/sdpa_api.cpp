@@ -48,14 +48,14 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 int64_t elem_size(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
 bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || dtype == SDPA_F16; }
 
-// Head dims the kernels cover: 16-bit inputs any multiple of 8 up to 128
-// (the 64- and 128-wide kernels read the missing chunks as zeros), fp32
-// exactly 64 or 128.
-// max16: the widest 16-bit head dim of the entry point (256 for the prefill
-// and decode kernels; 128 for the backward, whose lanes hold a full-width
-// operand and gradient).
+// Head dims the kernels cover: 16-bit inputs any multiple of 8 up to max16
+// (the 64-, 128- and 256-wide kernels read the missing chunks as zeros),
+// fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
+// kernel).  max16: the widest 16-bit head dim of the entry point (256 for
+// the prefill and decode kernels; 128 for the backward, whose lanes hold a
+// full-width operand and gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
-    if (dtype == SDPA_F32) return D == 64 || D == 128;
+    if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
     return D >= 8 && D <= max16 && D % 8 == 0;
 }
 
@@ -93,8 +93,8 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
         return fail(SDPA_ERR_UNSUPPORTED, "one head of q, k or v exceeds 2 GiB");
     if (!head_dim_ok(D, dtype, max16))
         return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (%s%lld)", (long long)D,
-                    dtype == SDPA_F32 ? "64 or 128 for fp32; " : "a multiple of 8 up to ",
-                    dtype == SDPA_F32 ? 0LL : (long long)max16);
+                    dtype == SDPA_F32 ? "fp32: a multiple of 4 up to " : "a multiple of 8 up to ",
+                    dtype == SDPA_F32 ? 128LL : (long long)max16);
     return SDPA_OK;
 }
 

@@ -95,9 +95,9 @@ enum {
  * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 256
  * (the 64-, 128- and 256-wide kernels, with the dims past D read as zeros on
  * chip; above 128 two workgroups per query block each produce 128 output
- * dims and both compute the scores), SDPA_F32 D in {64, 128}; one head
- * (Sq*D or Sk*D elements) must be under 2 GiB (SDPA_ERR_UNSUPPORTED
- * otherwise).
+ * dims and both compute the scores), SDPA_F32 any multiple of 4 from 4 to
+ * 128 (the 64- and 128-wide fp32 kernels, likewise); one head (Sq*D or
+ * Sk*D elements) must be under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
  */
 sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,

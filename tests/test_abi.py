@@ -71,7 +71,8 @@ def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, sca
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),     # past the 256-wide kernel
     (dict(D=252), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=96, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # fp32: multiples of 4
+    (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),  # fp32: up to 128
     (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(Sq=1 << 33, Sk=1 << 33, B=1, Hq=1, Hkv=1, D=64, out=ctypes.c_void_p(1 << 46)),
      sd.SDPA_ERR_UNSUPPORTED, "32-bit"),
@@ -169,7 +170,7 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_
     (dict(out=ctypes.c_void_p(0x7a000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=96, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
 ])

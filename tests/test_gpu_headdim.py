@@ -240,3 +240,33 @@ def test_backward_rejects_wide_head_dims():
     out, lse = sd.sdpa_forward_lse(q, k, v, 0.1, 0)
     with pytest.raises(sd.SdpaError, match="up to 128"):
         sd.sdpa_backward(q, k, v, out, out, lse, 0.1, 0)
+
+
+# ------------------------------------------------------------- fp32 head dims
+F32 = torch.float32
+
+
+@pytest.mark.parametrize("D", [4, 36, 96, 124])
+@pytest.mark.parametrize("mask", [0, 1, 2], ids=["none", "causal", "padding"])
+def test_forward_fp32_head_dims(D, mask):
+    # any multiple of 4 up to 128 on the 64- and 128-wide fp32 kernel
+    B, Hq, Hkv, S = 2, 4, 2, 150
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, F32, 810 + D + mask, DEV)
+    lens = torch.tensor([150, 61], dtype=torch.int32, device=DEV) if mask == 2 else None
+    scale = 1 / math.sqrt(D)
+    out = sd.sdpa_forward(q, k, v, scale, mask, lens)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    ref = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask, ln)
+    compare(to64(out), ref, F32, "fp32 D=%d mask=%d" % (D, mask))
+
+
+def test_fp32_outputs_past_head_dim_untouched():
+    B, Hq, S, D = 1, 2, 70, 52
+    q, k, v = draw_qkv(B, Hq, Hq, S, S, D, F32, 830, DEV)
+    big = torch.full((B * Hq * S * D + 64,), 7.0, dtype=F32, device=DEV)
+    out = big[: B * Hq * S * D].view(B, Hq, S, D)
+    sd.sdpa_forward(q, k, v, 0.1, sd.MASK_CAUSAL, out=out)
+    torch.cuda.synchronize()
+    assert (big[B * Hq * S * D:] == 7.0).all()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL), F32, "fp32 D=52")
