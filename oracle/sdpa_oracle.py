@@ -284,14 +284,20 @@ def merge_partials(o_part, lse_part):
     return o, lse
 
 
-def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None):
-    """dQ, dK, dV of L with dL/dO = dout, by the definition (fp64).
+def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None, bias=None,
+                  return_dbias=False):
+    """dQ, dK, dV (and the bias gradient) of L with dL/dO = dout, by the definition (fp64).
 
-    q, dout [B,Hq,Sq,D]; k, v [B,Hkv,Sk,D].  Per (b, h): P is the row softmax
-    of the masked scaled scores (hidden keys get exactly 0), O = P V, then
-    dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)), dQ = scale dS K,
-    dK = scale dS^T Q; dK and dV of a K/V head sum over its Hq/Hkv query heads.
-    Rows with no visible key contribute nothing.  Returns (dq, dk, dv).
+    q, dout [B,Hq,Sq,D]; k, v [B,Hkv,Sk,D]; bias None or [B or 1, Hq or 1,
+    Sq, Sk], added to the scaled scores as in sdpa_forward.  Per (b, h): P is
+    the row softmax of the masked biased scaled scores (hidden keys get
+    exactly 0), O = P V, then dV = P^T dO, dP = dO V^T, dS = P * (dP -
+    rowsum(dO * O)), dQ = scale dS K, dK = scale dS^T Q; dK and dV of a K/V
+    head sum over its Hq/Hkv query heads.  dS is the gradient of the biased
+    scores, so the gradient of a [B, Hq, Sq, Sk] bias is dS itself (a
+    broadcast bias would sum it over its size-1 axes).  Rows with no visible
+    key of finite weight (lse = -inf) contribute nothing.  Returns (dq, dk,
+    dv), or (dq, dk, dv, dbias [B, Hq, Sq, Sk]) with return_dbias.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -301,17 +307,19 @@ def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None):
     Sq = q.shape[2]
     if mask_kind & MASK_CAUSAL and Sq != Sk:
         raise ValueError("causal mask needs Sq == Sk")
+    bias = _check_bias(bias, B, Hq, Sq, Sk)
     G = Hq // Hkv
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    dbias = np.zeros((B, Hq, Sq, Sk)) if return_dbias else None
     rows = np.arange(Sq)
     for b in range(B):
         vis = visible_rows(mask_kind, rows, Sk, key_lens[b] if key_lens is not None else 0)
-        live = vis.any(axis=1)                 # rows with at least one visible key
         for h in range(Hq):
             g = h // G
-            _, _, p = attend(q[b, h], k[b, g], v[b, g], scale, vis)
+            _, lse, p = attend(q[b, h], k[b, g], v[b, g], scale, vis, bias_slice(bias, b, h))
+            live = np.isfinite(lse)            # rows with a visible key of finite weight
             p = np.where(live[:, None], p, 0.0)
             do = np.where(live[:, None], dout[b, h], 0.0)
             o = p @ v[b, g]
@@ -320,7 +328,9 @@ def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None):
             ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
             dq[b, h] = float(scale) * (ds @ k[b, g])
             dk[b, g] += float(scale) * (ds.T @ q[b, h])
-    return dq, dk, dv
+            if dbias is not None:
+                dbias[b, h] = ds
+    return (dq, dk, dv, dbias) if return_dbias else (dq, dk, dv)
 
 
 def split_heads(t, n_heads):

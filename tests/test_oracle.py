@@ -830,3 +830,72 @@ def test_golden_tensai_causal_mask():
     via_flag = O.sdpa_forward(q, k, v, 0.3, O.MASK_CAUSAL)
     via_bias = O.sdpa_forward(q, k, v, 0.3, O.MASK_NONE, bias=m[None, None])
     np.testing.assert_array_equal(via_bias, via_flag)
+
+
+# ------------------------------------------------------------------ backward with a bias
+
+def _loss_bias(q, k, v, g, scale, mask, lens, bias):
+    return float((O.sdpa_forward(q, k, v, scale, mask, lens, bias=bias) * g).sum())
+
+
+@pytest.mark.parametrize("mask,lens", [(O.MASK_NONE, None), (O.MASK_CAUSAL, None),
+                                       (O.MASK_KEY_PADDING, [4, 6])])
+def test_backward_bias_matches_finite_differences(mask, lens):
+    # central differences of L = sum(O * G) through the (pinned) biased
+    # forward, for q, k, v and every finite bias entry; some entries are -inf
+    rng = np.random.default_rng(66 + mask)
+    B, Hq, Hkv, S, D = 2, 4, 2, 6, 3
+    q, k, v = (rng.standard_normal((B, Hq, S, D)), rng.standard_normal((B, Hkv, S, D)),
+               rng.standard_normal((B, Hkv, S, D)))
+    g = rng.standard_normal((B, Hq, S, D))
+    bias = 1.5 * rng.standard_normal((B, Hq, S, S))
+    bias[0, 1, 2, [0, 3]] = -np.inf
+    bias[1, 3, 4, 1] = -np.inf
+    lens = None if lens is None else np.array(lens)
+    dq, dk, dv, db = O.sdpa_backward(q, k, v, g, 0.7, mask, lens, bias=bias, return_dbias=True)
+    h = 1e-6
+    args = {"q": q, "k": k, "v": v, "bias": bias}
+    for name, grad in (("q", dq), ("k", dk), ("v", dv), ("bias", db)):
+        x = args[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            if not np.isfinite(x[idx]):
+                continue
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = dict(args), dict(args)
+            ap[name], am[name] = xp, xm
+            num[idx] = (_loss_bias(ap["q"], ap["k"], ap["v"], g, 0.7, mask, lens, ap["bias"])
+                        - _loss_bias(am["q"], am["k"], am["v"], g, 0.7, mask, lens, am["bias"])) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=name)
+    # entries hidden by the -inf bias or the mask get no gradient
+    assert db[0, 1, 2, 0] == 0 and db[0, 1, 2, 3] == 0 and db[1, 3, 4, 1] == 0
+
+
+def test_backward_bias_rows_sum_to_zero_and_zero_bias():
+    rng = np.random.default_rng(69)
+    q, k, v = rng.standard_normal((2, 4, 30, 8)), rng.standard_normal((2, 2, 30, 8)), \
+        rng.standard_normal((2, 2, 30, 8))
+    g = rng.standard_normal((2, 4, 30, 8))
+    bias = rng.standard_normal((2, 4, 30, 30))
+    _, _, _, db = O.sdpa_backward(q, k, v, g, 0.3, O.MASK_CAUSAL, bias=bias, return_dbias=True)
+    # the softmax gradient of every row sums to zero (shift invariance)
+    assert np.abs(db.sum(axis=3)).max() < 1e-12
+    # a zero bias changes nothing, bit for bit
+    base = O.sdpa_backward(q, k, v, g, 0.3, O.MASK_CAUSAL)
+    zero = O.sdpa_backward(q, k, v, g, 0.3, O.MASK_CAUSAL, bias=np.zeros((1, 1, 30, 30)))
+    for a, b in zip(base, zero):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_backward_bias_dead_row_from_the_bias():
+    # a row whose visible keys all carry -inf bias has no output and no gradient
+    rng = np.random.default_rng(70)
+    q, k, v = rng.standard_normal((1, 2, 5, 4)), rng.standard_normal((1, 1, 5, 4)), \
+        rng.standard_normal((1, 1, 5, 4))
+    g = rng.standard_normal((1, 2, 5, 4))
+    bias = np.zeros((1, 2, 5, 5))
+    bias[0, 1, 3, :] = -np.inf
+    dq, dk, dv, db = O.sdpa_backward(q, k, v, g, 0.5, O.MASK_NONE, bias=bias, return_dbias=True)
+    assert (dq[0, 1, 3] == 0).all() and (db[0, 1, 3] == 0).all() and np.isfinite(dk).all()
