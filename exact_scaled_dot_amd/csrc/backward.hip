@@ -203,7 +203,10 @@ __device__ __forceinline__ int xcd_order(int total) {
 // heads of the group innermost; under a causal mask the longest blocks (the
 // last rows) first.
 // ---------------------------------------------------------------------------
-template <int D, class T, bool GEN = false>
+// BIAS: P is recomputed from the biased scores (exp2(s c + bias log2e -
+// lse2)); with a.dbias each lane also stores its dS words (the bias gradient)
+// and zero-fills the keys of its row that it never visits.
+template <int D, class T, bool GEN = false, bool BIAS = false>
 __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                                                                const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
@@ -279,6 +282,17 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
         }
     }
 
+    // Bias: a resource over this (batch, head)'s [Sq, Sk] slice (rows past
+    // Sq read as zeros); brow = byte offset of row qi.
+    const __amdgpu_buffer_rsrc_t rbias =
+        rsrc(BIAS ? static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh
+                  : static_cast<const uint16_t*>(a.q),
+             BIAS ? (uint32_t)a.Sq * a.Sk * 2 : 0u);
+    const uint32_t brow = (uint32_t)qi * a.Sk * 2;
+    uint16_t* const dbrow = (BIAS && a.dbias && qi < a.Sq)
+                                ? static_cast<uint16_t*>(a.dbias) + (bh * a.Sq + qi) * a.Sk
+                                : nullptr;
+
     const BwOffsets<D> off(wave, lane, DR);
     auto issue = [&](int j0, int stage) {
         const uint32_t bytes = (uint32_t)(a.Sk - j0) * DR * 2;
@@ -306,6 +320,15 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             const int kb0 = j0 + 32 * kb2;
             if (kb0 >= kv_lim || (a.causal && kb0 > qw + 31)) continue;  // wave-uniform
+            // bias of keys kb0 + 8g + 4hg .. +3 (registers 4g .. 4g+3), loaded
+            // ahead of the products
+            u32x2 bz[4];
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    bz[g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                          rbias, brow + (uint32_t)(kb0 + 8 * g + 4 * hg) * 2, 0, 0));
+            }
             f32x16 s = {}, dp = {};
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) {
@@ -316,14 +339,30 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
             uint32_t w[8];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                float p0 = fast_exp2(fmaf(s[r], c, -lse2));
-                float p1 = fast_exp2(fmaf(s[r + 1], c, -lse2));
+                float e0 = -lse2, e1 = -lse2;
+                if constexpr (BIAS) {
+                    const uint32_t bw2 = bz[r >> 2][(r & 3) >> 1];
+                    e0 = fmaf(bias_elem<T>(bw2, 0), kLog2e, e0);
+                    e1 = fmaf(bias_elem<T>(bw2, 1), kLog2e, e1);
+                }
+                float p0 = fast_exp2(fmaf(s[r], c, e0));
+                float p1 = fast_exp2(fmaf(s[r + 1], c, e1));
                 if (need_mask) {
                     const int key = kb0 + 8 * (r >> 2) + 4 * hg + (r & 3);
                     if (key >= kv_lim || (a.causal && key > qi)) p0 = 0.f;
                     if (key + 1 >= kv_lim || (a.causal && key + 1 > qi)) p1 = 0.f;
                 }
                 w[r >> 1] = pack2<T>(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
+            }
+            if constexpr (BIAS) {
+                // the bias gradient is dS: keys kb0 + 8g + 4hg .. +3 are words 2g, 2g+1
+                if (dbrow) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int key = kb0 + 8 * g + 4 * hg;
+                        if (key < a.Sk) *reinterpret_cast<u32x2*>(dbrow + key) = u32x2{w[2 * g], w[2 * g + 1]};
+                    }
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -354,6 +393,17 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
     for (int jt = 0; jt < ntiles; jt += 2) {
         step(jt, 0);
         if (jt + 1 < ntiles) step(jt + 1, 1);
+    }
+    if constexpr (BIAS) {
+        // The 32-key blocks this wave computed form a prefix of the row (the
+        // tile count, the key limit and the causal bound each cut it at a
+        // block edge); the rest of the row's bias gradient is 0.
+        if (dbrow) {
+            int kend = min(wave_tiles * kBwTile, (kv_lim + 31) / 32 * 32);
+            if (a.causal) kend = min(kend, qw + 32);
+            for (int key = max(kend, 0) + 4 * hg; key < a.Sk; key += 8)
+                *reinterpret_cast<u32x2*>(dbrow + key) = u32x2{0u, 0u};
+        }
     }
 
     // dQ = scale * (dS K): register r of d-block db holds dim
@@ -404,7 +454,10 @@ constexpr int kKvThreads = 512;  // 8 waves
 // the batch's limit get P = 0 here, so they add nothing.  Atomics count in
 // vmcnt on this GPU, so each step ends with vmcnt(0) and the tiles use two
 // LDS stages (loaded one step ahead) instead of three.
-template <int D, class T, bool GEN = false, bool DQ = false>
+// BIAS: the P role adds the bias of its 16 query rows at its key (2-byte
+// loads, issued ahead of the S product) before the exp, and hides keys past
+// the key limit itself (their bias may be anything).
+template <int D, class T, bool GEN = false, bool DQ = false, bool BIAS = false>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                                                                  const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
@@ -568,6 +621,19 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
             if (live) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
+                    // bias of rows q0 + 32qb + 8i + 4hg + j at key kj (rows past Sq read 0)
+                    float bb[16];
+                    if constexpr (BIAS) {
+                        const __amdgpu_buffer_rsrc_t rb =
+                            rsrc(static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + hstep * a.bias_sh,
+                                 (uint32_t)a.Sq * a.Sk * 2);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int q = q0 + 32 * qb + 8 * (r >> 2) + 4 * hg + (r & 3);
+                            bb[r] = half_to_float<T>(__builtin_amdgcn_raw_buffer_load_b16(
+                                rb, ((uint32_t)q * a.Sk + kj) * 2, 0, 0));
+                        }
+                    }
                     const f32x16 s = scores(qs, qb);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -578,9 +644,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                         float p[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            p[j] = fast_exp2(fmaf(s[4 * i + j], c, -l2[j]));
+                            const float e = BIAS ? fmaf(bb[4 * i + j], kLog2e, -l2[j]) : -l2[j];
+                            p[j] = fast_exp2(fmaf(s[4 * i + j], c, e));
                             if (mask) p[j] = kj > q0 + 32 * qb + 8 * i + 4 * hg + j ? 0.f : p[j];
-                            if (DQ) p[j] = kj >= kv_lim ? 0.f : p[j];  // dQ must not see them
+                            // dQ must not see them; with a bias they may be anything
+                            if (DQ || BIAS) p[j] = kj >= kv_lim ? 0.f : p[j];
                         }
                         pw[8 * qb + 2 * i] = pack2<T>(p[0], p[1]);
                         pw[8 * qb + 2 * i + 1] = pack2<T>(p[2], p[3]);
@@ -794,22 +862,28 @@ hipError_t launch_backward_atomic_d(const BackwardArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D, class T, bool GEN>
-hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
+template <int D, class T, bool GEN, bool BIAS>
+hipError_t launch_backward_db(const BackwardArgs& a, hipStream_t s) {
     const int nqb = (a.Sq + kBwRows - 1) / kBwRows;
     const int nkb = (a.Sk + kBwRows - 1) / kBwRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, T, GEN>), dim3(a.B * a.Hq * nqb), dim3(kBwThreads), 0, s, a,
-                       a.key_lens);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, GEN, BIAS>), dim3(a.B * a.Hq * nqb), dim3(kBwThreads), 0, s,
+                       a, a.key_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, GEN>), dim3(a.B * a.Hkv * nkb), dim3(kKvThreads), 0, s,
-                       a, a.key_lens);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, GEN, false, BIAS>), dim3(a.B * a.Hkv * nkb), dim3(kKvThreads),
+                       0, s, a, a.key_lens);
     return hipGetLastError();
+}
+
+template <int D, class T, bool GEN>
+hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
+    return a.bias ? launch_backward_db<D, T, GEN, true>(a, s) : launch_backward_db<D, T, GEN, false>(a, s);
 }
 
 template <class T>
 hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
-    if (a.dq_acc) {  // atomic dQ
+    if (a.dq_acc) {  // atomic dQ (no bias variant)
+        if (a.bias) return hipErrorInvalidValue;
         if (a.D == 128) return launch_backward_atomic_d<128, T, false>(a, s);
         if (a.D == 64) return launch_backward_atomic_d<64, T, false>(a, s);
         if (a.D < 64) return launch_backward_atomic_d<64, T, true>(a, s);

@@ -38,6 +38,12 @@ struct BackwardArgs {
     void* dv;
     float* delta;             // workspace [B, Hq, Sq]: rowsum(dO * O)
     float* dq_acc = nullptr;  // atomic variant: fp32 [B, Hq, Sq, D] dQ accumulator (workspace)
+    // Optional additive bias as in ForwardArgs (element (b, h, i, j) at
+    // bias[b * bias_sb + h * bias_sh + i * Sk + j]) and its gradient dS,
+    // dbias [B, Hq, Sq, Sk] (nullptr: not wanted).
+    const void* bias = nullptr;
+    int64_t bias_sb = 0, bias_sh = 0;
+    void* dbias = nullptr;
     int B, Hq, Hkv, Sq, Sk, D;
     float scale;
     bool causal;

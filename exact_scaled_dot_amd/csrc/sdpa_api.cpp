@@ -260,7 +260,8 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
                             int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
                             int mask_kind, const int32_t* key_lens, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes, int dtype, void* stream,
-                            bool atomic) {
+                            bool atomic, const void* bias = nullptr, int64_t bias_sb = 0,
+                            int64_t bias_sh = 0, void* dbias = nullptr) {
     if (!out || !dout || !lse || !dk || !dv)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     int64_t qbytes = 0, kbytes = 0;
@@ -293,10 +294,39 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
         const void* p;
         int64_t n;
     };
+    // Bias (as sdpa_forward_bias) and its gradient [B, Hq, Sq, Sk].
+    int64_t bbytes = 0, dbbytes = 0;
+    if (bias) {
+        if (bias_sb < 0 || bias_sh < 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "bias strides must be >= 0");
+        if (Sk % 8 != 0 || bias_sb % 8 != 0 || bias_sh % 8 != 0 ||
+            reinterpret_cast<uintptr_t>(bias) % 16 != 0)
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "bias rows must be 16-byte aligned (Sk and the strides multiples of 8, "
+                        "pointer 16-byte aligned)");
+        if (Sq * Sk * 2 > INT_MAX)
+            return fail(SDPA_ERR_UNSUPPORTED, "one head's bias exceeds 2 GiB");
+        int64_t last = 0, hext = 0;
+        if (!mul_ok(B - 1, bias_sb, &last) || !mul_ok(Hq - 1, bias_sh, &hext) ||
+            __builtin_add_overflow(last, hext, &last) || __builtin_add_overflow(last, Sq * Sk, &last) ||
+            last > INT64_MAX / 2)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "bias extent overflows");
+        bbytes = last * 2;
+        if (dbias) {
+            if (reinterpret_cast<uintptr_t>(dbias) % 16 != 0)
+                return fail(SDPA_ERR_UNSUPPORTED, "dbias must be 16-byte aligned");
+            const int64_t n = numel4(B, Hq, Sq, Sk);
+            if (n < 0 || n > INT64_MAX / 2) return fail(SDPA_ERR_INVALID_ARGUMENT, "dbias size overflows");
+            dbbytes = n * 2;
+        }
+    } else if (dbias) {
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "dbias needs a bias");
+    }
     const Span ins[] = {{q, qbytes}, {k, kbytes}, {v, kbytes}, {out, qbytes},
-                        {dout, qbytes}, {lse, lbytes}, {key_lens, kl}};
-    const Span outs[] = {{dq, qbytes}, {dk, kbytes}, {dv, kbytes}, {workspace, (int64_t)need}};
-    for (int i = 0; i < 4; ++i) {
+                        {dout, qbytes}, {lse, lbytes}, {key_lens, kl}, {bias, bbytes}};
+    const Span outs[] = {{dq, qbytes}, {dk, kbytes}, {dv, kbytes}, {workspace, (int64_t)need},
+                         {dbias, dbbytes}};
+    for (int i = 0; i < 5; ++i) {
         for (const Span& x : ins)
             if (overlap(outs[i].p, outs[i].n, x.p, x.n))
                 return fail(SDPA_ERR_INVALID_ARGUMENT, "an output or the workspace overlaps an input");
@@ -332,6 +362,10 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
     a.scale = scale;
     a.causal = causal;
     a.padded = padded;
+    a.bias = bias;
+    a.bias_sb = bias_sb;
+    a.bias_sh = bias_sh;
+    a.dbias = dbias;
     (void)hipGetLastError();
     return hip_status(sdpa::launch_backward_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream)),
                       "sdpa_backward launch");
@@ -348,6 +382,19 @@ sdpa_status_t sdpa_backward(const void* q, const void* k, const void* v, const v
                             void* workspace, size_t workspace_bytes, int dtype, void* stream) {
     return backward_impl(q, k, v, out, dout, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens,
                          dq, dk, dv, workspace, workspace_bytes, dtype, stream, false);
+}
+
+sdpa_status_t sdpa_backward_bias(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const float* lse, int64_t B, int64_t Hq,
+                                 int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                                 int mask_kind, const int32_t* key_lens, const void* bias,
+                                 int64_t bias_stride_b, int64_t bias_stride_h, void* dq, void* dk,
+                                 void* dv, void* dbias, void* workspace, size_t workspace_bytes,
+                                 int dtype, void* stream) {
+    if (!bias) return fail(SDPA_ERR_INVALID_ARGUMENT, "null bias pointer");
+    return backward_impl(q, k, v, out, dout, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, key_lens,
+                         dq, dk, dv, workspace, workspace_bytes, dtype, stream, false, bias,
+                         bias_stride_b, bias_stride_h, dbias);
 }
 
 size_t sdpa_backward_atomic_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t D) {

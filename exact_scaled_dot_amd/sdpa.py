@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so"
 
 EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_bias", "sdpa_backward",
             "sdpa_backward_workspace_size", "sdpa_backward_atomic",
-            "sdpa_backward_atomic_workspace_size", "sdpa_block_forward",
+            "sdpa_backward_atomic_workspace_size", "sdpa_backward_bias", "sdpa_block_forward",
             "sdpa_block_workspace_size",
             "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
             "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
@@ -69,6 +69,10 @@ def load_library():
                                   ctypes.c_float, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, i32, vp]
     lib.sdpa_backward_atomic.restype = i32
     lib.sdpa_backward_atomic.argtypes = lib.sdpa_backward.argtypes
+    lib.sdpa_backward_bias.restype = i32
+    lib.sdpa_backward_bias.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_float, i32, vp, vp, i64, i64, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, i32, vp]
     lib.sdpa_backward_atomic_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_backward_atomic_workspace_size.argtypes = [i64, i64, i64, i64]
     lib.sdpa_block_workspace_size.restype = ctypes.c_size_t
@@ -194,6 +198,20 @@ def sdpa_forward_lse(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None, out=Non
     return out, lse
 
 
+def _bias_strides(bias, q, B, Hq, Sq, Sk):
+    """Validate a [B or 1, Hq or 1, Sq, Sk] bias; its batch and head strides (0 if broadcast)."""
+    if not isinstance(bias, torch.Tensor) or bias.dim() != 4 or not bias.is_cuda:
+        raise ValueError("bias must be a 4-D device tensor")
+    if bias.dtype != q.dtype:
+        raise TypeError("bias must have q's dtype")
+    if (bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq)
+            or tuple(bias.shape[2:]) != (Sq, Sk)):
+        raise ValueError("bias must be [B or 1, Hq or 1, Sq, Sk]")
+    if bias.stride(3) != 1 or bias.stride(2) != Sk:
+        raise ValueError("bias rows must be contiguous (stride Sk between rows)")
+    return (bias.stride(0) if bias.shape[0] > 1 else 0, bias.stride(1) if bias.shape[1] > 1 else 0)
+
+
 def sdpa_forward_bias(q, k, v, bias, scale, mask_kind=MASK_NONE, key_lens=None, out=None,
                       lse=None, stream=None):
     """O = softmax(Q K^T * scale + bias + mask) V.
@@ -204,17 +222,7 @@ def sdpa_forward_bias(q, k, v, bias, scale, mask_kind=MASK_NONE, key_lens=None, 
     (out, lse) when lse is requested.
     """
     B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
-    if not isinstance(bias, torch.Tensor) or bias.dim() != 4 or not bias.is_cuda:
-        raise ValueError("bias must be a 4-D device tensor")
-    if bias.dtype != q.dtype:
-        raise TypeError("bias must have q's dtype")
-    if (bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq)
-            or tuple(bias.shape[2:]) != (Sq, Sk)):
-        raise ValueError("bias must be [B or 1, Hq or 1, Sq, Sk]")
-    if bias.stride(3) != 1 or bias.stride(2) != Sk:
-        raise ValueError("bias rows must be contiguous (stride Sk between rows)")
-    sb = bias.stride(0) if bias.shape[0] > 1 else 0
-    sh = bias.stride(1) if bias.shape[1] > 1 else 0
+    sb, sh = _bias_strides(bias, q, B, Hq, Sq, Sk)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -241,6 +249,53 @@ def sdpa_backward_workspace_size(B, Hq, Sq):
 
 def sdpa_backward_atomic_workspace_size(B, Hq, Sq, D):
     return int(load_library().sdpa_backward_atomic_workspace_size(B, Hq, Sq, D))
+
+
+def sdpa_backward_bias(q, k, v, out, dout, lse, bias, scale, mask_kind=MASK_NONE, key_lens=None,
+                       dbias=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv, dbias) of O = softmax(Q K^T * scale + bias + mask) V given dout.
+
+    out and lse are sdpa_forward_bias's with the same bias.  dbias: None (not
+    computed), True (allocated), or a [B, Hq, Sq, Sk] tensor in q's dtype; it
+    is dS per (batch, query head) and is returned as the fourth value (None
+    when not computed).
+    """
+    B, Hq, Hkv, Sq, Sk, D = _check_qkv(q, k, v, key_lens)
+    sb, sh = _bias_strides(bias, q, B, Hq, Sq, Sk)
+    for name, t in (("out", out), ("dout", dout)):
+        _check_tensor(name, t, 4)
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("%s must match q in shape and dtype" % name)
+    _check_tensor("lse", lse, 3)
+    if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Sq]")
+    if dbias is True:
+        dbias = torch.empty((B, Hq, Sq, Sk), dtype=q.dtype, device=q.device)
+    elif dbias is not None:
+        _check_tensor("dbias", dbias, 4)
+        if tuple(dbias.shape) != (B, Hq, Sq, Sk) or dbias.dtype != q.dtype:
+            raise ValueError("dbias must be [B, Hq, Sq, Sk] in q's dtype")
+    outs = []
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _check_tensor(name, t, 4)
+            if t.shape != like.shape or t.dtype != like.dtype:
+                raise ValueError("%s must match its input in shape and dtype" % name)
+        outs.append(t)
+    dq, dk, dv = outs
+    need = sdpa_backward_workspace_size(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check(lib.sdpa_backward_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                  B, Hq, Hkv, Sq, Sk, D, float(scale), int(mask_kind),
+                                  _ptr(key_lens), _ptr(bias), sb, sh, _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(dbias), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _dtype_code(q),
+                                  _stream(stream)))
+    return dq, dk, dv, dbias
 
 
 def sdpa_backward(q, k, v, out, dout, lse, scale, mask_kind=MASK_NONE, key_lens=None,

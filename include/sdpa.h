@@ -180,6 +180,31 @@ sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const v
                             void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
 /*
+ * The backward of sdpa_forward_bias (tensai guide, "Attention の組み立て":
+ * the additive mask enters after Scale, before Softmax): dq, dk, dv as
+ * sdpa_backward with P recomputed from the biased scores, and optionally the
+ * bias gradient, which is dS = P o (dP - rowsum(dO o O)) itself.
+ *   lse        device float [B, Hq, Sq] from sdpa_forward_bias with this bias
+ *   bias, bias_stride_b, bias_stride_h   as in sdpa_forward_bias
+ *   dbias      NULL, or device [B, Hq, Sq, Sk], dtype, 16-byte aligned:
+ *              written completely (0 at hidden keys); for a bias broadcast
+ *              over batch or heads the caller sums it over those axes
+ * Every other argument as sdpa_backward (same workspace size).  The bias is
+ * read by both passes; dbias is written by the query-parallel one.  Outputs
+ * and workspace must not overlap each other or any input.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128, bias
+ * rows 16-byte aligned (Sk and the strides multiples of 8), one head's bias
+ * (Sq * Sk elements) under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
+ */
+sdpa_status_t sdpa_backward_bias(const void *q, const void *k, const void *v, const void *out,
+                                 const void *dout, const float *lse,
+                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                                 int64_t D, float scale, int mask_kind, const int32_t *key_lens,
+                                 const void *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                                 void *dq, void *dk, void *dv, void *dbias,
+                                 void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/*
  * Bytes of device workspace sdpa_backward_atomic needs (0 if the sizes are
  * invalid): the row statistics of sdpa_backward_workspace_size, then an fp32
  * dQ accumulator [B, Hq, Sq, D], each section 256-byte aligned.

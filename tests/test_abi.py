@@ -373,3 +373,34 @@ def test_block_workspace_size():
     assert lib.sdpa_block_workspace_size(1, 3, 8) == 4 * 256
     assert lib.sdpa_block_workspace_size(0, 3, 8) == 0
     assert lib.sdpa_block_workspace_size(1, 3, -8) == 0
+
+
+def bwdb(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128,
+         scale=0.125, mask=0, key_lens=None, bias=ctypes.c_void_p(0x7a000000), sb=0, sh=128 * 128,
+         dq=ctypes.c_void_p(0x50000000), dk=ctypes.c_void_p(0x52000000),
+         dv=ctypes.c_void_p(0x54000000), dbias=None, ws=ctypes.c_void_p(0x56000000),
+         ws_bytes=1 << 20, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    return lib.sdpa_backward_bias(q, FAKE_K, FAKE_V, out, dout, lse, B, Hq, Hkv, Sq, Sk, D, scale,
+                                  mask, key_lens, bias, sb, sh, dq, dk, dv, dbias, ws, ws_bytes,
+                                  dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(bias=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null bias"),
+    (dict(dout=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),
+    (dict(sb=-8), sd.SDPA_ERR_INVALID_ARGUMENT, "strides"),
+    (dict(sh=12), sd.SDPA_ERR_UNSUPPORTED, "16-byte aligned"),
+    (dict(Sq=120, Sk=124), sd.SDPA_ERR_UNSUPPORTED, "16-byte aligned"),
+    (dict(bias=ctypes.c_void_p(0x7a000008)), sd.SDPA_ERR_UNSUPPORTED, "16-byte aligned"),
+    (dict(dbias=ctypes.c_void_p(0x5a000004)), sd.SDPA_ERR_UNSUPPORTED, "dbias must be 16-byte"),
+    (dict(Sq=46341, Sk=46344, ws_bytes=1 << 30), sd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(ws_bytes=16), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(dbias=ctypes.c_void_p(0x7a000000 + 4096)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(dq=ctypes.c_void_p(0x7a000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap"),
+])
+def test_backward_bias_rejects(kw, status, needle):
+    assert bwdb(**kw) == status
+    assert needle in sd.last_error()
