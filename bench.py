@@ -12,7 +12,9 @@ resident in HBM:
     as whole-sequence chunks over such a cache
   * the attention backward (dQ, dK, dV) of the causal prefill workload, from
     its forward output and log-sum-exp (computed once, before the timing),
-    with the ordered reduction and with the atomic-dQ one
+    with the ordered reduction and with the atomic-dQ one, and the same
+    backward with the per-head bias below, which also writes the bias
+    gradient [4, 16, 4096, 4096] bf16 in full
   * the causal prefill with a general additive mask: a per-head bias tensor
     [1, 16, 4096, 4096] bf16 added to the scaled scores
   * the causal prefill with 256-wide heads, bf16, B=4 Hq=Hkv=8 S=4096 D=256
@@ -84,6 +86,12 @@ def stored_traffic(workload, source):
 def backward_traffic():
     """HBM bytes of one backward call (both passes), if both records are valid."""
     parts = [stored_traffic(k, "backward.hip") for k in ("backward_dq", "backward_dkdv")]
+    return None if None in parts else sum(parts)
+
+
+def bias_backward_traffic():
+    """HBM bytes of one backward-with-bias call (both passes), if both records are valid."""
+    parts = [stored_traffic(k, "backward.hip") for k in ("backward_bias_dq", "backward_bias_dkdv")]
     return None if None in parts else sum(parts)
 
 
@@ -180,11 +188,11 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     if fwd in fetch:
         # a full step launches, in order: the causal prefill, the padded one,
         # the paged one, the bias prefill, the wide-head prefill, the large
-        # block's attention and the small block's (after one setup forward
-        # that gives the backward its output and lse)
+        # block's attention and the small block's (after the setup forwards
+        # that give the two backward legs their output and lse)
         fr, wr = fetch[fwd], write[fwd]
-        if len(fr) % 7 == 1:
-            fr, wr = fr[1:], wr[1:]
+        setup = len(fr) % 7        # the backward legs' setup forwards come first
+        fr, wr = fr[setup:], wr[setup:]
         for i, key in enumerate(("prefill", "padded", "paged_prefill", "bias", "wide", "block_attn",
                                  "block_small_attn")):
             out[key] = entry(fwd, "forward.hip", fr[i::7], wr[i::7])
@@ -195,16 +203,16 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     if gm in fetch:
         for i, key in enumerate(("block_qkv", "block_out", "block_small_qkv", "block_small_out")):
             out[key] = entry(gm, "gemm.hip", fetch[gm][i::4], write[gm][i::4])
-    if "bwd_dq_kernel" in fetch:
-        out["backward_dq"] = entry("bwd_dq_kernel", "backward.hip", fetch["bwd_dq_kernel"],
-                                   write["bwd_dq_kernel"])
+    # A full step runs the ordered backward, the atomic one and the one with a
+    # bias, in that order: their dQ and dK/dV dispatches interleave.
+    dq = "bwd_dq_kernel"
+    if dq in fetch:
+        out["backward_dq"] = entry(dq, "backward.hip", fetch[dq][0::2], write[dq][0::2])
+        out["backward_bias_dq"] = entry(dq, "backward.hip", fetch[dq][1::2], write[dq][1::2])
     dk = "bwd_dkdv_kernel"
     if dk in fetch:
-        if "bwd_prep_kernel" in fetch:  # ordered and atomic passes alternate
-            out["backward_dkdv"] = entry(dk, "backward.hip", fetch[dk][0::2], write[dk][0::2])
-            out["backward_atomic_dkdv"] = entry(dk, "backward.hip", fetch[dk][1::2], write[dk][1::2])
-        else:
-            out["backward_dkdv"] = entry(dk, "backward.hip", fetch[dk], write[dk])
+        for i, key in enumerate(("backward_dkdv", "backward_atomic_dkdv", "backward_bias_dkdv")):
+            out[key] = entry(dk, "backward.hip", fetch[dk][i::3], write[dk][i::3])
     for key, name in (("backward_atomic_prep", "bwd_prep_kernel"),
                       ("backward_atomic_convert", "bwd_dq_convert_kernel")):
         if name in fetch:
@@ -228,7 +236,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward", "backward_atomic", "bias", "wide",
+                                       "backward", "backward_atomic", "backward_bias", "bias",
+                                       "wide",
                                        "decode_wide", "block", "block_small"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
@@ -301,9 +310,22 @@ def main():
                                  dtype=torch.uint8, device=dev)}
     # Bias: the causal prefill workload with a per-head [1, Hq, Sq, Sk] bias.
     ibias = None
-    if args.only in (None, "bias"):
+    if args.only in (None, "bias", "backward_bias"):
         ibias = {"bias": draw_bias((1, wp.Hq, wp.Sq, wp.Sk), wp.dtype, wp.seed, dev),
                  "out": torch.empty_like(ip["q"])}
+    # Backward with that bias: output and lse from one biased forward here,
+    # the bias gradient [B, Hq, Sq, Sk] written in full by every call.
+    ibb = None
+    if args.only in (None, "backward_bias"):
+        out_bb, lse_bb = sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
+                                              sd.MASK_CAUSAL, None, lse=True)
+        ibb = {"out": out_bb, "lse": lse_bb,
+               "dout": draw_grad(tuple(ip["q"].shape), wp.dtype, wp.seed, dev),
+               "dq": torch.empty_like(ip["q"]), "dk": torch.empty_like(ip["k"]),
+               "dv": torch.empty_like(ip["v"]),
+               "dbias": torch.empty((wp.B, wp.Hq, wp.Sq, wp.Sk), dtype=wp.dtype, device=dev),
+               "ws": torch.empty(sd.sdpa_backward_workspace_size(wp.B, wp.Hq, wp.Sq),
+                                 dtype=torch.uint8, device=dev)}
     # Wide heads: the causal prefill's token count and model width in 8 heads
     # of 256.
     iwide = None
@@ -351,6 +373,9 @@ def main():
     calls["backward_atomic"] = lambda: sd.sdpa_backward(
         ip["q"], ip["k"], ip["v"], ibw["out"], ibw["dout"], ibw["lse"], wp.scale, sd.MASK_CAUSAL,
         None, ibw["dq"], ibw["dk"], ibw["dv"], ibw["ws"], atomic=True)
+    calls["backward_bias"] = lambda: sd.sdpa_backward_bias(
+        ip["q"], ip["k"], ip["v"], ibb["out"], ibb["dout"], ibb["lse"], ibias["bias"], wp.scale,
+        sd.MASK_CAUSAL, None, ibb["dbias"], ibb["dq"], ibb["dk"], ibb["dv"], ibb["ws"])
     calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
                                                  sd.MASK_CAUSAL, None, ibias["out"])
     calls["decode_wide"] = lambda: sd.sdpa_decode(idw["q"], idw["k"], idw["v"],
@@ -364,7 +389,7 @@ def main():
             *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "bias", "wide", "decode_wide", "block", "block_small"])
+              "backward_bias", "bias", "wide", "decode_wide", "block", "block_small"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -486,6 +511,22 @@ def main():
                                                "kernel": "bwd_prep + bwd_dkdv<128, atomic dQ> + "
                                                          "bwd_dq_convert",
                                                "flops_per_launch": fl}}
+    if "backward_bias" in ms:
+        fl = 2.5 * formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
+        tf = fl / (ms["backward_bias"] * 1e-3) / 1e12
+        dbias_bytes = wp.B * wp.Hq * wp.Sq * wp.Sk * 2
+        rec["backward_bias"] = {"workload": "bf16_causal_backward_bias_b4_h16_s4096_d128",
+                                "ms": round(ms["backward_bias"], 4), "value": round(tf, 3),
+                                "unit": "TFLOP/s", "bias_shape": [1, wp.Hq, wp.Sq, wp.Sk],
+                                "dbias_shape": [wp.B, wp.Hq, wp.Sq, wp.Sk],
+                                "dbias_bytes_written": dbias_bytes,
+                                "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                             "traffic": bias_backward_traffic(),
+                                             "kernel": "bwd_dq_kernel<128, bias> + "
+                                                       "bwd_dkdv_kernel<128, bias>",
+                                             "flops_per_launch": fl}}
     if "bias" in ms:
         fl = formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
         tf = fl / (ms["bias"] * 1e-3) / 1e12
@@ -554,6 +595,9 @@ def main():
         elif "bias" in rec:
             rec.update({"value": rec["bias"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["bias"]["workload"]}
+        elif "backward_bias" in rec:
+            rec.update({"value": rec["backward_bias"]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec["backward_bias"]["workload"]}
         elif "backward_atomic" in rec:
             rec.update({"value": rec["backward_atomic"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["backward_atomic"]["workload"]}
@@ -573,7 +617,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw, ibias, iblk, iwide, idw
+    del ip, ig, idd, ipg, ipp, ibw, ibias, ibb, iblk, iwide, idw
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

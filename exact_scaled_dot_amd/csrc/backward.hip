@@ -73,6 +73,10 @@ __device__ __forceinline__ void lds_st4(uint32_t* __restrict__ p, u32x4 v) {
 __device__ __forceinline__ void lds_st2(uint16_t* __restrict__ p, u32x2 v) {
     *(__attribute__((address_space(3))) u32x2*)((__attribute__((address_space(3))) char*)p) = v;
 }
+__device__ __forceinline__ u32x2 lds_ld2(const uint16_t* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) u32x2*)(
+        (const __attribute__((address_space(3))) char*)p);
+}
 __device__ __forceinline__ u32x4 lds_ld4(const uint32_t* __restrict__ p) {
     return *(const __attribute__((address_space(3))) u32x4*)(
         (const __attribute__((address_space(3))) char*)p);
@@ -204,14 +208,25 @@ __device__ __forceinline__ int xcd_order(int total) {
 // last rows) first.
 // ---------------------------------------------------------------------------
 // BIAS: P is recomputed from the biased scores (exp2(s c + bias log2e -
-// lse2)); with a.dbias each lane also stores its dS words (the bias gradient)
-// and zero-fills the keys of its row that it never visits.
+// lse2)).  Each wave moves its [32 query x 32 key] block of the bias, and of
+// the bias gradient dS, through a 2-KB LDS staging region per block: HBM
+// sees 64-byte row pieces (16 rows per instruction) while the products see
+// one query row per lane.  The bias of block b of tile jt+1 is loaded into
+// registers before block b of tile jt computes; after it, that block's dS
+// is read back row-major and stored (issued after the step's loads, so the
+// step's wait leaves the stores in flight), and the loaded bias takes its
+// place.  Keys a wave never visits get their (zero) gradient after the loop.
+// Staging layout: row r (a query of the wave) holds 8 units of 4 keys;
+// logical unit u sits at unit u ^ ((r >> 2) & 7), which keeps both the
+// per-lane 8-byte accesses (32 rows, one unit) and the row-major 16-byte
+// ones (4 rows, 4 chunks) free of bank conflicts.
 template <int D, class T, bool GEN = false, bool BIAS = false>
 __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                                                                const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
-    // Stage s: K tile at 2*s*TILE, V tile at (2*s+1)*TILE.
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE];
+    // Stage s: K tile at 2*s*TILE, V tile at (2*s+1)*TILE; (BIAS) then two
+    // 1024-element staging regions per wave.
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * L::TILE + (BIAS ? 4 * 2048 : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,16 +297,50 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
         }
     }
 
-    // Bias: a resource over this (batch, head)'s [Sq, Sk] slice (rows past
-    // Sq read as zeros); brow = byte offset of row qi.
+    // Bias and bias gradient: resources over this (batch, head)'s [Sq, Sk]
+    // slices (out-of-range offsets read 0 / are dropped).  Row-major staging
+    // access i of lane l: row 16i + l/4 of the wave, keys 8*(l%4) .. +7 of
+    // the block (stored chunk cs, halves swapped when sw).
+    const bool DB = BIAS && a.dbias != nullptr;
+    uint16_t* const stg = smem + 4 * L::TILE + 2048 * wave;
     const __amdgpu_buffer_rsrc_t rbias =
         rsrc(BIAS ? static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh
                   : static_cast<const uint16_t*>(a.q),
              BIAS ? (uint32_t)a.Sq * a.Sk * 2 : 0u);
-    const uint32_t brow = (uint32_t)qi * a.Sk * 2;
-    uint16_t* const dbrow = (BIAS && a.dbias && qi < a.Sq)
-                                ? static_cast<uint16_t*>(a.dbias) + (bh * a.Sq + qi) * a.Sk
-                                : nullptr;
+    const __amdgpu_buffer_rsrc_t rdb =
+        rsrc(DB ? static_cast<uint16_t*>(a.dbias) + bh * a.Sq * a.Sk : a.q, DB ? (uint32_t)a.Sq * a.Sk * 2 : 0u);
+    const int crow = lane >> 2, cchk = lane & 3;
+    auto stg_at = [&](int kb2, int i) {  // staging element offset of row-major access i
+        const int r = 16 * i + crow, x = (r >> 2) & 7;
+        return 1024 * kb2 + r * 32 + ((cchk ^ (x >> 1)) * 8);
+    };
+    auto swapped = [&](u32x4 v, int i) {  // logical <-> stored order of a chunk
+        return (((16 * i + crow) >> 2) & 1) ? u32x4{v[2], v[3], v[0], v[1]} : v;
+    };
+    // global byte offset of row-major access i of the block at key kb0
+    auto gofs = [&](int kb0, int i) -> uint32_t {
+        const int row = qw + 16 * i + crow, key = kb0 + 8 * cchk;
+        return (row < a.Sq && key < a.Sk) ? ((uint32_t)row * a.Sk + key) * 2 : kOutside;
+    };
+    u32x4 bl[2];  // bias of one block of the next tile, row-major
+    auto load_bias = [&](int kb0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) bl[i] = __builtin_amdgcn_raw_buffer_load_b128(rbias, gofs(kb0, i), 0, 0);
+    };
+    auto put_bias = [&](int kb2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_st4(reinterpret_cast<uint32_t*>(stg + stg_at(kb2, i)), swapped(bl[i], i));
+    };
+    // dS of the block at key kb0 (staging region kb2), or zeros, to the bias gradient
+    auto flush = [&](int kb2, int kb0, bool zero) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 v = zero ? u32x4{0u, 0u, 0u, 0u} : swapped(lds_row(stg + stg_at(kb2, i)), i);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rdb, gofs(kb0, i), 0, 0);
+        }
+    };
+    // per-lane staging offsets: row l32, logical unit 2g + hg of region kb2
+    auto stg_unit = [&](int kb2, int g) { return 1024 * kb2 + l32 * 32 + (((2 * g + hg) ^ ((l32 >> 2) & 7)) * 4); };
 
     const BwOffsets<D> off(wave, lane, DR);
     auto issue = [&](int j0, int stage) {
@@ -319,21 +368,29 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             const int kb0 = j0 + 32 * kb2;
-            if (kb0 >= kv_lim || (a.causal && kb0 > qw + 31)) continue;  // wave-uniform
-            // bias of keys kb0 + 8g + 4hg .. +3 (registers 4g .. 4g+3), loaded
-            // ahead of the products
-            u32x2 bz[4];
-            if constexpr (BIAS) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    bz[g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                          rbias, brow + (uint32_t)(kb0 + 8 * g + 4 * hg) * 2, 0, 0));
+            const bool more = BIAS && j0 + kBwTile < wave_tiles * kBwTile;  // a next tile to stage
+            if (kb0 >= kv_lim || (a.causal && kb0 > qw + 31)) {  // wave-uniform
+                // every key of the block is hidden: dS = 0
+                if (DB) flush(kb2, kb0, true);
+                if (more) {
+                    load_bias(kb0 + kBwTile);
+                    put_bias(kb2);
+                }
+                continue;
             }
+            if (more) load_bias(kb0 + kBwTile);
             f32x16 s = {}, dp = {};
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) {
                 s = mfma_32x32x16<T>(lds_row(ks + 32 * kb2 * D + off.row[k]), qr[k], s);
                 dp = mfma_32x32x16<T>(lds_row(vs + 32 * kb2 * D + off.row[k]), dr[k], dp);
+            }
+            // bias of keys kb0 + 8g + 4hg .. +3 (registers 4g .. 4g+3), read
+            // after the products (fewer registers live across them)
+            u32x2 bz[4];
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) bz[g] = lds_ld2(stg + stg_unit(kb2, g));
             }
             const bool need_mask = kb0 + 32 > kv_lim || (a.causal && kb0 + 31 > qw);
             uint32_t w[8];
@@ -354,16 +411,13 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                 }
                 w[r >> 1] = pack2<T>(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
             }
-            if constexpr (BIAS) {
+            if (DB) {
                 // the bias gradient is dS: keys kb0 + 8g + 4hg .. +3 are words 2g, 2g+1
-                if (dbrow) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int key = kb0 + 8 * g + 4 * hg;
-                        if (key < a.Sk) *reinterpret_cast<u32x2*>(dbrow + key) = u32x2{w[2 * g], w[2 * g + 1]};
-                    }
-                }
+                for (int g = 0; g < 4; ++g) lds_st2(stg + stg_unit(kb2, g), u32x2{w[2 * g], w[2 * g + 1]});
+                flush(kb2, kb0, false);
             }
+            if (more) put_bias(kb2);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const u32x4 bw = {w[4 * kk], w[4 * kk + 1], w[4 * kk + 2], w[4 * kk + 3]};
@@ -379,30 +433,43 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
     };
 
     if (ntiles > 0) issue(0, 0);
+    if (BIAS && wave_tiles > 0) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            load_bias(32 * kb2);
+            put_bias(kb2);
+        }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     // Tile jt sits in stage jt % 2; the next one is loaded into the other
-    // stage meanwhile (it was last read before the previous barrier).
+    // stage meanwhile (it was last read before the previous barrier).  A
+    // computing wave's last VMEM operations of a step are its 2 bias-gradient
+    // stores of the last block (when DB); vmcnt counts in issue order, so
+    // vmcnt(2) has every load of the step landed and leaves them in flight.
     auto step = [&](int jt, const int cur) __attribute__((always_inline)) {
         if (jt + 1 < ntiles) issue((jt + 1) * kBwTile, cur ^ 1);
         if (jt < wave_tiles)
             compute(smem + 2 * cur * L::TILE, smem + (2 * cur + 1) * L::TILE, jt * kBwTile);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (DB && jt < wave_tiles) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
     for (int jt = 0; jt < ntiles; jt += 2) {
         step(jt, 0);
         if (jt + 1 < ntiles) step(jt + 1, 1);
     }
-    if constexpr (BIAS) {
-        // The 32-key blocks this wave computed form a prefix of the row (the
-        // tile count, the key limit and the causal bound each cut it at a
-        // block edge); the rest of the row's bias gradient is 0.
-        if (dbrow) {
-            int kend = min(wave_tiles * kBwTile, (kv_lim + 31) / 32 * 32);
-            if (a.causal) kend = min(kend, qw + 32);
-            for (int key = max(kend, 0) + 4 * hg; key < a.Sk; key += 8)
-                *reinterpret_cast<u32x2*>(dbrow + key) = u32x2{0u, 0u};
+    if (DB && qw < a.Sq) {
+        // zeros for every key past the computed tiles (all hidden): 8 rows of
+        // 128 bytes per store
+        for (int j0 = wave_tiles * kBwTile; j0 < a.Sk; j0 += kBwTile) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = qw + 8 * i + (lane >> 3), key = j0 + 8 * (lane & 7);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{0u, 0u, 0u, 0u}, rdb,
+                    (row < a.Sq && key < a.Sk) ? ((uint32_t)row * a.Sk + key) * 2 : kOutside, 0, 0);
+            }
         }
     }
 
@@ -454,9 +521,14 @@ constexpr int kKvThreads = 512;  // 8 waves
 // the batch's limit get P = 0 here, so they add nothing.  Atomics count in
 // vmcnt on this GPU, so each step ends with vmcnt(0) and the tiles use two
 // LDS stages (loaded one step ahead) instead of three.
-// BIAS: the P role adds the bias of its 16 query rows at its key (2-byte
-// loads, issued ahead of the S product) before the exp, and hides keys past
-// the key limit itself (their bias may be anything).
+// BIAS: the P role adds the bias of its query rows at its key before the
+// exp, and hides keys past the key limit itself (their bias may be anything).
+// The bias of a step ([64 queries x the block's 128 keys], the layout of a
+// 128-wide tile) comes into a two-slot LDS ring by DMA: the bias of step
+// st+2 goes into the slot of step st as soon as the P hand-over barrier of
+// step st has passed (role P reads the bias only before it), so each load
+// has a step and a half to land.  A transposed read then gives a lane its
+// key at 4 consecutive query rows.
 template <int D, class T, bool GEN = false, bool DQ = false, bool BIAS = false>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                                                                  const int32_t* __restrict__ key_lens) {
@@ -474,7 +546,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     constexpr int EX = NSTG * STAGE;
     constexpr int DSX = EX + 4 * 64 * 32;
     constexpr int KB = DSX + 4 * 32 * 64;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[DQ ? KB + kBwRows * D : DSX];
+    constexpr int BT = kBwTile * kBwRows;  // (BIAS) one bias slot, after the hand-over
+    static_assert(!(DQ && BIAS), "the atomic variant takes no bias");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[DQ ? KB + kBwRows * D : DSX + (BIAS ? 2 * BT : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -540,6 +614,39 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         const int s = 64 * (DMA * wave + i) + lane;
         const int r = s / L::CPR, c = (s % L::CPR) ^ L::f(r);  // logical chunk
         dmo[i] = 8 * c < DR ? (uint32_t)r * DR * 2 + (uint32_t)(c * 16) : kOutside;
+    }
+
+    // Bias DMA: 2 loads per wave fill slot s = 64*(2*wave + i) + lane of a
+    // 128-wide tile: row s / 16 (a query), stored chunk s % 16 (8 keys).
+    using LB = BwGeo<kBwRows>;
+    int brow[2], boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = 64 * (2 * wave + i) + lane;
+        const int r = s / LB::CPR, key = k0 + 8 * ((s % LB::CPR) ^ LB::f(r));
+        brow[i] = r;
+        boff[i] = key < a.Sk ? key * 2 : -1;  // key bytes (the row is added per step)
+    }
+    auto issue_bias = [&](int st, int slot) {
+        const int h = gk * G + st / nqt;
+        const int q0 = (qt0 + st % nqt) * kBwTile;
+        const __amdgpu_buffer_rsrc_t rb =
+            rsrc(static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh, (uint32_t)a.Sq * a.Sk * 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dma(rb, smem + DSX + slot * BT + 512 * (2 * wave + i),
+                (boff[i] >= 0 && q0 + brow[i] < a.Sq) ? (uint32_t)(q0 + brow[i]) * a.Sk * 2 + (uint32_t)boff[i]
+                                                       : kOutside);
+    };
+    // Transposed-read offsets into a bias slot: rows 4hg + j/4 (lo) and 8 more
+    // (hi) of a 16-row step, keys 32*pair + ... (lane receives key kj).
+    int btr_lo, btr_hi;
+    {
+        const int g16 = lane >> 4, j16 = lane & 15;
+        const int rl = 4 * hg + (j16 >> 2), rh = rl + 8;
+        const int col = 32 * pair + 16 * (g16 & 1) + 4 * (j16 & 3);
+        btr_lo = rl * kBwRows + (((col >> 3) ^ LB::f(rl)) * 8) + (col & 7);
+        btr_hi = rh * kBwRows + (((col >> 3) ^ LB::f(rh)) * 8) + (col & 7);
     }
 
     auto issue = [&](int st, int stage) {
@@ -615,23 +722,25 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
     // One 64-query tile.  live: this pair has work here; mask: hide queries
     // before key kj (causal diagonal).
     auto compute = [&](const uint16_t* qs, const uint16_t* ds, const float* st, int q0, bool live,
-                       bool mask, int hstep) __attribute__((always_inline)) {
+                       bool mask, int hstep, const uint16_t* bs, int step_no) __attribute__((always_inline)) {
+        // after the hand-over barrier: the bias of step step_no+2 into this step's slot
+        auto next_bias = [&]() {
+            if (BIAS && step_no + 2 < steps) issue_bias(step_no + 2, step_no & 1);
+        };
         if (role == 0) {
             uint32_t pw[16];
             if (live) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    // bias of rows q0 + 32qb + 8i + 4hg + j at key kj (rows past Sq read 0)
+                    // bias of tile rows 32qb + 8i + 4hg + j at key kj (rows past Sq read 0)
                     float bb[16];
                     if constexpr (BIAS) {
-                        const __amdgpu_buffer_rsrc_t rb =
-                            rsrc(static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + hstep * a.bias_sh,
-                                 (uint32_t)a.Sq * a.Sk * 2);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int q = q0 + 32 * qb + 8 * (r >> 2) + 4 * hg + (r & 3);
-                            bb[r] = half_to_float<T>(__builtin_amdgcn_raw_buffer_load_b16(
-                                rb, ((uint32_t)q * a.Sk + kj) * 2, 0, 0));
+                        for (int i = 0; i < 4; ++i) {
+                            const int ii = 4 * qb + i;  // 8-row group of the tile
+                            const u32x2 v = lds_tr(bs + (ii >> 1) * 16 * kBwRows + ((ii & 1) ? btr_hi : btr_lo));
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) bb[4 * i + j] = bias_elem<T>(v[j >> 1], j & 1);
                         }
                     }
                     const f32x16 s = scores(qs, qb);
@@ -659,6 +768,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                     lds_st4(ex + exslot(i), u32x4{pw[4 * i], pw[4 * i + 1], pw[4 * i + 2], pw[4 * i + 3]});
             }
             lds_barrier();  // P handed over
+            next_bias();
             if (live) {
                 grads(ds, 0, pw);
                 grads(ds, 1, pw + 8);
@@ -670,6 +780,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                 dp[1] = scores(ds, 1);
             }
             lds_barrier();  // P handed over
+            next_bias();
             if (live) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
@@ -749,20 +860,25 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
 
     // Three LDS stages: the loads of step st+2 are issued at the start of step
     // st, so each tile has two steps to arrive.
+    // (BIAS: the two bias loads of step st+2, issued after them, may stay in
+    // flight as well.)
+    constexpr int BN = BIAS ? 2 : 0;
     auto wait_older = [&](bool last) __attribute__((always_inline)) {
         // Everything but this step's own loads has landed (vmcnt counts loads
         // in issue order; wave 0 also issued the statistics load).
         if (last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         else if (DQ) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // atomics count too
-        else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA + 1) : "memory");
-        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA) : "memory");
+        else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA + 1 + BN) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA + BN) : "memory");
     };
     // The barriers below are LDS-only: __syncthreads() would fence global
     // memory, i.e. wait for every load in flight, the newest stage's included,
     // and cut the prefetch to one step.  Each wave's own wait covers what the
     // next step reads; the barrier then covers every wave's.
+    if (BIAS && steps > 0) issue_bias(0, 0);
     if (steps > 0) issue(0, 0);
     if (NSTG == 3 && steps > 1) issue(1, 1);
+    if (BIAS && steps > 1) issue_bias(1, 1);
     wait_older(steps <= NSTG - 2);
     lds_barrier();
     auto step = [&](int st, const int cur) __attribute__((always_inline)) {
@@ -771,7 +887,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         const bool live = kw < kv_lim && (!a.causal || q0 + kBwTile - 1 >= kw);
         const uint16_t* base = smem + cur * STAGE;
         compute(base, base + L::TILE, reinterpret_cast<const float*>(base + 2 * L::TILE), q0, live,
-                a.causal && q0 < kw + 31, gk * G + st / nqt);
+                a.causal && q0 < kw + 31, gk * G + st / nqt, smem + DSX + (st & 1) * BT, st);
         wait_older(st + NSTG - 1 >= steps);
         lds_barrier();
     };

@@ -141,12 +141,6 @@ __device__ __forceinline__ float bias_elem(uint32_t w, int hi) {
         return __builtin_bit_cast(float, hi ? (w & 0xffff0000u) : (w << 16));
     }
 }
-// One 16-bit element (as loaded) to fp32, exactly.
-template <class T>
-__device__ __forceinline__ float half_to_float(uint16_t h) {
-    if constexpr (T::kF16) return (float)__builtin_bit_cast(_Float16, h);
-    else return __builtin_bit_cast(float, (uint32_t)h << 16);
-}
 // acc + lo + hi of a packed pair, in fp32 (v_dot2 with (1, 1)).
 template <class T>
 __device__ __forceinline__ float sum2(uint32_t w, float acc) {
