@@ -17,6 +17,8 @@ resident in HBM:
     gradient [4, 16, 4096, 4096] bf16 in full
   * the causal prefill with a general additive mask: a per-head bias tensor
     [1, 16, 4096, 4096] bf16 added to the scaled scores
+  * the causal prefill with 1024-wide heads, bf16, B=1 Hq=Hkv=8 S=4096 D=1024
+    (the same formula FLOPs again; the head dim is split across 8 waves)
   * the causal prefill with 256-wide heads, bf16, B=4 Hq=Hkv=8 S=4096 D=256
     (the same formula FLOPs as the headline; the kernel computes the output
     in two 128-dim slices that each recompute the scores), and the split-KV
@@ -62,6 +64,7 @@ PAGE_SIZE = 16                      # paged decode: keys per cache page
 # attention blocks: (batch, tokens, model width, heads)
 BLOCKS = {"block": (4, 4096, 2048, 16), "block_small": (8, 128, 256, 4)}
 WIDE = (4, 8, 4096, 256)            # wide heads: (batch, heads, tokens, head dim)
+WIDEST = (1, 8, 4096, 1024)         # head-dim-split kernel: (batch, heads, tokens, head dim)
 DECODE_WIDE = (32, 32, 8, 32768, 256)  # wide decode: (batch, Hq, Hkv, Sk, head dim)
 
 
@@ -196,6 +199,9 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
         for i, key in enumerate(("prefill", "padded", "paged_prefill", "bias", "wide", "block_attn",
                                  "block_small_attn")):
             out[key] = entry(fwd, "forward.hip", fr[i::7], wr[i::7])
+    if "forward_wide_kernel" in fetch:
+        out["widest"] = entry("forward_wide_kernel", "forward_wide.hip", fetch["forward_wide_kernel"],
+                              write["forward_wide_kernel"])
     # each block call: q/k/v projection GEMM, attention, output projection
     # GEMM; a step runs the large block, then the small one (names are
     # truncated, so the four GEMM dispatches of a step are told apart by order)
@@ -237,7 +243,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
                                        "backward", "backward_atomic", "backward_bias", "bias",
-                                       "wide",
+                                       "wide", "widest",
                                        "decode_wide", "block", "block_small"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
@@ -333,6 +339,12 @@ def main():
         iwide = dict(zip(("q", "k", "v"), draw_qkv(WIDE[0], WIDE[1], WIDE[1], WIDE[2], WIDE[2],
                                                    WIDE[3], wp.dtype, wp.seed + 31, dev)))
         iwide["out"] = torch.empty_like(iwide["q"])
+    # Widest heads: the same tokens and batch*heads*head dim in 8 heads of 1024.
+    iwst = None
+    if args.only in (None, "widest"):
+        iwst = dict(zip(("q", "k", "v"), draw_qkv(WIDEST[0], WIDEST[1], WIDEST[1], WIDEST[2],
+                                                  WIDEST[2], WIDEST[3], wp.dtype, wp.seed + 37, dev)))
+        iwst["out"] = torch.empty_like(iwst["q"])
     idw = None
     if args.only in (None, "decode_wide"):
         B, Hq, Hkv, Sk, D = DECODE_WIDE
@@ -384,12 +396,15 @@ def main():
     calls["wide"] = lambda: sd.sdpa_forward(iwide["q"], iwide["k"], iwide["v"],
                                             1.0 / math.sqrt(WIDE[3]), sd.MASK_CAUSAL, None,
                                             iwide["out"])
+    calls["widest"] = lambda: sd.sdpa_forward(iwst["q"], iwst["k"], iwst["v"],
+                                              1.0 / math.sqrt(WIDEST[3]), sd.MASK_CAUSAL, None,
+                                              iwst["out"])
     for name in iblk:
         calls[name] = (lambda blk: lambda: sd.sdpa_block_forward(
             *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "backward_bias", "bias", "wide", "decode_wide", "block", "block_small"])
+              "backward_bias", "bias", "wide", "widest", "decode_wide", "block", "block_small"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -559,6 +574,18 @@ def main():
                                     "traffic": stored_traffic("wide", "forward.hip"),
                                     "kernel": "forward_bf16_kernel<256, DV=128> x 2 slices",
                                     "flops_per_launch": fl}}
+    if "widest" in ms:
+        B, H, S, D = WIDEST
+        fl = formula_flops(B, H, S, S, D, True)
+        tf = fl / (ms["widest"] * 1e-3) / 1e12
+        rec["widest"] = {"workload": "bf16_causal_b%d_h%d_s%d_d%d" % (B, H, S, D),
+                         "ms": round(ms["widest"], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                         "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "traffic": stored_traffic("widest", "forward_wide.hip"),
+                                      "kernel": "forward_wide_kernel<8> (head dim split over 8 waves)",
+                                      "flops_per_launch": fl}}
     if "decode_wide" in ms:
         B, Hq, Hkv, Sk, D = DECODE_WIDE
         by = 2 * B * Hkv * Sk * D * 2 + 2 * B * Hq * D * 2
@@ -588,7 +615,7 @@ def main():
                                             "gemm_kernel<out>",
                                   "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
-        blk = [n for n in list(BLOCKS) + ["wide", "decode_wide"] if n in rec]
+        blk = [n for n in list(BLOCKS) + ["wide", "widest", "decode_wide"] if n in rec]
         if blk:
             rec.update({"value": rec[blk[0]]["value"], "unit": rec[blk[0]]["unit"]})
             rec["config"] = {"workload": rec[blk[0]]["workload"]}
@@ -617,7 +644,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw, ibias, ibb, iblk, iwide, idw
+    del ip, ig, idd, ipg, ipp, ibw, ibias, ibb, iblk, iwide, iwst, idw
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

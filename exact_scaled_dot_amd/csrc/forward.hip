@@ -806,11 +806,13 @@ hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s)
 }  // namespace
 
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s) {
+    if (a.D > 256) return launch_forward_wide(a, false, s);
     return a.bias ? launch_16bit<false, Bf16T, true>(a, PagedArgs{}, s)
                   : launch_16bit<false, Bf16T>(a, PagedArgs{}, s);
 }
 
 hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s) {
+    if (a.D > 256) return launch_forward_wide(a, true, s);
     return a.bias ? launch_16bit<false, F16T, true>(a, PagedArgs{}, s)
                   : launch_16bit<false, F16T>(a, PagedArgs{}, s);
 }

@@ -1,0 +1,366 @@
+// Exact attention forward for wide heads: 16-bit Q, K, V with a head dim D
+// above 256 and up to 1024 (a multiple of 8), the range the ruDNN user guide
+// allows for attention (section 9: D and Dv in 1..=1024).  Same definition
+// and options as the narrow forward: softmax over the keys of
+// Q K^T * scale (+ bias) under the causal / key-padding masks, grouped K/V
+// heads, optional log-sum-exp output (tensai autograd guide, "Attention の
+// 組み立て"; HOF essay section 4, the exact kernel with the n x n scores kept
+// out of HBM).
+//
+// A 32-row query block of D = 1024 has 64 KB of Q and 128 KB of fp32 output:
+// more than a wave's registers, so the head dim is split across the waves of
+// a workgroup.  Workgroup = NW waves (NW = 4, 6 or 8) and one 32-row block of
+// one (batch, query head); wave w owns dims 128w .. 128w+127: its Q rows
+// (B operands) and its slice of O^T stay in registers.  Per 16-key tile:
+//   A  every wave: partial S^T = K_w Q_w^T over its dims
+//      (v_mfma_f32_16x16x32; K fragments straight from HBM into registers,
+//      one tile ahead), written to LDS in fp32 (two buffers, alternating);
+//   -  one barrier;
+//   B  every wave: each lane sums the NW partials of exactly the scores it
+//      feeds to the P.V product (query lane%32, keys 8*(lane/32) .. +7),
+//      scales, adds the bias, masks, and runs the online softmax for that
+//      row (the row max across the two half-waves by v_permlane32_swap).
+//      Every wave computes the same row statistics, so P never leaves the
+//      registers and no second barrier is needed;
+//   C  every wave: rescale its O^T if a row's max moved, then
+//      O^T += V_w^T P^T (v_mfma_f32_32x32x16; V^T by transposed LDS reads
+//      from the wave's own V tiles, which arrive by buffer-load DMA two
+//      tiles ahead into a 3-stage ring per wave).
+// Each V DMA is issued before the K loads of the next tile, and vmcnt
+// counts in issue order, so the compiler's wait for those K fragments also
+// covers the V tile: no explicit wait is needed for V.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int kWRows = 32;       // query rows per workgroup
+constexpr int kWKeys = 16;       // keys per tile
+constexpr int kWChunk = 128;     // head dims per wave
+constexpr int kWVStages = 3;     // V tiles in flight per wave
+constexpr uint32_t kWOutside = 0x80000000u;  // buffer offset past any num_records
+constexpr float kWLog2e = 1.4426950408889634f;
+
+typedef short w_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void w_lds_void;
+
+// LDS accessors; the __restrict__ parameters give each inlined access an alias
+// scope of its own, so the compiler does not drain the in-flight LDS DMA
+// (vmcnt(0)) in front of it.
+__device__ __forceinline__ u32x2 w_lds_tr(const uint16_t* __restrict__ p) {
+    typedef __attribute__((address_space(3))) w_i16x4 lds_i16x4;
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((__attribute__((address_space(3))) char*)p)));
+}
+__device__ __forceinline__ void w_lds_st_f4(float* __restrict__ p, f32x4 v) {
+    *(__attribute__((address_space(3))) f32x4*)((__attribute__((address_space(3))) char*)p) = v;
+}
+__device__ __forceinline__ f32x4 w_lds_ld_f4(const float* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) f32x4*)((const __attribute__((address_space(3))) char*)p);
+}
+__device__ __forceinline__ void w_lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void w_dma(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (w_lds_void*)((__attribute__((address_space(3))) char*)lds), 16,
+                                             voff, 0, 0, 0);
+}
+
+// LDS layout (floats / 16-bit elements):
+//   partial S: 2 buffers x NW x [32 rows][16 keys] fp32; row q keeps its
+//     4-key chunk g at chunk (g + q/4) % 4, so both the 16-byte writes and
+//     the 16-byte reads (16 rows, one chunk each) are free of bank conflicts;
+//   V: NW x kWVStages x [16 keys][128 dims] 16-bit; row r keeps its 16-byte
+//     chunk c at c ^ 4*(r % 4), so a transposed read (4 rows x 64 bytes per
+//     32 lanes) touches 16 distinct bank groups.
+template <int NW>
+struct WideLds {
+    static constexpr int PBUF = NW * kWRows * kWKeys;                // floats per partial buffer
+    static constexpr int VFL = 2 * PBUF;                             // V, in floats (16-byte aligned)
+    static constexpr int VST = kWKeys * kWChunk;                     // 16-bit elements per V stage
+    static constexpr int FLOATS = VFL + NW * kWVStages * VST / 2;
+};
+
+// x[l] + x[l^32] in every lane (v_permlane32_swap; see max_half_waves).
+__device__ __forceinline__ float w_sum_half_waves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                   __builtin_bit_cast(unsigned, x), false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+__device__ __forceinline__ int w_xcd_order(int total) {
+    // workgroup id -> logical index such that each of the 8 XCDs (ids dealt
+    // round-robin) owns one contiguous run
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int nx = total >> 3, rem = total & 7;
+    return xcd * nx + min(xcd, rem) + local;
+}
+
+template <int NW, class T, bool BIAS>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(ForwardArgs a,
+                                                                  const int32_t* __restrict__ key_lens) {
+    using LY = WideLds<NW>;
+    __shared__ __attribute__((aligned(1024))) float smem[LY::FLOATS];
+    float* const part = smem;
+    uint16_t* const vring = reinterpret_cast<uint16_t*>(smem + LY::VFL);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int D = a.D;
+
+    // Logical order: (batch, K/V head) outermost, then query blocks (under a
+    // causal mask the longest first), then the query heads of the group.
+    const int G = a.Hq / a.Hkv;
+    const int nqb = (a.Sq + kWRows - 1) / kWRows;
+    int t = w_xcd_order(a.B * a.Hkv * nqb * G);
+    const int hsub = t % G;
+    t /= G;
+    const int qord = t % nqb;
+    const int unit = t / nqb;
+    const int b = unit / a.Hkv, gk = unit % a.Hkv, h = gk * G + hsub;
+    const int q0 = (a.causal ? nqb - 1 - qord : qord) * kWRows;
+    const int64_t bh = (int64_t)b * a.Hq + h;
+
+    int kv_lim = a.Sk;
+    if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
+    int kv_end = kv_lim;
+    if (a.causal) kv_end = min(kv_end, q0 + kWRows);
+    const int ntiles = kv_end > 0 ? (kv_end + kWKeys - 1) / kWKeys : 0;
+
+    const int d0 = kWChunk * wave;  // this wave's first dim
+    const uint32_t kvbytes = (uint32_t)a.Sk * D * 2;
+    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
+    const __amdgpu_buffer_rsrc_t rk = w_rsrc(static_cast<const uint16_t*>(a.k) + kvh, kvbytes);
+    const __amdgpu_buffer_rsrc_t rv = w_rsrc(static_cast<const uint16_t*>(a.v) + kvh, kvbytes);
+
+    // Q^T as B operands of the 16x16x32 products: column 16qb + lane%16 (a
+    // query), dims d0 + 32s + 8*(lane/16) .. +7 (rows past Sq and dims past D
+    // read as zeros).
+    const int l16 = lane & 15, g4 = lane >> 4;
+    u32x4 qf[2][4];
+    {
+        const __amdgpu_buffer_rsrc_t rq =
+            w_rsrc(static_cast<const uint16_t*>(a.q) + bh * a.Sq * D, (uint32_t)a.Sq * D * 2);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = q0 + 16 * qb + l16, dim = d0 + 32 * s + 8 * g4;
+                qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rq, (row < a.Sq && dim < D) ? ((uint32_t)row * D + dim) * 2 : kWOutside, 0, 0);
+            }
+    }
+    // K fragments (A operands): key kt + lane%16, dims d0 + 32s + 8*(lane/16).
+    auto load_k = [&](int kt, u32x4* kf) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int dim = d0 + 32 * s + 8 * g4;
+            kf[s] = __builtin_amdgcn_raw_buffer_load_b128(
+                rk, dim < D ? ((uint32_t)(kt + l16) * D + dim) * 2 : kWOutside, 0, 0);
+        }
+    };
+    // V tile of keys kt .. kt+15, this wave's dims, into ring stage st: DMA i
+    // fills rows 4i + lane/16, stored chunk lane%16 (logical chunk
+    // (lane%16) ^ 4*(lane/16)); keys past Sk read as zeros.
+    uint16_t* const vw = vring + wave * kWVStages * LY::VST;
+    const int vchunk = (lane & 15) ^ (4 * g4);
+    const bool vdim_ok = d0 + 8 * vchunk < D;
+    auto load_v = [&](int kt, int st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w_dma(rv, vw + st * LY::VST + 512 * i,
+                  vdim_ok ? ((uint32_t)(kt + 4 * i + g4) * D + d0 + 8 * vchunk) * 2 : kWOutside);
+    };
+    // Transposed-read offsets (32x32x16 A operand = V^T): lane reads rows
+    // (keys) 8*(lane/32) + (lane%16)/4 (+4 for the upper half), dims
+    // 32db + 16*((lane/16)%2) + 4*(lane%4).
+    int vtr[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int row = 8 * (g4 >> 1) + (l16 >> 2);
+        const int col = 32 * db + 16 * (g4 & 1) + 4 * (l16 & 3);
+        vtr[db] = row * kWChunk + (((col >> 3) ^ (4 * (row & 3))) * 8) + (col & 7);
+    }
+    // (row + 4 has the same swizzle term as row: (row + 4) % 4 == row % 4)
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+
+    // Softmax state of this lane's row: query qr = lane%32, keys 8*kh .. +7 of
+    // each tile (the lane's P^T operand); m_run is the same in both halves.
+    const int qr = lane & 31, kh = lane >> 5;
+    const int qa = q0 + qr;
+    float m_run = -INFINITY, l_part = 0.f;
+    const float c = a.scale * kWLog2e;
+    const __amdgpu_buffer_rsrc_t rb =
+        w_rsrc(BIAS ? static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh
+                    : static_cast<const uint16_t*>(a.q),
+               BIAS ? (uint32_t)a.Sq * a.Sk * 2 : 0u);
+    // this lane's two 4-key chunks (2kh, 2kh+1) of a partial row
+    const int poff0 = qr * kWKeys + (((2 * kh + (qr >> 2)) & 3) * 4);
+    const int poff1 = qr * kWKeys + (((2 * kh + 1 + (qr >> 2)) & 3) * 4);
+
+    u32x4 kcur[4], knext[4];
+    if (ntiles > 0) load_v(0, 0);
+    if (ntiles > 1) load_v(kWKeys, 1);
+    asm volatile("" ::: "memory");
+    if (ntiles > 0) load_k(0, kcur);
+
+    auto tile = [&](int j, u32x4* kc, u32x4* kn) __attribute__((always_inline)) {
+        const int kt = j * kWKeys;
+        float* const pb = part + (j & 1) * LY::PBUF;
+        // (BIAS) this lane's 8 bias values first, so that waiting for them
+        // does not wait for the loads issued below
+        u32x4 bw = {0u, 0u, 0u, 0u};
+        if constexpr (BIAS) {
+            const int key = kt + 8 * kh;
+            bw = __builtin_amdgcn_raw_buffer_load_b128(
+                rb, (qa < a.Sq && key < a.Sk) ? ((uint32_t)qa * a.Sk + key) * 2 : kWOutside, 0, 0);
+        }
+        // V two tiles ahead, then K one tile ahead (in this order: the wait
+        // for K(j+1) at the next tile then also covers V(j+2))
+        if (j + 2 < ntiles) load_v(kt + 2 * kWKeys, (j + 2) % kWVStages);
+        asm volatile("" ::: "memory");
+        if (j + 1 < ntiles) load_k(kt + kWKeys, kn);
+
+        // A: partial S^T over this wave's dims; register i of block qb holds
+        // key kt + 4*(lane/16) + i of query 16qb + lane%16.
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) sacc = mfma_16x16x32<T>(kc[st], qf[qb][st], sacc);
+            const int q = 16 * qb + l16;
+            w_lds_st_f4(pb + wave * (kWRows * kWKeys) + q * kWKeys + (((g4 + (q >> 2)) & 3) * 4), sacc);
+        }
+        // The buffer written here was last read in tile j-2, and every wave
+        // finished those reads before the previous tile's barrier: one
+        // barrier per tile suffices.
+        w_lds_barrier();
+
+        // B: this lane's 8 scores, keys kt + 8kh + e.
+        float x[8];
+        {
+            f32x4 s0 = w_lds_ld_f4(pb + poff0), s1 = w_lds_ld_f4(pb + poff1);
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                s0 += w_lds_ld_f4(pb + w * (kWRows * kWKeys) + poff0);
+                s1 += w_lds_ld_f4(pb + w * (kWRows * kWKeys) + poff1);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = s0[e] * c;
+                x[4 + e] = s1[e] * c;
+            }
+        }
+        if constexpr (BIAS) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wv = bw[e >> 1];
+                x[e] = fmaf(bias_elem<T>(wv, e & 1), kWLog2e, x[e]);
+            }
+        }
+        const int key0 = kt + 8 * kh;
+        const bool edge = key0 + 8 > kv_lim || (a.causal && key0 + 7 > qa);
+        if (edge) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (key0 + e >= kv_lim || (a.causal && key0 + e > qa)) x[e] = -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        tmax = max_half_waves(tmax);
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);  // 0 while the row had no key
+        m_run = m_new;
+        u32x4 pf;
+        float ls = l_part * alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pf[e] = pack2<T>(fast_exp2(x[2 * e] - m_use), fast_exp2(x[2 * e + 1] - m_use));
+            ls = sum2<T>(pf[e], ls);
+        }
+        l_part = ls;
+
+        // C: O^T += V^T P^T over this wave's dims (column = query lane%32).
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        }
+        const uint16_t* vs = vw + (j % kWVStages) * LY::VST;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const u32x2 lo = w_lds_tr(vs + vtr[db]);
+            const u32x2 hi = w_lds_tr(vs + vtr[db] + 4 * kWChunk);
+            acc[db] = mfma_32x32x16<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, acc[db]);
+        }
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+        tile(j, kcur, knext);
+        if (j + 1 < ntiles) tile(j + 1, knext, kcur);
+    }
+
+    // Row sum (both halves) and log-sum-exp.
+    const float l = w_sum_half_waves(l_part);
+    const float inv = 1.f / l;  // a row with no visible key: 0 * inf = NaN
+    if (wave == 0 && kh == 0 && a.lse && qa < a.Sq) {
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        a.lse[bh * a.Sq + qa] = (m_use + __log2f(l)) * 0.69314718055994531f;
+    }
+
+    // O: register r of d-block db holds dim d0 + 32db + 8*(r/4) + 4*(lane/32)
+    // + r%4 of query q0 + lane%32.
+    if (qa < a.Sq) {
+        uint16_t* row = static_cast<uint16_t*>(a.out) + (bh * a.Sq + qa) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int dim = d0 + 32 * db + 8 * r4 + 4 * kh;
+                const f32x16& xo = acc[db];
+                if (dim < D)
+                    *reinterpret_cast<u32x2*>(row + dim) =
+                        u32x2{pack2<T>(xo[4 * r4] * inv, xo[4 * r4 + 1] * inv),
+                              pack2<T>(xo[4 * r4 + 2] * inv, xo[4 * r4 + 3] * inv)};
+            }
+    }
+}
+
+template <int NW, class T>
+hipError_t launch_wide_nw(const ForwardArgs& a, hipStream_t s) {
+    const int nqb = (a.Sq + kWRows - 1) / kWRows;
+    const dim3 grid((unsigned)(a.B * a.Hq * nqb));
+    if (a.bias)
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, true>), grid, dim3(NW * 64), 0, s, a, a.key_lens);
+    else
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_wide_t(const ForwardArgs& a, hipStream_t s) {
+    if (a.D <= 4 * kWChunk) return launch_wide_nw<4, T>(a, s);
+    if (a.D <= 6 * kWChunk) return launch_wide_nw<6, T>(a, s);
+    return launch_wide_nw<8, T>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s) {
+    if (a.D <= 256 || a.D > 1024 || a.D % 8 != 0) return hipErrorInvalidValue;
+    return f16 ? launch_wide_t<F16T>(a, s) : launch_wide_t<Bf16T>(a, s);
+}
+
+}  // namespace sdpa

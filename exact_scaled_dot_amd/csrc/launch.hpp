@@ -80,6 +80,8 @@ struct PagedArgs {
 hipError_t launch_forward_bf16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
+// Dense 16-bit forward with 256 < D <= 1024 (the head-dim-split kernel).
+hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s);
 // Paged prefill chunks: a.B = num_seqs, a.Sq = longest chunk, a.Sk = max_seq_len;
 // bf16 or (f16) fp16.
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,

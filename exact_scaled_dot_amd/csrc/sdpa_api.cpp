@@ -51,9 +51,10 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // Head dims the kernels cover: 16-bit inputs any multiple of 8 up to max16
 // (the 64-, 128- and 256-wide kernels read the missing chunks as zeros),
 // fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
-// kernel).  max16: the widest 16-bit head dim of the entry point (256 for
-// the prefill and decode kernels; 128 for the backward, whose lanes hold a
-// full-width operand and gradient).
+// kernel).  max16: the widest 16-bit head dim of the entry point (1024 for
+// the dense forward, whose heads above 256 run on the head-dim-split
+// kernel; 256 for decode, paged attention and the block; 128 for the
+// backward, whose lanes hold a full-width operand and gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
     return D >= 8 && D <= max16 && D % 8 == 0;
@@ -132,7 +133,7 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
                            int64_t bias_sb = 0, int64_t bias_sh = 0) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st = check_common(q, k, v, out, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
-                                    &kbytes, 256);
+                                    &kbytes, 1024);
     if (st != SDPA_OK) return st;
     if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
@@ -178,8 +179,8 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
             (lse && overlap(lse, B * Hq * Sq * (int64_t)sizeof(float), bias, bbytes)))
             return fail(SDPA_ERR_INVALID_ARGUMENT, "out or lse overlaps the bias");
     }
-    const int64_t blocks = ((Sq + 127) / 128) * B * Hq;
-    if (blocks > INT_MAX / 256)
+    const int64_t blocks = ((Sq + 31) / 32) * B * Hq;  // the wide-head kernel's 32-row blocks
+    if (blocks > INT_MAX / 512)
         return fail(SDPA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)blocks);
 
     sdpa::ForwardArgs a;

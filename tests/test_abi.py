@@ -69,7 +69,8 @@ def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, sca
     (dict(out=ctypes.c_void_p(0x40000000 - 2)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(B=1 << 40, Hq=1 << 20), sd.SDPA_ERR_INVALID_ARGUMENT, "overflow"),
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),     # past the 256-wide kernel
+    (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "head dim"),    # past the widest (1024) kernel
+    (dict(D=1040), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
     (dict(D=252), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # fp32: multiples of 4
     (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),  # fp32: up to 128

@@ -270,3 +270,91 @@ def test_fp32_outputs_past_head_dim_untouched():
     torch.cuda.synchronize()
     assert (big[B * Hq * S * D:] == 7.0).all()
     compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL), F32, "fp32 D=52")
+
+
+# ------------------------------------------------- head dims above 256 (to 1024)
+# Above 256 the dense forward splits the head dim across the waves of a
+# workgroup (4, 6 or 8 waves of 128 dims): partial scores per wave, summed in
+# LDS; each wave keeps its own slice of the output.
+
+@pytest.mark.parametrize("D", [264, 384, 520, 768, 1024])
+@pytest.mark.parametrize("mask", [0, 1, 3], ids=["none", "causal", "causal+padding"])
+def test_forward_headdim_split(D, mask):
+    # 200 rows = 6 blocks of 32 + 8; 200 keys = 12 tiles of 16 + 8
+    B, Hq, Hkv, S = 2, 4, 2, 200
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 900 + D + mask, DEV)
+    lens = torch.tensor([200, 77], dtype=torch.int32, device=DEV) if mask & 2 else None
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask, ln, return_lse=True)
+    compare(to64(out), ref, BF16, "split forward D=%d mask=%d" % (D, mask))
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
+
+
+def test_forward_headdim_split_fp16_bias_gqa():
+    # 6 waves (D = 640), grouped K/V 8/2, a per-batch bias with -inf entries
+    B, Hq, Hkv, S, D = 2, 8, 2, 152, 640
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, F16, 910, DEV)
+    bias = draw_bias((B, 1, S, S), F16, 911, DEV)
+    bias[0, 0, 5, 3:90] = float("-inf")
+    out, lse = sd.sdpa_forward_bias(q, k, v, bias, 0.05, sd.MASK_CAUSAL, lse=True)
+    torch.cuda.synchronize()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), 0.05, O.MASK_CAUSAL, bias=to64(bias),
+                               return_lse=True)
+    compare(to64(out), ref, F16, "fp16 D=640 bias")
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
+
+
+def test_forward_headdim_split_rectangular_and_single_query():
+    # Sq != Sk without a mask, and one query row per head (a decode-like call)
+    for Sq, Sk, D in ((70, 333, 512), (1, 1000, 1024)):
+        q, k, v = draw_qkv(3, 4, 1, Sq, Sk, D, BF16, 920 + Sq, DEV)
+        out = sd.sdpa_forward(q, k, v, 1 / math.sqrt(D), sd.MASK_NONE)
+        torch.cuda.synchronize()
+        ref = O.sdpa_forward(to64(q), to64(k), to64(v), 1 / math.sqrt(D), O.MASK_NONE)
+        compare(to64(out), ref, BF16, "split forward Sq=%d Sk=%d D=%d" % (Sq, Sk, D))
+
+
+def test_forward_headdim_split_dead_rows():
+    # a batch with no valid key: its rows are NaN with lse -inf, like the
+    # narrow kernels; the other batch is unaffected
+    B, Hq, S, D = 2, 2, 96, 512
+    q, k, v = draw_qkv(B, Hq, Hq, S, S, D, BF16, 930, DEV)
+    lens = torch.tensor([0, 50], dtype=torch.int32, device=DEV)
+    out, lse = sd.sdpa_forward_lse(q, k, v, 0.05, sd.MASK_KEY_PADDING, lens)
+    torch.cuda.synchronize()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), 0.05, O.MASK_KEY_PADDING,
+                               lens.cpu().numpy(), return_lse=True)
+    compare(to64(out), ref, BF16, "dead rows D=512")
+    assert torch.isnan(out[0]).all() and torch.isneginf(lse[0]).all()
+    assert np.abs(to64(lse[1]) - rlse[1]).max() < 1e-2
+
+
+def test_headdim_split_outputs_past_head_dim_untouched():
+    # D = 520: the fifth wave owns dims 512..639 and stores only 512..519
+    B, Hq, S, D = 1, 2, 70, 520
+    q, k, v = draw_qkv(B, Hq, Hq, S, S, D, BF16, 940, DEV)
+    big = torch.full((B * Hq * S * D + 64,), 7.0, dtype=BF16, device=DEV)
+    out = big[: B * Hq * S * D].view(B, Hq, S, D)
+    sd.sdpa_forward(q, k, v, 0.1, sd.MASK_CAUSAL, out=out)
+    torch.cuda.synchronize()
+    assert (big[B * Hq * S * D:] == 7.0).all()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL), BF16, "D=520")
+
+
+def test_forward_headdim_split_full_size_sampled_rows():
+    # a 4096-token causal prefill with 1024-wide heads (the headline prefill's
+    # token count and B*H*D); sampled rows of every head against the oracle
+    B, H, S, D = 1, 8, 4096, 1024
+    q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 950, DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    rows = sample_rows(B, H, S, 48, 951)
+    ref, rlse = O.sdpa_forward_rows(to64(q), to64(k), to64(v), scale, O.MASK_CAUSAL, None, rows)
+    got = to64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    compare(got, ref, BF16, "D=1024 full size")
+    glse = to64(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(glse - rlse).max() < 1e-2
