@@ -23,7 +23,8 @@ resident in HBM:
     (the same formula FLOPs as the headline; the kernel computes the output
     in two 128-dim slices that each recompute the scores), and the split-KV
     decode with 256-wide heads, B=32 Hq=32 Hkv=8 Sk=32768 (the decode's K+V
-    bytes), 32 splits
+    bytes), 32 splits, and with 1024-wide heads, B=8 Hq=32 Hkv=8 Sk=32768 (the
+    same K+V bytes again)
   * the multi-head attention block (q/k/v projections, causal attention,
     output projection) at the tensai guide's shape (batch 8, 128 tokens,
     model 256, 4 heads) and at the prefill's (batch 4, 4096 tokens, model
@@ -66,6 +67,7 @@ BLOCKS = {"block": (4, 4096, 2048, 16), "block_small": (8, 128, 256, 4)}
 WIDE = (4, 8, 4096, 256)            # wide heads: (batch, heads, tokens, head dim)
 WIDEST = (1, 8, 4096, 1024)         # head-dim-split kernel: (batch, heads, tokens, head dim)
 DECODE_WIDE = (32, 32, 8, 32768, 256)  # wide decode: (batch, Hq, Hkv, Sk, head dim)
+DECODE_WIDEST = (8, 32, 8, 32768, 1024)  # head-dim-split decode (the same K+V bytes)
 
 
 def kernel_source_hash(name):
@@ -243,7 +245,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
                                        "backward", "backward_atomic", "backward_bias", "bias",
-                                       "wide", "widest",
+                                       "wide", "widest", "decode_widest",
                                        "decode_wide", "block", "block_small"],
                     default=None,
                     help="run one call per step (for per-kernel profiling)")
@@ -345,6 +347,13 @@ def main():
         iwst = dict(zip(("q", "k", "v"), draw_qkv(WIDEST[0], WIDEST[1], WIDEST[1], WIDEST[2],
                                                   WIDEST[2], WIDEST[3], wp.dtype, wp.seed + 37, dev)))
         iwst["out"] = torch.empty_like(iwst["q"])
+    idws = None
+    if args.only in (None, "decode_widest"):
+        B, Hq, Hkv, Sk, D = DECODE_WIDEST
+        idws = dict(zip(("q", "k", "v"), draw_qkv(B, Hq, Hkv, 1, Sk, D, wd.dtype, wd.seed + 41, dev)))
+        idws["out"] = torch.empty_like(idws["q"])
+        idws["ws"] = torch.empty(sd.sdpa_decode_workspace_size(B, Hq, D, wd.num_splits),
+                                 dtype=torch.uint8, device=dev)
     idw = None
     if args.only in (None, "decode_wide"):
         B, Hq, Hkv, Sk, D = DECODE_WIDE
@@ -393,6 +402,9 @@ def main():
     calls["decode_wide"] = lambda: sd.sdpa_decode(idw["q"], idw["k"], idw["v"],
                                                   1.0 / math.sqrt(DECODE_WIDE[4]), None,
                                                   wd.num_splits, idw["ws"], idw["out"])
+    calls["decode_widest"] = lambda: sd.sdpa_decode(idws["q"], idws["k"], idws["v"],
+                                                    1.0 / math.sqrt(DECODE_WIDEST[4]), None,
+                                                    wd.num_splits, idws["ws"], idws["out"])
     calls["wide"] = lambda: sd.sdpa_forward(iwide["q"], iwide["k"], iwide["v"],
                                             1.0 / math.sqrt(WIDE[3]), sd.MASK_CAUSAL, None,
                                             iwide["out"])
@@ -404,7 +416,8 @@ def main():
             *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "backward_bias", "bias", "wide", "widest", "decode_wide", "block", "block_small"])
+              "backward_bias", "bias", "wide", "widest", "decode_wide", "decode_widest", "block",
+              "block_small"])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -599,6 +612,18 @@ def main():
                                            "traffic": None,
                                            "kernel": "decode_split_bf16_kernel<256> + merge",
                                            "bytes_per_launch": by}}
+    if "decode_widest" in ms:
+        B, Hq, Hkv, Sk, D = DECODE_WIDEST
+        by = 2 * B * Hkv * Sk * D * 2 + 2 * B * Hq * D * 2
+        gbs = by / (ms["decode_widest"] * 1e-3) / 1e9
+        rec["decode_widest"] = {"workload": "bf16_gqa32x8_decode_b%d_sk%d_d%d" % (B, Sk, D),
+                                "ms": round(ms["decode_widest"], 4), "value": round(gbs, 1),
+                                "unit": "GB/s", "num_splits": wd.num_splits,
+                                "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                             "kernel": "forward_wide_kernel<8, decode> + merge",
+                                             "bytes_per_launch": by}}
     for name, (B, S, M, H) in BLOCKS.items():
         if name not in ms:
             continue
@@ -615,7 +640,7 @@ def main():
                                             "gemm_kernel<out>",
                                   "flops_per_launch": fl}}
     if "value" not in rec:  # --only another call: report that call
-        blk = [n for n in list(BLOCKS) + ["wide", "widest", "decode_wide"] if n in rec]
+        blk = [n for n in list(BLOCKS) + ["wide", "widest", "decode_wide", "decode_widest"] if n in rec]
         if blk:
             rec.update({"value": rec[blk[0]]["value"], "unit": rec[blk[0]]["unit"]})
             rec["config"] = {"workload": rec[blk[0]]["workload"]}
@@ -644,7 +669,7 @@ def main():
             rec.update({"value": rec["padded"]["tflops_formula"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": wg.name}
 
-    del ip, ig, idd, ipg, ipp, ibw, ibias, ibb, iblk, iwide, iwst, idw
+    del ip, ig, idd, ipg, ipp, ibw, ibias, ibb, iblk, iwide, iwst, idw, idws
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -498,6 +498,23 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    if (!PAGED && a.D > 256 && a.D <= 1024 && a.D % 8 == 0) {
+        // Wider heads: the head-dim-split kernel writes the same partials,
+        // then the same merge (D/4 threads per row).
+        const hipError_t ew = launch_decode_wide_split(a, T::kF16, s);
+        if (ew != hipSuccess) return ew;
+        const int dw = a.D <= 512 ? 512 : 1024;
+        const dim3 mg((unsigned)(((int64_t)a.B * a.Hq * dw / 4 + 255) / 256));
+        if (a.D == 512)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T>), mg, dim3(256), 0, s, a);
+        else if (a.D == 1024)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T>), mg, dim3(256), 0, s, a);
+        else if (dw == 512)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T, true>), mg, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T, true>), mg, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.D % 8 != 0 || a.D < 8 || a.D > 256) return hipErrorInvalidValue;
     // Head dims that are multiples of 8 run on the 64-, 128- or 256-wide
     // kernels (the 256-wide ring holds two steps per wave: one step ahead).

@@ -103,9 +103,20 @@ __device__ __forceinline__ int w_xcd_order(int total) {
     return xcd * nx + min(xcd, rem) + local;
 }
 
-template <int NW, class T, bool BIAS>
+// Extra arguments of the decode form (DEC): a workgroup takes one key range
+// (split) of one (batch, K/V head) for up to 32 query heads of its group
+// (the rows), Sq = 1, and writes its normalised fp32 partial output and
+// natural-log lse into the split-KV workspace for the merge pass.
+struct WideDec {
+    float* o_part;    // [B, Hq, splits, D]
+    float* lse_part;  // [B, Hq, splits]
+    int splits;
+};
+
+template <int NW, class T, bool BIAS, bool DEC>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(ForwardArgs a,
-                                                                  const int32_t* __restrict__ key_lens) {
+                                                                  const int32_t* __restrict__ key_lens,
+                                                                  WideDec dec) {
     using LY = WideLds<NW>;
     __shared__ __attribute__((aligned(1024))) float smem[LY::FLOATS];
     float* const part = smem;
@@ -118,22 +129,45 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
 
     // Logical order: (batch, K/V head) outermost, then query blocks (under a
     // causal mask the longest first), then the query heads of the group.
+    // DEC: (batch, K/V head), then splits, then blocks of 32 query heads.
     const int G = a.Hq / a.Hkv;
-    const int nqb = (a.Sq + kWRows - 1) / kWRows;
-    int t = w_xcd_order(a.B * a.Hkv * nqb * G);
-    const int hsub = t % G;
-    t /= G;
-    const int qord = t % nqb;
-    const int unit = t / nqb;
-    const int b = unit / a.Hkv, gk = unit % a.Hkv, h = gk * G + hsub;
-    const int q0 = (a.causal ? nqb - 1 - qord : qord) * kWRows;
+    int b, gk, h, q0, split = 0, hb = 0;
+    if constexpr (DEC) {
+        const int nhb = (G + kWRows - 1) / kWRows;
+        int t = w_xcd_order(a.B * a.Hkv * dec.splits * nhb);
+        hb = t % nhb;
+        t /= nhb;
+        split = t % dec.splits;
+        const int unit = t / dec.splits;
+        b = unit / a.Hkv;
+        gk = unit % a.Hkv;
+        h = gk * G + kWRows * hb;  // head of row 0
+        q0 = 0;
+    } else {
+        const int nqb = (a.Sq + kWRows - 1) / kWRows;
+        int t = w_xcd_order(a.B * a.Hkv * nqb * G);
+        const int hsub = t % G;
+        t /= G;
+        const int qord = t % nqb;
+        const int unit = t / nqb;
+        b = unit / a.Hkv;
+        gk = unit % a.Hkv;
+        h = gk * G + hsub;
+        q0 = (a.causal ? nqb - 1 - qord : qord) * kWRows;
+    }
     const int64_t bh = (int64_t)b * a.Hq + h;
 
-    int kv_lim = a.Sk;
+    // Visible keys [k_lo, kv_lim): DEC takes its split's range.
+    int kv_lim = a.Sk, k_lo = 0;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
+    if constexpr (DEC) {
+        const int chunk = (a.Sk + dec.splits - 1) / dec.splits;
+        k_lo = split * chunk;
+        kv_lim = min(kv_lim, k_lo + chunk);
+    }
     int kv_end = kv_lim;
     if (a.causal) kv_end = min(kv_end, q0 + kWRows);
-    const int ntiles = kv_end > 0 ? (kv_end + kWKeys - 1) / kWKeys : 0;
+    const int ntiles = kv_end > k_lo ? (kv_end - k_lo + kWKeys - 1) / kWKeys : 0;
 
     const int d0 = kWChunk * wave;  // this wave's first dim
     const uint32_t kvbytes = (uint32_t)a.Sk * D * 2;
@@ -147,15 +181,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int l16 = lane & 15, g4 = lane >> 4;
     u32x4 qf[2][4];
     {
+        // DEC: row r is query head h + r (one query each; heads past the group
+        // read as zeros), so the rows form [G - 32hb, D] from head h on.
+        const int nrows = DEC ? G - kWRows * hb : a.Sq;
         const __amdgpu_buffer_rsrc_t rq =
-            w_rsrc(static_cast<const uint16_t*>(a.q) + bh * a.Sq * D, (uint32_t)a.Sq * D * 2);
+            w_rsrc(static_cast<const uint16_t*>(a.q) + bh * a.Sq * D, (uint32_t)nrows * D * 2);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int row = q0 + 16 * qb + l16, dim = d0 + 32 * s + 8 * g4;
                 qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rq, (row < a.Sq && dim < D) ? ((uint32_t)row * D + dim) * 2 : kWOutside, 0, 0);
+                    rq, (row < nrows && dim < D) ? ((uint32_t)row * D + dim) * 2 : kWOutside, 0, 0);
             }
     }
     // K fragments (A operands): key kt + lane%16, dims d0 + 32s + 8*(lane/16).
@@ -210,13 +247,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int poff1 = qr * kWKeys + (((2 * kh + 1 + (qr >> 2)) & 3) * 4);
 
     u32x4 kcur[4], knext[4];
-    if (ntiles > 0) load_v(0, 0);
-    if (ntiles > 1) load_v(kWKeys, 1);
+    if (ntiles > 0) load_v(k_lo, 0);
+    if (ntiles > 1) load_v(k_lo + kWKeys, 1);
     asm volatile("" ::: "memory");
-    if (ntiles > 0) load_k(0, kcur);
+    if (ntiles > 0) load_k(k_lo, kcur);
 
     auto tile = [&](int j, u32x4* kc, u32x4* kn) __attribute__((always_inline)) {
-        const int kt = j * kWKeys;
+        const int kt = k_lo + j * kWKeys;
         float* const pb = part + (j & 1) * LY::PBUF;
         // (BIAS) this lane's 8 bias values first, so that waiting for them
         // does not wait for the loads issued below
@@ -314,6 +351,31 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
 
     // Row sum (both halves) and log-sum-exp.
     const float l = w_sum_half_waves(l_part);
+    if constexpr (DEC) {
+        // normalised partial (0 for a split with no visible key, whose lse
+        // is -inf and weight 0 in the merge)
+        const int hr = kWRows * hb + qr;  // head within the group
+        if (hr >= G) return;
+        const int64_t prow = (bh + qr) * dec.splits + split;
+        const float invd = l > 0.f ? 1.f / l : 0.f;
+        if (wave == 0 && kh == 0) {
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            dec.lse_part[prow] = l > 0.f ? (m_use + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+        }
+        float* orow = dec.o_part + prow * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int dim = d0 + 32 * db + 8 * r4 + 4 * kh;
+                const f32x16& xo = acc[db];
+                if (dim < D)
+                    *reinterpret_cast<f32x4*>(orow + dim) =
+                        f32x4{xo[4 * r4] * invd, xo[4 * r4 + 1] * invd, xo[4 * r4 + 2] * invd,
+                              xo[4 * r4 + 3] * invd};
+            }
+        return;
+    }
     const float inv = 1.f / l;  // a row with no visible key: 0 * inf = NaN
     if (wave == 0 && kh == 0 && a.lse && qa < a.Sq) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -343,10 +405,27 @@ hipError_t launch_wide_nw(const ForwardArgs& a, hipStream_t s) {
     const int nqb = (a.Sq + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hq * nqb));
     if (a.bias)
-        hipLaunchKernelGGL((forward_wide_kernel<NW, T, true>), grid, dim3(NW * 64), 0, s, a, a.key_lens);
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, true, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens,
+                           WideDec{});
     else
-        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens);
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens,
+                           WideDec{});
     return hipGetLastError();
+}
+
+template <int NW, class T>
+hipError_t launch_wide_dec_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
+    const int nhb = (a.Hq / a.Hkv + kWRows - 1) / kWRows;
+    const dim3 grid((unsigned)(a.B * a.Hkv * d.splits * nhb));
+    hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true>), grid, dim3(NW * 64), 0, s, a, a.key_lens, d);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_wide_dec_t(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
+    if (a.D <= 4 * kWChunk) return launch_wide_dec_nw<4, T>(a, d, s);
+    if (a.D <= 6 * kWChunk) return launch_wide_dec_nw<6, T>(a, d, s);
+    return launch_wide_dec_nw<8, T>(a, d, s);
 }
 
 template <class T>
@@ -361,6 +440,27 @@ hipError_t launch_wide_t(const ForwardArgs& a, hipStream_t s) {
 hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s) {
     if (a.D <= 256 || a.D > 1024 || a.D % 8 != 0) return hipErrorInvalidValue;
     return f16 ? launch_wide_t<F16T>(a, s) : launch_wide_t<Bf16T>(a, s);
+}
+
+hipError_t launch_decode_wide_split(const DecodeArgs& d, bool f16, hipStream_t s) {
+    if (d.D <= 256 || d.D > 1024 || d.D % 8 != 0) return hipErrorInvalidValue;
+    ForwardArgs a;
+    a.q = d.q;
+    a.k = d.k;
+    a.v = d.v;
+    a.out = nullptr;
+    a.key_lens = d.key_lens;
+    a.B = d.B;
+    a.Hq = d.Hq;
+    a.Hkv = d.Hkv;
+    a.Sq = 1;
+    a.Sk = d.Sk;
+    a.D = d.D;
+    a.scale = d.scale;
+    a.causal = false;
+    a.padded = d.key_lens != nullptr;
+    const WideDec w{d.o_part, d.lse_part, d.splits};
+    return f16 ? launch_wide_dec_t<F16T>(a, w, s) : launch_wide_dec_t<Bf16T>(a, w, s);
 }
 
 }  // namespace sdpa

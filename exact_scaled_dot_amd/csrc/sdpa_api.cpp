@@ -52,9 +52,10 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // (the 64-, 128- and 256-wide kernels read the missing chunks as zeros),
 // fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
 // kernel).  max16: the widest 16-bit head dim of the entry point (1024 for
-// the dense forward, whose heads above 256 run on the head-dim-split
-// kernel; 256 for decode, paged attention and the block; 128 for the
-// backward, whose lanes hold a full-width operand and gradient).
+// the dense forward and dense decode, whose heads above 256 run on the
+// head-dim-split kernel; 256 for paged attention, paged prefill and the
+// block; 128 for the backward, whose lanes hold a full-width operand and
+// gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
     return D >= 8 && D <= max16 && D % 8 == 0;
@@ -536,7 +537,7 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
                           size_t workspace_bytes, void* out, int dtype, void* stream) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st =
-        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes, 256);
+        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes, 1024);
     if (st != SDPA_OK) return st;
     if (num_splits < 1 || num_splits > SDPA_MAX_SPLITS)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..%d", num_splits,

@@ -92,12 +92,15 @@ enum {
  *   out      device [B, Hq, Sq, D], dtype; written completely
  *   dtype    SDPA_BF16, SDPA_F16 or SDPA_F32
  *   stream   hipStream_t as void*
- * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 256
- * (the 64-, 128- and 256-wide kernels, with the dims past D read as zeros on
- * chip; above 128 two workgroups per query block each produce 128 output
- * dims and both compute the scores), SDPA_F32 any multiple of 4 from 4 to
- * 128 (the 64- and 128-wide fp32 kernels, likewise); one head (Sq*D or
- * Sk*D elements) must be under 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
+ * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 1024
+ * (ruDNN user guide section 9 allows up to 1024): up to 256 on the 64-, 128-
+ * and 256-wide kernels, with the dims past D read as zeros on chip (above
+ * 128 two workgroups per query block each produce 128 output dims and both
+ * compute the scores); above 256 on a kernel that splits the head dim over
+ * 4, 6 or 8 waves of 128 dims per 32-row query block (partial scores summed
+ * in LDS).  SDPA_F32 any multiple of 4 from 4 to 128 (the 64- and 128-wide
+ * fp32 kernels, likewise).  One head (Sq*D or Sk*D elements) must be under
+ * 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
  */
 sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
@@ -130,8 +133,8 @@ sdpa_status_t sdpa_forward_lse(const void *q, const void *k, const void *v,
  *              (lse -inf).
  *   lse        NULL, or device float [B, Hq, Sq] as in sdpa_forward_lse
  * Every other argument as sdpa_forward.  The bias is read once per 128-row
- * query block (and output slice, D > 128).  Supported: dtype SDPA_BF16 or
- * SDPA_F16, D a multiple of 8 up to 256, bias
+ * query block (and output slice, 128 < D <= 256; by every wave above 256).
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024, bias
  * rows 16-byte aligned (Sk, bias_stride_b and bias_stride_h multiples of 8,
  * pointer 16-byte aligned), one head's bias (Sq * Sk elements) under 2 GiB
  * (SDPA_ERR_UNSUPPORTED otherwise).  out and lse must not overlap the bias.
@@ -285,8 +288,11 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
  *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
  *   out        device [B, Hq, 1, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 256
- * (above 128 each wave's LDS ring holds two 16-key steps instead of four).
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024
+ * (above 128 each wave's LDS ring holds two 16-key steps instead of four;
+ * above 256 the split pass runs on the head-dim-split kernel of
+ * sdpa_forward, with up to 32 query heads of a K/V group as its rows, and
+ * writes the same partials).
  */
 sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D,

@@ -109,7 +109,7 @@ def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1,
     (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "up to 256"),     # the decode kernel stops at 256
+    (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),   # the widest decode is 1024
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
 ])
 def test_decode_rejects(kw, status, needle):

@@ -358,3 +358,28 @@ def test_forward_headdim_split_full_size_sampled_rows():
     compare(got, ref, BF16, "D=1024 full size")
     glse = to64(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
     assert np.abs(glse - rlse).max() < 1e-2
+
+
+@pytest.mark.parametrize("D", [264, 512, 1024])
+@pytest.mark.parametrize("splits", [1, 5, 32])
+def test_decode_headdim_split(D, splits):
+    # grouped heads 16/4; key limits with an empty batch (every split empty:
+    # NaN) and short ones (several empty splits)
+    B, Hq, Hkv, Sk = 4, 16, 4, 1000
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 960 + D + splits, DEV)
+    lens = torch.tensor([1000, 0, 333, 17], dtype=torch.int32, device=DEV)
+    out = sd.sdpa_decode(q, k, v, 1 / math.sqrt(D), lens, splits)
+    torch.cuda.synchronize()
+    ref = O.sdpa_decode(to64(q), to64(k), to64(v), 1 / math.sqrt(D), lens.cpu().numpy())
+    compare(to64(out), ref, BF16, "split decode D=%d splits=%d" % (D, splits))
+    assert torch.isnan(out[1]).all()
+
+
+def test_decode_headdim_split_large_group_fp16():
+    # 40 query heads per K/V head: two 32-head row blocks; fp16; no key_lens
+    B, Hq, Hkv, Sk, D = 2, 80, 2, 777, 640
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, F16, 970, DEV)
+    out = sd.sdpa_decode(q, k, v, 0.04, None, 7)
+    torch.cuda.synchronize()
+    ref = O.sdpa_decode(to64(q), to64(k), to64(v), 0.04, None)
+    compare(to64(out), ref, F16, "split decode fp16 G=40 D=640")
