@@ -88,6 +88,12 @@ def stored_traffic(workload, source):
     return rec.get("hbm_bytes_per_launch")
 
 
+def pair_traffic(a, b, src_a, src_b=None):
+    """HBM bytes of a split pass and its merge, if both records are valid."""
+    parts = [stored_traffic(a, src_a), stored_traffic(b, src_b or src_a)]
+    return None if None in parts else sum(parts)
+
+
 def backward_traffic():
     """HBM bytes of one backward call (both passes), if both records are valid."""
     parts = [stored_traffic(k, "backward.hip") for k in ("backward_dq", "backward_dkdv")]
@@ -201,9 +207,12 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
         for i, key in enumerate(("prefill", "padded", "paged_prefill", "bias", "wide", "block_attn",
                                  "block_small_attn")):
             out[key] = entry(fwd, "forward.hip", fr[i::7], wr[i::7])
-    if "forward_wide_kernel" in fetch:
-        out["widest"] = entry("forward_wide_kernel", "forward_wide.hip", fetch["forward_wide_kernel"],
-                              write["forward_wide_kernel"])
+    # the head-dim-split kernel: the widest prefill, then the widest decode's
+    # split pass
+    fw = "forward_wide_kernel"
+    if fw in fetch:
+        out["widest"] = entry(fw, "forward_wide.hip", fetch[fw][0::2], write[fw][0::2])
+        out["decode_widest_split"] = entry(fw, "forward_wide.hip", fetch[fw][1::2], write[fw][1::2])
     # each block call: q/k/v projection GEMM, attention, output projection
     # GEMM; a step runs the large block, then the small one (names are
     # truncated, so the four GEMM dispatches of a step are told apart by order)
@@ -225,14 +234,17 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
                       ("backward_atomic_convert", "bwd_dq_convert_kernel")):
         if name in fetch:
             out[key] = entry(name, "backward.hip", fetch[name], write[name])
-    # A full step runs the dense decode, then the paged one: their split and
-    # merge dispatches alternate.
-    for key, name in (("decode_split", "decode_split_bf16_kernel"),
-                      ("decode_merge", "decode_merge_bf16_kernel")):
-        if name in fetch:
-            out[key] = entry(name, "decode.hip", fetch[name][0::2], write[name][0::2])
-            out["paged_" + key.split("_")[1]] = entry(name, "decode.hip", fetch[name][1::2],
-                                                      write[name][1::2])
+    # A full step runs the dense decode, the paged one and the 256-wide one
+    # (split and merge each), then the 1024-wide one (its own split kernel,
+    # the same merge kernel): 3 split and 4 merge dispatches per step.
+    sp, mg = "decode_split_bf16_kernel", "decode_merge_bf16_kernel"
+    if sp in fetch:
+        for i, key in enumerate(("decode_split", "paged_split", "decode_wide_split")):
+            out[key] = entry(sp, "decode.hip", fetch[sp][i::3], write[sp][i::3])
+    if mg in fetch:
+        for i, key in enumerate(("decode_merge", "paged_merge", "decode_wide_merge",
+                                 "decode_widest_merge")):
+            out[key] = entry(mg, "decode.hip", fetch[mg][i::4], write[mg][i::4])
     return out
 
 
@@ -609,7 +621,8 @@ def main():
                               "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                            "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                           "traffic": None,
+                                           "traffic": pair_traffic("decode_wide_split",
+                                                                   "decode_wide_merge", "decode.hip"),
                                            "kernel": "decode_split_bf16_kernel<256> + merge",
                                            "bytes_per_launch": by}}
     if "decode_widest" in ms:
@@ -621,7 +634,10 @@ def main():
                                 "unit": "GB/s", "num_splits": wd.num_splits,
                                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                             "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                             "traffic": pair_traffic("decode_widest_split",
+                                                                     "decode_widest_merge",
+                                                                     "forward_wide.hip", "decode.hip"),
                                              "kernel": "forward_wide_kernel<8, decode> + merge",
                                              "bytes_per_launch": by}}
     for name, (B, S, M, H) in BLOCKS.items():
