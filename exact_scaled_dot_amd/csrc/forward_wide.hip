@@ -14,7 +14,7 @@
 // (B operands) and its slice of O^T stay in registers.  Per 16-key tile:
 //   A  every wave: partial S^T = K_w Q_w^T over its dims
 //      (v_mfma_f32_16x16x32; K fragments straight from HBM into registers,
-//      one tile ahead), written to LDS in fp32 (two buffers, alternating);
+//      two tiles ahead), written to LDS in fp32 (two buffers, alternating);
 //   -  one barrier;
 //   B  every wave: each lane sums the NW partials of exactly the scores it
 //      feeds to the P.V product (query lane%32, keys 8*(lane/32) .. +7),
@@ -26,9 +26,9 @@
 //      O^T += V_w^T P^T (v_mfma_f32_32x32x16; V^T by transposed LDS reads
 //      from the wave's own V tiles, which arrive by buffer-load DMA two
 //      tiles ahead into a 3-stage ring per wave).
-// Each V DMA is issued before the K loads of the next tile, and vmcnt
-// counts in issue order, so the compiler's wait for those K fragments also
-// covers the V tile: no explicit wait is needed for V.
+// The V tile of step j is issued right before the K fragments of step j, and
+// vmcnt counts in issue order, so the compiler's wait for those K fragments
+// also covers the V tile: no explicit wait is needed for V.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -246,13 +246,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int poff0 = qr * kWKeys + (((2 * kh + (qr >> 2)) & 3) * 4);
     const int poff1 = qr * kWKeys + (((2 * kh + 1 + (qr >> 2)) & 3) * 4);
 
-    u32x4 kcur[4], knext[4];
+    // K fragments: a ring of three tiles (this one and the next two).
+    u32x4 kr0[4], kr1[4], kr2[4];
     if (ntiles > 0) load_v(k_lo, 0);
+    asm volatile("" ::: "memory");
+    if (ntiles > 0) load_k(k_lo, kr0);
+    asm volatile("" ::: "memory");
     if (ntiles > 1) load_v(k_lo + kWKeys, 1);
     asm volatile("" ::: "memory");
-    if (ntiles > 0) load_k(k_lo, kcur);
+    if (ntiles > 1) load_k(k_lo + kWKeys, kr1);
 
-    auto tile = [&](int j, u32x4* kc, u32x4* kn) __attribute__((always_inline)) {
+    auto tile = [&](int j, u32x4* kc, u32x4* kn2) __attribute__((always_inline)) {
         const int kt = k_lo + j * kWKeys;
         float* const pb = part + (j & 1) * LY::PBUF;
         // (BIAS) this lane's 8 bias values first, so that waiting for them
@@ -263,11 +267,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             bw = __builtin_amdgcn_raw_buffer_load_b128(
                 rb, (qa < a.Sq && key < a.Sk) ? ((uint32_t)qa * a.Sk + key) * 2 : kWOutside, 0, 0);
         }
-        // V two tiles ahead, then K one tile ahead (in this order: the wait
-        // for K(j+1) at the next tile then also covers V(j+2))
+        // V and K two tiles ahead, V first: the wait for K(j+2) two tiles
+        // from now then also covers V(j+2)
         if (j + 2 < ntiles) load_v(kt + 2 * kWKeys, (j + 2) % kWVStages);
         asm volatile("" ::: "memory");
-        if (j + 1 < ntiles) load_k(kt + kWKeys, kn);
+        if (j + 2 < ntiles) load_k(kt + 2 * kWKeys, kn2);
 
         // A: partial S^T over this wave's dims; register i of block qb holds
         // key kt + 4*(lane/16) + i of query 16qb + lane%16.
@@ -344,9 +348,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             acc[db] = mfma_32x32x16<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, acc[db]);
         }
     };
-    for (int j = 0; j < ntiles; j += 2) {
-        tile(j, kcur, knext);
-        if (j + 1 < ntiles) tile(j + 1, knext, kcur);
+    for (int j = 0; j < ntiles; j += 3) {
+        tile(j, kr0, kr2);
+        if (j + 1 < ntiles) tile(j + 1, kr1, kr0);
+        if (j + 2 < ntiles) tile(j + 2, kr2, kr1);
     }
 
     // Row sum (both halves) and log-sum-exp.
