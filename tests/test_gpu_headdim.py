@@ -383,3 +383,21 @@ def test_decode_headdim_split_large_group_fp16():
     torch.cuda.synchronize()
     ref = O.sdpa_decode(to64(q), to64(k), to64(v), 0.04, None)
     compare(to64(out), ref, F16, "split decode fp16 G=40 D=640")
+
+
+def test_decode_headdim_split_full_size_sampled_heads():
+    # the 1024-wide decode leg at full size (B8, 32/8 heads, 32768 cached
+    # keys, 32 splits; batch 5 padded to 20001 keys); the oracle checks every
+    # query head of two (batch, K/V head) groups
+    B, Hq, Hkv, Sk, D, splits = 8, 32, 8, 32768, 1024, 32
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 980, DEV)
+    lens = torch.full((B,), Sk, dtype=torch.int32, device=DEV)
+    lens[5] = 20001
+    out = sd.sdpa_decode(q, k, v, 1 / math.sqrt(D), lens, splits)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for b, g in ((0, 3), (5, 6)):
+        hs = slice(g * G, (g + 1) * G)
+        ref = O.sdpa_decode(to64(q[b:b + 1, hs]), to64(k[b:b + 1, g:g + 1]), to64(v[b:b + 1, g:g + 1]),
+                            1 / math.sqrt(D), lens[b:b + 1].cpu().numpy())
+        compare(to64(out[b:b + 1, hs]), ref, BF16, "D=1024 decode b=%d group=%d" % (b, g))
