@@ -498,10 +498,10 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
-    if (!PAGED && a.D > 256 && a.D <= 1024 && a.D % 8 == 0) {
+    if (a.D > 256 && a.D <= 1024 && a.D % 8 == 0) {
         // Wider heads: the head-dim-split kernel writes the same partials,
         // then the same merge (D/4 threads per row).
-        const hipError_t ew = launch_decode_wide_split(a, T::kF16, s);
+        const hipError_t ew = launch_decode_wide_split(a, PAGED ? &p : nullptr, T::kF16, s);
         if (ew != hipSuccess) return ew;
         const int dw = a.D <= 512 ? 512 : 1024;
         const dim3 mg((unsigned)(((int64_t)a.B * a.Hq * dw / 4 + 255) / 256));

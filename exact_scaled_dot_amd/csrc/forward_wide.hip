@@ -107,16 +107,32 @@ __device__ __forceinline__ int w_xcd_order(int total) {
 // (split) of one (batch, K/V head) for up to 32 query heads of its group
 // (the rows), Sq = 1, and writes its normalised fp32 partial output and
 // natural-log lse into the split-KV workspace for the merge pass.
+//
+// PAGED (with DEC): K and V come from page caches [pages, page_size, Hkv, D]
+// through the query's sequence's page table (B = queries); a query sees the
+// keys below its sequence's length and, under the causal flag, up to its
+// absolute position.  The split length is a multiple of 16, so a 16-key tile
+// lies in one page, found with one table lookup; an entry outside
+// [0, pages) is never dereferenced (no records: zeros) and its keys are
+// masked.
 struct WideDec {
     float* o_part;    // [B, Hq, splits, D]
     float* lse_part;  // [B, Hq, splits]
     int splits;
+    const int32_t* tables;     // [num_seqs, max_pages]   (PAGED)
+    const int32_t* seq_lens;   // [num_seqs]
+    const int32_t* query_seq;  // [queries]
+    const int32_t* query_pos;  // [queries]
+    int num_seqs, max_pages, pages, page_size;
+    bool causal;
 };
 
-template <int NW, class T, bool BIAS, bool DEC>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(ForwardArgs a,
-                                                                  const int32_t* __restrict__ key_lens,
-                                                                  WideDec dec) {
+template <int NW, class T, bool BIAS, bool DEC, bool PAGED = false>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
+    ForwardArgs a, const int32_t* __restrict__ key_lens, WideDec dec, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_seq,
+    const int32_t* __restrict__ query_pos) {
+    static_assert(!PAGED || DEC, "the paged policy is a decode form");
     using LY = WideLds<NW>;
     __shared__ __attribute__((aligned(1024))) float smem[LY::FLOATS];
     float* const part = smem;
@@ -158,10 +174,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int64_t bh = (int64_t)b * a.Hq + h;
 
     // Visible keys [k_lo, kv_lim): DEC takes its split's range.
-    int kv_lim = a.Sk, k_lo = 0;
+    int kv_lim = a.Sk, k_lo = 0, seq = 0;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
+    if constexpr (PAGED) {
+        seq = query_seq[b];
+        if (seq >= 0 && seq < dec.num_seqs) {
+            kv_lim = min(kv_lim, seq_lens[seq]);
+            if (dec.causal) kv_lim = min(kv_lim, query_pos[b] + 1);
+        } else {
+            kv_lim = 0;
+        }
+    }
     if constexpr (DEC) {
-        const int chunk = (a.Sk + dec.splits - 1) / dec.splits;
+        int chunk = (a.Sk + dec.splits - 1) / dec.splits;
+        if (PAGED) chunk = (chunk + kWKeys - 1) / kWKeys * kWKeys;  // whole tiles per split
         k_lo = split * chunk;
         kv_lim = min(kv_lim, k_lo + chunk);
     }
@@ -174,6 +200,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
     const __amdgpu_buffer_rsrc_t rk = w_rsrc(static_cast<const uint16_t*>(a.k) + kvh, kvbytes);
     const __amdgpu_buffer_rsrc_t rv = w_rsrc(static_cast<const uint16_t*>(a.v) + kvh, kvbytes);
+    // Where the 16 keys from kt live: dense, rows of D from the head's start;
+    // PAGED, rows of Hkv*D in the tile's page (head gk's columns), or no
+    // records at all for an invalid table entry.
+    struct Src {
+        __amdgpu_buffer_rsrc_t k, v;
+        uint32_t row0, rstride, col0;
+        bool ok;
+    };
+    auto src = [&](int kt) -> Src {
+        if constexpr (PAGED) {
+            const int lp = kt / dec.page_size;
+            const int pg = lp < dec.max_pages ? tables[(int64_t)seq * dec.max_pages + lp] : -1;
+            const bool ok = pg >= 0 && pg < dec.pages;
+            const uint32_t pbytes = ok ? (uint32_t)dec.page_size * a.Hkv * D * 2 : 0u;
+            const int64_t off = ok ? (int64_t)pg * dec.page_size * a.Hkv * D : 0;
+            return Src{w_rsrc(static_cast<const uint16_t*>(a.k) + off, pbytes),
+                       w_rsrc(static_cast<const uint16_t*>(a.v) + off, pbytes), (uint32_t)(kt % dec.page_size),
+                       (uint32_t)(a.Hkv * D), (uint32_t)(gk * D), ok};
+        } else {
+            return Src{rk, rv, (uint32_t)kt, (uint32_t)D, 0u, true};
+        }
+    };
 
     // Q^T as B operands of the 16x16x32 products: column 16qb + lane%16 (a
     // query), dims d0 + 32s + 8*(lane/16) .. +7 (rows past Sq and dims past D
@@ -197,11 +245,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     }
     // K fragments (A operands): key kt + lane%16, dims d0 + 32s + 8*(lane/16).
     auto load_k = [&](int kt, u32x4* kf) {
+        const Src sr = src(kt);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int dim = d0 + 32 * s + 8 * g4;
             kf[s] = __builtin_amdgcn_raw_buffer_load_b128(
-                rk, dim < D ? ((uint32_t)(kt + l16) * D + dim) * 2 : kWOutside, 0, 0);
+                sr.k, dim < D ? ((sr.row0 + l16) * sr.rstride + sr.col0 + dim) * 2 : kWOutside, 0, 0);
         }
     };
     // V tile of keys kt .. kt+15, this wave's dims, into ring stage st: DMA i
@@ -211,10 +260,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int vchunk = (lane & 15) ^ (4 * g4);
     const bool vdim_ok = d0 + 8 * vchunk < D;
     auto load_v = [&](int kt, int st) {
+        const Src sr = src(kt);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w_dma(rv, vw + st * LY::VST + 512 * i,
-                  vdim_ok ? ((uint32_t)(kt + 4 * i + g4) * D + d0 + 8 * vchunk) * 2 : kWOutside);
+            w_dma(sr.v, vw + st * LY::VST + 512 * i,
+                  vdim_ok ? ((sr.row0 + 4 * i + g4) * sr.rstride + sr.col0 + d0 + 8 * vchunk) * 2 : kWOutside);
     };
     // Transposed-read offsets (32x32x16 A operand = V^T): lane reads rows
     // (keys) 8*(lane/32) + (lane%16)/4 (+4 for the upper half), dims
@@ -311,6 +361,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             }
         }
         const int key0 = kt + 8 * kh;
+        if constexpr (PAGED) {
+            if (!src(kt).ok) {  // the tile's page is invalid: its keys are hidden
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
+            }
+        }
         const bool edge = key0 + 8 > kv_lim || (a.causal && key0 + 7 > qa);
         if (edge) {
 #pragma unroll
@@ -409,28 +465,30 @@ template <int NW, class T>
 hipError_t launch_wide_nw(const ForwardArgs& a, hipStream_t s) {
     const int nqb = (a.Sq + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hq * nqb));
+    const int32_t* none = nullptr;
     if (a.bias)
         hipLaunchKernelGGL((forward_wide_kernel<NW, T, true, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens,
-                           WideDec{});
+                           WideDec{}, none, none, none, none);
     else
         hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens,
-                           WideDec{});
+                           WideDec{}, none, none, none, none);
     return hipGetLastError();
 }
 
-template <int NW, class T>
+template <int NW, class T, bool PAGED>
 hipError_t launch_wide_dec_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
     const int nhb = (a.Hq / a.Hkv + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hkv * d.splits * nhb));
-    hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true>), grid, dim3(NW * 64), 0, s, a, a.key_lens, d);
+    hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true, PAGED>), grid, dim3(NW * 64), 0, s, a, a.key_lens, d,
+                       d.tables, d.seq_lens, d.query_seq, d.query_pos);
     return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool PAGED>
 hipError_t launch_wide_dec_t(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
-    if (a.D <= 4 * kWChunk) return launch_wide_dec_nw<4, T>(a, d, s);
-    if (a.D <= 6 * kWChunk) return launch_wide_dec_nw<6, T>(a, d, s);
-    return launch_wide_dec_nw<8, T>(a, d, s);
+    if (a.D <= 4 * kWChunk) return launch_wide_dec_nw<4, T, PAGED>(a, d, s);
+    if (a.D <= 6 * kWChunk) return launch_wide_dec_nw<6, T, PAGED>(a, d, s);
+    return launch_wide_dec_nw<8, T, PAGED>(a, d, s);
 }
 
 template <class T>
@@ -447,7 +505,7 @@ hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s) {
     return f16 ? launch_wide_t<F16T>(a, s) : launch_wide_t<Bf16T>(a, s);
 }
 
-hipError_t launch_decode_wide_split(const DecodeArgs& d, bool f16, hipStream_t s) {
+hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, bool f16, hipStream_t s) {
     if (d.D <= 256 || d.D > 1024 || d.D % 8 != 0) return hipErrorInvalidValue;
     ForwardArgs a;
     a.q = d.q;
@@ -464,8 +522,20 @@ hipError_t launch_decode_wide_split(const DecodeArgs& d, bool f16, hipStream_t s
     a.scale = d.scale;
     a.causal = false;
     a.padded = d.key_lens != nullptr;
-    const WideDec w{d.o_part, d.lse_part, d.splits};
-    return f16 ? launch_wide_dec_t<F16T>(a, w, s) : launch_wide_dec_t<Bf16T>(a, w, s);
+    WideDec w{d.o_part, d.lse_part, d.splits, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, false};
+    if (p) {
+        w.tables = p->block_tables;
+        w.seq_lens = p->seq_lens;
+        w.query_seq = p->query_seq;
+        w.query_pos = p->query_pos;
+        w.num_seqs = p->num_seqs;
+        w.max_pages = p->max_pages;
+        w.pages = p->pages;
+        w.page_size = p->page_size;
+        w.causal = p->causal;
+        return f16 ? launch_wide_dec_t<F16T, true>(a, w, s) : launch_wide_dec_t<Bf16T, true>(a, w, s);
+    }
+    return f16 ? launch_wide_dec_t<F16T, false>(a, w, s) : launch_wide_dec_t<Bf16T, false>(a, w, s);
 }
 
 }  // namespace sdpa

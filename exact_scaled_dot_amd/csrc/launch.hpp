@@ -111,9 +111,10 @@ hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s)
 
 // Split-KV decode and paged attention, bf16 or (f16) fp16.
 hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s);
-// The split pass of dense decode for 256 < D <= 1024 (head-dim-split kernel);
-// writes a.o_part / a.lse_part like the narrow split pass.
-hipError_t launch_decode_wide_split(const DecodeArgs& a, bool f16, hipStream_t s);
+// The split pass of decode for 256 < D <= 1024 (head-dim-split kernel), dense
+// (p == nullptr) or through a page cache; writes a.o_part / a.lse_part like
+// the narrow split pass.
+hipError_t launch_decode_wide_split(const DecodeArgs& a, const PagedArgs* p, bool f16, hipStream_t s);
 hipError_t launch_paged_16bit(const DecodeArgs& a, const PagedArgs& p, bool f16, hipStream_t s);
 
 // Work items of the decode split pass: (batch, K/V head, block of <= 16 query

@@ -52,10 +52,9 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // (the 64-, 128- and 256-wide kernels read the missing chunks as zeros),
 // fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
 // kernel).  max16: the widest 16-bit head dim of the entry point (1024 for
-// the dense forward and dense decode, whose heads above 256 run on the
-// head-dim-split kernel; 256 for paged attention, paged prefill and the
-// block; 128 for the backward, whose lanes hold a full-width operand and
-// gradient).
+// the dense forward, decode and paged attention, whose heads above 256 run
+// on the head-dim-split kernel; 256 for paged prefill and the block; 128 for
+// the backward, whose lanes hold a full-width operand and gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
     return D >= 8 && D <= max16 && D % 8 == 0;
@@ -635,8 +634,8 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     if (queries > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (!head_dim_ok(D, dtype, 256))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 256)",
+    if (!head_dim_ok(D, dtype, 1024))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 1024)",
                     (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 and fp16 only");

@@ -327,9 +327,9 @@ sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
  *                (same layout as sdpa_decode's with B = queries)
  *   out          device [queries, Hq, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 256,
- * page_size a
- * multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024
+ * (above 256 the split pass runs on the head-dim-split kernel, as in
+ * sdpa_decode), page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
  * [0, num_seqs), a negative query_pos under the causal flag, or a sequence

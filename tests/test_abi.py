@@ -170,7 +170,7 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_
     (dict(ws_bytes=64), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(out=ctypes.c_void_p(0x7a000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
     (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),

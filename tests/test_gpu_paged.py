@@ -291,3 +291,50 @@ def test_full_size_paged_prefill_sampled():
     ref = O.paged_attention(to64(inp["q"])[rows], kc, vc, inp["block_tables"].cpu().numpy(),
                             np.array([L] * n), qs[rows], qp[rows], scale, True)
     compare(got[rows], ref, torch.bfloat16, "full-size paged prefill rows")
+
+
+# ------------------------------------------------- head dims above 256 (to 1024)
+# The split pass runs on the head-dim-split kernel with the page policy.
+
+@pytest.mark.parametrize("D", [264, 512, 1024])
+@pytest.mark.parametrize("page_size,splits", [(16, 1), (32, 5), (64, 32)])
+def test_paged_decode_headdim_split(D, page_size, splits):
+    for causal in (True, False):
+        check([300, 129, 1], [0, 1, 1, 2], [299, 128, 64, 0], 8, 2, D, page_size, causal, splits,
+              seed=990 + D + page_size + causal)
+
+
+def test_paged_headdim_split_empty_out_of_range_and_invalid_pages():
+    D = 640
+    inp, out, scale = run_paged([0, 50, 30], [0, 1, 2, 1, 1], [0, 49, 29, 10, 20], 4, 2, D, 16,
+                                True, 4, seed=996)
+    inp["query_seq"][3] = 7
+    inp["query_pos"][4] = -1
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, True,
+                                  64, 4)
+    torch.cuda.synchronize()
+    got = to64(out)
+    assert np.isnan(got[[0, 3, 4]]).all()
+    keep = [1, 2]
+    ref = O.paged_attention(to64(inp["q"])[keep], to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            inp["block_tables"].cpu().numpy(), inp["seq_lens"].cpu().numpy(),
+                            inp["query_seq"].cpu().numpy()[keep], inp["query_pos"].cpu().numpy()[keep],
+                            scale, True)
+    compare(got[keep], ref, torch.bfloat16, "D=640: valid rows next to empty ones")
+    inp, out, scale = run_paged([64], [0, 0], [63, 63], 4, 2, D, 16, False, 2, seed=997,
+                                tables=[[0, -1, 2, 99999]])
+    valid = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                              np.array([[0, 2]]), np.array([32]), np.array([0, 0]),
+                              np.array([31, 31]), scale, False)
+    compare(to64(out), valid, torch.bfloat16, "D=640: invalid pages hidden")
+
+
+def test_paged_headdim_split_matches_dense_decode():
+    # one query per sequence at its last position over 16-key pages equals the
+    # dense decode of the same keys (both on the head-dim-split kernel)
+    D, Hq, Hkv, lens = 512, 8, 2, [500, 77, 256]
+    inp, out, scale = run_paged(lens, [0, 1, 2], [l - 1 for l in lens], Hq, Hkv, D, 16, True, 6,
+                                seed=998)
+    ref = oracle_of(inp, scale, True)
+    compare(to64(out), ref, torch.bfloat16, "paged D=512 decode")
