@@ -155,9 +155,9 @@ __global__ __launch_bounds__(kGThreads, WM * WN >= 16 ? 1 : 2) void gemm_kernel(
             const int k = k0 + a_kx[i];
             uint32_t part = 2u * (uint32_t)k;
             if (AH) {
-                // head h = k / hd by a float reciprocal: k < 2^16 and hd <= 128
-                // keep (k + 1/2) / hd at least 2^-16 (relative) from an integer,
-                // far above the product's rounding error
+                // head h = k / hd by a float reciprocal: (k + 1/2) / hd is at
+                // least 1/(2 hd) from an integer, i.e. (k < 2^16) at least
+                // 2^-17 of its value, far above the product's rounding error
                 const int h = (int)(((float)k + 0.5f) * inv_hd);
                 part = 2u * ((uint32_t)h * (uint32_t)(g.S * g.hd) + (uint32_t)(k - h * g.hd));
             }

@@ -52,8 +52,8 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // (the 64-, 128- and 256-wide kernels read the missing chunks as zeros),
 // fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
 // kernel).  max16: the widest 16-bit head dim of the entry point (1024 for
-// the dense forward, decode and paged attention, whose heads above 256 run
-// on the head-dim-split kernel; 256 for paged prefill and the block; 128 for
+// the dense forward, decode, paged attention and the block, whose heads
+// above 256 run on the head-dim-split kernel; 256 for paged prefill; 128 for
 // the backward, whose lanes hold a full-width operand and gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
@@ -439,8 +439,8 @@ sdpa_status_t sdpa_block_forward(const void* x, const void* wq, const void* wk, 
         return fail(SDPA_ERR_INVALID_ARGUMENT, "model width %lld is not a multiple of heads %lld",
                     (long long)model, (long long)heads);
     const int64_t hd = model / heads;
-    if (!head_dim_ok(hd, dtype, 256))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld not supported (a multiple of 8 up to 256)",
+    if (!head_dim_ok(hd, dtype, 1024))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld not supported (a multiple of 8 up to 1024)",
                     (long long)hd);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");

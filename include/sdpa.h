@@ -256,7 +256,7 @@ size_t sdpa_block_workspace_size(int64_t B, int64_t S, int64_t model);
  * straight into head layout), the attention, and the output projection
  * (reading the attention output from head layout).  Products accumulate in
  * fp32; q, k, v, the attention output and y are rounded to dtype.
- * Supported: dtype SDPA_BF16 or SDPA_F16, headDim a multiple of 8 up to 256,
+ * Supported: dtype SDPA_BF16 or SDPA_F16, headDim a multiple of 8 up to 1024,
  * x and each weight under 2 GiB.  y and the workspace must not overlap each
  * other or any input.
  */

@@ -350,7 +350,7 @@ def block(x=FAKE, wq=FAKE_K, wk=FAKE_V, wv=FAKE_O, wo=FAKE_W, B=2, S=128, model=
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
     (dict(dtype=9), sd.SDPA_ERR_INVALID_ARGUMENT, "dtype"),
     (dict(model=500), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
-    (dict(model=2112), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 264 wide
+    (dict(model=8256), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),   # 1032 wide
     (dict(model=168, heads=2), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # 84 wide
     (dict(scale=float("nan")), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
     (dict(mask=4), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),

@@ -401,3 +401,17 @@ def test_decode_headdim_split_full_size_sampled_heads():
         ref = O.sdpa_decode(to64(q[b:b + 1, hs]), to64(k[b:b + 1, g:g + 1]), to64(v[b:b + 1, g:g + 1]),
                             1 / math.sqrt(D), lens[b:b + 1].cpu().numpy())
         compare(to64(out[b:b + 1, hs]), ref, BF16, "D=1024 decode b=%d group=%d" % (b, g))
+
+
+@pytest.mark.parametrize("model,heads", [(1024, 2), (2048, 2), (1536, 3)])
+def test_block_headdim_split(model, heads):
+    # attention blocks whose heads are 512, 1024 and 512 wide: the projections
+    # address the wide head layout, the attention runs on the head-dim-split
+    # kernel
+    from exact_scaled_dot_amd.workloads import draw_block
+    from parity import compare_block
+    x, wq, wk, wv, wo = draw_block(2, 100, model, BF16, 1000 + model + heads, DEV)
+    y = sd.sdpa_block_forward(x, wq, wk, wv, wo, heads, None, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    ref = O.block_forward(to64(x), to64(wq), to64(wk), to64(wv), to64(wo), heads, None, O.MASK_CAUSAL)
+    compare_block(to64(y), ref, BF16, "block model=%d heads=%d" % (model, heads))
