@@ -108,13 +108,17 @@ __device__ __forceinline__ int w_xcd_order(int total) {
 // (the rows), Sq = 1, and writes its normalised fp32 partial output and
 // natural-log lse into the split-KV workspace for the merge pass.
 //
-// PAGED (with DEC): K and V come from page caches [pages, page_size, Hkv, D]
-// through the query's sequence's page table (B = queries); a query sees the
-// keys below its sequence's length and, under the causal flag, up to its
-// absolute position.  The split length is a multiple of 16, so a 16-key tile
-// lies in one page, found with one table lookup; an entry outside
+// PAGED: K and V come from page caches [pages, page_size, Hkv, D] through a
+// sequence's page table.  A 16-key tile lies in one page (page sizes are
+// multiples of 16), found with one table lookup; an entry outside
 // [0, pages) is never dereferenced (no records: zeros) and its keys are
-// masked.
+// masked.  With DEC (paged attention, B = queries): a query sees the keys
+// below its sequence's length and, under the causal flag, up to its
+// absolute position; split lengths are multiples of 16.  Without DEC
+// (prefill chunks, B = sequences, Sq = the longest chunk): the workgroup's
+// rows are rows q0 .. q0+31 of sequence b's chunk, packed rows
+// cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q / out ([rows, Hq, D]), and row i
+// sits at absolute position seq_lens[b] - n_b + i.
 struct WideDec {
     float* o_part;    // [B, Hq, splits, D]
     float* lse_part;  // [B, Hq, splits]
@@ -125,6 +129,8 @@ struct WideDec {
     const int32_t* query_pos;  // [queries]
     int num_seqs, max_pages, pages, page_size;
     bool causal;
+    const int32_t* cu_q;  // [num_seqs + 1]  (PAGED prefill chunks)
+    int total_q;
 };
 
 template <int NW, class T, bool BIAS, bool DEC, bool PAGED = false>
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     ForwardArgs a, const int32_t* __restrict__ key_lens, WideDec dec, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_seq,
     const int32_t* __restrict__ query_pos) {
-    static_assert(!PAGED || DEC, "the paged policy is a decode form");
+
     using LY = WideLds<NW>;
     __shared__ __attribute__((aligned(1024))) float smem[LY::FLOATS];
     float* const part = smem;
@@ -173,10 +179,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     }
     const int64_t bh = (int64_t)b * a.Hq + h;
 
-    // Visible keys [k_lo, kv_lim): DEC takes its split's range.
-    int kv_lim = a.Sk, k_lo = 0, seq = 0;
+    // Visible keys [k_lo, kv_lim): DEC takes its split's range.  PAGED
+    // prefill: this sequence's chunk rows (qbase, qstride) and the absolute
+    // position qpos0 of its first row.
+    int kv_lim = a.Sk, k_lo = 0, seq = 0, nrows = a.Sq, qpos0 = 0;
+    const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * D;
+    uint16_t* obase = static_cast<uint16_t*>(a.out) + bh * a.Sq * D;
+    int64_t qstride = D;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
-    if constexpr (PAGED) {
+    if constexpr (PAGED && !DEC) {
+        const int r0 = min(max(dec.cu_q[b], 0), dec.total_q);
+        const int r1 = min(max(dec.cu_q[b + 1], r0), dec.total_q);
+        nrows = r1 - r0;
+        if (q0 >= nrows) return;  // the whole workgroup, before any barrier
+        seq = b;
+        kv_lim = min(seq_lens[b], a.Sk);
+        qpos0 = kv_lim - nrows;
+        const int64_t rb = ((int64_t)r0 * a.Hq + h) * D;
+        qbase = static_cast<const uint16_t*>(a.q) + rb;
+        obase = static_cast<uint16_t*>(a.out) + rb;
+        qstride = (int64_t)a.Hq * D;
+    }
+    if constexpr (PAGED && DEC) {
         seq = query_seq[b];
         if (seq >= 0 && seq < dec.num_seqs) {
             kv_lim = min(kv_lim, seq_lens[seq]);
@@ -192,7 +216,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
         kv_lim = min(kv_lim, k_lo + chunk);
     }
     int kv_end = kv_lim;
-    if (a.causal) kv_end = min(kv_end, q0 + kWRows);
+    if (a.causal) kv_end = min(kv_end, qpos0 + q0 + kWRows);
     const int ntiles = kv_end > k_lo ? (kv_end - k_lo + kWKeys - 1) / kWKeys : 0;
 
     const int d0 = kWChunk * wave;  // this wave's first dim
@@ -231,16 +255,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     {
         // DEC: row r is query head h + r (one query each; heads past the group
         // read as zeros), so the rows form [G - 32hb, D] from head h on.
-        const int nrows = DEC ? G - kWRows * hb : a.Sq;
-        const __amdgpu_buffer_rsrc_t rq =
-            w_rsrc(static_cast<const uint16_t*>(a.q) + bh * a.Sq * D, (uint32_t)nrows * D * 2);
+        const int nq = DEC ? G - kWRows * hb : nrows;
+        const __amdgpu_buffer_rsrc_t rq = w_rsrc(qbase, (uint32_t)((nq - 1) * qstride + D) * 2);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int row = q0 + 16 * qb + l16, dim = d0 + 32 * s + 8 * g4;
                 qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rq, (row < nrows && dim < D) ? ((uint32_t)row * D + dim) * 2 : kWOutside, 0, 0);
+                    rq, (row < nq && dim < D) ? ((uint32_t)(row * qstride) + dim) * 2 : kWOutside, 0, 0);
             }
     }
     // K fragments (A operands): key kt + lane%16, dims d0 + 32s + 8*(lane/16).
@@ -367,11 +390,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
                 for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
             }
         }
-        const bool edge = key0 + 8 > kv_lim || (a.causal && key0 + 7 > qa);
+        const int qp = qpos0 + qa;  // this row's absolute position
+        const bool edge = key0 + 8 > kv_lim || (a.causal && key0 + 7 > qp);
         if (edge) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (key0 + e >= kv_lim || (a.causal && key0 + e > qa)) x[e] = -INFINITY;
+                if (key0 + e >= kv_lim || (a.causal && key0 + e > qp)) x[e] = -INFINITY;
         }
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -438,15 +462,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
         return;
     }
     const float inv = 1.f / l;  // a row with no visible key: 0 * inf = NaN
-    if (wave == 0 && kh == 0 && a.lse && qa < a.Sq) {
+    if (!PAGED && wave == 0 && kh == 0 && a.lse && qa < a.Sq) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         a.lse[bh * a.Sq + qa] = (m_use + __log2f(l)) * 0.69314718055994531f;
     }
 
     // O: register r of d-block db holds dim d0 + 32db + 8*(r/4) + 4*(lane/32)
     // + r%4 of query q0 + lane%32.
-    if (qa < a.Sq) {
-        uint16_t* row = static_cast<uint16_t*>(a.out) + (bh * a.Sq + qa) * D;
+    if (qa < nrows) {
+        uint16_t* row = obase + qa * qstride;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -505,6 +529,40 @@ hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s) {
     return f16 ? launch_wide_t<F16T>(a, s) : launch_wide_t<Bf16T>(a, s);
 }
 
+template <int NW, class T>
+hipError_t launch_wide_paged_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
+    const int nqb = (a.Sq + kWRows - 1) / kWRows;
+    const dim3 grid((unsigned)(a.B * a.Hq * nqb));
+    hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false, true>), grid, dim3(NW * 64), 0, s, a, nullptr, d,
+                       d.tables, d.seq_lens, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_wide_paged_t(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
+    if (a.D <= 4 * kWChunk) return launch_wide_paged_nw<4, T>(a, d, s);
+    if (a.D <= 6 * kWChunk) return launch_wide_paged_nw<6, T>(a, d, s);
+    return launch_wide_paged_nw<8, T>(a, d, s);
+}
+
+hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, bool f16, hipStream_t s) {
+    if (a.D <= 256 || a.D > 1024 || a.D % 8 != 0) return hipErrorInvalidValue;
+    WideDec w{};
+    w.tables = p.block_tables;
+    w.seq_lens = p.seq_lens;
+    w.num_seqs = p.num_seqs;
+    w.max_pages = p.max_pages;
+    w.pages = p.pages;
+    w.page_size = p.page_size;
+    w.cu_q = p.cu_seqlens_q;
+    w.total_q = p.total_q;
+    ForwardArgs b = a;
+    b.lse = nullptr;
+    b.bias = nullptr;
+    b.padded = false;
+    return f16 ? launch_wide_paged_t<F16T>(b, w, s) : launch_wide_paged_t<Bf16T>(b, w, s);
+}
+
 hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, bool f16, hipStream_t s) {
     if (d.D <= 256 || d.D > 1024 || d.D % 8 != 0) return hipErrorInvalidValue;
     ForwardArgs a;
@@ -522,7 +580,10 @@ hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, boo
     a.scale = d.scale;
     a.causal = false;
     a.padded = d.key_lens != nullptr;
-    WideDec w{d.o_part, d.lse_part, d.splits, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, false};
+    WideDec w{};
+    w.o_part = d.o_part;
+    w.lse_part = d.lse_part;
+    w.splits = d.splits;
     if (p) {
         w.tables = p->block_tables;
         w.seq_lens = p->seq_lens;

@@ -82,8 +82,10 @@ hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s);
 // Dense 16-bit forward with 256 < D <= 1024 (the head-dim-split kernel).
 hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s);
+hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, bool f16, hipStream_t s);
 // Paged prefill chunks: a.B = num_seqs, a.Sq = longest chunk, a.Sk = max_seq_len;
-// bf16 or (f16) fp16.
+// bf16 or (f16) fp16; head dims above 256 go to the head-dim-split kernel
+// (launch_paged_prefill_wide).
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
                                       hipStream_t s);
 // C = A . B (16-bit, fp32 accumulation) for the attention block's

@@ -52,9 +52,9 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // (the 64-, 128- and 256-wide kernels read the missing chunks as zeros),
 // fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
 // kernel).  max16: the widest 16-bit head dim of the entry point (1024 for
-// the dense forward, decode, paged attention and the block, whose heads
-// above 256 run on the head-dim-split kernel; 256 for paged prefill; 128 for
-// the backward, whose lanes hold a full-width operand and gradient).
+// every forward entry point, whose heads above 256 run on the head-dim-split
+// kernel; 128 for the backward, whose lanes hold a full-width operand and
+// gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
     return D >= 8 && D <= max16 && D % 8 == 0;
@@ -726,8 +726,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (!head_dim_ok(D, dtype, 256))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 256)",
+    if (!head_dim_ok(D, dtype, 1024))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 1024)",
                     (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 and fp16 only");

@@ -367,7 +367,8 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *                 keys j <= the row's absolute position
  *   out           device [total_q, Hq, D]
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
- * SDPA_F16, D a multiple of 8 up to 256, page_size a multiple of 16
+ * SDPA_F16, D a multiple of 8 up to 1024 (above 256 on the head-dim-split
+ * kernel), page_size a multiple of 16
  * (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside

@@ -202,7 +202,7 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, pages=100, p
     (dict(causal=-1), sd.SDPA_ERR_INVALID_ARGUMENT, "causal"),
     (dict(max_seq_len=801), sd.SDPA_ERR_INVALID_ARGUMENT, "capacity"),
     (dict(out=ctypes.c_void_p(0x7e000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=264), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
 ])

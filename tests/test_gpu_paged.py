@@ -338,3 +338,24 @@ def test_paged_headdim_split_matches_dense_decode():
                                 seed=998)
     ref = oracle_of(inp, scale, True)
     compare(to64(out), ref, torch.bfloat16, "paged D=512 decode")
+
+
+@pytest.mark.parametrize("D", [264, 512, 1024])
+def test_paged_prefill_headdim_split(D):
+    # whole sequences (ragged: 300 = 9 blocks of 32 + 12), chunks after cached
+    # history (bottom-right aligned, a single token, causal and not), a grid
+    # larger than the chunks, on the head-dim-split kernel
+    check_prefill([300, 129, 100], [300, 129, 100], 8, 2, D, 16, True, seed=1010 + D)
+    check_prefill([500, 300, 64, 777], [37, 100, 64, 1], 4, 4, D, 32, True, seed=1011 + D)
+    check_prefill([500, 300, 64, 777], [37, 100, 64, 1], 4, 4, D, 16, False, seed=1012 + D)
+    check_prefill([90, 300], [90, 20], 8, 8, D, 16, True, seed=1013 + D, max_q=300)
+
+
+def test_paged_prefill_headdim_split_invalid_table_entries():
+    D = 768
+    inp, out, scale, cu, qs, qp = run_prefill([64], [10], 4, 2, D, 16, False, seed=1020,
+                                              tables=[[0, -1, 2, 99999]])
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            np.array([[0, 2]]), np.array([32]), np.zeros(10, dtype=np.int64),
+                            np.full(10, 31), scale, False)
+    compare(to64(out), ref, torch.bfloat16, "prefill D=768: invalid pages hidden")
