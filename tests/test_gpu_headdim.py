@@ -184,9 +184,9 @@ def test_paged_prefill_wide_head_dim():
 
 
 def test_forward_wide_full_size_sampled_rows():
-    # a 4096-token causal prefill with 256-wide heads; the oracle checks
-    # sampled rows (tile edges included) of every head
-    B, H, S, D = 1, 8, 4096, 256
+    # the 256-wide causal prefill leg at its full size (B4 H8 S4096); the
+    # oracle checks sampled rows (tile edges included)
+    B, H, S, D = 4, 8, 4096, 256
     q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 797, DEV)
     scale = 1 / math.sqrt(D)
     out = sd.sdpa_forward(q, k, v, scale, sd.MASK_CAUSAL)
@@ -415,3 +415,21 @@ def test_block_headdim_split(model, heads):
     torch.cuda.synchronize()
     ref = O.block_forward(to64(x), to64(wq), to64(wk), to64(wv), to64(wo), heads, None, O.MASK_CAUSAL)
     compare_block(to64(y), ref, BF16, "block model=%d heads=%d" % (model, heads))
+
+
+def test_decode_wide_full_size_sampled_heads():
+    # the 256-wide decode leg at its full size (B32, 32/8 heads, 32768 cached
+    # keys, 32 splits; batch 17 padded to 9999 keys); every query head of two
+    # (batch, K/V head) groups against the oracle
+    B, Hq, Hkv, Sk, D, splits = 32, 32, 8, 32768, 256, 32
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 1030, DEV)
+    lens = torch.full((B,), Sk, dtype=torch.int32, device=DEV)
+    lens[17] = 9999
+    out = sd.sdpa_decode(q, k, v, 1 / math.sqrt(D), lens, splits)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for b, g in ((2, 1), (17, 7)):
+        hs = slice(g * G, (g + 1) * G)
+        ref = O.sdpa_decode(to64(q[b:b + 1, hs]), to64(k[b:b + 1, g:g + 1]), to64(v[b:b + 1, g:g + 1]),
+                            1 / math.sqrt(D), lens[b:b + 1].cpu().numpy())
+        compare(to64(out[b:b + 1, hs]), ref, BF16, "D=256 decode b=%d group=%d" % (b, g))
