@@ -46,6 +46,12 @@ constexpr int kBwThreads = 256;  // 4 waves of 64
 constexpr int kBwRows = 128;     // rows a workgroup owns (queries in pass 1, keys in pass 2)
 constexpr int kBwTile = 64;      // rows of the streamed operand per step
 constexpr uint32_t kOutside = 0x80000000u;  // a buffer offset past any num_records (<= INT_MAX)
+// Cache policy of the bias-gradient stores: non-temporal (written once, read
+// by nobody here; 3.5% faster than the default policy for the causal S=4096
+// backward with a bias, whose 2.15 GB of dS would otherwise pass through L2).
+// The bias loads keep the default policy: the batches that share a bias
+// re-read it from cache (non-temporal loads were 7% slower).
+constexpr int kStreamed = 2;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const u32x4 v = zero ? u32x4{0u, 0u, 0u, 0u} : swapped(lds_row(stg + stg_at(kb2, i)), i);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rdb, gofs(kb0, i), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rdb, gofs(kb0, i), 0, kStreamed);
         }
     };
     // per-lane staging offsets: row l32, logical unit 2g + hg of region kb2
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                 const int row = qw + 8 * i + (lane >> 3), key = j0 + 8 * (lane & 7);
                 __builtin_amdgcn_raw_buffer_store_b128(
                     u32x4{0u, 0u, 0u, 0u}, rdb,
-                    (row < a.Sq && key < a.Sk) ? ((uint32_t)row * a.Sk + key) * 2 : kOutside, 0, 0);
+                    (row < a.Sq && key < a.Sk) ? ((uint32_t)row * a.Sk + key) * 2 : kOutside, 0, kStreamed);
             }
         }
     }
