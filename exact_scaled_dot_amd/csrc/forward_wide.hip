@@ -67,9 +67,10 @@ __device__ __forceinline__ void w_lds_barrier() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+template <int AUX>
 __device__ __forceinline__ void w_dma(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (w_lds_void*)((__attribute__((address_space(3))) char*)lds), 16,
-                                             voff, 0, 0, 0);
+                                             voff, 0, 0, AUX);
 }
 
 // LDS layout (floats / 16-bit elements):
@@ -140,6 +141,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int32_t* __restrict__ query_pos) {
 
     using LY = WideLds<NW>;
+    // K/V cache policy: the decode forms read each K/V byte once (streamed,
+    // non-temporal); the prefill forms re-read a head's K/V from L2.
+    constexpr int kKVPolicy = DEC ? 2 : 0;
     __shared__ __attribute__((aligned(1024))) float smem[LY::FLOATS];
     float* const part = smem;
     uint16_t* const vring = reinterpret_cast<uint16_t*>(smem + LY::VFL);
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
         for (int s = 0; s < 4; ++s) {
             const int dim = d0 + 32 * s + 8 * g4;
             kf[s] = __builtin_amdgcn_raw_buffer_load_b128(
-                sr.k, dim < D ? ((sr.row0 + l16) * sr.rstride + sr.col0 + dim) * 2 : kWOutside, 0, 0);
+                sr.k, dim < D ? ((sr.row0 + l16) * sr.rstride + sr.col0 + dim) * 2 : kWOutside, 0, kKVPolicy);
         }
     };
     // V tile of keys kt .. kt+15, this wave's dims, into ring stage st: DMA i
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
         const Src sr = src(kt);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w_dma(sr.v, vw + st * LY::VST + 512 * i,
+            w_dma<kKVPolicy>(sr.v, vw + st * LY::VST + 512 * i,
                   vdim_ok ? ((sr.row0 + 4 * i + g4) * sr.rstride + sr.col0 + d0 + 8 * vchunk) * 2 : kWOutside);
     };
     // Transposed-read offsets (32x32x16 A operand = V^T): lane reads rows
