@@ -1021,6 +1021,7 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s) {
+    if (a.D > 128) return launch_backward_wide(a, f16, s);
     if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
     return f16 ? launch_backward_t<F16T>(a, s) : launch_backward_t<Bf16T>(a, s);
 }

@@ -110,6 +110,8 @@ hipError_t launch_gemm_16bit(const GemmArgs& g, bool f16, hipStream_t s);
 
 // Backward: the dQ pass (also writes delta), then the dK / dV pass.
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s);
+// Ordered backward without a bias for 128 < D <= 512 (head dim split across waves).
+hipError_t launch_backward_wide(const BackwardArgs& a, bool f16, hipStream_t s);
 
 // Split-KV decode and paged attention, bf16 or (f16) fp16.
 hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s);

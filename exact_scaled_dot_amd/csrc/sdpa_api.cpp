@@ -53,8 +53,9 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // fp32 any multiple of 4 up to 128 (likewise on the 64- and 128-wide fp32
 // kernel).  max16: the widest 16-bit head dim of the entry point (1024 for
 // every forward entry point, whose heads above 256 run on the head-dim-split
-// kernel; 128 for the backward, whose lanes hold a full-width operand and
-// gradient).
+// kernel; 512 for the ordered backward, above 128 on its head-dim-split
+// kernels; 128 for the atomic backward and the backward with a bias, whose
+// lanes hold a full-width operand and gradient).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
     return D >= 8 && D <= max16 && D % 8 == 0;
@@ -266,8 +267,10 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
     if (!out || !dout || !lse || !dk || !dv)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     int64_t qbytes = 0, kbytes = 0;
+    // head dims up to 512 on the ordered backward without a bias (above 128
+    // on the head-dim-split kernels), up to 128 with a bias or atomic dQ
     sdpa_status_t st = check_common(q, k, v, dq, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
-                                    &kbytes);
+                                    &kbytes, (atomic || bias) ? 128 : 512);
     if (st != SDPA_OK) return st;
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "the backward needs 16-bit inputs (bf16 or fp16)");

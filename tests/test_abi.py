@@ -262,8 +262,8 @@ def bwd(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128, 
     (dict(lse=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
     (dict(dq=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
-    (dict(D=256), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),     # the backward kernels stop at 128
+    (dict(D=520), sd.SDPA_ERR_UNSUPPORTED, "up to 512"),     # the ordered backward stops at 512
+    (dict(D=516), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(mask=1, Sq=64), sd.SDPA_ERR_INVALID_ARGUMENT, "Sq == Sk"),
     (dict(mask=2), sd.SDPA_ERR_INVALID_ARGUMENT, "key_lens"),
     (dict(mask=8), sd.SDPA_ERR_INVALID_ARGUMENT, "mask"),
@@ -332,6 +332,11 @@ def test_backward_atomic_workspace_and_rejects():
                                   ctypes.c_void_p(1 << 45), ctypes.c_void_p(1 << 46),
                                   ctypes.c_void_p(1 << 47), 1 << 40, sd.SDPA_BF16, None)
     assert st == sd.SDPA_ERR_UNSUPPORTED
+    # the atomic variant keeps the 128-wide kernels
+    st = lib.sdpa_backward_atomic(FAKE, FAKE_K, FAKE_V, FAKE_O, FAKE_DO, FAKE_L, 2, 4, 2, 128, 128,
+                                  136, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, 1 << 30,
+                                  sd.SDPA_BF16, None)
+    assert st == sd.SDPA_ERR_UNSUPPORTED and "up to 128" in sd.last_error()
 
 
 def block(x=FAKE, wq=FAKE_K, wk=FAKE_V, wv=FAKE_O, wo=FAKE_W, B=2, S=128, model=512, heads=8,

@@ -235,11 +235,16 @@ def test_paged_decode_wide_head_dim():
     compare(to64(out), ref, BF16, "paged decode D=256")
 
 
-def test_backward_rejects_wide_head_dims():
-    q, k, v = draw_qkv(1, 2, 1, 64, 64, 256, BF16, 801, DEV)
+def test_backward_rejects_head_dims_past_its_kernels():
+    # the ordered backward stops at 512, the atomic one and the one with a bias at 128
+    q, k, v = draw_qkv(1, 2, 1, 64, 64, 520, BF16, 801, DEV)
+    out, lse = sd.sdpa_forward_lse(q, k, v, 0.1, 0)
+    with pytest.raises(sd.SdpaError, match="up to 512"):
+        sd.sdpa_backward(q, k, v, out, out, lse, 0.1, 0)
+    q, k, v = draw_qkv(1, 2, 1, 64, 64, 256, BF16, 802, DEV)
     out, lse = sd.sdpa_forward_lse(q, k, v, 0.1, 0)
     with pytest.raises(sd.SdpaError, match="up to 128"):
-        sd.sdpa_backward(q, k, v, out, out, lse, 0.1, 0)
+        sd.sdpa_backward(q, k, v, out, out, lse, 0.1, 0, atomic=True)
 
 
 # ------------------------------------------------------------- fp32 head dims
@@ -433,3 +438,69 @@ def test_decode_wide_full_size_sampled_heads():
         ref = O.sdpa_decode(to64(q[b:b + 1, hs]), to64(k[b:b + 1, g:g + 1]), to64(v[b:b + 1, g:g + 1]),
                             1 / math.sqrt(D), lens[b:b + 1].cpu().numpy())
         compare(to64(out[b:b + 1, hs]), ref, BF16, "D=256 decode b=%d group=%d" % (b, g))
+
+
+# ------------------------------------------------ backward above 128 (to 512)
+# The head-dim-split backward: 2 or 4 waves of 128 dims per workgroup.
+
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("D", [136, 256, 384, 512])
+@pytest.mark.parametrize("mask", [0, 1, 3], ids=["none", "causal", "causal+padding"])
+def test_backward_headdim_split(dtype, D, mask):
+    # grouped K/V 4/2; 200 rows and keys = 6 blocks of 32 + 8 (12 tiles of 16 + 8)
+    B, Hq, Hkv, S = 2, 4, 2, 200
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, dtype, 1200 + D + mask, DEV)
+    dout = draw_grad((B, Hq, S, D), dtype, 1201 + D + mask, DEV)
+    lens = torch.tensor([200, 77], dtype=torch.int32, device=DEV) if mask & 2 else None
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    dq, dk, dv = sd.sdpa_backward(q, k, v, out, dout, lse, scale, mask, lens)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    rq, rk, rv = O.sdpa_backward(to64(q), to64(k), to64(v), to64(dout), scale, mask, ln)
+    what = "%s D=%d mask=%d" % (dtype, D, mask)
+    compare_grad(to64(dq), rq, dtype, what + " dq")
+    compare_grad(to64(dk), rk, dtype, what + " dk")
+    compare_grad(to64(dv), rv, dtype, what + " dv")
+
+
+def test_backward_headdim_split_rectangular_dead_rows_and_repeatable():
+    # Sq != Sk, a batch with no valid key (its dQ rows are 0), keys past the
+    # limit get dK = dV = 0, and a second call gives the same bits
+    B, Hq, Hkv, Sq, Sk, D = 2, 2, 1, 70, 150, 320
+    q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, BF16, 1210, DEV)
+    dout = draw_grad((B, Hq, Sq, D), BF16, 1211, DEV)
+    lens = torch.tensor([0, 99], dtype=torch.int32, device=DEV)
+    out, lse = sd.sdpa_forward_lse(q, k, v, 0.05, sd.MASK_KEY_PADDING, lens)
+    g1 = sd.sdpa_backward(q, k, v, out, dout, lse, 0.05, sd.MASK_KEY_PADDING, lens)
+    g2 = sd.sdpa_backward(q, k, v, out, dout, lse, 0.05, sd.MASK_KEY_PADDING, lens)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    dq, dk, dv = g1
+    assert not dq[0].any() and not dk[0].any() and not dv[0].any()
+    assert not dk[1, :, 99:].any() and not dv[1, :, 99:].any()
+    rq, rk, rv = O.sdpa_backward(to64(q[1:]), to64(k[1:]), to64(v[1:]), to64(dout[1:]), 0.05,
+                                 O.MASK_KEY_PADDING, np.array([99]))
+    compare_grad(to64(dq[1:]), rq, BF16, "rect dq")
+    compare_grad(to64(dk[1:]), rk, BF16, "rect dk")
+    compare_grad(to64(dv[1:]), rv, BF16, "rect dv")
+
+
+def test_backward_headdim_split_full_size_sampled_heads():
+    # a 4096-token causal backward with 256-wide heads (B2 H8); two heads
+    # against the oracle
+    B, H, S, D = 2, 8, 4096, 256
+    q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 1220, DEV)
+    dout = draw_grad((B, H, S, D), BF16, 1221, DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, sd.MASK_CAUSAL)
+    dq, dk, dv = sd.sdpa_backward(q, k, v, out, dout, lse, scale, sd.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    for b, h in ((0, 2), (1, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = O.sdpa_backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(dout[sl]), scale,
+                                     O.MASK_CAUSAL)
+        compare_grad(to64(dq[sl]), rq, BF16, "D=256 full b=%d h=%d dq" % (b, h))
+        compare_grad(to64(dk[sl]), rk, BF16, "D=256 full b=%d h=%d dk" % (b, h))
+        compare_grad(to64(dv[sl]), rv, BF16, "D=256 full b=%d h=%d dv" % (b, h))
