@@ -14,7 +14,9 @@ resident in HBM:
     its forward output and log-sum-exp (computed once, before the timing),
     with the ordered reduction and with the atomic-dQ one, and the same
     backward with the per-head bias below, which also writes the bias
-    gradient [4, 16, 4096, 4096] bf16 in full
+    gradient [4, 16, 4096, 4096] bf16 in full; and the backward of the
+    256-wide-head prefill below (B=4 Hq=Hkv=8 S=4096 D=256, causal) on the
+    head-dim-split backward kernels
   * the causal prefill with a general additive mask: a per-head bias tensor
     [1, 16, 4096, 4096] bf16 added to the scaled scores
   * the causal prefill with 1024-wide heads, bf16, B=1 Hq=Hkv=8 S=4096 D=1024
@@ -97,6 +99,13 @@ def pair_traffic(a, b, src_a, src_b=None):
 def backward_traffic():
     """HBM bytes of one backward call (both passes), if both records are valid."""
     parts = [stored_traffic(k, "backward.hip") for k in ("backward_dq", "backward_dkdv")]
+    return None if None in parts else sum(parts)
+
+
+def wide_backward_traffic():
+    """HBM bytes of one head-dim-split backward call (its three kernels), if valid."""
+    parts = [stored_traffic(k, "backward_wide.hip")
+             for k in ("backward_wide_stats", "backward_wide_dq", "backward_wide_dkdv")]
     return None if None in parts else sum(parts)
 
 
@@ -234,6 +243,12 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
                       ("backward_atomic_convert", "bwd_dq_convert_kernel")):
         if name in fetch:
             out[key] = entry(name, "backward.hip", fetch[name], write[name])
+    # the head-dim-split backward (256-wide heads): its own three kernels
+    for key, name in (("backward_wide_stats", "bwd_wide_stats_kernel"),
+                      ("backward_wide_dq", "bwd_wide_dq_kernel"),
+                      ("backward_wide_dkdv", "bwd_wide_dkdv_kernel")):
+        if name in fetch:
+            out[key] = entry(name, "backward_wide.hip", fetch[name], write[name])
     # A full step runs the dense decode, the paged one and the 256-wide one
     # (split and merge each), then the 1024-wide one (its own split kernel,
     # the same merge kernel): 3 split and 4 merge dispatches per step.
@@ -256,7 +271,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
-                                       "backward", "backward_atomic", "backward_bias", "bias",
+                                       "backward", "backward_atomic", "backward_bias",
+                                       "backward_wide", "bias",
                                        "wide", "widest", "decode_widest",
                                        "decode_wide", "block", "block_small"],
                     default=None,
@@ -349,10 +365,22 @@ def main():
     # Wide heads: the causal prefill's token count and model width in 8 heads
     # of 256.
     iwide = None
-    if args.only in (None, "wide"):
+    if args.only in (None, "wide", "backward_wide"):
         iwide = dict(zip(("q", "k", "v"), draw_qkv(WIDE[0], WIDE[1], WIDE[1], WIDE[2], WIDE[2],
                                                    WIDE[3], wp.dtype, wp.seed + 31, dev)))
         iwide["out"] = torch.empty_like(iwide["q"])
+    # Backward of the wide-head prefill (head-dim-split backward kernels):
+    # output and lse from one forward here.
+    ibwd = None
+    if args.only in (None, "backward_wide"):
+        out_w, lse_w = sd.sdpa_forward_lse(iwide["q"], iwide["k"], iwide["v"],
+                                           1.0 / math.sqrt(WIDE[3]), sd.MASK_CAUSAL)
+        ibwd = {"out": out_w, "lse": lse_w,
+                "dout": draw_grad(tuple(iwide["q"].shape), wp.dtype, wp.seed + 41, dev),
+                "dq": torch.empty_like(iwide["q"]), "dk": torch.empty_like(iwide["k"]),
+                "dv": torch.empty_like(iwide["v"]),
+                "ws": torch.empty(sd.sdpa_backward_workspace_size(WIDE[0], WIDE[1], WIDE[2]),
+                                  dtype=torch.uint8, device=dev)}
     # Widest heads: the same tokens and batch*heads*head dim in 8 heads of 1024.
     iwst = None
     if args.only in (None, "widest"):
@@ -409,6 +437,10 @@ def main():
     calls["backward_bias"] = lambda: sd.sdpa_backward_bias(
         ip["q"], ip["k"], ip["v"], ibb["out"], ibb["dout"], ibb["lse"], ibias["bias"], wp.scale,
         sd.MASK_CAUSAL, None, ibb["dbias"], ibb["dq"], ibb["dk"], ibb["dv"], ibb["ws"])
+    calls["backward_wide"] = lambda: sd.sdpa_backward(
+        iwide["q"], iwide["k"], iwide["v"], ibwd["out"], ibwd["dout"], ibwd["lse"],
+        1.0 / math.sqrt(WIDE[3]), sd.MASK_CAUSAL, None, ibwd["dq"], ibwd["dk"], ibwd["dv"],
+        ibwd["ws"])
     calls["bias"] = lambda: sd.sdpa_forward_bias(ip["q"], ip["k"], ip["v"], ibias["bias"], wp.scale,
                                                  sd.MASK_CAUSAL, None, ibias["out"])
     calls["decode_wide"] = lambda: sd.sdpa_decode(idw["q"], idw["k"], idw["v"],
@@ -428,7 +460,8 @@ def main():
             *blk["ins"], blk["H"], None, sd.MASK_CAUSAL, None, blk["y"], blk["ws"]))(iblk[name])
     order = ([args.only] if args.only else
              ["prefill", "padded", "decode", "paged", "paged_prefill", "backward", "backward_atomic",
-              "backward_bias", "bias", "wide", "widest", "decode_wide", "decode_widest", "block",
+              "backward_bias", "backward_wide", "bias", "wide", "widest", "decode_wide",
+              "decode_widest", "block",
               "block_small"])
 
     if args.copy_calibration:
@@ -599,6 +632,20 @@ def main():
                                     "traffic": stored_traffic("wide", "forward.hip"),
                                     "kernel": "forward_bf16_kernel<256, DV=128> x 2 slices",
                                     "flops_per_launch": fl}}
+    if "backward_wide" in ms:
+        B, H, S, D = WIDE
+        fl = 2.5 * formula_flops(B, H, S, S, D, True)
+        tf = fl / (ms["backward_wide"] * 1e-3) / 1e12
+        rec["backward_wide"] = {"workload": "bf16_causal_backward_b%d_h%d_s%d_d%d" % (B, H, S, D),
+                                "ms": round(ms["backward_wide"], 4), "value": round(tf, 3),
+                                "unit": "TFLOP/s",
+                                "roofline": {"bound": "mfma", "achieved": round(tf, 3),
+                                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                             "traffic": wide_backward_traffic(),
+                                             "kernel": "bwd_wide_stats_kernel + bwd_wide_dq_kernel<2>"
+                                                       " + bwd_wide_dkdv_kernel<2>",
+                                             "flops_per_launch": fl}}
     if "widest" in ms:
         B, H, S, D = WIDEST
         fl = formula_flops(B, H, S, S, D, True)
@@ -669,6 +716,9 @@ def main():
         elif "backward_atomic" in rec:
             rec.update({"value": rec["backward_atomic"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["backward_atomic"]["workload"]}
+        elif "backward_wide" in rec:
+            rec.update({"value": rec["backward_wide"]["value"], "unit": "TFLOP/s"})
+            rec["config"] = {"workload": rec["backward_wide"]["workload"]}
         elif "backward" in rec:
             rec.update({"value": rec["backward"]["value"], "unit": "TFLOP/s"})
             rec["config"] = {"workload": rec["backward"]["workload"]}

@@ -7,7 +7,7 @@
 // owning dims 128w .. 128w+127 (dims past D load as zeros, are never stored).
 //
 // dQ pass (workgroup = 32 query rows of one (batch, query head)); per 16-key
-// tile (K and V tiles of the wave's dims by DMA, three stages):
+// tile (K and V tiles of the wave's dims by DMA, two stages):
 //   every wave: partial S^T = K_w Q_w^T and dP^T = V_w dO_w^T
 //     (v_mfma_f32_16x16x32, Q and dO rows in registers, K and V rows read
 //     from LDS), both to LDS in fp32 (two buffers, alternating); a barrier;
@@ -34,7 +34,8 @@ namespace {
 constexpr int kXRows = 32;    // rows a workgroup owns (queries, or keys)
 constexpr int kXTile = 16;    // rows streamed per step (keys, or queries)
 constexpr int kXChunk = 128;  // head dims per wave
-constexpr int kXStages = 3;
+constexpr int kXStages = 3;    // dK/dV pass: Q/dO ring depth
+constexpr int kXStagesQ = 2;   // dQ pass: K/V ring depth (48 KB per 2-wave workgroup: 3 per CU)
 constexpr int kXTileEl = kXTile * kXChunk;  // 16-bit elements of one wave's tile
 constexpr uint32_t kXOut = 0x80000000u;     // buffer offset past any num_records
 constexpr float kXLog2e = 1.4426950408889634f;
@@ -160,7 +161,7 @@ struct XLds {
 template <int NW, class T>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a, const int32_t* __restrict__ key_lens) {
     using LY = XLds<NW>;
-    __shared__ __attribute__((aligned(1024))) float smem[LY::TFL + NW * kXStages * LY::STAGE_DQ / 2];
+    __shared__ __attribute__((aligned(1024))) float smem[LY::TFL + NW * kXStagesQ * LY::STAGE_DQ / 2];
     uint16_t* const tiles = reinterpret_cast<uint16_t*>(smem + LY::TFL);
 
     const int tid = threadIdx.x;
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
     const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
     const __amdgpu_buffer_rsrc_t rk = x_rsrc(static_cast<const uint16_t*>(a.k) + kvh, (uint32_t)a.Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = x_rsrc(static_cast<const uint16_t*>(a.v) + kvh, (uint32_t)a.Sk * D * 2);
-    uint16_t* const wt = tiles + wave * kXStages * LY::STAGE_DQ;
+    uint16_t* const wt = tiles + wave * kXStagesQ * LY::STAGE_DQ;
     // DMA i fills tile rows 4i + lane/16, stored chunk lane%16
     auto load_tiles = [&](int kt, int st) {
         uint16_t* base = wt + st * LY::STAGE_DQ;
@@ -236,12 +237,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
     const int poff0 = x_part(qr, 2 * kh), poff1 = x_part(qr, 2 * kh + 1);
 
     if (ntiles > 0) load_tiles(0, 0);
-    if (ntiles > 1) load_tiles(kXTile, 1);
     for (int j = 0; j < ntiles; ++j) {
         const int kt = j * kXTile;
-        if (j + 2 < ntiles) load_tiles(kt + 2 * kXTile, (j + 2) % kXStages);
-        x_wait<8>(min(2, ntiles - 1 - j));  // this tile's 8 DMA loads have landed
-        const uint16_t* kt_l = wt + (j % kXStages) * LY::STAGE_DQ;
+        // the stage refilled here was last read by this wave in tile j - 1
+        if (j + 1 < ntiles) load_tiles(kt + kXTile, (j + 1) & 1);
+        x_wait<8>(min(1, ntiles - 1 - j));  // this tile's 8 DMA loads have landed
+        const uint16_t* kt_l = wt + (j & 1) * LY::STAGE_DQ;
         const uint16_t* vt_l = kt_l + kXTileEl;
         float* const pb = smem + (j & 1) * LY::PBUF;
 

@@ -167,13 +167,16 @@ size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq);
  *   dq             device [B, Hq, Sq, D], dtype; written completely
  *   dk, dv         device [B, Hkv, Sk, D], dtype; written completely
  *   workspace      device buffer of at least sdpa_backward_workspace_size bytes
- * Two kernels are enqueued on stream: a query-parallel pass (dQ, and each
- * row's rowsum(dO o O) into the workspace) then a key-parallel pass (dK, dV).
+ * Up to D = 128 two kernels are enqueued on stream: a query-parallel pass
+ * (dQ, and each row's rowsum(dO o O) into the workspace) then a key-parallel
+ * pass (dK, dV); above 128 three (a row-statistics pass first, then the two
+ * passes with the head dim split over 2 or 4 waves of 128 dims).
  * Every sum runs in a fixed order: the result is bitwise reproducible (the
  * guide's ordered, atomic-free reduction).  Accumulation is fp32; P and dS are
  * rounded to dtype before their products, and the gradients to dtype at the end.
  * Outputs and workspace must not overlap each other or any input.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 128.
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 512
+ * (ruDNN user guide section 9; SDPA_ERR_UNSUPPORTED above).
  */
 sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const void *out,
                             const void *dout, const float *lse,
