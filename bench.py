@@ -209,7 +209,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
         # a full step launches, in order: the causal prefill, the padded one,
         # the paged one, the bias prefill, the wide-head prefill, the large
         # block's attention and the small block's (after the setup forwards
-        # that give the two backward legs their output and lse)
+        # that give the backward legs their output and lse)
         fr, wr = fetch[fwd], write[fwd]
         setup = len(fr) % 7        # the backward legs' setup forwards come first
         fr, wr = fr[setup:], wr[setup:]
@@ -292,7 +292,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+        print("bench.py measures one GPU only: the library runs on one device per process "
               "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 

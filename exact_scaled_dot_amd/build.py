@@ -55,7 +55,7 @@ def build_library(verbose=True):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     # A library with an unresolved symbol (e.g. a kernel stub the host pass
-    # never emitted) must fail here, not on the GPU machine.
+    # never emitted) must fail here, at build time, not at first use on a GPU.
     import ctypes
     ctypes.CDLL(os.path.abspath(tmp), mode=ctypes.RTLD_LOCAL | os.RTLD_NOW)
     os.replace(tmp, LIB)
