@@ -1,9 +1,12 @@
-"""GPU parity at head dims other than 64 and 128 (any multiple of 8 up to 128,
-16-bit inputs) on every entry point, against the fp64 oracle.
+"""GPU parity at head dims other than 64 and 128 (any multiple of 8 up to
+1024 on the forward entry points, up to 512 on the ordered backward; 16-bit
+inputs), against the fp64 oracle.
 
-The 64- and 128-wide kernels serve these widths: rows are D wide in memory,
-the chunks past D are read as zeros on chip and never stored.  Bars:
-tests/parity.py."""
+Up to 128 the 64- and 128-wide kernels serve these widths: rows are D wide in
+memory, the chunks past D are read as zeros on chip and never stored.  Above
+that, the 256-wide kernels (two 128-dim output slices) and the
+head-dim-split kernels (waves of 128 dims whose partial scores are summed on
+chip).  Bars: tests/parity.py."""
 
 import math
 
