@@ -161,8 +161,10 @@ struct XLds {
 template <int NW, class T>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a, const int32_t* __restrict__ key_lens) {
     using LY = XLds<NW>;
-    __shared__ __attribute__((aligned(1024))) float smem[LY::TFL + NW * kXStagesQ * LY::STAGE_DQ / 2];
-    uint16_t* const tiles = reinterpret_cast<uint16_t*>(smem + LY::TFL);
+    // one partial buffer (a second barrier per tile): 40 KB at NW = 2, four
+    // workgroups per CU
+    __shared__ __attribute__((aligned(1024))) float smem[LY::PBUF + NW * kXStagesQ * LY::STAGE_DQ / 2];
+    uint16_t* const tiles = reinterpret_cast<uint16_t*>(smem + LY::PBUF);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
         x_wait<8>(min(1, ntiles - 1 - j));  // this tile's 8 DMA loads have landed
         const uint16_t* kt_l = wt + (j & 1) * LY::STAGE_DQ;
         const uint16_t* vt_l = kt_l + kXTileEl;
-        float* const pb = smem + (j & 1) * LY::PBUF;
+        float* const pb = smem;
 
         // partial S^T and dP^T: register i of block qb = key 4*(lane/16) + i of
         // the tile, query 16qb + lane%16
@@ -260,8 +262,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
             x_lds_st_f4(pb + wave * (kXRows * kXTile) + x_part(q, g4), sa);
             x_lds_st_f4(pb + LY::PKIND + wave * (kXRows * kXTile) + x_part(q, g4), pa);
         }
-        // the buffer written here was last read two tiles ago, before the
-        // previous tile's barrier
         x_lds_barrier();
 
         f32x4 s0 = x_lds_ld_f4(pb + poff0), s1 = x_lds_ld_f4(pb + poff1);
@@ -273,6 +273,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
             p0 += x_lds_ld_f4(pb + LY::PKIND + w * (kXRows * kXTile) + poff0);
             p1 += x_lds_ld_f4(pb + LY::PKIND + w * (kXRows * kXTile) + poff1);
         }
+        // every wave has read the partials before any wave writes the next
+        // tile's into the same buffer
+        x_lds_barrier();
         const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
         const float dv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         const int key0 = kt + 8 * kh;
