@@ -72,10 +72,17 @@ DECODE_WIDE = (32, 32, 8, 32768, 256)  # wide decode: (batch, Hq, Hkv, Sk, head 
 DECODE_WIDEST = (8, 32, 8, 32768, 1024)  # head-dim-split decode (the same K+V bytes)
 
 
+# Headers every kernel source includes: a change to them changes every kernel.
+KERNEL_HEADERS = ("device_common.hpp", "launch.hpp")
+
+
 def kernel_source_hash(name):
-    path = os.path.join(ROOT, "exact_scaled_dot_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source together with the headers it includes."""
+    h = hashlib.sha256()
+    for part in (name,) + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, "exact_scaled_dot_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload, source):

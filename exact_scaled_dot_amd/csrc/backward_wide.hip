@@ -10,7 +10,8 @@
 // tile (K and V tiles of the wave's dims by DMA, two stages):
 //   every wave: partial S^T = K_w Q_w^T and dP^T = V_w dO_w^T
 //     (v_mfma_f32_16x16x32, Q and dO rows in registers, K and V rows read
-//     from LDS), both to LDS in fp32 (two buffers, alternating); a barrier;
+//     from LDS), both to LDS in fp32 (one buffer: a barrier before the
+//     partials are written and one after, before they are read);
 //   every lane: sums the partials of its query (lane%32) at keys
 //     8*(lane/32) .. +7, P = exp2(S scale log2e - lse2), dS = P o (dP - delta),
 //     exactly the B operand of dQ^T += K_w^T dS^T (v_mfma_f32_32x32x16, K^T
@@ -35,7 +36,7 @@ constexpr int kXRows = 32;    // rows a workgroup owns (queries, or keys)
 constexpr int kXTile = 16;    // rows streamed per step (keys, or queries)
 constexpr int kXChunk = 128;  // head dims per wave
 constexpr int kXStages = 3;    // dK/dV pass: Q/dO ring depth
-constexpr int kXStagesQ = 2;   // dQ pass: K/V ring depth (48 KB per 2-wave workgroup: 3 per CU)
+constexpr int kXStagesQ = 2;   // dQ pass: K/V ring depth (40 KB per 2-wave workgroup: 4 per CU)
 constexpr int kXTileEl = kXTile * kXChunk;  // 16-bit elements of one wave's tile
 constexpr uint32_t kXOut = 0x80000000u;     // buffer offset past any num_records
 constexpr float kXLog2e = 1.4426950408889634f;
