@@ -5,11 +5,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -533,10 +535,47 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
     return round_up((size_t)no * sizeof(float)) + round_up((size_t)rows * sizeof(float));
 }
 
-sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
+namespace {
+
+// Device scratch of sdpa_decode_noalloc: its split partials, laid out as the
+// workspace of sdpa_decode.  One copy per GPU, held until the process ends.
+// No part of it has to start at zero: the split pass writes every partial
+// slot (an empty split writes o_part = 0, lse = -inf) before the merge reads.
+static __device__ __align__(256) unsigned char scratch[SDPA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's copy of scratch, looked up once per
+// device.  In host code the array's own name is only a host-side stand-in.
+sdpa_status_t scratch_address(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SDPA_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices - 1);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return hip_status(e, "hipGetSymbolAddress(scratch)");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return SDPA_OK;
+}
+
+// sdpa_decode's checks and launch.  With noalloc the partials go to the
+// current device's scratch (workspace and workspace_bytes are ignored).
+sdpa_status_t decode_impl(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
                           int64_t Hkv, int64_t Sk, int64_t D, float scale,
                           const int32_t* key_lens, int num_splits, void* workspace,
-                          size_t workspace_bytes, void* out, int dtype, void* stream) {
+                          size_t workspace_bytes, void* out, int dtype, void* stream,
+                          bool noalloc) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st =
         check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes, 1024);
@@ -548,16 +587,27 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps key_lens");
     const size_t need = sdpa_decode_workspace_size(B, Hq, D, num_splits);
     if (need == 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace size overflows");
-    if (!workspace || workspace_bytes < need)
+    if (noalloc) {
+        if (need > (size_t)SDPA_NOALLOC_SCRATCH_BYTES)
+            return fail(SDPA_ERR_WORKSPACE,
+                        "decode partials need %zu bytes, beyond the %zu-byte device scratch of "
+                        "sdpa_decode_noalloc (fewer splits, or sdpa_decode with a workspace)",
+                        need, (size_t)SDPA_NOALLOC_SCRATCH_BYTES);
+    } else if (!workspace || workspace_bytes < need) {
         return fail(SDPA_ERR_WORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need,
                     workspace ? workspace_bytes : (size_t)0);
-    if (overlap(out, qbytes, workspace, (int64_t)need))
+    } else if (overlap(out, qbytes, workspace, (int64_t)need)) {
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps the workspace");
+    }
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "decode supports bf16 and fp16 only");
     const int64_t items = sdpa::decode_work_items(B, Hq, Hkv, num_splits);
     if (items > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "too many decode work items (%lld)", (long long)items);
+    if (noalloc) {
+        st = scratch_address(&workspace);
+        if (st != SDPA_OK) return st;
+    }
 
     sdpa::DecodeArgs a;
     a.q = q;
@@ -578,7 +628,25 @@ sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B
     (void)hipGetLastError();
     const hipError_t e =
         sdpa::launch_decode_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
-    return hip_status(e, "sdpa_decode launch");
+    return hip_status(e, noalloc ? "sdpa_decode_noalloc launch" : "sdpa_decode launch");
+}
+
+}  // namespace
+
+sdpa_status_t sdpa_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t Sk, int64_t D, float scale,
+                          const int32_t* key_lens, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* out, int dtype, void* stream) {
+    return decode_impl(q, k, v, B, Hq, Hkv, Sk, D, scale, key_lens, num_splits, workspace,
+                       workspace_bytes, out, dtype, stream, false);
+}
+
+sdpa_status_t sdpa_decode_noalloc(const void* q, const void* k, const void* v, int64_t B,
+                                  int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D, float scale,
+                                  const int32_t* key_lens, int num_splits, void* out, int dtype,
+                                  void* stream) {
+    return decode_impl(q, k, v, B, Hq, Hkv, Sk, D, scale, key_lens, num_splits, nullptr, 0, out,
+                       dtype, stream, true);
 }
 
 sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const void* v_cache,

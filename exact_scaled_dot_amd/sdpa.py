@@ -24,6 +24,7 @@ MASK_NONE = 0
 MASK_CAUSAL = 1
 MASK_KEY_PADDING = 2
 MAX_SPLITS = 32
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SDPA_NOALLOC_SCRATCH_BYTES
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
@@ -31,7 +32,8 @@ EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_bias", "sdpa_backw
             "sdpa_backward_workspace_size", "sdpa_backward_atomic",
             "sdpa_backward_atomic_workspace_size", "sdpa_backward_bias", "sdpa_block_forward",
             "sdpa_block_workspace_size",
-            "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_paged_attention",
+            "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_decode_noalloc",
+            "sdpa_paged_attention",
             "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
 
 _lib = None
@@ -83,6 +85,9 @@ def load_library():
     lib.sdpa_decode.restype = i32
     lib.sdpa_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, i32, vp,
                                 ctypes.c_size_t, vp, i32, vp]
+    lib.sdpa_decode_noalloc.restype = i32
+    lib.sdpa_decode_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp,
+                                        i32, vp, i32, vp]
     lib.sdpa_decode_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_decode_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.sdpa_paged_attention.restype = i32
@@ -409,6 +414,31 @@ def sdpa_decode(q, k, v, scale, key_lens=None, num_splits=MAX_SPLITS, workspace=
                            _ptr(key_lens), int(num_splits), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _ptr(out),
                            _dtype_code(q), _stream(stream)))
+    return out
+
+
+def sdpa_decode_noalloc(q, k, v, scale, out, key_lens=None, num_splits=MAX_SPLITS, stream=None):
+    """sdpa_decode with its partials in the library's static device scratch:
+    the call allocates no device memory (out is the caller's)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_tensor(name, t, 4)
+    B, Hq, Sq, D = q.shape
+    if Sq != 1:
+        raise ValueError("decode takes one query per (batch, head): q must be [B, Hq, 1, D]")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Sk, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share one dtype")
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, Hq, 1, D]")
+    if key_lens is not None:
+        _check_tensor("key_lens", key_lens, 1)
+        if key_lens.dtype != torch.int32:
+            raise TypeError("key_lens must be int32")
+    _check(load_library().sdpa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sk, D,
+                                              float(scale), _ptr(key_lens), int(num_splits),
+                                              _ptr(out), _dtype_code(q), _stream(stream)))
     return out
 
 

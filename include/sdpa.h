@@ -28,7 +28,8 @@
  *    rounded.
  *  - Pointers: every tensor pointer (q, k, v, out, key_lens, workspace) is a
  *    DEVICE pointer on the current HIP device, owned by the caller.  The
- *    library allocates nothing and keeps no per-call state.
+ *    library allocates nothing and keeps no per-call state, except the one
+ *    static device scratch array of sdpa_decode_noalloc (below).
  *  - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
  *    enqueued and the call returns; out is valid once the stream has reached
  *    that point.  The library never synchronises.
@@ -302,6 +303,34 @@ sdpa_status_t sdpa_decode(const void *q, const void *k, const void *v,
                           float scale, const int32_t *key_lens, int num_splits,
                           void *workspace, size_t workspace_bytes,
                           void *out, int dtype, void *stream);
+
+/* Bytes of the static device scratch array behind sdpa_decode_noalloc: room
+ * for the decode partials of B=64, Hq=32, D=128 at 32 splits (33.8 MB) with
+ * headroom.  Every GPU the library runs on holds one copy from module load
+ * until the process ends. */
+#define SDPA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * sdpa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Arguments, results, kernels and errors are
+ * those of sdpa_decode; the split partials go to a file-scope device array of
+ * SDPA_NOALLOC_SCRATCH_BYTES (one per GPU, its address looked up once per
+ * device on the first call there).  The call itself allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.
+ *   Returns SDPA_ERR_WORKSPACE, launching nothing, when
+ *   sdpa_decode_workspace_size(B, Hq, D, num_splits) exceeds
+ *   SDPA_NOALLOC_SCRATCH_BYTES.
+ *   Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ *   that overlap in time on one GPU (different streams, or host threads
+ *   without ordering) race and may return wrong results; order them on one
+ *   stream.  The scratch keeps the last call's partials; nothing in it needs
+ *   clearing between calls.
+ */
+sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Sk, int64_t D,
+                                  float scale, const int32_t *key_lens, int num_splits,
+                                  void *out, int dtype, void *stream);
 
 /*
  * Paged attention over a shared K/V page cache (ruDNN guide section 9): packed

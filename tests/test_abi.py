@@ -117,6 +117,39 @@ def test_decode_rejects(kw, status, needle):
     assert needle in sd.last_error()
 
 
+def dec_noalloc(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.125,
+                key_lens=None, splits=8, out=FAKE_O, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    return lib.sdpa_decode_noalloc(q, k, v, B, Hq, Hkv, Sk, D, scale, key_lens, splits, out,
+                                   dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(splits=0), sd.SDPA_ERR_INVALID_ARGUMENT, "num_splits"),
+    (dict(splits=33), sd.SDPA_ERR_INVALID_ARGUMENT, "num_splits"),
+    (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(out=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    # partials of 128 x 32 heads x 32 splits x 128 dims = 64 MiB + the lse section: one byte
+    # section past the scratch, so nothing is launched
+    (dict(B=128, Hq=32, Hkv=8, splits=32), sd.SDPA_ERR_WORKSPACE, "scratch"),
+    (dict(B=16, Hq=32, Hkv=8, D=1024, splits=32), sd.SDPA_ERR_WORKSPACE, "scratch"),
+])
+def test_decode_noalloc_rejects(kw, status, needle):
+    assert dec_noalloc(**kw) == status
+    assert needle in sd.last_error()
+
+
+def test_decode_noalloc_scratch_limit():
+    lib = sd.load_library()
+    assert sd.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the 64-sequence, 32-head, 32-split decode of 128-dim heads fits the scratch
+    assert lib.sdpa_decode_workspace_size(64, 32, 128, 32) <= sd.NOALLOC_SCRATCH_BYTES
+    assert lib.sdpa_decode_workspace_size(128, 32, 128, 32) > sd.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_workspace_size():
     lib = sd.load_library()
 
