@@ -34,6 +34,84 @@ def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def host_workers():
+    """Oracle threads: the cores this process may use, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_threaded(fn, items, workers=None):
+    """fn over items on a thread pool (NumPy releases the GIL in its array
+    loops), BLAS held to one thread per call so the pool does not oversubscribe
+    the cores.  Returns the results in order."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(min(workers or 16, host_workers())) as ex:
+            return list(ex.map(fn, items))
+
+
+def oracle_forward_whole(oracle, q, k, v, scale, mask_kind, key_lens=None, row_block=1024,
+                         return_lse=False, workers=None, bias=None):
+    """The oracle's forward over every (b, h, i) of q [B,Hq,Sq,D], k / v
+    [B,Hkv,Sk,D] (device or host tensors; bias None or [B or 1, Hq or 1, Sq,
+    Sk]): one head per thread, query rows in blocks of row_block (so an
+    8192 x 8192 fp64 score block never exists whole).  Inputs are copied to the
+    host in their own dtype and widened to fp64 one head at a time.  Returns
+    o [B,Hq,Sq,D] fp64 (and lse [B,Hq,Sq])."""
+    qh, kh, vh = (t.detach().cpu() for t in (q, k, v))
+    bh_all = None if bias is None else bias.detach().cpu()
+    B, Hq, Sq, D = qh.shape
+    G = Hq // kh.shape[1]
+    lens = None if key_lens is None else np.asarray(key_lens)
+    ref = np.empty((B, Hq, Sq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64)
+
+    def head(bh):
+        b, h = bh
+        q1 = qh[b, h].double().numpy()[None, None]
+        k1 = kh[b, h // G].double().numpy()[None, None]
+        v1 = vh[b, h // G].double().numpy()[None, None]
+        b1 = None
+        if bh_all is not None:
+            b1 = bh_all[b if bh_all.shape[0] > 1 else 0, h if bh_all.shape[1] > 1 else 0]
+            b1 = b1.double().numpy()[None, None]
+        for r0 in range(0, Sq, row_block):
+            rows = np.arange(r0, min(Sq, r0 + row_block))
+            idx = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], axis=1)
+            o, l = oracle.sdpa_forward_rows(q1, k1, v1, scale, mask_kind,
+                                            None if lens is None else lens[b:b + 1], idx,
+                                            bias=b1)
+            ref[b, h, r0:r0 + len(rows)] = o
+            lse[b, h, r0:r0 + len(rows)] = l
+
+    run_threaded(head, [(b, h) for b in range(B) for h in range(Hq)], workers)
+    return (ref, lse) if return_lse else ref
+
+
+def oracle_decode_whole(oracle, q, k, v, scale, key_lens=None):
+    """The oracle's decode over every (b, h) of q [B,Hq,1,D], k / v
+    [B,Hkv,Sk,D] (device or host tensors): one (batch, K/V head) group per
+    thread, its query heads together.  Returns o [B,Hq,1,D] fp64."""
+    qh, kh, vh = (t.detach().cpu() for t in (q, k, v))
+    B, Hq, _, D = qh.shape
+    Hkv = kh.shape[1]
+    G = Hq // Hkv
+    lens = None if key_lens is None else np.asarray(key_lens)
+    ref = np.empty((B, Hq, 1, D), dtype=np.float64)
+
+    def group(bg):
+        b, g = bg
+        hs = slice(g * G, (g + 1) * G)
+        ref[b:b + 1, hs] = oracle.sdpa_decode(
+            qh[b:b + 1, hs].double().numpy(), kh[b:b + 1, g:g + 1].double().numpy(),
+            vh[b:b + 1, g:g + 1].double().numpy(), scale, None if lens is None else lens[b:b + 1])
+
+    run_threaded(group, [(b, g) for b in range(B) for g in range(Hkv)])
+    return ref
+
+
 def compare(got, ref, dtype, what=""):
     """Assert the bars; returns (max_abs, rel_l2) for reporting."""
     got = np.asarray(got, dtype=np.float64)
@@ -90,6 +168,72 @@ def compare_rel(got, ref, rel_l2, max_rel, what=""):
     assert rel <= rel_l2, "%s: rel-L2 %.3e > %.0e" % (what, rel, rel_l2)
     assert mr <= max_rel, "%s: max-rel %.3e > %.0e" % (what, mr, max_rel)
     return mr, rel
+
+
+def rel_stats(got, ref, what=""):
+    """Pieces of compare_rel's measures for one slice of a tensor:
+    (sum (g-r)^2, sum r^2, max|g-r|, max|r|) over the non-NaN reference
+    elements, after the same NaN-pattern and finiteness checks."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), "%s: NaN pattern differs" % what
+    got, ref = got[~nan_ref], ref[~nan_ref]
+    assert np.isfinite(got).all(), "%s: non-finite value" % what
+    if ref.size == 0:
+        return 0.0, 0.0, 0.0, 0.0
+    d = got - ref
+    return float(d @ d), float(ref @ ref), float(np.abs(d).max()), float(np.abs(ref).max())
+
+
+def check_rel_stats(stats, rel_l2, max_rel, what=""):
+    """compare_rel's bars over a whole tensor from the rel_stats of its slices."""
+    d2 = sum(x[0] for x in stats)
+    r2 = sum(x[1] for x in stats)
+    dmax = max(x[2] for x in stats)
+    rmax = max(x[3] for x in stats)
+    if rmax == 0.0:
+        assert dmax == 0.0, "%s: reference is 0, got nonzero" % what
+        return 0.0, 0.0
+    mr, rel = dmax / rmax, float(np.sqrt(d2 / r2))
+    print("%s: max-rel %.3e rel-L2 %.3e" % (what, mr, rel))
+    assert rel <= rel_l2, "%s: rel-L2 %.3e > %.0e" % (what, rel, rel_l2)
+    assert mr <= max_rel, "%s: max-rel %.3e > %.0e" % (what, mr, max_rel)
+    return mr, rel
+
+
+def backward_whole_check(oracle, q, k, v, dout, scale, mask_kind, grads, dtype, what,
+                         key_lens=None, bias=None, dbias=None):
+    """Every (b, h) head of the gradients against the oracle's backward, one
+    head per thread, the backward bars taken over each whole gradient tensor
+    (dq, dk, dv and, with a bias, dbias [B, Hq, Sq, Sk]) without building the
+    whole fp64 reference.  Needs Hq == Hkv (each head's dk, dv is its own)."""
+    hosts = [t.detach().cpu() for t in (q, k, v, dout)]
+    gh = [t.detach().cpu() for t in grads] + ([dbias.detach().cpu()] if dbias is not None else [])
+    bh = None if bias is None else bias.detach().cpu()
+    B, Hq = q.shape[:2]
+    assert k.shape[1] == Hq, "one K/V head per query head"
+    lens = None if key_lens is None else np.asarray(key_lens)
+
+    def head(bh_):
+        b, h = bh_
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        kw = {}
+        if bh is not None:
+            kw = dict(bias=bh[:, h:h + 1].double().numpy(), return_dbias=True)
+        refs = oracle.sdpa_backward(*(t[sl].double().numpy() for t in hosts), scale, mask_kind,
+                                    None if lens is None else lens[b:b + 1], **kw)
+        out = []
+        for g, r in zip(gh, refs):
+            out.append(rel_stats(g[sl].double().numpy(), r, "%s b=%d h=%d" % (what, b, h)))
+        return out
+
+    res = run_threaded(head, [(b, h) for b in range(B) for h in range(Hq)])
+    names = ["dq", "dk", "dv", "dbias"]
+    for i in range(len(gh)):
+        check_rel_stats([r[i] for r in res], GRAD_REL_L2[dtype], GRAD_MAX_REL[dtype],
+                        "%s %s" % (what, names[i]))
 
 
 def compare_grad(got, ref, dtype, what=""):

@@ -14,7 +14,7 @@ import torch
 import exact_scaled_dot_amd as sd
 import oracle as O
 from exact_scaled_dot_amd.workloads import draw_grad, draw_qkv
-from parity import compare, compare_grad, to64
+from parity import backward_whole_check, compare, compare_grad, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -112,21 +112,16 @@ def test_backward_is_deterministic():
         assert torch.equal(a, b)
 
 
-def test_backward_full_size_sampled_heads():
-    # the causal prefill workload (B4 H16 S4096 D128, bf16) end to end; the
-    # oracle checks two whole heads (every dq, dk, dv row of them)
+def test_backward_full_size_whole_output():
+    # the causal prefill workload (B4 H16 S4096 D128, bf16) end to end; every
+    # dq, dk, dv row of all 64 heads against the oracle (one head per thread),
+    # the bars over each whole gradient tensor
     B, H, S, D = 4, 16, 4096, 128
     q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 560, DEV)
     dout = draw_grad((B, H, S, D), BF16, 561, DEV)
     scale = 1 / math.sqrt(D)
     _, _, dq, dk, dv = run_backward(q, k, v, dout, scale, sd.MASK_CAUSAL, None)
-    for b, h in ((0, 0), (3, 13)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        rq, rk, rv = O.sdpa_backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(dout[sl]),
-                                     scale, O.MASK_CAUSAL)
-        compare_grad(to64(dq[sl]), rq, BF16, "full b=%d h=%d dq" % (b, h))
-        compare_grad(to64(dk[sl]), rk, BF16, "full b=%d h=%d dk" % (b, h))
-        compare_grad(to64(dv[sl]), rv, BF16, "full b=%d h=%d dv" % (b, h))
+    backward_whole_check(O, q, k, v, dout, scale, O.MASK_CAUSAL, (dq, dk, dv), BF16, "full size")
 
 
 # ------------------------------------------------------------------ atomic dQ

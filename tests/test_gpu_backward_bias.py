@@ -12,7 +12,7 @@ import torch
 import exact_scaled_dot_amd as sd
 import oracle as O
 from exact_scaled_dot_amd.workloads import draw_bias, draw_grad, draw_qkv
-from parity import compare_grad, to64
+from parity import backward_whole_check, compare_grad, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -109,20 +109,14 @@ def test_dbias_hidden_keys_are_zero():
     assert db[0, :, ~hidden].abs().sum() > 0
 
 
-def test_backward_bias_full_size_sampled_heads():
+def test_backward_bias_full_size_whole_output():
     # the causal prefill workload with a per-head bias [1, 16, 4096, 4096];
-    # the oracle checks two whole heads, dbias included
+    # every head's dq, dk, dv and bias gradient against the oracle
     B, H, S, D = 4, 16, 4096, 128
     q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 1150, DEV)
     dout = draw_grad((B, H, S, D), BF16, 1151, DEV)
     bias = draw_bias((1, H, S, S), BF16, 1152, DEV)
     scale = 1 / math.sqrt(D)
     dq, dk, dv, db = run(q, k, v, dout, bias, scale, sd.MASK_CAUSAL, None)
-    for b, h in ((0, 3), (3, 14)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        rq, rk, rv, rb = O.sdpa_backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(dout[sl]), scale,
-                                         O.MASK_CAUSAL, bias=to64(bias[:, h:h + 1]), return_dbias=True)
-        compare_grad(to64(dq[sl]), rq, BF16, "full b=%d h=%d dq" % (b, h))
-        compare_grad(to64(dk[sl]), rk, BF16, "full b=%d h=%d dk" % (b, h))
-        compare_grad(to64(dv[sl]), rv, BF16, "full b=%d h=%d dv" % (b, h))
-        compare_grad(to64(db[sl]), rb, BF16, "full b=%d h=%d dbias" % (b, h))
+    backward_whole_check(O, q, k, v, dout, scale, O.MASK_CAUSAL, (dq, dk, dv), BF16,
+                         "bias full size", bias=bias, dbias=db)

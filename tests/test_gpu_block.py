@@ -10,7 +10,7 @@ import torch
 import exact_scaled_dot_amd as sd
 import oracle as O
 from exact_scaled_dot_amd.workloads import draw_block
-from parity import compare_block, to64
+from parity import compare_block, run_threaded, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -78,20 +78,23 @@ def test_block_deterministic_and_caller_buffers():
     assert torch.equal(a, b)
 
 
-def test_block_full_size_sampled_rows():
+def test_block_full_size_whole_output():
     # the causal prefill workload as a block: batch 4, 4096 tokens, 16 heads
-    # of 128 (model 2048); the oracle checks 96 rows of two batches, every
-    # column, with q, k, v for those batches computed whole
+    # of 128 (model 2048); every row of y against the oracle, one batch per
+    # thread (its projections and attention computed whole)
     B, S, M, H = 4, 4096, 2048, 16
     ins, y = run_block(B, S, M, H, BF16, 950, sd.MASK_CAUSAL)
-    rng = np.random.default_rng(951)
-    rows = [(b, s) for b in (0, 3) for s in (0, 1, 255, 256, 2047, 4095)]
-    rows += [(int(b), int(s)) for b, s in zip(rng.choice([0, 3], 84), rng.integers(0, S, 84))]
-    rows = np.array(rows)
-    x64 = to64(ins[0])
-    ref = O.block_forward_rows(x64, *(to64(t) for t in ins[1:]), H, rows, None, O.MASK_CAUSAL)
-    got = to64(y)[rows[:, 0], rows[:, 1]]
-    compare_block(got, ref, BF16, "full-size block rows")
+    x = ins[0].cpu()
+    w64 = [to64(t) for t in ins[1:]]
+    ref = np.empty((B, S, M))
+
+    def one(b):
+        xb = x[b:b + 1].double().numpy()
+        rows = np.stack([np.zeros(S, dtype=np.int64), np.arange(S)], axis=1)
+        ref[b] = O.block_forward_rows(xb, *w64, H, rows, None, O.MASK_CAUSAL)
+
+    run_threaded(one, range(B))
+    compare_block(to64(y), ref, BF16, "full-size block")
 
 
 def test_block_tile_sizes():

@@ -17,7 +17,8 @@ import torch
 import exact_scaled_dot_amd as sd
 import oracle as O
 from exact_scaled_dot_amd.workloads import draw_bias, draw_grad, draw_paged, draw_qkv
-from parity import compare, compare_grad, sample_rows, to64
+from parity import (backward_whole_check, compare, compare_grad, oracle_decode_whole,
+                    oracle_forward_whole, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -186,18 +187,15 @@ def test_paged_prefill_wide_head_dim():
     compare(to64(outp), refp, BF16, "paged prefill D=256")
 
 
-def test_forward_wide_full_size_sampled_rows():
-    # the 256-wide causal prefill leg at its full size (B4 H8 S4096); the
-    # oracle checks sampled rows (tile edges included)
+def test_forward_wide_full_size_whole_output():
+    # the 256-wide causal prefill leg at its full size (B4 H8 S4096), every row
     B, H, S, D = 4, 8, 4096, 256
     q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 797, DEV)
     scale = 1 / math.sqrt(D)
     out = sd.sdpa_forward(q, k, v, scale, sd.MASK_CAUSAL)
     torch.cuda.synchronize()
-    rows = sample_rows(B, H, S, 64, 798)
-    ref, _ = O.sdpa_forward_rows(to64(q), to64(k), to64(v), scale, O.MASK_CAUSAL, None, rows)
-    got = to64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    compare(got, ref, BF16, "wide full size")
+    ref = oracle_forward_whole(O, q, k, v, scale, O.MASK_CAUSAL)
+    compare(to64(out), ref, BF16, "wide full size")
 
 
 def test_block_wide_heads():
@@ -352,20 +350,18 @@ def test_headdim_split_outputs_past_head_dim_untouched():
     compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.1, O.MASK_CAUSAL), BF16, "D=520")
 
 
-def test_forward_headdim_split_full_size_sampled_rows():
+def test_forward_headdim_split_full_size_whole_output():
     # a 4096-token causal prefill with 1024-wide heads (the headline prefill's
-    # token count and B*H*D); sampled rows of every head against the oracle
+    # token count and B*H*D); every row and its lse against the oracle
     B, H, S, D = 1, 8, 4096, 1024
     q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 950, DEV)
     scale = 1 / math.sqrt(D)
     out, lse = sd.sdpa_forward_lse(q, k, v, scale, sd.MASK_CAUSAL)
     torch.cuda.synchronize()
-    rows = sample_rows(B, H, S, 48, 951)
-    ref, rlse = O.sdpa_forward_rows(to64(q), to64(k), to64(v), scale, O.MASK_CAUSAL, None, rows)
-    got = to64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    compare(got, ref, BF16, "D=1024 full size")
-    glse = to64(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    assert np.abs(glse - rlse).max() < 1e-2
+    ref, rlse = oracle_forward_whole(O, q, k, v, scale, O.MASK_CAUSAL, row_block=512,
+                                     return_lse=True)
+    compare(to64(out), ref, BF16, "D=1024 full size")
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
 
 
 @pytest.mark.parametrize("D", [264, 512, 1024])
@@ -393,22 +389,17 @@ def test_decode_headdim_split_large_group_fp16():
     compare(to64(out), ref, F16, "split decode fp16 G=40 D=640")
 
 
-def test_decode_headdim_split_full_size_sampled_heads():
+def test_decode_headdim_split_full_size_whole_output():
     # the 1024-wide decode leg at full size (B8, 32/8 heads, 32768 cached
-    # keys, 32 splits; batch 5 padded to 20001 keys); the oracle checks every
-    # query head of two (batch, K/V head) groups
+    # keys, 32 splits; batch 5 padded to 20001 keys); every query head
     B, Hq, Hkv, Sk, D, splits = 8, 32, 8, 32768, 1024, 32
     q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 980, DEV)
     lens = torch.full((B,), Sk, dtype=torch.int32, device=DEV)
     lens[5] = 20001
     out = sd.sdpa_decode(q, k, v, 1 / math.sqrt(D), lens, splits)
     torch.cuda.synchronize()
-    G = Hq // Hkv
-    for b, g in ((0, 3), (5, 6)):
-        hs = slice(g * G, (g + 1) * G)
-        ref = O.sdpa_decode(to64(q[b:b + 1, hs]), to64(k[b:b + 1, g:g + 1]), to64(v[b:b + 1, g:g + 1]),
-                            1 / math.sqrt(D), lens[b:b + 1].cpu().numpy())
-        compare(to64(out[b:b + 1, hs]), ref, BF16, "D=1024 decode b=%d group=%d" % (b, g))
+    ref = oracle_decode_whole(O, q, k, v, 1 / math.sqrt(D), lens.cpu().numpy())
+    compare(to64(out), ref, BF16, "D=1024 decode whole output")
 
 
 @pytest.mark.parametrize("model,heads", [(1024, 2), (2048, 2), (1536, 3)])
@@ -425,22 +416,17 @@ def test_block_headdim_split(model, heads):
     compare_block(to64(y), ref, BF16, "block model=%d heads=%d" % (model, heads))
 
 
-def test_decode_wide_full_size_sampled_heads():
+def test_decode_wide_full_size_whole_output():
     # the 256-wide decode leg at its full size (B32, 32/8 heads, 32768 cached
-    # keys, 32 splits; batch 17 padded to 9999 keys); every query head of two
-    # (batch, K/V head) groups against the oracle
+    # keys, 32 splits; batch 17 padded to 9999 keys); every query head
     B, Hq, Hkv, Sk, D, splits = 32, 32, 8, 32768, 256, 32
     q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 1030, DEV)
     lens = torch.full((B,), Sk, dtype=torch.int32, device=DEV)
     lens[17] = 9999
     out = sd.sdpa_decode(q, k, v, 1 / math.sqrt(D), lens, splits)
     torch.cuda.synchronize()
-    G = Hq // Hkv
-    for b, g in ((2, 1), (17, 7)):
-        hs = slice(g * G, (g + 1) * G)
-        ref = O.sdpa_decode(to64(q[b:b + 1, hs]), to64(k[b:b + 1, g:g + 1]), to64(v[b:b + 1, g:g + 1]),
-                            1 / math.sqrt(D), lens[b:b + 1].cpu().numpy())
-        compare(to64(out[b:b + 1, hs]), ref, BF16, "D=256 decode b=%d group=%d" % (b, g))
+    ref = oracle_decode_whole(O, q, k, v, 1 / math.sqrt(D), lens.cpu().numpy())
+    compare(to64(out), ref, BF16, "D=256 decode whole output")
 
 
 # ------------------------------------------------ backward above 128 (to 512)
@@ -490,9 +476,9 @@ def test_backward_headdim_split_rectangular_dead_rows_and_repeatable():
     compare_grad(to64(dv[1:]), rv, BF16, "rect dv")
 
 
-def test_backward_headdim_split_full_size_sampled_heads():
+def test_backward_headdim_split_full_size_whole_output():
     # the 256-wide-head causal backward at its benchmarked size (B4 H8 S4096
-    # D256, the same launch); two heads against the oracle
+    # D256, the same launch); every head against the oracle
     B, H, S, D = 4, 8, 4096, 256
     q, k, v = draw_qkv(B, H, H, S, S, D, BF16, 1220, DEV)
     dout = draw_grad((B, H, S, D), BF16, 1221, DEV)
@@ -500,10 +486,5 @@ def test_backward_headdim_split_full_size_sampled_heads():
     out, lse = sd.sdpa_forward_lse(q, k, v, scale, sd.MASK_CAUSAL)
     dq, dk, dv = sd.sdpa_backward(q, k, v, out, dout, lse, scale, sd.MASK_CAUSAL)
     torch.cuda.synchronize()
-    for b, h in ((0, 2), (3, 7)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        rq, rk, rv = O.sdpa_backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(dout[sl]), scale,
-                                     O.MASK_CAUSAL)
-        compare_grad(to64(dq[sl]), rq, BF16, "D=256 full b=%d h=%d dq" % (b, h))
-        compare_grad(to64(dk[sl]), rk, BF16, "D=256 full b=%d h=%d dk" % (b, h))
-        compare_grad(to64(dv[sl]), rv, BF16, "D=256 full b=%d h=%d dv" % (b, h))
+    backward_whole_check(O, q, k, v, dout, scale, O.MASK_CAUSAL, (dq, dk, dv), BF16,
+                         "D=256 full size")

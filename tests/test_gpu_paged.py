@@ -10,7 +10,7 @@ import torch
 import exact_scaled_dot_amd as sd
 import oracle as O
 from exact_scaled_dot_amd.workloads import draw_paged, draw_qkv
-from parity import compare, to64
+from parity import compare, oracle_forward_whole, run_threaded, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -154,9 +154,10 @@ def test_paged_deterministic():
 
 
 @pytest.mark.slow
-def test_full_size_paged_decode_sampled():
+def test_full_size_paged_decode_whole_output():
     # the serving shape next to the dense decode workload: 64 sequences of
-    # 32768 cached keys in 16-key pages, shuffled; check 4 whole queries
+    # 32768 cached keys in 16-key pages, shuffled; every query against the
+    # oracle (one query per thread, over that query's own pages)
     n, L = 64, 32768
     inp = draw_paged([L] * n, range(n), [L - 1] * n, 32, 8, 128, 16, torch.bfloat16, 20, DEV,
                      extra_pages=0)
@@ -165,15 +166,20 @@ def test_full_size_paged_decode_sampled():
                                   inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, True,
                                   L, 32)
     torch.cuda.synchronize()
-    got = to64(out)
     tables = inp["block_tables"].cpu().numpy()
-    for t in (0, 1, 31, 63):
-        pg = tables[t]
-        kq = to64(inp["k_cache"][torch.as_tensor(pg, device=DEV).long()])  # this query's pages only
-        vq = to64(inp["v_cache"][torch.as_tensor(pg, device=DEV).long()])
-        ref = O.paged_attention(to64(inp["q"][t:t + 1]), kq, vq, np.arange(len(pg))[None, :],
-                                np.array([L]), np.array([0]), np.array([L - 1]), scale, True)
-        compare(got[t:t + 1], ref, torch.bfloat16, "paged decode query %d" % t)
+    qh, kc, vc = (inp[x].cpu() for x in ("q", "k_cache", "v_cache"))
+    ref = np.empty((n, 32, 128))
+
+    def one(t):
+        pg = torch.as_tensor(tables[t]).long()
+        ref[t:t + 1] = O.paged_attention(qh[t:t + 1].double().numpy(), kc[pg].double().numpy(),
+                                         vc[pg].double().numpy(), np.arange(len(pg))[None, :],
+                                         np.array([L]), np.array([0]), np.array([L - 1]), scale,
+                                         True)
+
+    run_threaded(one, range(n), workers=8)
+    max_abs, rel = compare(to64(out), ref, torch.bfloat16, "paged decode whole output")
+    print("paged decode whole output: max-abs %.3e rel-L2 %.3e" % (max_abs, rel))
 
 
 # ------------------------------------------------------------ prefill chunks
@@ -278,19 +284,26 @@ def test_paged_prefill_matches_dense_prefill_bitwise():
 
 
 @pytest.mark.slow
-def test_full_size_paged_prefill_sampled():
+def test_full_size_paged_prefill_whole_output():
     # the long causal prefill workload's shape (4 sequences x 4096, 16 heads,
-    # D 128) as whole-sequence chunks over shuffled 16-key pages; 24 rows
-    n, L, H = 4, 4096, 16
-    inp, out, scale, cu, qs, qp = run_prefill([L] * n, [L] * n, H, H, 128, 16, True, seed=38)
-    got = to64(out)
-    rng = np.random.default_rng(38)
-    rows = sorted(set([0, 1, 127, 128, L - 1, L, 2 * L + 4000, 4 * L - 1]
-                      + rng.integers(0, 4 * L, size=16).tolist()))
-    kc, vc = to64(inp["k_cache"]), to64(inp["v_cache"])
-    ref = O.paged_attention(to64(inp["q"])[rows], kc, vc, inp["block_tables"].cpu().numpy(),
-                            np.array([L] * n), qs[rows], qp[rows], scale, True)
-    compare(got[rows], ref, torch.bfloat16, "full-size paged prefill rows")
+    # D 128) as whole-sequence chunks over shuffled 16-key pages, every row
+    # checked.  Each sequence's keys come through the oracle's page gather;
+    # a whole-sequence causal chunk is then the dense causal forward of that
+    # sequence (the reduction the oracle's own pins fix), evaluated per head
+    # in row blocks.
+    n, L, H, D = 4, 4096, 16, 128
+    inp, out, scale, cu, qs, qp = run_prefill([L] * n, [L] * n, H, H, D, 16, True, seed=38)
+    assert np.array_equal(qp, np.tile(np.arange(L), n))
+    tables = inp["block_tables"].cpu().numpy()
+    kc, vc = (inp[x].cpu().float().numpy() for x in ("k_cache", "v_cache"))
+    qd = inp["q"].cpu().view(n, L, H, D).permute(0, 2, 1, 3)
+    kd = torch.stack([torch.from_numpy(O.paged_gather(kc, tables[s], L, 16)) for s in range(n)])
+    vd = torch.stack([torch.from_numpy(O.paged_gather(vc, tables[s], L, 16)) for s in range(n)])
+    ref = oracle_forward_whole(O, qd, kd.permute(0, 2, 1, 3), vd.permute(0, 2, 1, 3), scale,
+                               O.MASK_CAUSAL)
+    got = to64(out).reshape(n, L, H, D).transpose(0, 2, 1, 3)
+    max_abs, rel = compare(got, ref, torch.bfloat16, "paged prefill whole output")
+    print("paged prefill whole output: max-abs %.3e rel-L2 %.3e" % (max_abs, rel))
 
 
 # ------------------------------------------------- head dims above 256 (to 1024)
