@@ -59,6 +59,9 @@ METRIC = "attention fwd TFLOP/s (+% bf16 MFMA peak); decode HBM GB/s (+% peak)"
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
+SMALL_FP32 = "fp32_single_head_s128_d64"
+SMALL_CAUSAL = "bf16_causal_b8_h4_s128_d64"
 
 PREFILL = "bf16_causal_b4_h16_s4096_d128"
 PADDED = "bf16_gqa32x8_padded_b2_s8192_d128"
@@ -146,6 +149,28 @@ def formula_flops(B, Hq, Sq, Sk, D, causal):
     return f / 2 if causal else f
 
 
+def timing(samples_ms):
+    """Mean, median and minimum of per-call HIP-event times, in ms."""
+    import statistics
+    return {"ms": round(sum(samples_ms) / len(samples_ms), 4),
+            "ms_median": round(statistics.median(samples_ms), 4),
+            "ms_min": round(min(samples_ms), 4), "calls_timed": len(samples_ms)}
+
+
+def stored_sq(workload, source):
+    """Sustained clock and MFMA activity of a kernel from the committed SQ
+    counter record (rocprofv3 --pmc passes), if it is still current."""
+    try:
+        with open(SQ_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    return {k: rec[k] for k in ("clock_ghz", "mfma_busy", "mfma_coexec_of_busy",
+                                "counter_duration_us") if k in rec}
+
+
 def padded_algorithmic_flops(w, key_lens):
     # 4 * Hq * Sq * D per visible key, summed over the batch (no causal mask here)
     return 4.0 * w.Hq * w.Sq * w.D * float(sum(int(x) for x in key_lens))
@@ -178,6 +203,42 @@ def cpu_baseline(budget_s):
             "kind": "oracle",
             "sample": "%d of %d (batch, head) pairs of %s, %.1f s, fp64 NumPy/BLAS; affinity %d cores"
                       % (heads, w.B * w.Hq, w.name, dt, len(os.sched_getaffinity(0)))}
+
+
+def cpu_baseline_padded(budget_s):
+    """fp64 oracle on whole (batch, query head) pairs of the padded grouped
+    prefill workload (its visible keys only count as work), until the budget
+    is spent; with the whole workload's time extrapolated from that rate."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from exact_scaled_dot_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[PADDED]
+    inp = make_inputs(w, "cpu")
+    q, k, v = (inp[x].to(torch.float64).numpy() for x in ("q", "k", "v"))
+    lens = inp["key_lens"].numpy()
+    G = w.Hq // w.Hkv
+    heads, flops, t0 = 0, 0.0, time.perf_counter()
+    while heads < w.B * w.Hq:
+        b, h = divmod(heads, w.Hq)
+        oracle.sdpa_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1],
+                            v[b:b + 1, h // G:h // G + 1], w.scale, oracle.MASK_KEY_PADDING,
+                            lens[b:b + 1])
+        flops += 4.0 * w.Sq * w.D * float(lens[b])
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    rate = flops / dt
+    total = padded_algorithmic_flops(w, lens.tolist())
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "whole_workload_s_extrapolated": round(total / rate, 1),
+            "sample": "%d of %d (batch, query head) pairs of %s, %.1f s, fp64 NumPy/BLAS"
+                      % (heads, w.B * w.Hq, w.name, dt)}
 
 
 def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
@@ -270,6 +331,53 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     return out
 
 
+# Kernels whose SQ counters --ingest-sq records: workload -> (kernel, source)
+SQ_KERNELS = {"prefill": ("forward_bf16_kernel", "forward.hip"),
+              "padded": ("forward_bf16_kernel", "forward.hip")}
+
+
+def ingest_sq(workload, csvs):
+    """One record of SQ counters for a kernel from rocprofv3 --pmc passes of a
+    one-call bench (--only WORKLOAD): the median of each counter over the
+    kernel's dispatches, the dispatch duration from the counter passes' own
+    timestamps, and from them the sustained clock (GRBM_GUI_ACTIVE counts GPU
+    clocks summed over the 8 XCDs) and the MFMA busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES sums over the 1024 SIMDs)."""
+    import csv
+    import statistics
+    kernel, src = SQ_KERNELS[workload]
+    per, dur = {}, []
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                dur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    med = {k: statistics.median(v) for k, v in per.items()}
+    d_ns = statistics.median(dur)
+    rec = {"kernel": kernel, "source_sha256_16": kernel_source_hash(src),
+           "counters": {k: med[k] for k in sorted(med)},
+           "counter_duration_us": round(d_ns / 1e3, 2)}
+    if "GRBM_GUI_ACTIVE" in med:
+        xcd_cycles = med["GRBM_GUI_ACTIVE"] / 8
+        rec["clock_ghz"] = round(xcd_cycles / d_ns, 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            rec["mfma_busy"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / xcd_cycles, 4)
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in med and med.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        rec["mfma_coexec_of_busy"] = round(med["SQ_VALU_MFMA_COEXEC_CYCLES"]
+                                           / med["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+    try:
+        with open(SQ_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = rec
+    with open(SQ_FILE, "w") as f:
+        json.dump(allrec, f, indent=1)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +385,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--small-iters", type=int, default=500,
+                    help="timed calls of each small configuration (0: skip them)")
     ap.add_argument("--only", choices=["prefill", "padded", "decode", "paged", "paged_prefill",
                                        "backward", "backward_atomic", "backward_bias",
                                        "backward_wide", "bias",
@@ -288,7 +398,14 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--ingest-sq", nargs="+", metavar="ARG",
+                    help="WORKLOAD CSV [CSV ...]: record SQ counters of a --only WORKLOAD run "
+                         "in profiles/sq_counters.json and exit")
     args = ap.parse_args()
+
+    if args.ingest_sq:
+        print(json.dumps(ingest_sq(args.ingest_sq[0], args.ingest_sq[1:]), indent=1))
+        return
 
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters)
@@ -496,7 +613,34 @@ def main():
             ev[name].append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name in order}
+    times = {name: [a.elapsed_time(b) for a, b in ev[name]] for name in order}
+    ms = {name: sum(t) / len(t) for name, t in times.items()}
+
+    # The small configurations (one fp32 head; the tensai guide's block-sized
+    # causal attention): microseconds per call, so each is timed over many
+    # calls of its own after the step loop (not part of a step).
+    small = {}
+    if args.only is None and args.small_iters > 0:
+        for key, w in (("config1_fp32", WORKLOADS[SMALL_FP32]),
+                       ("config2_causal_small", WORKLOADS[SMALL_CAUSAL])):
+            inp = make_inputs(w, dev)
+            o = torch.empty_like(inp["q"])
+            kind = sd.MASK_CAUSAL if w.causal else sd.MASK_NONE
+            call = (lambda i, o, w, kind: lambda: sd.sdpa_forward(
+                i["q"], i["k"], i["v"], w.scale, kind, None, o))(inp, o, w, kind)
+            for _ in range(50):
+                call()
+            torch.cuda.synchronize()
+            evs = []
+            for _ in range(args.small_iters):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                call()
+                b.record(stream)
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            small[key] = (w, [a.elapsed_time(b) for a, b in evs])
 
     rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
@@ -510,27 +654,41 @@ def main():
         rec["config"] = {"workload": wp.name, "B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq,
                          "Sk": wp.Sk, "D": wp.D, "mask": "causal", "scale": wp.scale,
                          "step_calls": order}
-        rec["prefill_ms"] = round(ms["prefill"], 4)
+        tp = timing(times["prefill"])
+        rec["prefill_ms"] = tp["ms"]
+        rec["prefill_ms_median"] = tp["ms_median"]
+        rec["prefill_ms_min"] = tp["ms_min"]
         rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 3),
                            "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                            "kernel": "forward_bf16_kernel<128>",
-                           "flops_per_launch": fl}
+                           "flops_per_launch": fl,
+                           "sq_counters": stored_sq("prefill", "forward.hip")}
     if "padded" in ms:
         fl = formula_flops(wg.B, wg.Hq, wg.Sq, wg.Sk, wg.D, False)
         fa = padded_algorithmic_flops(wg, lens_g)
-        rec["padded"] = {"workload": wg.name, "ms": round(ms["padded"], 4),
+        rec["padded"] = {"workload": wg.name, **timing(times["padded"]),
                          "tflops_formula": round(fl / (ms["padded"] * 1e-3) / 1e12, 3),
                          "tflops_algorithmic": round(fa / (ms["padded"] * 1e-3) / 1e12, 3),
                          "frac_algorithmic": round(fa / (ms["padded"] * 1e-3) / 1e12
                                                    / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "key_lens": lens_g}
+                         "key_lens": lens_g,
+                         "roofline": {"bound": "mfma",
+                                      "achieved": round(fa / (ms["padded"] * 1e-3) / 1e12, 3),
+                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(fa / (ms["padded"] * 1e-3) / 1e12
+                                                    / BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "traffic": stored_traffic("padded", "forward.hip"),
+                                      "kernel": "forward_bf16_kernel<128>",
+                                      "flops_per_launch": fa,
+                                      "flops": "4*Hq*Sq*D per visible key (key_lens)",
+                                      "sq_counters": stored_sq("padded", "forward.hip")}}
     if "decode" in ms:
         kv_bytes = 2 * wd.B * wd.Hkv * wd.Sk * wd.D * 2
         qo_bytes = 2 * wd.B * wd.Hq * wd.D * 2
         by = kv_bytes + qo_bytes
         gbs = by / (ms["decode"] * 1e-3) / 1e9
-        rec["decode"] = {"workload": wd.name, "ms": round(ms["decode"], 4), "value": round(gbs, 1),
+        rec["decode"] = {"workload": wd.name, **timing(times["decode"]), "value": round(gbs, 1),
                          "unit": "GB/s",
                          "tflops_formula": round(formula_flops(wd.B, wd.Hq, 1, wd.Sk, wd.D, False)
                                                  / (ms["decode"] * 1e-3) / 1e12, 3),
@@ -545,7 +703,7 @@ def main():
         by = kv_bytes + 2 * wd.B * wd.Hq * wd.D * 2 + ipg["block_tables"].numel() * 4
         gbs = by / (ms["paged"] * 1e-3) / 1e9
         rec["paged"] = {"workload": "bf16_gqa32x8_paged_decode_b64_sk32768_d128_page16",
-                        "ms": round(ms["paged"], 4), "value": round(gbs, 1), "unit": "GB/s",
+                        **timing(times["paged"]), "value": round(gbs, 1), "unit": "GB/s",
                         "page_size": PAGE_SIZE, "pages": ipg["pages"],
                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -557,7 +715,7 @@ def main():
         fl = formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
         tf = fl / (ms["paged_prefill"] * 1e-3) / 1e12
         rec["paged_prefill"] = {"workload": "bf16_causal_paged_prefill_b4_h16_s4096_d128_page16",
-                                "ms": round(ms["paged_prefill"], 4), "value": round(tf, 3),
+                                **timing(times["paged_prefill"]), "value": round(tf, 3),
                                 "unit": "TFLOP/s", "page_size": PAGE_SIZE,
                                 "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -570,7 +728,7 @@ def main():
         fl = 2.5 * formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
         tf = fl / (ms["backward"] * 1e-3) / 1e12
         rec["backward"] = {"workload": "bf16_causal_backward_b4_h16_s4096_d128",
-                           "ms": round(ms["backward"], 4), "value": round(tf, 3),
+                           **timing(times["backward"]), "value": round(tf, 3),
                            "unit": "TFLOP/s",
                            "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -582,7 +740,7 @@ def main():
         fl = 2.5 * formula_flops(wp.B, wp.Hq, wp.Sq, wp.Sk, wp.D, True)
         tf = fl / (ms["backward_atomic"] * 1e-3) / 1e12
         rec["backward_atomic"] = {"workload": "bf16_causal_backward_atomic_b4_h16_s4096_d128",
-                                  "ms": round(ms["backward_atomic"], 4), "value": round(tf, 3),
+                                  **timing(times["backward_atomic"]), "value": round(tf, 3),
                                   "unit": "TFLOP/s",
                                   "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -596,7 +754,7 @@ def main():
         tf = fl / (ms["backward_bias"] * 1e-3) / 1e12
         dbias_bytes = wp.B * wp.Hq * wp.Sq * wp.Sk * 2
         rec["backward_bias"] = {"workload": "bf16_causal_backward_bias_b4_h16_s4096_d128",
-                                "ms": round(ms["backward_bias"], 4), "value": round(tf, 3),
+                                **timing(times["backward_bias"]), "value": round(tf, 3),
                                 "unit": "TFLOP/s", "bias_shape": [1, wp.Hq, wp.Sq, wp.Sk],
                                 "dbias_shape": [wp.B, wp.Hq, wp.Sq, wp.Sk],
                                 "dbias_bytes_written": dbias_bytes,
@@ -616,7 +774,7 @@ def main():
         tiles = sum(2 * (qb + 1) for qb in range(nqb))          # 64-key tiles per (b, h)
         bias_bytes = wp.B * wp.Hq * 128 * 64 * 2 * tiles
         rec["bias"] = {"workload": "bf16_causal_bias_b4_h16_s4096_d128",
-                       "ms": round(ms["bias"], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                       **timing(times["bias"]), "value": round(tf, 3), "unit": "TFLOP/s",
                        "bias_shape": [1, wp.Hq, wp.Sq, wp.Sk],
                        "bias_bytes_read": bias_bytes,
                        "bias_gbs": round(bias_bytes / (ms["bias"] * 1e-3) / 1e9, 1),
@@ -631,7 +789,7 @@ def main():
         fl = formula_flops(B, H, S, S, D, True)
         tf = fl / (ms["wide"] * 1e-3) / 1e12
         rec["wide"] = {"workload": "bf16_causal_b%d_h%d_s%d_d%d" % (B, H, S, D),
-                       "ms": round(ms["wide"], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                       **timing(times["wide"]), "value": round(tf, 3), "unit": "TFLOP/s",
                        "executed_mfma_flops": 1.5 * fl,
                        "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -644,7 +802,7 @@ def main():
         fl = 2.5 * formula_flops(B, H, S, S, D, True)
         tf = fl / (ms["backward_wide"] * 1e-3) / 1e12
         rec["backward_wide"] = {"workload": "bf16_causal_backward_b%d_h%d_s%d_d%d" % (B, H, S, D),
-                                "ms": round(ms["backward_wide"], 4), "value": round(tf, 3),
+                                **timing(times["backward_wide"]), "value": round(tf, 3),
                                 "unit": "TFLOP/s",
                                 "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -658,7 +816,7 @@ def main():
         fl = formula_flops(B, H, S, S, D, True)
         tf = fl / (ms["widest"] * 1e-3) / 1e12
         rec["widest"] = {"workload": "bf16_causal_b%d_h%d_s%d_d%d" % (B, H, S, D),
-                         "ms": round(ms["widest"], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                         **timing(times["widest"]), "value": round(tf, 3), "unit": "TFLOP/s",
                          "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                       "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                       "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -670,7 +828,7 @@ def main():
         by = 2 * B * Hkv * Sk * D * 2 + 2 * B * Hq * D * 2
         gbs = by / (ms["decode_wide"] * 1e-3) / 1e9
         rec["decode_wide"] = {"workload": "bf16_gqa32x8_decode_b%d_sk%d_d%d" % (B, Sk, D),
-                              "ms": round(ms["decode_wide"], 4), "value": round(gbs, 1),
+                              **timing(times["decode_wide"]), "value": round(gbs, 1),
                               "unit": "GB/s", "num_splits": wd.num_splits,
                               "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -684,7 +842,7 @@ def main():
         by = 2 * B * Hkv * Sk * D * 2 + 2 * B * Hq * D * 2
         gbs = by / (ms["decode_widest"] * 1e-3) / 1e9
         rec["decode_widest"] = {"workload": "bf16_gqa32x8_decode_b%d_sk%d_d%d" % (B, Sk, D),
-                                "ms": round(ms["decode_widest"], 4), "value": round(gbs, 1),
+                                **timing(times["decode_widest"]), "value": round(gbs, 1),
                                 "unit": "GB/s", "num_splits": wd.num_splits,
                                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -700,7 +858,7 @@ def main():
         fl = block_flops(B, S, M, H, True)
         tf = fl / (ms[name] * 1e-3) / 1e12
         rec[name] = {"workload": "bf16_causal_block_b%d_s%d_m%d_h%d" % (B, S, M, H),
-                     "ms": round(ms[name], 4), "value": round(tf, 3), "unit": "TFLOP/s",
+                     **timing(times[name]), "value": round(tf, 3), "unit": "TFLOP/s",
                      "flops": "8*B*S*model^2 (four projections) + the causal attention formula",
                      "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                   "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -709,6 +867,14 @@ def main():
                                   "kernel": "gemm_kernel<q/k/v> + forward_bf16_kernel + "
                                             "gemm_kernel<out>",
                                   "flops_per_launch": fl}}
+    for key, (w, t) in small.items():
+        fl = formula_flops(w.B, w.Hq, w.Sq, w.Sk, w.D, w.causal)
+        med = timing(t)["ms_median"]
+        rec[key] = {"workload": w.name, "dtype": "f32" if w.dtype == torch.float32 else "bf16",
+                    **timing(t), "us_median": round(med * 1e3, 2),
+                    "us_min": round(min(t) * 1e3, 2),
+                    "tflops_median": round(fl / (med * 1e-3) / 1e12, 4),
+                    "note": "timed alone, per call, after the step loop; launch-bound"}
     if "value" not in rec:  # --only another call: report that call
         blk = [n for n in list(BLOCKS) + ["wide", "widest", "decode_wide", "decode_widest"] if n in rec]
         if blk:
@@ -746,6 +912,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    if not args.no_cpu_baseline and args.only in (None, "padded") and "padded" in rec:
+        rec["padded"]["cpu_baseline"] = cpu_baseline_padded(args.cpu_budget / 2)
     print(json.dumps(rec), flush=True)
 
 
