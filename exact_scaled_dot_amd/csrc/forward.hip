@@ -18,6 +18,10 @@
 // whenever the max moves.  Keys past a row's limit (causal, key padding, Sk)
 // get -inf and hence weight exactly 0; tiles past the workgroup's last
 // visible key are never loaded.
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -27,6 +31,9 @@ namespace {
 constexpr int kBr = 128;       // query rows per workgroup
 constexpr int kBc = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 waves of 64
+// Cache-policy operand of a buffer load: non-temporal (streamed through the
+// L2 with early eviction).
+constexpr int kNonTemporal = 2;
 
 // LDS row that holds tile key j in the bf16 K tile: bits 2 and 3 of j are
 // swapped inside each group of 32 keys.  With this order the 32x32 score
@@ -39,6 +46,7 @@ __device__ __forceinline__ int k_lds_row(int j) {
 
 struct TileInfo {
     int b, h, gk, q0;
+    bool rev;  // sweep the keys last tile first (only honoured where order is free)
 };
 
 // Workgroup -> (batch, head, query block).  Workgroups are dealt to the 8
@@ -50,7 +58,11 @@ struct TileInfo {
 // into one L2.  Under a causal mask the work of a query block grows with its
 // index; there the units go in pairs and, inside a pair, query blocks run
 // longest first across both units (a longest-first list schedule, which
-// keeps the XCD's last workgroups short).
+// keeps the XCD's last workgroups short).  Without a causal mask every
+// workgroup of a K/V head sweeps all its keys, and the XCD runs its
+// workgroups in groups of what it holds at once: every other group sweeps
+// the keys backwards (rev), so it starts on the keys the group before it
+// touched last, which the L2 still holds.
 __device__ __forceinline__ TileInfo decode_tile(const ForwardArgs& a) {
     const int nqb = (a.Sq + kBr - 1) / kBr;
     const int G = a.Hq / a.Hkv;
@@ -76,6 +88,7 @@ __device__ __forceinline__ TileInfo decode_tile(const ForwardArgs& a) {
     ti.gk = unit % a.Hkv;
     ti.h = ti.gk * G + hsub;
     ti.q0 = (a.causal ? nqb - 1 - qord : qord) * kBr;
+    ti.rev = !a.causal && a.sweep_group > 0 && ((local / a.sweep_group) & 1);
     return ti;
 }
 
@@ -258,13 +271,27 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
 
     // Q fragment for the B operand of S^T = K Q^T: lane holds Q[qi][16t + 8hg .. +7]
     // (rows >= nrows read as zeros).
+    // Without a causal mask (dense) Q is read non-temporally: it is read once,
+    // and the XCD's L2 is better spent keeping the K/V rows the next
+    // workgroups sweep (see decode_tile).
+    const bool stream_q_o = !PAGED && !a.causal;
     u32x4 qr[D / 16];
     {
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, (uint32_t)nrows * qstride);
+        if (stream_q_o) {
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            const int d0 = 16 * t + 8 * hg;
-            qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, d0 < DR ? qi * qstride + d0 * 2 : kOut, 0, 0);
+            for (int t = 0; t < D / 16; ++t) {
+                const int d0 = 16 * t + 8 * hg;
+                qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, d0 < DR ? qi * qstride + d0 * 2 : kOut,
+                                                              0, kNonTemporal);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+                const int d0 = 16 * t + 8 * hg;
+                qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, d0 < DR ? qi * qstride + d0 * 2 : kOut,
+                                                              0, 0);
+            }
         }
     }
 
@@ -533,19 +560,27 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         }
     };
 
+    // First key of the jt-th tile visited: tiles in order, or last first
+    // when this workgroup sweeps backwards (dense, no causal mask: every
+    // tile is visited, and the softmax does not depend on the order).
+    const bool rev = !PAGED && ti.rev;
+    auto tkey = [&](int jt) __attribute__((always_inline)) {
+        return (rev ? ntiles - 1 - jt : jt) * kBc;
+    };
+
     // Prologue: K(0), V(0), K(1) resident; scores of tile 0.
     if (ntiles > 0) {
-        issue_k(0, 0);
-        issue_v(0, 0);
+        issue_k(tkey(0), 0);
+        issue_v(tkey(0), 0);
     }
-    if (ntiles > 1) issue_k(kBc, 1);
-    if (ntiles > 0) load_bias(0);
+    if (ntiles > 1) issue_k(tkey(1), 1);
+    if (ntiles > 0) load_bias(tkey(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 sA[2], sB[2];
     if (wave_tiles > 0) {
         scores(smem, sA);
-        mask_tile(0, sA, tile_validity(0));
+        mask_tile(tkey(0), sA, tile_validity(tkey(0)));
     }
     __syncthreads();  // K stage 0 is refilled with K(2) by the first step
 
@@ -558,10 +593,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     auto step = [&](int jt, const int cur, f32x16 (&scur)[2], f32x16 (&snext)[2]) __attribute__((always_inline)) {
         // Tile jt+1's validity (written when its K was issued, a barrier ago);
         // K(jt+2)'s goes to the other slot.
-        const int vnext = tile_validity((jt + 1) * kBc);
-        if (jt + 2 < ntiles) issue_k((jt + 2) * kBc, cur);
-        if (jt + 1 < ntiles) issue_v((jt + 1) * kBc, cur ^ 1);
-        if (BIAS && jt + 1 < wave_tiles) load_bias((jt + 1) * kBc);
+        const int vnext = tile_validity(tkey(jt + 1));
+        if (jt + 2 < ntiles) issue_k(tkey(jt + 2), cur);
+        if (jt + 1 < ntiles) issue_v(tkey(jt + 1), cur ^ 1);
+        if (BIAS && jt + 1 < wave_tiles) load_bias(tkey(jt + 1));
         if (jt < wave_tiles) {
             uint32_t pk[2][8];
             if (jt + 1 < wave_tiles) scores(smem + (cur ^ 1) * L::TILE, snext);
@@ -576,7 +611,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
             }
             l_run += ps;
             accumulate(smem + VBASE + cur * LV::TILE, pk);
-            if (jt + 1 < wave_tiles) mask_tile((jt + 1) * kBc, snext, vnext);
+            if (jt + 1 < wave_tiles) mask_tile(tkey(jt + 1), snext, vnext);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA landed
         __syncthreads();
@@ -596,7 +631,34 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     if (!PAGED && a.lse && hg == 0 && qi < nrows && dv0 == 0)
         a.lse[((int64_t)ti.b * a.Hq + ti.h) * a.Sq + qi] =
             m_run == -INFINITY ? -INFINITY : m_run * a.scale + __logf(lt);
-    if (qi < nrows) {
+    if (stream_q_o) {
+        // The wave's 32 output rows go through LDS (free: every wave has passed
+        // the last tile's barrier) and out as whole 16-byte runs, a row's DV
+        // dims by consecutive lanes, with non-temporal stores: whole lines,
+        // kept from displacing K/V rows in the L2.  16-byte chunk c of LDS
+        // row r sits at c ^ (r % CPR).
+        constexpr int CPR = DV / 8;  // 16-byte chunks per row
+        uint16_t* stage = smem + wave * 32 * DV;
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const u32x2 w = {pack2<T>(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
+                                 pack2<T>(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
+                const int pc = (4 * db + r4) ^ (l32 % CPR);
+                *reinterpret_cast<u32x2*>(stage + l32 * DV + 8 * pc + 4 * hg) = w;
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own rows are in LDS
+#pragma unroll
+        for (int it = 0; it < 32 * CPR / 64; ++it) {
+            const int idx = 64 * it + lane;
+            const int row = idx / CPR, cc = idx % CPR;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * DV + 8 * (cc ^ (row % CPR)));
+            if (qw + row < nrows && 8 * cc < DRV)  // 8 dims of the slice, all < DRV or none
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(op + (int64_t)(qw + row) * (qstride / 2) + dv0 + 8 * cc));
+        }
+    } else if (qi < nrows) {
         uint16_t* orow = op + (int64_t)qi * (qstride / 2) + dv0;
 #pragma unroll
         for (int db = 0; db < DV / 32; ++db)
@@ -775,6 +837,27 @@ inline dim3 forward_grid(const ForwardArgs& a) {
     return dim3((unsigned)(nqb * a.B * a.Hq), a.D > 128 ? 2u : 1u);  // y: output slice of 128 dims
 }
 
+// Workgroups of this kernel one XCD holds at once (resident per CU times
+// the CUs of one of the 8 XCDs); 0 when the runtime cannot say.  Looked up
+// once per kernel (the instantiations share one pointer type, so the cache
+// is keyed by address).
+template <class Kernel>
+int xcd_resident(Kernel kernel, int threads) {
+    static std::mutex mu;
+    static std::vector<std::pair<const void*, int>> cache;
+    const void* key = reinterpret_cast<const void*>(kernel);
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+        if (e.first == key) return e.second;
+    int dev = 0, cus = 0, per_cu = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) == hipSuccess)
+        n = per_cu * (cus / 8);
+    cache.emplace_back(key, n);
+    return n;
+}
+
 // Head dims that are multiples of 8 run on the 64-, 128- or 256-wide kernel
 // (the general-width instantiation unless D is exactly 64, 128 or 256); above
 // 128 the output is computed in two 128-dim slices.
@@ -782,24 +865,23 @@ template <bool PAGED, class T, bool BIAS = false>
 hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
     if (a.D % 8 != 0 || a.D < 8 || a.D > 256) return hipErrorInvalidValue;
     const dim3 g = forward_grid(a), t(kThreads);
+    auto go = [&](auto kernel) {
+        ForwardArgs b = a;
+        b.sweep_group = (!PAGED && !a.causal) ? xcd_resident(kernel, kThreads) : 0;
+        hipLaunchKernelGGL(kernel, g, t, 0, s, b, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
+    };
     if (a.D == 64)
-        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS>), g, t, 0, s, a, p, p.block_tables,
-                           p.seq_lens, p.cu_seqlens_q);
+        go(forward_bf16_kernel<64, PAGED, T, BIAS>);
     else if (a.D == 128)
-        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS>), g, t, 0, s, a, p, p.block_tables,
-                           p.seq_lens, p.cu_seqlens_q);
+        go(forward_bf16_kernel<128, PAGED, T, BIAS>);
     else if (a.D == 256)
-        hipLaunchKernelGGL((forward_bf16_kernel<256, PAGED, T, BIAS, false, 128>), g, t, 0, s, a, p,
-                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        go(forward_bf16_kernel<256, PAGED, T, BIAS, false, 128>);
     else if (a.D < 64)
-        hipLaunchKernelGGL((forward_bf16_kernel<64, PAGED, T, BIAS, true>), g, t, 0, s, a, p,
-                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        go(forward_bf16_kernel<64, PAGED, T, BIAS, true>);
     else if (a.D < 128)
-        hipLaunchKernelGGL((forward_bf16_kernel<128, PAGED, T, BIAS, true>), g, t, 0, s, a, p,
-                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        go(forward_bf16_kernel<128, PAGED, T, BIAS, true>);
     else
-        hipLaunchKernelGGL((forward_bf16_kernel<256, PAGED, T, BIAS, true, 128>), g, t, 0, s, a, p,
-                           p.block_tables, p.seq_lens, p.cu_seqlens_q);
+        go(forward_bf16_kernel<256, PAGED, T, BIAS, true, 128>);
     return hipGetLastError();
 }
 

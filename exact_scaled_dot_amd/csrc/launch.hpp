@@ -22,6 +22,11 @@ struct ForwardArgs {
     // bias[b * bias_sb + h * bias_sh + i * Sk + j], input dtype.
     const void* bias = nullptr;
     int64_t bias_sb = 0, bias_sh = 0;
+    // Workgroups one XCD holds at once (set at launch from the kernel's
+    // occupancy; 0: unknown).  Dense non-causal launches sweep the keys
+    // backwards in every other such group of an XCD's run, so a group starts
+    // on the keys the previous one left in the XCD's L2.
+    int sweep_group = 0;
 };
 
 // Attention backward (16-bit inputs): dq [B,Hq,Sq,D], dk / dv [B,Hkv,Sk,D].

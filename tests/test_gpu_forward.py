@@ -8,7 +8,8 @@ import torch
 
 import exact_scaled_dot_amd as sd
 import oracle as O
-from exact_scaled_dot_amd.workloads import WORKLOADS, draw_key_lens, draw_qkv, make_inputs
+from exact_scaled_dot_amd.workloads import (WORKLOADS, draw_bias, draw_key_lens, draw_qkv,
+                                             make_inputs)
 from parity import compare, oracle_forward_whole, to64
 
 pytestmark = pytest.mark.gpu
@@ -166,6 +167,49 @@ def test_full_size_workload_whole_output(name):
     ref = oracle_forward_whole(O, inp["q"], inp["k"], inp["v"], w.scale, k_orc, lens)
     max_abs, rel = compare(to64(out), ref, w.dtype, name)
     print("%s whole output: max-abs %.3e rel-L2 %.3e" % (name, max_abs, rel))
+
+
+# ------------------------------------------------------------ many workgroups, no causal mask
+# Without a causal mask each XCD sweeps the keys backwards in every other
+# group of the workgroups it holds at once (64 per XCD at D=128, so launches
+# of more than 512 workgroups), and Q and O are streamed.  These launches run
+# 1056 workgroups (33 query blocks x 32 heads): every XCD runs forward and
+# backward groups, over a ragged last query block and ragged key limits.
+
+@pytest.mark.parametrize("D,dtype", [(64, torch.bfloat16), (128, torch.bfloat16),
+                                     (128, torch.float16), (200, torch.bfloat16),
+                                     (256, torch.bfloat16)])
+@pytest.mark.parametrize("padded", [False, True])
+def test_many_workgroups_non_causal(D, dtype, padded):
+    B, Hq, Hkv, Sq, Sk = 2, 16, 4, 4100, 777
+    q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, dtype, 700 + D + padded, DEV)
+    lens = torch.tensor([777, 300], dtype=torch.int32, device=DEV) if padded else None
+    kind = sd.MASK_KEY_PADDING if padded else sd.MASK_NONE
+    scale = 1 / math.sqrt(D)
+    out = torch.full_like(q, float("nan"))
+    sd.sdpa_forward(q, k, v, scale, kind, lens, out=out)
+    torch.cuda.synchronize()
+    ref = oracle_forward_whole(O, q, k, v, scale, kind, None if lens is None else lens.cpu().numpy())
+    compare(to64(out), ref, dtype, "non-causal D=%d %s padded=%d" % (D, dtype, padded))
+
+
+def test_many_workgroups_non_causal_bias():
+    B, Hq, Hkv, Sq, Sk, D = 2, 16, 16, 4100, 336, 128
+    q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, torch.bfloat16, 777, DEV)
+    bias = draw_bias((B, 1, Sq, Sk), torch.bfloat16, 778, DEV)
+    lens = torch.tensor([336, 129], dtype=torch.int32, device=DEV)
+    out = sd.sdpa_forward_bias(q, k, v, bias, 0.09, sd.MASK_KEY_PADDING, lens)
+    torch.cuda.synchronize()
+    ref = oracle_forward_whole(O, q, k, v, 0.09, O.MASK_KEY_PADDING, lens.cpu().numpy(), bias=bias)
+    compare(to64(out), ref, torch.bfloat16, "non-causal bias")
+
+
+def test_many_workgroups_non_causal_deterministic():
+    q, k, v = draw_qkv(2, 16, 4, 4100, 777, 128, torch.bfloat16, 779, DEV)
+    a = sd.sdpa_forward(q, k, v, 0.1)
+    b = sd.sdpa_forward(q, k, v, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 def _hot_key_inputs(B, Hq, Sq, Sk, D, dtype, seed):
