@@ -30,6 +30,10 @@ reordered:
 * lse        lse_i = m_i + ln(sum_j exp(z_ij - m_i))  (the log of the softmax
   denominator, used by the split-KV partials); -inf for a row with no
   visible key (the log of an empty sum).
+* widths     q and k share the key width D, v has its own width Dv and the
+  output has Dv columns (ruDNN user guide section 9: K is [.., Hkv, D], V is
+  [.., Hkv, Dv], the output [.., Hq, Dv], with D and Dv each in 1..=1024);
+  every function below takes v of any width Dv >= 1.
 * head map   query head h reads K/V head floor(h / (Hq / Hkv)) (grouped K/V,
   ruDNN user guide section 9 "ページ化アテンションと MLA": Hq must be divisible
   by Hkv; contiguous groups is the reading taken).
@@ -77,15 +81,17 @@ MASK_KEY_PADDING = 2
 
 
 def _check_shapes(q, k, v):
+    """Sizes of q [B,Hq,Sq,D], k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv]: (B, Hq, Hkv,
+    Sk, D, Dv)."""
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D (batch, head, seq, headDim)")
     B, Hq, _, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
-    if Bk != B or Dk != D or v.shape != k.shape:
+    if Bk != B or Dk != D or v.shape[:3] != k.shape[:3] or v.shape[3] < 1:
         raise ValueError("inconsistent q/k/v shapes %s %s %s" % (q.shape, k.shape, v.shape))
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
-    return B, Hq, Hkv, Sk, D
+    return B, Hq, Hkv, Sk, D, v.shape[3]
 
 
 def visible_rows(mask_kind, rows, Sk, key_len):
@@ -162,7 +168,7 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
     Returns o (fp64), plus lse [B,Hq,Sq] and/or probs [B,Hq,Sq,Sk] on request.
     """
     q = np.asarray(q)
-    B, Hq, Hkv, Sk, D = _check_shapes(q, np.asarray(k), np.asarray(v))
+    B, Hq, Hkv, Sk, D, Dv = _check_shapes(q, np.asarray(k), np.asarray(v))
     Sq = q.shape[2]
     if mask_kind & MASK_CAUSAL and Sq != Sk:
         raise ValueError("causal mask needs Sq == Sk")
@@ -170,7 +176,7 @@ def sdpa_forward(q, k, v, scale, mask_kind=MASK_NONE, key_lens=None,
         raise ValueError("key_lens is given exactly when the key-padding bit is set")
     bias = _check_bias(bias, B, Hq, Sq, Sk)
     G = Hq // Hkv
-    o = np.empty((B, Hq, Sq, D), dtype=np.float64)
+    o = np.empty((B, Hq, Sq, Dv), dtype=np.float64)
     lse = np.empty((B, Hq, Sq), dtype=np.float64)
     probs = np.empty((B, Hq, Sq, Sk), dtype=np.float64) if return_probs else None
     rows = np.arange(Sq)
@@ -197,17 +203,17 @@ def sdpa_forward_rows(q, k, v, scale, mask_kind, key_lens, index, bias=None):
     (grouped by head) so that it scales to full-size workloads.  q, k, v (and
     bias, [B or 1, Hq or 1, Sq, Sk]) may be any array-likes indexable as
     [b, h] (only the needed heads are read).
-    Returns (o [n, D], lse [n]) in the order of index.
+    Returns (o [n, Dv], lse [n]) in the order of index (v is [B, Hkv, Sk, Dv]).
     """
     B, Hq, _ = q.shape[0], q.shape[1], q.shape[2]
-    Hkv, Sk, D = k.shape[1], k.shape[2], k.shape[3]
+    Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
     if mask_kind & MASK_CAUSAL and q.shape[2] != Sk:
         raise ValueError("causal mask needs Sq == Sk")
     G = Hq // Hkv
     index = np.asarray(index, dtype=np.int64).reshape(-1, 3)
-    o = np.empty((index.shape[0], D), dtype=np.float64)
+    o = np.empty((index.shape[0], Dv), dtype=np.float64)
     lse = np.empty(index.shape[0], dtype=np.float64)
     heads = {}
     for n, (b, h, i) in enumerate(index):
@@ -249,9 +255,9 @@ def decode_split_partials(q, k, v, scale, key_lens, num_splits):
     no visible key contributes o = 0 and lse = -inf (an empty softmax
     denominator).  Returns (o_part [B,Hq,n,D], lse_part [B,Hq,n]).
     """
-    B, Hq, Hkv, Sk, D = _check_shapes(q, k, v)
+    B, Hq, Hkv, Sk, D, Dv = _check_shapes(q, k, v)
     G = Hq // Hkv
-    o_part = np.zeros((B, Hq, num_splits, D), dtype=np.float64)
+    o_part = np.zeros((B, Hq, num_splits, Dv), dtype=np.float64)
     lse_part = np.full((B, Hq, num_splits), -np.inf, dtype=np.float64)
     for b in range(B):
         vis_all = visible_rows(MASK_KEY_PADDING if key_lens is not None else MASK_NONE,
@@ -288,7 +294,7 @@ def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None, bias
                   return_dbias=False):
     """dQ, dK, dV (and the bias gradient) of L with dL/dO = dout, by the definition (fp64).
 
-    q, dout [B,Hq,Sq,D]; k, v [B,Hkv,Sk,D]; bias None or [B or 1, Hq or 1,
+    q [B,Hq,Sq,D], dout [B,Hq,Sq,Dv]; k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv]; bias None or [B or 1, Hq or 1,
     Sq, Sk], added to the scaled scores as in sdpa_forward.  Per (b, h): P is
     the row softmax of the masked biased scaled scores (hidden keys get
     exactly 0), O = P V, then dV = P^T dO, dP = dO V^T, dS = P * (dP -
@@ -303,10 +309,12 @@ def sdpa_backward(q, k, v, dout, scale, mask_kind=MASK_NONE, key_lens=None, bias
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
-    B, Hq, Hkv, Sk, D = _check_shapes(q, k, v)
+    B, Hq, Hkv, Sk, D, Dv = _check_shapes(q, k, v)
     Sq = q.shape[2]
     if mask_kind & MASK_CAUSAL and Sq != Sk:
         raise ValueError("causal mask needs Sq == Sk")
+    if dout.shape != (B, Hq, Sq, Dv):
+        raise ValueError("dout must be [B, Hq, Sq, Dv]")
     bias = _check_bias(bias, B, Hq, Sq, Sk)
     G = Hq // Hkv
     dq = np.zeros_like(q)
@@ -421,23 +429,26 @@ def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq, quer
                     scale, causal):
     """Packed paged attention (ruDNN user guide section 9).
 
-    q [queries, Hq, D]; k_cache, v_cache [pages, page_size, Hkv, D];
+    q [queries, Hq, D]; k_cache [pages, page_size, Hkv, D]; v_cache [pages,
+    page_size, Hkv, Dv];
     block_tables [num_seqs, max_pages_per_seq]; seq_lens [num_seqs];
     query_seq, query_pos [queries].  Query t (sequence s = query_seq[t],
     position p = query_pos[t]) attends to keys j < seq_lens[s] of its own
     sequence, and with causal only to j <= p.  Query head h reads K/V head
-    h // (Hq / Hkv).  Returns o [queries, Hq, D] in fp64 (NaN rows where no key
+    h // (Hq / Hkv).  Returns o [queries, Hq, Dv] in fp64 (NaN rows where no key
     is visible).
     """
     q = np.asarray(q)
     nq, Hq, D = q.shape
     pages, page_size, Hkv, Dk = np.asarray(k_cache).shape
-    if Dk != D or np.asarray(v_cache).shape != np.asarray(k_cache).shape:
+    vshape = np.asarray(v_cache).shape
+    if Dk != D or len(vshape) != 4 or vshape[:3] != (pages, page_size, Hkv) or vshape[3] < 1:
         raise ValueError("inconsistent q / cache shapes")
+    Dv = vshape[3]
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
-    o = np.empty((nq, Hq, D), dtype=np.float64)
+    o = np.empty((nq, Hq, Dv), dtype=np.float64)
     for t in range(nq):
         s_id, pos = int(query_seq[t]), int(query_pos[t])
         length = int(seq_lens[s_id])

@@ -298,8 +298,8 @@ def test_merge_closed_form():
 def brute_force(q, k, v, scale, mask, lens):
     """Scalar loops with exactly rounded sums (math.fsum), tiny shapes only."""
     B, Hq, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
-    out = np.zeros(q.shape)
+    Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
+    out = np.zeros((B, Hq, Sq, Dv))
     for b, h, i in itertools.product(range(B), range(Hq), range(Sq)):
         g = h * Hkv // Hq
         keys = [j for j in range(Sk)
@@ -309,7 +309,7 @@ def brute_force(q, k, v, scale, mask, lens):
         mx = max(s.values())
         e = {j: math.exp(s[j] - mx) for j in keys}
         den = math.fsum(e.values())
-        for d in range(D):
+        for d in range(Dv):
             out[b, h, i, d] = math.fsum(e[j] * v[b, g, j, d] for j in keys) / den
     return out
 
@@ -322,6 +322,100 @@ def test_brute_force_tiny(mask):
         lens = np.array([max(1, S // 2), S]) if mask & O.MASK_KEY_PADDING else None
         o = O.sdpa_forward(q, k, v, 0.75, mask, lens)
         np.testing.assert_allclose(o, brute_force(q, k, v, 0.75, mask, lens), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------- value width Dv different from D
+
+@pytest.mark.parametrize("mask", [O.MASK_NONE, O.MASK_CAUSAL, O.MASK_KEY_PADDING,
+                                  O.MASK_CAUSAL | O.MASK_KEY_PADDING])
+def test_brute_force_value_width(mask):
+    # V of its own width: scores over D, output over Dv, by scalar loops
+    for S, D, Dv, Hq, Hkv in [(4, 3, 5, 2, 1), (6, 4, 1, 4, 2), (5, 2, 7, 3, 3), (3, 6, 2, 2, 2)]:
+        q, k, v = rand(2, Hq, S, D, scale=2), rand(2, Hkv, S, D, scale=2), rand(2, Hkv, S, Dv)
+        lens = np.array([max(1, S // 2), S]) if mask & O.MASK_KEY_PADDING else None
+        o = O.sdpa_forward(q, k, v, 0.6, mask, lens)
+        assert o.shape == (2, Hq, S, Dv)
+        np.testing.assert_allclose(o, brute_force(q, k, v, 0.6, mask, lens), rtol=0, atol=1e-13)
+
+
+def test_value_identity_gives_the_weights():
+    # V = the identity over keys (Dv = Sk): each output row is the row of
+    # softmax weights itself, written out here from the definition
+    B, H, S, D = 1, 2, 6, 3
+    q, k = rand(B, H, S, D, scale=1.5), rand(B, H, S, D, scale=1.5)
+    v = np.broadcast_to(np.eye(S), (B, H, S, S)).copy()
+    o = O.sdpa_forward(q, k, v, 0.8, O.MASK_CAUSAL)
+    for h, i in itertools.product(range(H), range(S)):
+        s = [0.8 * float(np.dot(q[0, h, i], k[0, h, j])) for j in range(i + 1)]
+        e = [math.exp(x - max(s)) for x in s]
+        want = [x / math.fsum(e) for x in e] + [0.0] * (S - i - 1)
+        np.testing.assert_allclose(o[0, h, i], want, rtol=0, atol=1e-14)
+
+
+def test_value_width_rows_decode_and_split_merge():
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, S, D, Dv = 2, 4, 2, 9, 5, 3
+    q, k, v = (rng.standard_normal((B, Hq, S, D)), rng.standard_normal((B, Hkv, S, D)),
+               rng.standard_normal((B, Hkv, S, Dv)))
+    full = O.sdpa_forward(q, k, v, 0.5, O.MASK_CAUSAL)
+    idx = np.array([(0, 1, 0), (1, 3, 8), (1, 0, 4)])
+    rows, _ = O.sdpa_forward_rows(q, k, v, 0.5, O.MASK_CAUSAL, None, idx)
+    np.testing.assert_allclose(rows, full[idx[:, 0], idx[:, 1], idx[:, 2]], rtol=0, atol=1e-13)
+    q1 = q[:, :, :1]
+    lens = np.array([9, 4])
+    dec = O.sdpa_decode(q1, k, v, 0.5, lens)
+    assert dec.shape == (B, Hq, 1, Dv)
+    np.testing.assert_allclose(dec, brute_force(q1, k, v, 0.5, O.MASK_KEY_PADDING, lens), rtol=0,
+                               atol=1e-13)
+    op, lp = O.decode_split_partials(q1, k, v, 0.5, lens, 4)
+    assert op.shape == (B, Hq, 4, Dv)
+    merged, _ = O.merge_partials(op, lp)
+    np.testing.assert_allclose(merged, dec[:, :, 0], rtol=0, atol=1e-13)
+
+
+def test_paged_value_width():
+    rng = np.random.default_rng(23)
+    lens = [7, 3]
+    nseq, Hq, Hkv, D, Dv, S = 2, 4, 2, 3, 6, 7
+    q = rng.standard_normal((nseq, Hq, S, D))
+    k = rng.standard_normal((nseq, Hkv, S, D))
+    v = rng.standard_normal((nseq, Hkv, S, Dv))
+    kc, vc, tables = make_paged(k, v, lens, 2, 1, rng)
+    qs = np.array([s for s in range(nseq) for _ in range(lens[s])])
+    qp = np.array([i for s in range(nseq) for i in range(lens[s])])
+    qq = np.stack([q[s, :, i] for s, i in zip(qs, qp)])
+    got = O.paged_attention(qq, kc, vc, tables, lens, qs, qp, 0.9, True)
+    assert got.shape == (len(qs), Hq, Dv)
+    for s in range(nseq):
+        n = lens[s]
+        ref = brute_force(q[s:s + 1, :, :n], k[s:s + 1, :, :n], v[s:s + 1, :, :n], 0.9,
+                          O.MASK_CAUSAL, None)[0]
+        np.testing.assert_allclose(got[qs == s], ref.transpose(1, 0, 2), rtol=0, atol=1e-13)
+
+
+def test_backward_value_width_matches_finite_differences():
+    rng = np.random.default_rng(29)
+    B, Hq, Hkv, S, D, Dv = 1, 2, 1, 4, 3, 5
+    q, k, v = (rng.standard_normal((B, Hq, S, D)), rng.standard_normal((B, Hkv, S, D)),
+               rng.standard_normal((B, Hkv, S, Dv)))
+    g = rng.standard_normal((B, Hq, S, Dv))
+    dq, dk, dv = O.sdpa_backward(q, k, v, g, 0.8, O.MASK_CAUSAL)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_loss(args_p["q"], args_p["k"], args_p["v"], g, 0.8, O.MASK_CAUSAL, None)
+                        - _loss(args_m["q"], args_m["k"], args_m["v"], g, 0.8, O.MASK_CAUSAL, None)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=name)
+    with pytest.raises(ValueError):
+        O.sdpa_backward(q, k, v, rng.standard_normal((B, Hq, S, D)), 0.8)
 
 
 def test_printed_kernel_without_max_subtraction():
@@ -375,12 +469,13 @@ def make_paged(k, v, lens, page_size, extra_pages, rng):
     filled with large garbage so that reading one by mistake shows.
     """
     nseq, Hkv, S, D = k.shape
+    Dv = v.shape[3]
     need = [-(-int(n) // page_size) for n in lens]
     max_pages = max(need)
     pages = sum(need) + extra_pages
     perm = rng.permutation(pages)
     k_cache = rng.standard_normal((pages, page_size, Hkv, D)) * 50.0
-    v_cache = rng.standard_normal((pages, page_size, Hkv, D)) * 50.0
+    v_cache = rng.standard_normal((pages, page_size, Hkv, Dv)) * 50.0
     tables = np.full((nseq, max_pages), -1, dtype=np.int64)
     nxt = 0
     for s in range(nseq):
