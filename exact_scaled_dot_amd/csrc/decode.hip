@@ -166,19 +166,29 @@ __device__ __forceinline__ Item item_geo(const DecodeArgs& a, const PagedArgs& p
 // contraction slots it feeds to the P.V product.  The kernel has no
 // workgroup barrier: every wave runs its own items start to end.
 //
-// PAGED: K and V come from a page cache [pages, page_size, Hkv, D]; a step's
+// DV: on-chip width of V and of the partial output (the value head dim Dv,
+// which may differ from D: ruDNN user guide section 9); K tiles are D wide,
+// V tiles DV wide, each with its own swizzle and DMA count.
+//
+// PAGED: K and V come from page caches [pages, page_size, Hkv, D] and
+// [.., Dv]; a step's
 // 16 keys lie in one page (page_size and the split length are multiples of
 // 16), found through the sequence's page table when the step enters a new
 // page.  A table entry outside [0, pages) is never dereferenced: its keys
 // load as zeros and are masked out.
-template <int D, bool PAGED, class T, bool GEN = false>
+template <int D, bool PAGED, class T, bool GEN = false, int DV = D>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     DecodeArgs a, PagedArgs p, const int32_t* __restrict__ key_lens,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ query_seq, const int32_t* __restrict__ query_pos, int items) {
-    using L = DecGeo<D>;
+    using L = DecGeo<D>;    // K
+    using LV = DecGeo<DV>;  // V
+    constexpr int STAGE = L::TILE + LV::TILE;          // K tile, then V tile
+    constexpr int NS = kRingBytes / (2 * STAGE);       // ring stages per wave
+    constexpr int OPS = L::DMA + LV::DMA;              // vector memory ops per step
+    static_assert(NS >= 2, "ring depth");
     const Meta meta{key_lens, tables, seq_lens, query_seq, query_pos};
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * L::NS * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * NS * STAGE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,22 +215,31 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     // are DR wide in HBM and D wide on chip; chunks at or past DR read as
     // zeros (offsets outside the buffer) and are never stored.
     const int DR = GEN ? a.D : D;
+    const int DVR = GEN ? a.Dv : DV;  // value head dim in memory
     constexpr uint32_t kOut = 0x80000000u;  // past any num_records (<= INT_MAX)
     const uint32_t head_bytes = (uint32_t)a.Sk * DR * 2;
+    const uint32_t vhead_bytes = (uint32_t)a.Sk * DVR * 2;
     // Bytes between consecutive keys of one K/V head: DR*2 in a dense head,
-    // Hkv*DR*2 inside a page.
+    // Hkv*DR*2 inside a page (DVR for V).
     const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * DR * 2 : (uint32_t)DR * 2;
+    const uint32_t vrow_bytes = PAGED ? (uint32_t)a.Hkv * DVR * 2 : (uint32_t)DVR * 2;
     const uint32_t page_bytes = PAGED ? (uint32_t)p.page_size * row_bytes : 0u;
+    const uint32_t vpage_bytes = PAGED ? (uint32_t)p.page_size * vrow_bytes : 0u;
 
     // Lane-constant DMA offsets (bytes from the step's first key) and LDS read
     // offsets (elements from the stage start).
-    uint32_t koff[L::DMA], voff[L::DMA];
+    uint32_t koff[L::DMA], voff[LV::DMA];
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int q = 64 * i + lane, row = q / L::CPR, pc = q % L::CPR;
-        const int ck = pc ^ L::fk(row), cv = pc ^ L::fv(row);  // logical chunks
+        const int ck = pc ^ L::fk(row);  // logical chunk
         koff[i] = 8 * ck < DR ? row * row_bytes + ck * 16 : kOut;
-        voff[i] = 8 * cv < DR ? row * row_bytes + cv * 16 : kOut;
+    }
+#pragma unroll
+    for (int i = 0; i < LV::DMA; ++i) {
+        const int q = 64 * i + lane, row = q / LV::CPR, pc = q % LV::CPR;
+        const int cv = pc ^ LV::fv(row);  // logical chunk
+        voff[i] = 8 * cv < DVR ? row * vrow_bytes + cv * 16 : kOut;
     }
     // K fragment of kstep t: key row col, dims (D/4)*grp + 8t .. +7 (contraction
     // slot (t, grp, e) <-> dim (D/4)*grp + 8t + e, matching qb below).
@@ -231,14 +250,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     // Transposed V read: lane j of group grp points at row 4*grp + j/4, dims
     // 16*dt + 4*(j%4); it receives V[4*grp .. 4*grp+3][16*dt + col].
     const int tr_row = 4 * grp + (col >> 2);
-    int vrd[D / 16];
+    int vrd[DV / 16];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < DV / 16; ++dt) {
         const int e = 16 * dt + 4 * (col & 3);
-        vrd[dt] = L::TILE + tr_row * D + (((e >> 3) ^ L::fv(tr_row)) * 8) + (e & 7);
+        vrd[dt] = L::TILE + tr_row * DV + (((e >> 3) ^ LV::fv(tr_row)) * 8) + (e & 7);
     }
 
-    uint16_t* ring = smem + wave * L::NS * L::STAGE;
+    uint16_t* ring = smem + wave * NS * STAGE;
 
     // Issue cursor: the next step to load, running NS-1 steps ahead of compute
     // across item boundaries.  Empty items (no visible key) are skipped.
@@ -258,9 +277,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 i_gk = g.gk;
                 i_page = -1;
                 if (!PAGED) {
-                    const int64_t kvh = ((int64_t)g.b * a.Hkv + g.gk) * a.Sk * DR;
-                    ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + kvh, head_bytes);
-                    ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kvh, head_bytes);
+                    const int64_t kvh = ((int64_t)g.b * a.Hkv + g.gk) * a.Sk;
+                    ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + kvh * DR, head_bytes);
+                    ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kvh * DVR, vhead_bytes);
                 }
                 return;
             }
@@ -268,17 +287,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     };
     int issued = 0;
     auto issue_next = [&]() {
-        uint16_t* st = ring + (issued % L::NS) * L::STAGE;
-        uint32_t base;
+        uint16_t* st = ring + (issued % NS) * STAGE;
+        uint32_t base, vbase;
         if (PAGED) {
             const int lp = i_k0 / p.page_size;
             if (lp != i_page) {  // entering a new page: look it up
                 i_page = lp;
                 const int pg = lp < p.max_pages ? meta.tables[(int64_t)i_seq * p.max_pages + lp] : -1;
                 const bool ok = pg >= 0 && pg < p.pages;
-                const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * DR : 0;
-                ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + off, ok ? page_bytes : 0u);
-                ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + off, ok ? page_bytes : 0u);
+                const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv : 0;
+                ikrs = make_rsrc(static_cast<const uint16_t*>(a.k) + off * DR, ok ? page_bytes : 0u);
+                ivrs = make_rsrc(static_cast<const uint16_t*>(a.v) + off * DVR, ok ? vpage_bytes : 0u);
                 valid_bits = ok ? (valid_bits | (1u << (issued & 31))) : (valid_bits & ~(1u << (issued & 31)));
             } else {
                 // same page as the previous step: same validity
@@ -286,19 +305,22 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                 valid_bits = (valid_bits & ~(1u << (issued & 31))) | (prev << (issued & 31));
             }
             base = ((uint32_t)(i_k0 % p.page_size) * a.Hkv + i_gk) * DR * 2;
+            vbase = ((uint32_t)(i_k0 % p.page_size) * a.Hkv + i_gk) * DVR * 2;
         } else {
             base = (uint32_t)i_k0 * DR * 2;
+            vbase = (uint32_t)i_k0 * DVR * 2;
         }
         // The buffer range check covers the per-lane offset but not the scalar
         // one.  Dense: the step offset goes into the per-lane offset, so rows
         // past Sk read zeros.  Paged: a step never leaves its page (and an
         // invalid page has no records at all), so it can ride in the scalar
         // offset.
-        const uint32_t vb = PAGED ? 0u : base, sb = PAGED ? base : 0u;
+        const uint32_t kb = PAGED ? 0u : base, ksb = PAGED ? base : 0u;
+        const uint32_t vb = PAGED ? 0u : vbase, vsb = PAGED ? vbase : 0u;
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, koff[i] + vb, sb);
+        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, koff[i] + kb, ksb);
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, voff[i] + vb, sb);
+        for (int i = 0; i < LV::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, voff[i] + vb, vsb);
         ++issued;
         if (++i_st < i_nst)
             i_k0 += kStep;
@@ -306,7 +328,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
             seek(i_it + kDecWaves);
     };
     seek(it0);
-    for (int j = 0; j < L::NS - 1 && i_it < it1; ++j) issue_next();
+    for (int j = 0; j < NS - 1 && i_it < it1; ++j) issue_next();
 
     u32x4 qb[L::KSTEPS];
     int q_head = -1;
@@ -316,10 +338,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         const int64_t prow0 = ((int64_t)g.b * a.Hq + g.h0) * a.splits + g.split;
         if (g.nst == 0) {  // no visible key in this split
             if (col < g.nh) {
-                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * DR + 4 * grp;
+                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * DVR + 4 * grp;
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-                    if (16 * dt + 4 * grp < DR)
+                for (int dt = 0; dt < DV / 16; ++dt)
+                    if (16 * dt + 4 * grp < DVR)
                         *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (grp == 0) a.lse_part[prow0 + (int64_t)col * a.splits] = -INFINITY;
             }
@@ -344,33 +366,33 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
             q_head = head;
         }
 
-        f32x4 oacc[D / 16];
+        f32x4 oacc[DV / 16];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m_run = -INFINITY, l_run = 0.f;
 
         for (int st = 0; st < g.nst; ++st, ++done) {
             if (i_it < it1) issue_next();
             // Every load but those of the steps issued after this one has landed.
             const int ahead = issued - done - 1;
-            if (L::NS == 8 && ahead >= 7)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(7 * L::OPS) : "memory");
-            else if (L::NS == 8 && ahead == 6)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * L::OPS) : "memory");
-            else if (L::NS == 8 && ahead == 5)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * L::OPS) : "memory");
-            else if (L::NS == 8 && ahead == 4)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * L::OPS) : "memory");
-            else if (ahead >= 3)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L::OPS) : "memory");
-            else if (ahead == 2)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L::OPS) : "memory");
+            if (NS == 8 && ahead >= 7)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(7 * OPS) : "memory");
+            else if (NS == 8 && ahead == 6)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * OPS) : "memory");
+            else if (NS == 8 && ahead == 5)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * OPS) : "memory");
+            else if (NS == 8 && ahead == 4)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * OPS) : "memory");
+            else if (NS >= 4 && ahead >= 3)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * OPS) : "memory");
+            else if (ahead >= 2)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
             else if (ahead == 1)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::OPS) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-            const uint16_t* stg = ring + (done % L::NS) * L::STAGE;
+            const uint16_t* stg = ring + (done % NS) * STAGE;
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < L::KSTEPS; ++t)
@@ -405,17 +427,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                     m_run = m_new;
                     l_run *= alpha;
 #pragma unroll
-                    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+                    for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] *= alpha;
                 }
                 ps = weights();
             }
             l_run += ps;
             const u32x2 pb = u32x2{p01, p23};
-            u32x2 vf[D / 16];
+            u32x2 vf[DV / 16];
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) vf[dt] = lds_read_tr(stg + vrd[dt]);
+            for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = lds_read_tr(stg + vrd[dt]);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
+            for (int dt = 0; dt < DV / 16; ++dt)
                 oacc[dt] = mfma_16x16x16<T>(vf[dt], pb, oacc[dt]);
         }
 
@@ -424,17 +446,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         l_run += __shfl_xor(l_run, 32);
         if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
-            float* op = a.o_part + prow * DR + 4 * grp;
+            float* op = a.o_part + prow * DVR + 4 * grp;
             if (m_run == -INFINITY) {  // every key masked (paged: invalid pages only)
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-                    if (16 * dt + 4 * grp < DR)
+                for (int dt = 0; dt < DV / 16; ++dt)
+                    if (16 * dt + 4 * grp < DVR)
                         *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (grp == 0) a.lse_part[prow] = -INFINITY;
             } else {
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
-                    if (16 * dt + 4 * grp < DR)
+                for (int dt = 0; dt < DV / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
+                    if (16 * dt + 4 * grp < DVR)
                         *reinterpret_cast<f32x4*>(op + 16 * dt) =
                             f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
                                   oacc[dt][3] / l_run};
@@ -450,7 +472,7 @@ __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     constexpr int RPB = 256 / TPR;   // rows (batch, query head) per block
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int d4 = threadIdx.x % TPR;
-    const int DR = GEN ? a.D : D;  // head dim in memory (a multiple of 8, <= D)
+    const int DR = GEN ? a.Dv : D;  // value head dim in memory (a multiple of 8, <= D)
     if (row >= (int64_t)a.B * a.Hq || 4 * d4 >= DR) return;
     const float* lse = a.lse_part + row * a.splits;
     const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * DR) + d4;
@@ -489,6 +511,26 @@ hipError_t compute_units(int* n) {
     return hipSuccess;
 }
 
+// Split and merge for a value head dim Dv other than D (both multiples of 8
+// up to 256): general-width kernels on the padded widths DP (K) and VP (V).
+template <int DP, int VP, bool PAGED, class T>
+void launch_dv(const DecodeArgs& a, const PagedArgs& p, int wgs, int items, hipStream_t s) {
+    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * VP / 4 + 255) / 256));
+    hipLaunchKernelGGL((decode_split_bf16_kernel<DP, PAGED, T, true, VP>), dim3(wgs), dim3(kDecThreads), 0,
+                       s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos, items);
+    hipLaunchKernelGGL((decode_merge_bf16_kernel<VP, T, true>), mgrid, dim3(256), 0, s, a);
+}
+
+template <int DP, bool PAGED, class T>
+void launch_dv_v(const DecodeArgs& a, const PagedArgs& p, int wgs, int items, hipStream_t s) {
+    if (a.Dv <= 64)
+        launch_dv<DP, 64, PAGED, T>(a, p, wgs, items, s);
+    else if (a.Dv <= 128)
+        launch_dv<DP, 128, PAGED, T>(a, p, wgs, items, s);
+    else
+        launch_dv<DP, 256, PAGED, T>(a, p, wgs, items, s);
+}
+
 template <bool PAGED, class T>
 hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
     const int items = (int)decode_work_items(a.B, a.Hq, a.Hkv, a.splits);
@@ -498,6 +540,20 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    if (a.Dv != a.D) {
+        if constexpr (PAGED) {
+            if (a.D % 8 != 0 || a.Dv % 8 != 0 || a.D < 8 || a.Dv < 8 || a.D > 256 || a.Dv > 256)
+                return hipErrorInvalidValue;
+            if (a.D <= 64)
+                launch_dv_v<64, PAGED, T>(a, p, wgs, items, s);
+            else if (a.D <= 128)
+                launch_dv_v<128, PAGED, T>(a, p, wgs, items, s);
+            else
+                launch_dv_v<256, PAGED, T>(a, p, wgs, items, s);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;  // the dense decode has Dv = D
+    }
     if (a.D > 256 && a.D <= 1024 && a.D % 8 == 0) {
         // Wider heads: the head-dim-split kernel writes the same partials,
         // then the same merge (D/4 threads per row).

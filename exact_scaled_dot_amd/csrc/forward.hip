@@ -222,9 +222,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     // DR wide in HBM and D wide on chip; the 16-byte chunks at or past DR are
     // read as zeros (their offsets lie outside the buffer) and never stored.
     const int DR = GEN ? a.D : D;
-    // Output slice: dims dv0 .. dv0 + DRV - 1 of the DR in memory.
-    const int dv0 = DV < D ? DV * (int)blockIdx.y : 0;
-    const int DRV = DV < D ? min(DV, DR - dv0) : DR;
+    // Value head dim in memory: DVM (GEN: a.Dv, which may differ from D; else
+    // D).  Output slice: dims dv0 .. dv0 + DRV - 1 of the DVM (one slice of DV
+    // dims per blockIdx.y).
+    const int DVM = GEN ? a.Dv : DR;
+    const int dv0 = DV * (int)blockIdx.y;
+    const int DRV = min(DV, DVM - dv0);
     constexpr uint32_t kOut = 0x80000000u;  // past any num_records (<= INT_MAX)
     const uint16_t* kp;
     const uint16_t* vp;
@@ -232,6 +235,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     uint16_t* op;
     int nrows, qoff, kv_lim, kv_end;
     uint32_t qstride;  // bytes between consecutive query rows
+    uint32_t ostride;  // bytes between consecutive output rows
     if (PAGED) {
         // This workgroup's rows of sequence b's chunk (bounds clamped to the
         // packed rows so no store can leave out).
@@ -243,20 +247,22 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         qoff = kv_lim - nrows;  // absolute position of the chunk's first row
         kv_end = kv_lim;
         if (a.causal) kv_end = min(kv_end, qoff + ti.q0 + kBr);
-        const int64_t rb = ((int64_t)r0 * a.Hq + ti.h) * DR;
-        qbase = static_cast<const uint16_t*>(a.q) + rb;
-        op = static_cast<uint16_t*>(a.out) + rb;
+        const int64_t rb = (int64_t)r0 * a.Hq + ti.h;
+        qbase = static_cast<const uint16_t*>(a.q) + rb * DR;
+        op = static_cast<uint16_t*>(a.out) + rb * DVM;
         qstride = (uint32_t)a.Hq * DR * 2;
+        ostride = (uint32_t)a.Hq * DVM * 2;
         kp = static_cast<const uint16_t*>(a.k);
         vp = static_cast<const uint16_t*>(a.v);
     } else {
         const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
-        const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * DR;
-        kp = static_cast<const uint16_t*>(a.k) + kvh;
-        vp = static_cast<const uint16_t*>(a.v) + kvh;
+        const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk;
+        kp = static_cast<const uint16_t*>(a.k) + kvh * DR;
+        vp = static_cast<const uint16_t*>(a.v) + kvh * DVM;
         qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * DR;
-        op = static_cast<uint16_t*>(a.out) + bh * a.Sq * DR;
+        op = static_cast<uint16_t*>(a.out) + bh * a.Sq * DVM;
         qstride = (uint32_t)DR * 2;
+        ostride = (uint32_t)DVM * 2;
         nrows = a.Sq;
         qoff = 0;
         key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
@@ -317,6 +323,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     // (Paged: relative to the wave's 16-key group, rows Hkv*D*2 bytes apart.)
     // The wave's LDS rows are 16*wave .. 16*wave+15, i.e. keys of the same group.
     const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * DR * 2 : (uint32_t)DR * 2;
+    const uint32_t vrow_bytes = PAGED ? (uint32_t)a.Hkv * DVM * 2 : (uint32_t)DVM * 2;
     const int row_base = PAGED ? 16 * wave : 0;
     uint32_t koff[L::DMA], voff[LV::DMA];
 #pragma unroll
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         const int q = 64 * (LV::DMA * wave + i) + lane;
         const int row = q / LV::CPR, pc = q % LV::CPR;
         const int cv = pc ^ LV::fv(row);  // logical chunk of the slice
-        voff[i] = 8 * cv < DRV ? (row - row_base) * row_bytes + (dv0 + 8 * cv) * 2 : kOut;
+        voff[i] = 8 * cv < DRV ? (row - row_base) * vrow_bytes + (dv0 + 8 * cv) * 2 : kOut;
     }
     // Paged: resource over the page of keys j0 + 16*wave .. +15 (zero records
     // when the table entry is outside the cache) and the group's scalar
@@ -339,8 +346,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     int* const kvalid = reinterpret_cast<int*>(smem + VBASE + 2 * LV::TILE);  // [K stage][group]
     // The lookup for a tile is made when its K is issued and kept (per K
     // stage) for its V, issued one step later.
-    int64_t pg_off[2] = {0, 0};
+    int64_t pg_off[2] = {0, 0}, vpg_off[2] = {0, 0};
     uint32_t pg_bytes[2] = {0u, 0u}, pg_soff[2] = {0u, 0u};
+    uint32_t vpg_bytes[2] = {0u, 0u}, vpg_soff[2] = {0u, 0u};
     auto page_of = [&](int j0, int stage) -> bool {
         const int key = j0 + 16 * wave;
         const int lp = key / p.page_size;
@@ -349,6 +357,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         pg_off[stage] = ok ? (int64_t)pg * p.page_size * a.Hkv * DR : 0;
         pg_bytes[stage] = ok ? (uint32_t)p.page_size * row_bytes : 0u;
         pg_soff[stage] = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * DR * 2;
+        vpg_off[stage] = ok ? (int64_t)pg * p.page_size * a.Hkv * DVM : 0;
+        vpg_bytes[stage] = ok ? (uint32_t)p.page_size * vrow_bytes : 0u;
+        vpg_soff[stage] = ((uint32_t)(key % p.page_size) * a.Hkv + ti.gk) * DVM * 2;
         return ok;
     };
     // Dense: resources start at the tile's first key; num_records ends at key Sk.
@@ -372,12 +383,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         if (PAGED) {
             // K of this tile went to K stage (j0 / kBc) % 2 with the lookup.
             const int ks = (j0 / kBc) & 1;
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + pg_off[ks], pg_bytes[ks]);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + vpg_off[ks], vpg_bytes[ks]);
 #pragma unroll
-            for (int i = 0; i < LV::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], pg_soff[ks]);
+            for (int i = 0; i < LV::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], vpg_soff[ks]);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(vp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
+                make_rsrc(vp + (int64_t)j0 * DVM, (uint32_t)(a.Sk - j0) * DVM * 2);
 #pragma unroll
             for (int i = 0; i < LV::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
         }
@@ -656,10 +667,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
             const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * DV + 8 * (cc ^ (row % CPR)));
             if (qw + row < nrows && 8 * cc < DRV)  // 8 dims of the slice, all < DRV or none
                 __builtin_nontemporal_store(
-                    v, reinterpret_cast<u32x4*>(op + (int64_t)(qw + row) * (qstride / 2) + dv0 + 8 * cc));
+                    v, reinterpret_cast<u32x4*>(op + (int64_t)(qw + row) * (ostride / 2) + dv0 + 8 * cc));
         }
     } else if (qi < nrows) {
-        uint16_t* orow = op + (int64_t)qi * (qstride / 2) + dv0;
+        uint16_t* orow = op + (int64_t)qi * (ostride / 2) + dv0;
 #pragma unroll
         for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -834,7 +845,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
 
 inline dim3 forward_grid(const ForwardArgs& a) {
     const int nqb = (a.Sq + kBr - 1) / kBr;
-    return dim3((unsigned)(nqb * a.B * a.Hq), a.D > 128 ? 2u : 1u);  // y: output slice of 128 dims
+    // y: output slice of 128 dims when the value head dim is above 128
+    return dim3((unsigned)(nqb * a.B * a.Hq), a.Dv > 128 ? 2u : 1u);
 }
 
 // Workgroups of this kernel one XCD holds at once (resident per CU times
@@ -870,6 +882,26 @@ hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s)
         b.sweep_group = (!PAGED && !a.causal) ? xcd_resident(kernel, kThreads) : 0;
         hipLaunchKernelGGL(kernel, g, t, 0, s, b, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     };
+    if (a.Dv != a.D) {
+        // A value head dim of its own (paged prefill): general-width kernels
+        // on the padded K width, V in one 64- or 128-dim pass or two 128-dim
+        // slices.
+        if constexpr (PAGED && !BIAS) {
+            if (a.Dv % 8 != 0 || a.Dv < 8 || a.Dv > 256) return hipErrorInvalidValue;
+            const bool v64 = a.Dv <= 64;
+            if (a.D <= 64)
+                v64 ? go(forward_bf16_kernel<64, PAGED, T, false, true, 64>)
+                    : go(forward_bf16_kernel<64, PAGED, T, false, true, 128>);
+            else if (a.D <= 128)
+                v64 ? go(forward_bf16_kernel<128, PAGED, T, false, true, 64>)
+                    : go(forward_bf16_kernel<128, PAGED, T, false, true, 128>);
+            else
+                v64 ? go(forward_bf16_kernel<256, PAGED, T, false, true, 64>)
+                    : go(forward_bf16_kernel<256, PAGED, T, false, true, 128>);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.D == 64)
         go(forward_bf16_kernel<64, PAGED, T, BIAS>);
     else if (a.D == 128)

@@ -581,6 +581,7 @@ hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, boo
     a.Sq = 1;
     a.Sk = d.Sk;
     a.D = d.D;
+    a.Dv = d.D;
     a.scale = d.scale;
     a.causal = false;
     a.padded = d.key_lens != nullptr;

@@ -22,6 +22,9 @@ struct ForwardArgs {
     // bias[b * bias_sb + h * bias_sh + i * Sk + j], input dtype.
     const void* bias = nullptr;
     int64_t bias_sb = 0, bias_sh = 0;
+    // Value / output head dim (v rows and out rows); equal to D except on the
+    // paged prefill, where V may be narrower or wider (up to 256).
+    int Dv = 0;
     // Workgroups one XCD holds at once (set at launch from the kernel's
     // occupancy; 0: unknown).  Dense non-causal launches sweep the keys
     // backwards in every other such group of an XCD's run, so a group starts
@@ -61,16 +64,17 @@ struct DecodeArgs {
     const void* v;
     void* out;
     const int32_t* key_lens;  // nullptr = every key valid
-    float* o_part;            // [B, Hq, splits, D]
+    float* o_part;            // [B, Hq, splits, Dv]
     float* lse_part;          // [B, Hq, splits]
     int B, Hq, Hkv, Sk, D;
     int splits;
     float scale;
+    int Dv = 0;               // value / output head dim (v rows, o_part, out); set to D when equal
 };
 
 // Paged K/V cache (packed queries).  With these, DecodeArgs holds B = queries,
-// Sk = max_seq_len, k / v = the page caches [pages, page_size, Hkv, D] and no
-// key_lens.
+// Sk = max_seq_len, k / v = the page caches [pages, page_size, Hkv, D] and
+// [pages, page_size, Hkv, Dv], and no key_lens.
 struct PagedArgs {
     const int32_t* block_tables;  // [num_seqs, max_pages]
     const int32_t* seq_lens;      // [num_seqs]

@@ -63,6 +63,18 @@ bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
     return D >= 8 && D <= max16 && D % 8 == 0;
 }
 
+// Value head dim of the paged entry points: Dv == D on every kernel; Dv != D
+// on the 16-bit kernels with D and Dv both multiples of 8 up to 256.
+sdpa_status_t check_value_dim(int64_t D, int64_t Dv, int dtype) {
+    if (Dv == D) return SDPA_OK;
+    if (dtype == SDPA_F32 || !head_dim_ok(D, dtype, 256) || !head_dim_ok(Dv, dtype, 256))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "value head dim Dv=%lld differs from D=%lld: supported for bf16 / fp16 with "
+                    "both multiples of 8 up to 256",
+                    (long long)Dv, (long long)D);
+    return SDPA_OK;
+}
+
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -198,6 +210,7 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
     a.Sq = (int)Sq;
     a.Sk = (int)Sk;
     a.D = (int)D;
+    a.Dv = (int)D;
     a.scale = scale;
     a.causal = causal;
     a.padded = padded;
@@ -510,6 +523,7 @@ sdpa_status_t sdpa_block_forward(const void* x, const void* wq, const void* wk, 
     a.Sq = (int)S;
     a.Sk = (int)S;
     a.D = (int)hd;
+    a.Dv = (int)hd;
     a.scale = scale;
     a.causal = mask_kind & SDPA_MASK_CAUSAL;
     a.padded = padded;
@@ -623,6 +637,7 @@ sdpa_status_t decode_impl(const void* q, const void* k, const void* v, int64_t B
     a.Hkv = (int)Hkv;
     a.Sk = (int)Sk;
     a.D = (int)D;
+    a.Dv = (int)D;
     a.splits = num_splits;
     a.scale = scale;
     (void)hipGetLastError();
@@ -650,7 +665,7 @@ sdpa_status_t sdpa_decode_noalloc(const void* q, const void* k, const void* v, i
 }
 
 sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const void* v_cache,
-                                   int64_t queries, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int64_t queries, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                                    int64_t pages, int64_t page_size, const int32_t* block_tables,
                                    int64_t num_seqs, int64_t max_pages_per_seq,
                                    const int32_t* seq_lens, const int32_t* query_seq,
@@ -659,14 +674,15 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
                                    size_t workspace_bytes, void* out, int dtype, void* stream) {
     if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !query_seq || !query_pos)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null pointer argument");
-    if (queries < 1 || Hq < 1 || Hkv < 1 || D < 1 || pages < 1 || page_size < 1 || num_seqs < 1 ||
-        max_pages_per_seq < 1 || max_seq_len < 1)
+    if (queries < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || pages < 1 || page_size < 1 ||
+        num_seqs < 1 || max_pages_per_seq < 1 || max_seq_len < 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT,
-                    "every size must be >= 1 (queries=%lld Hq=%lld Hkv=%lld D=%lld pages=%lld "
-                    "page_size=%lld num_seqs=%lld max_pages_per_seq=%lld max_seq_len=%lld)",
-                    (long long)queries, (long long)Hq, (long long)Hkv, (long long)D, (long long)pages,
-                    (long long)page_size, (long long)num_seqs, (long long)max_pages_per_seq,
-                    (long long)max_seq_len);
+                    "every size must be >= 1 (queries=%lld Hq=%lld Hkv=%lld D=%lld Dv=%lld "
+                    "pages=%lld page_size=%lld num_seqs=%lld max_pages_per_seq=%lld "
+                    "max_seq_len=%lld)",
+                    (long long)queries, (long long)Hq, (long long)Hkv, (long long)D, (long long)Dv,
+                    (long long)pages, (long long)page_size, (long long)num_seqs,
+                    (long long)max_pages_per_seq, (long long)max_seq_len);
     if (Hq % Hkv != 0)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
                     (long long)Hq, (long long)Hkv);
@@ -685,22 +701,24 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
                     "page_size",
                     (long long)max_seq_len);
     const int64_t es = elem_size(dtype);
-    const int64_t nq = numel4(queries, Hq, D, 1), nc = numel4(pages, page_size, Hkv, D);
+    const int64_t nq = numel4(queries, Hq, D, 1), no = numel4(queries, Hq, Dv, 1);
+    const int64_t nc = numel4(pages, page_size, Hkv, D), nvc = numel4(pages, page_size, Hkv, Dv);
     const int64_t nt = numel4(num_seqs, max_pages_per_seq, 1, 1);
-    int64_t qbytes = 0, cbytes = 0;
-    if (nq < 0 || nc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) || !mul_ok(nc, es, &cbytes))
+    int64_t qbytes = 0, obytes = 0, cbytes = 0, vcbytes = 0;
+    if (nq < 0 || no < 0 || nc < 0 || nvc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) ||
+        !mul_ok(no, es, &obytes) || !mul_ok(nc, es, &cbytes) || !mul_ok(nvc, es, &vcbytes))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
-    if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_cache, cbytes) ||
-        overlap(out, qbytes, v_cache, cbytes) || overlap(out, qbytes, block_tables, nt * 4) ||
-        overlap(out, qbytes, seq_lens, num_seqs * 4) || overlap(out, qbytes, query_seq, queries * 4) ||
-        overlap(out, qbytes, query_pos, queries * 4))
+    if (overlap(out, obytes, q, qbytes) || overlap(out, obytes, k_cache, cbytes) ||
+        overlap(out, obytes, v_cache, vcbytes) || overlap(out, obytes, block_tables, nt * 4) ||
+        overlap(out, obytes, seq_lens, num_seqs * 4) || overlap(out, obytes, query_seq, queries * 4) ||
+        overlap(out, obytes, query_pos, queries * 4))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps an input");
-    const size_t need = sdpa_decode_workspace_size(queries, Hq, D, num_splits);
+    const size_t need = sdpa_decode_workspace_size(queries, Hq, Dv, num_splits);
     if (need == 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace size overflows");
     if (!workspace || workspace_bytes < need)
         return fail(SDPA_ERR_WORKSPACE, "paged attention needs a workspace of %zu bytes (got %zu)",
                     need, workspace ? workspace_bytes : (size_t)0);
-    if (overlap(out, qbytes, workspace, (int64_t)need))
+    if (overlap(out, obytes, workspace, (int64_t)need))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps the workspace");
     if (queries > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX)
@@ -710,10 +728,12 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
                     (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 and fp16 only");
+    const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
+    if (vst != SDPA_OK) return vst;
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
-    const int64_t page_elems = numel4(page_size, Hkv, D, es);
+    const int64_t page_elems = numel4(page_size, Hkv, D > Dv ? D : Dv, es);
     if (page_elems < 0 || page_elems > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "one page exceeds 2 GiB");
     const int64_t items = sdpa::decode_work_items(queries, Hq, Hkv, num_splits);
@@ -728,12 +748,13 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     a.key_lens = nullptr;
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          round_up((size_t)numel4(queries, Hq, num_splits, D) * 4));
+                                          round_up((size_t)numel4(queries, Hq, num_splits, Dv) * 4));
     a.B = (int)queries;
     a.Hq = (int)Hq;
     a.Hkv = (int)Hkv;
     a.Sk = (int)max_seq_len;
     a.D = (int)D;
+    a.Dv = (int)Dv;
     a.splits = num_splits;
     a.scale = scale;
     sdpa::PagedArgs p;
@@ -753,22 +774,23 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
 }
 
 sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
-                                 int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t pages,
+                                 int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
+                                 int64_t pages,
                                  int64_t page_size, const int32_t* block_tables, int64_t num_seqs,
                                  int64_t max_pages_per_seq, const int32_t* seq_lens,
                                  const int32_t* cu_seqlens_q, int64_t max_q, int64_t max_seq_len,
                                  float scale, int causal, void* out, int dtype, void* stream) {
     if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !cu_seqlens_q)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null pointer argument");
-    if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || pages < 1 || page_size < 1 || num_seqs < 1 ||
-        max_pages_per_seq < 1 || max_q < 1 || max_seq_len < 1)
+    if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || pages < 1 || page_size < 1 ||
+        num_seqs < 1 || max_pages_per_seq < 1 || max_q < 1 || max_seq_len < 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT,
-                    "every size must be >= 1 (total_q=%lld Hq=%lld Hkv=%lld D=%lld pages=%lld "
-                    "page_size=%lld num_seqs=%lld max_pages_per_seq=%lld max_q=%lld "
+                    "every size must be >= 1 (total_q=%lld Hq=%lld Hkv=%lld D=%lld Dv=%lld "
+                    "pages=%lld page_size=%lld num_seqs=%lld max_pages_per_seq=%lld max_q=%lld "
                     "max_seq_len=%lld)",
-                    (long long)total_q, (long long)Hq, (long long)Hkv, (long long)D, (long long)pages,
-                    (long long)page_size, (long long)num_seqs, (long long)max_pages_per_seq,
-                    (long long)max_q, (long long)max_seq_len);
+                    (long long)total_q, (long long)Hq, (long long)Hkv, (long long)D, (long long)Dv,
+                    (long long)pages, (long long)page_size, (long long)num_seqs,
+                    (long long)max_pages_per_seq, (long long)max_q, (long long)max_seq_len);
     if (Hq % Hkv != 0)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
                     (long long)Hq, (long long)Hkv);
@@ -784,15 +806,17 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                     "page_size",
                     (long long)max_seq_len);
     const int64_t es = elem_size(dtype);
-    const int64_t nq = numel4(total_q, Hq, D, 1), nc = numel4(pages, page_size, Hkv, D);
+    const int64_t nq = numel4(total_q, Hq, D, 1), no = numel4(total_q, Hq, Dv, 1);
+    const int64_t nc = numel4(pages, page_size, Hkv, D), nvc = numel4(pages, page_size, Hkv, Dv);
     const int64_t nt = numel4(num_seqs, max_pages_per_seq, 1, 1);
-    int64_t qbytes = 0, cbytes = 0;
-    if (nq < 0 || nc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) || !mul_ok(nc, es, &cbytes))
+    int64_t qbytes = 0, obytes = 0, cbytes = 0, vcbytes = 0;
+    if (nq < 0 || no < 0 || nc < 0 || nvc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) ||
+        !mul_ok(no, es, &obytes) || !mul_ok(nc, es, &cbytes) || !mul_ok(nvc, es, &vcbytes))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
-    if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_cache, cbytes) ||
-        overlap(out, qbytes, v_cache, cbytes) || overlap(out, qbytes, block_tables, nt * 4) ||
-        overlap(out, qbytes, seq_lens, num_seqs * 4) ||
-        overlap(out, qbytes, cu_seqlens_q, (num_seqs + 1) * 4))
+    if (overlap(out, obytes, q, qbytes) || overlap(out, obytes, k_cache, cbytes) ||
+        overlap(out, obytes, v_cache, vcbytes) || overlap(out, obytes, block_tables, nt * 4) ||
+        overlap(out, obytes, seq_lens, num_seqs * 4) ||
+        overlap(out, obytes, cu_seqlens_q, (num_seqs + 1) * 4))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps an input");
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
@@ -802,11 +826,14 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                     (long long)D);
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 and fp16 only");
+    const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
+    if (vst != SDPA_OK) return vst;
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
-    const int64_t page_elems = numel4(page_size, Hkv, D, es);
-    const int64_t chunk_bytes = numel4(max_q + 127, Hq, D, es);  // one workgroup's Q rows
+    const int64_t DM = D > Dv ? D : Dv;
+    const int64_t page_elems = numel4(page_size, Hkv, DM, es);
+    const int64_t chunk_bytes = numel4(max_q + 127, Hq, DM, es);  // one workgroup's Q / O rows
     if (page_elems < 0 || page_elems > INT_MAX || chunk_bytes < 0 || chunk_bytes > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "one page or one chunk of q exceeds 2 GiB");
     const int64_t blocks = ((max_q + 127) / 128) * num_seqs * Hq;
@@ -825,6 +852,7 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     a.Sq = (int)max_q;
     a.Sk = (int)max_seq_len;
     a.D = (int)D;
+    a.Dv = (int)Dv;
     a.scale = scale;
     a.causal = causal != 0;
     a.padded = false;

@@ -91,12 +91,12 @@ def load_library():
     lib.sdpa_decode_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_decode_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.sdpa_paged_attention.restype = i32
-    lib.sdpa_paged_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
-                                         vp, vp, i64, ctypes.c_float, i32, i32, vp, ctypes.c_size_t,
-                                         vp, i32, vp]
+    lib.sdpa_paged_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, i64,
+                                         vp, vp, vp, i64, ctypes.c_float, i32, i32, vp,
+                                         ctypes.c_size_t, vp, i32, vp]
     lib.sdpa_paged_prefill.restype = i32
-    lib.sdpa_paged_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp, vp,
-                                       i64, i64, ctypes.c_float, i32, vp, i32, vp]
+    lib.sdpa_paged_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
+                                       vp, i64, i64, ctypes.c_float, i32, vp, i32, vp]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_status_string.argtypes = [i32]
     lib.sdpa_last_error.restype = ctypes.c_char_p
@@ -457,10 +457,10 @@ def sdpa_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq,
                          stream=None):
     """Packed queries over a K/V page cache.
 
-    q [queries, Hq, D]; k_cache, v_cache [pages, page_size, Hkv, D];
-    block_tables int32 [num_seqs, max_pages_per_seq]; seq_lens int32
-    [num_seqs]; query_seq, query_pos int32 [queries]; max_seq_len (host int)
-    bounds seq_lens.  Returns out [queries, Hq, D].
+    q [queries, Hq, D]; k_cache [pages, page_size, Hkv, D]; v_cache [pages,
+    page_size, Hkv, Dv]; block_tables int32 [num_seqs, max_pages_per_seq];
+    seq_lens int32 [num_seqs]; query_seq, query_pos int32 [queries];
+    max_seq_len (host int) bounds seq_lens.  Returns out [queries, Hq, Dv].
     """
     _check_tensor("q", q, 3)
     _check_tensor("k_cache", k_cache, 4)
@@ -474,21 +474,24 @@ def sdpa_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq,
             raise TypeError("%s must be int32" % name)
     nq, Hq, D = q.shape
     pages, page_size, Hkv, Dk = k_cache.shape
-    if Dk != D or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must be [pages, page_size, Hkv, D] matching q")
+    Dv = v_cache.shape[3]
+    if Dk != D or tuple(v_cache.shape[:3]) != (pages, page_size, Hkv):
+        raise ValueError("k_cache must be [pages, page_size, Hkv, D] matching q and v_cache "
+                         "[pages, page_size, Hkv, Dv]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share one dtype")
     num_seqs, max_pages = block_tables.shape
     if seq_lens.shape[0] != num_seqs or query_seq.shape[0] != nq or query_pos.shape[0] != nq:
         raise ValueError("seq_lens must have num_seqs entries, query_seq and query_pos one per query")
     lib = load_library()
-    need = int(lib.sdpa_decode_workspace_size(nq, Hq, D, int(num_splits)))
+    need = int(lib.sdpa_decode_workspace_size(nq, Hq, Dv, int(num_splits)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((nq, Hq, Dv), dtype=q.dtype, device=q.device)
     _check(lib.sdpa_paged_attention(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, pages, page_size, _ptr(block_tables),
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, Dv, pages, page_size,
+        _ptr(block_tables),
         num_seqs, max_pages, _ptr(seq_lens), _ptr(query_seq), _ptr(query_pos), int(max_seq_len),
         float(scale), int(bool(causal)), int(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _dtype_code(q), _stream(stream)))
@@ -499,11 +502,11 @@ def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q
                        max_q, max_seq_len, out=None, stream=None):
     """Packed prefill chunks over a K/V page cache.
 
-    q [total_q, Hq, D]; k_cache, v_cache [pages, page_size, Hkv, D];
-    block_tables int32 [num_seqs, max_pages_per_seq]; seq_lens int32
-    [num_seqs] (the chunk included); cu_seqlens_q int32 [num_seqs + 1];
-    max_q, max_seq_len host bounds.  Row i of sequence s's chunk sits at
-    position seq_lens[s] - n_s + i.  Returns out [total_q, Hq, D].
+    q [total_q, Hq, D]; k_cache [pages, page_size, Hkv, D]; v_cache [pages,
+    page_size, Hkv, Dv]; block_tables int32 [num_seqs, max_pages_per_seq];
+    seq_lens int32 [num_seqs] (the chunk included); cu_seqlens_q int32
+    [num_seqs + 1]; max_q, max_seq_len host bounds.  Row i of sequence s's
+    chunk sits at position seq_lens[s] - n_s + i.  Returns out [total_q, Hq, Dv].
     """
     _check_tensor("q", q, 3)
     _check_tensor("k_cache", k_cache, 4)
@@ -517,18 +520,21 @@ def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q
             raise TypeError("%s must be int32" % name)
     nq, Hq, D = q.shape
     pages, page_size, Hkv, Dk = k_cache.shape
-    if Dk != D or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must be [pages, page_size, Hkv, D] matching q")
+    Dv = v_cache.shape[3]
+    if Dk != D or tuple(v_cache.shape[:3]) != (pages, page_size, Hkv):
+        raise ValueError("k_cache must be [pages, page_size, Hkv, D] matching q and v_cache "
+                         "[pages, page_size, Hkv, Dv]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share one dtype")
     num_seqs, max_pages = block_tables.shape
     if seq_lens.shape[0] != num_seqs or cu_seqlens_q.shape[0] != num_seqs + 1:
         raise ValueError("seq_lens needs num_seqs entries and cu_seqlens_q num_seqs + 1")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((nq, Hq, Dv), dtype=q.dtype, device=q.device)
     lib = load_library()
     _check(lib.sdpa_paged_prefill(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, pages, page_size, _ptr(block_tables),
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, Dv, pages, page_size,
+        _ptr(block_tables),
         num_seqs, max_pages, _ptr(seq_lens), _ptr(cu_seqlens_q), int(max_q), int(max_seq_len),
         float(scale), int(bool(causal)), _ptr(out), _dtype_code(q), _stream(stream)))
     return out

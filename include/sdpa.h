@@ -339,7 +339,9 @@ sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
  * page table.  Split-KV with the same log-sum-exp merge as sdpa_decode.
  *   q            device [queries, Hq, D]
  *   k_cache      device [pages, page_size, Hkv, D]
- *   v_cache      device [pages, page_size, Hkv, D]
+ *   v_cache      device [pages, page_size, Hkv, Dv]: the value head dim Dv
+ *                may differ from D (the guide's K [.., Hkv, D], V [.., Hkv,
+ *                Dv], output [.., Hq, Dv])
  *   block_tables device int32 [num_seqs, max_pages_per_seq]: logical key j of
  *                sequence s is slot j % page_size of physical page
  *                block_tables[s][j / page_size]
@@ -355,13 +357,14 @@ sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
  *                at the end of a sequence is aligned bottom-right)
  *   num_splits   1..SDPA_MAX_SPLITS
  *   workspace    device buffer of at least
- *                sdpa_decode_workspace_size(queries, Hq, D, num_splits) bytes
- *                (same layout as sdpa_decode's with B = queries)
- *   out          device [queries, Hq, D]
+ *                sdpa_decode_workspace_size(queries, Hq, Dv, num_splits) bytes
+ *                (same layout as sdpa_decode's with B = queries, D = Dv)
+ *   out          device [queries, Hq, Dv]
  * Two kernels are enqueued on stream: the split pass, then the merge.
  * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024
  * (above 256 the split pass runs on the head-dim-split kernel, as in
- * sdpa_decode), page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
+ * sdpa_decode) with Dv = D, or D and Dv both multiples of 8 up to 256;
+ * page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
  * [0, num_seqs), a negative query_pos under the causal flag, or a sequence
@@ -369,7 +372,7 @@ sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
  * block_tables entry outside [0, pages) is never read: its keys are hidden.
  */
 sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const void *v_cache,
-                                   int64_t queries, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int64_t queries, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                                    int64_t pages, int64_t page_size, const int32_t *block_tables,
                                    int64_t num_seqs, int64_t max_pages_per_seq,
                                    const int32_t *seq_lens, const int32_t *query_seq,
@@ -387,8 +390,8 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  * seq_lens[s] - n_s + i.  Equivalent to sdpa_paged_attention with those
  * query_seq / query_pos.
  *   q             device [total_q, Hq, D]
- *   k_cache,
- *   v_cache       device [pages, page_size, Hkv, D]
+ *   k_cache       device [pages, page_size, Hkv, D]
+ *   v_cache       device [pages, page_size, Hkv, Dv] (Dv may differ from D)
  *   block_tables  device int32 [num_seqs, max_pages_per_seq] (as above)
  *   seq_lens      device int32 [num_seqs]: cached keys, the chunk included
  *   cu_seqlens_q  device int32 [num_seqs + 1]: 0 = cu[0] <= cu[1] <= ... <=
@@ -397,11 +400,12 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *   max_seq_len   host: bound on seq_lens, <= max_pages_per_seq * page_size
  *   causal        0: every cached key of the sequence is visible; 1: only
  *                 keys j <= the row's absolute position
- *   out           device [total_q, Hq, D]
+ *   out           device [total_q, Hq, Dv]
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
  * SDPA_F16, D a multiple of 8 up to 1024 (above 256 on the head-dim-split
- * kernel), page_size a multiple of 16
- * (SDPA_ERR_UNSUPPORTED otherwise).
+ * kernel) with Dv = D, or D and Dv both multiples of 8 up to 256 (a value
+ * head dim above 128 in two 128-dim output slices); page_size a multiple of
+ * 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside
  * out is ever written); a chunk longer than max_q is only computed for its
@@ -411,7 +415,8 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  * keys are hidden.
  */
 sdpa_status_t sdpa_paged_prefill(const void *q, const void *k_cache, const void *v_cache,
-                                 int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t pages,
+                                 int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
+                                 int64_t pages,
                                  int64_t page_size, const int32_t *block_tables, int64_t num_seqs,
                                  int64_t max_pages_per_seq, const int32_t *seq_lens,
                                  const int32_t *cu_seqlens_q, int64_t max_q, int64_t max_seq_len,

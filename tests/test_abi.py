@@ -177,14 +177,15 @@ FAKE_S = ctypes.c_void_p(0x7c000000)
 FAKE_P = ctypes.c_void_p(0x7d000000)
 
 
-def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_size=16,
+def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, Dv=None, pages=100, page_size=16,
           tables=FAKE_T, num_seqs=2, max_pages=50, seq_lens=FAKE_L, qseq=FAKE_S, qpos=FAKE_P,
           max_seq_len=800, scale=0.1, causal=0, splits=4, ws=FAKE_W, ws_bytes=None, out=FAKE_O,
           dtype=sd.SDPA_BF16):
     lib = sd.load_library()
+    Dv = D if Dv is None else Dv
     if ws_bytes is None:
-        ws_bytes = lib.sdpa_decode_workspace_size(nq, Hq, D, splits)
-    return lib.sdpa_paged_attention(q, k, v, nq, Hq, Hkv, D, pages, page_size, tables, num_seqs,
+        ws_bytes = lib.sdpa_decode_workspace_size(nq, Hq, Dv, splits)
+    return lib.sdpa_paged_attention(q, k, v, nq, Hq, Hkv, D, Dv, pages, page_size, tables, num_seqs,
                                     max_pages, seq_lens, qseq, qpos, max_seq_len, scale, causal,
                                     splits, ws, ws_bytes, out, dtype, None)
 
@@ -207,6 +208,13 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, pages=100, page_
     (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
+    (dict(Dv=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Dv=100), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=512, Dv=128), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=64, Dv=264), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    # the workspace holds Dv-wide partials: one sized for D = 128 is too small at Dv = 256
+    (dict(D=128, Dv=256, ws_bytes=(3 * 8 * 4 * 128 * 4 + 255) // 256 * 256 + 256),
+     sd.SDPA_ERR_WORKSPACE, "workspace"),
 ])
 def test_paged_rejects(kw, status, needle):
     assert paged(**kw) == status
@@ -216,11 +224,12 @@ def test_paged_rejects(kw, status, needle):
 FAKE_C = ctypes.c_void_p(0x7e000000)
 
 
-def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, pages=100, page_size=16,
-            tables=FAKE_T, num_seqs=3, max_pages=50, seq_lens=FAKE_L, cu=FAKE_C, max_q=200,
-            max_seq_len=800, scale=0.1, causal=1, out=FAKE_O, dtype=sd.SDPA_BF16):
+def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pages=100,
+            page_size=16, tables=FAKE_T, num_seqs=3, max_pages=50, seq_lens=FAKE_L, cu=FAKE_C,
+            max_q=200, max_seq_len=800, scale=0.1, causal=1, out=FAKE_O, dtype=sd.SDPA_BF16):
     lib = sd.load_library()
-    return lib.sdpa_paged_prefill(q, k, v, nq, Hq, Hkv, D, pages, page_size, tables, num_seqs,
+    Dv = D if Dv is None else Dv
+    return lib.sdpa_paged_prefill(q, k, v, nq, Hq, Hkv, D, Dv, pages, page_size, tables, num_seqs,
                                   max_pages, seq_lens, cu, max_q, max_seq_len, scale, causal, out,
                                   dtype, None)
 
@@ -238,6 +247,12 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, pages=100, p
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
+    (dict(Dv=-3), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Dv=60), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=64, Dv=512), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    # v_cache spans 100 * 16 * 2 * Dv * 2 bytes: 1 MB in lies inside it only at Dv = 256
+    (dict(Dv=256, out=ctypes.c_void_p(0x40000000 + (1 << 20))), sd.SDPA_ERR_INVALID_ARGUMENT,
+     "overlaps"),
 ])
 def test_paged_prefill_rejects(kw, status, needle):
     assert prefill(**kw) == status

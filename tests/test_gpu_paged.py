@@ -372,3 +372,81 @@ def test_paged_prefill_headdim_split_invalid_table_entries():
                             np.array([[0, 2]]), np.array([32]), np.zeros(10, dtype=np.int64),
                             np.full(10, 31), scale, False)
     compare(to64(out), ref, torch.bfloat16, "prefill D=768: invalid pages hidden")
+
+
+# ------------------------------------------------ value head dim Dv != D
+# V [pages, page_size, Hkv, Dv] and the output [.., Hq, Dv] with Dv other than
+# D (ruDNN user guide section 9): the general-width kernels, K and V with
+# their own widths; above 128 value dims the prefill writes two 128-dim
+# output slices.
+
+DV_PAIRS = [(64, 128), (128, 64), (128, 256), (256, 64), (192, 96), (40, 200), (256, 136), (8, 16)]
+
+
+def with_value_width(inp, Dv, dtype, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed + 7919)
+    pages, ps, Hkv, _ = inp["k_cache"].shape
+    inp["v_cache"] = torch.randn(pages, ps, Hkv, Dv, generator=g, device=DEV).to(dtype)
+    return inp
+
+
+@pytest.mark.parametrize("D,Dv", DV_PAIRS)
+@pytest.mark.parametrize("splits", [1, 5])
+def test_paged_attention_value_width(D, Dv, splits):
+    lens, qs, qp = [300, 129, 1, 50], [0, 1, 2, 0, 3, 1], [299, 128, 0, 17, 49, 3]
+    for causal in (False, True):
+        seed = 2000 + D + Dv + splits + causal
+        inp = with_value_width(draw_paged(lens, qs, qp, 8, 2, D, 16, torch.bfloat16, seed, DEV), Dv,
+                               torch.bfloat16, seed)
+        scale = 1 / math.sqrt(D)
+        out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                      inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale,
+                                      causal, inp["block_tables"].shape[1] * 16, splits)
+        torch.cuda.synchronize()
+        assert out.shape == (len(qs), 8, Dv)
+        compare(to64(out), oracle_of(inp, scale, causal), torch.bfloat16,
+                "paged D=%d Dv=%d splits=%d causal=%d" % (D, Dv, splits, causal))
+
+
+@pytest.mark.parametrize("D,Dv", DV_PAIRS)
+def test_paged_prefill_value_width(D, Dv):
+    lens, chunks = [300, 129, 1000], [300, 40, 257]
+    nq = sum(chunks)
+    for causal in (False, True):
+        seed = 2100 + D + Dv + causal
+        inp = with_value_width(draw_paged(lens, [0] * nq, [0] * nq, 8, 2, D, 16, torch.bfloat16,
+                                          seed, DEV), Dv, torch.bfloat16, seed)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device=DEV)
+        scale = 1 / math.sqrt(D)
+        out = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                    inp["seq_lens"], cu, scale, causal, max(chunks),
+                                    inp["block_tables"].shape[1] * 16)
+        torch.cuda.synchronize()
+        assert out.shape == (nq, 8, Dv)
+        qs, qp = O.chunk_positions(cu.cpu().numpy(), np.array(lens))
+        ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                                inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, scale,
+                                causal)
+        compare(to64(out), ref, torch.bfloat16, "prefill D=%d Dv=%d causal=%d" % (D, Dv, causal))
+
+
+def test_paged_value_width_fp16_and_prefill_matches_per_query():
+    D, Dv = 128, 64
+    lens, chunks = [700, 333], [200, 333]
+    nq = sum(chunks)
+    inp = with_value_width(draw_paged(lens, [0] * nq, [0] * nq, 8, 4, D, 32, torch.float16, 2200, DEV),
+                           Dv, torch.float16, 2200)
+    cu = torch.tensor([0, 200, 533], dtype=torch.int32, device=DEV)
+    qs, qp = O.chunk_positions(cu.cpu().numpy(), np.array(lens))
+    i32 = dict(dtype=torch.int32, device=DEV)
+    pre = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                inp["seq_lens"], cu, 0.1, True, 333, inp["block_tables"].shape[1] * 32)
+    per = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], torch.tensor(qs, **i32), torch.tensor(qp, **i32),
+                                  0.1, True, inp["block_tables"].shape[1] * 32, 7)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, 0.1, True)
+    compare(to64(pre), ref, torch.float16, "fp16 prefill Dv=64")
+    compare(to64(per), ref, torch.float16, "fp16 paged attention Dv=64")
