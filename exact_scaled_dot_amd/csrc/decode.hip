@@ -496,6 +496,303 @@ __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * DR + 4 * d4) = u32x2{lo, hi};
 }
 
+// fp32 inputs (the ruDNN user guide's F32 Q/K/V, section 9): the same items,
+// persistent grid, per-wave DMA ring and page lookup as the 16-bit split
+// pass, with fp32 MFMAs (v_mfma_f32_16x16x4_f32) and no rounding of the
+// weights.  Per 16-key step of an item, in one wave:
+//   S^T[16 keys x 16 queries] = K Q^T   D/4 MFMAs; lane group g (lanes
+//     16g .. 16g+15) contracts dims (D/4) g .. (D/4) g + D/4 - 1, so one
+//     16-byte LDS read of K feeds four MFMAs;
+//   O^T[D x 16 queries] += V^T P^T      4 x D/16 MFMAs; MFMA i takes key
+//     4g + i in contraction slot g, which is exactly the score register i of
+//     the lanes of group g: the weights never leave their lanes.
+// Row r of the A operand of O^T tile dt is dim 4r + dt%4 + 64 (dt/4), so a
+// lane's V^T operands of four tiles are one 16-byte run of its V row.
+template <int D>
+struct DecGeoF32 {
+    static constexpr int CPR = D / 4;                    // 16-byte chunks per row
+    static constexpr int TILE = kStep * D;               // floats of one K or V step
+    static constexpr int STAGE = 2 * TILE;               // K tile, then V tile
+    static constexpr int NS = kRingBytes / (4 * STAGE);  // ring stages per wave
+    static constexpr int DMA = TILE * 4 / 1024;          // 1-KB DMA loads per tile
+    static constexpr int OPS = 2 * DMA;                  // vector memory ops per step
+    static constexpr int CG = CPR / 4;                   // K chunks per lane group
+    // K chunk swizzle: the 16 rows a lane group reads at one logical chunk
+    // fall on 16 distinct 16-byte bank groups.
+    __device__ static int fk(int r) { return r % 16; }
+};
+static_assert(DecGeoF32<128>::NS == 2 && DecGeoF32<64>::NS == 4, "fp32 ring depth");
+
+template <int D, bool PAGED, bool GEN = false>
+__global__ __launch_bounds__(kDecThreads, 1) void decode_split_f32_kernel(
+    DecodeArgs a, PagedArgs p, const int32_t* __restrict__ key_lens,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ query_seq, const int32_t* __restrict__ query_pos, int items) {
+    using L = DecGeoF32<D>;
+    constexpr int DT = D / 16;  // O^T tiles
+    const Meta meta{key_lens, tables, seq_lens, query_seq, query_pos};
+    __shared__ __attribute__((aligned(1024))) float smem[kDecWaves * L::NS * L::STAGE];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15;  // query column (and key row of the S^T tile)
+    const int grp = lane >> 4;  // lane group
+
+    const int wg0 = (int)((int64_t)blockIdx.x * items / gridDim.x);
+    const int it1 = (int)((int64_t)(blockIdx.x + 1) * items / gridDim.x);
+    const int it0 = wg0 + wave;
+    if (it0 >= it1) return;
+
+    const int G = a.Hq / a.Hkv;
+    const int nqc = (G + kQ - 1) / kQ;
+    int chunk = (a.Sk + a.splits - 1) / a.splits;
+    if (PAGED) chunk = (chunk + kStep - 1) / kStep * kStep;
+    const float c = a.scale * kLog2e;
+    const float tau = kTau / c;
+    // Head dim in memory: DR floats (GEN: a multiple of 4 below D; else D).
+    const int DR = GEN ? a.D : D;
+    constexpr uint32_t kOut = 0x80000000u;
+    const uint32_t head_bytes = (uint32_t)a.Sk * DR * 4;
+    const uint32_t row_bytes = PAGED ? (uint32_t)a.Hkv * DR * 4 : (uint32_t)DR * 4;
+    const uint32_t page_bytes = PAGED ? (uint32_t)p.page_size * row_bytes : 0u;
+
+    // DMA slot s = 64 i + lane of a tile holds row s / CPR, physical chunk
+    // s % CPR; K's logical chunk is swizzled, V's is not.
+    uint32_t koff[L::DMA], voff[L::DMA];
+#pragma unroll
+    for (int i = 0; i < L::DMA; ++i) {
+        const int q = 64 * i + lane, row = q / L::CPR, pc = q % L::CPR;
+        const int ck = pc ^ L::fk(row);
+        koff[i] = 4 * ck < DR ? row * row_bytes + ck * 16 : kOut;
+        voff[i] = 4 * pc < DR ? row * row_bytes + pc * 16 : kOut;
+    }
+
+    float* ring = smem + wave * L::NS * L::STAGE;
+
+    int i_it = it0, i_st = 0, i_nst = 0, i_k0 = 0, i_seq = 0, i_gk = 0, i_page = -1;
+    __amdgpu_buffer_rsrc_t ikrs = make_rsrc(a.k, 0), ivrs = make_rsrc(a.v, 0);
+    uint32_t valid_bits = 0xffffffffu;
+    auto seek = [&](int from) {
+        for (i_it = from; i_it < it1; i_it += kDecWaves) {
+            const Item g = item_geo<PAGED>(a, p, meta, i_it, G, nqc, chunk);
+            if (g.nst > 0) {
+                i_st = 0;
+                i_nst = g.nst;
+                i_k0 = g.lo;
+                i_seq = g.seq;
+                i_gk = g.gk;
+                i_page = -1;
+                if (!PAGED) {
+                    const int64_t kvh = ((int64_t)g.b * a.Hkv + g.gk) * a.Sk * DR;
+                    ikrs = make_rsrc(static_cast<const float*>(a.k) + kvh, head_bytes);
+                    ivrs = make_rsrc(static_cast<const float*>(a.v) + kvh, head_bytes);
+                }
+                return;
+            }
+        }
+    };
+    int issued = 0;
+    auto issue_next = [&]() {
+        uint16_t* st = reinterpret_cast<uint16_t*>(ring + (issued % L::NS) * L::STAGE);
+        uint32_t base;
+        if (PAGED) {
+            const int lp = i_k0 / p.page_size;
+            if (lp != i_page) {
+                i_page = lp;
+                const int pg = lp < p.max_pages ? meta.tables[(int64_t)i_seq * p.max_pages + lp] : -1;
+                const bool ok = pg >= 0 && pg < p.pages;
+                const int64_t off = ok ? (int64_t)pg * p.page_size * a.Hkv * DR : 0;
+                ikrs = make_rsrc(static_cast<const float*>(a.k) + off, ok ? page_bytes : 0u);
+                ivrs = make_rsrc(static_cast<const float*>(a.v) + off, ok ? page_bytes : 0u);
+                valid_bits = ok ? (valid_bits | (1u << (issued & 31))) : (valid_bits & ~(1u << (issued & 31)));
+            } else {
+                const uint32_t prev = (valid_bits >> ((issued - 1) & 31)) & 1u;
+                valid_bits = (valid_bits & ~(1u << (issued & 31))) | (prev << (issued & 31));
+            }
+            base = ((uint32_t)(i_k0 % p.page_size) * a.Hkv + i_gk) * DR * 4;
+        } else {
+            base = (uint32_t)i_k0 * DR * 4;
+        }
+        const uint32_t vb = PAGED ? 0u : base, sb = PAGED ? base : 0u;
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, koff[i] + vb, sb);
+#pragma unroll
+        for (int i = 0; i < L::DMA; ++i) dma16(ivrs, st + 2 * L::TILE + 512 * i, voff[i] + vb, sb);
+        ++issued;
+        if (++i_st < i_nst)
+            i_k0 += kStep;
+        else
+            seek(i_it + kDecWaves);
+    };
+    seek(it0);
+    for (int j = 0; j < L::NS - 1 && i_it < it1; ++j) issue_next();
+
+    // K operand reads: row col, logical chunk CG*grp + u (dims (D/4) grp + 4u ..).
+    int krd[L::CG];
+#pragma unroll
+    for (int u = 0; u < L::CG; ++u) krd[u] = col * D + (((L::CG * grp + u) ^ L::fk(col)) * 4);
+
+    f32x4 qf[L::CG];
+    int q_head = -1;
+    int done = 0;
+    for (int it = it0; it < it1; it += kDecWaves) {
+        const Item g = item_geo<PAGED>(a, p, meta, it, G, nqc, chunk);
+        const int64_t prow0 = ((int64_t)g.b * a.Hq + g.h0) * a.splits + g.split;
+        if (g.nst == 0) {
+            if (col < g.nh) {
+                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * DR;
+#pragma unroll
+                for (int dh = 0; dh < D / 64; ++dh)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int d0 = 16 * grp + 4 * j + 64 * dh;
+                        if (d0 < DR) *reinterpret_cast<f32x4*>(op + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                if (grp == 0) a.lse_part[prow0 + (int64_t)col * a.splits] = -INFINITY;
+            }
+            continue;
+        }
+        const int head = g.b * a.Hq + g.h0;
+        if (head != q_head) {
+            const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+                static_cast<const float*>(a.q) + (int64_t)head * DR, (uint32_t)g.nh * DR * 4);
+#pragma unroll
+            for (int u = 0; u < L::CG; ++u) {
+                const int d0 = (D / 4) * grp + 4 * u;
+                qf[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      qrs, d0 < DR ? (col * DR + d0) * 4 : kOut, 0, 0));
+            }
+#pragma unroll
+            for (int u = 0; u < L::CG; ++u) asm volatile("" ::"v"(qf[u]));
+            q_head = head;
+        }
+
+        f32x4 oacc[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.f;
+
+        for (int st = 0; st < g.nst; ++st, ++done) {
+            if (i_it < it1) issue_next();
+            const int ahead = issued - done - 1;
+            if (L::NS == 4 && ahead >= 3)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L::OPS) : "memory");
+            else if (L::NS == 4 && ahead == 2)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L::OPS) : "memory");
+            else if (ahead >= 1)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::OPS) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+            const float* stg = ring + (done % L::NS) * L::STAGE;
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < L::CG; ++u) {
+                const f32x4 kv = __builtin_bit_cast(
+                    f32x4, lds_read128(reinterpret_cast<const uint16_t*>(stg + krd[u])));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qf[u][e], s, 0, 0, 0);
+            }
+            const int k0 = g.lo + kStep * st;
+            if (k0 + kStep > g.hi) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + 4 * grp + i >= g.hi) s[i] = -INFINITY;
+            }
+            if (PAGED && !((valid_bits >> (done & 31)) & 1u)) s = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            f32x4 pw;
+            auto weights = [&]() -> float {
+                const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pw[i] = fast_exp2(fmaf(s[i], c, neg));
+                return (pw[0] + pw[1]) + (pw[2] + pw[3]);
+            };
+            float ps = weights();
+            if (__any(ps > 256.f || m_run == -INFINITY)) {
+                float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = max_half_waves(mx);
+                if (__any(mx > m_run + tau)) {
+                    const float m_new = fmaxf(m_run, mx);
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    const float alpha = fast_exp2((m_run - m_use) * c);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                }
+                ps = weights();
+            }
+            l_run += ps;
+            // V row of key 4*grp + i, runs 16h + col (dims 64h + 4col ..).
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* vrow = stg + L::TILE + (4 * grp + i) * D + 4 * col;
+#pragma unroll
+                for (int dh = 0; dh < D / 64; ++dh) {
+                    const f32x4 vv = __builtin_bit_cast(
+                        f32x4, lds_read128(reinterpret_cast<const uint16_t*>(vrow + 64 * dh)));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        oacc[4 * dh + e] =
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(vv[e], pw[i], oacc[4 * dh + e], 0, 0, 0);
+                }
+            }
+        }
+
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        if (col < g.nh) {
+            const int64_t prow = prow0 + (int64_t)col * a.splits;
+            float* op = a.o_part + prow * DR;
+            const bool empty = m_run == -INFINITY;  // every key masked (paged: invalid pages only)
+            const float inv = empty ? 0.f : 1.f / l_run;
+            // O^T register j of tile 4 dh + e: dim 16 grp + 4 j + e + 64 dh.
+#pragma unroll
+            for (int dh = 0; dh < D / 64; ++dh)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d0 = 16 * grp + 4 * j + 64 * dh;
+                    if (d0 < DR)
+                        *reinterpret_cast<f32x4*>(op + d0) =
+                            f32x4{oacc[4 * dh][j] * inv, oacc[4 * dh + 1][j] * inv,
+                                  oacc[4 * dh + 2][j] * inv, oacc[4 * dh + 3][j] * inv};
+                }
+            if (grp == 0) a.lse_part[prow] = empty ? -INFINITY : m_run * a.scale + __logf(l_run);
+        }
+    }
+}
+
+// Merge of fp32 partials into an fp32 output (4 dims per thread).
+template <int D, bool GEN = false>
+__global__ __launch_bounds__(256) void decode_merge_f32_kernel(DecodeArgs a) {
+    constexpr int TPR = D / 4;
+    constexpr int RPB = 256 / TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int d4 = threadIdx.x % TPR;
+    const int DR = GEN ? a.Dv : D;
+    if (row >= (int64_t)a.B * a.Hq || 4 * d4 >= DR) return;
+    const float* lse = a.lse_part + row * a.splits;
+    const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * DR) + d4;
+    float M = -INFINITY;
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, lse[s]);
+    float den = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.splits; ++s) {
+        const float w = fast_exp2((lse[s] - M) * kLog2e);
+        den += w;
+        const f32x4 o = op[(int64_t)s * (DR / 4)];
+        acc[0] = fmaf(w, o[0], acc[0]);
+        acc[1] = fmaf(w, o[1], acc[1]);
+        acc[2] = fmaf(w, o[2], acc[2]);
+        acc[3] = fmaf(w, o[3], acc[3]);
+    }
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * DR + 4 * d4) =
+        f32x4{acc[0] / den, acc[1] / den, acc[2] / den, acc[3] / den};
+}
+
 // Compute units of the current device (cached per device).
 hipError_t compute_units(int* n) {
     static std::atomic<int> cache[64];
@@ -607,6 +904,37 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     return hipGetLastError();
 }
 
+template <bool PAGED>
+hipError_t launch_split_and_merge_f32(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
+    if (a.D % 4 != 0 || a.D < 4 || a.D > 128 || a.Dv != a.D) return hipErrorInvalidValue;
+    const int items = (int)decode_work_items(a.B, a.Hq, a.Hkv, a.splits);
+    int cus = 0;
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+    const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    const dim3 sg(wgs), st(kDecThreads), mt(256);
+    const int dpad = a.D <= 64 ? 64 : 128;
+    const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * dpad / 4 + 255) / 256));
+    const int32_t *kl = a.key_lens, *bt = p.block_tables, *sl = p.seq_lens, *qs = p.query_seq,
+                  *qp = p.query_pos;
+    if (a.D == 64) {
+        hipLaunchKernelGGL((decode_split_f32_kernel<64, PAGED>), sg, st, 0, s, a, p, kl, bt, sl, qs, qp, items);
+        hipLaunchKernelGGL((decode_merge_f32_kernel<64>), mgrid, mt, 0, s, a);
+    } else if (a.D == 128) {
+        hipLaunchKernelGGL((decode_split_f32_kernel<128, PAGED>), sg, st, 0, s, a, p, kl, bt, sl, qs, qp, items);
+        hipLaunchKernelGGL((decode_merge_f32_kernel<128>), mgrid, mt, 0, s, a);
+    } else if (dpad == 64) {
+        hipLaunchKernelGGL((decode_split_f32_kernel<64, PAGED, true>), sg, st, 0, s, a, p, kl, bt, sl, qs, qp,
+                           items);
+        hipLaunchKernelGGL((decode_merge_f32_kernel<64, true>), mgrid, mt, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((decode_split_f32_kernel<128, PAGED, true>), sg, st, 0, s, a, p, kl, bt, sl, qs, qp,
+                           items);
+        hipLaunchKernelGGL((decode_merge_f32_kernel<128, true>), mgrid, mt, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits) {
@@ -617,6 +945,14 @@ int64_t decode_work_items(int64_t B, int64_t Hq, int64_t Hkv, int splits) {
 hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s) {
     return f16 ? launch_split_and_merge<false, F16T>(a, PagedArgs{}, s)
                : launch_split_and_merge<false, Bf16T>(a, PagedArgs{}, s);
+}
+
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
+    return launch_split_and_merge_f32<false>(a, PagedArgs{}, s);
+}
+
+hipError_t launch_paged_f32(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
+    return launch_split_and_merge_f32<true>(a, p, s);
 }
 
 hipError_t launch_paged_16bit(const DecodeArgs& a, const PagedArgs& p, bool f16, hipStream_t s) {

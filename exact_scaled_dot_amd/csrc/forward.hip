@@ -688,8 +688,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
 // ---------------------------------------------------------------------------
 // GEN: rows are DR = a.D floats in memory (a multiple of 4 below D); the
 // 16-byte chunks past DR load as zeros and are never stored.
-template <int D, bool GEN = false>
-__global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a) {
+// PAGED: prefill chunks over fp32 page caches, with the row, position and
+// page-table conventions of the 16-bit paged prefill above (each key row of a
+// tile looks up its page; a table entry outside the cache is never read and
+// its keys are hidden).
+template <int D, bool GEN = false, bool PAGED = false>
+__global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
+    ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
     constexpr int RS = D + 4;  // row stride in LDS (floats), 16 B of padding
     __shared__ __attribute__((aligned(16))) float ks[kBc * RS];
     __shared__ __attribute__((aligned(16))) float vs[kBc * RS];
@@ -702,17 +708,42 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
 
     const TileInfo ti = decode_tile(a);
     const int DR = GEN ? a.D : D;
-    const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
-    const float* qp = static_cast<const float*>(a.q) + bh * a.Sq * DR;
-    const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * DR;
-    const float* kp = static_cast<const float*>(a.k) + kvh;
-    const float* vp = static_cast<const float*>(a.v) + kvh;
-    float* op = static_cast<float*>(a.out) + bh * a.Sq * DR;
+    const float* qp;
+    const float* kp;
+    const float* vp;
+    float* op;
+    int64_t rstride;  // floats between consecutive query (and output) rows
+    int nrows, qoff, kv_lim, kv_end;
+    if (PAGED) {
+        const int r0 = min(max(cu_q[ti.b], 0), p.total_q);
+        const int r1 = min(max(cu_q[ti.b + 1], r0), p.total_q);
+        nrows = r1 - r0;
+        if (ti.q0 >= nrows) return;  // the whole workgroup: no barrier reached yet
+        kv_lim = min(seq_lens[ti.b], a.Sk);
+        qoff = kv_lim - nrows;
+        kv_end = kv_lim;
+        if (a.causal) kv_end = min(kv_end, qoff + ti.q0 + kBr);
+        const int64_t rb = ((int64_t)r0 * a.Hq + ti.h) * DR;
+        qp = static_cast<const float*>(a.q) + rb;
+        op = static_cast<float*>(a.out) + rb;
+        rstride = (int64_t)a.Hq * DR;
+        kp = static_cast<const float*>(a.k);
+        vp = static_cast<const float*>(a.v);
+    } else {
+        const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
+        qp = static_cast<const float*>(a.q) + bh * a.Sq * DR;
+        const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * DR;
+        kp = static_cast<const float*>(a.k) + kvh;
+        vp = static_cast<const float*>(a.v) + kvh;
+        op = static_cast<float*>(a.out) + bh * a.Sq * DR;
+        rstride = DR;
+        nrows = a.Sq;
+        qoff = 0;
+        key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
+    }
 
     const int qw = ti.q0 + wave * 32;
     const int qi = qw + l32;
-    int kv_lim, kv_end;
-    key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
     const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
 
     // Contraction slot (step t, lane half hg) <-> dim 8*(t/4) + 4*hg + t%4, so a
@@ -721,8 +752,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
 #pragma unroll
     for (int T = 0; T < D / 8; ++T) {
         qf[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (qi < a.Sq && 8 * T + 4 * hg < DR)
-            qf[T] = *reinterpret_cast<const f32x4*>(qp + (int64_t)qi * DR + 8 * T + 4 * hg);
+        if (qi < nrows && 8 * T + 4 * hg < DR)
+            qf[T] = *reinterpret_cast<const f32x4*>(qp + (int64_t)qi * rstride + 8 * T + 4 * hg);
     }
 
     f32x16 oacc[D / 32];
@@ -740,7 +771,18 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
             const int row = cidx / (D / 4), cc = cidx % (D / 4);
             const int key = j0 + row;
             f32x4 wk = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
-            if (key < a.Sk && 4 * cc < DR) {
+            if (PAGED) {
+                // Key rows of invalid pages load zeros; the mask below hides them.
+                const int lp = key / p.page_size;
+                const int pg = (key < kv_lim && lp < p.max_pages)
+                                   ? tables[(int64_t)ti.b * p.max_pages + lp] : -1;
+                if (pg >= 0 && pg < p.pages && 4 * cc < DR) {
+                    const int64_t off =
+                        (((int64_t)pg * p.page_size + key % p.page_size) * a.Hkv + ti.gk) * DR + cc * 4;
+                    wk = *reinterpret_cast<const f32x4*>(kp + off);
+                    wv = *reinterpret_cast<const f32x4*>(vp + off);
+                }
+            } else if (key < a.Sk && 4 * cc < DR) {
                 wk = *reinterpret_cast<const f32x4*>(kp + (int64_t)key * DR + cc * 4);
                 wv = *reinterpret_cast<const f32x4*>(vp + (int64_t)key * DR + cc * 4);
             }
@@ -748,7 +790,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
             *reinterpret_cast<f32x4*>(vs + row * RS + cc * 4) = wv;
         }
         __syncthreads();
-        if (a.causal && j0 > qw + 31) continue;
+        if (a.causal && j0 > qoff + qw + 31) continue;
 
         // S^T: register r of sacc[kb2] holds key j0 + 32*kb2 + 8*(r/4) + 4*hg + r%4.
         f32x16 sacc[2];
@@ -765,14 +807,27 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
             }
         }
 
-        const bool need_mask = (a.causal && j0 + kBc - 1 > qw) || (j0 + kBc > kv_lim);
+        // Paged: bit g says keys j0 + 16g .. +15 (one page: page sizes are
+        // multiples of 16) come from a valid page.
+        int vmask = 15;
+        if (PAGED) {
+            vmask = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int key = j0 + 16 * g, lp = key / p.page_size;
+                const int pg = (key < kv_lim && lp < p.max_pages) ? tables[(int64_t)ti.b * p.max_pages + lp] : -1;
+                vmask |= (pg >= 0 && pg < p.pages) ? (1 << g) : 0;
+            }
+        }
+        const bool need_mask = (a.causal && j0 + kBc - 1 > qoff + qw) || (j0 + kBc > kv_lim) || vmask != 15;
         if (need_mask) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + 32 * kb2 + 8 * (r >> 2) + 4 * hg + (r & 3);
-                    const bool hide = key >= kv_lim || (a.causal && key > qi);
+                    const int kt = 32 * kb2 + 8 * (r >> 2) + 4 * hg + (r & 3), key = j0 + kt;
+                    const bool hide = key >= kv_lim || (a.causal && key > qoff + qi) ||
+                                      !((vmask >> (kt >> 4)) & 1);
                     if (hide) sacc[kb2][r] = -INFINITY;
                 }
         }
@@ -829,8 +884,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(ForwardArgs a)
 
     const float lt = l_run + swap_half_wave(l_run);
     const float inv = 1.f / lt;
-    if (qi < a.Sq) {
-        float* orow = op + (int64_t)qi * DR;
+    if (qi < nrows) {
+        float* orow = op + (int64_t)qi * rstride;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -937,17 +992,28 @@ hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, 
     return f16 ? launch_16bit<true, F16T>(a, p, s) : launch_16bit<true, Bf16T>(a, p, s);
 }
 
-hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s) {
-    if (a.D % 4 != 0 || a.D < 4 || a.D > 128) return hipErrorInvalidValue;
+template <bool PAGED>
+hipError_t launch_f32(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
+    if (a.D % 4 != 0 || a.D < 4 || a.D > 128 || a.Dv != a.D) return hipErrorInvalidValue;
+    const dim3 g = forward_grid(a), t(kThreads);
+    const int32_t *bt = p.block_tables, *sl = p.seq_lens, *cu = p.cu_seqlens_q;
     if (a.D == 64)
-        hipLaunchKernelGGL(forward_f32_kernel<64>, forward_grid(a), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((forward_f32_kernel<64, false, PAGED>), g, t, 0, s, a, p, bt, sl, cu);
     else if (a.D == 128)
-        hipLaunchKernelGGL(forward_f32_kernel<128>, forward_grid(a), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((forward_f32_kernel<128, false, PAGED>), g, t, 0, s, a, p, bt, sl, cu);
     else if (a.D < 64)
-        hipLaunchKernelGGL((forward_f32_kernel<64, true>), forward_grid(a), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((forward_f32_kernel<64, true, PAGED>), g, t, 0, s, a, p, bt, sl, cu);
     else
-        hipLaunchKernelGGL((forward_f32_kernel<128, true>), forward_grid(a), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((forward_f32_kernel<128, true, PAGED>), g, t, 0, s, a, p, bt, sl, cu);
     return hipGetLastError();
+}
+
+hipError_t launch_forward_f32(const ForwardArgs& a, hipStream_t s) {
+    return launch_f32<false>(a, PagedArgs{}, s);
+}
+
+hipError_t launch_paged_prefill_f32(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
+    return launch_f32<true>(a, p, s);
 }
 
 }  // namespace sdpa

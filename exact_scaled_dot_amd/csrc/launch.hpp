@@ -97,6 +97,8 @@ hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, b
 // (launch_paged_prefill_wide).
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
                                       hipStream_t s);
+// fp32 paged prefill chunks (D a multiple of 4 up to 128, Dv = D).
+hipError_t launch_paged_prefill_f32(const ForwardArgs& a, const PagedArgs& p, hipStream_t s);
 // C = A . B (16-bit, fp32 accumulation) for the attention block's
 // projections.  a_heads: A [M = B*S, K = model] is read from (batch, head,
 // seq, headDim) layout; c_heads: C [M, N = model] is written to it (headDim
@@ -129,6 +131,10 @@ hipError_t launch_decode_16bit(const DecodeArgs& a, bool f16, hipStream_t s);
 // the narrow split pass.
 hipError_t launch_decode_wide_split(const DecodeArgs& a, const PagedArgs* p, bool f16, hipStream_t s);
 hipError_t launch_paged_16bit(const DecodeArgs& a, const PagedArgs& p, bool f16, hipStream_t s);
+// fp32 inputs (D a multiple of 4 up to 128, Dv = D): the same split pass and
+// merge on fp32 MFMAs.
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_paged_f32(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
 
 // Work items of the decode split pass: (batch, K/V head, block of <= 16 query
 // heads, split).

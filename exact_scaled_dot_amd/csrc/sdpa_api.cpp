@@ -613,8 +613,6 @@ sdpa_status_t decode_impl(const void* q, const void* k, const void* v, int64_t B
     } else if (overlap(out, qbytes, workspace, (int64_t)need)) {
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps the workspace");
     }
-    if (dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "decode supports bf16 and fp16 only");
     const int64_t items = sdpa::decode_work_items(B, Hq, Hkv, num_splits);
     if (items > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "too many decode work items (%lld)", (long long)items);
@@ -642,7 +640,9 @@ sdpa_status_t decode_impl(const void* q, const void* k, const void* v, int64_t B
     a.scale = scale;
     (void)hipGetLastError();
     const hipError_t e =
-        sdpa::launch_decode_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
+        dtype == SDPA_F32
+            ? sdpa::launch_decode_f32(a, static_cast<hipStream_t>(stream))
+            : sdpa::launch_decode_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
     return hip_status(e, noalloc ? "sdpa_decode_noalloc launch" : "sdpa_decode launch");
 }
 
@@ -724,10 +724,10 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
         max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
     if (!head_dim_ok(D, dtype, 1024))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 1024)",
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "head dim D=%lld not supported (16-bit: a multiple of 8 up to 1024; fp32: a "
+                    "multiple of 4 up to 128)",
                     (long long)D);
-    if (dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "paged attention supports bf16 and fp16 only");
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
     if (page_size % 16 != 0)
@@ -769,7 +769,9 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     p.causal = causal != 0;
     (void)hipGetLastError();
     const hipError_t e =
-        sdpa::launch_paged_16bit(a, p, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
+        dtype == SDPA_F32
+            ? sdpa::launch_paged_f32(a, p, static_cast<hipStream_t>(stream))
+            : sdpa::launch_paged_16bit(a, p, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
     return hip_status(e, "sdpa_paged_attention launch");
 }
 
@@ -822,10 +824,10 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
     if (!head_dim_ok(D, dtype, 1024))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (a multiple of 8 up to 1024)",
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "head dim D=%lld not supported (16-bit: a multiple of 8 up to 1024; fp32: a "
+                    "multiple of 4 up to 128)",
                     (long long)D);
-    if (dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "paged prefill supports bf16 and fp16 only");
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
     if (page_size % 16 != 0)
@@ -867,8 +869,10 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     p.total_q = (int)total_q;
     p.causal = causal != 0;
     (void)hipGetLastError();
-    const hipError_t e = sdpa::launch_paged_prefill_16bit(a, p, dtype == SDPA_F16,
-                                                          static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        dtype == SDPA_F32
+            ? sdpa::launch_paged_prefill_f32(a, p, static_cast<hipStream_t>(stream))
+            : sdpa::launch_paged_prefill_16bit(a, p, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
     return hip_status(e, "sdpa_paged_prefill launch");
 }
 

@@ -110,7 +110,8 @@ def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1,
     (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),   # the widest decode is 1024
-    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),  # fp32: up to 128
+    (dict(D=66, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # fp32: multiples of 4
 ])
 def test_decode_rejects(kw, status, needle):
     assert dec(**kw) == status
@@ -131,7 +132,7 @@ def dec_noalloc(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, sc
     (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
     (dict(out=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=84), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     # partials of 128 x 32 heads x 32 splits x 128 dims = 64 MiB + the lse section: one byte
     # section past the scratch, so nothing is launched
     (dict(B=128, Hq=32, Hkv=8, splits=32), sd.SDPA_ERR_WORKSPACE, "scratch"),
@@ -206,7 +207,8 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, Dv=None, pages=1
     (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
     (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),
+    (dict(D=64, Dv=128, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
     (dict(Dv=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
     (dict(Dv=100), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
@@ -245,7 +247,7 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pag
     (dict(max_seq_len=801), sd.SDPA_ERR_INVALID_ARGUMENT, "capacity"),
     (dict(out=ctypes.c_void_p(0x7e000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
-    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "bf16"),
+    (dict(D=136, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
     (dict(Dv=-3), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
     (dict(Dv=60), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
