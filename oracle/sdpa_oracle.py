@@ -64,6 +64,9 @@ reordered:
   block_tables[s][j // page_size], slot j % page_size; with the causal flag
   key j is visible only when j <= query_pos[t] (absolute positions, so a
   chunk of new queries at the end of a sequence is aligned bottom-right).
+  Its backward (ruDNN user guide section 11) gives dq and the gradients of
+  the cache slots: each logical key's contribution is added into the slot it
+  sits in, unreached slots get 0.
 
 A row with no visible key has 0/0 weights and yields NaN, the literal result
 of the essay's normalisation (ruDNN user guide section 4 likewise keeps NaN
@@ -464,6 +467,63 @@ def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq, quer
     return o
 
 
+def paged_attention_backward(q, k_cache, v_cache, dout, block_tables, seq_lens, query_seq,
+                             query_pos, scale, causal):
+    """Gradients of L with dL/dO = dout through paged_attention (ruDNN user
+    guide section 11: the paged plan's attention backward returns dq and the
+    history gradients dk, dv, recomputing the probabilities).
+
+    q [queries, Hq, D], dout [queries, Hq, Dv]; k_cache [pages, page_size,
+    Hkv, D], v_cache [.., Dv].  Per query t and head h, with ks, vs the keys
+    and values its sequence reaches through its page table (paged_gather) and
+    p the softmax of the visible scaled scores: dv_j += p_j dout, dp_j =
+    dout . vs_j, ds_j = p_j (dp_j - dout . o), dq = scale sum_j ds_j ks_j,
+    dk_j += scale ds_j q.  The cache gradients are added into the physical
+    slot each logical key j sits in (a slot reached twice gets both
+    contributions); slots no visible key reaches get 0.  Returns (dq,
+    dk_cache, dv_cache) in fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    nq, Hq, D = q.shape
+    pages, page_size, Hkv, Dk = k_cache.shape
+    Dv = v_cache.shape[3]
+    if Dk != D or v_cache.shape[:3] != k_cache.shape[:3] or dout.shape != (nq, Hq, Dv):
+        raise ValueError("inconsistent q / cache / dout shapes")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k_cache)
+    dv = np.zeros_like(v_cache)
+    for t in range(nq):
+        s_id, pos = int(query_seq[t]), int(query_pos[t])
+        length = int(seq_lens[s_id])
+        table_row = np.asarray(block_tables[s_id], dtype=np.int64)
+        j = np.arange(length, dtype=np.int64)
+        page, slot = table_row[j // page_size], j % page_size
+        ks = k_cache[page, slot]               # [length, Hkv, D]
+        vs = v_cache[page, slot]
+        vis = np.ones((1, length), dtype=bool)
+        if causal:
+            vis &= (j <= pos)[None, :]
+        for h in range(Hq):
+            g = h // G
+            o, lse, p = attend(q[t, h:h + 1], ks[:, g], vs[:, g], scale, vis)
+            if not np.isfinite(lse[0]):
+                continue                       # no visible key: no output, no gradient
+            p = p[0]
+            do = dout[t, h]
+            dp = vs[:, g] @ do
+            ds = p * (dp - float(do @ o[0]))
+            dq[t, h] = float(scale) * (ds @ ks[:, g])
+            np.add.at(dk, (page, slot, g), float(scale) * ds[:, None] * q[t, h][None, :])
+            np.add.at(dv, (page, slot, g), p[:, None] * do[None, :])
+    return dq, dk, dv
+
+
 def chunk_positions(cu_seqlens_q, seq_lens):
     """Sequence and absolute position of every packed query of a prefill chunk.
 
@@ -488,5 +548,5 @@ __all__ = [
     "sdpa_forward", "sdpa_forward_rows", "sdpa_decode", "split_ranges",
     "decode_split_partials", "merge_partials", "paged_gather", "paged_attention",
     "chunk_positions", "sdpa_backward", "bias_slice", "split_heads", "merge_heads",
-    "block_forward", "block_forward_rows",
+    "block_forward", "block_forward_rows", "paged_attention_backward",
 ]

@@ -662,6 +662,73 @@ def test_backward_matches_finite_differences(mask, lens):
         np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=name)
 
 
+def _paged_loss(q, kc, vc, g, tables, lens, qs, qp, scale, causal):
+    return float((O.paged_attention(q, kc, vc, tables, lens, qs, qp, scale, causal) * g).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_paged_backward_matches_finite_differences(causal):
+    # two sequences over 7 physical pages of 2 slots; physical page 3 is in
+    # both tables (its slots get both sequences' contributions), pages 5 and
+    # 6 are unreached (zero gradient); Dv != D
+    rng = np.random.default_rng(71 + causal)
+    Hq, Hkv, D, Dv, ps = 2, 1, 3, 2, 2
+    kc, vc = rng.standard_normal((7, ps, Hkv, D)), rng.standard_normal((7, ps, Hkv, Dv))
+    tables = np.array([[0, 3, 1], [2, 3, 4]])
+    lens = np.array([5, 6])
+    qs, qp = np.array([0, 0, 1, 1, 1]), np.array([4, 2, 5, 0, 3])
+    q = rng.standard_normal((5, Hq, D))
+    g = rng.standard_normal((5, Hq, Dv))
+    dq, dk, dv = O.paged_attention_backward(q, kc, vc, g, tables, lens, qs, qp, 0.9, causal)
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", kc, dk), ("v", vc, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args_p = {"q": q, "k": kc, "v": vc}
+            args_m = dict(args_p)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_paged_loss(args_p["q"], args_p["k"], args_p["v"], g, tables, lens, qs, qp,
+                                    0.9, causal)
+                        - _paged_loss(args_m["q"], args_m["k"], args_m["v"], g, tables, lens, qs, qp,
+                                      0.9, causal)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=name)
+    assert not dk[5:].any() and not dv[5:].any()
+    assert np.abs(dk[3]).sum() > 0
+
+
+def test_paged_backward_equals_dense_backward_of_each_sequence():
+    # whole-sequence causal chunks over shuffled pages: dq rows and the cache
+    # slots' gradients are the dense causal backward of each sequence
+    rng = np.random.default_rng(73)
+    lens = [9, 4, 7]
+    nseq, Hq, Hkv, D, S, ps = len(lens), 4, 2, 3, max(lens), 2
+    q = rng.standard_normal((nseq, Hq, S, D))
+    k = rng.standard_normal((nseq, Hkv, S, D))
+    v = rng.standard_normal((nseq, Hkv, S, D))
+    g = rng.standard_normal((nseq, Hq, S, D))
+    kc, vc, tables = make_paged(k, v, lens, ps, 2, rng)
+    qs = np.array([s for s in range(nseq) for _ in range(lens[s])])
+    qp = np.array([i for s in range(nseq) for i in range(lens[s])])
+    qq = np.stack([q[s, :, i] for s, i in zip(qs, qp)])
+    gg = np.stack([g[s, :, i] for s, i in zip(qs, qp)])
+    dq, dk, dv = O.paged_attention_backward(qq, kc, vc, gg, tables, lens, qs, qp, 0.6, True)
+    reached = np.zeros(kc.shape[:2], dtype=bool)
+    for s in range(nseq):
+        n = lens[s]
+        rq, rk, rv = O.sdpa_backward(q[s:s + 1, :, :n], k[s:s + 1, :, :n], v[s:s + 1, :, :n],
+                                     g[s:s + 1, :, :n], 0.6, O.MASK_CAUSAL)
+        np.testing.assert_allclose(dq[qs == s], rq[0].transpose(1, 0, 2), rtol=0, atol=1e-12)
+        for j in range(n):
+            pg, sl = tables[s, j // ps], j % ps
+            reached[pg, sl] = True
+            np.testing.assert_allclose(dk[pg, sl], rk[0][:, j], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dv[pg, sl], rv[0][:, j], rtol=0, atol=1e-12)
+    assert not dk[~reached].any() and not dv[~reached].any()
+
+
 def test_backward_key_gradients_sum_to_zero():
     # each row of dS sums to 0 (softmax is shift invariant), so the dK rows of
     # a K/V head sum to the zero vector
