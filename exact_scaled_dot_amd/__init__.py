@@ -10,5 +10,6 @@ from .sdpa import (  # noqa: F401
     SdpaError, decode_workspace_views, last_error, load_library, sdpa_backward, sdpa_backward_bias,
     sdpa_backward_atomic_workspace_size, sdpa_backward_workspace_size, sdpa_block_forward,
     sdpa_block_workspace_size, sdpa_decode, sdpa_decode_noalloc, sdpa_decode_workspace_size, sdpa_forward,
-    sdpa_forward_bias, sdpa_forward_lse, sdpa_paged_attention, sdpa_paged_prefill, status_string,
+    sdpa_forward_bias, sdpa_forward_lse, sdpa_paged_attention, sdpa_paged_backward,
+    sdpa_paged_backward_workspace_size, sdpa_paged_prefill, status_string,
 )

@@ -234,12 +234,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     const uint16_t* qbase;
     uint16_t* op;
     int nrows, qoff, kv_lim, kv_end;
+    int r0 = 0;        // paged: first packed row of the chunk
     uint32_t qstride;  // bytes between consecutive query rows
     uint32_t ostride;  // bytes between consecutive output rows
     if (PAGED) {
         // This workgroup's rows of sequence b's chunk (bounds clamped to the
         // packed rows so no store can leave out).
-        const int r0 = min(max(cu_q[ti.b], 0), p.total_q);
+        r0 = min(max(cu_q[ti.b], 0), p.total_q);
         const int r1 = min(max(cu_q[ti.b + 1], r0), p.total_q);
         nrows = r1 - r0;
         if (ti.q0 >= nrows) return;  // the whole workgroup: no barrier reached yet
@@ -639,8 +640,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     // Optional log-sum-exp of the row (natural log, scaled-score units) for
     // the backward: the reference max plus ln of the denominator; -inf for a
     // row with no visible key.
-    if (!PAGED && a.lse && hg == 0 && qi < nrows && dv0 == 0)
-        a.lse[((int64_t)ti.b * a.Hq + ti.h) * a.Sq + qi] =
+    // (Dense: lse [B, Hq, Sq]; paged: [packed rows, Hq].)
+    if (a.lse && hg == 0 && qi < nrows && dv0 == 0)
+        a.lse[PAGED ? (int64_t)(r0 + qi) * a.Hq + ti.h : ((int64_t)ti.b * a.Hq + ti.h) * a.Sq + qi] =
             m_run == -INFINITY ? -INFINITY : m_run * a.scale + __logf(lt);
     if (stream_q_o) {
         // The wave's 32 output rows go through LDS (free: every wave has passed

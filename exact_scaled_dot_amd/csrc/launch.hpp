@@ -121,6 +121,39 @@ hipError_t launch_gemm_16bit(const GemmArgs& g, bool f16, hipStream_t s);
 
 // Backward: the dQ pass (also writes delta), then the dK / dV pass.
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s);
+
+// Attention backward through a page cache (packed prefill chunks of the paged
+// forward): gathers into the dense sections, the dense ordered backward,
+// scatters back.  Sizes: L = max_seq_len; D = Dv, a multiple of 8.
+struct PagedBackwardArgs {
+    const void* q;          // [total_q, Hq, D]
+    const void* k_cache;    // [pages, page_size, Hkv, D]
+    const void* v_cache;
+    const void* out;        // [total_q, Hq, D], the forward's output
+    const void* dout;
+    const float* lse;       // [total_q, Hq], the forward's log-sum-exp
+    void* dq;               // [total_q, Hq, D]
+    void* dk_cache;         // [pages, page_size, Hkv, D]
+    void* dv_cache;
+    const int32_t* block_tables;  // [num_seqs, max_pages]
+    const int32_t* seq_lens;      // [num_seqs]
+    const int32_t* cu_seqlens_q;  // [num_seqs + 1]
+    int total_q, Hq, Hkv, D, num_seqs, max_pages, pages, page_size, L;
+    float scale;
+    bool causal;
+    // workspace sections
+    void* qd;    // [num_seqs, Hq, L, D] each: Q, dO, O and dQ at absolute positions
+    void* dod;
+    void* od;
+    void* dqd;
+    void* kd;    // [num_seqs, Hkv, L, D] each: K, V, dK, dV of the reachable keys
+    void* vd;
+    void* dkd;
+    void* dvd;
+    float* lsed;   // [num_seqs, Hq, L]
+    float* stats;  // the dense backward's workspace
+};
+hipError_t launch_paged_backward_16bit(const PagedBackwardArgs& a, bool f16, hipStream_t s);
 // Ordered backward without a bias for 128 < D <= 512 (head dim split across waves).
 hipError_t launch_backward_wide(const BackwardArgs& a, bool f16, hipStream_t s);
 

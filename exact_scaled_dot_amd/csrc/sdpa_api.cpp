@@ -781,7 +781,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                                  int64_t page_size, const int32_t* block_tables, int64_t num_seqs,
                                  int64_t max_pages_per_seq, const int32_t* seq_lens,
                                  const int32_t* cu_seqlens_q, int64_t max_q, int64_t max_seq_len,
-                                 float scale, int causal, void* out, int dtype, void* stream) {
+                                 float scale, int causal, void* out, float* lse, int dtype,
+                                 void* stream) {
     if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !cu_seqlens_q)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null pointer argument");
     if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || pages < 1 || page_size < 1 ||
@@ -820,6 +821,12 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
         overlap(out, obytes, seq_lens, num_seqs * 4) ||
         overlap(out, obytes, cu_seqlens_q, (num_seqs + 1) * 4))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    const int64_t lbytes = lse ? numel4(total_q, Hq, 4, 1) : 0;
+    if (lse && (overlap(lse, lbytes, out, obytes) || overlap(lse, lbytes, q, qbytes) ||
+                overlap(lse, lbytes, k_cache, cbytes) || overlap(lse, lbytes, v_cache, vcbytes) ||
+                overlap(lse, lbytes, block_tables, nt * 4) || overlap(lse, lbytes, seq_lens, num_seqs * 4) ||
+                overlap(lse, lbytes, cu_seqlens_q, (num_seqs + 1) * 4)))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "lse overlaps out or an input");
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
@@ -830,6 +837,9 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
+    if (lse && (dtype == SDPA_F32 || D > 256))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "the log-sum-exp output needs 16-bit inputs and D up to 256");
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
@@ -858,6 +868,7 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     a.scale = scale;
     a.causal = causal != 0;
     a.padded = false;
+    a.lse = lse;
     sdpa::PagedArgs p{};
     p.block_tables = block_tables;
     p.seq_lens = seq_lens;
@@ -874,6 +885,144 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
             ? sdpa::launch_paged_prefill_f32(a, p, static_cast<hipStream_t>(stream))
             : sdpa::launch_paged_prefill_16bit(a, p, dtype == SDPA_F16, static_cast<hipStream_t>(stream));
     return hip_status(e, "sdpa_paged_prefill launch");
+}
+
+size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t Hkv,
+                                          int64_t max_seq_len, int64_t D) {
+    if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || D < 1) return 0;
+    const int64_t rows = numel4(num_seqs, Hq, max_seq_len, D), kv = numel4(num_seqs, Hkv, max_seq_len, D);
+    const int64_t l = numel4(num_seqs, Hq, max_seq_len, 1);
+    if (rows < 0 || kv < 0 || l < 0 || rows > INT64_MAX / 64 || kv > INT64_MAX / 64) return 0;
+    const size_t stats = sdpa_backward_workspace_size(num_seqs, Hq, max_seq_len);
+    if (stats == 0) return 0;
+    return 4 * round_up((size_t)rows * 2) + 4 * round_up((size_t)kv * 2) + round_up((size_t)l * 4) + stats;
+}
+
+sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void* v_cache,
+                                  const void* out, const void* dout, const float* lse,
+                                  int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t pages,
+                                  int64_t page_size, const int32_t* block_tables, int64_t num_seqs,
+                                  int64_t max_pages_per_seq, const int32_t* seq_lens,
+                                  const int32_t* cu_seqlens_q, int64_t max_seq_len, float scale,
+                                  int causal, void* dq, void* dk_cache, void* dv_cache,
+                                  void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !out || !dout || !lse || !block_tables || !seq_lens ||
+        !cu_seqlens_q || !dq || !dk_cache || !dv_cache)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || pages < 1 || page_size < 1 || num_seqs < 1 ||
+        max_pages_per_seq < 1 || max_seq_len < 1)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "every size must be >= 1 (total_q=%lld Hq=%lld Hkv=%lld D=%lld pages=%lld "
+                    "page_size=%lld num_seqs=%lld max_pages_per_seq=%lld max_seq_len=%lld)",
+                    (long long)total_q, (long long)Hq, (long long)Hkv, (long long)D, (long long)pages,
+                    (long long)page_size, (long long)num_seqs, (long long)max_pages_per_seq,
+                    (long long)max_seq_len);
+    if (Hq % Hkv != 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                    (long long)Hq, (long long)Hkv);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if (!known_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (causal != 0 && causal != 1)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+    int64_t cap = 0;
+    if (!mul_ok(max_pages_per_seq, page_size, &cap) || max_seq_len > cap)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "max_seq_len (%lld) exceeds the page table capacity max_pages_per_seq * "
+                    "page_size",
+                    (long long)max_seq_len);
+    const int64_t es = elem_size(dtype);
+    const int64_t nq = numel4(total_q, Hq, D, 1), nc = numel4(pages, page_size, Hkv, D);
+    const int64_t nt = numel4(num_seqs, max_pages_per_seq, 1, 1);
+    int64_t qbytes = 0, cbytes = 0;
+    if (nq < 0 || nc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) || !mul_ok(nc, es, &cbytes))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
+    const size_t need = sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D);
+    if (need == 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    if (!workspace || workspace_bytes < need)
+        return fail(SDPA_ERR_WORKSPACE, "paged backward needs a workspace of %zu bytes (got %zu)",
+                    need, workspace ? workspace_bytes : (size_t)0);
+    // Outputs and the workspace overlap no input and each other.
+    struct Span {
+        const void* p;
+        int64_t n;
+    };
+    const Span ins[] = {{q, qbytes},         {k_cache, cbytes},         {v_cache, cbytes},
+                        {out, qbytes},       {dout, qbytes},            {lse, total_q * Hq * 4},
+                        {block_tables, nt * 4}, {seq_lens, num_seqs * 4}, {cu_seqlens_q, (num_seqs + 1) * 4}};
+    const Span outs[] = {{dq, qbytes}, {dk_cache, cbytes}, {dv_cache, cbytes}, {workspace, (int64_t)need}};
+    for (const Span& o : outs) {
+        for (const Span& i : ins)
+            if (overlap(o.p, o.n, i.p, i.n))
+                return fail(SDPA_ERR_INVALID_ARGUMENT, "an output or the workspace overlaps an input");
+        for (const Span& o2 : outs)
+            if (&o2 != &o && overlap(o.p, o.n, o2.p, o2.n))
+                return fail(SDPA_ERR_INVALID_ARGUMENT, "outputs overlap each other or the workspace");
+    }
+    if (dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "the paged backward needs 16-bit inputs (bf16 or fp16)");
+    if (!head_dim_ok(D, dtype, 256))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "head dim D=%lld not supported by the paged backward (a multiple of 8 up to 256)",
+                    (long long)D);
+    if (page_size % 16 != 0)
+        return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
+                    (long long)page_size);
+    const int64_t rows_chunks = numel4(num_seqs, Hq, max_seq_len, D / 8);
+    const int64_t cache_chunks = numel4(pages, page_size, Hkv, D / 8);
+    const int64_t qblocks = ((max_seq_len + 127) / 128) * num_seqs * Hq;
+    if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
+        max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX || rows_chunks < 0 ||
+        rows_chunks / 256 > INT_MAX || cache_chunks < 0 || cache_chunks / 256 > INT_MAX ||
+        qblocks > INT_MAX / 256)
+        return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
+
+    const size_t rowsz = (size_t)numel4(num_seqs, Hq, max_seq_len, D) * 2;
+    const size_t kvsz = (size_t)numel4(num_seqs, Hkv, max_seq_len, D) * 2;
+    char* w = static_cast<char*>(workspace);
+    auto take = [&](size_t bytes) {
+        char* p = w;
+        w += round_up(bytes);
+        return p;
+    };
+    sdpa::PagedBackwardArgs a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk_cache = dk_cache;
+    a.dv_cache = dv_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.cu_seqlens_q = cu_seqlens_q;
+    a.total_q = (int)total_q;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.D = (int)D;
+    a.num_seqs = (int)num_seqs;
+    a.max_pages = (int)max_pages_per_seq;
+    a.pages = (int)pages;
+    a.page_size = (int)page_size;
+    a.L = (int)max_seq_len;
+    a.scale = scale;
+    a.causal = causal != 0;
+    a.qd = take(rowsz);
+    a.dod = take(rowsz);
+    a.od = take(rowsz);
+    a.dqd = take(rowsz);
+    a.kd = take(kvsz);
+    a.vd = take(kvsz);
+    a.dkd = take(kvsz);
+    a.dvd = take(kvsz);
+    a.lsed = reinterpret_cast<float*>(take((size_t)numel4(num_seqs, Hq, max_seq_len, 4)));
+    a.stats = reinterpret_cast<float*>(w);
+    (void)hipGetLastError();
+    return hip_status(sdpa::launch_paged_backward_16bit(a, dtype == SDPA_F16,
+                                                        static_cast<hipStream_t>(stream)),
+                      "sdpa_paged_backward launch");
 }
 
 }  // extern "C"

@@ -34,7 +34,8 @@ EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_bias", "sdpa_backw
             "sdpa_block_workspace_size",
             "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_decode_noalloc",
             "sdpa_paged_attention",
-            "sdpa_paged_prefill", "sdpa_status_string", "sdpa_last_error")
+            "sdpa_paged_prefill", "sdpa_paged_backward", "sdpa_paged_backward_workspace_size",
+            "sdpa_status_string", "sdpa_last_error")
 
 _lib = None
 
@@ -96,7 +97,13 @@ def load_library():
                                          ctypes.c_size_t, vp, i32, vp]
     lib.sdpa_paged_prefill.restype = i32
     lib.sdpa_paged_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
-                                       vp, i64, i64, ctypes.c_float, i32, vp, i32, vp]
+                                       vp, i64, i64, ctypes.c_float, i32, vp, vp, i32, vp]
+    lib.sdpa_paged_backward_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_paged_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.sdpa_paged_backward.restype = i32
+    lib.sdpa_paged_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp,
+                                        i64, i64, vp, vp, i64, ctypes.c_float, i32, vp, vp, vp, vp,
+                                        ctypes.c_size_t, i32, vp]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_status_string.argtypes = [i32]
     lib.sdpa_last_error.restype = ctypes.c_char_p
@@ -499,14 +506,15 @@ def sdpa_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_seq,
 
 
 def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, scale, causal,
-                       max_q, max_seq_len, out=None, stream=None):
+                       max_q, max_seq_len, out=None, stream=None, lse=False):
     """Packed prefill chunks over a K/V page cache.
 
     q [total_q, Hq, D]; k_cache [pages, page_size, Hkv, D]; v_cache [pages,
     page_size, Hkv, Dv]; block_tables int32 [num_seqs, max_pages_per_seq];
     seq_lens int32 [num_seqs] (the chunk included); cu_seqlens_q int32
     [num_seqs + 1]; max_q, max_seq_len host bounds.  Row i of sequence s's
-    chunk sits at position seq_lens[s] - n_s + i.  Returns out [total_q, Hq, Dv].
+    chunk sits at position seq_lens[s] - n_s + i.  Returns out [total_q, Hq, Dv],
+    or (out, lse fp32 [total_q, Hq]) with lse=True (or an lse tensor to fill).
     """
     _check_tensor("q", q, 3)
     _check_tensor("k_cache", k_cache, 4)
@@ -531,10 +539,67 @@ def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q
         raise ValueError("seq_lens needs num_seqs entries and cu_seqlens_q num_seqs + 1")
     if out is None:
         out = torch.empty((nq, Hq, Dv), dtype=q.dtype, device=q.device)
+    lse_t = None
+    if isinstance(lse, torch.Tensor):
+        _check_tensor("lse", lse, 2)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (nq, Hq):
+            raise ValueError("lse must be float32 [total_q, Hq]")
+        lse_t = lse
+    elif lse:
+        lse_t = torch.empty((nq, Hq), dtype=torch.float32, device=q.device)
     lib = load_library()
     _check(lib.sdpa_paged_prefill(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), nq, Hq, Hkv, D, Dv, pages, page_size,
         _ptr(block_tables),
         num_seqs, max_pages, _ptr(seq_lens), _ptr(cu_seqlens_q), int(max_q), int(max_seq_len),
-        float(scale), int(bool(causal)), _ptr(out), _dtype_code(q), _stream(stream)))
-    return out
+        float(scale), int(bool(causal)), _ptr(out), _ptr(lse_t), _dtype_code(q), _stream(stream)))
+    return out if lse_t is None else (out, lse_t)
+
+
+def sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D):
+    return int(load_library().sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D))
+
+
+def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_lens, cu_seqlens_q,
+                        scale, causal, max_seq_len, dq=None, dk_cache=None, dv_cache=None,
+                        workspace=None, stream=None):
+    """Backward of sdpa_paged_prefill: (dq [total_q, Hq, D], dk_cache,
+    dv_cache [pages, page_size, Hkv, D]) for dL/dout = dout, from the
+    forward's out and lse (fp32 [total_q, Hq])."""
+    for name, t, nd in (("q", q, 3), ("k_cache", k_cache, 4), ("v_cache", v_cache, 4),
+                        ("out", out, 3), ("dout", dout, 3), ("lse", lse, 2),
+                        ("block_tables", block_tables, 2), ("seq_lens", seq_lens, 1),
+                        ("cu_seqlens_q", cu_seqlens_q, 1)):
+        _check_tensor(name, t, nd)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("cu_seqlens_q", cu_seqlens_q)):
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % name)
+    nq, Hq, D = q.shape
+    pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [pages, page_size, Hkv, D] matching q")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must be [total_q, Hq, D]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (nq, Hq):
+        raise ValueError("lse must be float32 [total_q, Hq]")
+    for t in (k_cache, v_cache, out, dout):
+        if t.dtype != q.dtype:
+            raise TypeError("q, the caches, out and dout must share one dtype")
+    num_seqs, max_pages = block_tables.shape
+    if seq_lens.shape[0] != num_seqs or cu_seqlens_q.shape[0] != num_seqs + 1:
+        raise ValueError("seq_lens needs num_seqs entries and cu_seqlens_q num_seqs + 1")
+    lib = load_library()
+    need = int(lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, int(max_seq_len), D))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk_cache = torch.empty_like(k_cache) if dk_cache is None else dk_cache
+    dv_cache = torch.empty_like(v_cache) if dv_cache is None else dv_cache
+    _check(lib.sdpa_paged_backward(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(dout), _ptr(lse), nq, Hq, Hkv, D,
+        pages, page_size, _ptr(block_tables), num_seqs, max_pages, _ptr(seq_lens),
+        _ptr(cu_seqlens_q), int(max_seq_len), float(scale), int(bool(causal)), _ptr(dq),
+        _ptr(dk_cache), _ptr(dv_cache), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _dtype_code(q), _stream(stream)))
+    return dq, dk_cache, dv_cache

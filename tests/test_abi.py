@@ -228,12 +228,13 @@ FAKE_C = ctypes.c_void_p(0x7e000000)
 
 def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pages=100,
             page_size=16, tables=FAKE_T, num_seqs=3, max_pages=50, seq_lens=FAKE_L, cu=FAKE_C,
-            max_q=200, max_seq_len=800, scale=0.1, causal=1, out=FAKE_O, dtype=sd.SDPA_BF16):
+            max_q=200, max_seq_len=800, scale=0.1, causal=1, out=FAKE_O, lse=None,
+            dtype=sd.SDPA_BF16):
     lib = sd.load_library()
     Dv = D if Dv is None else Dv
     return lib.sdpa_paged_prefill(q, k, v, nq, Hq, Hkv, D, Dv, pages, page_size, tables, num_seqs,
                                   max_pages, seq_lens, cu, max_q, max_seq_len, scale, causal, out,
-                                  dtype, None)
+                                  lse, dtype, None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -255,6 +256,9 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pag
     # v_cache spans 100 * 16 * 2 * Dv * 2 bytes: 1 MB in lies inside it only at Dv = 256
     (dict(Dv=256, out=ctypes.c_void_p(0x40000000 + (1 << 20))), sd.SDPA_ERR_INVALID_ARGUMENT,
      "overlaps"),
+    (dict(lse=ctypes.c_void_p(0x60000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
+    (dict(lse=ctypes.c_void_p(0x7f000000), dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "log-sum-exp"),
+    (dict(lse=ctypes.c_void_p(0x7f000000), D=512), sd.SDPA_ERR_UNSUPPORTED, "log-sum-exp"),
 ])
 def test_paged_prefill_rejects(kw, status, needle):
     assert prefill(**kw) == status
@@ -460,3 +464,59 @@ def bwdb(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128,
 def test_backward_bias_rejects(kw, status, needle):
     assert bwdb(**kw) == status
     assert needle in sd.last_error()
+
+
+FAKE_DO = ctypes.c_void_p(0x80000000)
+FAKE_OUT = ctypes.c_void_p(0x90000000)
+FAKE_LSE = ctypes.c_void_p(0xa0000000)
+FAKE_DQ = ctypes.c_void_p(0xb0000000)
+FAKE_DK = ctypes.c_void_p(0xc0000000)
+FAKE_DV = ctypes.c_void_p(0xd0000000)
+FAKE_PW = ctypes.c_void_p(0x100000000)
+
+
+def paged_bwd(q=FAKE, k=FAKE_K, v=FAKE_V, out=FAKE_OUT, dout=FAKE_DO, lse=FAKE_LSE, nq=300, Hq=8,
+              Hkv=2, D=128, pages=100, page_size=16, tables=FAKE_T, num_seqs=3, max_pages=50,
+              seq_lens=FAKE_L, cu=FAKE_C, max_seq_len=800, scale=0.1, causal=1, dq=FAKE_DQ,
+              dk=FAKE_DK, dv=FAKE_DV, ws=FAKE_PW, ws_bytes=None, dtype=sd.SDPA_BF16):
+    lib = sd.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D)
+    return lib.sdpa_paged_backward(q, k, v, out, dout, lse, nq, Hq, Hkv, D, pages, page_size, tables,
+                                   num_seqs, max_pages, seq_lens, cu, max_seq_len, scale, causal,
+                                   dq, dk, dv, ws, ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(dk=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
+    (dict(num_seqs=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(scale=0.0), sd.SDPA_ERR_INVALID_ARGUMENT, "scale"),
+    (dict(causal=3), sd.SDPA_ERR_INVALID_ARGUMENT, "causal"),
+    (dict(max_seq_len=801), sd.SDPA_ERR_INVALID_ARGUMENT, "capacity"),
+    (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=4096), sd.SDPA_ERR_WORKSPACE, "workspace"),
+    (dict(dq=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps an input"),
+    (dict(dv=ctypes.c_void_p(0xc0000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap each other"),
+    (dict(dtype=sd.SDPA_F32, D=64), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(D=512), sd.SDPA_ERR_UNSUPPORTED, "up to 256"),
+    (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
+])
+def test_paged_backward_rejects(kw, status, needle):
+    assert paged_bwd(**kw) == status
+    assert needle in sd.last_error()
+
+
+def test_paged_backward_workspace_size():
+    lib = sd.load_library()
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    S, Hq, Hkv, L, D = 3, 8, 2, 800, 128
+    stats = lib.sdpa_backward_workspace_size(S, Hq, L)
+    want = 4 * up(S * Hq * L * D * 2) + 4 * up(S * Hkv * L * D * 2) + up(S * Hq * L * 4) + stats
+    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, D) == want
+    assert lib.sdpa_paged_backward_workspace_size(0, Hq, Hkv, L, D) == 0
