@@ -176,7 +176,12 @@ __device__ __forceinline__ Item item_geo(const DecodeArgs& a, const PagedArgs& p
 // 16), found through the sequence's page table when the step enters a new
 // page.  A table entry outside [0, pages) is never dereferenced: its keys
 // load as zeros and are masked out.
-template <int D, bool PAGED, class T, bool GEN = false, int DV = D>
+// ELEM (with GEN; head dims that are not multiples of 8): Q, K and V are
+// read one element at a time (2-byte buffer loads into the lanes' 16-byte
+// slots, elements past a row reading as zeros), loaded and written to the
+// ring at issue time; the partials' rows are padded to a multiple of 4
+// floats (DVP) so their 16-byte stores stay aligned.
+template <int D, bool PAGED, class T, bool GEN = false, int DV = D, bool ELEM = false>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     DecodeArgs a, PagedArgs p, const int32_t* __restrict__ key_lens,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     // zeros (offsets outside the buffer) and are never stored.
     const int DR = GEN ? a.D : D;
     const int DVR = GEN ? a.Dv : DV;  // value head dim in memory
+    const int DVP = ELEM ? (DVR + 3) & ~3 : DVR;  // floats per partial row
     constexpr uint32_t kOut = 0x80000000u;  // past any num_records (<= INT_MAX)
     const uint32_t head_bytes = (uint32_t)a.Sk * DR * 2;
     const uint32_t vhead_bytes = (uint32_t)a.Sk * DVR * 2;
@@ -229,18 +235,31 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     // Lane-constant DMA offsets (bytes from the step's first key) and LDS read
     // offsets (elements from the stage start).
     uint32_t koff[L::DMA], voff[LV::DMA];
+    int kvn[ELEM ? L::DMA : 1], vvn[ELEM ? LV::DMA : 1];  // ELEM: elements of the slot inside the row
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int q = 64 * i + lane, row = q / L::CPR, pc = q % L::CPR;
         const int ck = pc ^ L::fk(row);  // logical chunk
         koff[i] = 8 * ck < DR ? row * row_bytes + ck * 16 : kOut;
+        if constexpr (ELEM) kvn[i] = min(8, max(0, DR - 8 * ck));
     }
 #pragma unroll
     for (int i = 0; i < LV::DMA; ++i) {
         const int q = 64 * i + lane, row = q / LV::CPR, pc = q % LV::CPR;
         const int cv = pc ^ LV::fv(row);  // logical chunk
         voff[i] = 8 * cv < DVR ? row * vrow_bytes + cv * 16 : kOut;
+        if constexpr (ELEM) vvn[i] = min(8, max(0, DVR - 8 * cv));
     }
+    auto elem_slot = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, int valid, uint32_t soff) -> u32x4 {
+        u32x4 v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w < valid ? off + 4 * w : kOut, soff, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w + 1 < valid ? off + 4 * w + 2 : kOut, soff, 0);
+            v[w] = lo | (hi << 16);
+        }
+        return v;
+    };
     // K fragment of kstep t: key row col, dims (D/4)*grp + 8t .. +7 (contraction
     // slot (t, grp, e) <-> dim (D/4)*grp + 8t + e, matching qb below).
     int krd[L::KSTEPS];
@@ -317,10 +336,22 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         // offset.
         const uint32_t kb = PAGED ? 0u : base, ksb = PAGED ? base : 0u;
         const uint32_t vb = PAGED ? 0u : vbase, vsb = PAGED ? vbase : 0u;
+        if constexpr (ELEM) {
+            // (an out-of-range slot stays out of range: kOut plus a step offset
+            // still exceeds every num_records)
 #pragma unroll
-        for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, koff[i] + kb, ksb);
+            for (int i = 0; i < L::DMA; ++i)
+                lds_store(reinterpret_cast<u32x4*>(st + 512 * i) + lane, elem_slot(ikrs, koff[i] + kb, kvn[i], ksb));
 #pragma unroll
-        for (int i = 0; i < LV::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, voff[i] + vb, vsb);
+            for (int i = 0; i < LV::DMA; ++i)
+                lds_store(reinterpret_cast<u32x4*>(st + L::TILE + 512 * i) + lane,
+                          elem_slot(ivrs, voff[i] + vb, vvn[i], vsb));
+        } else {
+#pragma unroll
+            for (int i = 0; i < L::DMA; ++i) dma16(ikrs, st + 512 * i, koff[i] + kb, ksb);
+#pragma unroll
+            for (int i = 0; i < LV::DMA; ++i) dma16(ivrs, st + L::TILE + 512 * i, voff[i] + vb, vsb);
+        }
         ++issued;
         if (++i_st < i_nst)
             i_k0 += kStep;
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         const int64_t prow0 = ((int64_t)g.b * a.Hq + g.h0) * a.splits + g.split;
         if (g.nst == 0) {  // no visible key in this split
             if (col < g.nh) {
-                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * DVR + 4 * grp;
+                float* op = a.o_part + (prow0 + (int64_t)col * a.splits) * DVP + 4 * grp;
 #pragma unroll
                 for (int dt = 0; dt < DV / 16; ++dt)
                     if (16 * dt + 4 * grp < DVR)
@@ -356,8 +387,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
 #pragma unroll
             for (int t = 0; t < L::KSTEPS; ++t) {
                 const int d0 = (D / 4) * grp + 8 * t;
-                qb[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                    qrs, d0 < DR ? (col * DR + d0) * 2 : kOut, 0, 0);
+                if constexpr (ELEM)
+                    qb[t] = elem_slot(qrs, d0 < DR ? (col * DR + d0) * 2 : kOut, min(8, max(0, DR - d0)), 0u);
+                else
+                    qb[t] = __builtin_amdgcn_raw_buffer_load_b128(
+                        qrs, d0 < DR ? (col * DR + d0) * 2 : kOut, 0, 0);
             }
             // Take the wait for the Q loads here, once per head, not inside the
             // step loop.
@@ -446,7 +480,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         l_run += __shfl_xor(l_run, 32);
         if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
-            float* op = a.o_part + prow * DVR + 4 * grp;
+            float* op = a.o_part + prow * DVP + 4 * grp;
             if (m_run == -INFINITY) {  // every key masked (paged: invalid pages only)
 #pragma unroll
                 for (int dt = 0; dt < DV / 16; ++dt)
@@ -466,16 +500,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     }
 }
 
-template <int D, class T, bool GEN = false>
+template <int D, class T, bool GEN = false, bool ELEM = false>
 __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     constexpr int TPR = D / 4;       // threads per row, 4 dims each
     constexpr int RPB = 256 / TPR;   // rows (batch, query head) per block
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int d4 = threadIdx.x % TPR;
-    const int DR = GEN ? a.Dv : D;  // value head dim in memory (a multiple of 8, <= D)
+    const int DR = GEN ? a.Dv : D;  // value head dim in memory (<= D; a multiple of 8 unless ELEM)
+    const int DP = ELEM ? (DR + 3) & ~3 : DR;  // floats per partial row
     if (row >= (int64_t)a.B * a.Hq || 4 * d4 >= DR) return;
     const float* lse = a.lse_part + row * a.splits;
-    const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * DR) + d4;
+    const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.splits * DP) + d4;
     float M = -INFINITY;
     for (int s = 0; s < a.splits; ++s) M = fmaxf(M, lse[s]);
     float den = 0.f;
@@ -484,16 +519,23 @@ __global__ __launch_bounds__(256) void decode_merge_bf16_kernel(DecodeArgs a) {
     for (int s = 0; s < a.splits; ++s) {
         const float w = fast_exp2((lse[s] - M) * kLog2e);  // empty split: exp(-inf) = 0
         den += w;
-        const f32x4 o = op[(int64_t)s * (DR / 4)];
+        const f32x4 o = op[(int64_t)s * (DP / 4)];
         acc[0] = fmaf(w, o[0], acc[0]);
         acc[1] = fmaf(w, o[1], acc[1]);
         acc[2] = fmaf(w, o[2], acc[2]);
         acc[3] = fmaf(w, o[3], acc[3]);
     }
     // Every split empty (no visible key): M = -inf, w = NaN, and the row is NaN.
-    const uint32_t lo = pack_lo16(to16<T>(acc[0] / den), to16<T>(acc[1] / den));
-    const uint32_t hi = pack_lo16(to16<T>(acc[2] / den), to16<T>(acc[3] / den));
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * DR + 4 * d4) = u32x2{lo, hi};
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + row * DR + 4 * d4;
+    if constexpr (ELEM) {  // element by element: the row need not be 8-byte aligned
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * d4 + e < DR) orow[e] = (uint16_t)to16<T>(acc[e] / den);
+    } else {
+        const uint32_t lo = pack_lo16(to16<T>(acc[0] / den), to16<T>(acc[1] / den));
+        const uint32_t hi = pack_lo16(to16<T>(acc[2] / den), to16<T>(acc[3] / den));
+        *reinterpret_cast<u32x2*>(orow) = u32x2{lo, hi};
+    }
 }
 
 // fp32 inputs (the ruDNN user guide's F32 Q/K/V, section 9): the same items,
@@ -809,23 +851,24 @@ hipError_t compute_units(int* n) {
 }
 
 // Split and merge for a value head dim Dv other than D (both multiples of 8
-// up to 256): general-width kernels on the padded widths DP (K) and VP (V).
-template <int DP, int VP, bool PAGED, class T>
+// up to 256), or (ELEM) head dims that are not multiples of 8 (up to 256):
+// general-width kernels on the padded widths DP (K) and VP (V).
+template <int DP, int VP, bool PAGED, class T, bool ELEM>
 void launch_dv(const DecodeArgs& a, const PagedArgs& p, int wgs, int items, hipStream_t s) {
     const dim3 mgrid((unsigned)(((int64_t)a.B * a.Hq * VP / 4 + 255) / 256));
-    hipLaunchKernelGGL((decode_split_bf16_kernel<DP, PAGED, T, true, VP>), dim3(wgs), dim3(kDecThreads), 0,
-                       s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos, items);
-    hipLaunchKernelGGL((decode_merge_bf16_kernel<VP, T, true>), mgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_bf16_kernel<DP, PAGED, T, true, VP, ELEM>), dim3(wgs), dim3(kDecThreads),
+                       0, s, a, p, a.key_lens, p.block_tables, p.seq_lens, p.query_seq, p.query_pos, items);
+    hipLaunchKernelGGL((decode_merge_bf16_kernel<VP, T, true, ELEM>), mgrid, dim3(256), 0, s, a);
 }
 
-template <int DP, bool PAGED, class T>
+template <int DP, bool PAGED, class T, bool ELEM = false>
 void launch_dv_v(const DecodeArgs& a, const PagedArgs& p, int wgs, int items, hipStream_t s) {
     if (a.Dv <= 64)
-        launch_dv<DP, 64, PAGED, T>(a, p, wgs, items, s);
+        launch_dv<DP, 64, PAGED, T, ELEM>(a, p, wgs, items, s);
     else if (a.Dv <= 128)
-        launch_dv<DP, 128, PAGED, T>(a, p, wgs, items, s);
+        launch_dv<DP, 128, PAGED, T, ELEM>(a, p, wgs, items, s);
     else
-        launch_dv<DP, 256, PAGED, T>(a, p, wgs, items, s);
+        launch_dv<DP, 256, PAGED, T, ELEM>(a, p, wgs, items, s);
 }
 
 template <bool PAGED, class T>
@@ -837,6 +880,26 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    if (a.D % 8 != 0 || a.Dv % 8 != 0) {
+        if (a.D < 1 || a.Dv < 1 || a.D > 256 || a.Dv > 256) return hipErrorInvalidValue;
+        if constexpr (PAGED) {
+            if (a.D <= 64)
+                launch_dv_v<64, PAGED, T, true>(a, p, wgs, items, s);
+            else if (a.D <= 128)
+                launch_dv_v<128, PAGED, T, true>(a, p, wgs, items, s);
+            else
+                launch_dv_v<256, PAGED, T, true>(a, p, wgs, items, s);
+        } else {  // the dense decode has Dv = D
+            if (a.Dv != a.D) return hipErrorInvalidValue;
+            if (a.D <= 64)
+                launch_dv<64, 64, PAGED, T, true>(a, p, wgs, items, s);
+            else if (a.D <= 128)
+                launch_dv<128, 128, PAGED, T, true>(a, p, wgs, items, s);
+            else
+                launch_dv<256, 256, PAGED, T, true>(a, p, wgs, items, s);
+        }
+        return hipGetLastError();
+    }
     if (a.Dv != a.D) {
         if constexpr (PAGED) {
             if (a.D % 8 != 0 || a.Dv % 8 != 0 || a.D < 8 || a.Dv < 8 || a.D > 256 || a.Dv > 256)

@@ -199,7 +199,16 @@ struct Bf16Geo {
 // dims but only the DV output dims of slice blockIdx.y (V columns
 // DV*y .. DV*y + DV - 1), so the registers hold D-wide Q fragments and a
 // DV-wide output; the slices of a query block recompute its scores.
-template <int D, bool PAGED, class T, bool BIAS = false, bool GEN = false, int DV = D>
+//
+// ELEM (with GEN; head dims that are not multiples of 8): rows of such a
+// width do not start on 16-byte boundaries, and a row's last 16-byte chunk
+// would carry the next row's first elements, so Q, K and V are read one
+// element at a time (2-byte buffer loads; elements past the row read as
+// zeros through the same out-of-range offsets) and each 16-byte LDS slot is
+// written by the lane the DMA would have filled it with, in the same
+// layout; the output is stored element by element.  The loads are waited
+// for where they are written: no prefetch across steps on this path.
+template <int D, bool PAGED, class T, bool BIAS = false, bool GEN = false, int DV = D, bool ELEM = false>
 __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel(
     ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
@@ -281,11 +290,25 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     // Without a causal mask (dense) Q is read non-temporally: it is read once,
     // and the XCD's L2 is better spent keeping the K/V rows the next
     // workgroups sweep (see decode_tile).
-    const bool stream_q_o = !PAGED && !a.causal;
+    const bool stream_q_o = !PAGED && !a.causal && !ELEM;
     u32x4 qr[D / 16];
     {
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, (uint32_t)nrows * qstride);
-        if (stream_q_o) {
+        if constexpr (ELEM) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+                const int d0 = 16 * t + 8 * hg;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int e0 = d0 + 2 * w;
+                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                        qrs, e0 < DR ? qi * qstride + e0 * 2 : kOut, 0, 0);
+                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                        qrs, e0 + 1 < DR ? qi * qstride + e0 * 2 + 2 : kOut, 0, 0);
+                    qr[t][w] = lo | (hi << 16);
+                }
+            }
+        } else if (stream_q_o) {
 #pragma unroll
             for (int t = 0; t < D / 16; ++t) {
                 const int d0 = 16 * t + 8 * hg;
@@ -327,12 +350,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
     const uint32_t vrow_bytes = PAGED ? (uint32_t)a.Hkv * DVM * 2 : (uint32_t)DVM * 2;
     const int row_base = PAGED ? 16 * wave : 0;
     uint32_t koff[L::DMA], voff[LV::DMA];
+    int kvn[ELEM ? L::DMA : 1], vvn[ELEM ? LV::DMA : 1];  // ELEM: elements of the slot inside the row
 #pragma unroll
     for (int i = 0; i < L::DMA; ++i) {
         const int q = 64 * (L::DMA * wave + i) + lane;
         const int row = q / L::CPR, pc = q % L::CPR;
         const int ck = pc ^ L::fk(row);  // logical chunk
         koff[i] = 8 * ck < DR ? (k_lds_row(row) - row_base) * row_bytes + ck * 16 : kOut;
+        if constexpr (ELEM) kvn[i] = min(8, max(0, DR - 8 * ck));
     }
 #pragma unroll
     for (int i = 0; i < LV::DMA; ++i) {
@@ -340,7 +365,20 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         const int row = q / LV::CPR, pc = q % LV::CPR;
         const int cv = pc ^ LV::fv(row);  // logical chunk of the slice
         voff[i] = 8 * cv < DRV ? (row - row_base) * vrow_bytes + (dv0 + 8 * cv) * 2 : kOut;
+        if constexpr (ELEM) vvn[i] = min(8, max(0, DRV - 8 * cv));
     }
+    // ELEM: the 16 bytes of one slot from 2-byte loads (elements past the row,
+    // and whole slots at kOut, read as zeros).
+    auto elem_slot = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, int valid, uint32_t soff) -> u32x4 {
+        u32x4 v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w < valid ? off + 4 * w : kOut, soff, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w + 1 < valid ? off + 4 * w + 2 : kOut, soff, 0);
+            v[w] = lo | (hi << 16);
+        }
+        return v;
+    };
     // Paged: resource over the page of keys j0 + 16*wave .. +15 (zero records
     // when the table entry is outside the cache) and the group's scalar
     // offset inside it; the validity goes to LDS for the mask.
@@ -369,14 +407,27 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
         if (PAGED) {
             const bool ok = page_of(j0, stage);
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + pg_off[stage], pg_bytes[stage]);
+            if constexpr (ELEM) {
 #pragma unroll
-            for (int i = 0; i < L::DMA; ++i) dma16s(rk, dst + 512 * i, koff[i], pg_soff[stage]);
+                for (int i = 0; i < L::DMA; ++i)
+                    *reinterpret_cast<u32x4*>(dst + 512 * i + 8 * lane) =
+                        elem_slot(rk, koff[i], kvn[i], pg_soff[stage]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < L::DMA; ++i) dma16s(rk, dst + 512 * i, koff[i], pg_soff[stage]);
+            }
             if (lane == 0) lds_store_i32(kvalid + 4 * stage + wave, ok ? 1 : 0);
         } else {
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(kp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
+            if constexpr (ELEM) {
 #pragma unroll
-            for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, koff[i]);
+                for (int i = 0; i < L::DMA; ++i)
+                    *reinterpret_cast<u32x4*>(dst + 512 * i + 8 * lane) = elem_slot(rs, koff[i], kvn[i], 0u);
+            } else {
+#pragma unroll
+                for (int i = 0; i < L::DMA; ++i) dma16(rs, dst + 512 * i, koff[i]);
+            }
         }
     };
     auto issue_v = [&](int j0, int stage) {
@@ -385,13 +436,26 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
             // K of this tile went to K stage (j0 / kBc) % 2 with the lookup.
             const int ks = (j0 / kBc) & 1;
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + vpg_off[ks], vpg_bytes[ks]);
+            if constexpr (ELEM) {
 #pragma unroll
-            for (int i = 0; i < LV::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], vpg_soff[ks]);
+                for (int i = 0; i < LV::DMA; ++i)
+                    *reinterpret_cast<u32x4*>(dst + 512 * i + 8 * lane) =
+                        elem_slot(rv, voff[i], vvn[i], vpg_soff[ks]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < LV::DMA; ++i) dma16s(rv, dst + 512 * i, voff[i], vpg_soff[ks]);
+            }
         } else {
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(vp + (int64_t)j0 * DVM, (uint32_t)(a.Sk - j0) * DVM * 2);
+            if constexpr (ELEM) {
 #pragma unroll
-            for (int i = 0; i < LV::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
+                for (int i = 0; i < LV::DMA; ++i)
+                    *reinterpret_cast<u32x4*>(dst + 512 * i + 8 * lane) = elem_slot(rs, voff[i], vvn[i], 0u);
+            } else {
+#pragma unroll
+                for (int i = 0; i < LV::DMA; ++i) dma16(rs, dst + 512 * i, voff[i]);
+            }
         }
     };
 
@@ -680,7 +744,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
                 const u32x2 w = {pack2<T>(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
                                  pack2<T>(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
                 const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims of the slice, all < DRV or none
-                if (d0 < DRV) *reinterpret_cast<u32x2*>(orow + d0) = w;
+                if constexpr (ELEM) {  // element by element: the row need not be 8-byte aligned
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (d0 + e < DRV) orow[d0 + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                } else if (d0 < DRV) {
+                    *reinterpret_cast<u32x2*>(orow + d0) = w;
+                }
             }
     }
 }
@@ -932,13 +1002,32 @@ int xcd_resident(Kernel kernel, int threads) {
 // 128 the output is computed in two 128-dim slices.
 template <bool PAGED, class T, bool BIAS = false>
 hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
-    if (a.D % 8 != 0 || a.D < 8 || a.D > 256) return hipErrorInvalidValue;
+    if (a.D < 1 || a.D > 256) return hipErrorInvalidValue;
     const dim3 g = forward_grid(a), t(kThreads);
     auto go = [&](auto kernel) {
         ForwardArgs b = a;
         b.sweep_group = (!PAGED && !a.causal) ? xcd_resident(kernel, kThreads) : 0;
         hipLaunchKernelGGL(kernel, g, t, 0, s, b, p, p.block_tables, p.seq_lens, p.cu_seqlens_q);
     };
+    if (a.D % 8 != 0 || a.Dv % 8 != 0) {
+        // Head dims that are not multiples of 8 (up to 256): the element-wise
+        // load path on the padded widths (no bias).
+        if constexpr (!BIAS) {
+            if (a.D < 1 || a.Dv < 1 || a.D > 256 || a.Dv > 256) return hipErrorInvalidValue;
+            const bool v64 = a.Dv <= 64;
+            if (a.D <= 64)
+                v64 ? go(forward_bf16_kernel<64, PAGED, T, false, true, 64, true>)
+                    : go(forward_bf16_kernel<64, PAGED, T, false, true, 128, true>);
+            else if (a.D <= 128)
+                v64 ? go(forward_bf16_kernel<128, PAGED, T, false, true, 64, true>)
+                    : go(forward_bf16_kernel<128, PAGED, T, false, true, 128, true>);
+            else
+                v64 ? go(forward_bf16_kernel<256, PAGED, T, false, true, 64, true>)
+                    : go(forward_bf16_kernel<256, PAGED, T, false, true, 128, true>);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.Dv != a.D) {
         // A value head dim of its own (paged prefill): general-width kernels
         // on the padded K width, V in one 64- or 128-dim pass or two 128-dim

@@ -57,23 +57,30 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // every forward entry point, whose heads above 256 run on the head-dim-split
 // kernel; 512 for the ordered backward, above 128 on its head-dim-split
 // kernels; 128 for the atomic backward and the backward with a bias, whose
-// lanes hold a full-width operand and gradient).
-bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128) {
+// lanes hold a full-width operand and gradient).  any16: the entry point
+// also takes every 16-bit head dim from 1 to 256 (the forward and decode
+// kernels' element-wise load path for widths that are not multiples of 8).
+bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128, bool any16 = false) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
+    if (any16 && D >= 1 && D <= 256) return true;
     return D >= 8 && D <= max16 && D % 8 == 0;
 }
 
 // Value head dim of the paged entry points: Dv == D on every kernel; Dv != D
-// on the 16-bit kernels with D and Dv both multiples of 8 up to 256.
+// on the 16-bit kernels with D and Dv both up to 256.
 sdpa_status_t check_value_dim(int64_t D, int64_t Dv, int dtype) {
     if (Dv == D) return SDPA_OK;
-    if (dtype == SDPA_F32 || !head_dim_ok(D, dtype, 256) || !head_dim_ok(Dv, dtype, 256))
+    if (dtype == SDPA_F32 || !head_dim_ok(D, dtype, 256, true) || !head_dim_ok(Dv, dtype, 256, true))
         return fail(SDPA_ERR_UNSUPPORTED,
                     "value head dim Dv=%lld differs from D=%lld: supported for bf16 / fp16 with "
-                    "both multiples of 8 up to 256",
+                    "both up to 256",
                     (long long)Dv, (long long)D);
     return SDPA_OK;
 }
+
+// Floats per row of the split partials: the value head dim rounded up to 4,
+// so each row starts 16-byte aligned.
+int64_t partial_pitch(int64_t Dv) { return (Dv + 3) & ~int64_t(3); }
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -82,7 +89,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 sdpa_status_t check_common(const void* q, const void* k, const void* v, void* out, int64_t B,
                            int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                            float scale, int dtype, int64_t* qbytes, int64_t* kbytes,
-                           int64_t max16 = 128) {
+                           int64_t max16 = 128, bool any16 = false) {
     if (!q || !k || !v || !out) return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT,
@@ -107,9 +114,11 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
     // Per-head rows are addressed through buffer resources with 32-bit extents.
     if (Sq * D * es > INT_MAX || Sk * D * es > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "one head of q, k or v exceeds 2 GiB");
-    if (!head_dim_ok(D, dtype, max16))
+    if (!head_dim_ok(D, dtype, max16, any16))
         return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (%s%lld)", (long long)D,
-                    dtype == SDPA_F32 ? "fp32: a multiple of 4 up to " : "a multiple of 8 up to ",
+                    dtype == SDPA_F32 ? "fp32: a multiple of 4 up to "
+                    : any16           ? "any up to 256, or a multiple of 8 up to "
+                                      : "a multiple of 8 up to ",
                     dtype == SDPA_F32 ? 128LL : (long long)max16);
     return SDPA_OK;
 }
@@ -148,7 +157,7 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
                            int64_t bias_sb = 0, int64_t bias_sh = 0) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st = check_common(q, k, v, out, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
-                                    &kbytes, 1024);
+                                    &kbytes, 1024, bias == nullptr);
     if (st != SDPA_OK) return st;
     if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
@@ -544,7 +553,7 @@ sdpa_status_t sdpa_block_forward(const void* x, const void* wq, const void* wk, 
 size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_splits) {
     if (B < 1 || Hq < 1 || D < 1 || num_splits < 1 || num_splits > SDPA_MAX_SPLITS) return 0;
     const int64_t rows = numel4(B, Hq, num_splits, 1);
-    const int64_t no = numel4(B, Hq, num_splits, D);
+    const int64_t no = numel4(B, Hq, num_splits, partial_pitch(D));
     if (rows < 0 || no < 0 || no > INT64_MAX / 8) return 0;
     return round_up((size_t)no * sizeof(float)) + round_up((size_t)rows * sizeof(float));
 }
@@ -592,7 +601,7 @@ sdpa_status_t decode_impl(const void* q, const void* k, const void* v, int64_t B
                           bool noalloc) {
     int64_t qbytes = 0, kbytes = 0;
     sdpa_status_t st =
-        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes, 1024);
+        check_common(q, k, v, out, B, Hq, Hkv, 1, Sk, D, scale, dtype, &qbytes, &kbytes, 1024, true);
     if (st != SDPA_OK) return st;
     if (num_splits < 1 || num_splits > SDPA_MAX_SPLITS)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..%d", num_splits,
@@ -629,7 +638,7 @@ sdpa_status_t decode_impl(const void* q, const void* k, const void* v, int64_t B
     a.key_lens = key_lens;
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          round_up((size_t)numel4(B, Hq, num_splits, D) * 4));
+                                          round_up((size_t)numel4(B, Hq, num_splits, partial_pitch(D)) * 4));
     a.B = (int)B;
     a.Hq = (int)Hq;
     a.Hkv = (int)Hkv;
@@ -723,10 +732,10 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     if (queries > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (!head_dim_ok(D, dtype, 1024))
+    if (!head_dim_ok(D, dtype, 1024, true))
         return fail(SDPA_ERR_UNSUPPORTED,
-                    "head dim D=%lld not supported (16-bit: a multiple of 8 up to 1024; fp32: a "
-                    "multiple of 4 up to 128)",
+                    "head dim D=%lld not supported (16-bit: any up to 256, or a multiple of 8 up "
+                    "to 1024; fp32: a multiple of 4 up to 128)",
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
@@ -748,7 +757,7 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
     a.key_lens = nullptr;
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          round_up((size_t)numel4(queries, Hq, num_splits, Dv) * 4));
+                                          round_up((size_t)numel4(queries, Hq, num_splits, partial_pitch(Dv)) * 4));
     a.B = (int)queries;
     a.Hq = (int)Hq;
     a.Hkv = (int)Hkv;
@@ -830,10 +839,10 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
         max_pages_per_seq > INT_MAX || max_q > INT_MAX || max_seq_len > INT_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
-    if (!head_dim_ok(D, dtype, 1024))
+    if (!head_dim_ok(D, dtype, 1024, true))
         return fail(SDPA_ERR_UNSUPPORTED,
-                    "head dim D=%lld not supported (16-bit: a multiple of 8 up to 1024; fp32: a "
-                    "multiple of 4 up to 128)",
+                    "head dim D=%lld not supported (16-bit: any up to 256, or a multiple of 8 up "
+                    "to 1024; fp32: a multiple of 4 up to 128)",
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;

@@ -450,11 +450,15 @@ def sdpa_decode_noalloc(q, k, v, scale, out, key_lens=None, num_splits=MAX_SPLIT
 
 
 def decode_workspace_views(workspace, B, Hq, D, num_splits):
-    """(o_part [B,Hq,n,D], lse [B,Hq,n]) fp32 views of a decode workspace."""
-    n_o = B * Hq * num_splits * D
+    """(o_part [B,Hq,n,D], lse [B,Hq,n]) fp32 views of a decode workspace.
+
+    Each partial row is D floats rounded up to a multiple of 4; the view
+    drops the padding."""
+    Dp = (D + 3) // 4 * 4
+    n_o = B * Hq * num_splits * Dp
     off = (n_o * 4 + 255) // 256 * 256
     f = workspace.view(torch.uint8)
-    o_part = f[: n_o * 4].view(torch.float32).view(B, Hq, num_splits, D)
+    o_part = f[: n_o * 4].view(torch.float32).view(B, Hq, num_splits, Dp)[..., :D]
     lse = f[off: off + B * Hq * num_splits * 4].view(torch.float32).view(B, Hq, num_splits)
     return o_part, lse
 

@@ -99,7 +99,9 @@ enum {
  * 128 two workgroups per query block each produce 128 output dims and both
  * compute the scores); above 256 on a kernel that splits the head dim over
  * 4, 6 or 8 waves of 128 dims per 32-row query block (partial scores summed
- * in LDS).  SDPA_F32 any multiple of 4 from 4 to 128 (the 64- and 128-wide
+ * in LDS).  Any other D from 1 to 255 on the same kernels with Q, K and V
+ * read element by element (rows of such a width are not 16-byte aligned);
+ * not with a bias.  SDPA_F32 any multiple of 4 from 4 to 128 (the 64- and 128-wide
  * fp32 kernels, likewise).  One head (Sq*D or Sk*D elements) must be under
  * 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
  */
@@ -273,7 +275,9 @@ sdpa_status_t sdpa_block_forward(const void *x, const void *wq, const void *wk, 
 /*
  * Bytes of device workspace sdpa_decode needs for these sizes (0 if the sizes
  * are invalid).  Layout, fp32, 256-byte aligned sections:
- *   o_part [B, Hq, num_splits, D]  normalised partial outputs
+ *   o_part [B, Hq, num_splits, Dp] normalised partial outputs, Dp = D
+ *                                  rounded up to a multiple of 4 (the
+ *                                  padding floats are unspecified)
  *   lse    [B, Hq, num_splits]     natural-log log-sum-exp of each partial
  * Split s covers keys [s*C, min((s+1)*C, len_b)) with C = ceil(Sk / num_splits)
  * and len_b = key_lens[b] (or Sk); an empty split holds o_part = 0, lse = -inf.
@@ -292,8 +296,10 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
  *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
  *   out        device [B, Hq, 1, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024
- * (above 128 each wave's LDS ring holds two 16-key steps instead of four;
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 256 or a
+ * multiple of 8 up to 1024 (a width that is not a multiple of 8 is read
+ * element by element; above 128 each wave's LDS ring holds two 16-key steps
+ * instead of four;
  * above 256 the split pass runs on the head-dim-split kernel of
  * sdpa_forward, with up to 32 query heads of a K/V group as its rows, and
  * writes the same partials).
@@ -363,7 +369,8 @@ sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
  * Two kernels are enqueued on stream: the split pass, then the merge.
  * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024
  * (above 256 the split pass runs on the head-dim-split kernel, as in
- * sdpa_decode) with Dv = D, or D and Dv both multiples of 8 up to 256;
+ * sdpa_decode) with Dv = D, or D and Dv both any width up to 256 (widths
+ * that are not multiples of 8 read element by element);
  * page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
@@ -407,8 +414,9 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *                 with D up to 256 only (SDPA_ERR_UNSUPPORTED otherwise)
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
  * SDPA_F16, D a multiple of 8 up to 1024 (above 256 on the head-dim-split
- * kernel) with Dv = D, or D and Dv both multiples of 8 up to 256 (a value
- * head dim above 128 in two 128-dim output slices); page_size a multiple of
+ * kernel) with Dv = D, or D and Dv both any width up to 256 (a value head
+ * dim above 128 in two 128-dim output slices; widths that are not multiples
+ * of 8 read element by element); page_size a multiple of
  * 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside
