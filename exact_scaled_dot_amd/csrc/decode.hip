@@ -880,8 +880,8 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
-    if (a.D % 8 != 0 || a.Dv % 8 != 0) {
-        if (a.D < 1 || a.Dv < 1 || a.D > 256 || a.Dv > 256) return hipErrorInvalidValue;
+    if ((a.D % 8 != 0 || a.Dv % 8 != 0) && a.D <= 256) {
+        if (a.D < 1 || a.Dv < 1 || a.Dv > 256) return hipErrorInvalidValue;
         if constexpr (PAGED) {
             if (a.D <= 64)
                 launch_dv_v<64, PAGED, T, true>(a, p, wgs, items, s);
@@ -914,14 +914,19 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
         }
         return hipErrorInvalidValue;  // the dense decode has Dv = D
     }
-    if (a.D > 256 && a.D <= 1024 && a.D % 8 == 0) {
+    if (a.D > 256 && a.D <= 1024) {
         // Wider heads: the head-dim-split kernel writes the same partials,
         // then the same merge (D/4 threads per row).
+        if (a.Dv != a.D) return hipErrorInvalidValue;
         const hipError_t ew = launch_decode_wide_split(a, PAGED ? &p : nullptr, T::kF16, s);
         if (ew != hipSuccess) return ew;
         const int dw = a.D <= 512 ? 512 : 1024;
         const dim3 mg((unsigned)(((int64_t)a.B * a.Hq * dw / 4 + 255) / 256));
-        if (a.D == 512)
+        if (a.D % 8 != 0 && dw == 512)  // partial rows padded to a multiple of 4 floats
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T, true, true>), mg, dim3(256), 0, s, a);
+        else if (a.D % 8 != 0)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T, true, true>), mg, dim3(256), 0, s, a);
+        else if (a.D == 512)
             hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T>), mg, dim3(256), 0, s, a);
         else if (a.D == 1024)
             hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T>), mg, dim3(256), 0, s, a);

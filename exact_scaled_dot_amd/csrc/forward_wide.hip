@@ -1,5 +1,5 @@
 // Exact attention forward for wide heads: 16-bit Q, K, V with a head dim D
-// above 256 and up to 1024 (a multiple of 8), the range the ruDNN user guide
+// above 256 and up to 1024 (any width), the range the ruDNN user guide
 // allows for attention (section 9: D and Dv in 1..=1024).  Same definition
 // and options as the narrow forward: softmax over the keys of
 // Q K^T * scale (+ bias) under the causal / key-padding masks, grouped K/V
@@ -29,6 +29,13 @@
 // The V tile of step j is issued right before the K fragments of step j, and
 // vmcnt counts in issue order, so the compiler's wait for those K fragments
 // also covers the V tile: no explicit wait is needed for V.
+//
+// ELEM (head dims that are not multiples of 8): rows of such a width are not
+// 16-byte aligned, so Q, K and V are read one element at a time (2-byte
+// buffer loads; elements past the row at out-of-range offsets read as
+// zeros) into the same registers and V ring slots the 16-byte loads and the
+// DMA would fill, and the output is stored element by element; the decode
+// partials' rows are padded to a multiple of 4 floats.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -67,6 +74,21 @@ __device__ __forceinline__ void w_lds_barrier() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// 16 bytes (8 elements) of a row from 2-byte loads: element e at byte
+// offset off + 2e when e < valid, else zero.
+template <int AUX>
+__device__ __forceinline__ u32x4 w_elem16(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w < valid ? off + 4 * w : kWOutside, 0, AUX);
+        const uint32_t hi =
+            __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w + 1 < valid ? off + 4 * w + 2 : kWOutside, 0, AUX);
+        v[w] = lo | (hi << 16);
+    }
+    return v;
+}
+
 template <int AUX>
 __device__ __forceinline__ void w_dma(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (w_lds_void*)((__attribute__((address_space(3))) char*)lds), 16,
@@ -134,7 +156,7 @@ struct WideDec {
     int total_q;
 };
 
-template <int NW, class T, bool BIAS, bool DEC, bool PAGED = false>
+template <int NW, class T, bool BIAS, bool DEC, bool PAGED = false, bool ELEM = false>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     ForwardArgs a, const int32_t* __restrict__ key_lens, WideDec dec, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_seq,
@@ -266,8 +288,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int row = q0 + 16 * qb + l16, dim = d0 + 32 * s + 8 * g4;
-                qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rq, (row < nq && dim < D) ? ((uint32_t)(row * qstride) + dim) * 2 : kWOutside, 0, 0);
+                const uint32_t off = (row < nq && dim < D) ? ((uint32_t)(row * qstride) + dim) * 2 : kWOutside;
+                if constexpr (ELEM)
+                    qf[qb][s] = w_elem16<0>(rq, off, D - dim);
+                else
+                    qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
             }
     }
     // K fragments (A operands): key kt + lane%16, dims d0 + 32s + 8*(lane/16).
@@ -276,8 +301,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int dim = d0 + 32 * s + 8 * g4;
-            kf[s] = __builtin_amdgcn_raw_buffer_load_b128(
-                sr.k, dim < D ? ((sr.row0 + l16) * sr.rstride + sr.col0 + dim) * 2 : kWOutside, 0, kKVPolicy);
+            const uint32_t off = dim < D ? ((sr.row0 + l16) * sr.rstride + sr.col0 + dim) * 2 : kWOutside;
+            if constexpr (ELEM)
+                kf[s] = w_elem16<kKVPolicy>(sr.k, off, D - dim);
+            else
+                kf[s] = __builtin_amdgcn_raw_buffer_load_b128(sr.k, off, 0, kKVPolicy);
         }
     };
     // V tile of keys kt .. kt+15, this wave's dims, into ring stage st: DMA i
@@ -289,9 +317,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     auto load_v = [&](int kt, int st) {
         const Src sr = src(kt);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w_dma<kKVPolicy>(sr.v, vw + st * LY::VST + 512 * i,
-                  vdim_ok ? ((sr.row0 + 4 * i + g4) * sr.rstride + sr.col0 + d0 + 8 * vchunk) * 2 : kWOutside);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off =
+                vdim_ok ? ((sr.row0 + 4 * i + g4) * sr.rstride + sr.col0 + d0 + 8 * vchunk) * 2 : kWOutside;
+            if constexpr (ELEM)  // the slot the DMA would fill: 16 bytes at lane * 16
+                *reinterpret_cast<u32x4*>(vw + st * LY::VST + 512 * i + 8 * lane) =
+                    w_elem16<kKVPolicy>(sr.v, off, D - (d0 + 8 * vchunk));
+            else
+                w_dma<kKVPolicy>(sr.v, vw + st * LY::VST + 512 * i, off);
+        }
     };
     // Transposed-read offsets (32x32x16 A operand = V^T): lane reads rows
     // (keys) 8*(lane/32) + (lane%16)/4 (+4 for the upper half), dims
@@ -451,7 +485,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             const float m_use = m_run == -INFINITY ? 0.f : m_run;
             dec.lse_part[prow] = l > 0.f ? (m_use + __log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
-        float* orow = dec.o_part + prow * D;
+        const int DP = ELEM ? (D + 3) & ~3 : D;  // floats per partial row
+        float* orow = dec.o_part + prow * DP;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -481,10 +516,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int dim = d0 + 32 * db + 8 * r4 + 4 * kh;
                 const f32x16& xo = acc[db];
-                if (dim < D)
-                    *reinterpret_cast<u32x2*>(row + dim) =
-                        u32x2{pack2<T>(xo[4 * r4] * inv, xo[4 * r4 + 1] * inv),
-                              pack2<T>(xo[4 * r4 + 2] * inv, xo[4 * r4 + 3] * inv)};
+                const u32x2 w = {pack2<T>(xo[4 * r4] * inv, xo[4 * r4 + 1] * inv),
+                                 pack2<T>(xo[4 * r4 + 2] * inv, xo[4 * r4 + 3] * inv)};
+                if constexpr (ELEM) {  // element by element: the row need not be 8-byte aligned
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (dim + e < D) row[dim + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                } else if (dim < D) {
+                    *reinterpret_cast<u32x2*>(row + dim) = w;
+                }
             }
     }
 }
@@ -494,7 +534,11 @@ hipError_t launch_wide_nw(const ForwardArgs& a, hipStream_t s) {
     const int nqb = (a.Sq + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hq * nqb));
     const int32_t* none = nullptr;
-    if (a.bias)
+    if (a.D % 8 != 0) {
+        if (a.bias) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false, false, true>), grid, dim3(NW * 64), 0, s, a,
+                           a.key_lens, WideDec{}, none, none, none, none);
+    } else if (a.bias)
         hipLaunchKernelGGL((forward_wide_kernel<NW, T, true, false>), grid, dim3(NW * 64), 0, s, a, a.key_lens,
                            WideDec{}, none, none, none, none);
     else
@@ -507,8 +551,12 @@ template <int NW, class T, bool PAGED>
 hipError_t launch_wide_dec_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
     const int nhb = (a.Hq / a.Hkv + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hkv * d.splits * nhb));
-    hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true, PAGED>), grid, dim3(NW * 64), 0, s, a, a.key_lens, d,
-                       d.tables, d.seq_lens, d.query_seq, d.query_pos);
+    if (a.D % 8 != 0)
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true, PAGED, true>), grid, dim3(NW * 64), 0, s, a,
+                           a.key_lens, d, d.tables, d.seq_lens, d.query_seq, d.query_pos);
+    else
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true, PAGED>), grid, dim3(NW * 64), 0, s, a,
+                           a.key_lens, d, d.tables, d.seq_lens, d.query_seq, d.query_pos);
     return hipGetLastError();
 }
 
@@ -529,7 +577,7 @@ hipError_t launch_wide_t(const ForwardArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_forward_wide(const ForwardArgs& a, bool f16, hipStream_t s) {
-    if (a.D <= 256 || a.D > 1024 || a.D % 8 != 0) return hipErrorInvalidValue;
+    if (a.D <= 256 || a.D > 1024) return hipErrorInvalidValue;
     return f16 ? launch_wide_t<F16T>(a, s) : launch_wide_t<Bf16T>(a, s);
 }
 
@@ -537,8 +585,12 @@ template <int NW, class T>
 hipError_t launch_wide_paged_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
     const int nqb = (a.Sq + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hq * nqb));
-    hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false, true>), grid, dim3(NW * 64), 0, s, a, nullptr, d,
-                       d.tables, d.seq_lens, nullptr, nullptr);
+    if (a.D % 8 != 0)
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false, true, true>), grid, dim3(NW * 64), 0, s, a,
+                           nullptr, d, d.tables, d.seq_lens, nullptr, nullptr);
+    else
+        hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false, true>), grid, dim3(NW * 64), 0, s, a, nullptr,
+                           d, d.tables, d.seq_lens, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -550,7 +602,7 @@ hipError_t launch_wide_paged_t(const ForwardArgs& a, const WideDec& d, hipStream
 }
 
 hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, bool f16, hipStream_t s) {
-    if (a.D <= 256 || a.D > 1024 || a.D % 8 != 0) return hipErrorInvalidValue;
+    if (a.D <= 256 || a.D > 1024) return hipErrorInvalidValue;
     WideDec w{};
     w.tables = p.block_tables;
     w.seq_lens = p.seq_lens;
@@ -568,7 +620,7 @@ hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, b
 }
 
 hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, bool f16, hipStream_t s) {
-    if (d.D <= 256 || d.D > 1024 || d.D % 8 != 0) return hipErrorInvalidValue;
+    if (d.D <= 256 || d.D > 1024) return hipErrorInvalidValue;
     ForwardArgs a;
     a.q = d.q;
     a.k = d.k;

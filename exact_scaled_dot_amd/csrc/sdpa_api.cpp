@@ -58,11 +58,11 @@ bool known_dtype(int dtype) { return dtype == SDPA_F32 || dtype == SDPA_BF16 || 
 // kernel; 512 for the ordered backward, above 128 on its head-dim-split
 // kernels; 128 for the atomic backward and the backward with a bias, whose
 // lanes hold a full-width operand and gradient).  any16: the entry point
-// also takes every 16-bit head dim from 1 to 256 (the forward and decode
+// also takes every 16-bit head dim from 1 to max16 (the forward and decode
 // kernels' element-wise load path for widths that are not multiples of 8).
 bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128, bool any16 = false) {
     if (dtype == SDPA_F32) return D >= 4 && D <= 128 && D % 4 == 0;
-    if (any16 && D >= 1 && D <= 256) return true;
+    if (any16) return D >= 1 && D <= max16;
     return D >= 8 && D <= max16 && D % 8 == 0;
 }
 
@@ -117,7 +117,7 @@ sdpa_status_t check_common(const void* q, const void* k, const void* v, void* ou
     if (!head_dim_ok(D, dtype, max16, any16))
         return fail(SDPA_ERR_UNSUPPORTED, "head dim D=%lld not supported (%s%lld)", (long long)D,
                     dtype == SDPA_F32 ? "fp32: a multiple of 4 up to "
-                    : any16           ? "any up to 256, or a multiple of 8 up to "
+                    : any16           ? "any width up to "
                                       : "a multiple of 8 up to ",
                     dtype == SDPA_F32 ? 128LL : (long long)max16);
     return SDPA_OK;
@@ -734,8 +734,8 @@ sdpa_status_t sdpa_paged_attention(const void* q, const void* k_cache, const voi
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
     if (!head_dim_ok(D, dtype, 1024, true))
         return fail(SDPA_ERR_UNSUPPORTED,
-                    "head dim D=%lld not supported (16-bit: any up to 256, or a multiple of 8 up "
-                    "to 1024; fp32: a multiple of 4 up to 128)",
+                    "head dim D=%lld not supported (16-bit: any width up to 1024; fp32: a "
+                    "multiple of 4 up to 128)",
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
@@ -841,8 +841,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
     if (!head_dim_ok(D, dtype, 1024, true))
         return fail(SDPA_ERR_UNSUPPORTED,
-                    "head dim D=%lld not supported (16-bit: any up to 256, or a multiple of 8 up "
-                    "to 1024; fp32: a multiple of 4 up to 128)",
+                    "head dim D=%lld not supported (16-bit: any width up to 1024; fp32: a "
+                    "multiple of 4 up to 128)",
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;

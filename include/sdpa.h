@@ -99,7 +99,7 @@ enum {
  * 128 two workgroups per query block each produce 128 output dims and both
  * compute the scores); above 256 on a kernel that splits the head dim over
  * 4, 6 or 8 waves of 128 dims per 32-row query block (partial scores summed
- * in LDS).  Any other D from 1 to 255 on the same kernels with Q, K and V
+ * in LDS).  Any other D from 1 to 1023 on the same kernels with Q, K and V
  * read element by element (rows of such a width are not 16-byte aligned);
  * not with a bias.  SDPA_F32 any multiple of 4 from 4 to 128 (the 64- and 128-wide
  * fp32 kernels, likewise).  One head (Sq*D or Sk*D elements) must be under
@@ -296,10 +296,9 @@ size_t sdpa_decode_workspace_size(int64_t B, int64_t Hq, int64_t D, int num_spli
  *   workspace  device buffer of at least sdpa_decode_workspace_size() bytes
  *   out        device [B, Hq, 1, D]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 256 or a
- * multiple of 8 up to 1024 (a width that is not a multiple of 8 is read
- * element by element; above 128 each wave's LDS ring holds two 16-key steps
- * instead of four;
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 1024 (a width
+ * that is not a multiple of 8 is read element by element; above 128 each
+ * wave's LDS ring holds two 16-key steps instead of four;
  * above 256 the split pass runs on the head-dim-split kernel of
  * sdpa_forward, with up to 32 query heads of a K/V group as its rows, and
  * writes the same partials).
@@ -367,10 +366,10 @@ sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
  *                (same layout as sdpa_decode's with B = queries, D = Dv)
  *   out          device [queries, Hq, Dv]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 1024
- * (above 256 the split pass runs on the head-dim-split kernel, as in
- * sdpa_decode) with Dv = D, or D and Dv both any width up to 256 (widths
- * that are not multiples of 8 read element by element);
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 1024 (above
+ * 256 the split pass runs on the head-dim-split kernel, as in sdpa_decode)
+ * with Dv = D, or D and Dv both any width up to 256 (widths that are not
+ * multiples of 8 read element by element);
  * page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
@@ -413,10 +412,10 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *                 key), the input sdpa_paged_backward needs; 16-bit inputs
  *                 with D up to 256 only (SDPA_ERR_UNSUPPORTED otherwise)
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
- * SDPA_F16, D a multiple of 8 up to 1024 (above 256 on the head-dim-split
- * kernel) with Dv = D, or D and Dv both any width up to 256 (a value head
- * dim above 128 in two 128-dim output slices; widths that are not multiples
- * of 8 read element by element); page_size a multiple of
+ * SDPA_F16, D any width up to 1024 (above 256 on the head-dim-split kernel)
+ * with Dv = D, or D and Dv both any width up to 256 (a value head dim above
+ * 128 in two 128-dim output slices; widths that are not multiples of 8 read
+ * element by element); page_size a multiple of
  * 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside

@@ -68,10 +68,9 @@ def fwd(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, sca
     (dict(out=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(out=ctypes.c_void_p(0x40000000 - 2)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(B=1 << 40, Hq=1 << 20), sd.SDPA_ERR_INVALID_ARGUMENT, "overflow"),
-    (dict(D=260), sd.SDPA_ERR_UNSUPPORTED, "any up to 256"),  # past 256: multiples of 8 only
+    (dict(D=1025), sd.SDPA_ERR_UNSUPPORTED, "any width up to 1024"),
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "head dim"),    # past the widest (1024) kernel
     (dict(D=1040), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
-    (dict(D=300), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
     (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # fp32: multiples of 4
     (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),  # fp32: up to 128
@@ -109,7 +108,7 @@ def dec(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, scale=0.1,
     (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws_bytes=100), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x60000000 - 256)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=276), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=1027), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),   # the widest decode is 1024
     (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),  # fp32: up to 128
     (dict(D=66, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),   # fp32: multiples of 4
@@ -132,7 +131,7 @@ def dec_noalloc(q=FAKE, k=FAKE_K, v=FAKE_V, B=2, Hq=8, Hkv=2, Sk=1000, D=128, sc
     (dict(splits=33), sd.SDPA_ERR_INVALID_ARGUMENT, "num_splits"),
     (dict(Hq=6, Hkv=4), sd.SDPA_ERR_INVALID_ARGUMENT, "multiple"),
     (dict(out=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=276), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=1027), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=132, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     # partials of 128 x 32 heads x 32 splits x 128 dims = 64 MiB + the lse section: one byte
     # section past the scratch, so nothing is launched
@@ -161,7 +160,7 @@ def test_decode_workspace_size():
     for B, Hq, D, n in [(64, 32, 128, 32), (1, 1, 64, 1), (3, 5, 64, 7)]:
         assert lib.sdpa_decode_workspace_size(B, Hq, D, n) == up(B * Hq * n * D * 4) + up(B * Hq * n * 4)
     # a partial row is D floats rounded up to 4
-    for D, Dp in [(1, 4), (3, 4), (17, 20), (100, 100), (255, 256)]:
+    for D, Dp in [(1, 4), (3, 4), (17, 20), (100, 100), (255, 256), (517, 520), (1023, 1024)]:
         assert lib.sdpa_decode_workspace_size(3, 5, D, 7) == up(3 * 5 * 7 * Dp * 4) + up(3 * 5 * 7 * 4)
     # 64 x 32 heads x 32 splits x 128 dims stays inside the 64 MiB split-workspace budget
     assert lib.sdpa_decode_workspace_size(64, 32, 128, 32) <= 64 << 20
@@ -208,7 +207,7 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, Dv=None, pages=1
     (dict(ws=None), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(ws_bytes=64), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(out=ctypes.c_void_p(0x7a000000 - 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps"),
-    (dict(D=260), sd.SDPA_ERR_UNSUPPORTED, "any up to 256"),
+    (dict(D=1100), sd.SDPA_ERR_UNSUPPORTED, "any width up to 1024"),
     (dict(D=1032), sd.SDPA_ERR_UNSUPPORTED, "up to 1024"),
     (dict(D=98, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=256, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),
@@ -257,7 +256,8 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pag
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
     (dict(Dv=-3), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
     (dict(Dv=260), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
-    (dict(D=300), sd.SDPA_ERR_UNSUPPORTED, "any up to 256"),
+    (dict(D=300, Dv=128), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=1030), sd.SDPA_ERR_UNSUPPORTED, "any width up to 1024"),
     (dict(D=64, Dv=512), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     # v_cache spans 100 * 16 * 2 * Dv * 2 bytes: 1 MB in lies inside it only at Dv = 256
     (dict(Dv=256, out=ctypes.c_void_p(0x40000000 + (1 << 20))), sd.SDPA_ERR_INVALID_ARGUMENT,
@@ -277,8 +277,8 @@ def test_dtype_codes():
     assert dec(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
     assert paged(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
     assert prefill(dtype=3) == sd.SDPA_ERR_INVALID_ARGUMENT and "dtype" in sd.last_error()
-    assert fwd(dtype=sd.SDPA_F16, D=260) == sd.SDPA_ERR_UNSUPPORTED  # reaches the head-dim check
-    assert dec(dtype=sd.SDPA_F16, D=260) == sd.SDPA_ERR_UNSUPPORTED
+    assert fwd(dtype=sd.SDPA_F16, D=1025) == sd.SDPA_ERR_UNSUPPORTED  # reaches the head-dim check
+    assert dec(dtype=sd.SDPA_F16, D=1025) == sd.SDPA_ERR_UNSUPPORTED
 
 
 def fwd_lse(lse=ctypes.c_void_p(0x78000000), dtype=sd.SDPA_BF16, q=FAKE, out=FAKE_O, Sq=128):

@@ -1,4 +1,4 @@
-"""GPU parity at 16-bit head dims that are not multiples of 8 (1 to 255; the
+"""GPU parity at 16-bit head dims that are not multiples of 8 (1 to 1023; the
 ruDNN user guide section 9 sets no alignment on the head dim), against the
 fp64 oracle, on every entry point that takes them: the dense forward (and its
 log-sum-exp), the split-KV decode (its partials included), the alloc-free
@@ -8,6 +8,8 @@ their own.
 Rows of such a width are not 16-byte aligned, so the kernels read Q, K and V
 element by element into the same on-chip layout as the aligned widths and
 store the output element by element; the dims past D are zeros on chip.
+Above 256 the head-dim-split kernel (4, 6 or 8 waves of 128 dims) does the
+same.
 Sizes span several key tiles with a ragged tail.  Bars: tests/parity.py."""
 
 import math
@@ -182,3 +184,94 @@ def test_paged_prefill_any_width(D, Dv):
             for h in range(8):  # K/V head h // 4 (8 query heads over 2)
                 want[t, h] = O.attend(q64[t, h:h + 1], ks[:, h // 4], vs[:, h // 4], scale, vis)[1][0]
         assert np.abs(to64(lse) - want).max() < 2e-3, what + ": lse"
+
+
+WIDE = [257, 300, 517, 700, 1023]
+
+
+@pytest.mark.parametrize("D", WIDE)
+@pytest.mark.parametrize("mask", [0, 1, 3], ids=["none", "causal", "causal+padding"])
+def test_forward_wide_any_width(D, mask):
+    B, Hq, Hkv, S = 2, 4, 2, 150
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 5800 + D + 7 * mask, DEV)
+    lens = torch.tensor([150, 33], dtype=torch.int32, device=DEV) if mask & 2 else None
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask, ln, return_lse=True)
+    what = "wide forward D=%d mask=%d" % (D, mask)
+    compare(to64(out), ref, BF16, what)
+    assert np.abs(to64(lse) - rlse).max() < 1e-2, what + ": lse"
+
+
+def test_forward_wide_any_width_fp16_guarded():
+    B, Hq, S, D = 1, 4, 70, 389
+    q, k, v = draw_qkv(B, Hq, 2, S, S, D, F16, 5900, DEV)
+    n = B * Hq * S * D
+    buf = torch.full((n + 64,), 7.0, dtype=F16, device=DEV)
+    out = buf[:n].view(B, Hq, S, D)
+    sd.sdpa_forward(q, k, v, 0.05, sd.MASK_CAUSAL, out=out)
+    torch.cuda.synchronize()
+    assert (buf[n:] == 7.0).all()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 0.05, O.MASK_CAUSAL), F16,
+            "fp16 wide forward D=389")
+
+
+@pytest.mark.parametrize("D", [300, 517, 1023])
+@pytest.mark.parametrize("splits", [1, 7])
+def test_decode_wide_any_width(D, splits):
+    B, Hq, Hkv, Sk = 3, 8, 2, 700
+    q, k, v = draw_qkv(B, Hq, Hkv, 1, Sk, D, BF16, 6000 + D + splits, DEV)
+    lens = torch.tensor([700, 123, 1], dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(D)
+    ws = torch.empty(sd.sdpa_decode_workspace_size(B, Hq, D, splits), dtype=torch.uint8, device=DEV)
+    out = sd.sdpa_decode(q, k, v, scale, lens, splits, workspace=ws)
+    torch.cuda.synchronize()
+    q64, k64, v64, ln = to64(q), to64(k), to64(v), lens.cpu().numpy()
+    what = "wide decode D=%d splits=%d" % (D, splits)
+    compare(to64(out), O.sdpa_decode(q64, k64, v64, scale, ln), BF16, what)
+    op, lp = sd.decode_workspace_views(ws, B, Hq, D, splits)
+    rop, rlp = O.decode_split_partials(q64, k64, v64, scale, ln, splits)
+    op, lp = op.cpu().double().numpy(), lp.cpu().double().numpy()
+    empty = np.isneginf(rlp)
+    assert np.array_equal(np.isneginf(lp), empty), what + ": empty-split pattern"
+    assert (op[empty] == 0).all(), what + ": empty partials"
+    compare(op[~empty], rop[~empty], BF16, what + ": partials")
+
+
+@pytest.mark.parametrize("D", [300, 1023])
+def test_paged_wide_any_width(D):
+    lens, qs, qp = [300, 129, 1], [0, 1, 2, 0], [299, 128, 0, 17]
+    for causal in (False, True):
+        seed = 6100 + D + causal
+        inp = draw_paged(lens, qs, qp, 4, 2, D, 16, BF16, seed, DEV)
+        scale = 1 / math.sqrt(D)
+        out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                      inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale,
+                                      causal, inp["block_tables"].shape[1] * 16, 3)
+        torch.cuda.synchronize()
+        ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                                inp["block_tables"].cpu().numpy(), np.array(lens), np.array(qs),
+                                np.array(qp), scale, causal)
+        compare(to64(out), ref, BF16, "wide paged D=%d causal=%d" % (D, causal))
+
+
+@pytest.mark.parametrize("D", [300, 1023])
+def test_paged_prefill_wide_any_width(D):
+    lens, chunks = [300, 129, 70], [100, 40, 1]
+    nq = sum(chunks)
+    for causal in (False, True):
+        seed = 6200 + D + causal
+        inp = draw_paged(lens, [0] * nq, [0] * nq, 4, 2, D, 16, BF16, seed, DEV)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device=DEV)
+        scale = 1 / math.sqrt(D)
+        out = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                    inp["seq_lens"], cu, scale, causal, max(chunks),
+                                    inp["block_tables"].shape[1] * 16)
+        torch.cuda.synchronize()
+        qs, qp = O.chunk_positions(cu.cpu().numpy(), np.array(lens))
+        ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                                inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, scale,
+                                causal)
+        compare(to64(out), ref, BF16, "wide prefill D=%d causal=%d" % (D, causal))
