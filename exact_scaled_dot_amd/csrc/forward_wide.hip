@@ -209,12 +209,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     // prefill: this sequence's chunk rows (qbase, qstride) and the absolute
     // position qpos0 of its first row.
     int kv_lim = a.Sk, k_lo = 0, seq = 0, nrows = a.Sq, qpos0 = 0;
+    int r0 = 0;  // PAGED prefill: the chunk's first packed row
     const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * D;
     uint16_t* obase = static_cast<uint16_t*>(a.out) + bh * a.Sq * D;
     int64_t qstride = D;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
     if constexpr (PAGED && !DEC) {
-        const int r0 = min(max(dec.cu_q[b], 0), dec.total_q);
+        r0 = min(max(dec.cu_q[b], 0), dec.total_q);
         const int r1 = min(max(dec.cu_q[b + 1], r0), dec.total_q);
         nrows = r1 - r0;
         if (q0 >= nrows) return;  // the whole workgroup, before any barrier
@@ -501,9 +502,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
         return;
     }
     const float inv = 1.f / l;  // a row with no visible key: 0 * inf = NaN
-    if (!PAGED && wave == 0 && kh == 0 && a.lse && qa < a.Sq) {
+    // log-sum-exp of the row (natural log; -inf with no visible key): dense
+    // [B, Hq, Sq], paged prefill [packed rows, Hq]
+    if (wave == 0 && kh == 0 && a.lse && qa < nrows) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        a.lse[bh * a.Sq + qa] = (m_use + __log2f(l)) * 0.69314718055994531f;
+        a.lse[PAGED ? (int64_t)(r0 + qa) * a.Hq + h : bh * a.Sq + qa] = (m_use + __log2f(l)) * 0.69314718055994531f;
     }
 
     // O: register r of d-block db holds dim d0 + 32db + 8*(r/4) + 4*(lane/32)
@@ -613,7 +616,6 @@ hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, b
     w.cu_q = p.cu_seqlens_q;
     w.total_q = p.total_q;
     ForwardArgs b = a;
-    b.lse = nullptr;
     b.bias = nullptr;
     b.padded = false;
     return f16 ? launch_wide_paged_t<F16T>(b, w, s) : launch_wide_paged_t<Bf16T>(b, w, s);

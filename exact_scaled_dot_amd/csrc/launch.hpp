@@ -128,25 +128,26 @@ hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s)
 struct PagedBackwardArgs {
     const void* q;          // [total_q, Hq, D]
     const void* k_cache;    // [pages, page_size, Hkv, D]
-    const void* v_cache;
-    const void* out;        // [total_q, Hq, D], the forward's output
+    const void* v_cache;    // [pages, page_size, Hkv, Dv]
+    const void* out;        // [total_q, Hq, Dv], the forward's output
     const void* dout;
     const float* lse;       // [total_q, Hq], the forward's log-sum-exp
     void* dq;               // [total_q, Hq, D]
     void* dk_cache;         // [pages, page_size, Hkv, D]
-    void* dv_cache;
+    void* dv_cache;         // [pages, page_size, Hkv, Dv]
     const int32_t* block_tables;  // [num_seqs, max_pages]
     const int32_t* seq_lens;      // [num_seqs]
     const int32_t* cu_seqlens_q;  // [num_seqs + 1]
-    int total_q, Hq, Hkv, D, num_seqs, max_pages, pages, page_size, L;
+    int total_q, Hq, Hkv, D, Dv, W, num_seqs, max_pages, pages, page_size, L;
     float scale;
     bool causal;
-    // workspace sections
-    void* qd;    // [num_seqs, Hq, L, D] each: Q, dO, O and dQ at absolute positions
+    // workspace sections, rows W wide (W = max(D, Dv) rounded up to 8; the
+    // dims past D of Q, K, dQ, dK and past Dv of V, O, dO, dV are zeros)
+    void* qd;    // [num_seqs, Hq, L, W] each: Q, dO, O and dQ at absolute positions
     void* dod;
     void* od;
     void* dqd;
-    void* kd;    // [num_seqs, Hkv, L, D] each: K, V, dK, dV of the reachable keys
+    void* kd;    // [num_seqs, Hkv, L, W] each: K, V, dK, dV of the reachable keys
     void* vd;
     void* dkd;
     void* dvd;

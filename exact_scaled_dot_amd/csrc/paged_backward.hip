@@ -12,13 +12,19 @@
 // gradients are those of the dense backward: rows without a query have
 // dO = 0 and probabilities 0, so they add nothing to dK or dV.  So the pass
 // is
-//   1. gathers: Q, dO, O, lse of the chunks into [S, Hq, L, D] at their
+//   1. gathers: Q, dO, O, lse of the chunks into [S, Hq, L, W] at their
 //      positions; K and V of each sequence's reachable keys through its page
-//      table into [S, Hkv, L, D];
+//      table into [S, Hkv, L, W];
 //   2. the ordered dense backward (causal and key padding with key_lens =
-//      seq_lens), deterministic;
+//      seq_lens), deterministic, at head dim W;
 //   3. scatters: dQ back to the packed rows, dK and dV into the cache slots
 //      their keys sit in, every other slot zeroed first.
+// W is the larger of the key and value head dims D and Dv rounded up to a
+// multiple of 8.  The gathers write zeros past D (Q, K) and past Dv (V, O,
+// dO): the scores Q K^T, dO V^T and the row terms rowsum(dO * O) are those
+// of the true widths, and the dims past D of dQ = dS K, dK = dS^T Q and past
+// Dv of dV = P^T dO come out zero and are not scattered.  With D = Dv a
+// multiple of 8 (W = D) the copies move 16-byte chunks; otherwise elements.
 // The page logic lives only in the copies, which are HBM-bound; the
 // backward's tiles are the tuned dense ones.
 #include "device_common.hpp"
@@ -155,18 +161,124 @@ __global__ __launch_bounds__(kPbThreads) void pb_scatter_rows_kernel(PagedBackwa
         live ? reinterpret_cast<const u32x4*>(a.dqd)[(((int64_t)lo * a.Hq + h) * a.L + pos) * cpr + c] : z;
 }
 
+// Element-wise forms (any D, Dv; rows W wide in the workspace).  One thread
+// per element of a W-wide row; consecutive threads take consecutive
+// elements.
+
+__global__ __launch_bounds__(kPbThreads) void pb_gather_rows_elem_kernel(PagedBackwardArgs a) {
+    const int64_t n = (int64_t)a.num_seqs * a.Hq * a.L * a.W;
+    const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
+    if (idx >= n) return;
+    const int e = (int)(idx % a.W);
+    int64_t r = idx / a.W;
+    const int pos = (int)(r % a.L);
+    r /= a.L;
+    const int h = (int)(r % a.Hq);
+    const int s = (int)(r / a.Hq);
+    const ChunkRows cr = chunk_rows(a, s);
+    const int i = pos - cr.qoff;
+    const bool live = pos < cr.kv_lim && i >= 0;
+    const int64_t row = live ? (int64_t)(cr.r0 + i) * a.Hq + h : 0;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+    const uint16_t* out = static_cast<const uint16_t*>(a.out);
+    static_cast<uint16_t*>(a.qd)[idx] = live && e < a.D ? q[row * a.D + e] : (uint16_t)0;
+    static_cast<uint16_t*>(a.dod)[idx] = live && e < a.Dv ? dout[row * a.Dv + e] : (uint16_t)0;
+    static_cast<uint16_t*>(a.od)[idx] = live && e < a.Dv ? out[row * a.Dv + e] : (uint16_t)0;
+    if (e == 0) a.lsed[r * a.L + pos] = live ? a.lse[row] : -INFINITY;
+}
+
+// Physical slot (page row) of logical key j of sequence s, K/V head g; -1
+// when the key is past the sequence or its table entry is outside the cache.
+__device__ __forceinline__ int64_t slot_row(const PagedBackwardArgs& a, int s, int g, int j, int kv_lim) {
+    if (j >= kv_lim) return -1;
+    const int lp = j / a.page_size;
+    const int pg = lp < a.max_pages ? a.block_tables[(int64_t)s * a.max_pages + lp] : -1;
+    if (pg < 0 || pg >= a.pages) return -1;
+    return ((int64_t)pg * a.page_size + j % a.page_size) * a.Hkv + g;
+}
+
+__global__ __launch_bounds__(kPbThreads) void pb_gather_kv_elem_kernel(PagedBackwardArgs a) {
+    const int64_t n = (int64_t)a.num_seqs * a.Hkv * a.L * a.W;
+    const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
+    if (idx >= n) return;
+    const int e = (int)(idx % a.W);
+    int64_t r = idx / a.W;
+    const int j = (int)(r % a.L);
+    r /= a.L;
+    const int g = (int)(r % a.Hkv);
+    const int s = (int)(r / a.Hkv);
+    const int kv_lim = max(0, min(a.seq_lens[s], a.L));
+    const int64_t slot = slot_row(a, s, g, j, kv_lim);
+    const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+    static_cast<uint16_t*>(a.kd)[idx] = slot >= 0 && e < a.D ? kc[slot * a.D + e] : (uint16_t)0;
+    static_cast<uint16_t*>(a.vd)[idx] = slot >= 0 && e < a.Dv ? vc[slot * a.Dv + e] : (uint16_t)0;
+}
+
+// Zero n 16-bit elements of p.
+__global__ __launch_bounds__(kPbThreads) void pb_zero_elem_kernel(uint16_t* p, int64_t n) {
+    const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
+    if (idx < n) p[idx] = 0;
+}
+
+__global__ __launch_bounds__(kPbThreads) void pb_scatter_kv_elem_kernel(PagedBackwardArgs a) {
+    const int64_t n = (int64_t)a.num_seqs * a.Hkv * a.L * a.W;
+    const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
+    if (idx >= n) return;
+    const int e = (int)(idx % a.W);
+    int64_t r = idx / a.W;
+    const int j = (int)(r % a.L);
+    r /= a.L;
+    const int g = (int)(r % a.Hkv);
+    const int s = (int)(r / a.Hkv);
+    const int kv_lim = max(0, min(a.seq_lens[s], a.L));
+    const int64_t slot = slot_row(a, s, g, j, kv_lim);
+    if (slot < 0) return;
+    if (e < a.D) static_cast<uint16_t*>(a.dk_cache)[slot * a.D + e] = static_cast<const uint16_t*>(a.dkd)[idx];
+    if (e < a.Dv) static_cast<uint16_t*>(a.dv_cache)[slot * a.Dv + e] = static_cast<const uint16_t*>(a.dvd)[idx];
+}
+
+__global__ __launch_bounds__(kPbThreads) void pb_scatter_rows_elem_kernel(PagedBackwardArgs a) {
+    const int64_t n = (int64_t)a.total_q * a.Hq * a.D;
+    const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
+    if (idx >= n) return;
+    const int e = (int)(idx % a.D);
+    const int64_t r = idx / a.D;
+    const int h = (int)(r % a.Hq);
+    const int t = (int)(r / a.Hq);
+    int lo = 0, hi = a.num_seqs - 1;  // last s with clamped r0(s) <= t
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (min(max(a.cu_seqlens_q[mid], 0), a.total_q) <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const ChunkRows cr = chunk_rows(a, lo);
+    const int pos = cr.qoff + (t - cr.r0);
+    const bool live = t >= cr.r0 && t < cr.r1 && pos >= 0 && pos < cr.kv_lim;
+    static_cast<uint16_t*>(a.dq)[idx] =
+        live ? static_cast<const uint16_t*>(a.dqd)[(((int64_t)lo * a.Hq + h) * a.L + pos) * a.W + e] : (uint16_t)0;
+}
+
 dim3 grid_of(int64_t n) { return dim3((unsigned)((n + kPbThreads - 1) / kPbThreads)); }
 
 }  // namespace
 
 hipError_t launch_paged_backward_16bit(const PagedBackwardArgs& a, bool f16, hipStream_t s) {
-    if (a.D % 8 != 0 || a.D < 8) return hipErrorInvalidValue;
-    const int64_t cpr = a.D / 8;
+    if (a.D < 1 || a.Dv < 1 || a.W % 8 != 0 || a.W < a.D || a.W < a.Dv || a.W > 512) return hipErrorInvalidValue;
+    // 16-byte chunks when every row is W = D = Dv wide
+    const bool chunks = a.D == a.W && a.Dv == a.W;
+    const int64_t cpr = a.W / 8;
     const int64_t rows = (int64_t)a.num_seqs * a.Hq * a.L * cpr;
     const int64_t kv = (int64_t)a.num_seqs * a.Hkv * a.L * cpr;
     const int64_t cache = (int64_t)a.pages * a.page_size * a.Hkv * cpr;
-    hipLaunchKernelGGL(pb_gather_rows_kernel, grid_of(rows), dim3(kPbThreads), 0, s, a);
-    hipLaunchKernelGGL(pb_gather_kv_kernel, grid_of(kv), dim3(kPbThreads), 0, s, a);
+    if (chunks) {
+        hipLaunchKernelGGL(pb_gather_rows_kernel, grid_of(rows), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_gather_kv_kernel, grid_of(kv), dim3(kPbThreads), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(pb_gather_rows_elem_kernel, grid_of(rows * 8), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_gather_kv_elem_kernel, grid_of(kv * 8), dim3(kPbThreads), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     BackwardArgs b;
@@ -186,17 +298,28 @@ hipError_t launch_paged_backward_16bit(const PagedBackwardArgs& a, bool f16, hip
     b.Hkv = a.Hkv;
     b.Sq = a.L;
     b.Sk = a.L;
-    b.D = a.D;
+    b.D = a.W;
     b.scale = a.scale;
     b.causal = a.causal;
     b.padded = true;
     e = launch_backward_16bit(b, f16, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pb_zero_kernel, grid_of(cache), dim3(kPbThreads), 0, s,
-                       static_cast<u32x4*>(a.dk_cache), static_cast<u32x4*>(a.dv_cache), cache);
-    hipLaunchKernelGGL(pb_scatter_kv_kernel, grid_of(kv), dim3(kPbThreads), 0, s, a);
-    hipLaunchKernelGGL(pb_scatter_rows_kernel, grid_of((int64_t)a.total_q * a.Hq * cpr), dim3(kPbThreads), 0,
-                       s, a);
+    if (chunks) {
+        hipLaunchKernelGGL(pb_zero_kernel, grid_of(cache), dim3(kPbThreads), 0, s,
+                           static_cast<u32x4*>(a.dk_cache), static_cast<u32x4*>(a.dv_cache), cache);
+        hipLaunchKernelGGL(pb_scatter_kv_kernel, grid_of(kv), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_scatter_rows_kernel, grid_of((int64_t)a.total_q * a.Hq * cpr), dim3(kPbThreads),
+                           0, s, a);
+    } else {
+        const int64_t slots = (int64_t)a.pages * a.page_size * a.Hkv;
+        hipLaunchKernelGGL(pb_zero_elem_kernel, grid_of(slots * a.D), dim3(kPbThreads), 0, s,
+                           static_cast<uint16_t*>(a.dk_cache), slots * a.D);
+        hipLaunchKernelGGL(pb_zero_elem_kernel, grid_of(slots * a.Dv), dim3(kPbThreads), 0, s,
+                           static_cast<uint16_t*>(a.dv_cache), slots * a.Dv);
+        hipLaunchKernelGGL(pb_scatter_kv_elem_kernel, grid_of(kv * 8), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_scatter_rows_elem_kernel, grid_of((int64_t)a.total_q * a.Hq * a.D),
+                           dim3(kPbThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -82,6 +82,10 @@ sdpa_status_t check_value_dim(int64_t D, int64_t Dv, int dtype) {
 // so each row starts 16-byte aligned.
 int64_t partial_pitch(int64_t Dv) { return (Dv + 3) & ~int64_t(3); }
 
+// Head dim of the paged backward's dense pass: the larger of D and Dv
+// rounded up to a multiple of 8 (the narrower operands are zero-padded).
+int64_t paged_backward_width(int64_t D, int64_t Dv) { return ((D > Dv ? D : Dv) + 7) & ~int64_t(7); }
+
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -846,9 +850,8 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
-    if (lse && (dtype == SDPA_F32 || D > 256))
-        return fail(SDPA_ERR_UNSUPPORTED,
-                    "the log-sum-exp output needs 16-bit inputs and D up to 256");
+    if (lse && dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "the log-sum-exp output needs 16-bit inputs");
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
@@ -897,9 +900,12 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
 }
 
 size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t Hkv,
-                                          int64_t max_seq_len, int64_t D) {
-    if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || D < 1) return 0;
-    const int64_t rows = numel4(num_seqs, Hq, max_seq_len, D), kv = numel4(num_seqs, Hkv, max_seq_len, D);
+                                          int64_t max_seq_len, int64_t D, int64_t Dv) {
+    if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || D < 1 || Dv < 1 || D > 1 << 20 ||
+        Dv > 1 << 20)
+        return 0;
+    const int64_t W = paged_backward_width(D, Dv);
+    const int64_t rows = numel4(num_seqs, Hq, max_seq_len, W), kv = numel4(num_seqs, Hkv, max_seq_len, W);
     const int64_t l = numel4(num_seqs, Hq, max_seq_len, 1);
     if (rows < 0 || kv < 0 || l < 0 || rows > INT64_MAX / 64 || kv > INT64_MAX / 64) return 0;
     const size_t stats = sdpa_backward_workspace_size(num_seqs, Hq, max_seq_len);
@@ -909,7 +915,8 @@ size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t 
 
 sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void* v_cache,
                                   const void* out, const void* dout, const float* lse,
-                                  int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t pages,
+                                  int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
+                                  int64_t pages,
                                   int64_t page_size, const int32_t* block_tables, int64_t num_seqs,
                                   int64_t max_pages_per_seq, const int32_t* seq_lens,
                                   const int32_t* cu_seqlens_q, int64_t max_seq_len, float scale,
@@ -918,14 +925,15 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
     if (!q || !k_cache || !v_cache || !out || !dout || !lse || !block_tables || !seq_lens ||
         !cu_seqlens_q || !dq || !dk_cache || !dv_cache)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null pointer argument");
-    if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || pages < 1 || page_size < 1 || num_seqs < 1 ||
-        max_pages_per_seq < 1 || max_seq_len < 1)
+    if (total_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || pages < 1 || page_size < 1 ||
+        num_seqs < 1 || max_pages_per_seq < 1 || max_seq_len < 1)
         return fail(SDPA_ERR_INVALID_ARGUMENT,
-                    "every size must be >= 1 (total_q=%lld Hq=%lld Hkv=%lld D=%lld pages=%lld "
-                    "page_size=%lld num_seqs=%lld max_pages_per_seq=%lld max_seq_len=%lld)",
-                    (long long)total_q, (long long)Hq, (long long)Hkv, (long long)D, (long long)pages,
-                    (long long)page_size, (long long)num_seqs, (long long)max_pages_per_seq,
-                    (long long)max_seq_len);
+                    "every size must be >= 1 (total_q=%lld Hq=%lld Hkv=%lld D=%lld Dv=%lld "
+                    "pages=%lld page_size=%lld num_seqs=%lld max_pages_per_seq=%lld "
+                    "max_seq_len=%lld)",
+                    (long long)total_q, (long long)Hq, (long long)Hkv, (long long)D, (long long)Dv,
+                    (long long)pages, (long long)page_size, (long long)num_seqs,
+                    (long long)max_pages_per_seq, (long long)max_seq_len);
     if (Hq % Hkv != 0)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
                     (long long)Hq, (long long)Hkv);
@@ -942,11 +950,13 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
                     (long long)max_seq_len);
     const int64_t es = elem_size(dtype);
     const int64_t nq = numel4(total_q, Hq, D, 1), nc = numel4(pages, page_size, Hkv, D);
+    const int64_t no = numel4(total_q, Hq, Dv, 1), nvc = numel4(pages, page_size, Hkv, Dv);
     const int64_t nt = numel4(num_seqs, max_pages_per_seq, 1, 1);
-    int64_t qbytes = 0, cbytes = 0;
-    if (nq < 0 || nc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) || !mul_ok(nc, es, &cbytes))
+    int64_t qbytes = 0, cbytes = 0, obytes = 0, vcbytes = 0;
+    if (nq < 0 || nc < 0 || no < 0 || nvc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) ||
+        !mul_ok(nc, es, &cbytes) || !mul_ok(no, es, &obytes) || !mul_ok(nvc, es, &vcbytes))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
-    const size_t need = sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D);
+    const size_t need = sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv);
     if (need == 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace size overflows");
     if (!workspace || workspace_bytes < need)
         return fail(SDPA_ERR_WORKSPACE, "paged backward needs a workspace of %zu bytes (got %zu)",
@@ -956,10 +966,10 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
         const void* p;
         int64_t n;
     };
-    const Span ins[] = {{q, qbytes},         {k_cache, cbytes},         {v_cache, cbytes},
-                        {out, qbytes},       {dout, qbytes},            {lse, total_q * Hq * 4},
+    const Span ins[] = {{q, qbytes},         {k_cache, cbytes},         {v_cache, vcbytes},
+                        {out, obytes},       {dout, obytes},            {lse, total_q * Hq * 4},
                         {block_tables, nt * 4}, {seq_lens, num_seqs * 4}, {cu_seqlens_q, (num_seqs + 1) * 4}};
-    const Span outs[] = {{dq, qbytes}, {dk_cache, cbytes}, {dv_cache, cbytes}, {workspace, (int64_t)need}};
+    const Span outs[] = {{dq, qbytes}, {dk_cache, cbytes}, {dv_cache, vcbytes}, {workspace, (int64_t)need}};
     for (const Span& o : outs) {
         for (const Span& i : ins)
             if (overlap(o.p, o.n, i.p, i.n))
@@ -970,24 +980,29 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
     }
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "the paged backward needs 16-bit inputs (bf16 or fp16)");
-    if (!head_dim_ok(D, dtype, 256))
+    if (D > 512 || Dv > 512)
         return fail(SDPA_ERR_UNSUPPORTED,
-                    "head dim D=%lld not supported by the paged backward (a multiple of 8 up to 256)",
-                    (long long)D);
+                    "head dims D=%lld Dv=%lld not supported by the paged backward (any width up to 512)",
+                    (long long)D, (long long)Dv);
+    const int64_t W = paged_backward_width(D, Dv);
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
-    const int64_t rows_chunks = numel4(num_seqs, Hq, max_seq_len, D / 8);
-    const int64_t cache_chunks = numel4(pages, page_size, Hkv, D / 8);
+    // The copies launch one thread per element (per 16-byte chunk when D =
+    // Dv = W): a launch's thread count must fit 32 bits.
+    const int64_t row_elems = numel4(num_seqs, Hq, max_seq_len, W);
+    const int64_t kv_elems = numel4(num_seqs, Hkv, max_seq_len, W);
+    const int64_t cache_elems = numel4(pages, page_size, Hkv, D > Dv ? D : Dv);
     const int64_t qblocks = ((max_seq_len + 127) / 128) * num_seqs * Hq;
+    constexpr int64_t kMaxThreads = (int64_t)UINT32_MAX - 256;
     if (total_q > INT_MAX || Hq > INT_MAX || pages > INT_MAX || num_seqs > INT_MAX ||
-        max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX || rows_chunks < 0 ||
-        rows_chunks / 256 > INT_MAX || cache_chunks < 0 || cache_chunks / 256 > INT_MAX ||
-        qblocks > INT_MAX / 256)
+        max_pages_per_seq > INT_MAX || max_seq_len > INT_MAX || row_elems < 0 ||
+        row_elems > kMaxThreads || kv_elems < 0 || kv_elems > kMaxThreads || cache_elems < 0 ||
+        cache_elems > kMaxThreads || nq > kMaxThreads || qblocks > INT_MAX / 256)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
 
-    const size_t rowsz = (size_t)numel4(num_seqs, Hq, max_seq_len, D) * 2;
-    const size_t kvsz = (size_t)numel4(num_seqs, Hkv, max_seq_len, D) * 2;
+    const size_t rowsz = (size_t)numel4(num_seqs, Hq, max_seq_len, W) * 2;
+    const size_t kvsz = (size_t)numel4(num_seqs, Hkv, max_seq_len, W) * 2;
     char* w = static_cast<char*>(workspace);
     auto take = [&](size_t bytes) {
         char* p = w;
@@ -1011,6 +1026,8 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
     a.Hq = (int)Hq;
     a.Hkv = (int)Hkv;
     a.D = (int)D;
+    a.Dv = (int)Dv;
+    a.W = (int)W;
     a.num_seqs = (int)num_seqs;
     a.max_pages = (int)max_pages_per_seq;
     a.pages = (int)pages;

@@ -99,9 +99,9 @@ def load_library():
     lib.sdpa_paged_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
                                        vp, i64, i64, ctypes.c_float, i32, vp, vp, i32, vp]
     lib.sdpa_paged_backward_workspace_size.restype = ctypes.c_size_t
-    lib.sdpa_paged_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.sdpa_paged_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.sdpa_paged_backward.restype = i32
-    lib.sdpa_paged_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp,
+    lib.sdpa_paged_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp,
                                         i64, i64, vp, vp, i64, ctypes.c_float, i32, vp, vp, vp, vp,
                                         ctypes.c_size_t, i32, vp]
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -560,16 +560,19 @@ def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q
     return out if lse_t is None else (out, lse_t)
 
 
-def sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D):
-    return int(load_library().sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D))
+def sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv=None):
+    Dv = D if Dv is None else Dv
+    return int(load_library().sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D,
+                                                                 Dv))
 
 
 def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_lens, cu_seqlens_q,
                         scale, causal, max_seq_len, dq=None, dk_cache=None, dv_cache=None,
                         workspace=None, stream=None):
-    """Backward of sdpa_paged_prefill: (dq [total_q, Hq, D], dk_cache,
-    dv_cache [pages, page_size, Hkv, D]) for dL/dout = dout, from the
-    forward's out and lse (fp32 [total_q, Hq])."""
+    """Backward of sdpa_paged_prefill: (dq [total_q, Hq, D], dk_cache [pages,
+    page_size, Hkv, D], dv_cache [pages, page_size, Hkv, Dv]) for dL/dout =
+    dout [total_q, Hq, Dv], from the forward's out and lse (fp32 [total_q,
+    Hq])."""
     for name, t, nd in (("q", q, 3), ("k_cache", k_cache, 4), ("v_cache", v_cache, 4),
                         ("out", out, 3), ("dout", dout, 3), ("lse", lse, 2),
                         ("block_tables", block_tables, 2), ("seq_lens", seq_lens, 1),
@@ -581,10 +584,12 @@ def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_l
             raise TypeError("%s must be int32" % name)
     nq, Hq, D = q.shape
     pages, page_size, Hkv, Dk = k_cache.shape
-    if Dk != D or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must be [pages, page_size, Hkv, D] matching q")
-    if out.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("out and dout must be [total_q, Hq, D]")
+    Dv = v_cache.shape[3]
+    if Dk != D or v_cache.shape[:3] != k_cache.shape[:3]:
+        raise ValueError("k_cache must be [pages, page_size, Hkv, D] matching q and v_cache "
+                         "[pages, page_size, Hkv, Dv]")
+    if tuple(out.shape) != (nq, Hq, Dv) or tuple(dout.shape) != (nq, Hq, Dv):
+        raise ValueError("out and dout must be [total_q, Hq, Dv]")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (nq, Hq):
         raise ValueError("lse must be float32 [total_q, Hq]")
     for t in (k_cache, v_cache, out, dout):
@@ -594,7 +599,7 @@ def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_l
     if seq_lens.shape[0] != num_seqs or cu_seqlens_q.shape[0] != num_seqs + 1:
         raise ValueError("seq_lens needs num_seqs entries and cu_seqlens_q num_seqs + 1")
     lib = load_library()
-    need = int(lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, int(max_seq_len), D))
+    need = int(lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, int(max_seq_len), D, Dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
@@ -602,7 +607,7 @@ def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_l
     dv_cache = torch.empty_like(v_cache) if dv_cache is None else dv_cache
     _check(lib.sdpa_paged_backward(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(dout), _ptr(lse), nq, Hq, Hkv, D,
-        pages, page_size, _ptr(block_tables), num_seqs, max_pages, _ptr(seq_lens),
+        Dv, pages, page_size, _ptr(block_tables), num_seqs, max_pages, _ptr(seq_lens),
         _ptr(cu_seqlens_q), int(max_seq_len), float(scale), int(bool(causal)), _ptr(dq),
         _ptr(dk_cache), _ptr(dv_cache), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _dtype_code(q), _stream(stream)))

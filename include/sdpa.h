@@ -410,7 +410,7 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *   lse           device fp32 [total_q, Hq] or NULL: natural-log log-sum-exp
  *                 of each row's scaled scores (-inf for a row with no visible
  *                 key), the input sdpa_paged_backward needs; 16-bit inputs
- *                 with D up to 256 only (SDPA_ERR_UNSUPPORTED otherwise)
+ *                 only (SDPA_ERR_UNSUPPORTED for SDPA_F32)
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
  * SDPA_F16, D any width up to 1024 (above 256 on the head-dim-split kernel)
  * with Dv = D, or D and Dv both any width up to 256 (a value head dim above
@@ -437,12 +437,12 @@ sdpa_status_t sdpa_paged_prefill(const void *q, const void *k_cache, const void 
 /*
  * Bytes of device workspace sdpa_paged_backward needs (0 if the sizes are
  * invalid): Q, dO, O and dQ of every sequence at its absolute positions
- * [num_seqs, Hq, max_seq_len, D] (16-bit), K, V, dK and dV of its reachable
- * keys [num_seqs, Hkv, max_seq_len, D], their fp32 log-sum-exp and the dense
- * backward's statistics.
+ * [num_seqs, Hq, max_seq_len, W] (16-bit), K, V, dK and dV of its reachable
+ * keys [num_seqs, Hkv, max_seq_len, W], their fp32 log-sum-exp and the dense
+ * backward's statistics; W = max(D, Dv) rounded up to a multiple of 8.
  */
 size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t Hkv,
-                                          int64_t max_seq_len, int64_t D);
+                                          int64_t max_seq_len, int64_t D, int64_t Dv);
 
 /*
  * Backward of sdpa_paged_prefill (ruDNN guide section 11: the paged plan's
@@ -450,20 +450,21 @@ size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t 
  * recomputes the probabilities from the forward's log-sum-exp).  For a loss
  * L with dL/dout = dout:
  *   dq        device [total_q, Hq, D]: dL/dq
- *   dk_cache,
- *   dv_cache  device [pages, page_size, Hkv, D]: dL/dk_cache, dL/dv_cache;
+ *   dk_cache  device [pages, page_size, Hkv, D]: dL/dk_cache
+ *   dv_cache  device [pages, page_size, Hkv, Dv]: dL/dv_cache; in both,
  *             every slot a sequence's keys j < seq_lens[s] sit in gets that
  *             key's gradient, every other slot 0 (written in full)
- * Inputs as sdpa_paged_prefill (Dv = D), plus its out and lse (fp32
- * [total_q, Hq]) and dout [total_q, Hq, D].  Each sequence's chunk rows are
- * placed at their absolute positions in dense per-sequence tensors in the
- * workspace (with the zero rows of absent positions adding nothing), the
- * dense ordered backward runs on them (causal flag and key limit seq_lens),
- * and the gradients are scattered back: deterministic, no atomics.
- * Several kernels are enqueued on stream.  Supported: SDPA_BF16 or SDPA_F16,
- * D a multiple of 8 up to 256, page_size a multiple of 16
- * (SDPA_ERR_UNSUPPORTED otherwise).  Outputs and the workspace must overlap
- * no input and each other.
+ * Inputs as sdpa_paged_prefill (V of its own width Dv), plus its out and lse
+ * (fp32 [total_q, Hq]) and dout [total_q, Hq, Dv].  Each sequence's chunk
+ * rows are placed at their absolute positions in dense per-sequence tensors
+ * in the workspace (with the zero rows of absent positions adding nothing),
+ * zero-padded to the common width W (zero dims change no score, row term or
+ * gradient of the true dims); the dense ordered backward runs on them
+ * (causal flag and key limit seq_lens), and the gradients' true dims are
+ * scattered back: deterministic, no atomics.  Several kernels are enqueued
+ * on stream.  Supported: SDPA_BF16 or SDPA_F16, D and Dv any width up to
+ * 512, page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
+ * Outputs and the workspace must overlap no input and each other.
  * Not checked (device data): as sdpa_paged_prefill; in addition every table
  * entry a sequence's keys j < seq_lens[s] use must lie in [0, pages) (an
  * entry outside reads as zero keys and values) and no physical page may be
@@ -472,7 +473,7 @@ size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t 
  */
 sdpa_status_t sdpa_paged_backward(const void *q, const void *k_cache, const void *v_cache,
                                   const void *out, const void *dout, const float *lse,
-                                  int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D,
+                                  int64_t total_q, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                                   int64_t pages, int64_t page_size, const int32_t *block_tables,
                                   int64_t num_seqs, int64_t max_pages_per_seq,
                                   const int32_t *seq_lens, const int32_t *cu_seqlens_q,

@@ -264,7 +264,6 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pag
      "overlaps"),
     (dict(lse=ctypes.c_void_p(0x60000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
     (dict(lse=ctypes.c_void_p(0x7f000000), dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "log-sum-exp"),
-    (dict(lse=ctypes.c_void_p(0x7f000000), D=512), sd.SDPA_ERR_UNSUPPORTED, "log-sum-exp"),
 ])
 def test_paged_prefill_rejects(kw, status, needle):
     assert prefill(**kw) == status
@@ -483,13 +482,14 @@ FAKE_PW = ctypes.c_void_p(0x100000000)
 
 
 def paged_bwd(q=FAKE, k=FAKE_K, v=FAKE_V, out=FAKE_OUT, dout=FAKE_DO, lse=FAKE_LSE, nq=300, Hq=8,
-              Hkv=2, D=128, pages=100, page_size=16, tables=FAKE_T, num_seqs=3, max_pages=50,
+              Hkv=2, D=128, Dv=None, pages=100, page_size=16, tables=FAKE_T, num_seqs=3, max_pages=50,
               seq_lens=FAKE_L, cu=FAKE_C, max_seq_len=800, scale=0.1, causal=1, dq=FAKE_DQ,
               dk=FAKE_DK, dv=FAKE_DV, ws=FAKE_PW, ws_bytes=None, dtype=sd.SDPA_BF16):
     lib = sd.load_library()
+    Dv = D if Dv is None else Dv
     if ws_bytes is None:
-        ws_bytes = lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D)
-    return lib.sdpa_paged_backward(q, k, v, out, dout, lse, nq, Hq, Hkv, D, pages, page_size, tables,
+        ws_bytes = lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv)
+    return lib.sdpa_paged_backward(q, k, v, out, dout, lse, nq, Hq, Hkv, D, Dv, pages, page_size, tables,
                                    num_seqs, max_pages, seq_lens, cu, max_seq_len, scale, causal,
                                    dq, dk, dv, ws, ws_bytes, dtype, None)
 
@@ -507,8 +507,9 @@ def paged_bwd(q=FAKE, k=FAKE_K, v=FAKE_V, out=FAKE_OUT, dout=FAKE_DO, lse=FAKE_L
     (dict(dq=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps an input"),
     (dict(dv=ctypes.c_void_p(0xc0000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap each other"),
     (dict(dtype=sd.SDPA_F32, D=64), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
-    (dict(D=512), sd.SDPA_ERR_UNSUPPORTED, "up to 256"),
-    (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=520, nq=30, pages=10), sd.SDPA_ERR_UNSUPPORTED, "up to 512"),
+    (dict(Dv=513, nq=30, pages=10), sd.SDPA_ERR_UNSUPPORTED, "up to 512"),
+    (dict(Dv=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
 ])
 def test_paged_backward_rejects(kw, status, needle):
@@ -522,8 +523,11 @@ def test_paged_backward_workspace_size():
     def up(x):
         return (x + 255) // 256 * 256
 
-    S, Hq, Hkv, L, D = 3, 8, 2, 800, 128
+    S, Hq, Hkv, L = 3, 8, 2, 800
     stats = lib.sdpa_backward_workspace_size(S, Hq, L)
-    want = 4 * up(S * Hq * L * D * 2) + 4 * up(S * Hkv * L * D * 2) + up(S * Hq * L * 4) + stats
-    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, D) == want
-    assert lib.sdpa_paged_backward_workspace_size(0, Hq, Hkv, L, D) == 0
+    # rows W = max(D, Dv) rounded up to 8 wide
+    for D, Dv, W in [(128, 128, 128), (100, 100, 104), (64, 200, 200), (3, 1, 8), (257, 13, 264)]:
+        want = 4 * up(S * Hq * L * W * 2) + 4 * up(S * Hkv * L * W * 2) + up(S * Hq * L * 4) + stats
+        assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, D, Dv) == want
+    assert lib.sdpa_paged_backward_workspace_size(0, Hq, Hkv, L, 128, 128) == 0
+    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, 128, 0) == 0

@@ -1,6 +1,8 @@
 """GPU parity of the paged backward (sdpa_paged_backward, with the lse output of
 sdpa_paged_prefill) against the oracle's paged_attention_backward: dq and the
-gradients of every cache slot, at the backward bars."""
+gradients of every cache slot, at the backward bars.  Head dims of any width
+up to 512 and a value head dim of its own (ruDNN user guide section 9: D and
+Dv in 1..=1024, forward and first-order backward)."""
 
 import math
 
@@ -19,16 +21,22 @@ DEV = "cuda:0"
 BF16, F16 = torch.bfloat16, torch.float16
 
 
-def run(lens, chunks, Hq, Hkv, D, page_size, causal, dtype, seed, extra_pages=3):
+def run(lens, chunks, Hq, Hkv, D, page_size, causal, dtype, seed, extra_pages=3, Dv=None):
     nq = int(sum(chunks))
     inp = draw_paged(lens, [0] * nq, [0] * nq, Hq, Hkv, D, page_size, dtype, seed, DEV,
                      extra_pages=extra_pages)
+    if Dv is not None and Dv != D:  # V of its own width
+        g = torch.Generator(device=DEV)
+        g.manual_seed(seed + 7919)
+        pages, ps, hk, _ = inp["k_cache"].shape
+        inp["v_cache"] = torch.randn(pages, ps, hk, Dv, generator=g, device=DEV).to(dtype)
+    Dv = inp["v_cache"].shape[3]
     cu = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device=DEV)
     L = inp["block_tables"].shape[1] * page_size
     scale = 1 / math.sqrt(D)
     out, lse = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
                                      inp["seq_lens"], cu, scale, causal, max(chunks), L, lse=True)
-    dout = draw_grad((nq, Hq, D), dtype, seed + 1, DEV)
+    dout = draw_grad((nq, Hq, Dv), dtype, seed + 1, DEV)
     dq, dk, dv = sd.sdpa_paged_backward(inp["q"], inp["k_cache"], inp["v_cache"], out, dout, lse,
                                         inp["block_tables"], inp["seq_lens"], cu, scale, causal, L)
     torch.cuda.synchronize()
@@ -37,13 +45,13 @@ def run(lens, chunks, Hq, Hkv, D, page_size, causal, dtype, seed, extra_pages=3)
     return inp, out, lse, dout, (dq, dk, dv), qs, qp, tables, scale
 
 
-def check(lens, chunks, Hq, Hkv, D, page_size, causal, dtype=BF16, seed=0):
+def check(lens, chunks, Hq, Hkv, D, page_size, causal, dtype=BF16, seed=0, Dv=None):
     inp, out, lse, dout, grads, qs, qp, tables, scale = run(lens, chunks, Hq, Hkv, D, page_size,
-                                                            causal, dtype, seed)
+                                                            causal, dtype, seed, Dv=Dv)
     refs = O.paged_attention_backward(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
                                       to64(dout), tables, np.array(lens), qs, qp, scale, causal)
-    what = "paged bwd lens=%s chunks=%s Hq=%d Hkv=%d D=%d ps=%d causal=%d" % (
-        lens, chunks, Hq, Hkv, D, page_size, causal)
+    what = "paged bwd lens=%s chunks=%s Hq=%d Hkv=%d D=%d Dv=%d ps=%d causal=%d" % (
+        lens, chunks, Hq, Hkv, D, inp["v_cache"].shape[3], page_size, causal)
     for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
         compare_grad(to64(g), r, dtype, what + " " + name)
     # slots no key of any sequence reaches: exactly zero
@@ -98,3 +106,25 @@ def test_paged_backward_deterministic():
     b = run([640, 100], [640, 3], 8, 2, 128, 16, True, BF16, 4400)[4]
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("D", [3, 100, 130, 255])
+def test_paged_backward_any_width(D):
+    # widths that are not multiples of 8: the copies pad to W on the fly
+    check([333, 70], [333, 17], 8, 4, D, 32, True, seed=4500 + D)
+
+
+@pytest.mark.parametrize("D,Dv", [(64, 128), (128, 36), (17, 250), (256, 8)])
+def test_paged_backward_value_width(D, Dv):
+    check([300, 129, 64], [300, 40, 1], 8, 2, D, 16, True, seed=4600 + D + Dv, Dv=Dv)
+
+
+@pytest.mark.parametrize("D", [264, 300, 512])
+def test_paged_backward_wide(D):
+    # above 256: the head-dim-split prefill writes the lse, the head-dim-split
+    # backward runs the dense pass
+    check([200, 90], [200, 31], 4, 2, D, 16, True, seed=4700 + D)
+
+
+def test_paged_backward_value_width_non_causal_fp16():
+    check([500, 64], [77, 64], 8, 8, 96, 16, False, dtype=F16, seed=4800, Dv=40)
