@@ -111,6 +111,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
+// 16 bytes (8 elements) of a row from 2-byte loads, for head dims that are
+// not multiples of 8 (such rows are not 16-byte aligned): element e from byte
+// offset off + 2e when e < valid, else zero.
+__device__ __forceinline__ u32x4 elem16(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w < valid ? off + 4 * w : kOutside, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w + 1 < valid ? off + 4 * w + 2 : kOutside, 0, 0);
+        v[w] = lo | (hi << 16);
+    }
+    return v;
+}
+// Four 16-bit values of a row stored element by element (e < valid).
+__device__ __forceinline__ void store4_elem(uint16_t* p, u32x2 w, int valid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < valid) p[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+}
+
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
 // lds + 16*l (the destination is wave-uniform).
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
@@ -167,6 +187,7 @@ struct BwOffsets {
     int trl[D / 32];  // transposed read, rows 4hg + j/4 of a 16-row step, dims 32db + ...
     int trh[D / 32];  // the same 8 rows further on
     uint32_t dma[L::DMA];  // DMA source offsets (bytes) of this wave's tile slots
+    int dmv[L::DMA];       // elements of each slot inside the row (element-wise loads)
     // DR: head dim in memory (rows DR wide in HBM; chunks at or past DR are
     // pointed outside the buffer and read as zeros).
     __device__ BwOffsets(int wave, int lane, int DR) {
@@ -190,6 +211,7 @@ struct BwOffsets {
             const int s = 64 * (L::DMA * wave + i) + lane;
             const int r = s / L::CPR, c = (s % L::CPR) ^ L::f(r);  // logical chunk
             dma[i] = 8 * c < DR ? (uint32_t)r * DR * 2 + (uint32_t)(c * 16) : kOutside;
+            dmv[i] = min(8, max(0, DR - 8 * c));
         }
     }
 };
@@ -226,7 +248,10 @@ __device__ __forceinline__ int xcd_order(int total) {
 // logical unit u sits at unit u ^ ((r >> 2) & 7), which keeps both the
 // per-lane 8-byte accesses (32 rows, one unit) and the row-major 16-byte
 // ones (4 rows, 4 chunks) free of bank conflicts.
-template <int D, class T, bool GEN = false, bool BIAS = false>
+// ELEM (with GEN, no bias; head dims that are not multiples of 8): Q, dO, O
+// and the K/V tile slots are read element by element (the slots written to
+// LDS by the lane the DMA would have filled), dQ stored element by element.
+template <int D, class T, bool GEN = false, bool BIAS = false, bool ELEM = false>
 __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                                                                const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
@@ -283,9 +308,15 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
         for (int k = 0; k < D / 16; ++k) {
             const int d0 = 16 * k + 8 * hg;
             const uint32_t off = d0 < DR ? (uint32_t)qi * DR * 2 + d0 * 2 : kOutside;
-            qr[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-            dr[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
-            part = dot8<T>(dr[k], __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0), part);
+            if constexpr (ELEM) {
+                qr[k] = elem16(rq, off, DR - d0);
+                dr[k] = elem16(rd, off, DR - d0);
+                part = dot8<T>(dr[k], elem16(ro, off, DR - d0), part);
+            } else {
+                qr[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+                dr[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
+                part = dot8<T>(dr[k], __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0), part);
+            }
         }
         delta = part + swap_half_wave(part);
     }
@@ -357,8 +388,13 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
         uint16_t* dv = dk + L::TILE;
 #pragma unroll
         for (int i = 0; i < L::DMA; ++i) {
-            dma(rk, dk + 512 * i, off.dma[i]);
-            dma(rv, dv + 512 * i, off.dma[i]);
+            if constexpr (ELEM) {  // the slots the DMA would fill: 16 bytes at lane * 16
+                lds_st4(reinterpret_cast<uint32_t*>(dk + 512 * i + 8 * lane), elem16(rk, off.dma[i], off.dmv[i]));
+                lds_st4(reinterpret_cast<uint32_t*>(dv + 512 * i + 8 * lane), elem16(rv, off.dma[i], off.dmv[i]));
+            } else {
+                dma(rk, dk + 512 * i, off.dma[i]);
+                dma(rv, dv + 512 * i, off.dma[i]);
+            }
         }
     };
 
@@ -490,8 +526,9 @@ __global__ __launch_bounds__(kBwThreads, 2) void bwd_dq_kernel(BackwardArgs a,
                 const f32x16& x = acc[db];
                 const u32x2 w = {pack2<T>(x[4 * r4] * a.scale, x[4 * r4 + 1] * a.scale),
                                  pack2<T>(x[4 * r4 + 2] * a.scale, x[4 * r4 + 3] * a.scale)};
-                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
-                if (d0 < DR) *reinterpret_cast<u32x2*>(row + d0) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none (unless ELEM)
+                if constexpr (ELEM) store4_elem(row + d0, w, DR - d0);
+                else if (d0 < DR) *reinterpret_cast<u32x2*>(row + d0) = w;
             }
     }
 }
@@ -535,7 +572,10 @@ constexpr int kKvThreads = 512;  // 8 waves
 // step st has passed (role P reads the bias only before it), so each load
 // has a step and a half to land.  A transposed read then gives a lane its
 // key at 4 consecutive query rows.
-template <int D, class T, bool GEN = false, bool DQ = false, bool BIAS = false>
+// ELEM (with GEN, no bias, no DQ; head dims that are not multiples of 8): K
+// and V rows and the Q/dO tile slots are read element by element, dK and dV
+// stored element by element.
+template <int D, class T, bool GEN = false, bool DQ = false, bool BIAS = false, bool ELEM = false>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                                                                  const int32_t* __restrict__ key_lens) {
     using L = BwGeo<D>;
@@ -587,8 +627,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
             const int d0 = 16 * k + 8 * hg;
-            xr[k] = __builtin_amdgcn_raw_buffer_load_b128(
-                rx, d0 < DR ? (uint32_t)kj * DR * 2 + d0 * 2 : kOutside, 0, 0);
+            const uint32_t off = d0 < DR ? (uint32_t)kj * DR * 2 + d0 * 2 : kOutside;
+            if constexpr (ELEM)
+                xr[k] = elem16(rx, off, DR - d0);
+            else
+                xr[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
         }
     }
 
@@ -615,11 +658,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
 
     const BwOffsets<D> off(0, lane, DR);  // row and transposed read offsets
     uint32_t dmo[DMA];
+    int dmv[DMA];  // (ELEM) elements of each slot inside the row
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
         const int s = 64 * (DMA * wave + i) + lane;
         const int r = s / L::CPR, c = (s % L::CPR) ^ L::f(r);  // logical chunk
         dmo[i] = 8 * c < DR ? (uint32_t)r * DR * 2 + (uint32_t)(c * 16) : kOutside;
+        dmv[i] = min(8, max(0, DR - 8 * c));
     }
 
     // Bias DMA: 2 loads per wave fill slot s = 64*(2*wave + i) + lane of a
@@ -667,8 +712,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
         uint16_t* dd = dq + L::TILE;
 #pragma unroll
         for (int i = 0; i < DMA; ++i) {
-            dma(rq, dq + 512 * i, dmo[i]);
-            dma(rd, dd + 512 * i, dmo[i]);
+            if constexpr (ELEM) {  // the slots the DMA would fill: 16 bytes at lane * 16
+                lds_st4(reinterpret_cast<uint32_t*>(dq + 512 * i + 8 * lane), elem16(rq, dmo[i], dmv[i]));
+                lds_st4(reinterpret_cast<uint32_t*>(dd + 512 * i + 8 * lane), elem16(rd, dmo[i], dmv[i]));
+            } else {
+                dma(rq, dq + 512 * i, dmo[i]);
+                dma(rd, dd + 512 * i, dmo[i]);
+            }
         }
         if (wave == 0) {
             // 8 bytes per row; rows >= Sq read as zeros (and meet zero Q and
@@ -917,8 +967,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BackwardArgs a,
                 const f32x16& x = acc[db];
                 const u32x2 w = {pack2<T>(x[4 * r4] * sc, x[4 * r4 + 1] * sc),
                                  pack2<T>(x[4 * r4 + 2] * sc, x[4 * r4 + 3] * sc)};
-                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
-                if (d0 < DR) *reinterpret_cast<u32x2*>(row + d0) = w;
+                const int d0 = 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none (unless ELEM)
+                if constexpr (ELEM) store4_elem(row + d0, w, DR - d0);
+                else if (d0 < DR) *reinterpret_cast<u32x2*>(row + d0) = w;
             }
     }
 }
@@ -1002,8 +1053,26 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     return a.bias ? launch_backward_db<D, T, GEN, true>(a, s) : launch_backward_db<D, T, GEN, false>(a, s);
 }
 
+// Head dims that are not multiples of 8 (ordered, no bias): the element-wise forms.
+template <int D, class T>
+hipError_t launch_backward_elem(const BackwardArgs& a, hipStream_t s) {
+    const int nqb = (a.Sq + kBwRows - 1) / kBwRows;
+    const int nkb = (a.Sk + kBwRows - 1) / kBwRows;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, true, false, true>), dim3(a.B * a.Hq * nqb), dim3(kBwThreads), 0, s,
+                       a, a.key_lens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, true, false, false, true>), dim3(a.B * a.Hkv * nkb),
+                       dim3(kKvThreads), 0, s, a, a.key_lens);
+    return hipGetLastError();
+}
+
 template <class T>
 hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
+    if (a.D % 8 != 0) {
+        if (a.bias || a.dq_acc) return hipErrorInvalidValue;
+        return a.D < 64 ? launch_backward_elem<64, T>(a, s) : launch_backward_elem<128, T>(a, s);
+    }
     if (a.dq_acc) {  // atomic dQ (no bias variant)
         if (a.bias) return hipErrorInvalidValue;
         if (a.D == 128) return launch_backward_atomic_d<128, T, false>(a, s);
@@ -1022,7 +1091,7 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
 
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s) {
     if (a.D > 128) return launch_backward_wide(a, f16, s);
-    if (a.D % 8 != 0 || a.D < 8 || a.D > 128) return hipErrorInvalidValue;
+    if (a.D < 1 || a.D > 128) return hipErrorInvalidValue;
     return f16 ? launch_backward_t<F16T>(a, s) : launch_backward_t<Bf16T>(a, s);
 }
 

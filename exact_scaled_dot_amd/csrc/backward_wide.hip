@@ -1,4 +1,4 @@
-// Attention backward for head dims above 128, up to 512 (ruDNN user guide
+// Attention backward for head dims above 128, up to 512, of any width (ruDNN user guide
 // section 11: dq, dk, dv recomputed from the forward's log-sum-exp, ordered
 // reductions; section 9 for the head-dim range).  The same three passes as
 // the narrow backward (row statistics, a query-parallel dQ pass, a
@@ -26,6 +26,10 @@
 //     and Q tiles).
 // P and dS enter their products rounded to the input type; dS is formed from
 // the unrounded P; accumulation is fp32.
+// ELEM (head dims that are not multiples of 8): rows are not 16-byte
+// aligned, so Q, dO, O, K and V are read element by element (into the same
+// registers and LDS slots the 16-byte loads and the DMA fill) and dQ, dK, dV
+// are stored element by element.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -67,6 +71,27 @@ __device__ __forceinline__ void x_lds_barrier() {
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void x_lds_st4(uint16_t* __restrict__ p, u32x4 v) {
+    *(__attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) char*)p) = v;
+}
+// 16 bytes (8 elements) of a row from 2-byte loads: element e from byte
+// offset off + 2e when e < valid, else zero.
+__device__ __forceinline__ u32x4 x_elem16(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w < valid ? off + 4 * w : kXOut, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * w + 1 < valid ? off + 4 * w + 2 : kXOut, 0, 0);
+        v[w] = lo | (hi << 16);
+    }
+    return v;
+}
+// Four 16-bit values stored element by element (e < valid).
+__device__ __forceinline__ void x_store4(uint16_t* p, u32x2 w, int valid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < valid) p[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
 }
 __device__ __forceinline__ void x_dma(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (x_lds_void*)((__attribute__((address_space(3))) char*)lds), 16,
@@ -118,15 +143,29 @@ struct XTr {
 // Row statistics for both passes: (lse * log2e, rowsum(dO o O)) per query row,
 // (+inf, 0) for a row with no visible key (lse = -inf).  One wave per row,
 // 8 dims per lane.
-template <class T>
+template <class T, bool ELEM = false>
 __global__ __launch_bounds__(256) void bwd_wide_stats_kernel(BackwardArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= (int64_t)a.B * a.Hq * a.Sq) return;
     float part = 0.f;
     if (8 * lane < a.D) {
-        const u32x4 o = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.out) + row * a.D + 8 * lane);
-        const u32x4 d = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + row * a.D + 8 * lane);
+        u32x4 o, d;
+        if constexpr (ELEM) {  // rows not 16-byte aligned: element by element, zeros past D
+            const uint16_t* orow = static_cast<const uint16_t*>(a.out) + row * a.D + 8 * lane;
+            const uint16_t* drow = static_cast<const uint16_t*>(a.dout) + row * a.D + 8 * lane;
+            const int n = min(8, a.D - 8 * lane);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t o0 = 2 * w < n ? orow[2 * w] : 0u, o1 = 2 * w + 1 < n ? orow[2 * w + 1] : 0u;
+                const uint32_t d0 = 2 * w < n ? drow[2 * w] : 0u, d1 = 2 * w + 1 < n ? drow[2 * w + 1] : 0u;
+                o[w] = o0 | (o1 << 16);
+                d[w] = d0 | (d1 << 16);
+            }
+        } else {
+            o = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.out) + row * a.D + 8 * lane);
+            d = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + row * a.D + 8 * lane);
+        }
         const uint32_t os[4] = {o[0], o[1], o[2], o[3]}, ds[4] = {d[0], d[1], d[2], d[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -159,7 +198,7 @@ struct XLds {
 };
 
 // ---------------------------------------------------------------- dQ pass
-template <int NW, class T>
+template <int NW, class T, bool ELEM = false>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a, const int32_t* __restrict__ key_lens) {
     using LY = XLds<NW>;
     // one partial buffer (a second barrier per tile): 40 KB at NW = 2, four
@@ -203,8 +242,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
             for (int s = 0; s < 4; ++s) {
                 const int row = q0 + 16 * qb + l16, dim = d0 + 32 * s + 8 * g4;
                 const uint32_t o = (row < a.Sq && dim < D) ? ((uint32_t)row * D + dim) * 2 : kXOut;
-                qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
-                df[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, 0);
+                if constexpr (ELEM) {
+                    qf[qb][s] = x_elem16(rq, o, D - dim);
+                    df[qb][s] = x_elem16(rd, o, D - dim);
+                } else {
+                    qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+                    df[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, 0);
+                }
             }
     }
     // this lane's query: (lse2, delta)
@@ -227,8 +271,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * i + g4, c = (lane & 15) ^ x_f(r);
             const uint32_t o = d0 + 8 * c < D ? ((uint32_t)(kt + r) * D + d0 + 8 * c) * 2 : kXOut;
-            x_dma(rk, base + 512 * i, o);
-            x_dma(rv, base + kXTileEl + 512 * i, o);
+            if constexpr (ELEM) {  // the slots the DMA would fill: 16 bytes at lane * 16
+                x_lds_st4(base + 512 * i + 8 * lane, x_elem16(rk, o, D - d0 - 8 * c));
+                x_lds_st4(base + kXTileEl + 512 * i + 8 * lane, x_elem16(rv, o, D - d0 - 8 * c));
+            } else {
+                x_dma(rk, base + 512 * i, o);
+                x_dma(rv, base + kXTileEl + 512 * i, o);
+            }
         }
     };
     const XTr tr(lane);
@@ -310,16 +359,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dq_kernel(BackwardArgs a,
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int dim = d0 + 32 * db + 8 * r4 + 4 * kh;
                 const f32x16& x = acc[db];
-                if (dim < D)
-                    *reinterpret_cast<u32x2*>(row + dim) =
-                        u32x2{pack2<T>(x[4 * r4] * a.scale, x[4 * r4 + 1] * a.scale),
-                              pack2<T>(x[4 * r4 + 2] * a.scale, x[4 * r4 + 3] * a.scale)};
+                const u32x2 w = {pack2<T>(x[4 * r4] * a.scale, x[4 * r4 + 1] * a.scale),
+                                 pack2<T>(x[4 * r4 + 2] * a.scale, x[4 * r4 + 3] * a.scale)};
+                if constexpr (ELEM) x_store4(row + dim, w, D - dim);
+                else if (dim < D) *reinterpret_cast<u32x2*>(row + dim) = w;
             }
     }
 }
 
 // ---------------------------------------------------------------- dK/dV pass
-template <int NW, class T>
+template <int NW, class T, bool ELEM = false>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dkdv_kernel(BackwardArgs a,
                                                                    const int32_t* __restrict__ key_lens) {
     using LY = XLds<NW>;
@@ -356,8 +405,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dkdv_kernel(BackwardArgs 
             for (int s = 0; s < 4; ++s) {
                 const int row = k0 + 16 * kb + l16, dim = d0 + 32 * s + 8 * g4;
                 const uint32_t o = (row < a.Sk && dim < D) ? ((uint32_t)row * D + dim) * 2 : kXOut;
-                kf[kb][s] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
-                vf[kb][s] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
+                if constexpr (ELEM) {
+                    kf[kb][s] = x_elem16(rk, o, D - dim);
+                    vf[kb][s] = x_elem16(rv, o, D - dim);
+                } else {
+                    kf[kb][s] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+                    vf[kb][s] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
+                }
             }
     }
 
@@ -384,8 +438,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dkdv_kernel(BackwardArgs 
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * i + g4, c = (lane & 15) ^ x_f(r);
             const uint32_t o = (q0 + r < a.Sq && d0 + 8 * c < D) ? ((uint32_t)(q0 + r) * D + d0 + 8 * c) * 2 : kXOut;
-            x_dma(rq, base + 512 * i, o);
-            x_dma(rd, base + kXTileEl + 512 * i, o);
+            if constexpr (ELEM) {  // the slots the DMA would fill: 16 bytes at lane * 16
+                x_lds_st4(base + 512 * i + 8 * lane, x_elem16(rq, o, D - d0 - 8 * c));
+                x_lds_st4(base + kXTileEl + 512 * i + 8 * lane, x_elem16(rd, o, D - d0 - 8 * c));
+            } else {
+                x_dma(rq, base + 512 * i, o);
+                x_dma(rd, base + kXTileEl + 512 * i, o);
+            }
         }
         const int64_t srow = bh * ((a.Sq + 1) & ~1);
         const __amdgpu_buffer_rsrc_t rs =
@@ -479,46 +538,51 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_wide_dkdv_kernel(BackwardArgs 
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int dim = d0 + 32 * db + 8 * r4 + 4 * kh;
-                if (dim < D) {
-                    const f32x16& xk = acck[db];
-                    const f32x16& xv = accv[db];
-                    *reinterpret_cast<u32x2*>(krow + dim) =
-                        u32x2{pack2<T>(xk[4 * r4] * sk, xk[4 * r4 + 1] * sk),
-                              pack2<T>(xk[4 * r4 + 2] * sk, xk[4 * r4 + 3] * sk)};
-                    *reinterpret_cast<u32x2*>(vrow + dim) =
-                        u32x2{pack2<T>(xv[4 * r4] * sv1, xv[4 * r4 + 1] * sv1),
-                              pack2<T>(xv[4 * r4 + 2] * sv1, xv[4 * r4 + 3] * sv1)};
+                const f32x16& xk = acck[db];
+                const f32x16& xv = accv[db];
+                const u32x2 wk = {pack2<T>(xk[4 * r4] * sk, xk[4 * r4 + 1] * sk),
+                                  pack2<T>(xk[4 * r4 + 2] * sk, xk[4 * r4 + 3] * sk)};
+                const u32x2 wv = {pack2<T>(xv[4 * r4] * sv1, xv[4 * r4 + 1] * sv1),
+                                  pack2<T>(xv[4 * r4 + 2] * sv1, xv[4 * r4 + 3] * sv1)};
+                if constexpr (ELEM) {
+                    x_store4(krow + dim, wk, D - dim);
+                    x_store4(vrow + dim, wv, D - dim);
+                } else if (dim < D) {
+                    *reinterpret_cast<u32x2*>(krow + dim) = wk;
+                    *reinterpret_cast<u32x2*>(vrow + dim) = wv;
                 }
             }
     }
 }
 
-template <int NW, class T>
+template <int NW, class T, bool ELEM>
 hipError_t launch_bw_wide_nw(const BackwardArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-    hipLaunchKernelGGL(bwd_wide_stats_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_wide_stats_kernel<T, ELEM>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqb = (a.Sq + kXRows - 1) / kXRows;
-    hipLaunchKernelGGL((bwd_wide_dq_kernel<NW, T>), dim3((unsigned)(a.B * a.Hq * nqb)), dim3(NW * 64), 0, s, a,
-                       a.key_lens);
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<NW, T, ELEM>), dim3((unsigned)(a.B * a.Hq * nqb)), dim3(NW * 64), 0, s,
+                       a, a.key_lens);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkb = (a.Sk + kXRows - 1) / kXRows;
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<NW, T>), dim3((unsigned)(a.B * a.Hkv * nkb)), dim3(NW * 64), 0, s, a,
-                       a.key_lens);
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<NW, T, ELEM>), dim3((unsigned)(a.B * a.Hkv * nkb)), dim3(NW * 64), 0,
+                       s, a, a.key_lens);
     return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_bw_wide_t(const BackwardArgs& a, hipStream_t s) {
-    return a.D <= 2 * kXChunk ? launch_bw_wide_nw<2, T>(a, s) : launch_bw_wide_nw<4, T>(a, s);
+    if (a.D % 8 != 0)
+        return a.D <= 2 * kXChunk ? launch_bw_wide_nw<2, T, true>(a, s) : launch_bw_wide_nw<4, T, true>(a, s);
+    return a.D <= 2 * kXChunk ? launch_bw_wide_nw<2, T, false>(a, s) : launch_bw_wide_nw<4, T, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_backward_wide(const BackwardArgs& a, bool f16, hipStream_t s) {
-    if (a.D <= 128 || a.D > 4 * kXChunk || a.D % 8 != 0 || a.bias || a.dq_acc) return hipErrorInvalidValue;
+    if (a.D <= 128 || a.D > 4 * kXChunk || a.bias || a.dq_acc) return hipErrorInvalidValue;
     return f16 ? launch_bw_wide_t<F16T>(a, s) : launch_bw_wide_t<Bf16T>(a, s);
 }
 

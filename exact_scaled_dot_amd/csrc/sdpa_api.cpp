@@ -295,10 +295,11 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
     if (!out || !dout || !lse || !dk || !dv)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     int64_t qbytes = 0, kbytes = 0;
-    // head dims up to 512 on the ordered backward without a bias (above 128
-    // on the head-dim-split kernels), up to 128 with a bias or atomic dQ
+    // head dims of any width up to 512 on the ordered backward without a
+    // bias (above 128 on the head-dim-split kernels); multiples of 8 up to
+    // 128 with a bias or atomic dQ
     sdpa_status_t st = check_common(q, k, v, dq, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
-                                    &kbytes, (atomic || bias) ? 128 : 512);
+                                    &kbytes, (atomic || bias) ? 128 : 512, !(atomic || bias));
     if (st != SDPA_OK) return st;
     if (dtype == SDPA_F32)
         return fail(SDPA_ERR_UNSUPPORTED, "the backward needs 16-bit inputs (bf16 or fp16)");

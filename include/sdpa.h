@@ -178,8 +178,9 @@ size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq);
  * guide's ordered, atomic-free reduction).  Accumulation is fp32; P and dS are
  * rounded to dtype before their products, and the gradients to dtype at the end.
  * Outputs and workspace must not overlap each other or any input.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D a multiple of 8 up to 512
- * (ruDNN user guide section 9; SDPA_ERR_UNSUPPORTED above).
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 512 (ruDNN user
+ * guide section 9; SDPA_ERR_UNSUPPORTED above); a width that is not a
+ * multiple of 8 is read and written element by element.
  */
 sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const void *out,
                             const void *dout, const float *lse,

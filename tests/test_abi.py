@@ -397,6 +397,11 @@ def test_backward_atomic_workspace_and_rejects():
                                   136, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, 1 << 30,
                                   sd.SDPA_BF16, None)
     assert st == sd.SDPA_ERR_UNSUPPORTED and "up to 128" in sd.last_error()
+    # and multiples of 8 only
+    st = lib.sdpa_backward_atomic(FAKE, FAKE_K, FAKE_V, FAKE_O, FAKE_DO, FAKE_L, 2, 4, 2, 128, 128,
+                                  100, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, 1 << 30,
+                                  sd.SDPA_BF16, None)
+    assert st == sd.SDPA_ERR_UNSUPPORTED and "a multiple of 8" in sd.last_error()
 
 
 def block(x=FAKE, wq=FAKE_K, wk=FAKE_V, wv=FAKE_O, wo=FAKE_W, B=2, S=128, model=512, heads=8,
@@ -457,6 +462,7 @@ def bwdb(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128,
     (dict(dout=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
     (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
     (dict(D=136), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),
+    (dict(D=100), sd.SDPA_ERR_UNSUPPORTED, "a multiple of 8"),
     (dict(sb=-8), sd.SDPA_ERR_INVALID_ARGUMENT, "strides"),
     (dict(sh=12), sd.SDPA_ERR_UNSUPPORTED, "16-byte aligned"),
     (dict(Sq=120, Sk=124), sd.SDPA_ERR_UNSUPPORTED, "16-byte aligned"),

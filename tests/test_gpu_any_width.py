@@ -275,3 +275,35 @@ def test_paged_prefill_wide_any_width(D):
                                 inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, scale,
                                 causal)
         compare(to64(out), ref, BF16, "wide prefill D=%d causal=%d" % (D, causal))
+
+
+# ------------------------------------------------ the dense ordered backward
+
+
+def backward_case(B, Hq, Hkv, Sq, Sk, D, mask, lens, dtype, seed):
+    from exact_scaled_dot_amd.workloads import draw_grad
+    from parity import compare_grad
+    q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, dtype, seed, DEV)
+    dout = draw_grad((B, Hq, Sq, D), dtype, seed + 1, DEV)
+    kl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, kl)
+    dq, dk, dv = sd.sdpa_backward(q, k, v, out, dout, lse, scale, mask, kl)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.sdpa_backward(to64(q), to64(k), to64(v), to64(dout), scale, mask,
+                                 None if lens is None else np.array(lens))
+    what = "backward D=%d mask=%d" % (D, mask)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        compare_grad(to64(g), r, dtype, what + " " + name)
+
+
+@pytest.mark.parametrize("D", [3, 36, 100, 130, 257, 300, 511])
+@pytest.mark.parametrize("mask", [1, 2], ids=["causal", "padding"])
+def test_backward_any_width(D, mask):
+    # ragged lengths (300 = 4 tiles of 64 + 44), grouped K/V heads
+    lens = [300, 97] if mask & 2 else None
+    backward_case(2, 4, 2, 300, 300, D, mask, lens, BF16, 6300 + D + mask)
+
+
+def test_backward_any_width_fp16_rectangular():
+    backward_case(2, 6, 3, 130, 333, 77, 2, [333, 45], F16, 6400)
