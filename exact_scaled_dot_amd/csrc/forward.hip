@@ -786,8 +786,9 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
     float* op;
     int64_t rstride;  // floats between consecutive query (and output) rows
     int nrows, qoff, kv_lim, kv_end;
+    int r0 = 0;  // paged: first packed row of the chunk
     if (PAGED) {
-        const int r0 = min(max(cu_q[ti.b], 0), p.total_q);
+        r0 = min(max(cu_q[ti.b], 0), p.total_q);
         const int r1 = min(max(cu_q[ti.b + 1], r0), p.total_q);
         nrows = r1 - r0;
         if (ti.q0 >= nrows) return;  // the whole workgroup: no barrier reached yet
@@ -956,6 +957,11 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
 
     const float lt = l_run + swap_half_wave(l_run);
     const float inv = 1.f / lt;
+    // Optional log-sum-exp (natural log; -inf for a row with no visible key):
+    // dense [B, Hq, Sq], paged [packed rows, Hq].  m_run is in log2 units.
+    if (a.lse && hg == 0 && qi < nrows)
+        a.lse[PAGED ? (int64_t)(r0 + qi) * a.Hq + ti.h : ((int64_t)ti.b * a.Hq + ti.h) * a.Sq + qi] =
+            m_run == -INFINITY ? -INFINITY : (m_run + __log2f(lt)) * 0.69314718055994531f;
     if (qi < nrows) {
         float* orow = op + (int64_t)qi * rstride;
 #pragma unroll

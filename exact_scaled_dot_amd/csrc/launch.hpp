@@ -121,6 +121,8 @@ hipError_t launch_gemm_16bit(const GemmArgs& g, bool f16, hipStream_t s);
 
 // Backward: the dQ pass (also writes delta), then the dK / dV pass.
 hipError_t launch_backward_16bit(const BackwardArgs& a, bool f16, hipStream_t s);
+// fp32 inputs: ordered backward without a bias, D a multiple of 4 up to 128.
+hipError_t launch_backward_f32(const BackwardArgs& a, hipStream_t s);
 
 // Attention backward through a page cache (packed prefill chunks of the paged
 // forward): gathers into the dense sections, the dense ordered backward,
@@ -155,6 +157,8 @@ struct PagedBackwardArgs {
     float* stats;  // the dense backward's workspace
 };
 hipError_t launch_paged_backward_16bit(const PagedBackwardArgs& a, bool f16, hipStream_t s);
+// fp32 caches and rows (D = Dv = W a multiple of 4 up to 128).
+hipError_t launch_paged_backward_f32(const PagedBackwardArgs& a, hipStream_t s);
 // Ordered backward without a bias for 128 < D <= 512 (head dim split across waves).
 hipError_t launch_backward_wide(const BackwardArgs& a, bool f16, hipStream_t s);
 

@@ -161,10 +161,11 @@ __global__ __launch_bounds__(kPbThreads) void pb_scatter_rows_kernel(PagedBackwa
         live ? reinterpret_cast<const u32x4*>(a.dqd)[(((int64_t)lo * a.Hq + h) * a.L + pos) * cpr + c] : z;
 }
 
-// Element-wise forms (any D, Dv; rows W wide in the workspace).  One thread
-// per element of a W-wide row; consecutive threads take consecutive
-// elements.
+// Element-wise forms (any D, Dv; rows W wide in the workspace), for 16-bit
+// (E = uint16_t) or fp32 (E = float) elements.  One thread per element of a
+// W-wide row; consecutive threads take consecutive elements.
 
+template <class E>
 __global__ __launch_bounds__(kPbThreads) void pb_gather_rows_elem_kernel(PagedBackwardArgs a) {
     const int64_t n = (int64_t)a.num_seqs * a.Hq * a.L * a.W;
     const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
@@ -179,12 +180,12 @@ __global__ __launch_bounds__(kPbThreads) void pb_gather_rows_elem_kernel(PagedBa
     const int i = pos - cr.qoff;
     const bool live = pos < cr.kv_lim && i >= 0;
     const int64_t row = live ? (int64_t)(cr.r0 + i) * a.Hq + h : 0;
-    const uint16_t* q = static_cast<const uint16_t*>(a.q);
-    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-    const uint16_t* out = static_cast<const uint16_t*>(a.out);
-    static_cast<uint16_t*>(a.qd)[idx] = live && e < a.D ? q[row * a.D + e] : (uint16_t)0;
-    static_cast<uint16_t*>(a.dod)[idx] = live && e < a.Dv ? dout[row * a.Dv + e] : (uint16_t)0;
-    static_cast<uint16_t*>(a.od)[idx] = live && e < a.Dv ? out[row * a.Dv + e] : (uint16_t)0;
+    const E* q = static_cast<const E*>(a.q);
+    const E* dout = static_cast<const E*>(a.dout);
+    const E* out = static_cast<const E*>(a.out);
+    static_cast<E*>(a.qd)[idx] = live && e < a.D ? q[row * a.D + e] : E(0);
+    static_cast<E*>(a.dod)[idx] = live && e < a.Dv ? dout[row * a.Dv + e] : E(0);
+    static_cast<E*>(a.od)[idx] = live && e < a.Dv ? out[row * a.Dv + e] : E(0);
     if (e == 0) a.lsed[r * a.L + pos] = live ? a.lse[row] : -INFINITY;
 }
 
@@ -198,6 +199,7 @@ __device__ __forceinline__ int64_t slot_row(const PagedBackwardArgs& a, int s, i
     return ((int64_t)pg * a.page_size + j % a.page_size) * a.Hkv + g;
 }
 
+template <class E>
 __global__ __launch_bounds__(kPbThreads) void pb_gather_kv_elem_kernel(PagedBackwardArgs a) {
     const int64_t n = (int64_t)a.num_seqs * a.Hkv * a.L * a.W;
     const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
@@ -210,18 +212,20 @@ __global__ __launch_bounds__(kPbThreads) void pb_gather_kv_elem_kernel(PagedBack
     const int s = (int)(r / a.Hkv);
     const int kv_lim = max(0, min(a.seq_lens[s], a.L));
     const int64_t slot = slot_row(a, s, g, j, kv_lim);
-    const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-    static_cast<uint16_t*>(a.kd)[idx] = slot >= 0 && e < a.D ? kc[slot * a.D + e] : (uint16_t)0;
-    static_cast<uint16_t*>(a.vd)[idx] = slot >= 0 && e < a.Dv ? vc[slot * a.Dv + e] : (uint16_t)0;
+    const E* kc = static_cast<const E*>(a.k_cache);
+    const E* vc = static_cast<const E*>(a.v_cache);
+    static_cast<E*>(a.kd)[idx] = slot >= 0 && e < a.D ? kc[slot * a.D + e] : E(0);
+    static_cast<E*>(a.vd)[idx] = slot >= 0 && e < a.Dv ? vc[slot * a.Dv + e] : E(0);
 }
 
-// Zero n 16-bit elements of p.
-__global__ __launch_bounds__(kPbThreads) void pb_zero_elem_kernel(uint16_t* p, int64_t n) {
+// Zero n elements of p.
+template <class E>
+__global__ __launch_bounds__(kPbThreads) void pb_zero_elem_kernel(E* p, int64_t n) {
     const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
-    if (idx < n) p[idx] = 0;
+    if (idx < n) p[idx] = E(0);
 }
 
+template <class E>
 __global__ __launch_bounds__(kPbThreads) void pb_scatter_kv_elem_kernel(PagedBackwardArgs a) {
     const int64_t n = (int64_t)a.num_seqs * a.Hkv * a.L * a.W;
     const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
@@ -235,10 +239,11 @@ __global__ __launch_bounds__(kPbThreads) void pb_scatter_kv_elem_kernel(PagedBac
     const int kv_lim = max(0, min(a.seq_lens[s], a.L));
     const int64_t slot = slot_row(a, s, g, j, kv_lim);
     if (slot < 0) return;
-    if (e < a.D) static_cast<uint16_t*>(a.dk_cache)[slot * a.D + e] = static_cast<const uint16_t*>(a.dkd)[idx];
-    if (e < a.Dv) static_cast<uint16_t*>(a.dv_cache)[slot * a.Dv + e] = static_cast<const uint16_t*>(a.dvd)[idx];
+    if (e < a.D) static_cast<E*>(a.dk_cache)[slot * a.D + e] = static_cast<const E*>(a.dkd)[idx];
+    if (e < a.Dv) static_cast<E*>(a.dv_cache)[slot * a.Dv + e] = static_cast<const E*>(a.dvd)[idx];
 }
 
+template <class E>
 __global__ __launch_bounds__(kPbThreads) void pb_scatter_rows_elem_kernel(PagedBackwardArgs a) {
     const int64_t n = (int64_t)a.total_q * a.Hq * a.D;
     const int64_t idx = (int64_t)blockIdx.x * kPbThreads + threadIdx.x;
@@ -256,8 +261,8 @@ __global__ __launch_bounds__(kPbThreads) void pb_scatter_rows_elem_kernel(PagedB
     const ChunkRows cr = chunk_rows(a, lo);
     const int pos = cr.qoff + (t - cr.r0);
     const bool live = t >= cr.r0 && t < cr.r1 && pos >= 0 && pos < cr.kv_lim;
-    static_cast<uint16_t*>(a.dq)[idx] =
-        live ? static_cast<const uint16_t*>(a.dqd)[(((int64_t)lo * a.Hq + h) * a.L + pos) * a.W + e] : (uint16_t)0;
+    static_cast<E*>(a.dq)[idx] =
+        live ? static_cast<const E*>(a.dqd)[(((int64_t)lo * a.Hq + h) * a.L + pos) * a.W + e] : E(0);
 }
 
 dim3 grid_of(int64_t n) { return dim3((unsigned)((n + kPbThreads - 1) / kPbThreads)); }
@@ -276,8 +281,8 @@ hipError_t launch_paged_backward_16bit(const PagedBackwardArgs& a, bool f16, hip
         hipLaunchKernelGGL(pb_gather_rows_kernel, grid_of(rows), dim3(kPbThreads), 0, s, a);
         hipLaunchKernelGGL(pb_gather_kv_kernel, grid_of(kv), dim3(kPbThreads), 0, s, a);
     } else {
-        hipLaunchKernelGGL(pb_gather_rows_elem_kernel, grid_of(rows * 8), dim3(kPbThreads), 0, s, a);
-        hipLaunchKernelGGL(pb_gather_kv_elem_kernel, grid_of(kv * 8), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_gather_rows_elem_kernel<uint16_t>, grid_of(rows * 8), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_gather_kv_elem_kernel<uint16_t>, grid_of(kv * 8), dim3(kPbThreads), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -312,14 +317,58 @@ hipError_t launch_paged_backward_16bit(const PagedBackwardArgs& a, bool f16, hip
                            0, s, a);
     } else {
         const int64_t slots = (int64_t)a.pages * a.page_size * a.Hkv;
-        hipLaunchKernelGGL(pb_zero_elem_kernel, grid_of(slots * a.D), dim3(kPbThreads), 0, s,
+        hipLaunchKernelGGL(pb_zero_elem_kernel<uint16_t>, grid_of(slots * a.D), dim3(kPbThreads), 0, s,
                            static_cast<uint16_t*>(a.dk_cache), slots * a.D);
-        hipLaunchKernelGGL(pb_zero_elem_kernel, grid_of(slots * a.Dv), dim3(kPbThreads), 0, s,
+        hipLaunchKernelGGL(pb_zero_elem_kernel<uint16_t>, grid_of(slots * a.Dv), dim3(kPbThreads), 0, s,
                            static_cast<uint16_t*>(a.dv_cache), slots * a.Dv);
-        hipLaunchKernelGGL(pb_scatter_kv_elem_kernel, grid_of(kv * 8), dim3(kPbThreads), 0, s, a);
-        hipLaunchKernelGGL(pb_scatter_rows_elem_kernel, grid_of((int64_t)a.total_q * a.Hq * a.D),
+        hipLaunchKernelGGL(pb_scatter_kv_elem_kernel<uint16_t>, grid_of(kv * 8), dim3(kPbThreads), 0, s, a);
+        hipLaunchKernelGGL(pb_scatter_rows_elem_kernel<uint16_t>, grid_of((int64_t)a.total_q * a.Hq * a.D),
                            dim3(kPbThreads), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+// fp32: the same three stages with fp32 copies (W = D = Dv) and the fp32
+// dense backward.
+hipError_t launch_paged_backward_f32(const PagedBackwardArgs& a, hipStream_t s) {
+    if (a.D != a.Dv || a.W != a.D || a.D % 4 != 0 || a.D < 4 || a.D > 128) return hipErrorInvalidValue;
+    const int64_t rows = (int64_t)a.num_seqs * a.Hq * a.L * a.W;
+    const int64_t kv = (int64_t)a.num_seqs * a.Hkv * a.L * a.W;
+    const int64_t slots = (int64_t)a.pages * a.page_size * a.Hkv;
+    hipLaunchKernelGGL(pb_gather_rows_elem_kernel<float>, grid_of(rows), dim3(kPbThreads), 0, s, a);
+    hipLaunchKernelGGL(pb_gather_kv_elem_kernel<float>, grid_of(kv), dim3(kPbThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    BackwardArgs b;
+    b.q = a.qd;
+    b.k = a.kd;
+    b.v = a.vd;
+    b.out = a.od;
+    b.dout = a.dod;
+    b.lse = a.lsed;
+    b.key_lens = a.seq_lens;
+    b.dq = a.dqd;
+    b.dk = a.dkd;
+    b.dv = a.dvd;
+    b.delta = a.stats;
+    b.B = a.num_seqs;
+    b.Hq = a.Hq;
+    b.Hkv = a.Hkv;
+    b.Sq = a.L;
+    b.Sk = a.L;
+    b.D = a.W;
+    b.scale = a.scale;
+    b.causal = a.causal;
+    b.padded = true;
+    e = launch_backward_f32(b, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pb_zero_elem_kernel<float>, grid_of(slots * a.D), dim3(kPbThreads), 0, s,
+                       static_cast<float*>(a.dk_cache), slots * a.D);
+    hipLaunchKernelGGL(pb_zero_elem_kernel<float>, grid_of(slots * a.D), dim3(kPbThreads), 0, s,
+                       static_cast<float*>(a.dv_cache), slots * a.D);
+    hipLaunchKernelGGL(pb_scatter_kv_elem_kernel<float>, grid_of(kv), dim3(kPbThreads), 0, s, a);
+    hipLaunchKernelGGL(pb_scatter_rows_elem_kernel<float>, grid_of((int64_t)a.total_q * a.Hq * a.D),
+                       dim3(kPbThreads), 0, s, a);
     return hipGetLastError();
 }
 

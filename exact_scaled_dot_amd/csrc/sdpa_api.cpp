@@ -176,8 +176,6 @@ sdpa_status_t forward_impl(const void* q, const void* k, const void* v, int64_t 
     if (padded && overlap(out, qbytes, key_lens, B * (int64_t)sizeof(int32_t)))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out overlaps key_lens");
     if (lse) {
-        if (dtype == SDPA_F32)
-            return fail(SDPA_ERR_UNSUPPORTED, "the log-sum-exp output needs 16-bit inputs");
         const int64_t lbytes = B * Hq * Sq * (int64_t)sizeof(float);
         if (overlap(lse, lbytes, out, qbytes) || overlap(lse, lbytes, q, qbytes) ||
             overlap(lse, lbytes, k, kbytes) || overlap(lse, lbytes, v, kbytes) ||
@@ -301,8 +299,10 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
     sdpa_status_t st = check_common(q, k, v, dq, B, Hq, Hkv, Sq, Sk, D, scale, dtype, &qbytes,
                                     &kbytes, (atomic || bias) ? 128 : 512, !(atomic || bias));
     if (st != SDPA_OK) return st;
-    if (dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "the backward needs 16-bit inputs (bf16 or fp16)");
+    if (dtype == SDPA_F32 && (atomic || bias))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "the atomic backward and the backward with a bias need 16-bit inputs (bf16 or "
+                    "fp16)");
     if (mask_kind & ~(SDPA_MASK_CAUSAL | SDPA_MASK_KEY_PADDING))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown mask flags 0x%x", mask_kind);
     const bool causal = mask_kind & SDPA_MASK_CAUSAL;
@@ -400,7 +400,9 @@ sdpa_status_t backward_impl(const void* q, const void* k, const void* v, const v
     a.bias_sh = bias_sh;
     a.dbias = dbias;
     (void)hipGetLastError();
-    return hip_status(sdpa::launch_backward_16bit(a, dtype == SDPA_F16, static_cast<hipStream_t>(stream)),
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(dtype == SDPA_F32 ? sdpa::launch_backward_f32(a, s)
+                                        : sdpa::launch_backward_16bit(a, dtype == SDPA_F16, s),
                       "sdpa_backward launch");
 }
 
@@ -851,8 +853,6 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
                     (long long)D);
     const sdpa_status_t vst = check_value_dim(D, Dv, dtype);
     if (vst != SDPA_OK) return vst;
-    if (lse && dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "the log-sum-exp output needs 16-bit inputs");
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
@@ -901,17 +901,18 @@ sdpa_status_t sdpa_paged_prefill(const void* q, const void* k_cache, const void*
 }
 
 size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t Hkv,
-                                          int64_t max_seq_len, int64_t D, int64_t Dv) {
+                                          int64_t max_seq_len, int64_t D, int64_t Dv, int dtype) {
     if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || D < 1 || Dv < 1 || D > 1 << 20 ||
-        Dv > 1 << 20)
+        Dv > 1 << 20 || !known_dtype(dtype))
         return 0;
-    const int64_t W = paged_backward_width(D, Dv);
+    const int64_t W = dtype == SDPA_F32 ? D : paged_backward_width(D, Dv);
+    const int64_t es = elem_size(dtype);
     const int64_t rows = numel4(num_seqs, Hq, max_seq_len, W), kv = numel4(num_seqs, Hkv, max_seq_len, W);
     const int64_t l = numel4(num_seqs, Hq, max_seq_len, 1);
     if (rows < 0 || kv < 0 || l < 0 || rows > INT64_MAX / 64 || kv > INT64_MAX / 64) return 0;
     const size_t stats = sdpa_backward_workspace_size(num_seqs, Hq, max_seq_len);
     if (stats == 0) return 0;
-    return 4 * round_up((size_t)rows * 2) + 4 * round_up((size_t)kv * 2) + round_up((size_t)l * 4) + stats;
+    return 4 * round_up((size_t)(rows * es)) + 4 * round_up((size_t)(kv * es)) + round_up((size_t)l * 4) + stats;
 }
 
 sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void* v_cache,
@@ -957,7 +958,7 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
     if (nq < 0 || nc < 0 || no < 0 || nvc < 0 || nt < 0 || !mul_ok(nq, es, &qbytes) ||
         !mul_ok(nc, es, &cbytes) || !mul_ok(no, es, &obytes) || !mul_ok(nvc, es, &vcbytes))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "tensor byte size overflows int64");
-    const size_t need = sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv);
+    const size_t need = sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv, dtype);
     if (need == 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace size overflows");
     if (!workspace || workspace_bytes < need)
         return fail(SDPA_ERR_WORKSPACE, "paged backward needs a workspace of %zu bytes (got %zu)",
@@ -979,13 +980,16 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
             if (&o2 != &o && overlap(o.p, o.n, o2.p, o2.n))
                 return fail(SDPA_ERR_INVALID_ARGUMENT, "outputs overlap each other or the workspace");
     }
-    if (dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "the paged backward needs 16-bit inputs (bf16 or fp16)");
+    if (dtype == SDPA_F32 && (Dv != D || !head_dim_ok(D, dtype)))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "head dims D=%lld Dv=%lld not supported by the fp32 paged backward (Dv = D, a "
+                    "multiple of 4 up to 128)",
+                    (long long)D, (long long)Dv);
     if (D > 512 || Dv > 512)
         return fail(SDPA_ERR_UNSUPPORTED,
                     "head dims D=%lld Dv=%lld not supported by the paged backward (any width up to 512)",
                     (long long)D, (long long)Dv);
-    const int64_t W = paged_backward_width(D, Dv);
+    const int64_t W = dtype == SDPA_F32 ? D : paged_backward_width(D, Dv);
     if (page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%lld is not a multiple of 16",
                     (long long)page_size);
@@ -1002,8 +1006,8 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
         cache_elems > kMaxThreads || nq > kMaxThreads || qblocks > INT_MAX / 256)
         return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the kernels' 32-bit index range");
 
-    const size_t rowsz = (size_t)numel4(num_seqs, Hq, max_seq_len, W) * 2;
-    const size_t kvsz = (size_t)numel4(num_seqs, Hkv, max_seq_len, W) * 2;
+    const size_t rowsz = (size_t)numel4(num_seqs, Hq, max_seq_len, W) * es;
+    const size_t kvsz = (size_t)numel4(num_seqs, Hkv, max_seq_len, W) * es;
     char* w = static_cast<char*>(workspace);
     auto take = [&](size_t bytes) {
         char* p = w;
@@ -1047,8 +1051,9 @@ sdpa_status_t sdpa_paged_backward(const void* q, const void* k_cache, const void
     a.lsed = reinterpret_cast<float*>(take((size_t)numel4(num_seqs, Hq, max_seq_len, 4)));
     a.stats = reinterpret_cast<float*>(w);
     (void)hipGetLastError();
-    return hip_status(sdpa::launch_paged_backward_16bit(a, dtype == SDPA_F16,
-                                                        static_cast<hipStream_t>(stream)),
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(dtype == SDPA_F32 ? sdpa::launch_paged_backward_f32(a, s)
+                                        : sdpa::launch_paged_backward_16bit(a, dtype == SDPA_F16, s),
                       "sdpa_paged_backward launch");
 }
 

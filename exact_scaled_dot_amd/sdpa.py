@@ -99,7 +99,7 @@ def load_library():
     lib.sdpa_paged_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, i64, vp,
                                        vp, i64, i64, ctypes.c_float, i32, vp, vp, i32, vp]
     lib.sdpa_paged_backward_workspace_size.restype = ctypes.c_size_t
-    lib.sdpa_paged_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.sdpa_paged_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32]
     lib.sdpa_paged_backward.restype = i32
     lib.sdpa_paged_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp,
                                         i64, i64, vp, vp, i64, ctypes.c_float, i32, vp, vp, vp, vp,
@@ -560,10 +560,11 @@ def sdpa_paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q
     return out if lse_t is None else (out, lse_t)
 
 
-def sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv=None):
+def sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv=None,
+                                       dtype=SDPA_BF16):
     Dv = D if Dv is None else Dv
     return int(load_library().sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D,
-                                                                 Dv))
+                                                                 Dv, dtype))
 
 
 def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_lens, cu_seqlens_q,
@@ -599,7 +600,8 @@ def sdpa_paged_backward(q, k_cache, v_cache, out, dout, lse, block_tables, seq_l
     if seq_lens.shape[0] != num_seqs or cu_seqlens_q.shape[0] != num_seqs + 1:
         raise ValueError("seq_lens needs num_seqs entries and cu_seqlens_q num_seqs + 1")
     lib = load_library()
-    need = int(lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, int(max_seq_len), D, Dv))
+    need = int(lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, int(max_seq_len), D, Dv,
+                                                      _dtype_code(q)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq

@@ -118,7 +118,7 @@ sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
  *            over the visible keys j of row i (natural log, scaled-score
  *            units), -inf for a row with no visible key
  * Every other argument as sdpa_forward; lse must not overlap any tensor.
- * Supported: dtype SDPA_BF16 or SDPA_F16 (SDPA_ERR_UNSUPPORTED for SDPA_F32).
+ * Supported: the dtypes and head dims of sdpa_forward.
  */
 sdpa_status_t sdpa_forward_lse(const void *q, const void *k, const void *v,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
@@ -180,7 +180,10 @@ size_t sdpa_backward_workspace_size(int64_t B, int64_t Hq, int64_t Sq);
  * Outputs and workspace must not overlap each other or any input.
  * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 512 (ruDNN user
  * guide section 9; SDPA_ERR_UNSUPPORTED above); a width that is not a
- * multiple of 8 is read and written element by element.
+ * multiple of 8 is read and written element by element.  SDPA_F32 (section
+ * 9: F32 inputs), D a multiple of 4 up to 128: three kernels (the row
+ * statistics, then the dQ and the dK/dV passes on fp32 MFMA), P and dS kept
+ * in fp32.
  */
 sdpa_status_t sdpa_backward(const void *q, const void *k, const void *v, const void *out,
                             const void *dout, const float *lse,
@@ -410,8 +413,7 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *   out           device [total_q, Hq, Dv]
  *   lse           device fp32 [total_q, Hq] or NULL: natural-log log-sum-exp
  *                 of each row's scaled scores (-inf for a row with no visible
- *                 key), the input sdpa_paged_backward needs; 16-bit inputs
- *                 only (SDPA_ERR_UNSUPPORTED for SDPA_F32)
+ *                 key), the input sdpa_paged_backward needs
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
  * SDPA_F16, D any width up to 1024 (above 256 on the head-dim-split kernel)
  * with Dv = D, or D and Dv both any width up to 256 (a value head dim above
@@ -436,14 +438,15 @@ sdpa_status_t sdpa_paged_prefill(const void *q, const void *k_cache, const void 
                                  void *stream);
 
 /*
- * Bytes of device workspace sdpa_paged_backward needs (0 if the sizes are
- * invalid): Q, dO, O and dQ of every sequence at its absolute positions
- * [num_seqs, Hq, max_seq_len, W] (16-bit), K, V, dK and dV of its reachable
- * keys [num_seqs, Hkv, max_seq_len, W], their fp32 log-sum-exp and the dense
- * backward's statistics; W = max(D, Dv) rounded up to a multiple of 8.
+ * Bytes of device workspace sdpa_paged_backward needs (0 if the sizes or the
+ * dtype are invalid): Q, dO, O and dQ of every sequence at its absolute
+ * positions [num_seqs, Hq, max_seq_len, W] (in dtype), K, V, dK and dV of its
+ * reachable keys [num_seqs, Hkv, max_seq_len, W], their fp32 log-sum-exp and
+ * the dense backward's statistics; W = max(D, Dv) rounded up to a multiple
+ * of 8 (16-bit) or W = D (SDPA_F32).
  */
 size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t Hkv,
-                                          int64_t max_seq_len, int64_t D, int64_t Dv);
+                                          int64_t max_seq_len, int64_t D, int64_t Dv, int dtype);
 
 /*
  * Backward of sdpa_paged_prefill (ruDNN guide section 11: the paged plan's
@@ -463,8 +466,10 @@ size_t sdpa_paged_backward_workspace_size(int64_t num_seqs, int64_t Hq, int64_t 
  * gradient of the true dims); the dense ordered backward runs on them
  * (causal flag and key limit seq_lens), and the gradients' true dims are
  * scattered back: deterministic, no atomics.  Several kernels are enqueued
- * on stream.  Supported: SDPA_BF16 or SDPA_F16, D and Dv any width up to
- * 512, page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
+ * on stream.  Supported: SDPA_BF16 or SDPA_F16 with D and Dv any width up to
+ * 512, or SDPA_F32 with Dv = D a multiple of 4 up to 128 (the fp32 dense
+ * backward, all in fp32); page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED
+ * otherwise).
  * Outputs and the workspace must overlap no input and each other.
  * Not checked (device data): as sdpa_paged_prefill; in addition every table
  * entry a sequence's keys j < seq_lens[s] use must lie in [0, pages) (an

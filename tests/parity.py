@@ -19,6 +19,12 @@ BF16_REL_L2 = 5e-3
 # max|g - r| / max|r|.
 GRAD_REL_L2 = {torch.bfloat16: 1e-2, torch.float16: 2e-3}
 GRAD_MAX_REL = {torch.bfloat16: 4e-2, torch.float16: 8e-3}
+# fp32 inputs: nothing is rounded to 16 bits; every product is exact in fp32
+# and each sum carries a relative error of order sqrt(n) * 2^-24 (about 1e-6
+# over a few hundred keys), the recomputed exponentials about 2^-22.  Bars at
+# about 10x and 100x that.
+GRAD_REL_L2[torch.float32] = 1e-5
+GRAD_MAX_REL[torch.float32] = 1e-4
 
 # Attention block y (projections, attention, output projection): q, k, v, the
 # attention output and y are each rounded to the input type (unit roundoff u

@@ -263,7 +263,6 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pag
     (dict(Dv=256, out=ctypes.c_void_p(0x40000000 + (1 << 20))), sd.SDPA_ERR_INVALID_ARGUMENT,
      "overlaps"),
     (dict(lse=ctypes.c_void_p(0x60000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
-    (dict(lse=ctypes.c_void_p(0x7f000000), dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "log-sum-exp"),
 ])
 def test_paged_prefill_rejects(kw, status, needle):
     assert prefill(**kw) == status
@@ -289,7 +288,6 @@ def fwd_lse(lse=ctypes.c_void_p(0x78000000), dtype=sd.SDPA_BF16, q=FAKE, out=FAK
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(lse=None), sd.SDPA_ERR_INVALID_ARGUMENT, "lse"),
     (dict(q=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
-    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
     (dict(lse=ctypes.c_void_p(0x60000000 + 4096)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
     (dict(lse=ctypes.c_void_p(0x20000000 + 16)), sd.SDPA_ERR_INVALID_ARGUMENT, "lse overlaps"),
 ])
@@ -320,7 +318,8 @@ def bwd(q=FAKE, out=FAKE_O, dout=FAKE_DO, lse=FAKE_L, B=2, Hq=4, Hkv=2, Sq=128, 
     (dict(dout=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
     (dict(lse=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
     (dict(dq=None), sd.SDPA_ERR_INVALID_ARGUMENT, "null"),
-    (dict(dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(dtype=sd.SDPA_F32, D=132), sd.SDPA_ERR_UNSUPPORTED, "fp32: a multiple of 4 up to 128"),
+    (dict(dtype=sd.SDPA_F32, D=66), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(D=520), sd.SDPA_ERR_UNSUPPORTED, "up to 512"),     # the ordered backward stops at 512
     (dict(D=516), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(mask=1, Sq=64), sd.SDPA_ERR_INVALID_ARGUMENT, "Sq == Sk"),
@@ -397,6 +396,11 @@ def test_backward_atomic_workspace_and_rejects():
                                   136, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, 1 << 30,
                                   sd.SDPA_BF16, None)
     assert st == sd.SDPA_ERR_UNSUPPORTED and "up to 128" in sd.last_error()
+    # 16-bit only
+    st = lib.sdpa_backward_atomic(FAKE, FAKE_K, FAKE_V, FAKE_O, FAKE_DO, FAKE_L, 2, 4, 2, 128, 128,
+                                  64, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, 1 << 30,
+                                  sd.SDPA_F32, None)
+    assert st == sd.SDPA_ERR_UNSUPPORTED and "16-bit" in sd.last_error()
     # and multiples of 8 only
     st = lib.sdpa_backward_atomic(FAKE, FAKE_K, FAKE_V, FAKE_O, FAKE_DO, FAKE_L, 2, 4, 2, 128, 128,
                                   100, 0.125, 0, None, FAKE_DQ, FAKE_DK, FAKE_DV, FAKE_BW, 1 << 30,
@@ -494,7 +498,7 @@ def paged_bwd(q=FAKE, k=FAKE_K, v=FAKE_V, out=FAKE_OUT, dout=FAKE_DO, lse=FAKE_L
     lib = sd.load_library()
     Dv = D if Dv is None else Dv
     if ws_bytes is None:
-        ws_bytes = lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv)
+        ws_bytes = lib.sdpa_paged_backward_workspace_size(num_seqs, Hq, Hkv, max_seq_len, D, Dv, dtype)
     return lib.sdpa_paged_backward(q, k, v, out, dout, lse, nq, Hq, Hkv, D, Dv, pages, page_size, tables,
                                    num_seqs, max_pages, seq_lens, cu, max_seq_len, scale, causal,
                                    dq, dk, dv, ws, ws_bytes, dtype, None)
@@ -512,7 +516,8 @@ def paged_bwd(q=FAKE, k=FAKE_K, v=FAKE_V, out=FAKE_OUT, dout=FAKE_DO, lse=FAKE_L
     (dict(ws_bytes=4096), sd.SDPA_ERR_WORKSPACE, "workspace"),
     (dict(dq=ctypes.c_void_p(0x10000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlaps an input"),
     (dict(dv=ctypes.c_void_p(0xc0000000 + 64)), sd.SDPA_ERR_INVALID_ARGUMENT, "overlap each other"),
-    (dict(dtype=sd.SDPA_F32, D=64), sd.SDPA_ERR_UNSUPPORTED, "16-bit"),
+    (dict(dtype=sd.SDPA_F32, D=64, Dv=32), sd.SDPA_ERR_UNSUPPORTED, "fp32 paged backward"),
+    (dict(dtype=sd.SDPA_F32, D=132, nq=30, pages=10), sd.SDPA_ERR_UNSUPPORTED, "fp32 paged backward"),
     (dict(D=520, nq=30, pages=10), sd.SDPA_ERR_UNSUPPORTED, "up to 512"),
     (dict(Dv=513, nq=30, pages=10), sd.SDPA_ERR_UNSUPPORTED, "up to 512"),
     (dict(Dv=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
@@ -534,6 +539,11 @@ def test_paged_backward_workspace_size():
     # rows W = max(D, Dv) rounded up to 8 wide
     for D, Dv, W in [(128, 128, 128), (100, 100, 104), (64, 200, 200), (3, 1, 8), (257, 13, 264)]:
         want = 4 * up(S * Hq * L * W * 2) + 4 * up(S * Hkv * L * W * 2) + up(S * Hq * L * 4) + stats
-        assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, D, Dv) == want
-    assert lib.sdpa_paged_backward_workspace_size(0, Hq, Hkv, L, 128, 128) == 0
-    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, 128, 0) == 0
+        for dt in (sd.SDPA_BF16, sd.SDPA_F16):
+            assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, D, Dv, dt) == want
+    # fp32: rows D floats wide
+    want = 4 * up(S * Hq * L * 100 * 4) + 4 * up(S * Hkv * L * 100 * 4) + up(S * Hq * L * 4) + stats
+    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, 100, 100, sd.SDPA_F32) == want
+    assert lib.sdpa_paged_backward_workspace_size(0, Hq, Hkv, L, 128, 128, sd.SDPA_BF16) == 0
+    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, 128, 0, sd.SDPA_BF16) == 0
+    assert lib.sdpa_paged_backward_workspace_size(S, Hq, Hkv, L, 128, 128, 7) == 0
