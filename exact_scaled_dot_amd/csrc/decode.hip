@@ -880,6 +880,30 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
     // One workgroup per compute unit (the LDS rings admit no second one), or
     // fewer when there are fewer items.
     const int wgs = std::min(cus, (items + kDecWaves - 1) / kDecWaves);
+    if (a.D > 256 || a.Dv > 256) {
+        // Wider heads (key or value): the head-dim-split kernel writes the
+        // same partials (Dv wide), then the same merge (Dv/4 threads per row).
+        if (a.D > 1024 || a.Dv > 1024 || a.D < 1 || a.Dv < 1 || (!PAGED && a.Dv != a.D))
+            return hipErrorInvalidValue;
+        const hipError_t ew = launch_decode_wide_split(a, PAGED ? &p : nullptr, T::kF16, s);
+        if (ew != hipSuccess) return ew;
+        const int dw = a.Dv <= 512 ? 512 : 1024;
+        const bool elem = a.D % 8 != 0 || a.Dv % 8 != 0;  // partial rows padded to a multiple of 4 floats
+        const dim3 mg((unsigned)(((int64_t)a.B * a.Hq * dw / 4 + 255) / 256));
+        if (elem && dw == 512)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T, true, true>), mg, dim3(256), 0, s, a);
+        else if (elem)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T, true, true>), mg, dim3(256), 0, s, a);
+        else if (a.Dv == 512)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T>), mg, dim3(256), 0, s, a);
+        else if (a.Dv == 1024)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T>), mg, dim3(256), 0, s, a);
+        else if (dw == 512)
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T, true>), mg, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T, true>), mg, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if ((a.D % 8 != 0 || a.Dv % 8 != 0) && a.D <= 256) {
         if (a.D < 1 || a.Dv < 1 || a.Dv > 256) return hipErrorInvalidValue;
         if constexpr (PAGED) {
@@ -913,28 +937,6 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const PagedArgs& p, hipSt
             return hipGetLastError();
         }
         return hipErrorInvalidValue;  // the dense decode has Dv = D
-    }
-    if (a.D > 256 && a.D <= 1024) {
-        // Wider heads: the head-dim-split kernel writes the same partials,
-        // then the same merge (D/4 threads per row).
-        if (a.Dv != a.D) return hipErrorInvalidValue;
-        const hipError_t ew = launch_decode_wide_split(a, PAGED ? &p : nullptr, T::kF16, s);
-        if (ew != hipSuccess) return ew;
-        const int dw = a.D <= 512 ? 512 : 1024;
-        const dim3 mg((unsigned)(((int64_t)a.B * a.Hq * dw / 4 + 255) / 256));
-        if (a.D % 8 != 0 && dw == 512)  // partial rows padded to a multiple of 4 floats
-            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T, true, true>), mg, dim3(256), 0, s, a);
-        else if (a.D % 8 != 0)
-            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T, true, true>), mg, dim3(256), 0, s, a);
-        else if (a.D == 512)
-            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T>), mg, dim3(256), 0, s, a);
-        else if (a.D == 1024)
-            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T>), mg, dim3(256), 0, s, a);
-        else if (dw == 512)
-            hipLaunchKernelGGL((decode_merge_bf16_kernel<512, T, true>), mg, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((decode_merge_bf16_kernel<1024, T, true>), mg, dim3(256), 0, s, a);
-        return hipGetLastError();
     }
     if (a.D % 8 != 0 || a.D < 8 || a.D > 256) return hipErrorInvalidValue;
     // Head dims that are multiples of 8 run on the 64-, 128- or 256-wide

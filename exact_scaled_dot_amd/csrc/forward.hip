@@ -1085,7 +1085,7 @@ hipError_t launch_forward_f16(const ForwardArgs& a, hipStream_t s) {
 
 hipError_t launch_paged_prefill_16bit(const ForwardArgs& a, const PagedArgs& p, bool f16,
                                       hipStream_t s) {
-    if (a.D > 256) return launch_paged_prefill_wide(a, p, f16, s);
+    if (a.D > 256 || a.Dv > 256) return launch_paged_prefill_wide(a, p, f16, s);
     return f16 ? launch_16bit<true, F16T>(a, p, s) : launch_16bit<true, Bf16T>(a, p, s);
 }
 

@@ -30,6 +30,11 @@
 // vmcnt counts in issue order, so the compiler's wait for those K fragments
 // also covers the V tile: no explicit wait is needed for V.
 //
+// PAGED: V rows may be Dv wide (Dv != D, the paged plan's value head dim):
+// wave w then owns dims 128w .. 128w+127 of both, i.e. the waves cover the
+// larger of D and Dv; a wave past D adds zero partial scores, a wave past Dv
+// has no output dims.
+//
 // ELEM (head dims that are not multiples of 8): rows of such a width are not
 // 16-byte aligned, so Q, K and V are read one element at a time (2-byte
 // buffer loads; elements past the row at out-of-range offsets read as
@@ -174,6 +179,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int D = a.D;
+    const int Dv = a.Dv > 0 ? a.Dv : D;  // value / output head dim
 
     // Logical order: (batch, K/V head) outermost, then query blocks (under a
     // causal mask the longest first), then the query heads of the group.
@@ -211,8 +217,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     int kv_lim = a.Sk, k_lo = 0, seq = 0, nrows = a.Sq, qpos0 = 0;
     int r0 = 0;  // PAGED prefill: the chunk's first packed row
     const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * D;
-    uint16_t* obase = static_cast<uint16_t*>(a.out) + bh * a.Sq * D;
-    int64_t qstride = D;
+    uint16_t* obase = static_cast<uint16_t*>(a.out) + bh * a.Sq * Dv;
+    int64_t qstride = D, ostride = Dv;
     if (a.padded) kv_lim = max(0, min(kv_lim, key_lens[b]));
     if constexpr (PAGED && !DEC) {
         r0 = min(max(dec.cu_q[b], 0), dec.total_q);
@@ -222,10 +228,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
         seq = b;
         kv_lim = min(seq_lens[b], a.Sk);
         qpos0 = kv_lim - nrows;
-        const int64_t rb = ((int64_t)r0 * a.Hq + h) * D;
-        qbase = static_cast<const uint16_t*>(a.q) + rb;
-        obase = static_cast<uint16_t*>(a.out) + rb;
+        const int64_t rb = (int64_t)r0 * a.Hq + h;
+        qbase = static_cast<const uint16_t*>(a.q) + rb * D;
+        obase = static_cast<uint16_t*>(a.out) + rb * Dv;
         qstride = (int64_t)a.Hq * D;
+        ostride = (int64_t)a.Hq * Dv;
     }
     if constexpr (PAGED && DEC) {
         seq = query_seq[b];
@@ -247,16 +254,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     const int ntiles = kv_end > k_lo ? (kv_end - k_lo + kWKeys - 1) / kWKeys : 0;
 
     const int d0 = kWChunk * wave;  // this wave's first dim
-    const uint32_t kvbytes = (uint32_t)a.Sk * D * 2;
-    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk * D;
-    const __amdgpu_buffer_rsrc_t rk = w_rsrc(static_cast<const uint16_t*>(a.k) + kvh, kvbytes);
-    const __amdgpu_buffer_rsrc_t rv = w_rsrc(static_cast<const uint16_t*>(a.v) + kvh, kvbytes);
-    // Where the 16 keys from kt live: dense, rows of D from the head's start;
-    // PAGED, rows of Hkv*D in the tile's page (head gk's columns), or no
-    // records at all for an invalid table entry.
+    const int64_t kvh = ((int64_t)b * a.Hkv + gk) * a.Sk;
+    const __amdgpu_buffer_rsrc_t rk = w_rsrc(static_cast<const uint16_t*>(a.k) + kvh * D, (uint32_t)a.Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv =
+        w_rsrc(static_cast<const uint16_t*>(a.v) + kvh * Dv, (uint32_t)a.Sk * Dv * 2);
+    // Where the 16 keys from kt live: dense, rows of D (V: Dv) from the head's
+    // start; PAGED, rows of Hkv*D (V: Hkv*Dv) in the tile's page (head gk's
+    // columns), or no records at all for an invalid table entry.
     struct Src {
         __amdgpu_buffer_rsrc_t k, v;
-        uint32_t row0, rstride, col0;
+        uint32_t row0, rstride, col0, vrstride, vcol0;
         bool ok;
     };
     auto src = [&](int kt) -> Src {
@@ -264,13 +271,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             const int lp = kt / dec.page_size;
             const int pg = lp < dec.max_pages ? tables[(int64_t)seq * dec.max_pages + lp] : -1;
             const bool ok = pg >= 0 && pg < dec.pages;
-            const uint32_t pbytes = ok ? (uint32_t)dec.page_size * a.Hkv * D * 2 : 0u;
-            const int64_t off = ok ? (int64_t)pg * dec.page_size * a.Hkv * D : 0;
-            return Src{w_rsrc(static_cast<const uint16_t*>(a.k) + off, pbytes),
-                       w_rsrc(static_cast<const uint16_t*>(a.v) + off, pbytes), (uint32_t)(kt % dec.page_size),
-                       (uint32_t)(a.Hkv * D), (uint32_t)(gk * D), ok};
+            const int64_t off = ok ? (int64_t)pg * dec.page_size * a.Hkv : 0;
+            return Src{w_rsrc(static_cast<const uint16_t*>(a.k) + off * D,
+                              ok ? (uint32_t)dec.page_size * a.Hkv * D * 2 : 0u),
+                       w_rsrc(static_cast<const uint16_t*>(a.v) + off * Dv,
+                              ok ? (uint32_t)dec.page_size * a.Hkv * Dv * 2 : 0u),
+                       (uint32_t)(kt % dec.page_size), (uint32_t)(a.Hkv * D), (uint32_t)(gk * D),
+                       (uint32_t)(a.Hkv * Dv), (uint32_t)(gk * Dv), ok};
         } else {
-            return Src{rk, rv, (uint32_t)kt, (uint32_t)D, 0u, true};
+            return Src{rk, rv, (uint32_t)kt, (uint32_t)D, 0u, (uint32_t)Dv, 0u, true};
         }
     };
 
@@ -314,16 +323,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     // (lane%16) ^ 4*(lane/16)); keys past Sk read as zeros.
     uint16_t* const vw = vring + wave * kWVStages * LY::VST;
     const int vchunk = (lane & 15) ^ (4 * g4);
-    const bool vdim_ok = d0 + 8 * vchunk < D;
+    const bool vdim_ok = d0 + 8 * vchunk < Dv;
     auto load_v = [&](int kt, int st) {
         const Src sr = src(kt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off =
-                vdim_ok ? ((sr.row0 + 4 * i + g4) * sr.rstride + sr.col0 + d0 + 8 * vchunk) * 2 : kWOutside;
+                vdim_ok ? ((sr.row0 + 4 * i + g4) * sr.vrstride + sr.vcol0 + d0 + 8 * vchunk) * 2 : kWOutside;
             if constexpr (ELEM)  // the slot the DMA would fill: 16 bytes at lane * 16
                 *reinterpret_cast<u32x4*>(vw + st * LY::VST + 512 * i + 8 * lane) =
-                    w_elem16<kKVPolicy>(sr.v, off, D - (d0 + 8 * vchunk));
+                    w_elem16<kKVPolicy>(sr.v, off, Dv - (d0 + 8 * vchunk));
             else
                 w_dma<kKVPolicy>(sr.v, vw + st * LY::VST + 512 * i, off);
         }
@@ -486,7 +495,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             const float m_use = m_run == -INFINITY ? 0.f : m_run;
             dec.lse_part[prow] = l > 0.f ? (m_use + __log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
-        const int DP = ELEM ? (D + 3) & ~3 : D;  // floats per partial row
+        const int DP = ELEM ? (Dv + 3) & ~3 : Dv;  // floats per partial row
         float* orow = dec.o_part + prow * DP;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -494,7 +503,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int dim = d0 + 32 * db + 8 * r4 + 4 * kh;
                 const f32x16& xo = acc[db];
-                if (dim < D)
+                if (dim < Dv)
                     *reinterpret_cast<f32x4*>(orow + dim) =
                         f32x4{xo[4 * r4] * invd, xo[4 * r4 + 1] * invd, xo[4 * r4 + 2] * invd,
                               xo[4 * r4 + 3] * invd};
@@ -512,7 +521,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
     // O: register r of d-block db holds dim d0 + 32db + 8*(r/4) + 4*(lane/32)
     // + r%4 of query q0 + lane%32.
     if (qa < nrows) {
-        uint16_t* row = obase + qa * qstride;
+        uint16_t* row = obase + qa * ostride;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -524,13 +533,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
                 if constexpr (ELEM) {  // element by element: the row need not be 8-byte aligned
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (dim + e < D) row[dim + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                } else if (dim < D) {
+                        if (dim + e < Dv) row[dim + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                } else if (dim < Dv) {
                     *reinterpret_cast<u32x2*>(row + dim) = w;
                 }
             }
     }
 }
+
+// The waves cover the larger of the key and value head dims.
+inline int wide_dims(const ForwardArgs& a) { return a.Dv > a.D ? a.Dv : a.D; }
+inline bool wide_elem(const ForwardArgs& a) { return a.D % 8 != 0 || (a.Dv > 0 && a.Dv % 8 != 0); }
 
 template <int NW, class T>
 hipError_t launch_wide_nw(const ForwardArgs& a, hipStream_t s) {
@@ -554,7 +567,7 @@ template <int NW, class T, bool PAGED>
 hipError_t launch_wide_dec_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
     const int nhb = (a.Hq / a.Hkv + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hkv * d.splits * nhb));
-    if (a.D % 8 != 0)
+    if (wide_elem(a))
         hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, true, PAGED, true>), grid, dim3(NW * 64), 0, s, a,
                            a.key_lens, d, d.tables, d.seq_lens, d.query_seq, d.query_pos);
     else
@@ -565,8 +578,8 @@ hipError_t launch_wide_dec_nw(const ForwardArgs& a, const WideDec& d, hipStream_
 
 template <class T, bool PAGED>
 hipError_t launch_wide_dec_t(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
-    if (a.D <= 4 * kWChunk) return launch_wide_dec_nw<4, T, PAGED>(a, d, s);
-    if (a.D <= 6 * kWChunk) return launch_wide_dec_nw<6, T, PAGED>(a, d, s);
+    if (wide_dims(a) <= 4 * kWChunk) return launch_wide_dec_nw<4, T, PAGED>(a, d, s);
+    if (wide_dims(a) <= 6 * kWChunk) return launch_wide_dec_nw<6, T, PAGED>(a, d, s);
     return launch_wide_dec_nw<8, T, PAGED>(a, d, s);
 }
 
@@ -588,7 +601,7 @@ template <int NW, class T>
 hipError_t launch_wide_paged_nw(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
     const int nqb = (a.Sq + kWRows - 1) / kWRows;
     const dim3 grid((unsigned)(a.B * a.Hq * nqb));
-    if (a.D % 8 != 0)
+    if (wide_elem(a))
         hipLaunchKernelGGL((forward_wide_kernel<NW, T, false, false, true, true>), grid, dim3(NW * 64), 0, s, a,
                            nullptr, d, d.tables, d.seq_lens, nullptr, nullptr);
     else
@@ -599,13 +612,13 @@ hipError_t launch_wide_paged_nw(const ForwardArgs& a, const WideDec& d, hipStrea
 
 template <class T>
 hipError_t launch_wide_paged_t(const ForwardArgs& a, const WideDec& d, hipStream_t s) {
-    if (a.D <= 4 * kWChunk) return launch_wide_paged_nw<4, T>(a, d, s);
-    if (a.D <= 6 * kWChunk) return launch_wide_paged_nw<6, T>(a, d, s);
+    if (wide_dims(a) <= 4 * kWChunk) return launch_wide_paged_nw<4, T>(a, d, s);
+    if (wide_dims(a) <= 6 * kWChunk) return launch_wide_paged_nw<6, T>(a, d, s);
     return launch_wide_paged_nw<8, T>(a, d, s);
 }
 
 hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, bool f16, hipStream_t s) {
-    if (a.D <= 256 || a.D > 1024) return hipErrorInvalidValue;
+    if (wide_dims(a) <= 256 || wide_dims(a) > 1024 || a.D < 1 || a.Dv < 1) return hipErrorInvalidValue;
     WideDec w{};
     w.tables = p.block_tables;
     w.seq_lens = p.seq_lens;
@@ -622,7 +635,8 @@ hipError_t launch_paged_prefill_wide(const ForwardArgs& a, const PagedArgs& p, b
 }
 
 hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, bool f16, hipStream_t s) {
-    if (d.D <= 256 || d.D > 1024) return hipErrorInvalidValue;
+    const int dv = d.Dv > 0 ? d.Dv : d.D;
+    if ((d.D <= 256 && dv <= 256) || d.D > 1024 || dv > 1024 || (!p && dv != d.D)) return hipErrorInvalidValue;
     ForwardArgs a;
     a.q = d.q;
     a.k = d.k;
@@ -635,7 +649,7 @@ hipError_t launch_decode_wide_split(const DecodeArgs& d, const PagedArgs* p, boo
     a.Sq = 1;
     a.Sk = d.Sk;
     a.D = d.D;
-    a.Dv = d.D;
+    a.Dv = dv;
     a.scale = d.scale;
     a.causal = false;
     a.padded = d.key_lens != nullptr;

@@ -67,13 +67,14 @@ bool head_dim_ok(int64_t D, int dtype, int64_t max16 = 128, bool any16 = false) 
 }
 
 // Value head dim of the paged entry points: Dv == D on every kernel; Dv != D
-// on the 16-bit kernels with D and Dv both up to 256.
+// on the 16-bit kernels with D and Dv both up to 1024 (above 256 on the
+// head-dim-split kernel, whose waves cover the larger of the two).
 sdpa_status_t check_value_dim(int64_t D, int64_t Dv, int dtype) {
     if (Dv == D) return SDPA_OK;
-    if (dtype == SDPA_F32 || !head_dim_ok(D, dtype, 256, true) || !head_dim_ok(Dv, dtype, 256, true))
+    if (dtype == SDPA_F32 || !head_dim_ok(D, dtype, 1024, true) || !head_dim_ok(Dv, dtype, 1024, true))
         return fail(SDPA_ERR_UNSUPPORTED,
                     "value head dim Dv=%lld differs from D=%lld: supported for bf16 / fp16 with "
-                    "both up to 256",
+                    "both up to 1024",
                     (long long)Dv, (long long)D);
     return SDPA_OK;
 }

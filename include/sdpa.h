@@ -370,10 +370,10 @@ sdpa_status_t sdpa_decode_noalloc(const void *q, const void *k, const void *v,
  *                (same layout as sdpa_decode's with B = queries, D = Dv)
  *   out          device [queries, Hq, Dv]
  * Two kernels are enqueued on stream: the split pass, then the merge.
- * Supported: dtype SDPA_BF16 or SDPA_F16, D any width up to 1024 (above
- * 256 the split pass runs on the head-dim-split kernel, as in sdpa_decode)
- * with Dv = D, or D and Dv both any width up to 256 (widths that are not
- * multiples of 8 read element by element);
+ * Supported: dtype SDPA_BF16 or SDPA_F16, D and Dv any width up to 1024
+ * (when either is above 256 the split pass runs on the head-dim-split
+ * kernel, as in sdpa_decode, its waves covering the larger of the two;
+ * widths that are not multiples of 8 read element by element);
  * page_size a multiple of 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernels' behaviour outside the
  * contract: seq_lens above max_seq_len act as max_seq_len; a query_seq outside
@@ -415,10 +415,10 @@ sdpa_status_t sdpa_paged_attention(const void *q, const void *k_cache, const voi
  *                 of each row's scaled scores (-inf for a row with no visible
  *                 key), the input sdpa_paged_backward needs
  * One kernel is enqueued; no workspace.  Supported: dtype SDPA_BF16 or
- * SDPA_F16, D any width up to 1024 (above 256 on the head-dim-split kernel)
- * with Dv = D, or D and Dv both any width up to 256 (a value head dim above
- * 128 in two 128-dim output slices; widths that are not multiples of 8 read
- * element by element); page_size a multiple of
+ * SDPA_F16, D and Dv any width up to 1024 (when either is above 256 on the
+ * head-dim-split kernel; otherwise a value head dim above 128 in two 128-dim
+ * output slices; widths that are not multiples of 8 read element by
+ * element); page_size a multiple of
  * 16 (SDPA_ERR_UNSUPPORTED otherwise).
  * Not checked (device data), with the kernel's behaviour outside the
  * contract: cu_seqlens_q entries are clamped into [0, total_q] (no row outside

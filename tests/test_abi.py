@@ -214,10 +214,10 @@ def paged(q=FAKE, k=FAKE_K, v=FAKE_V, nq=3, Hq=8, Hkv=2, D=128, Dv=None, pages=1
     (dict(D=64, Dv=128, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     (dict(page_size=8, max_pages=100), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
     (dict(Dv=0), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
-    (dict(Dv=300), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(Dv=1030), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     (dict(D=102, Dv=102, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
-    (dict(D=512, Dv=128), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
-    (dict(D=64, Dv=264), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=1032, Dv=128), sd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(D=64, Dv=1025), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     # the workspace holds Dv-wide partials: one sized for D = 128 is too small at Dv = 256
     (dict(D=128, Dv=256, ws_bytes=(3 * 8 * 4 * 128 * 4 + 255) // 256 * 256 + 256),
      sd.SDPA_ERR_WORKSPACE, "workspace"),
@@ -255,10 +255,10 @@ def prefill(q=FAKE, k=FAKE_K, v=FAKE_V, nq=300, Hq=8, Hkv=2, D=128, Dv=None, pag
     (dict(D=136, dtype=sd.SDPA_F32), sd.SDPA_ERR_UNSUPPORTED, "up to 128"),
     (dict(page_size=24, max_pages=40), sd.SDPA_ERR_UNSUPPORTED, "multiple of 16"),
     (dict(Dv=-3), sd.SDPA_ERR_INVALID_ARGUMENT, ">= 1"),
-    (dict(Dv=260), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
-    (dict(D=300, Dv=128), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(Dv=1100), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=300, Dv=1028), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     (dict(D=1030), sd.SDPA_ERR_UNSUPPORTED, "any width up to 1024"),
-    (dict(D=64, Dv=512), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
+    (dict(D=64, Dv=2048), sd.SDPA_ERR_UNSUPPORTED, "value head dim"),
     # v_cache spans 100 * 16 * 2 * Dv * 2 bytes: 1 MB in lies inside it only at Dv = 256
     (dict(Dv=256, out=ctypes.c_void_p(0x40000000 + (1 << 20))), sd.SDPA_ERR_INVALID_ARGUMENT,
      "overlaps"),

@@ -307,3 +307,52 @@ def test_backward_any_width(D, mask):
 
 def test_backward_any_width_fp16_rectangular():
     backward_case(2, 6, 3, 130, 333, 77, 2, [333, 45], F16, 6400)
+
+
+# ------------------------------------- value head dims above 256 (Dv != D)
+
+WIDE_PAIRS = [(128, 512), (512, 128), (300, 1023), (1024, 64), (257, 513), (64, 300)]
+
+
+@pytest.mark.parametrize("D,Dv", WIDE_PAIRS)
+@pytest.mark.parametrize("splits", [1, 5])
+def test_paged_attention_wide_value_width(D, Dv, splits):
+    lens, qs, qp = [300, 129, 1, 50], [0, 1, 2, 0, 3, 1], [299, 128, 0, 17, 49, 3]
+    for causal in (False, True):
+        seed = 6500 + D + Dv + splits + causal
+        inp = value_width(draw_paged(lens, qs, qp, 4, 2, D, 16, BF16, seed, DEV), Dv, BF16, seed)
+        scale = 1 / math.sqrt(D)
+        out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                      inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale,
+                                      causal, inp["block_tables"].shape[1] * 16, splits)
+        torch.cuda.synchronize()
+        assert out.shape == (len(qs), 4, Dv)
+        ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                                inp["block_tables"].cpu().numpy(), np.array(lens), np.array(qs),
+                                np.array(qp), scale, causal)
+        compare(to64(out), ref, BF16, "wide paged D=%d Dv=%d splits=%d causal=%d"
+                % (D, Dv, splits, causal))
+
+
+@pytest.mark.parametrize("D,Dv", WIDE_PAIRS)
+def test_paged_prefill_wide_value_width(D, Dv):
+    lens, chunks = [300, 129, 70], [100, 40, 1]
+    nq = sum(chunks)
+    for causal in (False, True):
+        seed = 6600 + D + Dv + causal
+        inp = value_width(draw_paged(lens, [0] * nq, [0] * nq, 4, 2, D, 16, BF16, seed, DEV), Dv,
+                          BF16, seed)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device=DEV)
+        scale = 1 / math.sqrt(D)
+        out, lse = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"],
+                                         inp["block_tables"], inp["seq_lens"], cu, scale, causal,
+                                         max(chunks), inp["block_tables"].shape[1] * 16, lse=True)
+        torch.cuda.synchronize()
+        assert out.shape == (nq, 4, Dv)
+        qs, qp = O.chunk_positions(cu.cpu().numpy(), np.array(lens))
+        ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                                inp["block_tables"].cpu().numpy(), np.array(lens), qs, qp, scale,
+                                causal)
+        what = "wide prefill D=%d Dv=%d causal=%d" % (D, Dv, causal)
+        compare(to64(out), ref, BF16, what)
+        assert np.isfinite(to64(lse)).all(), what + ": lse"

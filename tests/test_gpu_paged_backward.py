@@ -128,3 +128,9 @@ def test_paged_backward_wide(D):
 
 def test_paged_backward_value_width_non_causal_fp16():
     check([500, 64], [77, 64], 8, 8, 96, 16, False, dtype=F16, seed=4800, Dv=40)
+
+
+@pytest.mark.parametrize("D,Dv", [(128, 400), (300, 64), (512, 264)])
+def test_paged_backward_wide_value_width(D, Dv):
+    # the head-dim-split prefill writes the lse with a value width of its own
+    check([200, 90], [200, 31], 4, 2, D, 16, True, seed=4900 + D + Dv, Dv=Dv)
