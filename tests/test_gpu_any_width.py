@@ -356,3 +356,65 @@ def test_paged_prefill_wide_value_width(D, Dv):
         what = "wide prefill D=%d Dv=%d causal=%d" % (D, Dv, causal)
         compare(to64(out), ref, BF16, what)
         assert np.isfinite(to64(lse)).all(), what + ": lse"
+
+
+# --------------------------------------------- invalid pages, random shapes
+
+
+@pytest.mark.parametrize("D,Dv", [(100, 100), (36, 130), (300, 300), (77, 513)])
+def test_paged_any_width_invalid_table_entries_hide_their_keys(D, Dv):
+    # logical pages 1 and 3 of a 64-key sequence point outside the cache: on
+    # the element-wise paths too they are never read and their keys hidden
+    inp = value_width(draw_paged([64], [0, 0], [63, 63], 4, 2, D, 16, BF16, 6700 + D + Dv, DEV), Dv,
+                      BF16, 6700 + D + Dv)
+    inp["block_tables"] = torch.tensor([[0, -1, 2, 99999]], dtype=torch.int32, device=DEV)
+    cu = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(D)
+    out = sd.sdpa_paged_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                  inp["seq_lens"], inp["query_seq"], inp["query_pos"], scale, False,
+                                  64, 3)
+    pre = sd.sdpa_paged_prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                                inp["seq_lens"], cu, scale, False, 2, 64)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(to64(inp["q"]), to64(inp["k_cache"]), to64(inp["v_cache"]),
+                            np.array([[0, 2]]), np.array([32]), np.array([0, 0]), np.array([31, 31]),
+                            scale, False)
+    compare(to64(out), ref, BF16, "invalid pages hidden D=%d Dv=%d (attention)" % (D, Dv))
+    compare(to64(pre), ref, BF16, "invalid pages hidden D=%d Dv=%d (prefill)" % (D, Dv))
+
+
+def random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        G = int(rng.choice([1, 2, 3, 8]))
+        Hkv = int(rng.integers(1, 3))
+        D = int(rng.choice([int(rng.integers(1, 256)), int(rng.integers(257, 1024))], p=[0.75, 0.25]))
+        S = int(rng.integers(1, 260))
+        mask = int(rng.integers(0, 4))
+        yield i, G * Hkv, Hkv, S, D, mask, int(rng.integers(0, 1 << 30))
+
+
+@pytest.mark.parametrize("case", list(random_cases(24, 6800)), ids=lambda c: "r%d" % c[0])
+def test_forward_and_decode_random_shapes(case):
+    # seeded random shapes: head dims of any width (a quarter above 256),
+    # grouped heads, short and ragged lengths, every mask; the forward with
+    # its lse and the decode of the last row, against the oracle
+    _, Hq, Hkv, S, D, mask, seed = case
+    B = 2
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, seed % 100000, DEV)
+    lens = None
+    if mask & 2:
+        lens = torch.tensor([S, max(1, S // 3)], dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+    splits = 1 + seed % 9
+    qd = q[:, :, -1:].contiguous()
+    dec = sd.sdpa_decode(qd, k, v, scale, lens, splits)
+    torch.cuda.synchronize()
+    ln = None if lens is None else lens.cpu().numpy()
+    what = "random Hq=%d Hkv=%d S=%d D=%d mask=%d" % (Hq, Hkv, S, D, mask)
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask, ln, return_lse=True)
+    compare(to64(out), ref, BF16, what)
+    assert np.abs(to64(lse) - rlse).max() < 1e-2, what + ": lse"
+    compare(to64(dec), O.sdpa_decode(to64(qd), to64(k), to64(v), scale, ln), BF16,
+            what + " decode splits=%d" % splits)
