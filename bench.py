@@ -22,8 +22,8 @@ resident in HBM:
   * the causal prefill with 1024-wide heads, bf16, B=1 Hq=Hkv=8 S=4096 D=1024
     (the same formula FLOPs again; the head dim is split across 8 waves)
   * the causal prefill with 256-wide heads, bf16, B=4 Hq=Hkv=8 S=4096 D=256
-    (the same formula FLOPs as the headline; the kernel computes the output
-    in two 128-dim slices that each recompute the scores), and the split-KV
+    (the same formula FLOPs as the headline; pairs of waves split the head
+    dim and add each other's partial scores on chip), and the split-KV
     decode with 256-wide heads, B=32 Hq=32 Hkv=8 Sk=32768 (the decode's K+V
     bytes), 32 splits, and with 1024-wide heads, B=8 Hq=32 Hkv=8 Sk=32768 (the
     same K+V bytes again)
@@ -275,15 +275,21 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes=1 << 30):
     fwd = "forward_bf16_kernel"
     if fwd in fetch:
         # a full step launches, in order: the causal prefill, the padded one,
-        # the paged one, the bias prefill, the wide-head prefill, the large
-        # block's attention and the small block's (after the setup forwards
-        # that give the backward legs their output and lse)
+        # the paged one, the bias prefill, the large block's attention and the
+        # small block's (after the setup forwards that give the backward legs
+        # their output and lse)
         fr, wr = fetch[fwd], write[fwd]
-        setup = len(fr) % 7        # the backward legs' setup forwards come first
+        setup = len(fr) % 6        # the backward legs' setup forwards come first
         fr, wr = fr[setup:], wr[setup:]
-        for i, key in enumerate(("prefill", "padded", "paged_prefill", "bias", "wide", "block_attn",
+        for i, key in enumerate(("prefill", "padded", "paged_prefill", "bias", "block_attn",
                                  "block_small_attn")):
-            out[key] = entry(fwd, "forward.hip", fr[i::7], wr[i::7])
+            out[key] = entry(fwd, "forward.hip", fr[i::6], wr[i::6])
+    # the wide-head prefill (paired waves): once per step, after one setup
+    # forward for the wide backward leg
+    fp = "forward_pair_kernel"
+    if fp in fetch:
+        skip = 1 if len(fetch[fp]) > 1 else 0
+        out["wide"] = entry(fp, "forward.hip", fetch[fp][skip:], write[fp][skip:])
     # the head-dim-split kernel: the widest prefill, then the widest decode's
     # split pass
     fw = "forward_wide_kernel"
@@ -790,12 +796,11 @@ def main():
         tf = fl / (ms["wide"] * 1e-3) / 1e12
         rec["wide"] = {"workload": "bf16_causal_b%d_h%d_s%d_d%d" % (B, H, S, D),
                        **timing(times["wide"]), "value": round(tf, 3), "unit": "TFLOP/s",
-                       "executed_mfma_flops": 1.5 * fl,
                        "roofline": {"bound": "mfma", "achieved": round(tf, 3),
                                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                     "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                                     "traffic": stored_traffic("wide", "forward.hip"),
-                                    "kernel": "forward_bf16_kernel<256, DV=128> x 2 slices",
+                                    "kernel": "forward_pair_kernel<256>",
                                     "flops_per_launch": fl}}
     if "backward_wide" in ms:
         B, H, S, D = WIDE

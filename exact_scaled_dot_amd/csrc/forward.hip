@@ -756,6 +756,232 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
 }
 
 // ---------------------------------------------------------------------------
+// Head dims above 128 and up to 256 (16-bit, dense, no bias) on paired waves.
+// A workgroup of 8 waves owns 128 query rows of one (batch, head); waves w
+// and w + 4 share rows 32*(w%4) .. +31 and split the head dim: wave w owns
+// dims 0..127, wave w + 4 dims 128..255 (of both Q.K and the output).  Per
+// 32-key tile each wave forms the partial scores S^T over its dims (the
+// layout of forward_bf16_kernel, K rows from LDS), hands them to its partner
+// through LDS, adds the partner's, and both waves of a pair then run the
+// same online softmax on the full scores (the fp32 sum a + b is the same
+// in either order) and form their own 128 output dims, O^T += V^T P^T.
+// Every product is thus computed once (the two-slice form recomputes the
+// scores in each slice), each wave holds a 128-dim Q and O like the 128-wide
+// kernel (two waves per SIMD), and K and V tiles (all 256 dims) are shared
+// by the 8 waves.  Per tile: two barriers (partials handed over; the next
+// tile's DMA landed), K and V one tile ahead in two LDS stages.
+// ---------------------------------------------------------------------------
+constexpr int kPairThreads = 512;
+constexpr int kPairKeys = 32;
+
+template <class T, bool GEN = false>
+__global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardArgs a) {
+    constexpr int D = 256;
+    constexpr int KT = kPairKeys;
+    using L = Bf16Geo<D>;
+    constexpr int TILE = KT * D;                   // 16-bit elements per K or V tile
+    constexpr int DMA = TILE * 2 / 1024 / 8;       // 1-KB DMA loads per wave per tensor
+    constexpr int XF = 64 * 16;                    // floats of one wave's partial scores
+    static_assert(DMA == 2, "tile geometry");
+    // K stage s at s*TILE, V stage s at (2+s)*TILE, then the hand-over slots.
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE + 8 * XF * 2];
+    float* const xch = reinterpret_cast<float*>(smem + 4 * TILE);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hg = lane >> 5;
+    const int rb = wave & 3, dh = wave >> 2;  // row block, head-dim half
+    const TileInfo ti = decode_tile(a);
+    const int DR = GEN ? a.D : D;  // head dim in memory
+    constexpr uint32_t kOut = 0x80000000u;
+    const int64_t bh = (int64_t)ti.b * a.Hq + ti.h;
+    const int64_t kvh = ((int64_t)ti.b * a.Hkv + ti.gk) * a.Sk * DR;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kvh;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kvh;
+    const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bh * a.Sq * DR;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + bh * a.Sq * DR;
+    int kv_lim, kv_end;
+    key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
+    const int qw = ti.q0 + 32 * rb;  // first row of this wave (and its partner)
+    const int qi = qw + l32;
+    const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
+    const int wave_tiles = a.causal ? max(0, min(ntiles, (qw + 31) / KT + 1)) : ntiles;
+
+    // Q of this wave's dims as B operands: lane holds Q[qi][128*dh + 16t + 8hg .. +7]
+    // (rows past Sq, dims past DR read as zeros).
+    u32x4 qr[8];
+    {
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, (uint32_t)a.Sq * DR * 2);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int d0 = 128 * dh + 16 * t + 8 * hg;
+            qr[t] = __builtin_amdgcn_raw_buffer_load_b128(qrs, d0 < DR ? ((uint32_t)qi * DR + d0) * 2 : kOut, 0, 0);
+        }
+    }
+    // DMA: load i of this wave fills 16-byte slot 64*(2*wave + i) + lane of a
+    // tile, i.e. LDS row slot / 32, stored chunk slot % 32 (K rows in the
+    // permuted key order of k_lds_row).
+    uint32_t koff[DMA], voff[DMA];
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+        const int s = 64 * (DMA * wave + i) + lane;
+        const int row = s / L::CPR, pc = s % L::CPR;
+        const int ck = pc ^ L::fk(row), cv = pc ^ L::fv(row);
+        koff[i] = 8 * ck < DR ? (uint32_t)k_lds_row(row) * DR * 2 + ck * 16 : kOut;
+        voff[i] = 8 * cv < DR ? (uint32_t)row * DR * 2 + cv * 16 : kOut;
+    }
+    auto issue = [&](int j0, int stage) {
+        const uint32_t bytes = (uint32_t)(a.Sk - j0) * DR * 2;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)j0 * DR, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)j0 * DR, bytes);
+#pragma unroll
+        for (int i = 0; i < DMA; ++i) {
+            dma16(rk, smem + stage * TILE + 512 * (DMA * wave + i), koff[i]);
+            dma16(rv, smem + (2 + stage) * TILE + 512 * (DMA * wave + i), voff[i]);
+        }
+    };
+    // K operand: LDS row l32, logical chunk 16*dh + 2t + hg (dims of this wave).
+    int krd[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) krd[t] = l32 * D + (((16 * dh + 2 * t + hg) ^ L::fk(l32)) * 8);
+    // V^T operand: row 16*kk + tr_row (+4), column 128*dh + 32*db + tr_col.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int tr_row = 8 * hg + (j16 >> 2);
+    const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
+    int vrd[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int col = 128 * dh + 32 * db + tr_col;
+        vrd[db] = tr_row * D + (((col >> 3) ^ L::fv(tr_row)) * 8) + (col & 7);
+    }
+    // Hand-over slots: 16 floats per lane as 4 chunks, chunk i at slot
+    // (i + lane/4) % 4, so 16 lanes of one 16-byte access touch 16 bank groups.
+    float* const xmine = xch + (wave * 64 + lane) * 16;
+    const float* const xpart = xch + ((wave ^ 4) * 64 + lane) * 16;
+    auto xslot = [&](int i) { return 4 * ((i + (lane >> 2)) & 3); };
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY;  // reference max of row qi (raw score units)
+    float l_run = 0.f;        // this lane's share of the denominator
+    const float c = a.scale * kLog2e;
+    const float tau = 8.0f / c;
+    const bool rev = ti.rev;
+    auto tkey = [&](int jt) { return (rev ? ntiles - 1 - jt : jt) * KT; };
+
+    if (ntiles > 0) issue(tkey(0), 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int jt = 0; jt < ntiles; ++jt) {
+        const int cur = jt & 1, j0 = tkey(jt);
+        if (jt + 1 < ntiles) issue(tkey(jt + 1), cur ^ 1);  // stage cur^1 was last read before the previous barrier
+        const bool act = jt < wave_tiles;  // the same for both waves of a pair
+        f32x16 s = {};
+        if (act) {
+            // partial S^T: register r holds key j0 + 16*(r/8) + 8*hg + r%8 of query qi
+            const uint16_t* ks = smem + cur * TILE;
+            u32x4 kf[3];
+            kf[0] = *reinterpret_cast<const u32x4*>(ks + krd[0]);
+            kf[1] = *reinterpret_cast<const u32x4*>(ks + krd[1]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (t + 2 < 8) kf[(t + 2) % 3] = *reinterpret_cast<const u32x4*>(ks + krd[t + 2]);
+                s = mfma_32x32x16<T>(kf[t % 3], qr[t], s);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(xmine + xslot(i)) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // partial scores handed over (the DMA stays in flight)
+        asm volatile("" ::: "memory");
+        if (act) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 o = *reinterpret_cast<const f32x4*>(xpart + xslot(i));
+                s[4 * i] += o[0];
+                s[4 * i + 1] += o[1];
+                s[4 * i + 2] += o[2];
+                s[4 * i + 3] += o[3];
+            }
+            if ((a.causal && j0 + KT - 1 > qw) || j0 + KT > kv_lim) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + 16 * (r >> 3) + 8 * hg + (r & 7);
+                    if (key >= kv_lim || (a.causal && key > qi)) s[r] = -INFINITY;
+                }
+            }
+            uint32_t pk[8];
+            auto weights = [&]() -> float {
+                const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+                float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    pk[r >> 1] = pack2<T>(fast_exp2(fmaf(s[r], c, neg)), fast_exp2(fmaf(s[r + 1], c, neg)));
+                    if (r & 2) ps1 = sum2<T>(pk[r >> 1], ps1);
+                    else ps0 = sum2<T>(pk[r >> 1], ps0);
+                }
+                return ps0 + ps1;
+            };
+            float ps = weights();
+            if (__any(ps > 256.f || m_run == -INFINITY)) {
+                float mx = s[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+                mx = max_half_waves(mx);
+                if (__any(mx > m_run + tau)) {
+                    const float m_new = fmaxf(m_run, mx);
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    const float alpha = fast_exp2((m_run - m_use) * c);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+                }
+                ps = weights();
+            }
+            l_run += ps;
+            // O^T += V^T P^T over the tile's two 16-key slices (this wave's dims)
+            const uint16_t* vs = smem + (2 + cur) * TILE;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 pw = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
+                u32x4 vf[4];
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const uint16_t* vb = vs + 16 * kk * D + vrd[db];
+                    const u32x2 lo = lds_read_tr16x4(vb);
+                    const u32x2 hi = lds_read_tr16x4(vb + 4 * D);
+                    vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+#pragma unroll
+                for (int db = 0; db < 4; ++db) oacc[db] = mfma_32x32x16<T>(vf[db], pw, oacc[db]);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's DMA landed
+        __syncthreads();
+    }
+
+    const float lt = l_run + swap_half_wave(l_run);
+    const float inv = 1.f / lt;
+    if (a.lse && dh == 0 && hg == 0 && qi < a.Sq)
+        a.lse[bh * a.Sq + qi] = m_run == -INFINITY ? -INFINITY : m_run * a.scale + __logf(lt);
+    if (qi < a.Sq) {
+        uint16_t* orow = op + (int64_t)qi * DR;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const u32x2 w = {pack2<T>(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
+                                 pack2<T>(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
+                const int d0 = 128 * dh + 32 * db + 8 * r4 + 4 * hg;  // 4 dims, all < DR or none
+                if (d0 < DR) *reinterpret_cast<u32x2*>(orow + d0) = w;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 inputs, fp32 MFMA (v_mfma_f32_32x32x2_f32): every product exact in fp32.
 // ---------------------------------------------------------------------------
 // GEN: rows are DR = a.D floats in memory (a multiple of 4 below D); the
@@ -1004,8 +1230,9 @@ int xcd_resident(Kernel kernel, int threads) {
 }
 
 // Head dims that are multiples of 8 run on the 64-, 128- or 256-wide kernel
-// (the general-width instantiation unless D is exactly 64, 128 or 256); above
-// 128 the output is computed in two 128-dim slices.
+// (the general-width instantiation unless D is exactly 64, 128 or 256).  Above
+// 128 the dense forward without a bias runs on paired waves; the paged and
+// biased ones compute the output in two 128-dim slices.
 template <bool PAGED, class T, bool BIAS = false>
 hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
     if (a.D < 1 || a.D > 256) return hipErrorInvalidValue;
@@ -1054,10 +1281,17 @@ hipError_t launch_16bit(const ForwardArgs& a, const PagedArgs& p, hipStream_t s)
         }
         return hipErrorInvalidValue;
     }
+    auto pair = [&](auto kernel) {
+        ForwardArgs b = a;
+        b.sweep_group = !a.causal ? xcd_resident(kernel, kPairThreads) : 0;
+        hipLaunchKernelGGL(kernel, dim3(g.x, 1), dim3(kPairThreads), 0, s, b);
+    };
     if (a.D == 64)
         go(forward_bf16_kernel<64, PAGED, T, BIAS>);
     else if (a.D == 128)
         go(forward_bf16_kernel<128, PAGED, T, BIAS>);
+    else if (a.D > 128 && !PAGED && !BIAS)
+        a.D == 256 ? pair(forward_pair_kernel<T>) : pair(forward_pair_kernel<T, true>);
     else if (a.D == 256)
         go(forward_bf16_kernel<256, PAGED, T, BIAS, false, 128>);
     else if (a.D < 64)

@@ -4,7 +4,7 @@ inputs), against the fp64 oracle.
 
 Up to 128 the 64- and 128-wide kernels serve these widths: rows are D wide in
 memory, the chunks past D are read as zeros on chip and never stored.  Above
-that, the 256-wide kernels (two 128-dim output slices) and the
+that, the paired-wave and 256-wide kernels (two 128-dim output slices) and the
 head-dim-split kernels (waves of 128 dims whose partial scores are summed on
 chip).  Bars: tests/parity.py."""
 
@@ -122,8 +122,10 @@ def test_outputs_past_head_dim_untouched():
 
 
 # ------------------------------------------------------------- wide head dims
-# Above 128 the prefill kernel computes the output in two 128-dim slices (two
-# workgroups per query block, each with the full-width scores).
+# Above 128 the dense prefill pairs waves that split the head dim (partial
+# scores summed on chip); with a bias or over pages it computes the output in
+# two 128-dim slices (two workgroups per query block, each with the
+# full-width scores).
 
 @pytest.mark.parametrize("D", [136, 200, 256])
 @pytest.mark.parametrize("mask", [0, 1, 3], ids=["none", "causal", "causal+padding"])
@@ -155,6 +157,50 @@ def test_forward_wide_fp16_bias_and_gqa():
     torch.cuda.synchronize()
     compare(to64(outb), O.sdpa_forward(to64(q2), to64(k2), to64(v2), 0.07, O.MASK_CAUSAL,
                                        bias=to64(bias)), F16, "fp16 D=256 bias")
+
+
+# Dense 16-bit forward from 129 to 256 dims (no bias) runs on paired waves:
+# two waves share 32 query rows and split the head dim, adding each other's
+# partial scores through LDS.
+
+@pytest.mark.parametrize("D", [144, 168, 232, 248])
+def test_forward_paired_wave_widths(D):
+    B, Hq, Hkv, S = 2, 4, 1, 333
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 805 + D, DEV)
+    lens = torch.tensor([333, 130], dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = sd.sdpa_forward_lse(q, k, v, scale, sd.MASK_CAUSAL | sd.MASK_KEY_PADDING, lens)
+    torch.cuda.synchronize()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, O.MASK_CAUSAL | O.MASK_KEY_PADDING,
+                               lens.cpu().numpy(), return_lse=True)
+    compare(to64(out), ref, BF16, "paired D=%d" % D)
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("mask", [0, 2], ids=["none", "padding"])
+def test_forward_paired_wave_cross_lengths(dtype, mask):
+    # Sq != Sk, both ragged against the 128-row and 32-key tiles
+    B, Hq, Hkv, Sq, Sk, D = 3, 4, 2, 77, 301, 256
+    q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, dtype, 810 + mask, DEV)
+    lens = torch.tensor([301, 33, 1], dtype=torch.int32, device=DEV) if mask else None
+    out, lse = sd.sdpa_forward_lse(q, k, v, 0.05, mask, lens)
+    torch.cuda.synchronize()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), 0.05, mask,
+                               None if lens is None else lens.cpu().numpy(), return_lse=True)
+    compare(to64(out), ref, dtype, "paired cross mask=%d" % mask)
+    assert np.abs(to64(lse) - rlse).max() < 1e-2
+
+
+def test_forward_paired_wave_swept_grid():
+    # more workgroups than the chip holds at once: the non-causal sweep order
+    # over query blocks sharing one K/V head
+    B, Hq, Hkv, S, D = 1, 80, 8, 512, 256
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 815, DEV)
+    out = sd.sdpa_forward(q, k, v, 1 / 16, sd.MASK_NONE)
+    torch.cuda.synchronize()
+    compare(to64(out), O.sdpa_forward(to64(q), to64(k), to64(v), 1 / 16, O.MASK_NONE), BF16,
+            "paired swept grid")
 
 
 def test_wide_outputs_past_head_dim_untouched():
