@@ -768,8 +768,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void forward_bf16_kernel
 // Every product is thus computed once (the two-slice form recomputes the
 // scores in each slice), each wave holds a 128-dim Q and O like the 128-wide
 // kernel (two waves per SIMD), and K and V tiles (all 256 dims) are shared
-// by the 8 waves.  Per tile: two barriers (partials handed over; the next
-// tile's DMA landed), K and V one tile ahead in two LDS stages.
+// by the 8 waves.  The partial scores run one tile ahead: step j forms the
+// partial scores of tile j + 1 beside tile j's softmax and P.V, so the
+// MFMA and exponential work of one wave overlap; the hand-over slots
+// alternate between two buffers by tile, and one barrier per step covers
+// both the hand-over and the K/V tiles (two LDS stages each, loaded a step
+// ahead).
 // ---------------------------------------------------------------------------
 constexpr int kPairThreads = 512;
 constexpr int kPairKeys = 32;
@@ -783,8 +787,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
     constexpr int DMA = TILE * 2 / 1024 / 8;       // 1-KB DMA loads per wave per tensor
     constexpr int XF = 64 * 16;                    // floats of one wave's partial scores
     static_assert(DMA == 2, "tile geometry");
-    // K stage s at s*TILE, V stage s at (2+s)*TILE, then the hand-over slots.
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE + 8 * XF * 2];
+    // K stage s at s*TILE, V stage s at (2+s)*TILE, then two hand-over buffers.
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE + 2 * 8 * XF * 2];
     float* const xch = reinterpret_cast<float*>(smem + 4 * TILE);
 
     const int tid = threadIdx.x;
@@ -830,16 +834,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
         koff[i] = 8 * ck < DR ? (uint32_t)k_lds_row(row) * DR * 2 + ck * 16 : kOut;
         voff[i] = 8 * cv < DR ? (uint32_t)row * DR * 2 + cv * 16 : kOut;
     }
-    auto issue = [&](int j0, int stage) {
-        const uint32_t bytes = (uint32_t)(a.Sk - j0) * DR * 2;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)j0 * DR, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)j0 * DR, bytes);
-#pragma unroll
-        for (int i = 0; i < DMA; ++i) {
-            dma16(rk, smem + stage * TILE + 512 * (DMA * wave + i), koff[i]);
-            dma16(rv, smem + (2 + stage) * TILE + 512 * (DMA * wave + i), voff[i]);
-        }
-    };
     // K operand: LDS row l32, logical chunk 16*dh + 2t + hg (dims of this wave).
     int krd[8];
 #pragma unroll
@@ -856,7 +850,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
     }
     // Hand-over slots: 16 floats per lane as 4 chunks, chunk i at slot
     // (i + lane/4) % 4, so 16 lanes of one 16-byte access touch 16 bank groups.
-    float* const xmine = xch + (wave * 64 + lane) * 16;
+    float* const xmine = xch + (wave * 64 + lane) * 16;  // + buffer * 8 * XF
     const float* const xpart = xch + ((wave ^ 4) * 64 + lane) * 16;
     auto xslot = [&](int i) { return 4 * ((i + (lane >> 2)) & 3); };
 
@@ -870,41 +864,84 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
     const bool rev = ti.rev;
     auto tkey = [&](int jt) { return (rev ? ntiles - 1 - jt : jt) * KT; };
 
-    if (ntiles > 0) issue(tkey(0), 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int cur = jt & 1, j0 = tkey(jt);
-        if (jt + 1 < ntiles) issue(tkey(jt + 1), cur ^ 1);  // stage cur^1 was last read before the previous barrier
-        const bool act = jt < wave_tiles;  // the same for both waves of a pair
+    // partial S^T of tile jt over this wave's dims: register r holds key
+    // tkey(jt) + 16*(r/8) + 8*hg + r%8 of query qi
+    auto partial = [&](int jt) {
+        const uint16_t* ks = smem + (jt & 1) * TILE;
         f32x16 s = {};
-        if (act) {
-            // partial S^T: register r holds key j0 + 16*(r/8) + 8*hg + r%8 of query qi
-            const uint16_t* ks = smem + cur * TILE;
-            u32x4 kf[3];
-            kf[0] = *reinterpret_cast<const u32x4*>(ks + krd[0]);
-            kf[1] = *reinterpret_cast<const u32x4*>(ks + krd[1]);
+        u32x4 kf[3];
+        kf[0] = *reinterpret_cast<const u32x4*>(ks + krd[0]);
+        kf[1] = *reinterpret_cast<const u32x4*>(ks + krd[1]);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (t + 2 < 8) kf[(t + 2) % 3] = *reinterpret_cast<const u32x4*>(ks + krd[t + 2]);
-                s = mfma_32x32x16<T>(kf[t % 3], qr[t], s);
-            }
+        for (int t = 0; t < 8; ++t) {
+            if (t + 2 < 8) kf[(t + 2) % 3] = *reinterpret_cast<const u32x4*>(ks + krd[t + 2]);
+            s = mfma_32x32x16<T>(kf[t % 3], qr[t], s);
+        }
+        return s;
+    };
+    auto hand_over = [&](int jt, const f32x16& s) {
+        float* x = xmine + (jt & 1) * 8 * XF;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<f32x4*>(xmine + xslot(i)) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(x + xslot(i)) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
+    };
+    auto add_partner = [&](int jt, f32x16& s) {
+        const float* x = xpart + (jt & 1) * 8 * XF;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 o = *reinterpret_cast<const f32x4*>(x + xslot(i));
+            s[4 * i] += o[0];
+            s[4 * i + 1] += o[1];
+            s[4 * i + 2] += o[2];
+            s[4 * i + 3] += o[3];
+        }
+    };
+
+    // K of tile jt sits in K stage jt % 2, V of tile jt in V stage jt % 2.
+    // Entering step jt: the full scores of tile jt are in s, K of tile jt + 1
+    // and V of tile jt have landed.  Step jt issues K of jt + 2 and V of
+    // jt + 1, forms the partial scores of tile jt + 1 (MFMA) beside the
+    // softmax of tile jt (VALU), accumulates P.V of tile jt, hands the
+    // partial over (hand-over buffers alternate by tile), and after the
+    // barrier adds the partner's partial.
+    auto issue_k = [&](int jt) {
+        const int j0 = tkey(jt);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
+#pragma unroll
+        for (int i = 0; i < DMA; ++i) dma16(rk, smem + (jt & 1) * TILE + 512 * (DMA * wave + i), koff[i]);
+    };
+    auto issue_v = [&](int jt) {
+        const int j0 = tkey(jt);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
+#pragma unroll
+        for (int i = 0; i < DMA; ++i) dma16(rv, smem + (2 + (jt & 1)) * TILE + 512 * (DMA * wave + i), voff[i]);
+    };
+    f32x16 s = {};
+    if (ntiles > 0) {
+        issue_k(0);
+        issue_v(0);
+        if (ntiles > 1) issue_k(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (wave_tiles > 0) {
+            s = partial(0);
+            hand_over(0, s);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // partial scores handed over (the DMA stays in flight)
+        __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if (wave_tiles > 0) add_partner(0, s);
+    }
+    for (int jt = 0; jt < ntiles; ++jt) {
+        const int j0 = tkey(jt);
+        // K stage jt%2 was last read for tile jt's partial, V stage (jt+1)%2
+        // for tile jt-1's P.V: both before the previous barrier
+        if (jt + 2 < ntiles) issue_k(jt + 2);
+        if (jt + 1 < ntiles) issue_v(jt + 1);
+        const bool act = jt < wave_tiles, act_next = jt + 1 < wave_tiles;  // the same for both waves of a pair
+        f32x16 sn = {};
+        if (act_next) sn = partial(jt + 1);
         if (act) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 o = *reinterpret_cast<const f32x4*>(xpart + xslot(i));
-                s[4 * i] += o[0];
-                s[4 * i + 1] += o[1];
-                s[4 * i + 2] += o[2];
-                s[4 * i + 3] += o[3];
-            }
             if ((a.causal && j0 + KT - 1 > qw) || j0 + KT > kv_lim) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -943,7 +980,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
             }
             l_run += ps;
             // O^T += V^T P^T over the tile's two 16-key slices (this wave's dims)
-            const uint16_t* vs = smem + (2 + cur) * TILE;
+            const uint16_t* vs = smem + (2 + (jt & 1)) * TILE;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const u32x4 pw = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
@@ -959,8 +996,13 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
                 for (int db = 0; db < 4; ++db) oacc[db] = mfma_32x32x16<T>(vf[db], pw, oacc[db]);
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's DMA landed
+        if (act_next) hand_over(jt + 1, sn);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K of jt+2 and V of jt+1 landed
         __syncthreads();
+        if (act_next) {
+            add_partner(jt + 1, sn);
+            s = sn;
+        }
     }
 
     const float lt = l_run + swap_half_wave(l_run);
