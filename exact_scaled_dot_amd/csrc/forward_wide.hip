@@ -445,29 +445,46 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void forward_wide_kernel(
             for (int e = 0; e < 8; ++e)
                 if (key0 + e >= kv_lim || (a.causal && key0 + e > qp)) x[e] = -INFINITY;
         }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = max_half_waves(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);  // 0 while the row had no key
-        m_run = m_new;
+        // Weights against the current reference max; the reference moves only
+        // when a tile max exceeds it by 2^8 (log2 units), so O and l, which
+        // share the stale reference, rarely need rescaling.  A lane sum of at
+        // most 2^8 proves each of its (non-negative) weights is at most 2^8,
+        // so the tile max is only taken when a sum is larger or before the
+        // row has a reference.  Every wave holds the same summed scores and
+        // takes the same decisions.
         u32x4 pf;
-        float ls = l_part * alpha;
+        auto weights = [&]() -> float {
+            const float mu = m_run == -INFINITY ? 0.f : m_run;
+            float ws = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            pf[e] = pack2<T>(fast_exp2(x[2 * e] - m_use), fast_exp2(x[2 * e + 1] - m_use));
-            ls = sum2<T>(pf[e], ls);
+            for (int e = 0; e < 4; ++e) {
+                pf[e] = pack2<T>(fast_exp2(x[2 * e] - mu), fast_exp2(x[2 * e + 1] - mu));
+                ws = sum2<T>(pf[e], ws);
+            }
+            return ws;
+        };
+        float ls = weights();
+        if (__any(ls > 256.f || m_run == -INFINITY)) {
+            float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            tmax = max_half_waves(tmax);
+            if (__any(tmax > m_run + 8.f)) {
+                const float m_new = fmaxf(m_run, tmax);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run - m_use);  // 0 while the row had no key
+                m_run = m_new;
+                l_part *= alpha;
+                // C (first part): rescale O^T to the new reference
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            }
+            ls = weights();
         }
-        l_part = ls;
+        l_part += ls;
 
         // C: O^T += V^T P^T over this wave's dims (column = query lane%32).
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        }
         const uint16_t* vs = vw + (j % kWVStages) * LY::VST;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
