@@ -1032,21 +1032,48 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
 // page-table conventions of the 16-bit paged prefill above (each key row of a
 // tile looks up its page; a table entry outside the cache is never read and
 // its keys are hidden).
-template <int D, bool GEN = false, bool PAGED = false>
+// SPLIT (dense, for grids that leave CUs idle): a workgroup owns 32 query
+// rows instead of 128 and its 4 waves split the keys, wave w taking the
+// 32-key blocks w, w + 4, w + 8, ... with its own running (max, sum, O), so
+// each wave does a quarter of the serial work of a row block; at the end
+// waves 1..3 hand their state to wave 0 through LDS, which rescales all four
+// to the largest max and adds them (the merge of partial softmax states).
+template <int D, bool GEN = false, bool PAGED = false, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
     ForwardArgs a, PagedArgs p, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q) {
-    constexpr int RS = D + 4;  // row stride in LDS (floats), 16 B of padding
-    __shared__ __attribute__((aligned(16))) float ks[kBc * RS];
-    __shared__ __attribute__((aligned(16))) float vs[kBc * RS];
+    static_assert(!(SPLIT && PAGED), "key-split waves: dense only");
+    constexpr int RS = D + 4;                 // row stride in LDS (floats), 16 B of padding
+    constexpr int KT = SPLIT ? 32 : kBc;      // keys per tile (SPLIT: per wave's block)
+    constexpr int NH = KT / 32;               // 32-key halves per tile
+    constexpr int NG = SPLIT ? 4 : 1;         // key groups (one tile each per round)
+    constexpr int LT = SPLIT ? 64 : kThreads; // threads loading one tile
+    __shared__ __attribute__((aligned(16))) float ks[NG * KT * RS];
+    __shared__ __attribute__((aligned(16))) float vs[NG * KT * RS];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hg = lane >> 5;
+    const int grp = SPLIT ? wave : 0;   // key group
+    const int rwave = SPLIT ? 0 : wave; // 32-row block of the workgroup
 
-    const TileInfo ti = decode_tile(a);
+    TileInfo ti;
+    if constexpr (SPLIT) {
+        // 32-row blocks; a grid this small needs no XCD ordering
+        const int nqb = (a.Sq + 31) / 32;
+        int t = blockIdx.x;
+        const int qb = t % nqb;
+        t /= nqb;
+        ti.h = t % a.Hq;
+        ti.b = t / a.Hq;
+        ti.gk = ti.h / (a.Hq / a.Hkv);
+        ti.q0 = 32 * qb;
+        ti.rev = false;
+    } else {
+        ti = decode_tile(a);
+    }
     const int DR = GEN ? a.D : D;
     const float* qp;
     const float* kp;
@@ -1081,11 +1108,12 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
         nrows = a.Sq;
         qoff = 0;
         key_extent(a, ti.b, ti.q0, kv_lim, kv_end);
+        if (SPLIT && a.causal) kv_end = min(kv_end, ti.q0 + 32);
     }
 
-    const int qw = ti.q0 + wave * 32;
+    const int qw = ti.q0 + rwave * 32;
     const int qi = qw + l32;
-    const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
+    const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
 
     // Contraction slot (step t, lane half hg) <-> dim 8*(t/4) + 4*hg + t%4, so a
     // lane's operands for 4 consecutive steps are 4 consecutive floats.
@@ -1104,11 +1132,17 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
     float l_run = 0.f;
     const float c = a.scale * kLog2e;
 
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int j0 = jt * kBc;
+    float* const kg = ks + grp * KT * RS;  // this group's K and V tile
+    float* const vg = vs + grp * KT * RS;
+    // Every wave runs the same number of rounds (one barrier pair each);
+    // group g takes tile NG * round + g.
+    const int rounds = (ntiles + NG - 1) / NG;
+    for (int rr = 0; rr < rounds; ++rr) {
+        const int jt = rr * NG + grp;
+        const int j0 = jt * KT;
         __syncthreads();
 #pragma unroll
-        for (int cidx = tid; cidx < kBc * (D / 4); cidx += kThreads) {
+        for (int cidx = SPLIT ? lane : tid; cidx < KT * (D / 4); cidx += LT) {
             const int row = cidx / (D / 4), cc = cidx % (D / 4);
             const int key = j0 + row;
             f32x4 wk = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
@@ -1127,18 +1161,19 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
                 wk = *reinterpret_cast<const f32x4*>(kp + (int64_t)key * DR + cc * 4);
                 wv = *reinterpret_cast<const f32x4*>(vp + (int64_t)key * DR + cc * 4);
             }
-            *reinterpret_cast<f32x4*>(ks + row * RS + cc * 4) = wk;
-            *reinterpret_cast<f32x4*>(vs + row * RS + cc * 4) = wv;
+            *reinterpret_cast<f32x4*>(kg + row * RS + cc * 4) = wk;
+            *reinterpret_cast<f32x4*>(vg + row * RS + cc * 4) = wv;
         }
         __syncthreads();
+        if (jt >= ntiles) continue;  // (SPLIT) this wave has no block this round
         if (a.causal && j0 > qoff + qw + 31) continue;
 
         // S^T: register r of sacc[kb2] holds key j0 + 32*kb2 + 8*(r/4) + 4*hg + r%4.
-        f32x16 sacc[2];
+        f32x16 sacc[NH];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int kb2 = 0; kb2 < NH; ++kb2) {
             sacc[kb2] = f32x16{};
-            const float* krow = ks + (32 * kb2 + l32) * RS + 4 * hg;
+            const float* krow = kg + (32 * kb2 + l32) * RS + 4 * hg;
 #pragma unroll
             for (int T = 0; T < D / 8; ++T) {
                 const f32x4 kv = *reinterpret_cast<const f32x4*>(krow + 8 * T);
@@ -1160,10 +1195,10 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
                 vmask |= (pg >= 0 && pg < p.pages) ? (1 << g) : 0;
             }
         }
-        const bool need_mask = (a.causal && j0 + kBc - 1 > qoff + qw) || (j0 + kBc > kv_lim) || vmask != 15;
+        const bool need_mask = (a.causal && j0 + KT - 1 > qoff + qw) || (j0 + KT > kv_lim) || vmask != 15;
         if (need_mask) {
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kt = 32 * kb2 + 8 * (r >> 2) + 4 * hg + (r & 3), key = j0 + kt;
@@ -1179,7 +1214,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
         {
 #pragma clang fp contract(off)
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb2][r] = sacc[kb2][r] * c;
         }
@@ -1188,7 +1223,9 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        for (int kb2 = 1; kb2 < NH; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
         mx = fmaxf(mx, swap_half_wave(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -1197,7 +1234,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
 
         float psum = 0.f;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
 #pragma clang fp contract(off)
@@ -1211,16 +1248,54 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
 
         // O^T += V^T P^T: step u of block kb2 contracts the key held in register u.
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int key = 32 * kb2 + 8 * (u >> 2) + 4 * hg + (u & 3);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const float vv = vs[key * RS + 32 * db + l32];
+                    const float vv = vg[key * RS + 32 * db + l32];
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, sacc[kb2][u], oacc[db], 0, 0, 0);
                 }
             }
+    }
+
+    if constexpr (SPLIT) {
+        // Waves 1..3 hand (O^T registers, m, lane sum) to wave 0 through the
+        // K area, laid out [wave - 1][value][lane].
+        constexpr int NF = (D / 32) * 16 + 2;
+        static_assert(3 * NF * 64 <= NG * KT * RS, "hand-over fits the K area");
+        __syncthreads();  // every tile read is done
+        if (wave > 0) {
+            float* const xw = ks + (wave - 1) * NF * 64 + lane;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xw[(16 * db + r) * 64] = oacc[db][r];
+            xw[(NF - 2) * 64] = m_run;
+            xw[(NF - 1) * 64] = l_run;
+        }
+        __syncthreads();
+        if (wave > 0) return;
+        float m = m_run;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) m = fmaxf(m, ks[(w * NF + NF - 2) * 64 + lane]);
+        const float mu = m == -INFINITY ? 0.f : m;
+        const float f0 = fast_exp2(m_run - mu);  // 1 for the wave holding the max
+        l_run *= f0;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= f0;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            const float* xw = ks + w * NF * 64 + lane;
+            const float f = fast_exp2(xw[(NF - 2) * 64] - mu);
+            l_run = fmaf(xw[(NF - 1) * 64], f, l_run);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] = fmaf(xw[(16 * db + r) * 64], f, oacc[db][r]);
+        }
+        m_run = m;
     }
 
     const float lt = l_run + swap_half_wave(l_run);
@@ -1370,6 +1445,21 @@ hipError_t launch_f32(const ForwardArgs& a, const PagedArgs& p, hipStream_t s) {
     if (a.D % 4 != 0 || a.D < 4 || a.D > 128 || a.Dv != a.D) return hipErrorInvalidValue;
     const dim3 g = forward_grid(a), t(kThreads);
     const int32_t *bt = p.block_tables, *sl = p.seq_lens, *cu = p.cu_seqlens_q;
+    const int64_t g32 = (int64_t)a.B * a.Hq * ((a.Sq + 31) / 32);
+    if (!PAGED && g32 <= 256) {
+        // Grid of 32-row blocks fits the 256 CUs at one workgroup each: split
+        // each block's keys over its 4 waves.
+        const dim3 g2((unsigned)g32);
+        if (a.D == 64)
+            hipLaunchKernelGGL((forward_f32_kernel<64, false, false, true>), g2, t, 0, s, a, p, bt, sl, cu);
+        else if (a.D == 128)
+            hipLaunchKernelGGL((forward_f32_kernel<128, false, false, true>), g2, t, 0, s, a, p, bt, sl, cu);
+        else if (a.D < 64)
+            hipLaunchKernelGGL((forward_f32_kernel<64, true, false, true>), g2, t, 0, s, a, p, bt, sl, cu);
+        else
+            hipLaunchKernelGGL((forward_f32_kernel<128, true, false, true>), g2, t, 0, s, a, p, bt, sl, cu);
+        return hipGetLastError();
+    }
     if (a.D == 64)
         hipLaunchKernelGGL((forward_f32_kernel<64, false, PAGED>), g, t, 0, s, a, p, bt, sl, cu);
     else if (a.D == 128)

@@ -50,6 +50,40 @@ def test_bf16_small_causal_workload(seed_off):
     run_case(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.dtype, causal=True, seed=w.seed + seed_off)
 
 
+# fp32 when the grid of 32-row blocks fits the CUs: a workgroup owns 32 rows
+# and its 4 waves take every fourth 32-key block, merging their running
+# (max, sum, O) at the end.
+
+@pytest.mark.parametrize("D", [64, 128, 36, 100])
+@pytest.mark.parametrize("mask", [0, 1, 2, 3], ids=["none", "causal", "padding", "causal+padding"])
+def test_fp32_key_split_waves(D, mask):
+    # 6, 10 and 3 blocks of 32 keys: waves with two, three, one or no block
+    B, Hq, Hkv = 3, 2, 1
+    for Sq, Sk in ((190, 190), (70, 300), (129, 65)):
+        if mask & 1 and Sq != Sk:
+            continue
+        q, k, v = draw_qkv(B, Hq, Hkv, Sq, Sk, D, torch.float32, 830 + D + mask + Sk, DEV)
+        lens = torch.tensor([Sk, 0, max(1, Sk // 3)], dtype=torch.int32, device=DEV) if mask & 2 else None
+        scale = 1 / math.sqrt(D)
+        out, lse = sd.sdpa_forward_lse(q, k, v, scale, mask, lens)
+        torch.cuda.synchronize()
+        ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), scale, mask,
+                                   None if lens is None else lens.cpu().numpy(), return_lse=True)
+        o, l = to64(out), to64(lse)
+        if mask & 2:  # batch 1 has no visible key: NaN rows, lse -inf
+            assert np.isnan(o[1]).all() and np.isneginf(l[1]).all()
+            o, ref, l, rlse = o[[0, 2]], ref[[0, 2]], l[[0, 2]], rlse[[0, 2]]
+        compare(o, ref, torch.float32, "fp32 split D=%d mask=%d Sq=%d Sk=%d" % (D, mask, Sq, Sk))
+        assert np.abs(l - rlse).max() < 1e-5
+
+
+@pytest.mark.parametrize("Hq", [64, 65])
+def test_fp32_key_split_grid_boundary(Hq):
+    # 256 blocks of 32 rows take the key-split form, 260 the plain one
+    run_case(1, Hq, 1, 100, 333, 64, torch.float32, causal=False, seed=840 + Hq)
+    run_case(1, Hq, 1, 100, 100, 128, torch.float32, causal=True, seed=850 + Hq)
+
+
 # ------------------------------------------------------------ ragged sweeps
 
 SIZES = [1, 2, 17, 63, 64, 65, 127, 129, 200]
