@@ -94,16 +94,20 @@ enum {
  *   dtype    SDPA_BF16, SDPA_F16 or SDPA_F32
  *   stream   hipStream_t as void*
  * Supported head dims: SDPA_BF16 / SDPA_F16 any multiple of 8 from 8 to 1024
- * (ruDNN user guide section 9 allows up to 1024): up to 256 on the 64-, 128-
- * and 256-wide kernels, with the dims past D read as zeros on chip (above
- * 128 two workgroups per query block each produce 128 output dims and both
- * compute the scores); above 256 on a kernel that splits the head dim over
- * 4, 6 or 8 waves of 128 dims per 32-row query block (partial scores summed
- * in LDS).  Any other D from 1 to 1023 on the same kernels with Q, K and V
- * read element by element (rows of such a width are not 16-byte aligned);
- * not with a bias.  SDPA_F32 any multiple of 4 from 4 to 128 (the 64- and 128-wide
- * fp32 kernels, likewise).  One head (Sq*D or Sk*D elements) must be under
- * 2 GiB (SDPA_ERR_UNSUPPORTED otherwise).
+ * (ruDNN user guide section 9 allows up to 1024): up to 128 on the 64- and
+ * 128-wide kernels, with the dims past D read as zeros on chip; from 136 to
+ * 256 on paired waves that split the head dim in two and add each other's
+ * partial scores in LDS (with a bias: two workgroups per query block each
+ * produce 128 output dims and both compute the scores); above 256 on a
+ * kernel that splits the head dim over 4, 6 or 8 waves of 128 dims per
+ * 32-row query block (partial scores summed in LDS).  Any other D from 1 to
+ * 1023 on the same kernels with Q, K and V read element by element (rows of
+ * such a width are not 16-byte aligned); not with a bias.  SDPA_F32 any
+ * multiple of 4 from 4 to 128 (the 64- and 128-wide fp32 kernels, likewise;
+ * when the grid of 32-row query blocks fits the CUs, each block's keys are
+ * split over its workgroup's waves and their softmax states merged).  One
+ * head (Sq*D or Sk*D elements) must be under 2 GiB (SDPA_ERR_UNSUPPORTED
+ * otherwise).
  */
 sdpa_status_t sdpa_forward(const void *q, const void *k, const void *v,
                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
