@@ -864,89 +864,78 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
     const bool rev = ti.rev;
     auto tkey = [&](int jt) { return (rev ? ntiles - 1 - jt : jt) * KT; };
 
-    // partial S^T of tile jt over this wave's dims: register r holds key
-    // tkey(jt) + 16*(r/8) + 8*hg + r%8 of query qi
-    auto partial = [&](int jt) {
-        const uint16_t* ks = smem + (jt & 1) * TILE;
-        f32x16 s = {};
+    // This lane's hand-over slot addresses (its own 4 chunks, the partner's).
+    float* xw[4];
+    const float* xr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xw[i] = xmine + xslot(i);
+        xr[i] = xpart + xslot(i);
+    }
+    // Partial S^T over this wave's dims of the tile in K stage st: register r
+    // holds key j0 + 16*(r/8) + 8*hg + r%8 of query qi.
+    auto partial = [&](const int st, f32x16& s) __attribute__((always_inline)) {
+        const uint16_t* ks = smem + st * TILE;
         u32x4 kf[3];
         kf[0] = *reinterpret_cast<const u32x4*>(ks + krd[0]);
         kf[1] = *reinterpret_cast<const u32x4*>(ks + krd[1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             if (t + 2 < 8) kf[(t + 2) % 3] = *reinterpret_cast<const u32x4*>(ks + krd[t + 2]);
-            s = mfma_32x32x16<T>(kf[t % 3], qr[t], s);
+            s = mfma_32x32x16<T>(kf[t % 3], qr[t], t == 0 ? f32x16{} : s);
         }
-        return s;
     };
-    auto hand_over = [&](int jt, const f32x16& s) {
-        float* x = xmine + (jt & 1) * 8 * XF;
+    auto hand_over = [&](const int buf, const f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<f32x4*>(x + xslot(i)) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
+            *reinterpret_cast<f32x4*>(xw[i] + buf * 8 * XF) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
     };
-    auto add_partner = [&](int jt, f32x16& s) {
-        const float* x = xpart + (jt & 1) * 8 * XF;
+    auto add_partner = [&](const int buf, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 o = *reinterpret_cast<const f32x4*>(x + xslot(i));
+            const f32x4 o = *reinterpret_cast<const f32x4*>(xr[i] + buf * 8 * XF);
             s[4 * i] += o[0];
             s[4 * i + 1] += o[1];
             s[4 * i + 2] += o[2];
             s[4 * i + 3] += o[3];
         }
     };
-
-    // K of tile jt sits in K stage jt % 2, V of tile jt in V stage jt % 2.
-    // Entering step jt: the full scores of tile jt are in s, K of tile jt + 1
-    // and V of tile jt have landed.  Step jt issues K of jt + 2 and V of
-    // jt + 1, forms the partial scores of tile jt + 1 (MFMA) beside the
-    // softmax of tile jt (VALU), accumulates P.V of tile jt, hands the
-    // partial over (hand-over buffers alternate by tile), and after the
-    // barrier adds the partner's partial.
-    auto issue_k = [&](int jt) {
+    auto issue_k = [&](int jt, const int st) __attribute__((always_inline)) {
         const int j0 = tkey(jt);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
 #pragma unroll
-        for (int i = 0; i < DMA; ++i) dma16(rk, smem + (jt & 1) * TILE + 512 * (DMA * wave + i), koff[i]);
+        for (int i = 0; i < DMA; ++i) dma16(rk, smem + st * TILE + 512 * (DMA * wave + i), koff[i]);
     };
-    auto issue_v = [&](int jt) {
+    auto issue_v = [&](int jt, const int st) __attribute__((always_inline)) {
         const int j0 = tkey(jt);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)j0 * DR, (uint32_t)(a.Sk - j0) * DR * 2);
 #pragma unroll
-        for (int i = 0; i < DMA; ++i) dma16(rv, smem + (2 + (jt & 1)) * TILE + 512 * (DMA * wave + i), voff[i]);
+        for (int i = 0; i < DMA; ++i) dma16(rv, smem + (2 + st) * TILE + 512 * (DMA * wave + i), voff[i]);
     };
-    f32x16 s = {};
-    if (ntiles > 0) {
-        issue_k(0);
-        issue_v(0);
-        if (ntiles > 1) issue_k(1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (wave_tiles > 0) {
-            s = partial(0);
-            hand_over(0, s);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (wave_tiles > 0) add_partner(0, s);
-    }
-    for (int jt = 0; jt < ntiles; ++jt) {
+
+    // K of tile jt sits in K stage jt % 2, V of tile jt in V stage jt % 2,
+    // the partial scores of tile jt go to hand-over buffer jt % 2.  Step jt
+    // (cur = jt % 2, a literal in each call, so every LDS address is a
+    // constant offset and the two score tiles swap roles without copies):
+    // the full scores of tile jt are in scur, K of tile jt + 1 and V of tile
+    // jt have landed; it issues K of jt + 2 and V of jt + 1, forms the partial
+    // scores of tile jt + 1 into snext (MFMA) beside the softmax of tile jt
+    // (VALU), accumulates P.V of tile jt, hands the partial over and, after
+    // the barrier, adds the partner's.
+    auto step = [&](int jt, const int cur, f32x16& scur, f32x16& snext) __attribute__((always_inline)) {
         const int j0 = tkey(jt);
-        // K stage jt%2 was last read for tile jt's partial, V stage (jt+1)%2
+        // K stage cur was last read for tile jt's partial, V stage cur ^ 1
         // for tile jt-1's P.V: both before the previous barrier
-        if (jt + 2 < ntiles) issue_k(jt + 2);
-        if (jt + 1 < ntiles) issue_v(jt + 1);
+        if (jt + 2 < ntiles) issue_k(jt + 2, cur);
+        if (jt + 1 < ntiles) issue_v(jt + 1, cur ^ 1);
         const bool act = jt < wave_tiles, act_next = jt + 1 < wave_tiles;  // the same for both waves of a pair
-        f32x16 sn = {};
-        if (act_next) sn = partial(jt + 1);
+        if (act_next) partial(cur ^ 1, snext);
         if (act) {
             if ((a.causal && j0 + KT - 1 > qw) || j0 + KT > kv_lim) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + 16 * (r >> 3) + 8 * hg + (r & 7);
-                    if (key >= kv_lim || (a.causal && key > qi)) s[r] = -INFINITY;
+                    if (key >= kv_lim || (a.causal && key > qi)) scur[r] = -INFINITY;
                 }
             }
             uint32_t pk[8];
@@ -955,7 +944,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
                 float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
-                    pk[r >> 1] = pack2<T>(fast_exp2(fmaf(s[r], c, neg)), fast_exp2(fmaf(s[r + 1], c, neg)));
+                    pk[r >> 1] = pack2<T>(fast_exp2(fmaf(scur[r], c, neg)), fast_exp2(fmaf(scur[r + 1], c, neg)));
                     if (r & 2) ps1 = sum2<T>(pk[r >> 1], ps1);
                     else ps0 = sum2<T>(pk[r >> 1], ps0);
                 }
@@ -963,9 +952,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
             };
             float ps = weights();
             if (__any(ps > 256.f || m_run == -INFINITY)) {
-                float mx = s[0];
+                float mx = scur[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, scur[r]);
                 mx = max_half_waves(mx);
                 if (__any(mx > m_run + tau)) {
                     const float m_new = fmaxf(m_run, mx);
@@ -980,7 +969,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
             }
             l_run += ps;
             // O^T += V^T P^T over the tile's two 16-key slices (this wave's dims)
-            const uint16_t* vs = smem + (2 + (jt & 1)) * TILE;
+            const uint16_t* vs = smem + (2 + cur) * TILE;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const u32x4 pw = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
@@ -996,13 +985,31 @@ __global__ __launch_bounds__(kPairThreads, 1) void forward_pair_kernel(ForwardAr
                 for (int db = 0; db < 4; ++db) oacc[db] = mfma_32x32x16<T>(vf[db], pw, oacc[db]);
             }
         }
-        if (act_next) hand_over(jt + 1, sn);
+        if (act_next) hand_over(cur ^ 1, snext);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K of jt+2 and V of jt+1 landed
         __syncthreads();
-        if (act_next) {
-            add_partner(jt + 1, sn);
-            s = sn;
+        if (act_next) add_partner(cur ^ 1, snext);
+    };
+
+    f32x16 sA = {}, sB = {};
+    if (ntiles > 0) {
+        issue_k(0, 0);
+        issue_v(0, 0);
+        if (ntiles > 1) issue_k(1, 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (wave_tiles > 0) {
+            partial(0, sA);
+            hand_over(0, sA);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (wave_tiles > 0) add_partner(0, sA);
+    }
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        step(jt, 0, sA, sB);
+        if (jt + 1 < ntiles) step(jt + 1, 1, sB, sA);
     }
 
     const float lt = l_run + swap_half_wave(l_run);
@@ -1141,8 +1148,10 @@ __global__ __launch_bounds__(kThreads, 1) void forward_f32_kernel(
         const int jt = rr * NG + grp;
         const int j0 = jt * KT;
         __syncthreads();
+        static_assert(KT * (D / 4) % LT == 0, "whole load rounds");
 #pragma unroll
-        for (int cidx = SPLIT ? lane : tid; cidx < KT * (D / 4); cidx += LT) {
+        for (int li = 0; li < KT * (D / 4) / LT; ++li) {
+            const int cidx = (SPLIT ? lane : tid) + li * LT;
             const int row = cidx / (D / 4), cc = cidx % (D / 4);
             const int key = j0 + row;
             f32x4 wk = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};

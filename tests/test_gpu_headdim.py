@@ -192,6 +192,23 @@ def test_forward_paired_wave_cross_lengths(dtype, mask):
     assert np.abs(to64(lse) - rlse).max() < 1e-2
 
 
+@pytest.mark.parametrize("D", [256, 200])
+def test_forward_paired_wave_empty_batch(D):
+    # key_lens = 0: no tile at all for that batch (no barrier either); its rows
+    # are 0/0 = NaN with lse -inf, the other batches are unaffected
+    B, Hq, Hkv, S = 3, 4, 2, 150
+    q, k, v = draw_qkv(B, Hq, Hkv, S, S, D, BF16, 818 + D, DEV)
+    lens = torch.tensor([150, 0, 64], dtype=torch.int32, device=DEV)
+    out, lse = sd.sdpa_forward_lse(q, k, v, 0.06, sd.MASK_CAUSAL | sd.MASK_KEY_PADDING, lens)
+    torch.cuda.synchronize()
+    o, l = to64(out), to64(lse)
+    assert np.isnan(o[1]).all() and np.isneginf(l[1]).all()
+    ref, rlse = O.sdpa_forward(to64(q), to64(k), to64(v), 0.06, O.MASK_CAUSAL | O.MASK_KEY_PADDING,
+                               lens.cpu().numpy(), return_lse=True)
+    compare(o[[0, 2]], ref[[0, 2]], BF16, "paired D=%d empty batch" % D)
+    assert np.abs(l[[0, 2]] - rlse[[0, 2]]).max() < 1e-2
+
+
 def test_forward_paired_wave_swept_grid():
     # more workgroups than the chip holds at once: the non-causal sweep order
     # over query blocks sharing one K/V head
