@@ -373,8 +373,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
 #pragma unroll
                 for (int dt = 0; dt < DV / 16; ++dt)
                     if (16 * dt + 4 * grp < DVR)
-                        *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (grp == 0) a.lse_part[prow0 + (int64_t)col * a.splits] = -INFINITY;
+                        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4*>(op + 16 * dt));
+                if (grp == 0) __builtin_nontemporal_store(-INFINITY, a.lse_part + prow0 + (int64_t)col * a.splits);
             }
             continue;
         }
@@ -478,6 +478,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         // Column totals: the denominator is spread over the 4 lane groups.
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
+        // The partial and its lse go out with non-temporal stores (read once,
+        // by the merge pass).  vmcnt retires in issue order, so the ring
+        // loads issued after an item's stores wait for the stores too; with
+        // the default policy that cost the 128-wide decode 6% of its time.
         if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
             float* op = a.o_part + prow * DVP + 4 * grp;
@@ -485,16 +489,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
 #pragma unroll
                 for (int dt = 0; dt < DV / 16; ++dt)
                     if (16 * dt + 4 * grp < DVR)
-                        *reinterpret_cast<f32x4*>(op + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (grp == 0) a.lse_part[prow] = -INFINITY;
+                        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4*>(op + 16 * dt));
+                if (grp == 0) __builtin_nontemporal_store(-INFINITY, a.lse_part + prow);
             } else {
 #pragma unroll
                 for (int dt = 0; dt < DV / 16; ++dt)  // O^T register i of tile dt: dim 16*dt + 4*grp + i
                     if (16 * dt + 4 * grp < DVR)
-                        *reinterpret_cast<f32x4*>(op + 16 * dt) =
+                        __builtin_nontemporal_store(
                             f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
-                                  oacc[dt][3] / l_run};
-                if (grp == 0) a.lse_part[prow] = m_run * a.scale + __logf(l_run);
+                                  oacc[dt][3] / l_run},
+                            reinterpret_cast<f32x4*>(op + 16 * dt));
+                if (grp == 0) __builtin_nontemporal_store(m_run * a.scale + __logf(l_run), a.lse_part + prow);
             }
         }
     }
@@ -689,9 +694,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_f32_kernel(
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int d0 = 16 * grp + 4 * j + 64 * dh;
-                        if (d0 < DR) *reinterpret_cast<f32x4*>(op + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (d0 < DR)
+                            __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4*>(op + d0));
                     }
-                if (grp == 0) a.lse_part[prow0 + (int64_t)col * a.splits] = -INFINITY;
+                if (grp == 0) __builtin_nontemporal_store(-INFINITY, a.lse_part + prow0 + (int64_t)col * a.splits);
             }
             continue;
         }
@@ -798,11 +804,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_f32_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const int d0 = 16 * grp + 4 * j + 64 * dh;
                     if (d0 < DR)
-                        *reinterpret_cast<f32x4*>(op + d0) =
+                        __builtin_nontemporal_store(
                             f32x4{oacc[4 * dh][j] * inv, oacc[4 * dh + 1][j] * inv,
-                                  oacc[4 * dh + 2][j] * inv, oacc[4 * dh + 3][j] * inv};
+                                  oacc[4 * dh + 2][j] * inv, oacc[4 * dh + 3][j] * inv},
+                            reinterpret_cast<f32x4*>(op + d0));
                 }
-            if (grp == 0) a.lse_part[prow] = empty ? -INFINITY : m_run * a.scale + __logf(l_run);
+            if (grp == 0)
+                __builtin_nontemporal_store(empty ? -INFINITY : m_run * a.scale + __logf(l_run), a.lse_part + prow);
         }
     }
 }
