@@ -193,7 +193,16 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     constexpr int OPS = L::DMA + LV::DMA;              // vector memory ops per step
     static_assert(NS >= 2, "ring depth");
     const Meta meta{key_lens, tables, seq_lens, query_seq, query_pos};
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * NS * STAGE];
+    // Parked partials (kPark): items with at most 4 query heads leave their
+    // partial and lse in LDS, behind the rings, and a wave writes them out
+    // KPARK items at a time.  The ring loads issued after a store cannot
+    // retire before it (vmcnt retires in issue order), so one flush every
+    // KPARK items holds the stream back once instead of KPARK times.
+    constexpr bool kPark = !GEN && !ELEM && DV == 128;
+    constexpr int KPARK = 3;
+    constexpr int PSLOT = 4 * DV + 4;  // floats: 4 rows of DV, then 4 lse values
+    constexpr int PARK = kPark ? kDecWaves * KPARK * PSLOT * 2 : 0;  // 16-bit units
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * NS * STAGE + PARK];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -361,6 +370,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     seek(it0);
     for (int j = 0; j < NS - 1 && i_it < it1; ++j) issue_next();
 
+    float* const park = reinterpret_cast<float*>(smem + kDecWaves * NS * STAGE) + wave * KPARK * PSLOT;
+    int nparked = 0, pnh0 = 0, pnh1 = 0, pnh2 = 0;
+    int64_t prw0 = 0, prw1 = 0, prw2 = 0;
+    // Write out the parked partials: each lane its own values, as parked.
+    auto flush = [&]() {
+#pragma unroll
+        for (int k = 0; k < KPARK; ++k) {
+            if (k >= nparked) break;
+            const int nh = k == 0 ? pnh0 : (k == 1 ? pnh1 : pnh2);
+            const int64_t pr = k == 0 ? prw0 : (k == 1 ? prw1 : prw2);
+            if (col < nh) {
+                const float* sl = park + k * PSLOT;
+                const int64_t prow = pr + (int64_t)col * a.splits;
+                float* op = a.o_part + prow * DVP + 4 * grp;
+#pragma unroll
+                for (int dt = 0; dt < DV / 16; ++dt)
+                    __builtin_nontemporal_store(lds_load_f32x4(sl + col * DV + 16 * dt + 4 * grp),
+                                                reinterpret_cast<f32x4*>(op + 16 * dt));
+                if (grp == 0) __builtin_nontemporal_store(lds_load(sl + 4 * DV + col), a.lse_part + prow);
+            }
+        }
+        nparked = 0;
+    };
+
     u32x4 qb[L::KSTEPS];
     int q_head = -1;
     int done = 0;  // steps computed
@@ -482,7 +515,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
         // by the merge pass).  vmcnt retires in issue order, so the ring
         // loads issued after an item's stores wait for the stores too; with
         // the default policy that cost the 128-wide decode 6% of its time.
-        if (col < g.nh) {
+        if (kPark && g.nh <= 4) {
+            float* sl = park + nparked * PSLOT;
+            if (col < g.nh) {
+                const bool none = m_run == -INFINITY;  // every key masked (paged: invalid pages only)
+#pragma unroll
+                for (int dt = 0; dt < DV / 16; ++dt)
+                    lds_store_f32x4(sl + col * DV + 16 * dt + 4 * grp,
+                                    none ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                         : f32x4{oacc[dt][0] / l_run, oacc[dt][1] / l_run, oacc[dt][2] / l_run,
+                                                 oacc[dt][3] / l_run});
+                if (grp == 0) lds_store(sl + 4 * DV + col, none ? -INFINITY : m_run * a.scale + __logf(l_run));
+            }
+            if (nparked == 0) {
+                prw0 = prow0;
+                pnh0 = g.nh;
+            } else if (nparked == 1) {
+                prw1 = prow0;
+                pnh1 = g.nh;
+            } else {
+                prw2 = prow0;
+                pnh2 = g.nh;
+            }
+            if (++nparked == KPARK) flush();
+        } else if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
             float* op = a.o_part + prow * DVP + 4 * grp;
             if (m_run == -INFINITY) {  // every key masked (paged: invalid pages only)
@@ -503,6 +559,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
             }
         }
     }
+    if (kPark && nparked > 0) flush();
 }
 
 template <int D, class T, bool GEN = false, bool ELEM = false>
