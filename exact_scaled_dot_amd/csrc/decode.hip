@@ -189,17 +189,20 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     using L = DecGeo<D>;    // K
     using LV = DecGeo<DV>;  // V
     constexpr int STAGE = L::TILE + LV::TILE;          // K tile, then V tile
-    constexpr int NS = kRingBytes / (2 * STAGE);       // ring stages per wave
-    constexpr int OPS = L::DMA + LV::DMA;              // vector memory ops per step
-    static_assert(NS >= 2, "ring depth");
-    const Meta meta{key_lens, tables, seq_lens, query_seq, query_pos};
     // Parked partials (kPark): items with at most 4 query heads leave their
     // partial and lse in LDS, behind the rings, and a wave writes them out
     // KPARK items at a time.  The ring loads issued after a store cannot
     // retire before it (vmcnt retires in issue order), so one flush every
-    // KPARK items holds the stream back once instead of KPARK times.
+    // KPARK items holds the stream back once instead of KPARK times (the
+    // flush after a wave's last item holds nothing back).  The 128-wide form
+    // gives up a ring stage (24 KB per wave) for 7 slots.
     constexpr bool kPark = !GEN && !ELEM && DV == 128;
-    constexpr int KPARK = 3;
+    constexpr bool kDeep = kPark && D == 128;
+    constexpr int NS = (kDeep ? 24576 : kRingBytes) / (2 * STAGE);  // ring stages per wave
+    constexpr int OPS = L::DMA + LV::DMA;              // vector memory ops per step
+    static_assert(NS >= 2, "ring depth");
+    const Meta meta{key_lens, tables, seq_lens, query_seq, query_pos};
+    constexpr int KPARK = kDeep ? 7 : 3;
     constexpr int PSLOT = 4 * DV + 4;  // floats: 4 rows of DV, then 4 lse values
     constexpr int PARK = kPark ? kDecWaves * KPARK * PSLOT * 2 : 0;  // 16-bit units
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kDecWaves * NS * STAGE + PARK];
@@ -371,15 +374,16 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
     for (int j = 0; j < NS - 1 && i_it < it1; ++j) issue_next();
 
     float* const park = reinterpret_cast<float*>(smem + kDecWaves * NS * STAGE) + wave * KPARK * PSLOT;
-    int nparked = 0, pnh0 = 0, pnh1 = 0, pnh2 = 0;
-    int64_t prw0 = 0, prw1 = 0, prw2 = 0;
+    int nparked = 0;
+    int pnh[KPARK];         // query heads of each parked item
+    int64_t prw[KPARK];     // its first partial row
     // Write out the parked partials: each lane its own values, as parked.
     auto flush = [&]() {
 #pragma unroll
         for (int k = 0; k < KPARK; ++k) {
             if (k >= nparked) break;
-            const int nh = k == 0 ? pnh0 : (k == 1 ? pnh1 : pnh2);
-            const int64_t pr = k == 0 ? prw0 : (k == 1 ? prw1 : prw2);
+            const int nh = pnh[k];
+            const int64_t pr = prw[k];
             if (col < nh) {
                 const float* sl = park + k * PSLOT;
                 const int64_t prow = pr + (int64_t)col * a.splits;
@@ -527,16 +531,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_bf16_kernel(
                                                  oacc[dt][3] / l_run});
                 if (grp == 0) lds_store(sl + 4 * DV + col, none ? -INFINITY : m_run * a.scale + __logf(l_run));
             }
-            if (nparked == 0) {
-                prw0 = prow0;
-                pnh0 = g.nh;
-            } else if (nparked == 1) {
-                prw1 = prow0;
-                pnh1 = g.nh;
-            } else {
-                prw2 = prow0;
-                pnh2 = g.nh;
-            }
+#pragma unroll
+            for (int k = 0; k < KPARK; ++k)  // constant indices: the slots stay in registers
+                if (k == nparked) {
+                    prw[k] = prow0;
+                    pnh[k] = g.nh;
+                }
             if (++nparked == KPARK) flush();
         } else if (col < g.nh) {
             const int64_t prow = prow0 + (int64_t)col * a.splits;
