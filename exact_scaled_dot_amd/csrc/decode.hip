@@ -92,7 +92,6 @@ struct DecGeo {
     static constexpr int RPW = D > 128 ? 1 : 256 / (2 * D);  // rows per 256-byte bank window (1: a row spans two)
     static constexpr int TILE = kStep * D;             // bf16 elements of one K or V step
     static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
-    static constexpr int NS = kRingBytes / (2 * STAGE);  // ring stages per wave
     static constexpr int DMA = TILE * 2 / 1024;        // 1-KB DMA loads per tile
     static constexpr int OPS = 2 * DMA;                // vector memory ops per step
     static constexpr int KSTEPS = D / 32;              // MFMA contraction steps of S
@@ -103,7 +102,6 @@ struct DecGeo {
     // fall on 16 distinct 16-byte bank groups.
     __device__ static int fv(int r) { return 2 * ((r / RPW) % (8 / RPW)); }
 };
-static_assert(DecGeo<256>::NS == 2 && DecGeo<128>::NS == 4 && DecGeo<64>::NS == 8, "ring depth");
 
 // Per-launch metadata pointers, each read with scalar loads (hence separate
 // __restrict__ kernel arguments rather than struct members).
